@@ -1,0 +1,186 @@
+"""Reference oracle for batch speculative decoding's verify-and-resynchronize
+step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product library never calls it
+and shares no code with it.  `liboracle.so` (oracle.c) holds the batched
+reference; `brute.py` is a second, per-sequence numpy reference for tiny cases.
+
+Every function is pinned by CPU tests against values the pages fix (their
+worked examples), closed forms and brute force; see oracle.c for the passages
+each one follows and the readings taken where the pages leave a choice.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+F32, F16, BF16 = 0, 1, 2
+OK, E_ARG, E_CAPACITY, E_PRECOND = 0, -1, -2, -3
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code):
+        super().__init__("oracle returned %d" % code)
+        self.code = code
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.path.join(HERE, "liboracle.so")
+        if not os.path.exists(path):
+            from . import _build
+            _build.build()
+        L = C.CDLL(path)
+        vp, i32p, i8p = C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int8)
+        ci, i64 = C.c_int, C.c_int64
+        L.oracle_verify_greedy.argtypes = [vp, ci, i64, ci, ci, ci, i32p, i32p, i32p, i32p]
+        L.oracle_verify_sample.argtypes = [C.POINTER(C.c_float), C.POINTER(C.c_float), ci, ci, ci, i32p,
+                                           C.POINTER(C.c_float), C.POINTER(C.c_float), i32p, i32p,
+                                           C.POINTER(C.c_double)]
+        L.oracle_realign_eqspec.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, i32p, C.c_int32, i32p, i8p,
+                                            i32p, i32p, i32p, C.c_int32, i32p, i32p, i8p, i32p, i32p]
+        L.oracle_group_by_len.argtypes = [i32p, ci, ci, i32p, i32p, i32p, i32p]
+        L.oracle_gather.argtypes = [ci, ci, ci, ci, ci, ci, vp, i32p, i32p, i32p, ci, ci, i32p, ci, vp, i32p, i32p,
+                                    i8p, i32p, C.c_int32]
+        L.oracle_append.argtypes = [ci, ci, ci, ci, ci, ci, vp, i32p, i32p, i32p, ci, ci, vp, i32p, i32p, i32p]
+        for f in (L.oracle_verify_greedy, L.oracle_verify_sample, L.oracle_realign_eqspec, L.oracle_group_by_len,
+                  L.oracle_gather, L.oracle_append):
+            f.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, t=C.c_int32):
+    return None if a is None else a.ctypes.data_as(C.POINTER(t))
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _check(rc):
+    if rc != OK:
+        raise OracleError(rc)
+
+
+def _dtype_code(arr):
+    if arr.dtype == np.float32:
+        return F32
+    if arr.dtype == np.float16:
+        return F16
+    if arr.dtype == np.uint16 or arr.dtype == np.int16:
+        return BF16  # raw bfloat16 bits
+    raise TypeError("logits must be float32, float16 or raw bf16 bits (uint16)")
+
+
+def verify_greedy(logits, draft, B, D, V, row_stride=None):
+    """logits: [B*(D+1), row_stride] (float32 | float16 | uint16 bf16 bits)."""
+    logits = np.ascontiguousarray(logits)
+    row_stride = logits.shape[-1] if row_stride is None else row_stride
+    draft = _i32(draft).reshape(-1)
+    acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    tgt = np.empty(B * (D + 1), np.int32)
+    _check(lib().oracle_verify_greedy(logits.ctypes.data, _dtype_code(logits), row_stride, B, D, V, _p(draft),
+                                      _p(acc), _p(nxt), _p(tgt)))
+    return acc, nxt, tgt.reshape(B, D + 1)
+
+
+def verify_sample(p, q, draft, u_accept, u_draw):
+    """p [B,D+1,V], q [B,D,V] float32; u_accept [B,D], u_draw [B,D+1] float32."""
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, D1, V = p.shape
+    D = D1 - 1
+    draft = _i32(draft).reshape(-1)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(-1)
+    ud = np.ascontiguousarray(u_draw, dtype=np.float32).reshape(-1)
+    acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    mass = np.empty(B, np.float64)
+    rc = lib().oracle_verify_sample(_p(p, C.c_float), _p(q, C.c_float), B, D, V, _p(draft), _p(ua, C.c_float),
+                                    _p(ud, C.c_float), _p(acc), _p(nxt), _p(mass, C.c_double))
+    if rc not in (OK, E_PRECOND):
+        raise OracleError(rc)
+    return acc, nxt, mass
+
+
+def realign_eqspec(kv_in, kv_new, len_in, width_in, tok_in, mask_in, accept_len, next_token, draft,
+                   cap_out=None, pad_token=0, kv_out=None, tok_out=None, pos_out=None, mask_out=None):
+    """Unpad-append-repad of a left-padded rectangle.
+
+    kv_in [L,2,B,H,cap_in,Dh]; kv_new [L,2,B,H,D+1,Dh]; tok_in/mask_in [B,cap_in].
+    Output arrays are allocated (zero) unless passed in; only [0, width) of each
+    row is written.  Returns dict(kv, tokens, pos, mask, len, width)."""
+    L, two, B, H, cap_in, Dh = kv_in.shape
+    D = kv_new.shape[4] - 1
+    cap_out = cap_in if cap_out is None else cap_out
+    es = kv_in.dtype.itemsize
+    kv_in = np.ascontiguousarray(kv_in)
+    kv_new = np.ascontiguousarray(kv_new, dtype=kv_in.dtype)
+    if kv_out is None:
+        kv_out = np.zeros((L, 2, B, H, cap_out, Dh), dtype=kv_in.dtype)
+    tok_out = np.zeros((B, cap_out), np.int32) if tok_out is None else tok_out
+    pos_out = np.zeros((B, cap_out), np.int32) if pos_out is None else pos_out
+    mask_out = np.zeros((B, cap_out), np.int8) if mask_out is None else mask_out
+    len_out = np.empty(B, np.int32)
+    width_out = np.empty(1, np.int32)
+    mask_in = None if mask_in is None else np.ascontiguousarray(mask_in, dtype=np.int8)
+    tok_in = _i32(tok_in)
+    rc = lib().oracle_realign_eqspec(L, H, Dh, es, B, cap_in, cap_out, D, kv_in.ctypes.data, kv_out.ctypes.data,
+                                     kv_new.ctypes.data, _p(_i32(len_in)), int(width_in), _p(tok_in),
+                                     _p(mask_in, C.c_int8), _p(_i32(accept_len)), _p(_i32(next_token)),
+                                     _p(_i32(draft).reshape(-1)), pad_token, _p(tok_out), _p(pos_out),
+                                     _p(mask_out, C.c_int8), _p(len_out), _p(width_out))
+    _check(rc)
+    return dict(kv=kv_out, tokens=tok_out, pos=pos_out, mask=mask_out, len=len_out, width=int(width_out[0]))
+
+
+def group_by_len(lens, G):
+    lens = _i32(lens)
+    N = lens.shape[0]
+    nb = (N + G - 1) // G
+    order = np.empty(N, np.int32)
+    uni = np.empty(max(nb, 1), np.int32)
+    wid = np.empty(max(nb, 1), np.int32)
+    nu = np.empty(1, np.int32)
+    _check(lib().oracle_group_by_len(_p(lens), N, G, _p(order), _p(uni), _p(wid), _p(nu)))
+    return order, uni[:nb], wid[:nb], int(nu[0])
+
+
+def gather(kv_pool, tok_pool, len_pool, rows, G, skip_group, cap_out, pad_token=0, kv_out=None, tok_out=None,
+           pos_out=None, mask_out=None, width_out=None):
+    """Left-padded rectangles of the pool rows listed in `rows`, one per group of G."""
+    L, two, N, H, cap_pool, Dh = kv_pool.shape
+    rows = _i32(rows)
+    B = rows.shape[0]
+    ng = (B + G - 1) // G
+    if kv_out is None:
+        kv_out = np.zeros((L, 2, B, H, cap_out, Dh), dtype=kv_pool.dtype)
+    tok_out = np.zeros((B, cap_out), np.int32) if tok_out is None else tok_out
+    pos_out = np.zeros((B, cap_out), np.int32) if pos_out is None else pos_out
+    mask_out = np.zeros((B, cap_out), np.int8) if mask_out is None else mask_out
+    width_out = np.zeros(max(ng, 1), np.int32) if width_out is None else width_out
+    _check(lib().oracle_gather(L, H, Dh, kv_pool.dtype.itemsize, N, cap_pool, np.ascontiguousarray(kv_pool).ctypes.data,
+                               _p(_i32(tok_pool)), _p(_i32(len_pool)), _p(rows), B, G, _p(_i32(skip_group)), cap_out,
+                               kv_out.ctypes.data, _p(tok_out), _p(pos_out), _p(mask_out, C.c_int8), _p(width_out),
+                               pad_token))
+    return dict(kv=kv_out, tokens=tok_out, pos=pos_out, mask=mask_out, width=width_out[:ng])
+
+
+def append(kv_pool, tok_pool, len_pool, rows, kv_new, draft, accept_len, next_token):
+    """In-place append of each sequence's committed entries at its length (arrays are modified)."""
+    L, two, N, H, cap_pool, Dh = kv_pool.shape
+    B = kv_new.shape[2]
+    D = kv_new.shape[4] - 1
+    assert kv_pool.flags.c_contiguous and len_pool.dtype == np.int32 and len_pool.flags.c_contiguous
+    assert tok_pool is None or (tok_pool.dtype == np.int32 and tok_pool.flags.c_contiguous)
+    _check(lib().oracle_append(L, H, Dh, kv_pool.dtype.itemsize, N, cap_pool, kv_pool.ctypes.data, _p(tok_pool),
+                               _p(len_pool), _p(_i32(rows)), B, D,
+                               np.ascontiguousarray(kv_new, dtype=kv_pool.dtype).ctypes.data,
+                               _p(_i32(draft).reshape(-1)), _p(_i32(accept_len)), _p(_i32(next_token))))

@@ -1,0 +1,398 @@
+/* Reference oracle for the verify-and-resynchronize step of batch speculative
+ * decoding.  TEST INFRASTRUCTURE ONLY: plain, slow, single-threaded C that the
+ * tests, the smoke check and the benchmark's CPU-baseline leg call to decide
+ * what the GPU path must produce.  It shares no code, header or table with the
+ * GPU library and never runs on the product path.
+ *
+ * Sources (the pages this follows):
+ *  [NL]  "Inference Engineering Part 5/8: When Speculative Decoding Backfires",
+ *        sections "Draft Possible Tokens, Then Verify Them Together",
+ *        "One Verification Pass Can Commit Several Tokens",
+ *        "Exactness Means Different Things For Greedy And Sampled Output",
+ *        "Acceptance changes across the workload".
+ *  [BD]  "Batch Speculative Decoding Done Right" (technical summary), section 2.1
+ *        (synchronization invariants), 2.2 (EQSPEC unpad-append-repad),
+ *        2.3 (EXSPEC cross-batch scheduling).
+ *  [AB]  arXiv 2510.22876 abstract: invariants, contiguous layouts.
+ *
+ * Readings where the pages leave a choice open are stated at each function.
+ * Floating point: greedy compares exactly widened values; sampled acceptance
+ * and residual masses are evaluated in fp64.  Parity of every function here
+ * is pinned by the CPU tests (worked examples, closed forms, brute force). */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define EXPORT __attribute__((visibility("default")))
+
+enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2 };
+enum { O_OK = 0, O_E_ARG = -1, O_E_CAPACITY = -2, O_E_PRECOND = -3 };
+
+/* ---------------------------------------------------------------- values */
+
+static double decode_f16(uint16_t h) {
+  const int s = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(m + 1024), e - 25);
+  return s ? -v : v;
+}
+
+static double decode_bf16(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double logit_at(const void *base, int dtype, int64_t idx) {
+  if (dtype == O_F32) return (double)((const float *)base)[idx];
+  if (dtype == O_F16) return decode_f16(((const uint16_t *)base)[idx]);
+  return decode_bf16(((const uint16_t *)base)[idx]);
+}
+
+/* -------------------------------------------------- greedy verification
+ * [NL] "Exactness ...": greedy decoding picks the highest-scoring token; the
+ * target's choice is compared with each draft, matches are accepted and the
+ * first mismatch is replaced by the target's choice.  [NL] "Draft Possible
+ * Tokens ...": results are read left to right up to the first rejection; drafts
+ * after it are discarded unjudged; when all D drafts are accepted the
+ * distribution after the full draft gives one more (bonus) token, so a cycle
+ * commits 1..D+1 tokens.
+ * Readings: logit row i (0 <= i < D) verifies draft i and row D gives the
+ * bonus; ties at the maximum go to the lowest id; -0 and +0 compare equal;
+ * values are compared exactly (no temperature or softmax, which cannot change
+ * the argmax).  NaN logits are outside the contract. */
+EXPORT int oracle_verify_greedy(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                const int32_t *draft, int32_t *accept_len, int32_t *next_token,
+                                int32_t *target_tok) {
+  if (B < 0 || D < 0 || V <= 0 || row_stride < V) return O_E_ARG;
+  int32_t *t = (int32_t *)malloc(sizeof(int32_t) * (size_t)(D + 1));
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i <= D; ++i) {
+      const int64_t row = ((int64_t)b * (D + 1) + i) * row_stride;
+      int best = 0;
+      double bv = logit_at(logits, dtype, row);
+      for (int v = 1; v < V; ++v) {
+        const double x = logit_at(logits, dtype, row + v);
+        if (x > bv) { bv = x; best = v; }
+      }
+      t[i] = best;
+      if (target_tok) target_tok[(int64_t)b * (D + 1) + i] = best;
+    }
+    int a = 0;
+    while (a < D && draft[(int64_t)b * D + a] == t[a]) ++a;
+    accept_len[b] = a;
+    next_token[b] = t[a];
+  }
+  free(t);
+  return O_OK;
+}
+
+/* ------------------------------------------------- sampled verification
+ * [NL] "Exactness ...": a draft x proposed by the draft model with probability
+ * q(x) is accepted with probability min(1, p(x)/q(x)); at the first rejection
+ * the replacement is drawn from normalize(max(0, p - q)); when every draft is
+ * accepted the bonus comes from the target distribution after the full draft.
+ * Readings: the caller supplies the uniforms; draft i is accepted iff
+ * u_accept[i] <= p(x)/q(x), evaluated exactly as u*q <= p in fp64 (the product
+ * of two fp32 numbers is exact in fp64); q(x) = 0 accepts iff p(x) > 0.  The
+ * draw at stop position a uses u_draw[a]: with w the residual (a < D) or p at
+ * position D (a = D), T = sum of w in fp64 in id order, the token is the
+ * smallest id whose cumulative mass exceeds u*T; if rounding leaves none, the
+ * last id with w > 0.  If T is 0 the draw falls back to p at that position
+ * (unreachable for normalised p and q); an all-zero row yields id 0 and a
+ * return of O_E_PRECOND. */
+EXPORT int oracle_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
+                                const float *u_accept, const float *u_draw, int32_t *accept_len,
+                                int32_t *next_token, double *mass) {
+  if (B < 0 || D < 0 || V <= 0) return O_E_ARG;
+  int rc = O_OK;
+  double *w = (double *)malloc(sizeof(double) * (size_t)V);
+  for (int b = 0; b < B; ++b) {
+    int a = D;
+    for (int i = 0; i < D; ++i) {
+      const int32_t x = draft[(int64_t)b * D + i];
+      int ok = 0;
+      if (x >= 0 && x < V) {
+        const double px = p[((int64_t)b * (D + 1) + i) * V + x];
+        const double qx = q[((int64_t)b * D + i) * V + x];
+        const double u = u_accept[(int64_t)b * D + i];
+        ok = (qx > 0.0) ? (u * qx <= px) : (px > 0.0);
+      }
+      if (!ok) { a = i; break; }
+    }
+    const float *pa = p + ((int64_t)b * (D + 1) + a) * V;
+    const float *qa = (a < D) ? q + ((int64_t)b * D + a) * V : NULL;
+    double T = 0.0;
+    for (int v = 0; v < V; ++v) {
+      double d = qa ? (double)pa[v] - (double)qa[v] : (double)pa[v];
+      w[v] = d > 0.0 ? d : 0.0;
+      T += w[v];
+    }
+    if (!(T > 0.0)) {
+      T = 0.0;
+      for (int v = 0; v < V; ++v) { w[v] = pa[v] > 0.0f ? (double)pa[v] : 0.0; T += w[v]; }
+    }
+    int j = -1;
+    if (T > 0.0) {
+      const double target = (double)u_draw[(int64_t)b * (D + 1) + a] * T;
+      double c = 0.0;
+      for (int v = 0; v < V; ++v) {
+        c += w[v];
+        if (c > target) { j = v; break; }
+      }
+      if (j < 0)
+        for (int v = V - 1; v >= 0; --v)
+          if (w[v] > 0.0) { j = v; break; }
+    } else {
+      j = 0;
+      rc = O_E_PRECOND;
+    }
+    accept_len[b] = a;
+    next_token[b] = j;
+    if (mass) mass[b] = T;
+  }
+  free(w);
+  return rc;
+}
+
+/* ------------------------------------------------------------ realignment
+ * Buffers: KV [L][2][rows][H][cap][Dh] with esize-byte elements; tokens and
+ * position ids int32 [rows][cap]; mask int8 [rows][cap], 1 on content.
+ * [BD] 2.1: after each round every row has the same pad + content length
+ * (rectangular alignment) and position ids run 0,1,.. over the content as the
+ * attention mask marks it (position-id contiguity).  [BD] 2.2 EQSPEC: unpad
+ * every row, append its accepted tokens and bonus/replacement token, left-pad
+ * all rows to the longest one, recompute the position ids and shift the KV
+ * cache to match.  [NL] "Acceptance changes ...": committed KV entries are kept
+ * and speculative ones committed or discarded once acceptance is known.
+ * Readings: row b commits n = a+1 tokens (its a accepted drafts and the
+ * replacement/bonus) and keeps the first n of the D+1 speculative KV entries;
+ * the new width is the longest row (tight); pad KV entries are zero bytes, pad
+ * tokens are pad_token, pad position ids are 0; only positions [0, width) of
+ * the output are written; in and out do not overlap. */
+
+static int row_content_ok(const int8_t *mask, int S, int c) {
+  /* a left-padded row of width S with c content tokens: mask = 0^(S-c) 1^c */
+  for (int j = 0; j < S; ++j)
+    if (mask[j] != (j >= S - c)) return 0;
+  return 1;
+}
+
+static void positions_from_mask(const int8_t *mask, int W, int32_t *pos) {
+  int seen = 0;
+  for (int j = 0; j < W; ++j) {
+    if (mask[j]) { pos[j] = seen; ++seen; }
+    else pos[j] = 0;
+  }
+}
+
+EXPORT int oracle_realign_eqspec(int L, int H, int Dh, int esize, int B, int cap_in, int cap_out, int D,
+                                 const void *kv_in, void *kv_out, const void *kv_new, const int32_t *len_in,
+                                 int32_t width_in, const int32_t *tok_in, const int8_t *mask_in,
+                                 const int32_t *accept_len, const int32_t *next_token, const int32_t *draft,
+                                 int32_t pad_token, int32_t *tok_out, int32_t *pos_out, int8_t *mask_out,
+                                 int32_t *len_out, int32_t *width_out) {
+  if (L < 0 || H <= 0 || Dh <= 0 || esize <= 0 || B < 0 || D < 0 || width_in < 0 || width_in > cap_in)
+    return O_E_ARG;
+  const size_t pbytes = (size_t)Dh * (size_t)esize; /* one position of one head */
+  const int S = width_in;
+  /* step 1 (unpad) and 2 (append) on the token sequences */
+  int32_t **content = (int32_t **)calloc((size_t)(B > 0 ? B : 1), sizeof(int32_t *));
+  int *clen = (int *)calloc((size_t)(B > 0 ? B : 1), sizeof(int));
+  int rc = O_OK, Snew = 0;
+  for (int b = 0; b < B && rc == O_OK; ++b) {
+    const int c = len_in[b], a = accept_len[b];
+    if (c < 0 || c > S || a < 0 || a > D) { rc = O_E_PRECOND; break; }
+    if (mask_in && !row_content_ok(mask_in + (size_t)b * cap_in, S, c)) { rc = O_E_PRECOND; break; }
+    content[b] = (int32_t *)malloc(sizeof(int32_t) * (size_t)(c + a + 1));
+    int k = 0;
+    for (int j = S - c; j < S; ++j) content[b][k++] = tok_in[(size_t)b * cap_in + j];  /* unpad */
+    for (int i = 0; i < a; ++i) content[b][k++] = draft[(size_t)b * D + i];           /* accepted drafts */
+    content[b][k++] = next_token[b];                                                   /* replacement/bonus */
+    clen[b] = k;
+    if (k > Snew) Snew = k;
+  }
+  if (rc == O_OK && Snew > cap_out) rc = O_E_CAPACITY;
+  if (rc != O_OK) {
+    for (int b = 0; b < B; ++b) free(content[b]);
+    free(content); free(clen);
+    return rc;
+  }
+  /* step 3 (repad): left-pad to the longest row, mask, positions from the mask */
+  for (int b = 0; b < B; ++b) {
+    const int pad = Snew - clen[b];
+    int8_t *m = mask_out + (size_t)b * cap_out;
+    for (int j = 0; j < Snew; ++j) {
+      m[j] = (int8_t)(j >= pad);
+      tok_out[(size_t)b * cap_out + j] = (j >= pad) ? content[b][j - pad] : pad_token;
+    }
+    positions_from_mask(m, Snew, pos_out + (size_t)b * cap_out);
+    len_out[b] = clen[b];
+  }
+  *width_out = Snew;
+  /* the same unpad / append / repad on every (layer, K|V, head) KV sequence */
+  unsigned char *tmp = (unsigned char *)malloc(pbytes * (size_t)(cap_in + D + 1));
+  for (int l = 0; l < L; ++l)
+    for (int kv = 0; kv < 2; ++kv)
+      for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+          const size_t seg_in = ((((size_t)l * 2 + kv) * B + b) * H + h) * (size_t)cap_in * pbytes;
+          const size_t seg_out = ((((size_t)l * 2 + kv) * B + b) * H + h) * (size_t)cap_out * pbytes;
+          const size_t seg_new = ((((size_t)l * 2 + kv) * B + b) * H + h) * (size_t)(D + 1) * pbytes;
+          const int c = len_in[b], n = accept_len[b] + 1, pad = Snew - clen[b];
+          size_t k = 0;
+          for (int j = S - c; j < S; ++j, ++k)
+            memcpy(tmp + k * pbytes, (const unsigned char *)kv_in + seg_in + (size_t)j * pbytes, pbytes);
+          for (int j = 0; j < n; ++j, ++k)
+            memcpy(tmp + k * pbytes, (const unsigned char *)kv_new + seg_new + (size_t)j * pbytes, pbytes);
+          unsigned char *dst = (unsigned char *)kv_out + seg_out;
+          memset(dst, 0, (size_t)pad * pbytes);
+          memcpy(dst + (size_t)pad * pbytes, tmp, k * pbytes);
+        }
+  free(tmp);
+  for (int b = 0; b < B; ++b) free(content[b]);
+  free(content); free(clen);
+  return O_OK;
+}
+
+/* ------------------------------------------------------- EXSPEC grouping
+ * [BD] 2.3: keep a pool of active sequences rather than a fixed batch, group
+ * sequences of equal length into batches, which then need no realignment, and
+ * realign only mixed-length batches.
+ * Reading (one admissible policy, fixed so results are comparable): order the
+ * ids by (length, id); for each length in ascending order emit floor(cnt/G)
+ * full batches of that length; then chunk the remaining ids, still in (length,
+ * id) order, into batches of G (the last may be short).  For every batch:
+ * uniform = all its lengths equal, width = its longest length.  n_uniform is
+ * the number of uniform batches. */
+static const int32_t *g_len_for_sort;
+static int cmp_len_id(const void *x, const void *y) {
+  const int32_t i = *(const int32_t *)x, j = *(const int32_t *)y;
+  if (g_len_for_sort[i] != g_len_for_sort[j]) return g_len_for_sort[i] < g_len_for_sort[j] ? -1 : 1;
+  return (i > j) - (i < j);
+}
+
+EXPORT int oracle_group_by_len(const int32_t *len, int N, int G, int32_t *order, int32_t *uniform,
+                               int32_t *width, int32_t *n_uniform) {
+  if (N < 0 || G <= 0) return O_E_ARG;
+  int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+  for (int i = 0; i < N; ++i) ids[i] = i;
+  g_len_for_sort = len;
+  qsort(ids, (size_t)N, sizeof(int32_t), cmp_len_id);
+  int out = 0;
+  int32_t *left = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+  int nleft = 0;
+  for (int s = 0; s < N;) {
+    int e = s;
+    while (e < N && len[ids[e]] == len[ids[s]]) ++e;
+    const int full = ((e - s) / G) * G;
+    for (int k = s; k < s + full; ++k) order[out++] = ids[k];
+    for (int k = s + full; k < e; ++k) left[nleft++] = ids[k];
+    s = e;
+  }
+  for (int k = 0; k < nleft; ++k) order[out++] = left[k];
+  const int nb = (N + G - 1) / G;
+  int nu = 0;
+  for (int g = 0; g < nb; ++g) {
+    const int lo = g * G, hi = (lo + G < N) ? lo + G : N;
+    int mn = len[order[lo]], mx = len[order[lo]];
+    for (int k = lo; k < hi; ++k) {
+      if (len[order[k]] < mn) mn = len[order[k]];
+      if (len[order[k]] > mx) mx = len[order[k]];
+    }
+    uniform[g] = (mn == mx);
+    width[g] = mx;
+    nu += (mn == mx);
+  }
+  *n_uniform = nu;
+  free(ids);
+  free(left);
+  return O_OK;
+}
+
+/* ----------------------------------------------- EXSPEC gather / append
+ * Reading of [BD] 2.3 for storage: pool rows hold their content left-aligned
+ * from position 0 with no padding, so a same-length batch is already
+ * rectangular with position ids 0..len-1 and is not copied.  A mixed batch is
+ * realigned into a left-padded rectangle of width = its longest row (the same
+ * repad as EQSPEC, without an append).  After verification every sequence
+ * appends its committed tokens and KV entries in place at its length. */
+EXPORT int oracle_gather(int L, int H, int Dh, int esize, int N, int cap_pool, const void *kv_pool,
+                         const int32_t *tok_pool, const int32_t *len_pool, const int32_t *rows, int B, int G,
+                         const int32_t *skip_group, int cap_out, void *kv_out, int32_t *tok_out, int32_t *pos_out,
+                         int8_t *mask_out, int32_t *width_out, int32_t pad_token) {
+  if (L < 0 || H <= 0 || Dh <= 0 || esize <= 0 || B < 0 || G <= 0) return O_E_ARG;
+  const size_t pbytes = (size_t)Dh * (size_t)esize;
+  const int ng = (B + G - 1) / G;
+  for (int g = 0; g < ng; ++g) {
+    if (skip_group && skip_group[g]) continue;
+    const int lo = g * G, hi = (lo + G < B) ? lo + G : B;
+    int W = 0;
+    for (int j = lo; j < hi; ++j) {
+      const int r = rows ? rows[j] : j;
+      if (r < 0 || r >= N || len_pool[r] < 0 || len_pool[r] > cap_pool) return O_E_PRECOND;
+      if (len_pool[r] > W) W = len_pool[r];
+    }
+    if (W > cap_out) return O_E_CAPACITY;
+    width_out[g] = W;
+    for (int j = lo; j < hi; ++j) {
+      const int r = rows ? rows[j] : j, c = len_pool[r], pad = W - c;
+      int8_t *m = mask_out + (size_t)j * cap_out;
+      for (int x = 0; x < W; ++x) {
+        m[x] = (int8_t)(x >= pad);
+        tok_out[(size_t)j * cap_out + x] = (x >= pad) ? tok_pool[(size_t)r * cap_pool + (x - pad)] : pad_token;
+      }
+      positions_from_mask(m, W, pos_out + (size_t)j * cap_out);
+      for (int l = 0; l < L; ++l)
+        for (int kv = 0; kv < 2; ++kv)
+          for (int h = 0; h < H; ++h) {
+            const unsigned char *src = (const unsigned char *)kv_pool +
+                                       ((((size_t)l * 2 + kv) * N + r) * H + h) * (size_t)cap_pool * pbytes;
+            unsigned char *dst = (unsigned char *)kv_out +
+                                 ((((size_t)l * 2 + kv) * B + j) * H + h) * (size_t)cap_out * pbytes;
+            memset(dst, 0, (size_t)pad * pbytes);
+            memcpy(dst + (size_t)pad * pbytes, src, (size_t)c * pbytes);
+          }
+    }
+  }
+  return O_OK;
+}
+
+EXPORT int oracle_append(int L, int H, int Dh, int esize, int N, int cap_pool, void *kv_pool, int32_t *tok_pool,
+                         int32_t *len_pool, const int32_t *rows, int B, int D, const void *kv_new,
+                         const int32_t *draft, const int32_t *accept_len, const int32_t *next_token) {
+  if (L < 0 || H <= 0 || Dh <= 0 || esize <= 0 || B < 0 || D < 0) return O_E_ARG;
+  const size_t pbytes = (size_t)Dh * (size_t)esize;
+  unsigned char *seen = (unsigned char *)calloc((size_t)(N > 0 ? N : 1), 1);
+  int rc = O_OK;
+  for (int b = 0; b < B && rc == O_OK; ++b) {
+    const int r = rows ? rows[b] : b;
+    if (r < 0 || r >= N || seen[r] || accept_len[b] < 0 || accept_len[b] > D || len_pool[r] < 0) rc = O_E_PRECOND;
+    else if (len_pool[r] + accept_len[b] + 1 > cap_pool) rc = O_E_CAPACITY;
+    else seen[r] = 1;
+  }
+  free(seen);
+  if (rc != O_OK) return rc;
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = len_pool[r], a = accept_len[b], n = a + 1;
+    if (tok_pool) {
+      for (int i = 0; i < a; ++i) tok_pool[(size_t)r * cap_pool + c + i] = draft[(size_t)b * D + i];
+      tok_pool[(size_t)r * cap_pool + c + a] = next_token[b];
+    }
+    for (int l = 0; l < L; ++l)
+      for (int kv = 0; kv < 2; ++kv)
+        for (int h = 0; h < H; ++h) {
+          unsigned char *dst = (unsigned char *)kv_pool +
+                               ((((size_t)l * 2 + kv) * N + r) * H + h) * (size_t)cap_pool * pbytes;
+          const unsigned char *src = (const unsigned char *)kv_new +
+                                     ((((size_t)l * 2 + kv) * B + b) * H + h) * (size_t)(D + 1) * pbytes;
+          memcpy(dst + (size_t)c * pbytes, src, (size_t)n * pbytes);
+        }
+    len_pool[r] = c + n;
+  }
+  return O_OK;
+}

@@ -1,0 +1,38 @@
+"""Build the seeded input generator: a host library (gcc, OpenMP) and a device
+library (hipcc for gfx950).  Both compile gen_core.h, the one definition of
+every generated value."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HOST_LIB = os.path.join(HERE, "libsynth_host.so")
+DEV_LIB = os.path.join(HERE, "libsynth_dev.so")
+
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+
+
+def build_host():
+    _run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-fvisibility=hidden", "-o", HOST_LIB + ".tmp",
+          "gen_host.c"])
+    os.replace(HOST_LIB + ".tmp", HOST_LIB)
+
+
+def build_device():
+    _run(["/opt/rocm/bin/hipcc", *HIP_FLAGS, "-o", DEV_LIB + ".tmp", "gen_device.hip"])
+    os.replace(DEV_LIB + ".tmp", DEV_LIB)
+
+
+def build():
+    build_host()
+    build_device()
+
+
+if __name__ == "__main__":
+    build()
