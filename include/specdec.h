@@ -1,0 +1,224 @@
+/* specdec.h - C ABI of the verify-and-resynchronize step of batch speculative
+ * decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One round of batched speculative decoding, as the pages define it:
+ *   1. verification: the target model has scored D+1 positions of every row in
+ *      one pass; each row keeps its drafts up to the first rejection and adds a
+ *      replacement token, or a bonus token when all D drafts are accepted, so it
+ *      commits between 1 and D+1 tokens ("Inference Engineering Part 5/8: When
+ *      Speculative Decoding Backfires", sections "Draft Possible Tokens, Then
+ *      Verify Them Together" and "Exactness Means Different Things For Greedy
+ *      And Sampled Output");
+ *   2. resynchronisation: rows that committed different counts no longer line
+ *      up; EQSPEC unpads every row, appends its committed tokens and repads all
+ *      rows on the left to the longest, recomputing position ids and shifting the
+ *      KV cache, so that rectangular alignment and position-id contiguity hold
+ *      again ("Batch Speculative Decoding Done Right", sections 2.1 and 2.2);
+ *   3. EXSPEC scheduling: a pool of sequences is grouped by equal length so
+ *      same-length batches need no realignment and only mixed batches are
+ *      realigned (same page, section 2.3).
+ *
+ * Conventions for every entry point:
+ *  - Pointers documented as "device" are device memory of the current HIP
+ *    device; structs and scalars are host memory read during the call only.
+ *  - The library allocates nothing, frees nothing and keeps no state between
+ *    calls; all work is enqueued on `stream` (a hipStream_t passed as void*,
+ *    NULL = the null stream).  Outputs are valid once the stream is
+ *    synchronised.
+ *  - Host-detected errors (the SPECDEC_E_* codes) are returned synchronously and
+ *    nothing is enqueued.
+ *  - Conditions only the device can see set bits of the optional device word
+ *    `status` (SPECDEC_S_*, OR-ed in, never cleared by the library).  A call
+ *    that sets CAPACITY or LEN_RANGE writes none of its outputs.
+ *  - Results are deterministic: identical inputs give identical bytes.
+ *  - Calls on different streams must not share output buffers or workspaces.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of logits and KV entries */
+#define SPECDEC_F32 0
+#define SPECDEC_F16 1
+#define SPECDEC_BF16 2
+
+/* host return codes */
+#define SPECDEC_OK 0
+#define SPECDEC_E_ARG (-1)       /* NULL pointer, size out of range, inconsistent shapes */
+#define SPECDEC_E_DTYPE (-2)     /* element type not one of SPECDEC_F32/F16/BF16 */
+#define SPECDEC_E_WORKSPACE (-3) /* workspace NULL or smaller than specdec_workspace_bytes() */
+#define SPECDEC_E_ALIAS (-4)     /* an output overlaps an input it must not overlap */
+#define SPECDEC_E_ALIGN (-5)     /* a KV position (head_dim * element size) is not a multiple of 16 bytes,
+                                    or a KV/kv_new base pointer is not 16-byte aligned */
+#define SPECDEC_E_LAUNCH (-6)    /* the HIP runtime refused a launch */
+
+/* device status bits */
+#define SPECDEC_S_DRAFT_RANGE 1  /* a draft id outside [0, V) (it never matches; results still written) */
+#define SPECDEC_S_CAPACITY 2     /* a row would grow past its buffer's cap: nothing written */
+#define SPECDEC_S_LEN_RANGE 4    /* a length outside [0, width] / [0, cap], an accepted length outside
+                                    [0, D] or a row id outside the pool: nothing written */
+#define SPECDEC_S_PROB 8         /* sampled verification met a position whose probabilities are all 0 */
+#define SPECDEC_S_ROWS_DUP 16    /* append: the same pool row listed twice (result undefined) */
+
+/* Library version string, e.g. "specdec 0.1 gfx950". */
+const char *specdec_version(void);
+
+/* ------------------------------------------------------------------ verify */
+
+/* Bytes of the workspace specdec_verify_greedy needs for B rows and D drafts. */
+size_t specdec_workspace_bytes(int B, int D);
+
+/* Clears a workspace (device memory, ws_bytes >= specdec_workspace_bytes) once,
+ * before its first use.  specdec_verify_greedy leaves it cleared again when it
+ * completes, so the same workspace serves any number of later calls on one
+ * stream. */
+int specdec_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Greedy verification ("Inference Engineering Part 5/8", sections "Draft
+ * Possible Tokens, Then Verify Them Together", "One Verification Pass Can
+ * Commit Several Tokens" and, for greedy exactness, "Exactness Means Different
+ * Things For Greedy And Sampled Output").
+ *
+ *  logits      device, element type `dtype`, rows (b, i) for b < B, i <= D at
+ *              logits + (b*(D+1) + i) * row_stride elements; V entries per row.
+ *              Row i < D scores draft i; row D gives the bonus token.
+ *  row_stride  elements between consecutive rows, >= V.
+ *  draft       device int32 [B][D].
+ *  accept_len  device int32 [B] out: number of leading drafts equal to the
+ *              target's choice, in [0, D].
+ *  next_token  device int32 [B] out: the target's choice at position
+ *              accept_len (the replacement, or the bonus when accept_len = D).
+ *  target_tok  device int32 [B][D+1] out, nullable: the target's choice at
+ *              every position.
+ *  ws          device workspace, cleared once by specdec_workspace_init.
+ *  status      device int32, nullable (SPECDEC_S_DRAFT_RANGE).
+ * The target's choice is the id of the largest logit, the lowest such id on
+ * ties; -0.0 and +0.0 are equal; NaN logits are outside the contract.
+ * B = 0 is a no-op.  Errors: E_ARG (B < 0, D < 0, V < 1, row_stride < V, NULL
+ * logits/draft/outputs), E_DTYPE, E_WORKSPACE, E_LAUNCH. */
+int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                          const int32_t *draft, int32_t *accept_len, int32_t *next_token,
+                          int32_t *target_tok, void *ws, size_t ws_bytes, int32_t *status, void *stream);
+
+/* Sampled verification (speculative sampling; "Inference Engineering Part
+ * 5/8", section "Exactness Means Different Things For Greedy And Sampled
+ * Output": accept with probability min(1, p(x)/q(x)), replace from
+ * normalize(max(0, p - q)), bonus from the target distribution after the full
+ * draft).
+ *
+ *  p           device fp32 [B][D+1][V]: target probabilities at each position.
+ *  q           device fp32 [B][D][V]: draft probabilities of each draft position.
+ *  draft       device int32 [B][D].
+ *  u_accept    device fp32 [B][D], uniforms in [0, 1): draft i is accepted iff
+ *              u_accept[i] * q(x) <= p(x), evaluated exactly (fp64 product of
+ *              fp32 values); q(x) = 0 accepts iff p(x) > 0.  A draft id outside
+ *              [0, V) is rejected and sets SPECDEC_S_DRAFT_RANGE.
+ *  u_draw      device fp32 [B][D+1]: u_draw[a] draws the token at stop position a
+ *              by inverse CDF: w = max(0, p - q) at a < D, or p at a = D, summed
+ *              in fp64; the token is the smallest id whose cumulative mass
+ *              exceeds u * sum(w).  A zero sum falls back to p; an all-zero row
+ *              gives id 0 and SPECDEC_S_PROB.
+ *  accept_len, next_token  device int32 [B] out, as for greedy verification.
+ * B = 0 is a no-op.  Errors: E_ARG, E_LAUNCH. */
+int specdec_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
+                          const float *u_accept, const float *u_draw, int32_t *accept_len,
+                          int32_t *next_token, int32_t *status, void *stream);
+
+/* --------------------------------------------------------------- realign */
+
+/* A set of sequences with a contiguous KV cache.
+ *  kv        device [layers][2 (K, V)][rows][heads][cap][head_dim] of `dtype`;
+ *            each (layer, K|V, row, head) sequence of cap positions is
+ *            contiguous, one position = head_dim elements.
+ *  tokens    device int32 [rows][cap] token ids.
+ *  pos       device int32 [rows][cap] position ids (nullable for a pool).
+ *  mask      device int8 [rows][cap] attention mask, 1 = content (nullable for
+ *            a pool).
+ *  len       device int32 [rows] content length of each row.
+ *  width     device int32: [1] the rectangle width of a left-padded batch, or
+ *            [groups] one width per rectangle of a GATHER output (NULL for a
+ *            pool).
+ * A left-padded rectangle of width S holds row b's content at positions
+ * [S - len[b], S); a pool holds it at [0, len[b]). */
+typedef struct {
+  void *kv;
+  int32_t *tokens;
+  int32_t *pos;
+  int8_t *mask;
+  int32_t *len;
+  int32_t *width;
+  int32_t rows, cap, layers, heads, head_dim;
+  int32_t dtype;
+} specdec_seqbuf_t;
+
+#define SPECDEC_EQSPEC 0         /* rectangle -> rectangle: unpad, append, repad (out of place) */
+#define SPECDEC_GATHER 1         /* pool rows -> one left-padded rectangle per group (no append) */
+#define SPECDEC_APPEND_INPLACE 2 /* pool rows: append committed entries at each row's length */
+
+/* Realignment ("Batch Speculative Decoding Done Right", sections 2.1-2.3;
+ * committed and discarded speculative KV: "Inference Engineering Part 5/8",
+ * section "Acceptance changes across the workload").
+ *
+ * Row b commits n_b = accept_len[b] + 1 tokens: draft[b][0 .. accept_len-1]
+ * then next_token[b], with the first n_b of its D+1 speculative KV entries
+ * kv_new [layers][2][B][heads][D+1][head_dim] (device, same type as the cache).
+ *
+ * SPECDEC_EQSPEC: `in` is a left-padded rectangle of B = in->rows rows and
+ *   width in->width[0]; `out` receives the rectangle of width
+ *   S' = max_b(len[b] + n_b): row b's old content, then its committed entries,
+ *   left-padded with zero KV bytes, pad_token, position id 0 and mask 0.
+ *   Position ids are 0..len-1 over the content.  out->len and out->width[0] are
+ *   written; positions [S', cap) of `out` are not touched.  in and out must
+ *   not overlap (E_ALIAS).  rows / group / skip_group are unused (NULL / 0).
+ * SPECDEC_GATHER: `in` is a pool; rows[j] (NULL = j) names the pool row of
+ *   batch entry j < B; entries form groups of `group` consecutive entries.
+ *   Every group whose skip_group[g] is 0 (skip_group NULL = none skipped) is
+ *   written to `out` (a rectangle buffer with out->rows >= B) as a left-padded
+ *   rectangle of width W_g = its longest row: out row j gets pool row rows[j]'s
+ *   content and tokens, with mask, position ids, out->len[j] and
+ *   out->width[g].  Skipped groups are not touched.  D, kv_new, draft,
+ *   accept_len, next_token are unused.
+ * SPECDEC_APPEND_INPLACE: `in` and `out` describe the same pool (same kv,
+ *   tokens, len); batch entry b < B (pool row rows[b], NULL = b) appends its
+ *   committed entries and tokens at its length, and its length grows by n_b.
+ *   Rows must be distinct (else SPECDEC_S_ROWS_DUP and an undefined result).
+ * Limits: B <= 1024; head_dim * element size a multiple of 16 bytes; KV
+ * pointers 16-byte aligned (E_ALIGN).  Device conditions: S' > out cap,
+ * W_g > out cap or len + n_b > cap set SPECDEC_S_CAPACITY; lengths outside
+ * [0, width] (EQSPEC) or [0, cap], accepted lengths outside [0, D] or rows
+ * outside the pool set SPECDEC_S_LEN_RANGE; either way nothing is written.
+ * Errors: E_ARG, E_DTYPE, E_ALIAS, E_ALIGN, E_LAUNCH. */
+int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbuf_t *out,
+                       const int32_t *rows, int B, int group, const int32_t *skip_group, int D,
+                       const void *kv_new, const int32_t *draft, const int32_t *accept_len,
+                       const int32_t *next_token, int32_t pad_token, int32_t *status, void *stream);
+
+/* Equal-length grouping of a sequence pool ("Batch Speculative Decoding Done
+ * Right", section 2.3: batches of same-length sequences need no realignment).
+ *
+ *  len        device int32 [N] content lengths, N <= 4096.
+ *  group      rows per batch (>= 1).
+ *  order      device int32 [N] out: pool ids in batch-major order.  Ids are
+ *             ranked by (length, id); for each length in ascending order the
+ *             first floor(count / group) * group ids form full same-length
+ *             batches, listed first; the remaining ids follow in (length, id)
+ *             order and are cut into batches of `group` (the last may be short).
+ *  uniform    device int32 [ceil(N / group)] out: 1 if every length in the
+ *             batch is equal (such a batch needs no realignment).
+ *  width      device int32 [ceil(N / group)] out: longest length in the batch.
+ *  n_uniform  device int32 [1] out: number of uniform batches.
+ * Errors: E_ARG (N < 0, N > 4096, group < 1, NULL outputs), E_LAUNCH. */
+int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, int32_t *uniform,
+                         int32_t *width, int32_t *n_uniform, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

@@ -1,0 +1,216 @@
+// C ABI of libspecdec: host-side validation, then one stream-ordered launch
+// per step.  Declarations and the contract of every entry point are in
+// include/specdec.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+#include "specdec.h"
+
+#define EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxRealignB = 1024;
+constexpr int kMaxPool = 4096;
+
+size_t esize(int dtype) { return dtype == SPECDEC_F32 ? 4 : 2; }
+bool dtype_ok(int dtype) { return dtype == SPECDEC_F32 || dtype == SPECDEC_F16 || dtype == SPECDEC_BF16; }
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+int launched(hipError_t e) { return e == hipSuccess ? SPECDEC_OK : SPECDEC_E_LAUNCH; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t kv_bytes(const specdec_seqbuf_t *s) {
+  return (size_t)s->layers * 2 * (size_t)s->rows * (size_t)s->heads * (size_t)s->cap * (size_t)s->head_dim *
+         esize(s->dtype);
+}
+
+size_t ws_keys_bytes(int B, int D) { return ((size_t)B * (size_t)(D + 1) * 8 + 255) / 256 * 256; }
+
+int check_seqbuf_shape(const specdec_seqbuf_t *s) {
+  if (!s || !s->kv || !s->len) return SPECDEC_E_ARG;
+  if (s->rows < 0 || s->cap < 0 || s->layers < 0 || s->heads < 1 || s->head_dim < 1) return SPECDEC_E_ARG;
+  if (!dtype_ok(s->dtype)) return SPECDEC_E_DTYPE;
+  if (((size_t)s->head_dim * esize(s->dtype)) % 16 != 0) return SPECDEC_E_ALIGN;
+  if (reinterpret_cast<uintptr_t>(s->kv) % 16 != 0) return SPECDEC_E_ALIGN;
+  return SPECDEC_OK;
+}
+
+bool same_geometry(const specdec_seqbuf_t *a, const specdec_seqbuf_t *b) {
+  return a->layers == b->layers && a->heads == b->heads && a->head_dim == b->head_dim && a->dtype == b->dtype;
+}
+
+}  // namespace
+
+EXPORT const char *specdec_version(void) { return "specdec 0.1 gfx950"; }
+
+EXPORT size_t specdec_workspace_bytes(int B, int D) {
+  if (B < 0 || D < 0) return 0;
+  return ws_keys_bytes(B, D) + ((size_t)B * 4 + 255) / 256 * 256;
+}
+
+EXPORT int specdec_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+  if (!ws) return SPECDEC_E_WORKSPACE;
+  return launched(sd::launch_zero(ws, ws_bytes / 4 * 4, as_stream(stream)));
+}
+
+EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                 const int32_t *draft, int32_t *accept_len, int32_t *next_token,
+                                 int32_t *target_tok, void *ws, size_t ws_bytes, int32_t *status, void *stream) {
+  if (B < 0 || D < 0 || V < 1 || row_stride < V) return SPECDEC_E_ARG;
+  if (!dtype_ok(dtype)) return SPECDEC_E_DTYPE;
+  if (B == 0) return SPECDEC_OK;
+  if (!logits || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+  if ((long long)B * (D + 1) > (1LL << 24) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  if (!ws || ws_bytes < specdec_workspace_bytes(B, D) || reinterpret_cast<uintptr_t>(ws) % 8 != 0)
+    return SPECDEC_E_WORKSPACE;
+  sd::GreedyParams p;
+  p.logits = logits;
+  p.dtype = dtype;
+  p.row_stride = row_stride;
+  p.B = B;
+  p.D = D;
+  p.V = V;
+  p.draft = draft;
+  p.accept_len = accept_len;
+  p.next_token = next_token;
+  p.target_tok = target_tok;
+  p.keys = static_cast<unsigned long long *>(ws);
+  p.counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D));
+  p.status = status;
+  p.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
+  return launched(sd::launch_verify_greedy(p, as_stream(stream)));
+}
+
+EXPORT int specdec_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
+                                 const float *u_accept, const float *u_draw, int32_t *accept_len,
+                                 int32_t *next_token, int32_t *status, void *stream) {
+  if (B < 0 || D < 0 || V < 1) return SPECDEC_E_ARG;
+  if (B == 0) return SPECDEC_OK;
+  if (!p || !u_draw || !accept_len || !next_token || (D > 0 && (!q || !draft || !u_accept))) return SPECDEC_E_ARG;
+  if ((long long)B > (1LL << 30) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  sd::SampleParams s;
+  s.p = p;
+  s.q = q;
+  s.B = B;
+  s.D = D;
+  s.V = V;
+  s.draft = draft;
+  s.u_accept = u_accept;
+  s.u_draw = u_draw;
+  s.accept_len = accept_len;
+  s.next_token = next_token;
+  s.status = status;
+  return launched(sd::launch_verify_sample(s, as_stream(stream)));
+}
+
+EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbuf_t *out,
+                              const int32_t *rows, int B, int group, const int32_t *skip_group, int D,
+                              const void *kv_new, const int32_t *draft, const int32_t *accept_len,
+                              const int32_t *next_token, int32_t pad_token, int32_t *status, void *stream) {
+  if (mode != SPECDEC_EQSPEC && mode != SPECDEC_GATHER && mode != SPECDEC_APPEND_INPLACE) return SPECDEC_E_ARG;
+  if (B < 0 || B > kMaxRealignB || D < 0) return SPECDEC_E_ARG;
+  int rc = check_seqbuf_shape(in);
+  if (rc) return rc;
+  rc = check_seqbuf_shape(out);
+  if (rc) return rc;
+  if (!same_geometry(in, out)) return SPECDEC_E_ARG;
+  const int units = (int)((size_t)in->head_dim * esize(in->dtype) / 16);
+  if (units > 256) return SPECDEC_E_ARG;
+
+  sd::RealignParams p;
+  memset(&p, 0, sizeof(p));
+  p.mode = mode;
+  p.kv_in = in->kv;
+  p.kv_out = out->kv;
+  p.kv_new = kv_new;
+  p.layers = in->layers;
+  p.heads = in->heads;
+  p.units = units;
+  p.rows_in = in->rows;
+  p.cap_in = in->cap;
+  p.rows_out = out->rows;
+  p.cap_out = out->cap;
+  p.B = B;
+  p.group = group;
+  p.D = D;
+  p.draft = draft;
+  p.accept_len = accept_len;
+  p.next_token = next_token;
+  p.pad_token = pad_token;
+  p.status = status;
+  p.rows = rows;
+  p.skip_group = skip_group;
+
+  const size_t tok_in_bytes = (size_t)in->rows * in->cap * 4, tok_out_bytes = (size_t)out->rows * out->cap * 4;
+  if (mode == SPECDEC_EQSPEC) {
+    if (in->rows != B || out->rows != B) return SPECDEC_E_ARG;
+    if (!in->tokens || !in->width || !out->tokens || !out->pos || !out->mask || !out->width) return SPECDEC_E_ARG;
+    if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+    if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
+    if (B == 0) return SPECDEC_OK;
+    const size_t kin = kv_bytes(in), kout = kv_bytes(out);
+    const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
+    if (overlap(in->kv, kin, out->kv, kout) || overlap(kv_new, knew, out->kv, kout)) return SPECDEC_E_ALIAS;
+    if (overlap(in->tokens, tok_in_bytes, out->tokens, tok_out_bytes) || overlap(in->len, B * 4u, out->len, B * 4u) ||
+        overlap(in->width, 4, out->width, 4) || overlap(accept_len, B * 4u, out->len, B * 4u))
+      return SPECDEC_E_ALIAS;
+    p.tok_in = in->tokens;
+    p.len_in = in->len;
+    p.width_in = in->width;
+    p.tok_out = out->tokens;
+    p.pos_out = out->pos;
+    p.mask_out = out->mask;
+    p.len_out = out->len;
+    p.width_out = out->width;
+  } else if (mode == SPECDEC_GATHER) {
+    if (group < 1) return SPECDEC_E_ARG;
+    if (out->rows < B) return SPECDEC_E_ARG;
+    if (B == 0) return SPECDEC_OK;
+    if (overlap(in->kv, kv_bytes(in), out->kv, kv_bytes(out))) return SPECDEC_E_ALIAS;
+    if (overlap(in->tokens, tok_in_bytes, out->tokens, tok_out_bytes)) return SPECDEC_E_ALIAS;
+    p.tok_in = in->tokens;
+    p.len_in = in->len;
+    p.tok_out = out->tokens;
+    p.pos_out = out->pos;
+    p.mask_out = out->mask;
+    p.len_out = out->len;
+    p.width_out = out->width;
+  } else {
+    if (in->kv != out->kv || in->len != out->len || in->tokens != out->tokens || in->rows != out->rows ||
+        in->cap != out->cap)
+      return SPECDEC_E_ARG;
+    if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+    if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
+    if (B == 0) return SPECDEC_OK;
+    const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
+    if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
+    p.tok_in = in->tokens;
+    p.len_in = in->len;
+    p.tok_out = out->tokens;
+    p.len_out = out->len;
+  }
+  return launched(sd::launch_realign(p, as_stream(stream)));
+}
+
+EXPORT int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, int32_t *uniform,
+                                int32_t *width, int32_t *n_uniform, void *stream) {
+  if (N < 0 || N > kMaxPool || group < 1) return SPECDEC_E_ARG;
+  if (!n_uniform) return SPECDEC_E_ARG;
+  if (N > 0 && (!len || !order || !uniform || !width)) return SPECDEC_E_ARG;
+  sd::GroupParams p;
+  p.len = len;
+  p.N = N;
+  p.group = group;
+  p.order = order;
+  p.uniform = uniform;
+  p.width = width;
+  p.n_uniform = n_uniform;
+  return launched(sd::launch_group_by_len(p, as_stream(stream)));
+}

@@ -1,0 +1,61 @@
+// Kernel launchers called by the C ABI layer after host-side validation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sd {
+
+struct GreedyParams {
+  const void *logits;
+  int dtype;
+  int64_t row_stride;
+  int B, D, V;
+  const int32_t *draft;
+  int32_t *accept_len, *next_token, *target_tok;
+  unsigned long long *keys;   // [B*(D+1)] workspace
+  unsigned int *counters;     // [B] workspace
+  int32_t *status;
+  bool vec;                   // 16-byte aligned rows: vector loads
+};
+
+struct SampleParams {
+  const float *p, *q;
+  int B, D, V;
+  const int32_t *draft;
+  const float *u_accept, *u_draw;
+  int32_t *accept_len, *next_token, *status;
+};
+
+struct RealignParams {
+  int mode;
+  // source / destination KV in 16-byte units
+  const void *kv_in;
+  void *kv_out;
+  const void *kv_new;
+  int layers, heads, units;   // units = 16-byte units per position (head_dim * esize / 16)
+  int rows_in, cap_in, rows_out, cap_out;
+  const int32_t *tok_in, *len_in, *width_in;
+  int32_t *tok_out, *pos_out, *len_out, *width_out;
+  int8_t *mask_out;
+  const int32_t *rows;        // GATHER / APPEND row map, nullable
+  int B, group, D;
+  const int32_t *skip_group;
+  const int32_t *draft, *accept_len, *next_token;
+  int32_t pad_token;
+  int32_t *status;
+};
+
+struct GroupParams {
+  const int32_t *len;
+  int N, group;
+  int32_t *order, *uniform, *width, *n_uniform;
+};
+
+int device_cus();
+hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s);
+hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s);
+hipError_t launch_realign(const RealignParams &p, hipStream_t s);
+hipError_t launch_group_by_len(const GroupParams &p, hipStream_t s);
+hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
+
+}  // namespace sd

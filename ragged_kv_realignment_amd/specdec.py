@@ -1,0 +1,280 @@
+"""Python binding of libspecdec (include/specdec.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+their device pointers and torch's current HIP stream are handed to the C ABI,
+and every step runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, calls raise.
+"""
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecdec.so")
+
+F32, F16, BF16 = 0, 1, 2
+EQSPEC, GATHER, APPEND_INPLACE = 0, 1, 2
+OK, E_ARG, E_DTYPE, E_WORKSPACE, E_ALIAS, E_ALIGN, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+S_DRAFT_RANGE, S_CAPACITY, S_LEN_RANGE, S_PROB, S_ROWS_DUP = 1, 2, 4, 8, 16
+
+_ERRORS = {E_ARG: "invalid argument", E_DTYPE: "unsupported element type", E_WORKSPACE: "workspace too small",
+           E_ALIAS: "output overlaps an input", E_ALIGN: "misaligned KV buffer", E_LAUNCH: "kernel launch failed"}
+_TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init", "specdec_verify_greedy",
+           "specdec_verify_sample", "specdec_realign_kv", "specdec_group_by_len")
+
+
+class SpecDecError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__("%s: %s (code %d)" % (where, _ERRORS.get(code, "error"), code))
+        self.code = code
+
+
+class SeqBufC(C.Structure):
+    _fields_ = [("kv", C.c_void_p), ("tokens", C.c_void_p), ("pos", C.c_void_p), ("mask", C.c_void_p),
+                ("len", C.c_void_p), ("width", C.c_void_p), ("rows", C.c_int32), ("cap", C.c_int32),
+                ("layers", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libspecdec.so is not built (run __graft_entry__.build()); there is no fallback")
+        L = C.CDLL(LIB_PATH)
+        vp, ci, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+        L.specdec_version.restype = C.c_char_p
+        L.specdec_workspace_bytes.argtypes = [ci, ci]
+        L.specdec_workspace_bytes.restype = sz
+        L.specdec_workspace_init.argtypes = [vp, sz, vp]
+        L.specdec_verify_greedy.argtypes = [vp, ci, i64, ci, ci, ci, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.specdec_verify_sample.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.specdec_realign_kv.argtypes = [ci, C.POINTER(SeqBufC), C.POINTER(SeqBufC), vp, ci, ci, vp, ci, vp, vp,
+                                         vp, vp, C.c_int32, vp, vp]
+        L.specdec_group_by_len.argtypes = [vp, ci, ci, vp, vp, vp, vp, vp]
+        for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample", "specdec_realign_kv",
+                  "specdec_group_by_len"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, cuda=True):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if cuda and not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _check(rc, where):
+    if rc != OK:
+        raise SpecDecError(rc, where)
+
+
+def specdec_version():
+    return lib().specdec_version().decode()
+
+
+def workspace(B, D, device="cuda"):
+    """A cleared verification workspace for B rows and D drafts."""
+    n = int(lib().specdec_workspace_bytes(B, D))
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    _check(lib().specdec_workspace_init(ws.data_ptr(), ws.numel(), _stream()), "specdec_workspace_init")
+    return ws
+
+
+def _i32(shape, device):
+    return torch.empty(shape, dtype=torch.int32, device=device)
+
+
+def specdec_verify_greedy(logits, draft, ws=None, status=None, accept_len=None, next_token=None, target_tok=None):
+    """Greedy verification of drafts [B, D] against logits [B, D+1, V].
+
+    Rows of `logits` may be strided (last dim contiguous, a uniform stride
+    between the B*(D+1) rows).  Returns (accept_len [B], next_token [B]).
+    """
+    if logits.dtype not in _TORCH_DT or not logits.is_cuda or logits.dim() != 3:
+        raise ValueError("logits must be a [B, D+1, V] float32/float16/bfloat16 device tensor")
+    B, D1, V = logits.shape
+    D = D1 - 1
+    if logits.stride(2) != 1:
+        raise ValueError("logits must have a contiguous last dimension")
+    if D1 == 1:
+        row_stride = logits.stride(0)
+    else:
+        row_stride = logits.stride(1)
+        if B > 1 and logits.stride(0) != D1 * row_stride:
+            raise ValueError("logits rows must share one stride")
+    _need(draft, "draft", torch.int32)
+    if tuple(draft.shape) != (B, D):
+        raise ValueError("draft must be [B, D]")
+    dev = logits.device
+    ws = workspace(B, D, dev) if ws is None else ws
+    accept_len = _i32(B, dev) if accept_len is None else accept_len
+    next_token = _i32(B, dev) if next_token is None else next_token
+    rc = lib().specdec_verify_greedy(logits.data_ptr(), _TORCH_DT[logits.dtype], row_stride, B, D, V, _ptr(draft),
+                                     _ptr(accept_len), _ptr(next_token), _ptr(target_tok), ws.data_ptr(),
+                                     ws.numel(), _ptr(status), _stream())
+    _check(rc, "specdec_verify_greedy")
+    return accept_len, next_token
+
+
+def specdec_verify_sample(p, q, draft, u_accept, u_draw, status=None, accept_len=None, next_token=None):
+    """Sampled verification: p [B, D+1, V], q [B, D, V] float32 probabilities,
+    uniforms u_accept [B, D] and u_draw [B, D+1].  Returns (accept_len, next_token)."""
+    _need(p, "p", torch.float32)
+    B, D1, V = p.shape
+    D = D1 - 1
+    _need(q, "q", torch.float32)
+    _need(draft, "draft", torch.int32)
+    _need(u_accept, "u_accept", torch.float32)
+    _need(u_draw, "u_draw", torch.float32)
+    if tuple(q.shape) != (B, D, V) or tuple(draft.shape) != (B, D) or tuple(u_accept.shape) != (B, D) or \
+            tuple(u_draw.shape) != (B, D1):
+        raise ValueError("shape mismatch between p, q, draft and the uniforms")
+    dev = p.device
+    accept_len = _i32(B, dev) if accept_len is None else accept_len
+    next_token = _i32(B, dev) if next_token is None else next_token
+    rc = lib().specdec_verify_sample(p.data_ptr(), q.data_ptr(), B, D, V, draft.data_ptr(), u_accept.data_ptr(),
+                                     u_draw.data_ptr(), _ptr(accept_len), _ptr(next_token), _ptr(status), _stream())
+    _check(rc, "specdec_verify_sample")
+    return accept_len, next_token
+
+
+class SeqBuf:
+    """Device tensors of a sequence set: a left-padded rectangle or a pool.
+
+    kv [L, 2, rows, H, cap, Dh]; tokens/pos [rows, cap] int32; mask [rows, cap]
+    int8; len [rows] int32; width [groups] int32 (None for a pool)."""
+
+    def __init__(self, kv, tokens, len, pos=None, mask=None, width=None):
+        _need(kv, "kv")
+        if kv.dtype not in _TORCH_DT or kv.dim() != 6 or kv.shape[1] != 2:
+            raise ValueError("kv must be a [L, 2, rows, H, cap, Dh] float32/float16/bfloat16 tensor")
+        self.kv, self.tokens, self.len, self.pos, self.mask, self.width = kv, tokens, len, pos, mask, width
+        L, _, rows, H, cap, Dh = kv.shape
+        for t, n, dt in ((tokens, "tokens", torch.int32), (pos, "pos", torch.int32), (mask, "mask", torch.int8)):
+            if t is not None:
+                _need(t, n, dt)
+                if tuple(t.shape) != (rows, cap):
+                    raise ValueError("%s must be [rows, cap]" % n)
+        _need(len, "len", torch.int32)
+        if width is not None:
+            _need(width, "width", torch.int32)
+        self.c = SeqBufC(kv.data_ptr(), _ptr(tokens), _ptr(pos), _ptr(mask), len.data_ptr(), _ptr(width), rows, cap,
+                         L, H, Dh, _TORCH_DT[kv.dtype])
+
+    @property
+    def rows(self):
+        return self.kv.shape[2]
+
+    @property
+    def cap(self):
+        return self.kv.shape[4]
+
+    @staticmethod
+    def empty(layers, rows, heads, cap, head_dim, dtype, device="cuda", groups=1, pool=False):
+        kv = torch.empty((layers, 2, rows, heads, cap, head_dim), dtype=dtype, device=device)
+        tok = torch.zeros((rows, cap), dtype=torch.int32, device=device)
+        ln = torch.zeros(rows, dtype=torch.int32, device=device)
+        if pool:
+            return SeqBuf(kv, tok, ln)
+        pos = torch.zeros((rows, cap), dtype=torch.int32, device=device)
+        mask = torch.zeros((rows, cap), dtype=torch.int8, device=device)
+        width = torch.zeros(max(groups, 1), dtype=torch.int32, device=device)
+        return SeqBuf(kv, tok, ln, pos, mask, width)
+
+
+def specdec_realign_kv(mode, src, dst, rows=None, B=None, group=0, skip_group=None, kv_new=None, draft=None,
+                       accept_len=None, next_token=None, pad_token=0, status=None):
+    """Realignment in one of the modes EQSPEC, GATHER, APPEND_INPLACE (see include/specdec.h)."""
+    if B is None:
+        B = rows.numel() if rows is not None else src.rows
+    D = 0
+    if kv_new is not None:
+        _need(kv_new, "kv_new", src.kv.dtype)
+        D = kv_new.shape[4] - 1
+    elif draft is not None:
+        D = draft.shape[1]
+    for t, n in ((rows, "rows"), (skip_group, "skip_group"), (draft, "draft"), (accept_len, "accept_len"),
+                 (next_token, "next_token"), (status, "status")):
+        if t is not None:
+            _need(t, n, torch.int32)
+    L, _, _, H, _, Dh = src.kv.shape
+    if kv_new is not None and tuple(kv_new.shape) != (L, 2, B, H, D + 1, Dh):
+        raise ValueError("kv_new must be [L, 2, B, H, D+1, Dh]")
+    for t, n, shape in ((draft, "draft", (B, D)), (accept_len, "accept_len", (B,)), (next_token, "next_token", (B,)),
+                        (rows, "rows", (B,))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError("%s must have shape %s" % (n, shape))
+    if mode == GATHER:
+        ng = (B + group - 1) // max(group, 1)
+        if skip_group is not None and skip_group.numel() < ng:
+            raise ValueError("skip_group needs one entry per group")
+        if dst.width is not None and dst.width.numel() < ng:
+            raise ValueError("the rectangle's width tensor needs one entry per group")
+    if mode == EQSPEC and (src.width is None or dst.width is None or dst.pos is None or dst.mask is None):
+        raise ValueError("EQSPEC needs width on both sides and pos/mask on the output")
+    rc = lib().specdec_realign_kv(mode, C.byref(src.c), C.byref(dst.c), _ptr(rows), B, group, _ptr(skip_group), D,
+                                  _ptr(kv_new), _ptr(draft), _ptr(accept_len), _ptr(next_token), pad_token,
+                                  _ptr(status), _stream())
+    _check(rc, "specdec_realign_kv")
+
+
+def realign_eqspec(src, dst, kv_new, draft, accept_len, next_token, pad_token=0, status=None):
+    """EQSPEC unpad-append-repad of rectangle `src` into rectangle `dst`."""
+    specdec_realign_kv(EQSPEC, src, dst, None, src.rows, 0, None, kv_new, draft, accept_len, next_token,
+                       pad_token, status)
+
+
+def gather(pool, rect, rows, group, skip_group=None, pad_token=0, status=None):
+    """Left-padded rectangles of the listed pool rows, one per group of `group` entries."""
+    specdec_realign_kv(GATHER, pool, rect, rows, rows.numel() if rows is not None else pool.rows, group,
+                       skip_group, None, None, None, None, pad_token, status)
+
+
+def append(pool, kv_new, draft, accept_len, next_token, rows=None, status=None):
+    """In-place append of every entry's committed tokens and KV at its pool row's length."""
+    B = kv_new.shape[2]
+    specdec_realign_kv(APPEND_INPLACE, pool, pool, rows, B, 0, None, kv_new, draft, accept_len, next_token, 0,
+                       status)
+
+
+def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_uniform=None):
+    """Equal-length grouping of a pool: returns (order, uniform, width, n_uniform) device tensors."""
+    _need(lens, "lens", torch.int32)
+    N = lens.numel()
+    nb = (N + group - 1) // group
+    dev = lens.device
+    order = _i32(N, dev) if order is None else order
+    uniform = _i32(max(nb, 1), dev) if uniform is None else uniform
+    width = _i32(max(nb, 1), dev) if width is None else width
+    n_uniform = _i32(1, dev) if n_uniform is None else n_uniform
+    rc = lib().specdec_group_by_len(lens.data_ptr(), N, group, order.data_ptr(), uniform.data_ptr(),
+                                    width.data_ptr(), n_uniform.data_ptr(), _stream())
+    _check(rc, "specdec_group_by_len")
+    return order, uniform[:nb], width[:nb], n_uniform
+
+
+verify_greedy = specdec_verify_greedy
+verify_sample = specdec_verify_sample
+group_by_len = specdec_group_by_len

@@ -1,0 +1,127 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point its
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from ragged_kv_realignment_amd import specdec as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specdec.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(specdec_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_steps():
+    names = _declared()
+    for n in ("specdec_verify_greedy", "specdec_verify_sample", "specdec_realign_kv", "specdec_group_by_len"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (specdec_\w+)", out))
+    assert set(_declared()) <= exported
+    assert set(S.EXPORTS) == set(_declared())
+
+
+def test_version_and_workspace_size():
+    assert S.specdec_version().startswith("specdec")
+    L = S.lib()
+    assert L.specdec_workspace_bytes(16, 5) >= 16 * 6 * 8 + 16 * 4
+    assert L.specdec_workspace_bytes(-1, 5) == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation on the host
+
+
+def test_verify_greedy_host_errors():
+    L = S.lib()
+    f = L.specdec_verify_greedy
+    ws_need = L.specdec_workspace_bytes(2, 3)
+    args = dict(logits=FAKE, dt=S.BF16, rs=100, B=2, D=3, V=100, draft=FAKE, acc=FAKE, nxt=FAKE, tgt=None,
+                ws=FAKE, wsb=ws_need, st=None, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["logits"], a["dt"], a["rs"], a["B"], a["D"], a["V"], a["draft"], a["acc"], a["nxt"], a["tgt"],
+                 a["ws"], a["wsb"], a["st"], a["stream"])
+
+    assert call(B=-1) == S.E_ARG
+    assert call(D=-1) == S.E_ARG
+    assert call(V=0) == S.E_ARG
+    assert call(rs=99) == S.E_ARG
+    assert call(dt=7) == S.E_DTYPE
+    assert call(logits=None) == S.E_ARG
+    assert call(draft=None) == S.E_ARG
+    assert call(ws=None) == S.E_WORKSPACE
+    assert call(wsb=ws_need - 1) == S.E_WORKSPACE
+    assert call(ws=FAKE + 4) == S.E_WORKSPACE
+    assert call(B=0) == S.OK  # empty batch: nothing to do
+
+
+def test_verify_sample_host_errors():
+    f = S.lib().specdec_verify_sample
+    assert f(FAKE, FAKE, -1, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
+    assert f(FAKE, FAKE, 2, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
+    assert f(None, FAKE, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
+    assert f(FAKE, None, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
+    assert f(FAKE, FAKE, 0, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.OK
+
+
+def _sb(kv=FAKE, rows=4, cap=64, layers=2, heads=2, head_dim=128, dtype=S.BF16, tokens=FAKE, pos=FAKE, mask=FAKE,
+        ln=FAKE, width=FAKE):
+    return S.SeqBufC(kv, tokens, pos, mask, ln, width, rows, cap, layers, heads, head_dim, dtype)
+
+
+def test_realign_host_errors():
+    f = S.lib().specdec_realign_kv
+
+    def call(mode, a, b, B=4, group=0, D=3, kv_new=FAKE * 100, rows=None, skip=None):
+        return f(mode, C.byref(a), C.byref(b), rows, B, group, skip, D, kv_new, FAKE, FAKE, FAKE, 0, None, None)
+
+    src = _sb(kv=FAKE * 1000)
+    dst = _sb(kv=FAKE * 2000)
+    assert call(9, src, dst) == S.E_ARG
+    assert call(S.EQSPEC, src, dst, B=1025) == S.E_ARG
+    assert call(S.EQSPEC, _sb(dtype=5), dst) == S.E_DTYPE
+    assert call(S.EQSPEC, _sb(kv=FAKE * 1000, head_dim=4), _sb(kv=FAKE * 2000, head_dim=4)) == S.E_ALIGN
+    assert call(S.EQSPEC, _sb(kv=FAKE * 1000 + 8), dst) == S.E_ALIGN
+    assert call(S.EQSPEC, src, _sb(kv=FAKE * 2000, heads=3)) == S.E_ARG
+    assert call(S.EQSPEC, src, _sb(kv=FAKE * 1000 + 4096)) == S.E_ALIAS       # KV ranges overlap
+    assert call(S.EQSPEC, src, dst, B=3) == S.E_ARG                            # B != rows
+    assert call(S.EQSPEC, src, _sb(kv=FAKE * 2000, width=None)) == S.E_ARG
+    assert call(S.EQSPEC, src, dst, kv_new=FAKE * 100 + 8) == S.E_ALIGN
+    assert call(S.GATHER, src, dst, group=0) == S.E_ARG
+    assert call(S.GATHER, src, _sb(kv=FAKE * 2000, rows=3), group=2) == S.E_ARG
+    assert call(S.APPEND_INPLACE, src, dst) == S.E_ARG                         # not the same pool
+    assert call(S.APPEND_INPLACE, src, src, kv_new=None) == S.E_ARG
+
+
+def test_group_by_len_host_errors():
+    f = S.lib().specdec_group_by_len
+    assert f(FAKE, -1, 8, FAKE, FAKE, FAKE, FAKE, None) == S.E_ARG
+    assert f(FAKE, 4097, 8, FAKE, FAKE, FAKE, FAKE, None) == S.E_ARG
+    assert f(FAKE, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == S.E_ARG
+    assert f(FAKE, 16, 8, None, FAKE, FAKE, FAKE, None) == S.E_ARG
+
+
+def test_workspace_init_null():
+    assert S.lib().specdec_workspace_init(None, 256, None) == S.E_WORKSPACE
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    monkeypatch.setattr(S, "_lib", None)
+    monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError):
+        S.lib()

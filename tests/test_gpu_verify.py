@@ -1,0 +1,249 @@
+"""GPU parity of verification: the HIP kernels against the oracle, bit-exact for
+greedy, within the stated band for sampling."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import synth.device as sdev
+from tests.gpu_util import from_np_raw, say, to_np_raw
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_kv_realignment_amd as m
+    return m
+
+
+def _encode(rows_f32, enc):
+    if enc == "f32":
+        return rows_f32.astype(np.float32), torch.float32
+    if enc == "f16":
+        return rows_f32.astype(np.float16), torch.float16
+    return (rows_f32.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16), torch.bfloat16
+
+
+def _gpu_greedy(sd, host_rows, tdt, B, D, V, draft, row_stride=None, offset_elems=0):
+    """Run the kernel on host rows [B*(D+1), V]; optional padded rows / misaligned base."""
+    rs = V if row_stride is None else row_stride
+    buf = np.zeros((B * (D + 1) * rs + offset_elems + 8,), dtype=host_rows.dtype)
+    view = buf[offset_elems:offset_elems + B * (D + 1) * rs].reshape(B * (D + 1), rs)
+    view[:, :V] = host_rows
+    dev = from_np_raw(buf, tdt)
+    logits = torch.as_strided(dev, (B, D + 1, V), (rs * (D + 1), rs, 1), offset_elems)
+    tgt = torch.empty((B, D + 1), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_greedy(logits, torch.from_numpy(np.ascontiguousarray(draft, np.int32)).cuda(),
+                                status=status, target_tok=tgt)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), nxt.cpu().numpy(), tgt.cpu().numpy(), int(status.item())
+
+
+@pytest.mark.parametrize("enc", ["f32", "f16", "bf16"])
+def test_greedy_ties_signed_zero_and_infinities(sd, enc):
+    say("greedy ties", enc)
+    V, D = 3000, 3
+    rows = np.full((D + 1, V), -3.0, np.float32)
+    rows[0, [2047, 5, 2999, 1000]] = 1.5
+    rows[1, :] = -1.0
+    rows[1, 2500] = -0.0
+    rows[1, 2600] = 0.0
+    rows[2, :] = -np.inf
+    rows[3, :] = 0.25
+    rows[3, 2999] = np.inf
+    host, tdt = _encode(rows, enc)
+    draft = np.array([[5, 2500, 0]], np.int32)
+    acc, nxt, tgt, st = _gpu_greedy(sd, host, tdt, 1, D, V, draft)
+    oacc, onxt, otgt = oracle.verify_greedy(host, draft, 1, D, V)
+    assert list(otgt[0]) == [5, 2500, 0, 2999]
+    assert np.array_equal(tgt, otgt) and np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
+    assert st == 0
+
+
+@pytest.mark.parametrize("enc", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 0, 1), (1, 0, 7), (3, 2, 9), (5, 4, 1000), (2, 6, 4099), (7, 3, 70001)])
+def test_greedy_discrete_random(sd, enc, shape):
+    """Logits drawn from a few values (many exact ties, -0 and +0), odd V, a
+    ragged last vector, several workgroups per row."""
+    B, D, V = shape
+    say("greedy discrete", enc, shape)
+    rng = np.random.default_rng(B * 1000 + D * 10 + V)
+    vals = np.array([-7.0, -0.0, 0.0, 0.5, 2.0, 2.0], np.float32)
+    rows = vals[rng.integers(0, len(vals), (B * (D + 1), V))]
+    host, tdt = _encode(rows, enc)
+    t0 = np.argmax(rows.reshape(B, D + 1, V), axis=-1)
+    draft = np.where(rng.random((B, D)) < 0.8, t0[:, :D], rng.integers(0, V, (B, D))).astype(np.int32)
+    acc, nxt, tgt, st = _gpu_greedy(sd, host, tdt, B, D, V, draft)
+    oacc, onxt, otgt = oracle.verify_greedy(host, draft, B, D, V)
+    assert np.array_equal(tgt, otgt)
+    assert np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
+
+
+@pytest.mark.parametrize("enc", ["f32", "bf16"])
+def test_greedy_strided_and_misaligned_rows(sd, enc):
+    """Rows with padding between them and a base that is not 16-byte aligned
+    (the kernel's scalar path)."""
+    B, D, V = 4, 3, 5003
+    rng = np.random.default_rng(9)
+    rows = rng.standard_normal((B * (D + 1), V)).astype(np.float32)
+    host, tdt = _encode(rows, enc)
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    oacc, onxt, otgt = oracle.verify_greedy(host, draft, B, D, V)
+    for rs, off in ((5008, 0), (5011, 1), (V, 3)):
+        say("greedy strided", enc, rs, off)
+        acc, nxt, tgt, _ = _gpu_greedy(sd, host, tdt, B, D, V, draft, row_stride=rs, offset_elems=off)
+        assert np.array_equal(tgt, otgt) and np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
+
+
+def test_greedy_draft_out_of_range_sets_status(sd):
+    say("greedy draft range")
+    B, D, V = 2, 3, 100
+    rows = np.random.default_rng(1).standard_normal((B * (D + 1), V)).astype(np.float32)
+    draft = np.array([[-1, 3, 4], [1, 2, 100]], np.int32)
+    acc, nxt, tgt, st = _gpu_greedy(sd, rows, torch.float32, B, D, V, draft)
+    oacc, onxt, _ = oracle.verify_greedy(rows, draft, B, D, V)
+    assert np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
+    assert st & sd.S_DRAFT_RANGE
+
+
+def test_greedy_workspace_reuse_many_calls(sd):
+    """One workspace serves consecutive calls (it is left cleared)."""
+    say("greedy workspace reuse")
+    B, D, V = 6, 4, 20000
+    ws = sd.workspace(B, D)
+    rng = np.random.default_rng(3)
+    for k in range(5):
+        rows = rng.standard_normal((B * (D + 1), V)).astype(np.float32)
+        draft = rng.integers(0, V, (B, D)).astype(np.int32)
+        dev = torch.from_numpy(rows).cuda().view(B, D + 1, V)
+        acc, nxt = sd.verify_greedy(dev, torch.from_numpy(draft).cuda(), ws=ws)
+        oacc, onxt, _ = oracle.verify_greedy(rows, draft, B, D, V)
+        assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(nxt.cpu().numpy(), onxt)
+    assert int(ws.count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "7b-mha", "8b-gqa", "exspec"])
+def test_greedy_workload_rounds(sd, name):
+    """Generated workloads at full size: every row of several rounds, bit-exact,
+    and the planted closed form (accepted length = designed first mismatch)."""
+    cfg = synth.CONFIGS[name]
+    rounds = 3 if name != "exspec" else 1
+    for r in range(rounds):
+        say("greedy workload", name, "round", r)
+        plant, miss, draft = synth.plan_greedy(cfg, r)
+        logits = torch.empty((cfg.B, cfg.D1, cfg.V), dtype=sdev.TORCH_DT[cfg.logit_dtype], device="cuda")
+        keep = sdev.fill_logits(cfg, r, plant, logits)
+        tgt = torch.empty((cfg.B, cfg.D1), dtype=torch.int32, device="cuda")
+        acc, nxt = sd.verify_greedy(logits, torch.from_numpy(draft).cuda(), target_tok=tgt)
+        torch.cuda.synchronize()
+        del keep
+        host = synth.logits_host(cfg, r, plant)
+        assert np.array_equal(to_np_raw(logits).reshape(host.shape).view(np.uint8), host.view(np.uint8)), \
+            "device generator differs from host generator"
+        oacc, onxt, otgt = oracle.verify_greedy(host, draft, cfg.B, cfg.D, cfg.V)
+        assert np.array_equal(tgt.cpu().numpy(), otgt)
+        assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(nxt.cpu().numpy(), onxt)
+        assert np.array_equal(oacc, miss)
+
+
+# ------------------------------------------------------------------ sampled
+
+BAND = 1e-6
+
+
+def _admissible_draw(p_row, q_row, u, j, band=BAND):
+    """Is id j an admissible inverse-CDF draw for uniform u (oracle arithmetic,
+    fp64 cumulative mass, decisions within band*T of a boundary accepted)?"""
+    w = np.maximum(p_row.astype(np.float64) - (q_row.astype(np.float64) if q_row is not None else 0.0), 0.0)
+    if not w.sum() > 0:
+        w = np.maximum(p_row.astype(np.float64), 0.0)
+    c = np.cumsum(w)
+    T = c[-1]
+    t = float(u) * T
+    lo = c[j - 1] if j > 0 else 0.0
+    return w[j] > 0 and lo - band * T <= t < c[j] + band * T
+
+
+def _check_sampled(p, q, draft, u_acc, u_draw, acc, nxt):
+    oacc, onxt, _ = oracle.verify_sample(p, q, draft, u_acc, u_draw)
+    assert np.array_equal(acc, oacc), "acceptance is exact on both sides"
+    D = q.shape[1]
+    n_amb = 0
+    for b in np.nonzero(nxt != onxt)[0]:
+        a = acc[b]
+        qrow = q[b, a] if a < D else None
+        assert _admissible_draw(p[b, a], qrow, u_draw[b, a], nxt[b]), "row %d: draw outside the band" % b
+        n_amb += 1
+    return n_amb
+
+
+def test_sample_stochastic_workload(sd):
+    cfg = synth.CONFIGS["stoch"]
+    say("sample workload stoch")
+    p, q, draft, u_acc, u_draw = synth.sampled_round(cfg, 0)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)), status=status)
+    torch.cuda.synchronize()
+    n_amb = _check_sampled(p, q, draft, u_acc, u_draw, acc.cpu().numpy(), nxt.cpu().numpy())
+    assert n_amb == 0
+    assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sample_random_small(sd, seed):
+    rng = np.random.default_rng(100 + seed)
+    B, D, V = int(rng.integers(1, 40)), int(rng.integers(0, 9)), int(rng.integers(1, 3000))
+    say("sample random", seed, B, D, V)
+    p = rng.random((B, D + 1, V)).astype(np.float32)
+    p[rng.random(p.shape) < 0.3] = 0.0
+    p[..., 0] += 1e-3
+    p /= p.sum(-1, keepdims=True)
+    q = rng.random((B, D, V)).astype(np.float32)
+    q[rng.random(q.shape) < 0.3] = 0.0
+    q[..., -1] += 1e-3
+    q /= q.sum(-1, keepdims=True)
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    if seed == 0 and D > 0:
+        q[0, 0] = p[0, 0]  # p == q at a position: certain acceptance
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)))
+    torch.cuda.synchronize()
+    _check_sampled(p, q, draft, u_acc, u_draw, acc.cpu().numpy(), nxt.cpu().numpy())
+
+
+def test_sample_worked_split(sd):
+    """The newsletter page's 40/60 example through the kernel, with stratified uniforms."""
+    say("sample worked split")
+    p = np.array([0.4, 0.6], np.float32)
+    q = np.array([0.8, 0.2], np.float32)
+    drafts = np.array([0] * 80 + [1] * 20, np.int32)[:, None]
+    u_acc = np.concatenate([(np.arange(80) + 0.5) / 80, (np.arange(20) + 0.5) / 20]).astype(np.float32)[:, None]
+    u_draw = ((np.arange(200) + 0.5) / 200).astype(np.float32).reshape(100, 2)
+    P = np.broadcast_to(p, (100, 2, 2)).copy()
+    Q = np.broadcast_to(q, (100, 1, 2)).copy()
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (P, Q, drafts, u_acc, u_draw)))
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    first = np.where(acc == 1, drafts[:, 0], nxt)
+    assert int(np.sum(first == 0)) == 40 and int(np.sum(first == 1)) == 60
+
+
+def test_sample_zero_row_status(sd):
+    say("sample zero row")
+    B, D, V = 1, 1, 16
+    p = np.zeros((B, D + 1, V), np.float32)
+    q = np.zeros((B, D, V), np.float32)
+    q[0, 0, 3] = 1.0
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in
+                                  (p, q, np.array([[3]], np.int32), np.zeros((1, 1), np.float32),
+                                   np.zeros((1, 2), np.float32))), status=status)
+    oacc, onxt, _ = oracle.verify_sample(p, q, np.array([[3]], np.int32), np.zeros((1, 1), np.float32),
+                                         np.zeros((1, 2), np.float32))
+    assert acc.item() == oacc[0] == 0 and nxt.item() == onxt[0] == 0
+    assert int(status.item()) & sd.S_PROB
