@@ -38,8 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=64, help="timed chained rounds")
     ap.add_argument("--warmup", type=int, default=8, help="untimed rounds before the timed chain")
     ap.add_argument("--config", default="8b-gqa")
-    ap.add_argument("--cpu-rounds", type=int, default=16, help="oracle sample: rounds")
-    ap.add_argument("--cpu-layers", type=int, default=12, help="oracle sample: KV layers realigned (scaled to all)")
+    ap.add_argument("--cpu-rounds", type=int, default=64, help="oracle sample: rounds")
+    ap.add_argument("--cpu-layers", type=int, default=36, help="oracle sample: KV layers realigned (scaled to all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration for profiling)")
@@ -198,18 +198,20 @@ def main():
 
     copy_note = None
     if args.copy_calib_gib > 0:
-        n = int(args.copy_calib_gib * (1 << 30))
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
-        a.fill_(1)
+        # a plain streaming elementwise kernel of known traffic (reads n bytes,
+        # writes n bytes), used to scale the hardware byte counters
+        n = int(args.copy_calib_gib * (1 << 30)) // 4 * 4
+        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record()
         for _ in range(5):
-            b.copy_(a)
+            torch.neg(a, out=b)
         c1.record()
         torch.cuda.synchronize()
-        copy_note = {"bytes_per_copy": 2 * n, "copy_gbs": 5 * 2 * n / (c0.elapsed_time(c1) * 1e-3) / 1e9}
+        copy_note = {"kernel": "torch.neg float32", "read_bytes": n, "write_bytes": n,
+                     "copy_gbs": 5 * 2 * n / (c0.elapsed_time(c1) * 1e-3) / 1e9}
         del a, b
 
     cpu = None

@@ -263,7 +263,7 @@ def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_un
     """Equal-length grouping of a pool: returns (order, uniform, width, n_uniform) device tensors."""
     _need(lens, "lens", torch.int32)
     N = lens.numel()
-    nb = (N + group - 1) // group
+    nb = (N + group - 1) // group if group > 0 else 0
     dev = lens.device
     order = _i32(N, dev) if order is None else order
     uniform = _i32(max(nb, 1), dev) if uniform is None else uniform

@@ -234,16 +234,17 @@ def test_sample_worked_split(sd):
 
 
 def test_sample_zero_row_status(sd):
+    """A position whose target probabilities are all zero: the draft is rejected
+    (0.5 * q(x) > p(x) = 0), the residual and its fallback are empty, so the
+    draw yields id 0 and the PROB status bit; the oracle agrees."""
     say("sample zero row")
     B, D, V = 1, 1, 16
     p = np.zeros((B, D + 1, V), np.float32)
     q = np.zeros((B, D, V), np.float32)
     q[0, 0, 3] = 1.0
+    args = (p, q, np.array([[3]], np.int32), np.full((1, 1), 0.5, np.float32), np.zeros((1, 2), np.float32))
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in
-                                  (p, q, np.array([[3]], np.int32), np.zeros((1, 1), np.float32),
-                                   np.zeros((1, 2), np.float32))), status=status)
-    oacc, onxt, _ = oracle.verify_sample(p, q, np.array([[3]], np.int32), np.zeros((1, 1), np.float32),
-                                         np.zeros((1, 2), np.float32))
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in args), status=status)
+    oacc, onxt, _ = oracle.verify_sample(*args)
     assert acc.item() == oacc[0] == 0 and nxt.item() == onxt[0] == 0
     assert int(status.item()) & sd.S_PROB
