@@ -100,8 +100,8 @@ int specdec_workspace_init(void *ws, size_t ws_bytes, void *stream);
  *  status      device int32, nullable (SPECDEC_S_DRAFT_RANGE).
  * The target's choice is the id of the largest logit, the lowest such id on
  * ties; -0.0 and +0.0 are equal; NaN logits are outside the contract.
- * B = 0 is a no-op.  Errors: E_ARG (B < 0, D < 0, V < 1, row_stride < V, NULL
- * logits/draft/outputs), E_DTYPE, E_WORKSPACE, E_LAUNCH. */
+ * B = 0 is a no-op.  Errors: E_ARG (B < 0, D < 0, D > 255, V < 1, row_stride < V,
+ * NULL logits/draft/outputs), E_DTYPE, E_WORKSPACE, E_LAUNCH. */
 int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
                           const int32_t *draft, int32_t *accept_len, int32_t *next_token,
                           int32_t *target_tok, void *ws, size_t ws_bytes, int32_t *status, void *stream);

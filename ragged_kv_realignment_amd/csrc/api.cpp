@@ -50,9 +50,11 @@ bool same_geometry(const specdec_seqbuf_t *a, const specdec_seqbuf_t *b) {
 
 EXPORT const char *specdec_version(void) { return "specdec 0.1 gfx950"; }
 
+static size_t ws_rowcnt_bytes(int B, int D) { return ((size_t)B * (size_t)(D + 1) * 4 + 255) / 256 * 256; }
+
 EXPORT size_t specdec_workspace_bytes(int B, int D) {
   if (B < 0 || D < 0) return 0;
-  return ws_keys_bytes(B, D) + ((size_t)B * 4 + 255) / 256 * 256;
+  return ws_keys_bytes(B, D) + ws_rowcnt_bytes(B, D) + ((size_t)B * 4 + 255) / 256 * 256;
 }
 
 EXPORT int specdec_workspace_init(void *ws, size_t ws_bytes, void *stream) {
@@ -67,7 +69,7 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
   if (!dtype_ok(dtype)) return SPECDEC_E_DTYPE;
   if (B == 0) return SPECDEC_OK;
   if (!logits || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
-  if ((long long)B * (D + 1) > (1LL << 24) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  if (D + 1 > 256 || (long long)B * (D + 1) > (1LL << 24) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
   if (!ws || ws_bytes < specdec_workspace_bytes(B, D) || reinterpret_cast<uintptr_t>(ws) % 8 != 0)
     return SPECDEC_E_WORKSPACE;
   sd::GreedyParams p;
@@ -82,7 +84,9 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
   p.next_token = next_token;
   p.target_tok = target_tok;
   p.keys = static_cast<unsigned long long *>(ws);
-  p.counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D));
+  p.row_counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D));
+  p.counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D) +
+                                                 ws_rowcnt_bytes(B, D));
   p.status = status;
   p.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
   return launched(sd::launch_verify_greedy(p, as_stream(stream)));
@@ -123,6 +127,14 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
   if (!same_geometry(in, out)) return SPECDEC_E_ARG;
   const int units = (int)((size_t)in->head_dim * esize(in->dtype) / 16);
   if (units > 256) return SPECDEC_E_ARG;
+  // one (layer, K|V, row, head) sequence is addressed with 32-bit byte offsets
+  if ((size_t)in->cap * units * 16 >= (1u << 31) || (size_t)out->cap * units * 16 >= (1u << 31) ||
+      (size_t)(D + 1) * units * 16 >= (1u << 31))
+    return SPECDEC_E_ARG;
+  // tiles are numbered with 32-bit integers
+  if ((size_t)out->layers * 2 * (size_t)(out->rows > B ? out->rows : B) * out->heads * ((size_t)out->cap + 1) >=
+      (1u << 31))
+    return SPECDEC_E_ARG;
 
   sd::RealignParams p;
   memset(&p, 0, sizeof(p));

@@ -5,7 +5,7 @@
 
 namespace sd {
 
-constexpr int kBlock = 256;     // threads per workgroup: 4 waves of 64
+constexpr int kBlock = 256;     // threads per workgroup of the verify kernels: 4 waves of 64
 constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -54,7 +54,8 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t bits) {
   if (status && bits) atomicOr(status, bits);
 }
 
-// Block-wide reductions for kBlock threads; `scratch` holds kBlock/kWave ints.
+// Block-wide reductions over NT threads; `scratch` holds NT/kWave ints.
+template <int NT = kBlock>
 __device__ __forceinline__ int block_max_int(int v, int *scratch) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
@@ -64,10 +65,11 @@ __device__ __forceinline__ int block_max_int(int v, int *scratch) {
   __syncthreads();
   int r = scratch[0];
 #pragma unroll
-  for (int k = 1; k < kBlock / kWave; ++k) r = max(r, scratch[k]);
+  for (int k = 1; k < NT / kWave; ++k) r = max(r, scratch[k]);
   return r;
 }
 
+template <int NT = kBlock>
 __device__ __forceinline__ int block_or_int(int v, int *scratch) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) v |= __shfl_xor(v, off);
@@ -77,8 +79,56 @@ __device__ __forceinline__ int block_or_int(int v, int *scratch) {
   __syncthreads();
   int r = 0;
 #pragma unroll
-  for (int k = 0; k < kBlock / kWave; ++k) r |= scratch[k];
+  for (int k = 0; k < NT / kWave; ++k) r |= scratch[k];
   return r;
+}
+
+template <int NT = kBlock>
+__device__ __forceinline__ float block_max_float(float v, float *scratch) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int k = 1; k < NT / kWave; ++k) r = fmaxf(r, scratch[k]);
+  return r;
+}
+
+template <int NT = kBlock>
+__device__ __forceinline__ int block_min_int(int v, int *scratch) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  int r = scratch[0];
+#pragma unroll
+  for (int k = 1; k < NT / kWave; ++k) r = min(r, scratch[k]);
+  return r;
+}
+
+// Division by a runtime-invariant divisor d (1 <= d < 2^31) for n < 2^31 with a
+// multiply-high: with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// n / d = (mulhi(n, m) + n) >> s (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+__device__ __forceinline__ FastDiv fast_div(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.s = d > 1 ? 32u - (uint32_t)__clz((int)(d - 1)) : 0u;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1ull);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  return (uint32_t)(((unsigned long long)__umulhi(n, f.m) + n) >> f.s);
 }
 
 }  // namespace sd

@@ -13,6 +13,7 @@ struct GreedyParams {
   const int32_t *draft;
   int32_t *accept_len, *next_token, *target_tok;
   unsigned long long *keys;   // [B*(D+1)] workspace
+  unsigned int *row_counters; // [B*(D+1)] workspace
   unsigned int *counters;     // [B] workspace
   int32_t *status;
   bool vec;                   // 16-byte aligned rows: vector loads

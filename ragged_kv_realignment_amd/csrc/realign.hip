@@ -15,8 +15,13 @@
 // multiple of 16): each (layer, K|V, row, head) sequence is contiguous, so a
 // row's shift is a whole number of positions and every load and store is a
 // naturally aligned 16-byte vector.  Threads of a workgroup cover
-// kBlock / units consecutive positions per pass, so a wave reads and writes
-// contiguous bytes; pad positions are store-only.
+// (workgroup size / units) consecutive positions per pass, so a wave reads and writes
+// contiguous bytes.  Loads and stores are raw buffer operations on one
+// descriptor per source and destination sequence: lanes whose position lies
+// outside a descriptor's range use an out-of-range offset, which returns zero
+// (loads) or is dropped (stores) without a memory access.  Pad positions are
+// thereby store-only, the tile body is straight-line code, and each thread
+// keeps all of its loads in flight before its stores.
 #include <limits.h>
 #include "device_common.h"
 #include "launch.h"
@@ -25,85 +30,232 @@
 namespace sd {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxB = 1024;
-constexpr int kPasses = 4;  // positions per thread per tile
 
-__device__ __forceinline__ u32x4 ld(const u32x4 *p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st(u32x4 v, u32x4 *p) { __builtin_nontemporal_store(v, p); }
+// Tuning knobs (defaults are the measured best on MI355X).
+#ifndef SPECDEC_RA_BLOCK
+#define SPECDEC_RA_BLOCK 1024    // threads per realign workgroup
+#endif
+#ifndef SPECDEC_RA_PASSES
+#define SPECDEC_RA_PASSES 4      // positions per thread per tile
+#endif
+#ifndef SPECDEC_RA_WG_PER_CU
+#define SPECDEC_RA_WG_PER_CU 128 // workgroups per CU in the grid (0: one tile per workgroup)
+#endif
+#ifndef SPECDEC_RA_INTERLEAVE
+#define SPECDEC_RA_INTERLEAVE 1  // tile t -> workgroup t mod grid (1) or contiguous ranges (0)
+#endif
+#ifndef SPECDEC_RA_AUX_LD
+#define SPECDEC_RA_AUX_LD 2      // cache policy of KV loads (2 = nt: streamed, read once)
+#endif
+#ifndef SPECDEC_RA_AUX_ST
+#define SPECDEC_RA_AUX_ST 2      // cache policy of KV stores (2 = nt)
+#endif
+constexpr int kPasses = SPECDEC_RA_PASSES;
+constexpr int kRaBlock = SPECDEC_RA_BLOCK;
 
-// Contiguous share [t0, t1) of `ntiles` tiles for this workgroup.
-__device__ __forceinline__ void my_tiles(long ntiles, long &t0, long &t1) {
-  const long per = (ntiles + gridDim.x - 1) / gridDim.x;
-  t0 = (long)blockIdx.x * per;
-  t1 = t0 + per < ntiles ? t0 + per : ntiles;
+constexpr uint32_t kOOB = 0x80000000u;       // above every descriptor's range
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ i32x4 bld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SPECDEC_RA_AUX_LD);
+}
+__device__ __forceinline__ void bst(i32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, SPECDEC_RA_AUX_ST);
+}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// A destination tile of the pipelined copy: positions [j_lo, j_lo + TP) of one
+// sequence; position j < a_hi takes source position j - a_lo when j >= a_lo and
+// zero otherwise (pad); positions at or past a_hi are not written here.
+struct Tile {
+  __amdgpu_buffer_rsrc_t ra, rd;
+  int j_lo, a_lo, a_hi;
+};
+
+__device__ __forceinline__ Tile empty_tile() {
+  Tile t;
+  t.ra = rsrc(nullptr, 0);
+  t.rd = rsrc(nullptr, 0);
+  t.j_lo = 0;
+  t.a_lo = 0;
+  t.a_hi = 0;
+  return t;
+}
+
+__device__ __forceinline__ void load_tile(const Tile &t, i32x4 *v, int poff, int PP, int U, int u, bool act) {
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int j = t.j_lo + poff + k * PP;
+    const bool in = act && j >= t.a_lo && j < t.a_hi;
+    v[k] = bld(t.ra, in ? (uint32_t)((j - t.a_lo) * U + u) * 16u : kOOB);
+  }
+}
+
+__device__ __forceinline__ void store_tile(const Tile &t, const i32x4 *v, int poff, int PP, int U, int u, bool act) {
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int j = t.j_lo + poff + k * PP;
+    bst(v[k], t.rd, (act && j < t.a_hi) ? (uint32_t)(j * U + u) * 16u : kOOB);
+  }
+}
+
+// Block-wide max of `mx` and OR of `bits` with a single barrier (scratch arrays
+// hold one entry per wave and are not reused before the barrier).
+__device__ __forceinline__ void block_max_or(int mx, int bits, int *s_m, int *s_o, int &out_mx, int &out_bits) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off));
+    bits |= __shfl_xor(bits, off);
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    s_m[threadIdx.x / kWave] = mx;
+    s_o[threadIdx.x / kWave] = bits;
+  }
+  __syncthreads();
+  out_mx = s_m[0];
+  out_bits = s_o[0];
+#pragma unroll
+  for (int k = 1; k < kRaBlock / kWave; ++k) {
+    out_mx = max(out_mx, s_m[k]);
+    out_bits |= s_o[k];
+  }
+}
+
+// This workgroup's tiles: t = first, first + step, ... < end.  Interleaved
+// (t mod grid) keeps all resident workgroups within one window of consecutive
+// tiles, so the pages they touch stay few; contiguous ranges are the
+// alternative.
+struct Sched {
+  uint32_t first, end, step;
+};
+
+__device__ __forceinline__ Sched my_tiles(uint32_t ntiles) {
+  Sched s;
+#if SPECDEC_RA_INTERLEAVE
+  s.first = blockIdx.x;
+  s.end = ntiles;
+  s.step = gridDim.x;
+#else
+  const uint32_t per = (ntiles + gridDim.x - 1) / gridDim.x;
+  s.first = blockIdx.x * per;
+  s.end = min(ntiles, s.first + per);
+  s.step = 1;
+#endif
+  return s;
+}
+
+// Software-pipelined copy over this workgroup's tiles: a tile's loads are
+// issued before the previous tile's stores, so waiting for loads never waits
+// for stores (the gfx9 vector-memory counter is in order).
+template <typename TileAt>
+__device__ __forceinline__ void run_tiles(uint32_t ntiles, TileAt tile_at, int poff, int PP, int U, int u,
+                                          bool act) {
+  const Sched sc = my_tiles(ntiles);
+  if (sc.first >= sc.end) return;
+  Tile cur = tile_at(sc.first);
+  i32x4 v[kPasses];
+  load_tile(cur, v, poff, PP, U, u, act);
+  for (uint32_t t = sc.first; t < sc.end; t += sc.step) {
+    const uint32_t tn = t + sc.step;
+    Tile nxt = tn < sc.end ? tile_at(tn) : empty_tile();
+    i32x4 w[kPasses];
+    load_tile(nxt, w, poff, PP, U, u, act);
+    store_tile(cur, v, poff, PP, U, u, act);
+    cur = nxt;
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) v[k] = w[k];
+  }
+}
+
+// EQSPEC tile (seg, chunk): old content [pin, S) of the input sequence lands at
+// [pout, pout + c) of the output; the committed entries after it are copied
+// separately.
+__device__ __forceinline__ Tile eq_tile(const char *in, char *out, const RealignParams &p, long seg, int chunk, int b,
+                                        const int *s_c, const int *s_n, int S, int Snew, int TP, size_t pos_bytes) {
+  const int c = uni(s_c[b]), n = uni(s_n[b]);
+  const int pin = S - c, pout = Snew - c - n;
+  Tile t;
+  t.ra = rsrc(in + ((size_t)seg * p.cap_in + pin) * pos_bytes, (uint32_t)(c * pos_bytes));
+  t.rd = rsrc(out + (size_t)seg * p.cap_out * pos_bytes, (uint32_t)((pout + c) * pos_bytes));
+  t.j_lo = chunk * TP;
+  t.a_lo = pout;
+  t.a_hi = pout + c;
+  return t;
 }
 
 // ------------------------------------------------------------------ EQSPEC
-__global__ __launch_bounds__(kBlock) void k_realign_eqspec(RealignParams p) {
+__global__ __launch_bounds__(kRaBlock) void k_realign_eqspec(RealignParams p) {
   __shared__ int s_c[kMaxB];
   __shared__ int s_n[kMaxB];
-  __shared__ int s_red[kBlock / kWave];
+  __shared__ int s_red[kRaBlock / kWave];
+  __shared__ int s_red2[kRaBlock / kWave];
   const int B = p.B, D = p.D, U = p.units, H = p.heads;
   const int S = p.width_in[0];
   int mx = 0, bad = (S < 0 || S > p.cap_in) ? SPECDEC_S_LEN_RANGE : 0;
-  for (int b = threadIdx.x; b < B; b += kBlock) {
+  for (int b = threadIdx.x; b < B; b += kRaBlock) {
     const int c = p.len_in[b], a = p.accept_len[b];
     if (c < 0 || c > S || a < 0 || a > D) bad = SPECDEC_S_LEN_RANGE;
     s_c[b] = c;
     s_n[b] = a + 1;
     mx = max(mx, c + a + 1);
   }
-  const int Snew = block_max_int(mx, s_red);
-  bad = block_or_int(bad, s_red);
+  // one fused reduction (new width, error bits) with a single barrier
+  int Snew;
+  block_max_or(mx, bad, s_red, s_red2, Snew, bad);
   if (!bad && Snew > p.cap_out) bad = SPECDEC_S_CAPACITY;
   if (bad) {
     if (blockIdx.x == 0 && threadIdx.x == 0) set_status(p.status, bad);
     return;
   }
 
-  const int PP = kBlock / U;             // positions per pass
+  const int PP = kRaBlock / U;             // positions per pass
   const int TP = PP * kPasses;           // positions per tile
   const int chunks = (Snew + TP - 1) / TP;
   const long nseg = (long)p.layers * 2 * B * H;
   const int poff = threadIdx.x / U, u = threadIdx.x - poff * U;
   const bool active = poff < PP;
-  const u32x4 *in = static_cast<const u32x4 *>(p.kv_in);
-  u32x4 *out = static_cast<u32x4 *>(p.kv_out);
-  const u32x4 *nw = static_cast<const u32x4 *>(p.kv_new);
+  const char *in = static_cast<const char *>(p.kv_in);
+  char *out = static_cast<char *>(p.kv_out);
+  const char *nw = static_cast<const char *>(p.kv_new);
+  const size_t pos_bytes = (size_t)U * 16;
 
-  long t0, t1;
-  my_tiles(nseg * chunks, t0, t1);
-  if (t0 < t1 && active) {
-    long seg = t0 / chunks;
-    int chunk = (int)(t0 - seg * chunks);
-    int b = (int)((seg / H) % B);
-    for (long t = t0; t < t1; ++t) {
-      const int c = s_c[b], n = s_n[b];
-      const int pin = S - c, pout = Snew - c - n;
-      const u32x4 *src = in + (size_t)seg * p.cap_in * U + u;
-      const u32x4 *srcn = nw + (size_t)seg * (D + 1) * U + u;
-      u32x4 *dst = out + (size_t)seg * p.cap_out * U + u;
-      const int j0 = chunk * TP + poff;
-      u32x4 v[kPasses];
-#pragma unroll
-      for (int k = 0; k < kPasses; ++k) {
-        const int j = j0 + k * PP;
-        const int cj = j - pout;
-        v[k] = (u32x4)(0u);
-        if (j < Snew && cj >= 0) v[k] = cj < c ? ld(src + (size_t)(pin + cj) * U) : ld(srcn + (size_t)(cj - c) * U);
-      }
-#pragma unroll
-      for (int k = 0; k < kPasses; ++k) {
-        const int j = j0 + k * PP;
-        if (j < Snew) st(v[k], dst + (size_t)j * U);
-      }
-      if (++chunk == chunks) {
-        chunk = 0;
-        ++seg;
-        b = (int)((seg / H) % B);
+  // 1. the n committed entries of every sequence: positions [Snew - n, Snew);
+  // a workgroup pass covers kRaBlock / ((D+1)*U) sequences
+  {
+    const int ups = (D + 1) * U;
+    const int spp = max(1, kRaBlock / ups);
+    const int sq = threadIdx.x / ups, f = threadIdx.x - sq * ups;
+    for (long s0 = (long)blockIdx.x * spp; s0 < nseg; s0 += (long)gridDim.x * spp) {
+      const long sg = s0 + sq;
+      if (sq < spp && sg < nseg) {
+        const int b = (int)((sg / H) % B);
+        const int n = s_n[b];
+        const char *src = nw + (size_t)sg * (D + 1) * pos_bytes;
+        char *dst = out + ((size_t)sg * p.cap_out + (Snew - n)) * pos_bytes;
+        for (int g = f; g < n * U; g += ups)
+          *reinterpret_cast<i32x4 *>(dst + (size_t)g * 16) = __builtin_nontemporal_load(
+              reinterpret_cast<const i32x4 *>(src + (size_t)g * 16));
       }
     }
   }
+
+  // 2. pad and old content, positions [0, Snew - n): tiles of TP positions,
+  // software-pipelined so a tile's loads are issued before the previous tile's
+  // stores (waiting for loads then never waits for stores)
+  const FastDiv fd_chunks = fast_div(chunks), fd_h = fast_div(H), fd_b = fast_div(B);
+  auto tile_at = [&](uint32_t t) {
+    const uint32_t seg = fdiv(t, fd_chunks);
+    const int chunk = (int)(t - seg * chunks);
+    const uint32_t sh = fdiv(seg, fd_h);
+    const int b = (int)(sh - fdiv(sh, fd_b) * B);
+    return eq_tile(in, out, p, seg, chunk, b, s_c, s_n, S, Snew, TP, pos_bytes);
+  };
+  run_tiles((uint32_t)(nseg * chunks), tile_at, poff, PP, U, u, active);
 
   // token ids, position ids and mask of every row, on [0, Snew)
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
@@ -113,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void k_realign_eqspec(RealignParams p) {
     int32_t *to = p.tok_out + (size_t)b * p.cap_out;
     int32_t *po = p.pos_out + (size_t)b * p.cap_out;
     int8_t *mo = p.mask_out + (size_t)b * p.cap_out;
-    for (int j = threadIdx.x; j < Snew; j += kBlock) {
+    for (int j = threadIdx.x; j < Snew; j += kRaBlock) {
       const int cj = j - pout;
       int32_t tok;
       if (cj < 0) tok = p.pad_token;
@@ -134,17 +286,17 @@ __global__ __launch_bounds__(kBlock) void k_realign_eqspec(RealignParams p) {
 // ------------------------------------------------------------------ GATHER
 // Pool rows (content at [0, len)) -> one left-padded rectangle per group of
 // `group` batch entries, for every group not marked in skip_group.
-__global__ __launch_bounds__(kBlock) void k_gather(RealignParams p) {
+__global__ __launch_bounds__(kRaBlock) void k_gather(RealignParams p) {
   __shared__ int s_r[kMaxB];
   __shared__ int s_c[kMaxB];
   __shared__ int s_W[kMaxB];
   __shared__ int s_act[kMaxB];
   __shared__ int s_nact;
-  __shared__ int s_red[kBlock / kWave];
+  __shared__ int s_red[kRaBlock / kWave];
   const int B = p.B, G = p.group, U = p.units, H = p.heads;
   const int ng = (B + G - 1) / G;
   int bad = 0;
-  for (int j = threadIdx.x; j < B; j += kBlock) {
+  for (int j = threadIdx.x; j < B; j += kRaBlock) {
     const int r = p.rows ? p.rows[j] : j;
     int c = 0;
     if (r < 0 || r >= p.rows_in) bad = SPECDEC_S_LEN_RANGE;
@@ -155,7 +307,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(RealignParams p) {
   }
   __syncthreads();
   int wmax = 0;
-  for (int g = threadIdx.x; g < ng; g += kBlock) {
+  for (int g = threadIdx.x; g < ng; g += kRaBlock) {
     int W = 0;
     for (int j = g * G; j < min(B, g * G + G); ++j) W = max(W, s_c[j]);
     const bool skip = p.skip_group && p.skip_group[g];
@@ -165,8 +317,8 @@ __global__ __launch_bounds__(kBlock) void k_gather(RealignParams p) {
       if (W > p.cap_out) bad |= SPECDEC_S_CAPACITY;
     }
   }
-  const int Wmax = block_max_int(wmax, s_red);
-  bad = block_or_int(bad, s_red);
+  const int Wmax = block_max_int<kRaBlock>(wmax, s_red);
+  bad = block_or_int<kRaBlock>(bad, s_red);
   if (bad) {
     if (blockIdx.x == 0 && threadIdx.x == 0) set_status(p.status, bad);
     return;
@@ -180,46 +332,37 @@ __global__ __launch_bounds__(kBlock) void k_gather(RealignParams p) {
   __syncthreads();
   const int nact = s_nact;
 
-  const int PP = kBlock / U;
+  const int PP = kRaBlock / U;
   const int TP = PP * kPasses;
   const int chunks = (Wmax + TP - 1) / TP;
   const long nseg = (long)p.layers * 2 * nact * H;
   const int poff = threadIdx.x / U, u = threadIdx.x - poff * U;
   const bool active = poff < PP;
-  const u32x4 *in = static_cast<const u32x4 *>(p.kv_in);
-  u32x4 *out = static_cast<u32x4 *>(p.kv_out);
+  const char *in = static_cast<const char *>(p.kv_in);
+  char *out = static_cast<char *>(p.kv_out);
+  const size_t pos_bytes = (size_t)U * 16;
 
-  long t0 = 0, t1 = 0;
-  if (chunks > 0) my_tiles(nseg * chunks, t0, t1);
-  if (t0 < t1 && active) {
-    long seg = t0 / chunks;
-    int chunk = (int)(t0 - seg * chunks);
-    for (long t = t0; t < t1; ++t) {
-      const long lk = seg / ((long)nact * H);
-      const int rem = (int)(seg - lk * nact * H);
-      const int k = rem / H, h = rem - k * H;
-      const int j = s_act[k], r = s_r[j], c = s_c[j], W = s_W[j / G];
-      const int pad = W - c;
-      const u32x4 *src = in + ((size_t)(lk * p.rows_in + r) * H + h) * p.cap_in * U + u;
-      u32x4 *dst = out + ((size_t)(lk * p.rows_out + j) * H + h) * p.cap_out * U + u;
-      const int j0 = chunk * TP + poff;
-      u32x4 v[kPasses];
-#pragma unroll
-      for (int q = 0; q < kPasses; ++q) {
-        const int x = j0 + q * PP;
-        v[q] = (u32x4)(0u);
-        if (x < W && x >= pad) v[q] = ld(src + (size_t)(x - pad) * U);
-      }
-#pragma unroll
-      for (int q = 0; q < kPasses; ++q) {
-        const int x = j0 + q * PP;
-        if (x < W) st(v[q], dst + (size_t)x * U);
-      }
-      if (++chunk == chunks) {
-        chunk = 0;
-        ++seg;
-      }
-    }
+  // tile (seg, chunk) of active entry k: the pool row's content [0, c) lands at
+  // [W - c, W) of the rectangle row; the same pipelined copy as EQSPEC
+  if (chunks > 0) {
+    const FastDiv fd_chunks = fast_div(chunks), fd_kh = fast_div(nact * H), fd_h = fast_div(H);
+    auto tile_at = [&](uint32_t t) {
+      const uint32_t seg = fdiv(t, fd_chunks);
+      const int chunk = (int)(t - seg * chunks);
+      const uint32_t lk = fdiv(seg, fd_kh);
+      const uint32_t rem = seg - lk * (uint32_t)(nact * H);
+      const uint32_t k = fdiv(rem, fd_h), h = rem - k * H;
+      const int j = uni(s_act[k]);
+      const int r = uni(s_r[j]), c = uni(s_c[j]), W = uni(s_W[j / G]);
+      Tile t2;
+      t2.ra = rsrc(in + ((size_t)(lk * p.rows_in + r) * H + h) * p.cap_in * pos_bytes, (uint32_t)(c * pos_bytes));
+      t2.rd = rsrc(out + ((size_t)(lk * p.rows_out + j) * H + h) * p.cap_out * pos_bytes, (uint32_t)(W * pos_bytes));
+      t2.j_lo = chunk * TP;
+      t2.a_lo = W - c;
+      t2.a_hi = W;
+      return t2;
+    };
+    run_tiles((uint32_t)(nseg * chunks), tile_at, poff, PP, U, u, active);
   }
 
   for (int k = blockIdx.x; k < nact; k += gridDim.x) {
@@ -229,7 +372,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(RealignParams p) {
     int32_t *to = p.tok_out ? p.tok_out + (size_t)j * p.cap_out : nullptr;
     int32_t *po = p.pos_out ? p.pos_out + (size_t)j * p.cap_out : nullptr;
     int8_t *mo = p.mask_out ? p.mask_out + (size_t)j * p.cap_out : nullptr;
-    for (int x = threadIdx.x; x < W; x += kBlock) {
+    for (int x = threadIdx.x; x < W; x += kRaBlock) {
       const int cj = x - pad;
       if (to) to[x] = (cj >= 0 && ti) ? ti[cj] : p.pad_token;
       if (po) po[x] = cj < 0 ? 0 : cj;
@@ -246,7 +389,7 @@ __global__ __launch_bounds__(kBlock) void k_gather(RealignParams p) {
 // Validation shared by both append kernels: returns status bits (0 = valid).
 __device__ int append_check(const RealignParams &p, int *s_r, int *s_c, int *s_n, int *s_red) {
   int bad = 0;
-  for (int b = threadIdx.x; b < p.B; b += kBlock) {
+  for (int b = threadIdx.x; b < p.B; b += kRaBlock) {
     const int r = p.rows ? p.rows[b] : b;
     const int a = p.accept_len[b];
     int c = 0;
@@ -260,40 +403,47 @@ __device__ int append_check(const RealignParams &p, int *s_r, int *s_c, int *s_n
     s_c[b] = c;
     s_n[b] = a + 1;
   }
-  return block_or_int(bad, s_red);
+  return block_or_int<kRaBlock>(bad, s_red);
 }
 
 // KV entries: tile = one (layer, K|V, entry, head) sequence, n_b positions.
-__global__ __launch_bounds__(kBlock) void k_append_kv(RealignParams p) {
+__global__ __launch_bounds__(kRaBlock) void k_append_kv(RealignParams p) {
   __shared__ int s_r[kMaxB];
   __shared__ int s_c[kMaxB];
   __shared__ int s_n[kMaxB];
-  __shared__ int s_red[kBlock / kWave];
+  __shared__ int s_red[kRaBlock / kWave];
   if (append_check(p, s_r, s_c, s_n, s_red)) return;  // reported by k_append_meta
   const int B = p.B, U = p.units, H = p.heads, D1 = p.D + 1;
   const long nseg = (long)p.layers * 2 * B * H;
-  long t0, t1;
-  my_tiles(nseg, t0, t1);
-  const u32x4 *nw = static_cast<const u32x4 *>(p.kv_new);
-  u32x4 *pool = static_cast<u32x4 *>(p.kv_out);
-  for (long seg = t0; seg < t1; ++seg) {
+  const char *nw = static_cast<const char *>(p.kv_new);
+  char *pool = static_cast<char *>(p.kv_out);
+  const size_t pos_bytes = (size_t)U * 16;
+  // a workgroup pass covers kRaBlock / ((D+1)*U) sequences
+  const int ups = D1 * U;
+  const int spp = max(1, kRaBlock / ups);
+  const int sq = threadIdx.x / ups, f = threadIdx.x - sq * ups;
+  for (long s0 = (long)blockIdx.x * spp; s0 < nseg; s0 += (long)gridDim.x * spp) {
+    const long seg = s0 + sq;
+    if (sq >= spp || seg >= nseg) continue;
     const long lk = seg / ((long)B * H);
     const int rem = (int)(seg - lk * B * H);
     const int b = rem / H, h = rem - b * H;
     const int r = s_r[b], c = s_c[b], n = s_n[b];
-    const u32x4 *src = nw + (size_t)seg * D1 * U;
-    u32x4 *dst = pool + ((size_t)(lk * p.rows_in + r) * H + h) * p.cap_in * U + (size_t)c * U;
-    for (int f = threadIdx.x; f < n * U; f += kBlock) st(ld(src + f), dst + f);
+    const char *src = nw + (size_t)seg * D1 * pos_bytes;
+    char *dst = pool + (((size_t)(lk * p.rows_in + r) * H + h) * p.cap_in + c) * pos_bytes;
+    for (int g = f; g < n * U; g += ups)
+      *reinterpret_cast<i32x4 *>(dst + (size_t)g * 16) =
+          __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + (size_t)g * 16));
   }
 }
 
 // Token ids and lengths, after the KV copy (stream order keeps len stable
 // while k_append_kv reads it).
-__global__ __launch_bounds__(kBlock) void k_append_meta(RealignParams p) {
+__global__ __launch_bounds__(kRaBlock) void k_append_meta(RealignParams p) {
   __shared__ int s_r[kMaxB];
   __shared__ int s_c[kMaxB];
   __shared__ int s_n[kMaxB];
-  __shared__ int s_red[kBlock / kWave];
+  __shared__ int s_red[kRaBlock / kWave];
   const int bad = append_check(p, s_r, s_c, s_n, s_red);
   if (bad) {
     if (threadIdx.x == 0) set_status(p.status, bad);
@@ -301,10 +451,10 @@ __global__ __launch_bounds__(kBlock) void k_append_meta(RealignParams p) {
   }
   const int B = p.B;
   int dup = 0;
-  for (int b = threadIdx.x; b < B; b += kBlock)
+  for (int b = threadIdx.x; b < B; b += kRaBlock)
     for (int o = 0; o < b; ++o) dup |= (s_r[o] == s_r[b]);
-  dup = block_or_int(dup, s_red);
-  for (int b = threadIdx.x; b < B; b += kBlock) {
+  dup = block_or_int<kRaBlock>(dup, s_red);
+  for (int b = threadIdx.x; b < B; b += kRaBlock) {
     const int r = s_r[b], c = s_c[b], n = s_n[b], a = n - 1;
     if (p.tok_out) {
       int32_t *to = p.tok_out + (size_t)r * p.cap_in + c;
@@ -317,18 +467,28 @@ __global__ __launch_bounds__(kBlock) void k_append_meta(RealignParams p) {
 }
 
 hipError_t launch_realign(const RealignParams &p, hipStream_t s) {
-  const int grid = 8 * device_cus();
+  int grid = SPECDEC_RA_WG_PER_CU * device_cus();
   if (p.mode == SPECDEC_EQSPEC) {
-    hipLaunchKernelGGL(k_realign_eqspec, dim3(grid), dim3(kBlock), 0, s, p);
+    if (SPECDEC_RA_WG_PER_CU == 0) {
+      // one tile per workgroup: enough workgroups for the widest possible output
+      const long tp = (long)(kRaBlock / p.units) * kPasses;
+      const long tiles = (long)p.layers * 2 * p.B * p.heads * ((p.cap_out + tp - 1) / tp);
+      grid = (int)(tiles > p.B ? tiles : p.B);
+    }
+    hipLaunchKernelGGL(k_realign_eqspec, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else if (p.mode == SPECDEC_GATHER) {
-    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kBlock), 0, s, p);
+    if (grid == 0) grid = 256 * device_cus();
+    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else {
-    const long nseg = (long)p.layers * 2 * p.B * p.heads;
+    if (grid == 0) grid = 8 * device_cus();
+    const long ups = (long)(p.D + 1) * p.units;
+    const long spp = ups < kRaBlock ? kRaBlock / ups : 1;
+    const long nseg = ((long)p.layers * 2 * p.B * p.heads + spp - 1) / spp;
     const long g = nseg < grid ? nseg : grid;
-    hipLaunchKernelGGL(k_append_kv, dim3((unsigned)(g > 0 ? g : 1)), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_append_kv, dim3((unsigned)(g > 0 ? g : 1)), dim3(kRaBlock), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_append_meta, dim3(1), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_append_meta, dim3(1), dim3(kRaBlock), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -32,110 +32,158 @@ __device__ __forceinline__ float load_scalar(const char *row, int v) {
   else return bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(row)[v]);
 }
 
-// Fold one 16-byte vector whose first element has id `base` into (bv, bi).
+// Element e of a 16-byte vector of type DT, widened exactly to fp32.
 template <int DT>
-__device__ __forceinline__ void consume(u32x4 r, int base, float &bv, int &bi) {
-  if constexpr (DT == 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = __uint_as_float(r[e]);
-      if (better(x, base + e, bv, bi)) { bv = x; bi = base + e; }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t w = r[e];
-      const float lo = DT == 2 ? __uint_as_float(w << 16) : f16_bits_to_f32(w & 0xFFFFu);
-      const float hi = DT == 2 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16);
-      if (better(lo, base + 2 * e, bv, bi)) { bv = lo; bi = base + 2 * e; }
-      if (better(hi, base + 2 * e + 1, bv, bi)) { bv = hi; bi = base + 2 * e + 1; }
-    }
-  }
+__device__ __forceinline__ float elem(u32x4 r, int e) {
+  if constexpr (DT == 0) return __uint_as_float(r[e]);
+  else if constexpr (DT == 2) return (e & 1) ? __uint_as_float(r[e >> 1] & 0xFFFF0000u) : __uint_as_float(r[e >> 1] << 16);
+  else return f16_bits_to_f32((e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xFFFFu));
 }
 
-// One workgroup scans `chunk` ids of one logit row (row = b*(D+1) + i), folds
-// its (value, id) into the row's 64-bit key with an atomic max, and the last
-// workgroup of row-block b to finish reads the D+1 keys and runs the
-// first-mismatch scan.  The workspace keys/counters are left zeroed.
+// Largest value of a vector.
+template <int DT>
+__device__ __forceinline__ float vmax(u32x4 r) {
+  constexpr int VW = 16 / Elem<DT>::size;
+  float m = elem<DT>(r, 0);
+#pragma unroll
+  for (int e = 1; e < VW; ++e) m = fmaxf(m, elem<DT>(r, e));
+  return m;
+}
+
+// Offset of the first element equal to M (-0.0 == +0.0), or VW if none.
+template <int DT>
+__device__ __forceinline__ int first_eq(u32x4 r, float M) {
+  constexpr int VW = 16 / Elem<DT>::size;
+  int at = VW;
+#pragma unroll
+  for (int e = VW - 1; e >= 0; --e)
+    if (elem<DT>(r, e) == M) at = e;
+  return at;
+}
+
+// Tuning: 16-byte vectors each thread loads at once, and workgroups per CU the
+// split aims for.  Defaults are the measured best on MI355X.
+#ifndef SPECDEC_VG_VPT
+#define SPECDEC_VG_VPT 4
+#endif
+
+// One workgroup scans `chunk` ids of one logit row (row = b*(D+1) + i): every
+// thread issues all its 16-byte loads before consuming any, the workgroup
+// reduces to one (value, id), and thread 0 folds it into the row's 64-bit key
+// with an atomic max.  The atomic's return is consumed before the per-batch-row
+// counter is incremented, so a workgroup that sees the counter complete also
+// sees every key (both are device-scope atomics, performed at the device's
+// coherence point; the keys are read back with device-scope atomic loads).  The
+// last workgroup of row-block b reads the D+1 keys in parallel, runs the
+// first-mismatch scan and leaves keys and counter zeroed for the next call.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int splits, int chunk) {
   constexpr int ES = Elem<DT>::size;
   constexpr int VW = 16 / ES;
-  constexpr int UNR = 4;
+  constexpr int VPT = SPECDEC_VG_VPT;
   const int wg = blockIdx.x;
   const int row = wg / splits;
   const int split = wg - row * splits;
-  const int D1 = p.D + 1;
+  const int D = p.D, D1 = p.D + 1;
   const int b = row / D1;
   const int start = split * chunk;
   const int end = min(p.V, start + chunk);
   const char *rowp = static_cast<const char *>(p.logits) + (size_t)row * (size_t)p.row_stride * ES;
 
-  float bv = -INFINITY;
-  int bi = INT_MAX;
+  // 1. every thread's largest value; all of its vector loads are issued before
+  //    any is used (one workgroup pass covers the chunk: chunk <= VPT*kBlock*VW)
+  float m = -INFINITY;
+  u32x4 r[VPT];
+  float tail_x = -INFINITY;
+  int tail_id = -1;
+  int nvec = 0;
+  const u32x4 *vp = nullptr;
   if constexpr (VEC) {
-    const int nvec = (end - start) / VW;
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp) + start / VW;
-    int k = threadIdx.x;
-    for (; k + (UNR - 1) * kBlock < nvec; k += UNR * kBlock) {
-      u32x4 r[UNR];
+    nvec = (end - start) / VW;
+    vp = reinterpret_cast<const u32x4 *>(rowp) + start / VW;
+    if (nvec > 0) {
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) r[u] = __builtin_nontemporal_load(vp + k + u * kBlock);
+      for (int u = 0; u < VPT; ++u)  // indices past the end re-read the last vector and are ignored
+        r[u] = __builtin_nontemporal_load(vp + min(u * kBlock + (int)threadIdx.x, nvec - 1));
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) consume<DT>(r[u], start + (k + u * kBlock) * VW, bv, bi);
+      for (int u = 0; u < VPT; ++u)
+        if (u * kBlock + (int)threadIdx.x < nvec) m = fmaxf(m, vmax<DT>(r[u]));
     }
-    for (; k < nvec; k += kBlock) consume<DT>(__builtin_nontemporal_load(vp + k), start + k * VW, bv, bi);
-    for (int v = start + nvec * VW + threadIdx.x; v < end; v += kBlock) {
-      const float x = load_scalar<DT>(rowp, v);
-      if (better(x, v, bv, bi)) { bv = x; bi = v; }
+    const int tv = start + nvec * VW + threadIdx.x;  // ragged last vector of the row
+    if (tv < end) {
+      tail_x = load_scalar<DT>(rowp, tv);
+      tail_id = tv;
+      m = fmaxf(m, tail_x);
     }
   } else {
-    for (int v = start + threadIdx.x; v < end; v += kBlock) {
-      const float x = load_scalar<DT>(rowp, v);
-      if (better(x, v, bv, bi)) { bv = x; bi = v; }
+    for (int v = start + threadIdx.x; v < end; v += kBlock) m = fmaxf(m, load_scalar<DT>(rowp, v));
+  }
+  __shared__ float s_f[kBlock / kWave];
+  __shared__ int s_i[kBlock / kWave];
+  __shared__ int s_last, s_a, s_bad;
+  __shared__ int s_t[kBlock];
+  const float M = block_max_float(m, s_f);
+
+  // 2. the lowest id holding M: only threads whose own maximum is M look
+  int bi = INT_MAX;
+  if (m == M) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int k = u * kBlock + (int)threadIdx.x;
+        if (bi == INT_MAX && k < nvec) {
+          const int at = first_eq<DT>(r[u], M);
+          if (at < VW) bi = start + k * VW + at;
+        }
+      }
+      if (bi == INT_MAX && tail_id >= 0 && tail_x == M) bi = tail_id;
+    } else {
+      for (int v = start + threadIdx.x; v < end; v += kBlock)
+        if (load_scalar<DT>(rowp, v) == M) { bi = v; break; }
     }
   }
-
-  wave_argmax(bv, bi);
-  __shared__ float s_v[kBlock / kWave];
-  __shared__ int s_i[kBlock / kWave];
-  __shared__ int s_last;
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  if (lane == 0) { s_v[w] = bv; s_i[w] = bi; }
-  __syncthreads();
+  bi = block_min_int(bi, s_i);
   if (threadIdx.x == 0) {
-#pragma unroll
-    for (int k = 1; k < kBlock / kWave; ++k)
-      if (better(s_v[k], s_i[k], bv, bi)) { bv = s_v[k]; bi = s_i[k]; }
-    atomicMax(&p.keys[row], argmax_key(bv, bi));
-    __threadfence();
-    const unsigned prev = atomicAdd(&p.counters[b], 1u);
-    s_last = (prev == (unsigned)(D1 * splits - 1));
+    const unsigned long long old = atomicMax(&p.keys[row], argmax_key(M, bi));
+    // opaque zero computed from the atomic's result: the counter update below
+    // cannot issue before the key update has completed
+    uint32_t dep = (uint32_t)old;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(dep));
+    // two-level completion count (splits per row, then D+1 rows per batch row)
+    // keeps the number of atomics on any one address small
+    int last = 0;
+    const unsigned prev = atomicAdd(&p.row_counters[row + (int)dep], 1u);
+    if (prev == (unsigned)(splits - 1)) {
+      store_agent(&p.row_counters[row], 0u);
+      last = atomicAdd(&p.counters[b], 1u) == (unsigned)(D1 - 1);
+    }
+    s_last = last;
+    s_a = D;
+    s_bad = 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) {
-    int a = 0, stop = 0, bad = 0;
-    int next = 0;
-    for (int i = 0; i < D1; ++i) {
-      unsigned long long *kp = &p.keys[(size_t)b * D1 + i];
-      const int t = key_id(load_agent(kp));
-      store_agent(kp, 0ull);
-      if (p.target_tok) p.target_tok[(size_t)b * D1 + i] = t;
-      if (i < p.D) {
-        const int d = p.draft[(size_t)b * p.D + i];
-        bad |= (d < 0 || d >= p.V);
-        if (!stop && d == t) ++a;
-        else if (!stop) { stop = 1; next = t; }
-      } else if (!stop) {
-        next = t;
-      }
+  // D + 1 <= kBlock (checked on the host): one position per thread
+  const int i = threadIdx.x;
+  if (i < D1) {
+    unsigned long long *kp = &p.keys[(size_t)b * D1 + i];
+    const int t = key_id(load_agent(kp));
+    store_agent(kp, 0ull);
+    s_t[i] = t;
+    if (p.target_tok) p.target_tok[(size_t)b * D1 + i] = t;
+    if (i < D) {
+      const int d = p.draft[(size_t)b * D + i];
+      if (d < 0 || d >= p.V) s_bad = 1;
+      if (d != t) atomicMin(&s_a, i);
     }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int a = s_a;
     p.accept_len[b] = a;
-    p.next_token[b] = next;
+    p.next_token[b] = s_t[a];
     store_agent(&p.counters[b], 0u);
-    if (bad) set_status(p.status, SPECDEC_S_DRAFT_RANGE);
+    if (s_bad) set_status(p.status, SPECDEC_S_DRAFT_RANGE);
   }
 }
 
@@ -149,23 +197,20 @@ int device_cus() {
 template <int DT>
 static hipError_t launch_greedy_dt(const GreedyParams &p, hipStream_t s) {
   constexpr int VW = 16 / Elem<DT>::size;
-  const int rows = p.B * (p.D + 1);
-  // Enough workgroups to keep every CU busy: aim at ~8 per CU, but never give a
-  // workgroup less than one vector per thread.
-  const long target = 8L * device_cus();
-  const int min_chunk = kBlock * VW;
-  int max_splits = (p.V + min_chunk - 1) / min_chunk;
-  int splits = (int)((target + rows - 1) / rows);
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int chunk = (p.V + splits - 1) / splits;
-  chunk = (chunk + VW - 1) / VW * VW;
-  splits = (p.V + chunk - 1) / chunk;
+  constexpr int step = kBlock * VW;  // ids covered by one vector per thread
+  const long rows = (long)p.B * (p.D + 1);
+  // Aim at ~8 workgroups per CU; a workgroup covers between one and
+  // SPECDEC_VG_VPT vectors per thread, all loaded before any is consumed.
+  const long want = (8L * device_cus() + rows - 1) / rows;
+  long chunk = (p.V + want - 1) / want;
+  chunk = (chunk + step - 1) / step * step;
+  if (chunk > (long)SPECDEC_VG_VPT * step) chunk = (long)SPECDEC_VG_VPT * step;
+  const int splits = (int)((p.V + chunk - 1) / chunk);
   const dim3 grid((unsigned)(rows * splits));
   if (p.vec)
-    hipLaunchKernelGGL((k_verify_greedy<DT, true>), grid, dim3(kBlock), 0, s, p, splits, chunk);
+    hipLaunchKernelGGL((k_verify_greedy<DT, true>), grid, dim3(kBlock), 0, s, p, splits, (int)chunk);
   else
-    hipLaunchKernelGGL((k_verify_greedy<DT, false>), grid, dim3(kBlock), 0, s, p, splits, chunk);
+    hipLaunchKernelGGL((k_verify_greedy<DT, false>), grid, dim3(kBlock), 0, s, p, splits, (int)chunk);
   return hipGetLastError();
 }
 
