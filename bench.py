@@ -35,9 +35,11 @@ REALIGN_SRC = os.path.join(ROOT, "ragged_kv_realignment_amd", "csrc", "realign.h
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64, help="timed chained rounds")
-    ap.add_argument("--warmup", type=int, default=8, help="untimed rounds before the timed chain")
-    ap.add_argument("--config", default="8b-gqa")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed rounds (default: the workload's round count)")
+    ap.add_argument("--warmup", type=int, default=8, help="untimed rounds before the timed ones")
+    ap.add_argument("--config", default="8b-gqa",
+                    help="8b-gqa (default: the B=16 chain the metric is quoted on), 7b-mha, stoch or exspec")
     ap.add_argument("--cpu-rounds", type=int, default=64, help="oracle sample: rounds")
     ap.add_argument("--cpu-layers", type=int, default=36, help="oracle sample: KV layers realigned (scaled to all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -129,29 +131,64 @@ def cpu_baseline(cfg, plans, lens0, width0, tok0, mask0, rounds, layers):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
+def _events(n, k):
+    import torch
+    return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(n)]
+
+
+def _ms(ev, i, j):
+    import numpy as np
+    return np.array([e[i].elapsed_time(e[j]) for e in ev])
+
+
+def copy_calibration(gib, dev):
+    """A plain streaming elementwise kernel of known traffic (reads n bytes, writes
+    n bytes), used to scale the hardware byte counters."""
+    import torch
+    n = int(gib * (1 << 30)) // 4 * 4
+    a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        torch.neg(a, out=b)
+    c1.record()
+    torch.cuda.synchronize()
+    return {"kernel": "torch.neg float32", "read_bytes": n, "write_bytes": n,
+            "copy_gbs": 5 * 2 * n / (c0.elapsed_time(c1) * 1e-3) / 1e9}
+
+
+def _line(metric, value, K, W, ms_per_step, dtype, config, roofline, cpu, extra):
+    line = {"metric": metric, "value": value, "unit": "rounds/s", "n_gpus": 1, "steps": K, "warmup": W,
+            "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic", "config": config, "roofline": roofline}
+    line.update(extra)
+    line["cpu_baseline"] = cpu
+    return line
+
+
+def _roof(kernel, gbs, bytes_per_launch, us, traffic=None):
+    return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": bytes_per_launch,
+            "avg_launch_us": us}
+
+
+def bench_chain(args, cfg):
+    """Chained greedy verify + EQSPEC rounds of a left-padded batch (8b-gqa, 7b-mha)."""
     import numpy as np
     import torch
-
     import synth
     import synth.device as sdev
     import ragged_kv_realignment_amd as sd
 
-    cfg = synth.CONFIGS[args.config]
-    K, W = args.steps, args.warmup
+    K = args.steps if args.steps is not None else cfg.rounds
+    W = args.warmup
     R = max(K, W, 1)
     cap = max(cfg.cap, cfg.len_hi + R * cfg.D1)
-    kv_dt = sdev.TORCH_DT[cfg.kv_dtype]
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
     w = sdev.GreedyRounds(cfg, R)
-    bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, kv_dt) for _ in range(2)]
+    bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, sdev.TORCH_DT[cfg.kv_dtype]) for _ in range(2)]
     ws = sd.workspace(cfg.B, cfg.D)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     acc_hist = torch.zeros((R, cfg.B), dtype=torch.int32, device=dev)
@@ -176,10 +213,8 @@ def main():
     torch.cuda.synchronize()
     w.load_initial(bufs[0])
     torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = _events(K, 3)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     run(K, ev)
     end.record()
@@ -187,85 +222,282 @@ def main():
     total_ms = start.elapsed_time(end)
     if int(status.item()) != 0:
         raise RuntimeError("device status %d during the timed rounds" % int(status.item()))
-    ver_ms = np.array([ev[r][0].elapsed_time(ev[r][1]) for r in range(K)])
-    re_ms = np.array([ev[r][1].elapsed_time(ev[r][2]) for r in range(K)])
-    accs = acc_hist[:K].cpu().numpy()
-    vbytes, rbytes = round_bytes(cfg, w.lens0, w.width0, accs)
-
+    ver_ms, re_ms = _ms(ev, 0, 1), _ms(ev, 1, 2)
+    vbytes, rbytes = round_bytes(cfg, w.lens0, w.width0, acc_hist[:K].cpu().numpy())
     re_gbs = rbytes.sum() / (re_ms.sum() * 1e-3) / 1e9
     ve_gbs = vbytes.sum() / (ver_ms.sum() * 1e-3) / 1e9
-    traffic = traffic_per_launch()
-
-    copy_note = None
+    extra = {}
     if args.copy_calib_gib > 0:
-        # a plain streaming elementwise kernel of known traffic (reads n bytes,
-        # writes n bytes), used to scale the hardware byte counters
-        n = int(args.copy_calib_gib * (1 << 30)) // 4 * 4
-        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(5):
-            torch.neg(a, out=b)
-        c1.record()
-        torch.cuda.synchronize()
-        copy_note = {"kernel": "torch.neg float32", "read_bytes": n, "write_bytes": n,
-                     "copy_gbs": 5 * 2 * n / (c0.elapsed_time(c1) * 1e-3) / 1e9}
-        del a, b
-
+        extra["copy_calibration"] = copy_calibration(args.copy_calib_gib, dev)
     cpu = None
     if not args.no_cpu:
         del bufs
         torch.cuda.empty_cache()
         cpu = cpu_baseline(cfg, w.plans, w.lens0, w.width0, w.tok0, w.mask0, min(args.cpu_rounds, R),
                            args.cpu_layers)
-
-    rounds_per_s = K / (total_ms * 1e-3)
-    line = {
-        "metric": METRIC,
-        "value": rounds_per_s,
-        "unit": "rounds/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": total_ms / K,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "%s: B=%d, D=%d, V=%d %s logits, KV %dx%dx%d %s, lengths U[%d,%d] left-padded, %d chained "
-                        "greedy verify+EQSPEC rounds" % (cfg.name, cfg.B, cfg.D, cfg.V,
-                                                         synth.DTYPE_NAME[cfg.logit_dtype], cfg.L, cfg.H, cfg.Dh,
-                                                         synth.DTYPE_NAME[cfg.kv_dtype], cfg.len_lo, cfg.len_hi, K),
-            "B": cfg.B, "D": cfg.D, "V": cfg.V, "layers": cfg.L, "kv_heads": cfg.H, "head_dim": cfg.Dh,
-            "cap": cap, "global_batch": cfg.B,
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "k_realign_eqspec",
-            "achieved": re_gbs,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": re_gbs / PEAK_HBM_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": float(rbytes.mean()),
-            "avg_launch_us": float(re_ms.mean() * 1e3),
-        },
-        "verify": {
-            "kernel": "k_verify_greedy",
-            "achieved_gbs": ve_gbs,
-            "frac": ve_gbs / PEAK_HBM_GBS,
-            "algorithmic_bytes_per_launch": float(vbytes.mean()),
-            "avg_launch_us": float(ver_ms.mean() * 1e3),
-        },
+    extra.update({
+        "verify": {"kernel": "k_verify_greedy", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
+                   "algorithmic_bytes_per_launch": float(vbytes.mean()), "avg_launch_us": float(ver_ms.mean() * 1e3)},
         "realign_share_of_round": float(re_ms.sum() / total_ms),
-        "cpu_baseline": cpu,
+    })
+    config = {
+        "workload": "%s: B=%d, D=%d, V=%d %s logits, KV %dx%dx%d %s, lengths U[%d,%d] left-padded, %d chained "
+                    "greedy verify+EQSPEC rounds" % (cfg.name, cfg.B, cfg.D, cfg.V, synth.DTYPE_NAME[cfg.logit_dtype],
+                                                     cfg.L, cfg.H, cfg.Dh, synth.DTYPE_NAME[cfg.kv_dtype], cfg.len_lo,
+                                                     cfg.len_hi, K),
+        "B": cfg.B, "D": cfg.D, "V": cfg.V, "layers": cfg.L, "kv_heads": cfg.H, "head_dim": cfg.Dh, "cap": cap,
+        "global_batch": cfg.B,
     }
-    if copy_note:
-        line["copy_calibration"] = copy_note
+    traffic = traffic_per_launch() if cfg.name == "8b-gqa" and K == 64 and W == 8 else None
+    metric = METRIC if cfg.name == "8b-gqa" else METRIC.replace("at B=16", "at B=%d (%s)" % (cfg.B, cfg.name))
+    return _line(metric, K / (total_ms * 1e-3), K, W, total_ms / K, synth.DTYPE_NAME[cfg.kv_dtype], config,
+                 _roof("k_realign_eqspec", re_gbs, float(rbytes.mean()), float(re_ms.mean() * 1e3), traffic), cpu,
+                 extra)
+
+
+def bench_stoch(args, cfg):
+    """Sampled verification + EQSPEC realign of the fp16 cache; the same out-of-place
+    round is repeated from the same state."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    import synth.device as sdev
+    import ragged_kv_realignment_amd as sd
+
+    K = args.steps if args.steps is not None else 16
+    W = args.warmup
+    dev = torch.device("cuda", 0)
+    tdt = sdev.TORCH_DT[cfg.kv_dtype]
+    lens = synth.lengths(cfg)
+    S = int(lens.max())
+    p, q, draft, u_acc, u_draw = synth.sampled_round(cfg, 0)
+    src = sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cfg.cap, cfg.Dh, tdt)
+    dst = sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cfg.cap, cfg.Dh, tdt)
+    sdev.fill_kv(cfg, src.kv, torch.from_numpy(lens).to(dev), S, True)
+    tok, pos, mask = synth.tokens_host(cfg, lens, S, True)
+    src.tokens.copy_(torch.from_numpy(tok))
+    src.pos.copy_(torch.from_numpy(pos))
+    src.mask.copy_(torch.from_numpy(mask))
+    src.len.copy_(torch.from_numpy(lens))
+    src.width.fill_(S)
+    kv_new = torch.empty((cfg.L, 2, cfg.B, cfg.H, cfg.D1, cfg.Dh), dtype=tdt, device=dev)
+    sdev.fill_kvnew(cfg, 0, kv_new)
+    dp, dq, dd, dua, dud = (torch.from_numpy(x).to(dev) for x in (p, q, draft, u_acc, u_draw))
+    acc = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(n, ev=None):
+        for r in range(n):
+            if ev:
+                ev[r][0].record()
+            sd.verify_sample(dp, dq, dd, dua, dud, status=status, accept_len=acc, next_token=nxt)
+            if ev:
+                ev[r][1].record()
+            sd.realign_eqspec(src, dst, kv_new, dd, acc, nxt, status=status)
+            if ev:
+                ev[r][2].record()
+
+    run(W)
+    torch.cuda.synchronize()
+    ev = _events(K, 3)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run(K, ev)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    if int(status.item()) != 0:
+        raise RuntimeError("device status %d during the timed rounds" % int(status.item()))
+    ver_ms, re_ms = _ms(ev, 0, 1), _ms(ev, 1, 2)
+    a = acc.cpu().numpy()
+    # sampled verify reads the accepted drafts' p(x), q(x) and one residual (p, q rows) or bonus (p row)
+    vbytes = float(sum(16 * min(int(x) + 1, cfg.D) + (8 if x < cfg.D else 4) * cfg.V + 12 for x in a))
+    _, rb = round_bytes(cfg, lens, S, a[None, :])
+    rbytes = float(rb[0])
+    re_gbs = rbytes / (re_ms.mean() * 1e-3) / 1e9
+    ve_gbs = vbytes / (ver_ms.mean() * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        del src, dst
+        torch.cuda.empty_cache()
+        layers = min(args.cpu_layers, 2)
+        kv_l = synth.kv_host(cfg, lens, S, True, layer0=0, nlayers=layers)
+        kvn_l = synth.kvnew_host(cfg, 0, layer0=0, nlayers=layers)
+        out = np.empty_like(kv_l)
+        reps = 4
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oacc, onxt, _ = oracle.verify_sample(p, q, draft, u_acc, u_draw)
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            oracle.realign_eqspec(kv_l, kvn_l, lens, S, tok, mask, oacc, onxt, draft, kv_out=out)
+        t2 = time.perf_counter()
+        per = ((t1 - t0) + (t2 - t1) * cfg.L / layers) / reps
+        cpu = {"value": 1.0 / per, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+               "sample": "%d repeats of the round: sampled verify of all %d rows (%.1f ms) and EQSPEC realign of "
+                         "layers 0-%d of %d (%.1f ms), realign scaled by %d/%d; single-threaded C oracle"
+                         % (reps, cfg.B, 1e3 * (t1 - t0) / reps, layers - 1, cfg.L, 1e3 * (t2 - t1) / reps, cfg.L,
+                            layers), "host_cpus": os.cpu_count()}
+    config = {"workload": "stoch: B=%d, D=%d, V=%d fp32 p/q (softmax(l/0.8)), KV %dx%dx%d fp16, lengths U[%d,%d], "
+                          "one sampled verify + EQSPEC round repeated" % (cfg.B, cfg.D, cfg.V, cfg.L, cfg.H, cfg.Dh,
+                                                                         cfg.len_lo, cfg.len_hi),
+              "B": cfg.B, "D": cfg.D, "V": cfg.V, "cap": cfg.cap, "global_batch": cfg.B}
+    extra = {"verify": {"kernel": "k_verify_sample", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
+                        "algorithmic_bytes_per_launch": vbytes, "avg_launch_us": float(ver_ms.mean() * 1e3)},
+             "realign_share_of_round": float(re_ms.sum() / total_ms)}
+    return _line("sampled verify+realign rounds/sec and realign HBM GB/s (stoch, B=32)", K / (total_ms * 1e-3), K, W,
+                 total_ms / K, "f16", config,
+                 _roof("k_realign_eqspec", re_gbs, rbytes, float(re_ms.mean() * 1e3)), cpu, extra)
+
+
+def bench_exspec(args, cfg):
+    """Pool rounds: group by length, gather mixed batches, verify every sequence,
+    append committed entries in place."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    import synth.device as sdev
+    import ragged_kv_realignment_amd as sd
+
+    K = args.steps if args.steps is not None else cfg.rounds
+    W = 0  # rounds change the pool; the timed chain starts from the initial pool
+    N, G = cfg.B, cfg.group
+    dev = torch.device("cuda", 0)
+    tdt = sdev.TORCH_DT[cfg.kv_dtype]
+    cap = max(cfg.cap, cfg.len_hi + K * cfg.D1)
+    lens0 = synth.lengths(cfg)
+    pool = sd.SeqBuf.empty(cfg.L, N, cfg.H, cap, cfg.Dh, tdt, pool=True)
+    sdev.fill_kv(cfg, pool.kv, torch.from_numpy(lens0).to(dev), 0, False)
+    tok0, _, _ = synth.tokens_host(cfg, lens0, 0, False, cap=cap)
+    pool.tokens.copy_(torch.from_numpy(tok0))
+    pool.len.copy_(torch.from_numpy(lens0))
+    ng = (N + G - 1) // G
+    rect = sd.SeqBuf.empty(cfg.L, N, cfg.H, cap, cfg.Dh, tdt, groups=ng)
+    plans = [synth.plan_greedy(cfg, r) for r in range(K)]
+    logits = torch.empty((K, N, cfg.D1, cfg.V), dtype=sdev.TORCH_DT[cfg.logit_dtype], device=dev)
+    keep = [sdev.fill_logits(cfg, r, plans[r][0], logits[r]) for r in range(K)]
+    kv_new = torch.empty((K, cfg.L, 2, N, cfg.H, cfg.D1, cfg.Dh), dtype=tdt, device=dev)
+    for r in range(K):
+        sdev.fill_kvnew(cfg, r, kv_new[r])
+    drafts = torch.from_numpy(np.stack([pl[2] for pl in plans])).to(dev)
+    ws = sd.workspace(N, cfg.D)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    acc_h = torch.zeros((K, N), dtype=torch.int32, device=dev)
+    nxt_h = torch.zeros((K, N), dtype=torch.int32, device=dev)
+    lens_h = torch.zeros((K, N), dtype=torch.int32, device=dev)
+    groups = []
+    torch.cuda.synchronize()
+    del keep
+    ev = _events(K, 5)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for r in range(K):
+        ev[r][0].record()
+        order, uni, wid, nu = sd.group_by_len(pool.len, G)
+        ev[r][1].record()
+        sd.gather(pool, rect, order, G, uni, status=status)
+        ev[r][2].record()
+        sd.verify_greedy(logits[r], drafts[r], ws=ws, status=status, accept_len=acc_h[r], next_token=nxt_h[r])
+        ev[r][3].record()
+        sd.append(pool, kv_new[r], drafts[r], acc_h[r], nxt_h[r], status=status)
+        ev[r][4].record()
+        groups.append((order, uni, wid))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    if int(status.item()) != 0:
+        raise RuntimeError("device status %d during the timed rounds" % int(status.item()))
+    g_ms, ga_ms, v_ms, ap_ms = _ms(ev, 0, 1), _ms(ev, 1, 2), _ms(ev, 2, 3), _ms(ev, 3, 4)
+    P = cfg.kv_pos_bytes
+    lens = lens0.astype(np.int64).copy()
+    gbytes, abytes, mixed = [], [], []
+    accs = acc_h.cpu().numpy()
+    for r in range(K):
+        order, uni, wid = (t.cpu().numpy() for t in groups[r])
+        gb = 0
+        for g in range(ng):
+            if uni[g]:
+                continue
+            rows = order[g * G:(g + 1) * G]
+            gb += P * (int(lens[rows].sum()) + len(rows) * int(wid[g]))
+        gbytes.append(gb)
+        mixed.append(int((uni == 0).sum()))
+        n = accs[r].astype(np.int64) + 1
+        abytes.append(2 * P * int(n.sum()))
+        lens = lens + n
+    gbytes = np.array(gbytes, dtype=np.float64)
+    vbytes = N * cfg.D1 * cfg.V * 2 + N * cfg.D * 4 + 8 * N
+    ga_gbs = gbytes.sum() / (ga_ms.sum() * 1e-3) / 1e9 if gbytes.sum() > 0 else 0.0
+    cpu = None
+    if not args.no_cpu:
+        del pool, rect, logits, kv_new
+        torch.cuda.empty_cache()
+        cpu = cpu_exspec(cfg, plans, lens0, min(args.cpu_rounds, K, 4))
+    config = {"workload": "exspec: pool of %d sequences, batches of %d, D=%d, V=%d bf16 logits, KV %dx%dx%d bf16, 16 "
+                          "distinct lengths in [512,4096], %d rounds" % (N, G, cfg.D, cfg.V, cfg.L, cfg.H, cfg.Dh, K),
+              "pool": N, "group": G, "D": cfg.D, "V": cfg.V, "cap": cap, "global_batch": N}
+    extra = {"verify": {"kernel": "k_verify_greedy", "achieved_gbs": vbytes / (v_ms.mean() * 1e-3) / 1e9,
+                        "avg_launch_us": float(v_ms.mean() * 1e3)},
+             "group_us": float(g_ms.mean() * 1e3), "append_us": float(ap_ms.mean() * 1e3),
+             "append_gbs": float(np.sum(abytes) / (ap_ms.sum() * 1e-3) / 1e9),
+             "gather_us": float(ga_ms.mean() * 1e3), "mixed_batches_per_round": mixed,
+             "realign_share_of_round": float((ga_ms.sum() + g_ms.sum()) / total_ms)}
+    return _line("EXSPEC pool rounds/sec and gather HBM GB/s (256-sequence pool)", K / (total_ms * 1e-3), K, W,
+                 total_ms / K, "bf16", config,
+                 _roof("k_gather", ga_gbs, float(gbytes.mean()), float(ga_ms.mean() * 1e3)), cpu, extra)
+
+
+def cpu_exspec(cfg, plans, lens0, rounds):
+    """The oracle on the first rounds of the pool chain: grouping, verification of
+    all sequences, gather and append of layer 0, scaled to all layers."""
+    import numpy as np
+    import oracle
+    import synth
+    N, G = cfg.B, cfg.group
+    kv = synth.kv_host(cfg, lens0, 0, False, layer0=0, nlayers=1)
+    tok, _, _ = synth.tokens_host(cfg, lens0, 0, False)
+    lens = lens0.copy()
+    t_fix = t_lay = 0.0
+    for r in range(rounds):
+        plant, _, draft = plans[r]
+        lg = synth.logits_host(cfg, r, plant)
+        kvn = synth.kvnew_host(cfg, r, layer0=0, nlayers=1)
+        t0 = time.perf_counter()
+        order, uni, wid, nu = oracle.group_by_len(lens, G)
+        acc, nxt, _ = oracle.verify_greedy(lg, draft, N, cfg.D, cfg.V)
+        t1 = time.perf_counter()
+        oracle.gather(kv, tok, lens, order, G, uni, cfg.cap)
+        oracle.append(kv, tok, lens, np.arange(N), kvn, draft, acc, nxt)
+        t2 = time.perf_counter()
+        t_fix += t1 - t0
+        t_lay += t2 - t1
+    per = (t_fix + t_lay * cfg.L) / rounds
+    return {"value": 1.0 / per, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": "rounds 0-%d of the pool chain: grouping and greedy verify of all %d sequences (%.1f ms/round), "
+                      "gather + append of layer 0 (%.1f ms/round) scaled by %d layers; single-threaded C oracle"
+                      % (rounds - 1, N, 1e3 * t_fix / rounds, 1e3 * t_lay / rounds, cfg.L),
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    if cfg.name == "stoch":
+        line = bench_stoch(args, cfg)
+    elif cfg.name == "exspec":
+        line = bench_exspec(args, cfg)
+    else:
+        line = bench_chain(args, cfg)
     print(json.dumps(line), flush=True)
 
 

@@ -227,15 +227,58 @@ __device__ __forceinline__ double resid(const float *pa, const float *qa, int v)
   return d > 0.0 ? d : 0.0;
 }
 
-// One workgroup per row b.  Thread t owns the contiguous ids [t*K, t*K+K): its
-// partial mass, an exclusive scan of the partials in id order, then the thread
-// whose range crosses u*T walks its ids.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Residual masses w of ids v0 .. v0+VW-1 (0 past V).  VW = 4 reads 16-byte vectors.
+template <int VW>
+__device__ __forceinline__ void load_w(const float *pa, const float *qa, int v0, int V, double *w) {
+  if constexpr (VW == 4) {
+    if (v0 + 4 <= V) {
+      const f32x4 pp = *reinterpret_cast<const f32x4 *>(pa + v0);
+      f32x4 qq = (f32x4)(0.0f);
+      if (qa) qq = *reinterpret_cast<const f32x4 *>(qa + v0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double d = qa ? (double)pp[e] - (double)qq[e] : (double)pp[e];
+        w[e] = d > 0.0 ? d : 0.0;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VW; ++e) w[e] = (v0 + e < V) ? resid(pa, qa, v0 + e) : 0.0;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// One workgroup per row b.  Each wave owns a contiguous quarter of the row and
+// reads it in chunks of 64 lanes x VW consecutive ids (coalesced).  Pass 1: the
+// fp64 mass of each quarter and the block total T; the draw target u*T falls in
+// the quarter whose running mass first exceeds it, which that wave re-walks
+// chunk by chunk with an fp64 wave scan.  Several waves may claim the crossing
+// when rounding puts u*T at a quarter boundary; the lowest id wins.
+template <int VW>
 __global__ __launch_bounds__(kBlock) void k_verify_sample(SampleParams p) {
+  constexpr int NW = kBlock / kWave;
+  constexpr int CH = kWave * VW;
   const int b = blockIdx.x;
   const int D = p.D, D1 = p.D + 1, V = p.V;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   __shared__ int s_a, s_bad, s_j, s_lastpos;
-  __shared__ double s_part[kBlock];
-  __shared__ double s_T;
+  __shared__ double s_wt[NW];
   if (threadIdx.x == 0) { s_a = D; s_bad = 0; s_j = INT_MAX; s_lastpos = -1; }
   __syncthreads();
   for (int i = threadIdx.x; i < D; i += kBlock) {
@@ -255,30 +298,44 @@ __global__ __launch_bounds__(kBlock) void k_verify_sample(SampleParams p) {
   const int a = s_a;
   const float *pa = p.p + ((size_t)b * D1 + a) * V;
   const float *qa = a < D ? p.q + ((size_t)b * D + a) * V : nullptr;
-  const int K = (V + kBlock - 1) / kBlock;
-  const int lo = min(V, (int)threadIdx.x * K), hi = min(V, lo + K);
+  const int nchunks = (V + CH - 1) / CH;
+  const int per = (nchunks + NW - 1) / NW;
+  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
 
-  double T = 0.0, mine = 0.0, before = 0.0;
+  double T = 0.0, before = 0.0, mine = 0.0;
   for (int pass = 0; pass < 2; ++pass) {
-    mine = 0.0;
-    for (int v = lo; v < hi; ++v) mine += resid(pa, qa, v);
-    s_part[threadIdx.x] = mine;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double run = 0.0;
-      for (int t = 0; t < kBlock; ++t) {
-        const double x = s_part[t];
-        s_part[t] = run;
-        run += x;
+    double acc = 0.0;
+    int lastpos = -1;
+    for (int c = c0; c < c1; ++c) {
+      double w[VW];
+      const int v0 = c * CH + lane * VW;
+      load_w<VW>(pa, qa, v0, V, w);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        acc += w[e];
+        if (w[e] > 0.0) lastpos = v0 + e;
       }
-      s_T = run;
+    }
+    mine = wave_sum(acc);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) lastpos = max(lastpos, __shfl_xor(lastpos, off));
+    if (lane == 0) {
+      s_wt[wave] = mine;
+      if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
     }
     __syncthreads();
-    T = s_T;
-    before = s_part[threadIdx.x];
+    T = 0.0;
+    before = 0.0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      if (k < wave) before += s_wt[k];
+      T += s_wt[k];
+    }
     __syncthreads();
     if (T > 0.0 || qa == nullptr) break;
     qa = nullptr;  // zero residual mass: fall back to p at this position
+    if (threadIdx.x == 0) s_lastpos = -1;
+    __syncthreads();
   }
 
   int j = 0;
@@ -286,15 +343,32 @@ __global__ __launch_bounds__(kBlock) void k_verify_sample(SampleParams p) {
     const double target = (double)p.u_draw[(size_t)b * D1 + a] * T;
     if (before + mine > target) {
       double run = before;
-      for (int v = lo; v < hi; ++v) {
-        run += resid(pa, qa, v);
-        if (run > target) { atomicMin(&s_j, v); break; }
+      for (int c = c0; c < c1; ++c) {
+        double w[VW];
+        const int v0 = c * CH + lane * VW;
+        load_w<VW>(pa, qa, v0, V, w);
+        double sl = 0.0;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) sl += w[e];
+        const double incl = wave_incl_scan(sl, lane);
+        const double chunk_total = __shfl(incl, kWave - 1);
+        if (run + chunk_total > target) {
+          // the crossing lies in this chunk: the first lane whose ids reach past u*T
+          double cum = run + incl - sl;
+          int cand = INT_MAX;
+#pragma unroll
+          for (int e = 0; e < VW; ++e) {
+            cum += w[e];
+            if (cand == INT_MAX && cum > target) cand = v0 + e;
+          }
+#pragma unroll
+          for (int off = kWave / 2; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off));
+          if (lane == 0 && cand != INT_MAX) atomicMin(&s_j, cand);
+          if (cand != INT_MAX) break;
+        }
+        run += chunk_total;
       }
     }
-    int lastpos = -1;
-    for (int v = hi - 1; v >= lo; --v)
-      if (resid(pa, qa, v) > 0.0) { lastpos = v; break; }
-    if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
     __syncthreads();
     j = s_j != INT_MAX ? s_j : s_lastpos;
   } else if (threadIdx.x == 0) {
@@ -309,7 +383,12 @@ __global__ __launch_bounds__(kBlock) void k_verify_sample(SampleParams p) {
 }
 
 hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_verify_sample, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  const bool vec = p.V % 4 == 0 && reinterpret_cast<uintptr_t>(p.p) % 16 == 0 &&
+                   (p.q == nullptr || reinterpret_cast<uintptr_t>(p.q) % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL(k_verify_sample<4>, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_verify_sample<1>, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
