@@ -37,11 +37,14 @@ constexpr int kMaxB = 1024;
 #ifndef SPECDEC_RA_BLOCK
 #define SPECDEC_RA_BLOCK 1024    // threads per realign workgroup
 #endif
+#ifndef SPECDEC_RA_TILES_PER_WG
+#define SPECDEC_RA_TILES_PER_WG 2  // EQSPEC grid: tiles of the widest possible output per workgroup
+#endif
+#ifndef SPECDEC_GA_TILES_PER_WG
+#define SPECDEC_GA_TILES_PER_WG 8  // GATHER grid: tiles per workgroup if every group were gathered
+#endif
 #ifndef SPECDEC_RA_PASSES
 #define SPECDEC_RA_PASSES 4      // positions per thread per tile
-#endif
-#ifndef SPECDEC_RA_WG_PER_CU
-#define SPECDEC_RA_WG_PER_CU 128 // workgroups per CU in the grid (0: one tile per workgroup)
 #endif
 #ifndef SPECDEC_RA_INTERLEAVE
 #define SPECDEC_RA_INTERLEAVE 1  // tile t -> workgroup t mod grid (1) or contiguous ranges (0)
@@ -291,8 +294,10 @@ __global__ __launch_bounds__(kRaBlock) void k_gather(RealignParams p) {
   __shared__ int s_c[kMaxB];
   __shared__ int s_W[kMaxB];
   __shared__ int s_act[kMaxB];
+  __shared__ int s_gpre[kMaxB];
   __shared__ int s_nact;
   __shared__ int s_red[kRaBlock / kWave];
+  __shared__ int s_red2[kRaBlock / kWave];
   const int B = p.B, G = p.group, U = p.units, H = p.heads;
   const int ng = (B + G - 1) / G;
   int bad = 0;
@@ -317,17 +322,34 @@ __global__ __launch_bounds__(kRaBlock) void k_gather(RealignParams p) {
       if (W > p.cap_out) bad |= SPECDEC_S_CAPACITY;
     }
   }
-  const int Wmax = block_max_int<kRaBlock>(wmax, s_red);
-  bad = block_or_int<kRaBlock>(bad, s_red);
+  int Wmax;
+  block_max_or(wmax, bad, s_red, s_red2, Wmax, bad);
   if (bad) {
     if (blockIdx.x == 0 && threadIdx.x == 0) set_status(p.status, bad);
     return;
   }
-  if (threadIdx.x == 0) {
-    int k = 0;
-    for (int j = 0; j < B; ++j)
-      if (s_W[j / G] >= 0) s_act[k++] = j;
-    s_nact = k;
+  // compact the entries of the gathered groups: exclusive prefix of the groups'
+  // entry counts (wave 0, 64 groups per step), then every entry places itself
+  if (threadIdx.x < kWave) {
+    int carry = 0;
+    for (int g0 = 0; g0 < ng; g0 += kWave) {
+      const int g = g0 + (int)threadIdx.x;
+      const int cnt = (g < ng && s_W[g] >= 0) ? min(B, g * G + G) - g * G : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if ((int)threadIdx.x >= off) incl += y;
+      }
+      if (g < ng) s_gpre[g] = carry + incl - cnt;
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (threadIdx.x == 0) s_nact = carry;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < B; j += kRaBlock) {
+    const int g = j / G;
+    if (s_W[g] >= 0) s_act[s_gpre[g] + (j - g * G)] = j;
   }
   __syncthreads();
   const int nact = s_nact;
@@ -467,20 +489,22 @@ __global__ __launch_bounds__(kRaBlock) void k_append_meta(RealignParams p) {
 }
 
 hipError_t launch_realign(const RealignParams &p, hipStream_t s) {
-  int grid = SPECDEC_RA_WG_PER_CU * device_cus();
+  const int cus = device_cus();
+  // tiles of the widest output the buffers allow (the true width is known only
+  // on the device); workgroups past the real tile count find no tile
+  const long tp = (long)(kRaBlock / p.units) * kPasses;
+  const long seqs = (long)p.layers * 2 * p.B * p.heads;
+  const long tiles_max = seqs * ((p.cap_out + tp - 1) / tp);
+  int grid = 8 * cus;
   if (p.mode == SPECDEC_EQSPEC) {
-    if (SPECDEC_RA_WG_PER_CU == 0) {
-      // one tile per workgroup: enough workgroups for the widest possible output
-      const long tp = (long)(kRaBlock / p.units) * kPasses;
-      const long tiles = (long)p.layers * 2 * p.B * p.heads * ((p.cap_out + tp - 1) / tp);
-      grid = (int)(tiles > p.B ? tiles : p.B);
-    }
+    const long g = (tiles_max + SPECDEC_RA_TILES_PER_WG - 1) / SPECDEC_RA_TILES_PER_WG;
+    if (g > grid) grid = (int)(g < (1L << 30) ? g : (1L << 30));
     hipLaunchKernelGGL(k_realign_eqspec, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else if (p.mode == SPECDEC_GATHER) {
-    if (grid == 0) grid = 256 * device_cus();
+    const long g = (tiles_max + SPECDEC_GA_TILES_PER_WG - 1) / SPECDEC_GA_TILES_PER_WG;
+    if (g > grid) grid = (int)(g < (1L << 30) ? g : (1L << 30));
     hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else {
-    if (grid == 0) grid = 8 * device_cus();
     const long ups = (long)(p.D + 1) * p.units;
     const long spp = ups < kRaBlock ? kRaBlock / ups : 1;
     const long nseg = ((long)p.layers * 2 * p.B * p.heads + spp - 1) / spp;

@@ -67,6 +67,7 @@ __device__ __forceinline__ int first_eq(u32x4 r, float M) {
 #define SPECDEC_VG_VPT 4
 #endif
 
+
 // One workgroup scans `chunk` ids of one logit row (row = b*(D+1) + i): every
 // thread issues all its 16-byte loads before consuming any, the workgroup
 // reduces to one (value, id), and thread 0 folds it into the row's 64-bit key
@@ -76,11 +77,10 @@ __device__ __forceinline__ int first_eq(u32x4 r, float M) {
 // coherence point; the keys are read back with device-scope atomic loads).  The
 // last workgroup of row-block b reads the D+1 keys in parallel, runs the
 // first-mismatch scan and leaves keys and counter zeroed for the next call.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int splits, int chunk) {
+template <int DT, bool VEC, int NT, int VPT>
+__global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits, int chunk) {
   constexpr int ES = Elem<DT>::size;
   constexpr int VW = 16 / ES;
-  constexpr int VPT = SPECDEC_VG_VPT;
   const int wg = blockIdx.x;
   const int row = wg / splits;
   const int split = wg - row * splits;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int sp
   const char *rowp = static_cast<const char *>(p.logits) + (size_t)row * (size_t)p.row_stride * ES;
 
   // 1. every thread's largest value; all of its vector loads are issued before
-  //    any is used (one workgroup pass covers the chunk: chunk <= VPT*kBlock*VW)
+  //    any is used (one workgroup pass covers the chunk: chunk <= VPT*NT*VW)
   float m = -INFINITY;
   u32x4 r[VPT];
   float tail_x = -INFINITY;
@@ -104,10 +104,10 @@ __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int sp
     if (nvec > 0) {
 #pragma unroll
       for (int u = 0; u < VPT; ++u)  // indices past the end re-read the last vector and are ignored
-        r[u] = __builtin_nontemporal_load(vp + min(u * kBlock + (int)threadIdx.x, nvec - 1));
+        r[u] = __builtin_nontemporal_load(vp + min(u * NT + (int)threadIdx.x, nvec - 1));
 #pragma unroll
       for (int u = 0; u < VPT; ++u)
-        if (u * kBlock + (int)threadIdx.x < nvec) m = fmaxf(m, vmax<DT>(r[u]));
+        if (u * NT + (int)threadIdx.x < nvec) m = fmaxf(m, vmax<DT>(r[u]));
     }
     const int tv = start + nvec * VW + threadIdx.x;  // ragged last vector of the row
     if (tv < end) {
@@ -116,13 +116,13 @@ __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int sp
       m = fmaxf(m, tail_x);
     }
   } else {
-    for (int v = start + threadIdx.x; v < end; v += kBlock) m = fmaxf(m, load_scalar<DT>(rowp, v));
+    for (int v = start + threadIdx.x; v < end; v += NT) m = fmaxf(m, load_scalar<DT>(rowp, v));
   }
-  __shared__ float s_f[kBlock / kWave];
-  __shared__ int s_i[kBlock / kWave];
+  __shared__ float s_f[NT / kWave];
+  __shared__ int s_i[NT / kWave];
   __shared__ int s_last, s_a, s_bad;
-  __shared__ int s_t[kBlock];
-  const float M = block_max_float(m, s_f);
+  __shared__ int s_t[NT];
+  const float M = block_max_float<NT>(m, s_f);
 
   // 2. the lowest id holding M: only threads whose own maximum is M look
   int bi = INT_MAX;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int sp
     if constexpr (VEC) {
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int k = u * kBlock + (int)threadIdx.x;
+        const int k = u * NT + (int)threadIdx.x;
         if (bi == INT_MAX && k < nvec) {
           const int at = first_eq<DT>(r[u], M);
           if (at < VW) bi = start + k * VW + at;
@@ -138,11 +138,11 @@ __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int sp
       }
       if (bi == INT_MAX && tail_id >= 0 && tail_x == M) bi = tail_id;
     } else {
-      for (int v = start + threadIdx.x; v < end; v += kBlock)
+      for (int v = start + threadIdx.x; v < end; v += NT)
         if (load_scalar<DT>(rowp, v) == M) { bi = v; break; }
     }
   }
-  bi = block_min_int(bi, s_i);
+  bi = block_min_int<NT>(bi, s_i);
   if (threadIdx.x == 0) {
     const unsigned long long old = atomicMax(&p.keys[row], argmax_key(M, bi));
     // opaque zero computed from the atomic's result: the counter update below
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void k_verify_greedy(GreedyParams p, int sp
   }
   __syncthreads();
   if (!s_last) return;
-  // D + 1 <= kBlock (checked on the host): one position per thread
+  // D + 1 <= NT (checked on the host): one position per thread
   const int i = threadIdx.x;
   if (i < D1) {
     unsigned long long *kp = &p.keys[(size_t)b * D1 + i];
@@ -197,20 +197,23 @@ int device_cus() {
 template <int DT>
 static hipError_t launch_greedy_dt(const GreedyParams &p, hipStream_t s) {
   constexpr int VW = 16 / Elem<DT>::size;
-  constexpr int step = kBlock * VW;  // ids covered by one vector per thread
   const long rows = (long)p.B * (p.D + 1);
+  const int cus = device_cus();
+  constexpr int step = kBlock * VW;  // ids covered by one vector per thread
   // Aim at ~8 workgroups per CU; a workgroup covers between one and
   // SPECDEC_VG_VPT vectors per thread, all loaded before any is consumed.
-  const long want = (8L * device_cus() + rows - 1) / rows;
+  const long want = (8L * cus + rows - 1) / rows;
   long chunk = (p.V + want - 1) / want;
   chunk = (chunk + step - 1) / step * step;
   if (chunk > (long)SPECDEC_VG_VPT * step) chunk = (long)SPECDEC_VG_VPT * step;
   const int splits = (int)((p.V + chunk - 1) / chunk);
   const dim3 grid((unsigned)(rows * splits));
   if (p.vec)
-    hipLaunchKernelGGL((k_verify_greedy<DT, true>), grid, dim3(kBlock), 0, s, p, splits, (int)chunk);
+    hipLaunchKernelGGL((k_verify_greedy<DT, true, kBlock, SPECDEC_VG_VPT>), grid, dim3(kBlock), 0, s, p, splits,
+                       (int)chunk);
   else
-    hipLaunchKernelGGL((k_verify_greedy<DT, false>), grid, dim3(kBlock), 0, s, p, splits, (int)chunk);
+    hipLaunchKernelGGL((k_verify_greedy<DT, false, kBlock, SPECDEC_VG_VPT>), grid, dim3(kBlock), 0, s, p, splits,
+                       (int)chunk);
   return hipGetLastError();
 }
 
