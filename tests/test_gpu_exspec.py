@@ -28,7 +28,7 @@ def sd():
 def test_group_by_len_random(sd, seed):
     rng = np.random.default_rng(900 + seed)
     N = [0, 1, 7, 256, 1000, 4096, 300, 64, 513, 2048][seed]
-    G = int(rng.integers(1, 17))
+    G = [1, 17, 4000][seed % 3] if seed in (1, 2, 7) else int(rng.integers(1, 17))
     lens = rng.integers(1, int(rng.integers(2, 40)), N).astype(np.int32)
     say("group_by_len", N, G)
     order, uni, wid, nu = sd.group_by_len(torch.from_numpy(lens).cuda(), G)

@@ -300,3 +300,47 @@ def test_stochastic_round_realign(sd):
     assert int(dst.width.item()) == W
     for k in ("tokens", "pos", "mask"):
         assert np.array_equal(getattr(dst, k).cpu().numpy()[:, :W], out[k][:, :W]), k
+
+
+@pytest.mark.parametrize("shape", [
+    # B, D, L, H, Dh, dtype, cap: the largest batch, the widest position, an odd number of 16-byte units
+    (1024, 3, 1, 1, 8, np.float16, 14),
+    (3, 2, 1, 1, 1024, np.float32, 10),
+    (5, 4, 2, 3, 96, np.float16, 40),
+    (7, 0, 1, 2, 8, np.float32, 9),
+])
+def test_eqspec_limits(sd, shape):
+    B, D, L, H, Dh, dt_np, cap = shape
+    tdt = torch.float16 if dt_np == np.float16 else torch.float32
+    rng = np.random.default_rng(B + Dh)
+    lens = rng.integers(0, cap - D - 1, B).astype(np.int32)
+    S = int(lens.max())
+    say("eqspec limits", shape)
+    kv = np.zeros((L, 2, B, H, cap, Dh), dt_np)
+    tok = np.zeros((B, cap), np.int32)
+    pos = np.zeros((B, cap), np.int32)
+    mask = np.zeros((B, cap), np.int8)
+    for b in range(B):
+        pad = S - lens[b]
+        kv[:, :, b, :, pad:S] = rng.standard_normal((L, 2, H, lens[b], Dh))
+        tok[b, pad:S] = rng.integers(1, 99, lens[b])
+        mask[b, pad:S] = 1
+        pos[b, pad:S] = np.arange(lens[b])
+    kv_new = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(dt_np)
+    acc = rng.integers(0, D + 1, B).astype(np.int32)
+    draft = rng.integers(1, 99, (B, D)).astype(np.int32)
+    nxt = rng.integers(1, 99, B).astype(np.int32)
+    src = _device_rect(sd, kv, tok, pos, mask, lens, S, tdt)
+    dst = sd.SeqBuf.empty(L, B, H, cap, Dh, tdt)
+    _poison(dst)
+    sd.realign_eqspec(src, dst, from_np_raw(kv_new, tdt), torch.from_numpy(draft).cuda(), torch.from_numpy(acc).cuda(),
+                      torch.from_numpy(nxt).cuda())
+    torch.cuda.synchronize()
+    want = oracle.realign_eqspec(kv, kv_new, lens, S, tok, mask, acc, nxt, draft, cap_out=cap)
+    W = want["width"]
+    assert int(dst.width.item()) == W
+    gkv = to_np_raw(dst.kv)
+    assert bytes_equal(gkv[..., :W, :], want["kv"][..., :W, :])
+    assert np.all(gkv[..., W:, :].view(np.uint8) == CANARY_KV)
+    for name in ("tokens", "pos", "mask"):
+        assert np.array_equal(getattr(dst, name).cpu().numpy()[:, :W], want[name][:, :W]), name

@@ -249,3 +249,20 @@ def test_sample_zero_row_status(sd):
     oacc, onxt, _ = oracle.verify_sample(*args)
     assert acc.item() == oacc[0] == 0 and nxt.item() == onxt[0] == 0
     assert int(status.item()) & sd.S_PROB
+
+
+def test_greedy_longest_draft(sd):
+    """D = 255, the longest draft the kernel accepts (D + 1 = 256 positions)."""
+    say("greedy D=255")
+    B, D, V = 2, 255, 300
+    rng = np.random.default_rng(255)
+    rows = rng.standard_normal((B * (D + 1), V)).astype(np.float32)
+    t = np.argmax(rows.reshape(B, D + 1, V), axis=-1)
+    draft = t[:, :D].copy().astype(np.int32)
+    draft[1, 200] = (draft[1, 200] + 1) % V
+    acc, nxt, tgt, _ = _gpu_greedy(sd, rows, torch.float32, B, D, V, draft)
+    oacc, onxt, otgt = oracle.verify_greedy(rows, draft, B, D, V)
+    assert list(oacc) == [255, 200]
+    assert np.array_equal(tgt, otgt) and np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
+    with pytest.raises(sd.SpecDecError):  # D = 256 is past the limit
+        _gpu_greedy(sd, np.zeros((2 * 257, V), np.float32), torch.float32, 2, 256, V, np.zeros((2, 256), np.int32))
