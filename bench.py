@@ -28,8 +28,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify+realign rounds/sec and realign HBM GB/s (% of peak) at B=16"
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt")
-REALIGN_SRC = os.path.join(ROOT, "ragged_kv_realignment_amd", "csrc", "realign.hip")
+_CSRC = os.path.join(ROOT, "ragged_kv_realignment_amd", "csrc")
+_HEADERS = ("buffer_io.h", "device_common.h", "launch.h")
+# counter summary and the sources of the realign kernel it was taken on, per realign mode
+TRAFFIC = {
+    False: (os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt"), ("realign.hip",) + _HEADERS),
+    True: (os.path.join(ROOT, "profiles", "realign_inplace_8b_gqa_traffic.txt"),
+           ("realign_inplace.hip",) + _HEADERS),
+}
 
 
 def parse():
@@ -43,25 +49,32 @@ def parse():
     ap.add_argument("--cpu-rounds", type=int, default=64, help="oracle sample: rounds")
     ap.add_argument("--cpu-layers", type=int, default=36, help="oracle sample: KV layers realigned (scaled to all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--inplace", action="store_true",
+                    help="realign the one rectangle in place (EQSPEC_INPLACE) instead of ping-ponging two")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration for profiling)")
     return ap.parse_args()
 
 
-def realign_kernel_sha():
-    with open(REALIGN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def realign_kernel_sha(inplace=False):
+    """First 16 hex digits of the SHA-256 of the realign kernel's sources."""
+    h = hashlib.sha256()
+    for name in TRAFFIC[inplace][1]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_per_launch():
+def traffic_per_launch(inplace=False):
     """HBM bytes per realign launch from the committed counter summary, or None
-    when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    when it is missing or was taken on different kernel sources."""
+    path = TRAFFIC[inplace][0]
+    if not os.path.exists(path):
         return None
-    txt = open(TRAFFIC_FILE).read()
+    txt = open(path).read()
     m_sha = re.search(r"^kernel_source_sha256_16:\s*(\w+)", txt, re.M)
     m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
-    if not m_sha or not m_b or m_sha.group(1) != realign_kernel_sha():
+    if not m_sha or not m_b or m_sha.group(1) != realign_kernel_sha(inplace):
         return None
     return float(m_b.group(1))
 
@@ -90,6 +103,34 @@ def round_bytes(cfg, lens0, width0, acc_hist):
         verify.append(B * (D + 1) * V * es_logit + B * D * 4 + 8 * B)
         lens = lens + n
     return np.array(verify, dtype=np.float64), np.array(realign, dtype=np.float64)
+
+
+def round_bytes_inplace(cfg, lens0, width0, acc_hist):
+    """Algorithmic bytes of each round's in-place realignment.
+
+    Row b moves by shift = S' - S - n_b positions.  A row with content that
+    moves reads and writes its c_b positions; a move to higher positions also
+    writes `shift` positions of zero pad; every row reads and writes its n_b
+    committed entries.  Token ids move with the content; pad and committed
+    token ids, and position ids and mask over [0, S'), are written."""
+    import numpy as np
+    B = cfg.B
+    P = cfg.kv_pos_bytes
+    lens = lens0.astype(np.int64).copy()
+    S = int(width0)
+    out = []
+    for acc in acc_hist:
+        n = acc.astype(np.int64) + 1
+        snew = int((lens + n).max())
+        shift = snew - S - n
+        moved = (shift != 0) & (lens > 0)
+        kv = P * (2 * int(lens[moved].sum()) + int(np.maximum(shift, 0).sum()) + 2 * int(n.sum()))
+        pout = snew - lens - n
+        meta = (8 * int(lens[moved].sum()) + 4 * int(pout.sum()) + 4 * int(n.sum()) + 5 * B * snew +
+                4 * int(acc.sum()) + 16 * B + 8)
+        out.append(kv + meta)
+        lens, S = lens + n, snew
+    return np.array(out, dtype=np.float64)
 
 
 def cpu_baseline(cfg, plans, lens0, width0, tok0, mask0, rounds, layers):
@@ -188,7 +229,8 @@ def bench_chain(args, cfg):
     cap = max(cfg.cap, cfg.len_hi + R * cfg.D1)
     dev = torch.device("cuda", 0)
     w = sdev.GreedyRounds(cfg, R)
-    bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, sdev.TORCH_DT[cfg.kv_dtype]) for _ in range(2)]
+    bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, sdev.TORCH_DT[cfg.kv_dtype])
+            for _ in range(1 if args.inplace else 2)]
     ws = sd.workspace(cfg.B, cfg.D)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     acc_hist = torch.zeros((R, cfg.B), dtype=torch.int32, device=dev)
@@ -196,14 +238,17 @@ def bench_chain(args, cfg):
 
     def run(n, ev=None):
         for r in range(n):
-            src, dst = bufs[r % 2], bufs[(r + 1) % 2]
+            src, dst = bufs[r % len(bufs)], bufs[(r + 1) % len(bufs)]
             if ev:
                 ev[r][0].record()
             sd.verify_greedy(w.logits[r], w.drafts[r], ws=ws, status=status, accept_len=acc_hist[r],
                              next_token=nxt_hist[r])
             if ev:
                 ev[r][1].record()
-            sd.realign_eqspec(src, dst, w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], status=status)
+            if args.inplace:
+                sd.realign_eqspec_inplace(bufs[0], w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], status=status)
+            else:
+                sd.realign_eqspec(src, dst, w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], status=status)
             if ev:
                 ev[r][2].record()
 
@@ -224,6 +269,8 @@ def bench_chain(args, cfg):
         raise RuntimeError("device status %d during the timed rounds" % int(status.item()))
     ver_ms, re_ms = _ms(ev, 0, 1), _ms(ev, 1, 2)
     vbytes, rbytes = round_bytes(cfg, w.lens0, w.width0, acc_hist[:K].cpu().numpy())
+    if args.inplace:
+        rbytes = round_bytes_inplace(cfg, w.lens0, w.width0, acc_hist[:K].cpu().numpy())
     re_gbs = rbytes.sum() / (re_ms.sum() * 1e-3) / 1e9
     ve_gbs = vbytes.sum() / (ver_ms.sum() * 1e-3) / 1e9
     extra = {}
@@ -240,18 +287,19 @@ def bench_chain(args, cfg):
                    "algorithmic_bytes_per_launch": float(vbytes.mean()), "avg_launch_us": float(ver_ms.mean() * 1e3)},
         "realign_share_of_round": float(re_ms.sum() / total_ms),
     })
+    workload = "%s: B=%d, D=%d, V=%d %s logits, KV %dx%dx%d %s, lengths U[%d,%d] left-padded, %d chained " \
+               "greedy verify+EQSPEC%s rounds" % (
+                   cfg.name, cfg.B, cfg.D, cfg.V, synth.DTYPE_NAME[cfg.logit_dtype], cfg.L, cfg.H, cfg.Dh,
+                   synth.DTYPE_NAME[cfg.kv_dtype], cfg.len_lo, cfg.len_hi, K, " in-place" if args.inplace else "")
     config = {
-        "workload": "%s: B=%d, D=%d, V=%d %s logits, KV %dx%dx%d %s, lengths U[%d,%d] left-padded, %d chained "
-                    "greedy verify+EQSPEC rounds" % (cfg.name, cfg.B, cfg.D, cfg.V, synth.DTYPE_NAME[cfg.logit_dtype],
-                                                     cfg.L, cfg.H, cfg.Dh, synth.DTYPE_NAME[cfg.kv_dtype], cfg.len_lo,
-                                                     cfg.len_hi, K),
+        "workload": workload,
         "B": cfg.B, "D": cfg.D, "V": cfg.V, "layers": cfg.L, "kv_heads": cfg.H, "head_dim": cfg.Dh, "cap": cap,
         "global_batch": cfg.B,
     }
-    traffic = traffic_per_launch() if cfg.name == "8b-gqa" and K == 64 and W == 8 else None
+    traffic = traffic_per_launch(args.inplace) if cfg.name == "8b-gqa" and K == 64 and W == 8 else None
     metric = METRIC if cfg.name == "8b-gqa" else METRIC.replace("at B=16", "at B=%d (%s)" % (cfg.B, cfg.name))
     return _line(metric, K / (total_ms * 1e-3), K, W, total_ms / K, synth.DTYPE_NAME[cfg.kv_dtype], config,
-                 _roof("k_realign_eqspec", re_gbs, float(rbytes.mean()), float(re_ms.mean() * 1e3), traffic), cpu,
+                 _roof("k_realign_inplace" if args.inplace else "k_realign_eqspec", re_gbs, float(rbytes.mean()), float(re_ms.mean() * 1e3), traffic), cpu,
                  extra)
 
 
@@ -349,7 +397,7 @@ def bench_stoch(args, cfg):
              "realign_share_of_round": float(re_ms.sum() / total_ms)}
     return _line("sampled verify+realign rounds/sec and realign HBM GB/s (stoch, B=32)", K / (total_ms * 1e-3), K, W,
                  total_ms / K, "f16", config,
-                 _roof("k_realign_eqspec", re_gbs, rbytes, float(re_ms.mean() * 1e3)), cpu, extra)
+                 _roof("k_realign_inplace" if args.inplace else "k_realign_eqspec", re_gbs, rbytes, float(re_ms.mean() * 1e3)), cpu, extra)
 
 
 def bench_exspec(args, cfg):

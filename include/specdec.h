@@ -160,6 +160,7 @@ typedef struct {
 #define SPECDEC_EQSPEC 0         /* rectangle -> rectangle: unpad, append, repad (out of place) */
 #define SPECDEC_GATHER 1         /* pool rows -> one left-padded rectangle per group (no append) */
 #define SPECDEC_APPEND_INPLACE 2 /* pool rows: append committed entries at each row's length */
+#define SPECDEC_EQSPEC_INPLACE 3 /* rectangle -> the same rectangle: unpad, append, repad in place */
 
 /* Realignment ("Batch Speculative Decoding Done Right", sections 2.1-2.3;
  * committed and discarded speculative KV: "Inference Engineering Part 5/8",
@@ -188,6 +189,14 @@ typedef struct {
  *   tokens, len); batch entry b < B (pool row rows[b], NULL = b) appends its
  *   committed entries and tokens at its length, and its length grows by n_b.
  *   Rows must be distinct (else SPECDEC_S_ROWS_DUP and an undefined result).
+ * SPECDEC_EQSPEC_INPLACE: the EQSPEC result on positions [0, S') of the same
+ *   rectangle (`in` and `out` describe identical buffers).  Each row's content
+ *   moves by S' - S - n_b positions; rows whose shift is 0 only append.  The
+ *   input's pad positions must hold zero KV bytes (every realignment leaves
+ *   them so); positions [S', cap) keep their previous bytes.  Moves only the
+ *   bytes that change: about twice each shifted row's content, its committed
+ *   entries and any newly exposed pad, instead of the whole new rectangle.
+ *   Device conditions as for EQSPEC; a failing call writes nothing.
  * Limits: B <= 1024; head_dim * element size a multiple of 16 bytes; KV
  * pointers 16-byte aligned (E_ALIGN).  Device conditions: S' > out cap,
  * W_g > out cap or len + n_b > cap set SPECDEC_S_CAPACITY; lengths outside

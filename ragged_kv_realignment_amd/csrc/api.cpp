@@ -12,7 +12,6 @@
 
 namespace {
 
-constexpr int kMaxRealignB = 1024;
 constexpr int kMaxPool = 4096;
 
 size_t esize(int dtype) { return dtype == SPECDEC_F32 ? 4 : 2; }
@@ -44,6 +43,12 @@ int check_seqbuf_shape(const specdec_seqbuf_t *s) {
 
 bool same_geometry(const specdec_seqbuf_t *a, const specdec_seqbuf_t *b) {
   return a->layers == b->layers && a->heads == b->heads && a->head_dim == b->head_dim && a->dtype == b->dtype;
+}
+
+// the two descriptors name the same buffers with the same shape
+bool same_buffers(const specdec_seqbuf_t *a, const specdec_seqbuf_t *b) {
+  return a->kv == b->kv && a->tokens == b->tokens && a->pos == b->pos && a->mask == b->mask && a->len == b->len &&
+         a->width == b->width && a->rows == b->rows && a->cap == b->cap && same_geometry(a, b);
 }
 
 }  // namespace
@@ -118,8 +123,10 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
                               const int32_t *rows, int B, int group, const int32_t *skip_group, int D,
                               const void *kv_new, const int32_t *draft, const int32_t *accept_len,
                               const int32_t *next_token, int32_t pad_token, int32_t *status, void *stream) {
-  if (mode != SPECDEC_EQSPEC && mode != SPECDEC_GATHER && mode != SPECDEC_APPEND_INPLACE) return SPECDEC_E_ARG;
-  if (B < 0 || B > kMaxRealignB || D < 0) return SPECDEC_E_ARG;
+  if (mode != SPECDEC_EQSPEC && mode != SPECDEC_GATHER && mode != SPECDEC_APPEND_INPLACE &&
+      mode != SPECDEC_EQSPEC_INPLACE)
+    return SPECDEC_E_ARG;
+  if (B < 0 || B > sd::kMaxRealignRows || D < 0) return SPECDEC_E_ARG;
   int rc = check_seqbuf_shape(in);
   if (rc) return rc;
   rc = check_seqbuf_shape(out);
@@ -181,6 +188,25 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
     p.mask_out = out->mask;
     p.len_out = out->len;
     p.width_out = out->width;
+  } else if (mode == SPECDEC_EQSPEC_INPLACE) {
+    if (in->rows != B || !same_buffers(in, out)) return SPECDEC_E_ARG;
+    if (!in->tokens || !in->pos || !in->mask || !in->width) return SPECDEC_E_ARG;
+    if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+    if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
+    if (B == 0) return SPECDEC_OK;
+    const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
+    if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
+    if (overlap(accept_len, B * 4u, in->len, B * 4u) || overlap(next_token, B * 4u, in->tokens, tok_in_bytes) ||
+        (D > 0 && overlap(draft, (size_t)B * D * 4, in->tokens, tok_in_bytes)))
+      return SPECDEC_E_ALIAS;
+    p.tok_in = in->tokens;
+    p.len_in = in->len;
+    p.width_in = in->width;
+    p.tok_out = out->tokens;
+    p.pos_out = out->pos;
+    p.mask_out = out->mask;
+    p.len_out = out->len;
+    p.width_out = out->width;
   } else if (mode == SPECDEC_GATHER) {
     if (group < 1) return SPECDEC_E_ARG;
     if (out->rows < B) return SPECDEC_E_ARG;
@@ -208,7 +234,8 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
     p.tok_out = out->tokens;
     p.len_out = out->len;
   }
-  return launched(sd::launch_realign(p, as_stream(stream)));
+  return launched(mode == SPECDEC_EQSPEC_INPLACE ? sd::launch_realign_inplace(p, as_stream(stream))
+                                                  : sd::launch_realign(p, as_stream(stream)));
 }
 
 EXPORT int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, int32_t *uniform,

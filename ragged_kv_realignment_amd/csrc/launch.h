@@ -5,6 +5,8 @@
 
 namespace sd {
 
+constexpr int kMaxRealignRows = 1024;  // B limit of every realignment mode
+
 struct GreedyParams {
   const void *logits;
   int dtype;
@@ -56,6 +58,7 @@ int device_cus();
 hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s);
 hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s);
 hipError_t launch_realign(const RealignParams &p, hipStream_t s);
+hipError_t launch_realign_inplace(const RealignParams &p, hipStream_t s);
 hipError_t launch_group_by_len(const GroupParams &p, hipStream_t s);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
 

@@ -17,21 +17,18 @@
 // naturally aligned 16-byte vector.  Threads of a workgroup cover
 // (workgroup size / units) consecutive positions per pass, so a wave reads and writes
 // contiguous bytes.  Loads and stores are raw buffer operations on one
-// descriptor per source and destination sequence: lanes whose position lies
-// outside a descriptor's range use an out-of-range offset, which returns zero
-// (loads) or is dropped (stores) without a memory access.  Pad positions are
+// descriptor per source and destination sequence (buffer_io.h).  Pad positions are
 // thereby store-only, the tile body is straight-line code, and each thread
 // keeps all of its loads in flight before its stores.
 #include <limits.h>
+#include "buffer_io.h"
 #include "device_common.h"
 #include "launch.h"
 #include "specdec.h"
 
 namespace sd {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-constexpr int kMaxB = 1024;
+constexpr int kMaxB = kMaxRealignRows;
 
 // Tuning knobs (defaults are the measured best on MI355X).
 #ifndef SPECDEC_RA_BLOCK
@@ -49,28 +46,8 @@ constexpr int kMaxB = 1024;
 #ifndef SPECDEC_RA_INTERLEAVE
 #define SPECDEC_RA_INTERLEAVE 1  // tile t -> workgroup t mod grid (1) or contiguous ranges (0)
 #endif
-#ifndef SPECDEC_RA_AUX_LD
-#define SPECDEC_RA_AUX_LD 2      // cache policy of KV loads (2 = nt: streamed, read once)
-#endif
-#ifndef SPECDEC_RA_AUX_ST
-#define SPECDEC_RA_AUX_ST 2      // cache policy of KV stores (2 = nt)
-#endif
 constexpr int kPasses = SPECDEC_RA_PASSES;
 constexpr int kRaBlock = SPECDEC_RA_BLOCK;
-
-constexpr uint32_t kOOB = 0x80000000u;       // above every descriptor's range
-constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, gfx9 family
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-__device__ __forceinline__ i32x4 bld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SPECDEC_RA_AUX_LD);
-}
-__device__ __forceinline__ void bst(i32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, SPECDEC_RA_AUX_ST);
-}
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // A destination tile of the pipelined copy: positions [j_lo, j_lo + TP) of one
 // sequence; position j < a_hi takes source position j - a_lo when j >= a_lo and

@@ -31,3 +31,47 @@ def test_round_bytes_match_oracle_rounds():
     meta = rb - np.array(expect, dtype=np.float64)
     assert np.all(meta > 0) and np.all(meta < 1e6)  # token/position/mask bytes only
     assert np.all(vb == cfg.B * cfg.D1 * cfg.V * 2 + cfg.B * cfg.D * 4 + 8 * cfg.B)
+
+
+def test_round_bytes_inplace_position_count():
+    """In-place byte model against a per-position walk of the oracle's rounds:
+    a position of [0, S') is written when its new content is not already there
+    (moved content, committed entries, pad where content or unused capacity
+    was), and read when it is moved content or a committed entry."""
+    cfg = synth.CONFIGS["8b-gqa"]
+    lens = synth.lengths(cfg)
+    S = int(lens.max())
+    tok, pos, mask = synth.tokens_host(cfg, lens, S, True)
+    kv = synth.kv_host(cfg, lens, S, True, layer0=0, nlayers=1)
+    accs, expect = [], []
+    lens0 = lens.copy()
+    for r in range(3):
+        plant, _, draft = synth.plan_greedy(cfg, r)
+        acc, nxt, _ = oracle.verify_greedy(synth.logits_host(cfg, r, plant), draft, cfg.B, cfg.D, cfg.V)
+        out = oracle.realign_eqspec(kv, synth.kvnew_host(cfg, r, 0, 1), lens, S, tok, mask, acc, nxt, draft)
+        W = out["width"]
+        moved_bytes = 0
+        for b in range(cfg.B):
+            c, n = int(lens[b]), int(acc[b]) + 1
+            old_start, new_start = S - c, W - c - n
+            reads = writes = 0
+            for j in range(W):
+                k = j - new_start  # index into the row's new content, < 0 on pad
+                if k < 0:
+                    writes += j >= old_start  # pad where old content (or unused capacity) was
+                elif k < c:
+                    if new_start != old_start:
+                        reads += 1
+                        writes += 1
+                else:
+                    reads += 1
+                    writes += 1
+            moved_bytes += cfg.kv_pos_bytes * (reads + writes)
+        expect.append(moved_bytes)
+        accs.append(acc)
+        kv, lens, S, tok, mask = out["kv"], out["len"], W, out["tokens"], out["mask"]
+    rb = bench.round_bytes_inplace(cfg, lens0, int(lens0.max()), np.array(accs))
+    meta = rb - np.array(expect, dtype=np.float64)
+    assert np.all(meta > 0) and np.all(meta < 1e6)  # token/position/mask bytes only
+    _, full = bench.round_bytes(cfg, lens0, int(lens0.max()), np.array(accs))
+    assert np.all(rb < full)
