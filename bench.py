@@ -10,6 +10,11 @@ each realigns the previous round's output.  All inputs are synthetic and
 already resident in HBM when timing starts; every round has its own logits
 buffer, so nothing is re-read from cache across rounds.
 
+The headline realigns in place: one rectangle, where only the bytes that
+change move.  The out-of-place realignment (two rectangles, the full new one
+written) is timed on the same rounds and reported beside it; both give the
+same result.
+
 Prints one JSON line: rounds/s over the timed rounds, the realign kernel's
 achieved HBM bandwidth against the 8 TB/s peak (per-launch HIP events on the
 launch stream), and the CPU oracle timed on a bounded sample of the same
@@ -30,6 +35,7 @@ METRIC = "verify+realign rounds/sec and realign HBM GB/s (% of peak) at B=16"
 PEAK_HBM_GBS = 8000.0
 _CSRC = os.path.join(ROOT, "ragged_kv_realignment_amd", "csrc")
 _HEADERS = ("buffer_io.h", "device_common.h", "launch.h")
+KERNEL = {False: "k_realign_eqspec", True: "k_realign_inplace"}
 # counter summary and the sources of the realign kernel it was taken on, per realign mode
 TRAFFIC = {
     False: (os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt"), ("realign.hip",) + _HEADERS),
@@ -49,8 +55,9 @@ def parse():
     ap.add_argument("--cpu-rounds", type=int, default=64, help="oracle sample: rounds")
     ap.add_argument("--cpu-layers", type=int, default=36, help="oracle sample: KV layers realigned (scaled to all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--inplace", action="store_true",
-                    help="realign the one rectangle in place (EQSPEC_INPLACE) instead of ping-ponging two")
+    ap.add_argument("--realign", choices=("both", "inplace", "eqspec"), default="both",
+                    help="chain workloads: realign in place on one buffer, out of place between two, or both "
+                         "(the headline is the first of the two)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration for profiling)")
     return ap.parse_args()
@@ -215,22 +222,18 @@ def _roof(kernel, gbs, bytes_per_launch, us, traffic=None):
             "avg_launch_us": us}
 
 
-def bench_chain(args, cfg):
-    """Chained greedy verify + EQSPEC rounds of a left-padded batch (8b-gqa, 7b-mha)."""
-    import numpy as np
+def _time_chain(args, cfg, w, mode, K, W, cap):
+    """Times K chained rounds (after W untimed ones and a reset of the initial
+    state) with the realignment done in place on one buffer ("inplace") or out
+    of place between two ("eqspec").  Per-launch HIP events on the launch stream."""
     import torch
-    import synth
     import synth.device as sdev
     import ragged_kv_realignment_amd as sd
 
-    K = args.steps if args.steps is not None else cfg.rounds
-    W = args.warmup
     R = max(K, W, 1)
-    cap = max(cfg.cap, cfg.len_hi + R * cfg.D1)
     dev = torch.device("cuda", 0)
-    w = sdev.GreedyRounds(cfg, R)
     bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, sdev.TORCH_DT[cfg.kv_dtype])
-            for _ in range(1 if args.inplace else 2)]
+            for _ in range(1 if mode == "inplace" else 2)]
     ws = sd.workspace(cfg.B, cfg.D)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     acc_hist = torch.zeros((R, cfg.B), dtype=torch.int32, device=dev)
@@ -238,17 +241,18 @@ def bench_chain(args, cfg):
 
     def run(n, ev=None):
         for r in range(n):
-            src, dst = bufs[r % len(bufs)], bufs[(r + 1) % len(bufs)]
             if ev:
                 ev[r][0].record()
             sd.verify_greedy(w.logits[r], w.drafts[r], ws=ws, status=status, accept_len=acc_hist[r],
                              next_token=nxt_hist[r])
             if ev:
                 ev[r][1].record()
-            if args.inplace:
-                sd.realign_eqspec_inplace(bufs[0], w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], status=status)
+            if mode == "inplace":
+                sd.realign_eqspec_inplace(bufs[0], w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r],
+                                          status=status)
             else:
-                sd.realign_eqspec(src, dst, w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], status=status)
+                sd.realign_eqspec(bufs[r % 2], bufs[(r + 1) % 2], w.kv_new[r], w.drafts[r], acc_hist[r],
+                                  nxt_hist[r], status=status)
             if ev:
                 ev[r][2].record()
 
@@ -266,41 +270,74 @@ def bench_chain(args, cfg):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     if int(status.item()) != 0:
-        raise RuntimeError("device status %d during the timed rounds" % int(status.item()))
-    ver_ms, re_ms = _ms(ev, 0, 1), _ms(ev, 1, 2)
-    vbytes, rbytes = round_bytes(cfg, w.lens0, w.width0, acc_hist[:K].cpu().numpy())
-    if args.inplace:
-        rbytes = round_bytes_inplace(cfg, w.lens0, w.width0, acc_hist[:K].cpu().numpy())
-    re_gbs = rbytes.sum() / (re_ms.sum() * 1e-3) / 1e9
-    ve_gbs = vbytes.sum() / (ver_ms.sum() * 1e-3) / 1e9
+        raise RuntimeError("device status %d during the timed rounds (%s)" % (int(status.item()), mode))
+    out = {"total_ms": total_ms, "ver_ms": _ms(ev, 0, 1), "re_ms": _ms(ev, 1, 2), "acc": acc_hist[:K].cpu().numpy()}
+    del bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_chain(args, cfg):
+    """Chained greedy verify + EQSPEC rounds of a left-padded batch (8b-gqa, 7b-mha).
+
+    The headline realigns in place (one buffer); with --realign both (the
+    default) the out-of-place realignment is timed on the same rounds and
+    reported beside it."""
+    import torch
+    import synth
+    import synth.device as sdev
+
+    K = args.steps if args.steps is not None else cfg.rounds
+    W = args.warmup
+    R = max(K, W, 1)
+    cap = max(cfg.cap, cfg.len_hi + R * cfg.D1)
+    dev = torch.device("cuda", 0)
+    w = sdev.GreedyRounds(cfg, R)
+    modes = ("inplace", "eqspec") if args.realign == "both" else (args.realign,)
+    runs = {m: _time_chain(args, cfg, w, m, K, W, cap) for m in modes}
+    with_traffic = cfg.name == "8b-gqa" and K == 64 and W == 8
+
+    def roof(mode):
+        r = runs[mode]
+        fn = round_bytes_inplace if mode == "inplace" else (lambda *a: round_bytes(*a)[1])
+        rbytes = fn(cfg, w.lens0, w.width0, r["acc"])
+        gbs = rbytes.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
+        return _roof(KERNEL[mode == "inplace"], gbs, float(rbytes.mean()), float(r["re_ms"].mean() * 1e3),
+                     traffic_per_launch(mode == "inplace") if with_traffic else None)
+
+    head = runs[modes[0]]
+    vbytes, _ = round_bytes(cfg, w.lens0, w.width0, head["acc"])
+    ve_gbs = vbytes.sum() / (head["ver_ms"].sum() * 1e-3) / 1e9
     extra = {}
     if args.copy_calib_gib > 0:
         extra["copy_calibration"] = copy_calibration(args.copy_calib_gib, dev)
-    cpu = None
-    if not args.no_cpu:
-        del bufs
-        torch.cuda.empty_cache()
-        cpu = cpu_baseline(cfg, w.plans, w.lens0, w.width0, w.tok0, w.mask0, min(args.cpu_rounds, R),
-                           args.cpu_layers)
     extra.update({
         "verify": {"kernel": "k_verify_greedy", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
-                   "algorithmic_bytes_per_launch": float(vbytes.mean()), "avg_launch_us": float(ver_ms.mean() * 1e3)},
-        "realign_share_of_round": float(re_ms.sum() / total_ms),
+                   "algorithmic_bytes_per_launch": float(vbytes.mean()),
+                   "avg_launch_us": float(head["ver_ms"].mean() * 1e3)},
+        "realign_share_of_round": float(head["re_ms"].sum() / head["total_ms"]),
     })
+    if len(modes) == 2:
+        o = runs["eqspec"]
+        extra["out_of_place"] = {"value": K / (o["total_ms"] * 1e-3), "unit": "rounds/s",
+                                 "ms_per_step": o["total_ms"] / K, "roofline": roof("eqspec")}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, w.plans, w.lens0, w.width0, w.tok0, w.mask0, min(args.cpu_rounds, R),
+                           args.cpu_layers)
+    how = {"inplace": " (realigned in place)", "eqspec": " (realigned out of place)"}[modes[0]]
     workload = "%s: B=%d, D=%d, V=%d %s logits, KV %dx%dx%d %s, lengths U[%d,%d] left-padded, %d chained " \
-               "greedy verify+EQSPEC%s rounds" % (
+               "greedy verify+EQSPEC rounds%s" % (
                    cfg.name, cfg.B, cfg.D, cfg.V, synth.DTYPE_NAME[cfg.logit_dtype], cfg.L, cfg.H, cfg.Dh,
-                   synth.DTYPE_NAME[cfg.kv_dtype], cfg.len_lo, cfg.len_hi, K, " in-place" if args.inplace else "")
+                   synth.DTYPE_NAME[cfg.kv_dtype], cfg.len_lo, cfg.len_hi, K, how)
     config = {
         "workload": workload,
         "B": cfg.B, "D": cfg.D, "V": cfg.V, "layers": cfg.L, "kv_heads": cfg.H, "head_dim": cfg.Dh, "cap": cap,
         "global_batch": cfg.B,
     }
-    traffic = traffic_per_launch(args.inplace) if cfg.name == "8b-gqa" and K == 64 and W == 8 else None
     metric = METRIC if cfg.name == "8b-gqa" else METRIC.replace("at B=16", "at B=%d (%s)" % (cfg.B, cfg.name))
-    return _line(metric, K / (total_ms * 1e-3), K, W, total_ms / K, synth.DTYPE_NAME[cfg.kv_dtype], config,
-                 _roof("k_realign_inplace" if args.inplace else "k_realign_eqspec", re_gbs, float(rbytes.mean()), float(re_ms.mean() * 1e3), traffic), cpu,
-                 extra)
+    return _line(metric, K / (head["total_ms"] * 1e-3), K, W, head["total_ms"] / K, synth.DTYPE_NAME[cfg.kv_dtype],
+                 config, roof(modes[0]), cpu, extra)
 
 
 def bench_stoch(args, cfg):
@@ -397,7 +434,7 @@ def bench_stoch(args, cfg):
              "realign_share_of_round": float(re_ms.sum() / total_ms)}
     return _line("sampled verify+realign rounds/sec and realign HBM GB/s (stoch, B=32)", K / (total_ms * 1e-3), K, W,
                  total_ms / K, "f16", config,
-                 _roof("k_realign_inplace" if args.inplace else "k_realign_eqspec", re_gbs, rbytes, float(re_ms.mean() * 1e3)), cpu, extra)
+                 _roof("k_realign_eqspec", re_gbs, rbytes, float(re_ms.mean() * 1e3)), cpu, extra)
 
 
 def bench_exspec(args, cfg):

@@ -12,44 +12,58 @@
 namespace sd {
 
 // The same result as EQSPEC on positions [0, S') of a single rectangle.  Row b's
-// content moves by shift = pout - pin positions (|shift| <= D+1): one workgroup
-// per (layer, K|V, row, head) sequence walks it in chunks, in ascending order
-// for a move to lower positions and descending order otherwise, so a chunk's
-// stores only overlap its own sources (a barrier separates its loads from its
-// stores) and the next chunk's sources, which it prefetches, are never written
-// by the current one.  Positions vacated by a move to higher positions become
-// pad (zero bytes); the committed entries follow the content.  Sequences whose
-// shift is 0 only append.  The old pad is taken to hold zero bytes, as every
-// realignment leaves it.  Token ids, position ids and mask of row b are rebuilt
-// by workgroup nseg + b; lengths and width are written by k_inplace_meta.
-constexpr int kIpBlock = 256;
-constexpr int kIpPasses = 4;
+// content moves by shift = pout - pin positions.  One workgroup per (layer,
+// K|V, row, head) sequence walks the move in chunks of 16-byte units, in
+// ascending order for a move to lower positions and descending order
+// otherwise: a chunk's stores then overlap only its own sources and those of
+// chunks already moved, never the sources of chunks still to come, which are
+// loaded (two chunks ahead) before the current chunk is stored.  Every thread
+// has its loads of a chunk back (the registers are consumed) before a barrier,
+// and the chunk is stored after it.  Positions vacated by a move to higher
+// positions become pad (zero bytes); the committed entries follow the content.
+// Sequences whose shift is 0 only append.  The old pad is taken to hold zero
+// bytes, as every realignment leaves it.  Token ids, position ids and mask of
+// row b are rebuilt by workgroup nseg + b; lengths and width are written by
+// k_inplace_meta.
+#ifndef SPECDEC_IP_BLOCK
+#define SPECDEC_IP_BLOCK 1024  // threads per workgroup (one sequence)
+#endif
+#ifndef SPECDEC_IP_PASSES
+#define SPECDEC_IP_PASSES 8   // 16-byte units per thread per chunk
+#endif
+constexpr int kIpBlock = SPECDEC_IP_BLOCK;
+constexpr int kIpWaves = kIpBlock / kWave;
+constexpr int kIpPasses = SPECDEC_IP_PASSES;
+constexpr int kIpChunk = kIpBlock * kIpPasses;  // 16-byte units per chunk
 
-__device__ __forceinline__ void ip_load(const char *base, int pin, int k0, int c, int PP, int U, int poff, int u,
-                                        bool act, size_t pos_bytes, i32x4 *v) {
-  const __amdgpu_buffer_rsrc_t r = rsrc(base + (size_t)pin * pos_bytes, (uint32_t)(c * pos_bytes));
+__device__ __forceinline__ void ip_load(__amdgpu_buffer_rsrc_t r, int f0, i32x4 *v) {
 #pragma unroll
-  for (int q = 0; q < kIpPasses; ++q) {
-    const int k = k0 + poff + q * PP;
-    v[q] = bld(r, (act && k >= 0 && k < c) ? (uint32_t)(k * U + u) * 16u : kOOB);
-  }
+  for (int q = 0; q < kIpPasses; ++q) v[q] = bld(r, (uint32_t)(f0 + q * kIpBlock) * 16u);
 }
 
-__device__ __forceinline__ void ip_store(char *base, int pout, int k0, int c, int PP, int U, int poff, int u,
-                                         bool act, size_t pos_bytes, const i32x4 *v) {
-  const __amdgpu_buffer_rsrc_t r = rsrc(base + (size_t)pout * pos_bytes, (uint32_t)(c * pos_bytes));
+__device__ __forceinline__ void ip_store(__amdgpu_buffer_rsrc_t r, int f0, const i32x4 *v) {
 #pragma unroll
-  for (int q = 0; q < kIpPasses; ++q) {
-    const int k = k0 + poff + q * PP;
-    bst(v[q], r, (act && k >= 0 && k < c) ? (uint32_t)(k * U + u) * 16u : kOOB);
-  }
+  for (int q = 0; q < kIpPasses; ++q) bst(v[q], r, (uint32_t)(f0 + q * kIpBlock) * 16u);
+}
+
+// Walk step k: every load of chunk k (in `cur`) has returned in every thread
+// before the first store; chunk k + 2 is loaded into `ahead`; chunk k is
+// stored.  Steps past the last chunk use zero-range descriptors: no access.
+__device__ __forceinline__ void ip_step(int k, int nch, int first, int step, int t, __amdgpu_buffer_rsrc_t rs,
+                                        __amdgpu_buffer_rsrc_t rd, __amdgpu_buffer_rsrc_t r0, i32x4 *cur,
+                                        i32x4 *ahead) {
+#pragma unroll
+  for (int q = 0; q < kIpPasses; ++q) asm volatile("" ::"v"(cur[q]));
+  __syncthreads();
+  ip_load(k + 2 < nch ? rs : r0, (first + (k + 2) * step) * kIpChunk + t, ahead);
+  ip_store(k < nch ? rd : r0, (first + k * step) * kIpChunk + t, cur);
 }
 
 __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
   __shared__ int s_c[kMaxRealignRows];
   __shared__ int s_n[kMaxRealignRows];
-  __shared__ int s_red[kIpBlock / kWave];
-  __shared__ int s_red2[kIpBlock / kWave];
+  __shared__ int s_red[kIpWaves];
+  __shared__ int s_red2[kIpWaves];
   const int B = p.B, D = p.D, U = p.units, H = p.heads;
   const int S = p.width_in[0];
   int mx = 0, bad = (S < 0 || S > p.cap_in) ? SPECDEC_S_LEN_RANGE : 0;
@@ -75,66 +89,74 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
     Snew = s_red[0];
     bad = s_red2[0];
 #pragma unroll
-    for (int k = 1; k < kIpBlock / kWave; ++k) {
+    for (int k = 1; k < kIpWaves; ++k) {
       Snew = max(Snew, s_red[k]);
       bad |= s_red2[k];
     }
   }
+  Snew = uni(Snew);
+  bad = uni(bad);
   if (!bad && Snew > p.cap_out) bad = SPECDEC_S_CAPACITY;
   if (bad) {
     if (blockIdx.x == 0 && threadIdx.x == 0) set_status(p.status, bad);
     return;
   }
   const long nseg = (long)p.layers * 2 * B * H;
-  const size_t pos_bytes = (size_t)U * 16;
-  const int PP = kIpBlock / U, TP = PP * kIpPasses;
-  const int poff = threadIdx.x / U, u = threadIdx.x - poff * U;
-  const bool act = poff < PP;
+  const uint32_t pos_bytes = (uint32_t)U * 16u;
+  const int t = threadIdx.x;
   char *kv = static_cast<char *>(p.kv_out);
   const char *nw = static_cast<const char *>(p.kv_new);
 
   for (long w = blockIdx.x; w < nseg + B; w += gridDim.x) {
     if (w < nseg) {
       const int b = (int)((w / H) % B);
-      const int c = s_c[b], n = s_n[b];
+      const int c = uni(s_c[b]), n = uni(s_n[b]);
       const int pin = S - c, pout = Snew - c - n, shift = pout - pin;
       char *base = kv + (size_t)w * p.cap_in * pos_bytes;
+      // committed entries go to [pout + c, Snew); their first kIpBlock units are
+      // loaded now, so storing them at the end waits for nothing still in flight
+      const __amdgpu_buffer_rsrc_t ra = rsrc(nw + (size_t)w * (D + 1) * pos_bytes, (uint32_t)n * pos_bytes);
+      const __amdgpu_buffer_rsrc_t rc = rsrc(base + (size_t)(pout + c) * pos_bytes, (uint32_t)n * pos_bytes);
+      i32x4 e0 = bld(ra, (uint32_t)t * 16u);
       if (shift != 0 && c > 0) {
-        const int nch = (c + TP - 1) / TP;
-        // chunk order: ascending for a move to lower positions, descending otherwise
+        const uint32_t cb = (uint32_t)c * pos_bytes;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(base + (size_t)pin * pos_bytes, cb);
+        const __amdgpu_buffer_rsrc_t rd = rsrc(base + (size_t)pout * pos_bytes, cb);
+        const __amdgpu_buffer_rsrc_t r0 = rsrc(base, 0);
+        const int nch = (c * U + kIpChunk - 1) / kIpChunk;
         const int first = shift < 0 ? 0 : nch - 1, step = shift < 0 ? 1 : -1;
-        i32x4 v[kIpPasses], nv[kIpPasses];
-        ip_load(base, pin, first * TP, c, PP, U, poff, u, act, pos_bytes, v);
-        for (int i = 0, ch = first; i < nch; ++i, ch += step) {
-          // every thread holds chunk ch (its loads have returned) before any of it
-          // is overwritten: consuming the registers makes the wait explicit
+        i32x4 v0[kIpPasses], v1[kIpPasses], v2[kIpPasses];
 #pragma unroll
-          for (int q = 0; q < kIpPasses; ++q) asm volatile("" ::"v"(v[q]));
-          __syncthreads();
-          const int nx = ch + step;
-          ip_load(base, pin, nx * TP, (i + 1 < nch) ? c : 0, PP, U, poff, u, act, pos_bytes, nv);
-          ip_store(base, pout, ch * TP, c, PP, U, poff, u, act, pos_bytes, v);
-#pragma unroll
-          for (int q = 0; q < kIpPasses; ++q) v[q] = nv[q];
+        for (int q = 0; q < kIpPasses; ++q) v2[q] = (i32x4)(0);
+        // the prologue issues loads and (empty) stores in the order of a
+        // steady-state step, so the loop starts with the same loads in flight
+        ip_load(rs, first * kIpChunk + t, v0);
+        ip_store(r0, t, v2);
+        ip_load(nch > 1 ? rs : r0, (first + step) * kIpChunk + t, v1);
+        ip_store(r0, t, v2);
+        // arrived before the first chunk, so this wait costs nothing; redefining
+        // the register leaves no load pending on it at the store below
+        asm volatile("" : "+v"(e0));
+        for (int k = 0; k < nch; k += 3) {
+          ip_step(k, nch, first, step, t, rs, rd, r0, v0, v2);
+          ip_step(k + 1, nch, first, step, t, rs, rd, r0, v1, v0);
+          ip_step(k + 2, nch, first, step, t, rs, rd, r0, v2, v1);
         }
+      } else {
+        asm volatile("" : "+v"(e0));
       }
       if (shift > 0) {
         // positions [pin, pout) become pad: zero bytes (vacated content, or for a
         // short row positions past the old width)
-        const __amdgpu_buffer_rsrc_t rz = rsrc(base + (size_t)pin * pos_bytes, (uint32_t)(shift * pos_bytes));
-        for (int f = threadIdx.x; f < shift * U; f += kIpBlock) bst((i32x4)(0), rz, (uint32_t)f * 16u);
+        const __amdgpu_buffer_rsrc_t rz = rsrc(base + (size_t)pin * pos_bytes, (uint32_t)shift * pos_bytes);
+        for (int f = t; f < shift * U; f += kIpBlock) bst((i32x4)(0), rz, (uint32_t)f * 16u);
       }
-      // committed entries at [pout + c, Snew)
-      const __amdgpu_buffer_rsrc_t ra = rsrc(nw + (size_t)w * (D + 1) * pos_bytes, (uint32_t)(n * pos_bytes));
-      const __amdgpu_buffer_rsrc_t rd = rsrc(base + (size_t)(pout + c) * pos_bytes, (uint32_t)(n * pos_bytes));
-      for (int f = threadIdx.x; f < (D + 1) * U; f += kIpBlock) {
-        const uint32_t off = f < n * U ? (uint32_t)f * 16u : kOOB;
-        bst(bld(ra, off), rd, off);
-      }
+      bst(e0, rc, (uint32_t)t * 16u);
+      for (int f = t + kIpBlock; f < n * U; f += kIpBlock) bst(bld(ra, (uint32_t)f * 16u), rc, (uint32_t)f * 16u);
     } else {
       // token ids, position ids and mask of row b
       const int b = (int)(w - nseg);
-      const int c = s_c[b], n = s_n[b], a = n - 1;
+      const int c = uni(s_c[b]), n = uni(s_n[b]), a = n - 1;
       const int pin = S - c, pout = Snew - c - n, shift = pout - pin;
       int32_t *tok = p.tok_out + (size_t)b * p.cap_in;
       if (shift != 0 && c > 0) {
@@ -142,24 +164,23 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
         const int nch = (c + E - 1) / E;
         const int first = shift < 0 ? 0 : nch - 1, step = shift < 0 ? 1 : -1;
         for (int i = 0, ch = first; i < nch; ++i, ch += step) {
-          int t[4];
+          int v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int k = ch * E + q * kIpBlock + (int)threadIdx.x;
-            t[q] = k < c ? tok[pin + k] : 0;
+            const int k = ch * E + q * kIpBlock + t;
+            v[q] = k < c ? tok[pin + k] : 0;
           }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(t[q]));
+          for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(v[q]));
           __syncthreads();
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int k = ch * E + q * kIpBlock + (int)threadIdx.x;
-            if (k < c) tok[pout + k] = t[q];
+            const int k = ch * E + q * kIpBlock + t;
+            if (k < c) tok[pout + k] = v[q];
           }
-          __syncthreads();
         }
       }
-      for (int j = threadIdx.x; j < Snew; j += kIpBlock) {
+      for (int j = t; j < Snew; j += kIpBlock) {
         const int cj = j - pout;
         if (cj < 0) tok[j] = p.pad_token;
         else if (cj >= c) tok[j] = (cj - c < a) ? p.draft[(size_t)b * D + (cj - c)] : p.next_token[b];
@@ -195,6 +216,7 @@ __global__ __launch_bounds__(kIpBlock) void k_inplace_meta(RealignParams p) {
 }
 
 hipError_t launch_realign_inplace(const RealignParams &p, hipStream_t s) {
+  // one workgroup per sequence and per row
   const long g = (long)p.layers * 2 * p.B * p.heads + p.B;
   hipLaunchKernelGGL(k_realign_inplace, dim3((unsigned)(g < (1L << 30) ? g : (1L << 30))), dim3(kIpBlock), 0, s, p);
   hipError_t e = hipGetLastError();

@@ -110,10 +110,11 @@ def test_inplace_random(sd, seed):
 
 
 def test_inplace_long_token_rows(sd):
-    """Rows of more than one chunk of token ids (1024), both move directions."""
+    """Rows of several chunks of token ids (a chunk is 4 ids per thread of a
+    1024-thread workgroup), both move directions."""
     rng = np.random.default_rng(31)
     B, D, L, H, Dh = 6, 5, 1, 1, 4
-    lens = np.array([2500, 1, 2200, 0, 1700, 2499], np.int32)
+    lens = np.array([9000, 1, 8200, 0, 4500, 8999], np.int32)
     acc = np.array([5, 0, 2, 5, 1, 0], np.int32)  # rows 0 and 5 move down, the others up
     S = int(lens.max())
     cap = S + D + 1
