@@ -42,14 +42,19 @@ def lib():
         L.oracle_verify_sample.argtypes = [C.POINTER(C.c_float), C.POINTER(C.c_float), ci, ci, ci, i32p,
                                            C.POINTER(C.c_float), C.POINTER(C.c_float), i32p, i32p,
                                            C.POINTER(C.c_double)]
+        L.oracle_verify_sample_logits.argtypes = [vp, vp, ci, ci, ci, ci, C.c_float, C.c_float, i32p,
+                                                  C.POINTER(C.c_float), C.POINTER(C.c_float), i32p, i32p,
+                                                  C.POINTER(C.c_double)]
+        L.oracle_softmax_row.argtypes = [vp, ci, ci, C.c_float, C.c_float, C.POINTER(C.c_double)]
         L.oracle_realign_eqspec.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, i32p, C.c_int32, i32p, i8p,
                                             i32p, i32p, i32p, C.c_int32, i32p, i32p, i8p, i32p, i32p]
         L.oracle_group_by_len.argtypes = [i32p, ci, ci, i32p, i32p, i32p, i32p]
         L.oracle_gather.argtypes = [ci, ci, ci, ci, ci, ci, vp, i32p, i32p, i32p, ci, ci, i32p, ci, vp, i32p, i32p,
                                     i8p, i32p, C.c_int32]
         L.oracle_append.argtypes = [ci, ci, ci, ci, ci, ci, vp, i32p, i32p, i32p, ci, ci, vp, i32p, i32p, i32p]
-        for f in (L.oracle_verify_greedy, L.oracle_verify_sample, L.oracle_realign_eqspec, L.oracle_group_by_len,
-                  L.oracle_gather, L.oracle_append):
+        for f in (L.oracle_verify_greedy, L.oracle_verify_sample, L.oracle_verify_sample_logits,
+                  L.oracle_softmax_row, L.oracle_realign_eqspec, L.oracle_group_by_len, L.oracle_gather,
+                  L.oracle_append):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -108,6 +113,38 @@ def verify_sample(p, q, draft, u_accept, u_draw):
     if rc not in (OK, E_PRECOND):
         raise OracleError(rc)
     return acc, nxt, mass
+
+
+def verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, temperature, top_p=1.0):
+    """target [B,D+1,V] and draft_logits [B,D,V] logits (float32 | float16 | uint16 bf16 bits), turned into
+    p and q with the same temperature and top-p; returns (accept_len, next_token, residual mass)."""
+    t = np.ascontiguousarray(target)
+    d = np.ascontiguousarray(draft_logits)
+    B, D1, V = t.shape
+    D = D1 - 1
+    if d.shape != (B, D, V) or d.dtype != t.dtype:
+        raise ValueError("draft logits must be [B, D, V] of the target's dtype")
+    draft = _i32(draft).reshape(-1)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(-1)
+    ud = np.ascontiguousarray(u_draw, dtype=np.float32).reshape(-1)
+    acc = np.empty(B, np.int32)
+    nxt = np.empty(B, np.int32)
+    mass = np.empty(B, np.float64)
+    rc = lib().oracle_verify_sample_logits(t.ctypes.data, d.ctypes.data, _dtype_code(t), B, D, V,
+                                           float(temperature), float(top_p), _p(draft), _p(ua, C.c_float),
+                                           _p(ud, C.c_float), _p(acc), _p(nxt), _p(mass, C.c_double))
+    if rc not in (OK, E_PRECOND):
+        raise OracleError(rc)
+    return acc, nxt, mass
+
+
+def softmax_row(logits, temperature, top_p=1.0):
+    """The fp64 probabilities verify_sample_logits forms from one row of logits."""
+    a = np.ascontiguousarray(logits).reshape(-1)
+    out = np.empty(a.shape[0], np.float64)
+    _check(lib().oracle_softmax_row(a.ctypes.data, _dtype_code(a), a.shape[0], float(temperature), float(top_p),
+                                    _p(out, C.c_double)))
+    return out
 
 
 def realign_eqspec(kv_in, kv_new, len_in, width_in, tok_in, mask_in, accept_len, next_token, draft,

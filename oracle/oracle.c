@@ -97,66 +97,182 @@ EXPORT int oracle_verify_greedy(const void *logits, int dtype, int64_t row_strid
  * the replacement is drawn from normalize(max(0, p - q)); when every draft is
  * accepted the bonus comes from the target distribution after the full draft.
  * Readings: the caller supplies the uniforms; draft i is accepted iff
- * u_accept[i] <= p(x)/q(x), evaluated exactly as u*q <= p in fp64 (the product
- * of two fp32 numbers is exact in fp64); q(x) = 0 accepts iff p(x) > 0.  The
- * draw at stop position a uses u_draw[a]: with w the residual (a < D) or p at
- * position D (a = D), T = sum of w in fp64 in id order, the token is the
- * smallest id whose cumulative mass exceeds u*T; if rounding leaves none, the
- * last id with w > 0.  If T is 0 the draw falls back to p at that position
- * (unreachable for normalised p and q); an all-zero row yields id 0 and a
- * return of O_E_PRECOND. */
+ * u_accept[i] <= p(x)/q(x), evaluated as u*q <= p in fp64; q(x) = 0 accepts iff
+ * p(x) > 0.  The draw at stop position a uses u_draw[a]: with w the residual
+ * (a < D) or p at position D (a = D), T = sum of w in fp64 in id order, the
+ * token is the smallest id whose cumulative mass exceeds u*T; if rounding
+ * leaves none, the last id with w > 0.  If T is 0 the draw falls back to p at
+ * that position (unreachable for normalised p and q); an all-zero row yields
+ * id 0 and a return of O_E_PRECOND.
+ *
+ * One batch row: P holds the D+1 target rows and Q the D draft rows, V fp64
+ * probabilities each; w is V doubles of scratch.  Returns 1 for an all-zero row. */
+static int sample_row(const double *P, const double *Q, int D, int V, const int32_t *draft,
+                      const float *u_accept, const float *u_draw, double *w, int32_t *a_out, int32_t *j_out,
+                      double *mass_out) {
+  int a = D;
+  for (int i = 0; i < D; ++i) {
+    const int32_t x = draft[i];
+    int ok = 0;
+    if (x >= 0 && x < V) {
+      const double px = P[(int64_t)i * V + x];
+      const double qx = Q[(int64_t)i * V + x];
+      const double u = u_accept[i];
+      ok = (qx > 0.0) ? (u * qx <= px) : (px > 0.0);
+    }
+    if (!ok) { a = i; break; }
+  }
+  const double *pa = P + (int64_t)a * V;
+  const double *qa = (a < D) ? Q + (int64_t)a * V : NULL;
+  double T = 0.0;
+  for (int v = 0; v < V; ++v) {
+    const double d = qa ? pa[v] - qa[v] : pa[v];
+    w[v] = d > 0.0 ? d : 0.0;
+    T += w[v];
+  }
+  if (!(T > 0.0)) {
+    T = 0.0;
+    for (int v = 0; v < V; ++v) { w[v] = pa[v] > 0.0 ? pa[v] : 0.0; T += w[v]; }
+  }
+  int j = -1, zero = 0;
+  if (T > 0.0) {
+    const double target = (double)u_draw[a] * T;
+    double c = 0.0;
+    for (int v = 0; v < V; ++v) {
+      c += w[v];
+      if (c > target) { j = v; break; }
+    }
+    if (j < 0)
+      for (int v = V - 1; v >= 0; --v)
+        if (w[v] > 0.0) { j = v; break; }
+  } else {
+    j = 0;
+    zero = 1;
+  }
+  *a_out = a;
+  *j_out = j;
+  if (mass_out) *mass_out = T;
+  return zero;
+}
+
+/* Probabilities given directly: fp32 p [B][D+1][V] and q [B][D][V], each value
+ * widened exactly to fp64. */
 EXPORT int oracle_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
                                 const float *u_accept, const float *u_draw, int32_t *accept_len,
                                 int32_t *next_token, double *mass) {
   if (B < 0 || D < 0 || V <= 0) return O_E_ARG;
   int rc = O_OK;
+  double *P = (double *)malloc(sizeof(double) * (size_t)(D + 1) * V);
+  double *Q = (double *)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1) * V);
   double *w = (double *)malloc(sizeof(double) * (size_t)V);
   for (int b = 0; b < B; ++b) {
-    int a = D;
-    for (int i = 0; i < D; ++i) {
-      const int32_t x = draft[(int64_t)b * D + i];
-      int ok = 0;
-      if (x >= 0 && x < V) {
-        const double px = p[((int64_t)b * (D + 1) + i) * V + x];
-        const double qx = q[((int64_t)b * D + i) * V + x];
-        const double u = u_accept[(int64_t)b * D + i];
-        ok = (qx > 0.0) ? (u * qx <= px) : (px > 0.0);
-      }
-      if (!ok) { a = i; break; }
-    }
-    const float *pa = p + ((int64_t)b * (D + 1) + a) * V;
-    const float *qa = (a < D) ? q + ((int64_t)b * D + a) * V : NULL;
-    double T = 0.0;
-    for (int v = 0; v < V; ++v) {
-      double d = qa ? (double)pa[v] - (double)qa[v] : (double)pa[v];
-      w[v] = d > 0.0 ? d : 0.0;
-      T += w[v];
-    }
-    if (!(T > 0.0)) {
-      T = 0.0;
-      for (int v = 0; v < V; ++v) { w[v] = pa[v] > 0.0f ? (double)pa[v] : 0.0; T += w[v]; }
-    }
-    int j = -1;
-    if (T > 0.0) {
-      const double target = (double)u_draw[(int64_t)b * (D + 1) + a] * T;
-      double c = 0.0;
-      for (int v = 0; v < V; ++v) {
-        c += w[v];
-        if (c > target) { j = v; break; }
-      }
-      if (j < 0)
-        for (int v = V - 1; v >= 0; --v)
-          if (w[v] > 0.0) { j = v; break; }
-    } else {
-      j = 0;
+    for (int64_t k = 0; k < (int64_t)(D + 1) * V; ++k) P[k] = p[(int64_t)b * (D + 1) * V + k];
+    for (int64_t k = 0; k < (int64_t)D * V; ++k) Q[k] = q[(int64_t)b * D * V + k];
+    if (sample_row(P, Q, D, V, draft + (int64_t)b * D, u_accept + (int64_t)b * D, u_draw + (int64_t)b * (D + 1),
+                   w, &accept_len[b], &next_token[b], mass ? &mass[b] : NULL))
       rc = O_E_PRECOND;
-    }
-    accept_len[b] = a;
-    next_token[b] = j;
-    if (mass) mass[b] = T;
   }
+  free(P);
+  free(Q);
   free(w);
   return rc;
+}
+
+/* Sampling settings ([NL] opening section: the decoding rule may sample among
+ * likely tokens using temperature and top-p; "Exactness ...": the draft and the
+ * target use the same sampling settings).  Row l of V logits becomes
+ * probabilities in fp64:
+ *  - temperature: e(v) = exp((l(v) - M) / T) with M = max l; the maximum is
+ *    subtracted so no term overflows, and the result does not depend on it;
+ *  - top-p (0 < top_p < 1): the nucleus is every id whose logit is at least t,
+ *    where t is the largest logit value such that the ids with logit >= t hold
+ *    at least top_p of the mass sum(e); ids tied at t are all kept.  If
+ *    rounding leaves the whole mass short of top_p * sum(e), every id is kept.
+ *    top_p >= 1 keeps every id;
+ *  - p(v) = e(v) / Z over the kept ids, 0 elsewhere; Z is summed in id order.
+ * `order` is V ints of scratch. */
+static const double *g_sort_key;
+static int by_key_desc(const void *x, const void *y) {
+  const double a = g_sort_key[*(const int *)x], b = g_sort_key[*(const int *)y];
+  return a < b ? 1 : (a > b ? -1 : 0);
+}
+
+static void softmax_row(const void *logits, int dtype, int64_t row0, int V, double T, double top_p, double *out,
+                        double *lv, int *order) {
+  double M = -INFINITY;
+  for (int v = 0; v < V; ++v) {
+    lv[v] = logit_at(logits, dtype, row0 + v);
+    if (lv[v] > M) M = lv[v];
+  }
+  for (int v = 0; v < V; ++v) out[v] = exp((lv[v] - M) / T);
+  if (top_p < 1.0) {
+    double total = 0.0;
+    for (int v = 0; v < V; ++v) total += out[v];
+    for (int v = 0; v < V; ++v) order[v] = v;
+    g_sort_key = lv;
+    qsort(order, (size_t)V, sizeof(int), by_key_desc);
+    const double need = top_p * total;
+    double cum = 0.0, t = -INFINITY;
+    int k = 0, found = 0;
+    while (k < V) {
+      const double val = lv[order[k]];
+      while (k < V && lv[order[k]] == val) cum += out[order[k++]];
+      if (cum >= need) { t = val; found = 1; break; }
+    }
+    if (found)
+      for (int v = 0; v < V; ++v)
+        if (lv[v] < t) out[v] = 0.0;
+  }
+  double Z = 0.0;
+  for (int v = 0; v < V; ++v) Z += out[v];
+  for (int v = 0; v < V; ++v) out[v] /= Z;
+}
+
+/* Logits given: target [B][D+1][V] and draft [B][D][V] of element type dtype
+ * (widened exactly), turned into p and q by softmax_row with the same
+ * temperature and top-p, then decided as oracle_verify_sample does. */
+EXPORT int oracle_verify_sample_logits(const void *target, const void *draftl, int dtype, int B, int D, int V,
+                                       float temperature, float top_p, const int32_t *draft,
+                                       const float *u_accept, const float *u_draw, int32_t *accept_len,
+                                       int32_t *next_token, double *mass) {
+  if (B < 0 || D < 0 || V <= 0 || !(temperature > 0.0f) || !isfinite(temperature) || !(top_p > 0.0f) ||
+      top_p > 1.0f)
+    return O_E_ARG;
+  int rc = O_OK;
+  double *P = (double *)malloc(sizeof(double) * (size_t)(D + 1) * V);
+  double *Q = (double *)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1) * V);
+  double *w = (double *)malloc(sizeof(double) * (size_t)V);
+  double *lv = (double *)malloc(sizeof(double) * (size_t)V);
+  int *order = (int *)malloc(sizeof(int) * (size_t)V);
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i <= D; ++i)
+      softmax_row(target, dtype, ((int64_t)b * (D + 1) + i) * V, V, temperature, top_p, P + (int64_t)i * V, lv,
+                  order);
+    for (int i = 0; i < D; ++i)
+      softmax_row(draftl, dtype, ((int64_t)b * D + i) * V, V, temperature, top_p, Q + (int64_t)i * V, lv, order);
+    if (sample_row(P, Q, D, V, draft + (int64_t)b * D, u_accept + (int64_t)b * D, u_draw + (int64_t)b * (D + 1),
+                   w, &accept_len[b], &next_token[b], mass ? &mass[b] : NULL))
+      rc = O_E_PRECOND;
+  }
+  free(P);
+  free(Q);
+  free(w);
+  free(lv);
+  free(order);
+  return rc;
+}
+
+/* One row's probabilities as softmax_row computes them (for tests: the band
+ * rule needs the exact masses the draw compared). */
+EXPORT int oracle_softmax_row(const void *logits, int dtype, int V, float temperature, float top_p, double *out) {
+  if (V <= 0 || !(temperature > 0.0f) || !isfinite(temperature) || !(top_p > 0.0f) || top_p > 1.0f)
+    return O_E_ARG;
+  double *lv = (double *)malloc(sizeof(double) * (size_t)V);
+  int *order = (int *)malloc(sizeof(int) * (size_t)V);
+  softmax_row(logits, dtype, 0, V, temperature, top_p, out, lv, order);
+  free(lv);
+  free(order);
+  return O_OK;
 }
 
 /* ------------------------------------------------------------ realignment
