@@ -130,6 +130,37 @@ int specdec_verify_sample(const float *p, const float *q, int B, int D, int V, c
                           const float *u_accept, const float *u_draw, int32_t *accept_len,
                           int32_t *next_token, int32_t *status, void *stream);
 
+/* Bytes of the workspace specdec_verify_sample_logits needs for B rows, D
+ * drafts and V logits per row. */
+size_t specdec_sample_workspace_bytes(int B, int D, int V);
+
+/* Sampled verification from logits: the rule of specdec_verify_sample with p
+ * and q formed from logits by the sampling settings ("Inference Engineering
+ * Part 5/8", opening section: the decoding rule may sample using temperature
+ * and top-p; section "Exactness Means Different Things For Greedy And Sampled
+ * Output": the draft and the target use the same settings).
+ *
+ *  target        device [B][D+1][V] target logits of element type `dtype`.
+ *  draft_logits  device [B][D][V] draft-model logits of the same type.
+ *  temperature   > 0 and finite: p(v) = exp((l(v) - M) / T) / Z with M the
+ *                row maximum and Z the row's sum, all in fp64.
+ *  top_p         in (0, 1]; only 1 (no nucleus) is accepted by this version.
+ *  draft, u_accept, u_draw, accept_len, next_token, status
+ *                as for specdec_verify_sample; the acceptance test and the
+ *                draw compare fp64 values formed on the device.
+ *  ws            device workspace of at least specdec_sample_workspace_bytes
+ *                (B, D, V) bytes, 16-byte aligned; scratch only, nothing is
+ *                kept between calls.  Calls that share a workspace must not
+ *                overlap.
+ * Logits are finite or -inf with at least one finite value per row; NaN is
+ * outside the contract.  B = 0 is a no-op.  Errors: E_ARG (B outside
+ * [0, 65535], D outside [0, 255], V outside [1, 2^24], temperature or top_p out
+ * of range, NULL pointers), E_DTYPE, E_WORKSPACE, E_ALIGN, E_LAUNCH. */
+int specdec_verify_sample_logits(const void *target, const void *draft_logits, int dtype, int B, int D, int V,
+                                 float temperature, float top_p, const int32_t *draft, const float *u_accept,
+                                 const float *u_draw, int32_t *accept_len, int32_t *next_token, void *ws,
+                                 size_t ws_bytes, int32_t *status, void *stream);
+
 /* --------------------------------------------------------------- realign */
 
 /* A set of sequences with a contiguous KV cache.

@@ -7,7 +7,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build():
-    cmd = ["gcc", "-O2", "-Wall", "-fPIC", "-shared", "-fvisibility=hidden", "-o", LIB + ".tmp", "oracle.c", "-lm"]
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-Wall", "-fPIC", "-shared", "-fvisibility=hidden", "-o", LIB + ".tmp", "oracle.c", "-lm"]
     r = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("oracle build failed:\n%s\n%s" % (r.stdout, r.stderr))

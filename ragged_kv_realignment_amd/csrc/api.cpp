@@ -2,6 +2,7 @@
 // per step.  Declarations and the contract of every entry point are in
 // include/specdec.h.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -117,6 +118,65 @@ EXPORT int specdec_verify_sample(const float *p, const float *q, int B, int D, i
   s.next_token = next_token;
   s.status = status;
   return launched(sd::launch_verify_sample(s, as_stream(stream)));
+}
+
+// Workspace of specdec_verify_sample_logits: per-split row statistics, per-split
+// masses and the stop position of every batch row.
+struct SlLayout {
+  size_t stats, part, stop, total;
+};
+
+static SlLayout sl_layout(int B, int D, int V) {
+  const size_t S = ((size_t)V + sd::kSlChunk - 1) / sd::kSlChunk, R = 2 * (size_t)D + 1;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  SlLayout l;
+  l.stats = 0;
+  l.part = up((size_t)B * R * S * 16);
+  l.stop = l.part + up((size_t)B * S * 16);
+  l.total = l.stop + up((size_t)B * 4);
+  return l;
+}
+
+EXPORT size_t specdec_sample_workspace_bytes(int B, int D, int V) {
+  if (B < 0 || D < 0 || V < 1) return 0;
+  return sl_layout(B, D, V).total;
+}
+
+EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_logits, int dtype, int B, int D,
+                                        int V, float temperature, float top_p, const int32_t *draft,
+                                        const float *u_accept, const float *u_draw, int32_t *accept_len,
+                                        int32_t *next_token, void *ws, size_t ws_bytes, int32_t *status,
+                                        void *stream) {
+  if (B < 0 || B > 65535 || D < 0 || D > 255 || V < 1 || V > (1 << 24)) return SPECDEC_E_ARG;
+  if (!(temperature > 0.0f) || !isfinite(temperature) || !(top_p > 0.0f) || top_p > 1.0f) return SPECDEC_E_ARG;
+  if (top_p < 1.0f) return SPECDEC_E_ARG;  // the nucleus is not implemented on the device yet
+  if (dtype != SPECDEC_F32 && dtype != SPECDEC_F16 && dtype != SPECDEC_BF16) return SPECDEC_E_DTYPE;
+  if (B == 0) return SPECDEC_OK;
+  if (!target || !u_draw || !accept_len || !next_token || (D > 0 && (!draft_logits || !draft || !u_accept)))
+    return SPECDEC_E_ARG;
+  const SlLayout l = sl_layout(B, D, V);
+  if (!ws || ws_bytes < l.total) return SPECDEC_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return SPECDEC_E_ALIGN;
+  sd::SampleLogitsParams s;
+  s.target = target;
+  s.draftl = draft_logits;
+  s.dtype = dtype;
+  s.B = B;
+  s.D = D;
+  s.V = V;
+  s.S = (int)((V + sd::kSlChunk - 1) / sd::kSlChunk);
+  s.inv_t = 1.0 / (double)temperature;
+  s.draft = draft;
+  s.u_accept = u_accept;
+  s.u_draw = u_draw;
+  s.accept_len = accept_len;
+  s.next_token = next_token;
+  s.status = status;
+  char *w = static_cast<char *>(ws);
+  s.stats = reinterpret_cast<double *>(w + l.stats);
+  s.part = reinterpret_cast<double *>(w + l.part);
+  s.stop = reinterpret_cast<int32_t *>(w + l.stop);
+  return launched(sd::launch_verify_sample_logits(s, as_stream(stream)));
 }
 
 EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbuf_t *out,

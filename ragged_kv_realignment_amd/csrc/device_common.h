@@ -111,6 +111,22 @@ __device__ __forceinline__ int block_min_int(int v, int *scratch) {
   return r;
 }
 
+// fp64 wave reductions (a fixed order of additions for a given lane mapping).
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // Division by a runtime-invariant divisor d (1 <= d < 2^31) for n < 2^31 with a
 // multiply-high: with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
 // n / d = (mulhi(n, m) + n) >> s (Granlund and Montgomery, "Division by

@@ -29,6 +29,20 @@ struct SampleParams {
   int32_t *accept_len, *next_token, *status;
 };
 
+struct SampleLogitsParams {
+  const void *target, *draftl;  // logits [B][D+1][V] and [B][D][V] of `dtype`
+  int dtype, B, D, V, S;        // S = splits of kSlChunk logits per row
+  double inv_t;                 // 1 / temperature
+  const int32_t *draft;
+  const float *u_accept, *u_draw;
+  int32_t *accept_len, *next_token, *status;
+  double *stats;                // workspace [B][2D+1][S] x (max, exp-sum)
+  double *part;                 // workspace [B][S] x (residual mass, target mass)
+  int32_t *stop;                // workspace [B]: stop position
+};
+
+constexpr int kSlChunk = 4096;  // logits per split in sampled verification from logits
+
 struct RealignParams {
   int mode;
   // source / destination KV in 16-byte units
@@ -57,6 +71,7 @@ struct GroupParams {
 int device_cus();
 hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s);
 hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s);
+hipError_t launch_verify_sample_logits(const SampleLogitsParams &p, hipStream_t s);
 hipError_t launch_realign(const RealignParams &p, hipStream_t s);
 hipError_t launch_realign_inplace(const RealignParams &p, hipStream_t s);
 hipError_t launch_group_by_len(const GroupParams &p, hipStream_t s);

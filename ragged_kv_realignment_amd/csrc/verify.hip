@@ -252,21 +252,6 @@ __device__ __forceinline__ void load_w(const float *pa, const float *qa, int v0,
   for (int e = 0; e < VW; ++e) w[e] = (v0 + e < V) ? resid(pa, qa, v0 + e) : 0.0;
 }
 
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-
-__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
 // One workgroup per row b.  Each wave owns a contiguous quarter of the row and
 // reads it in chunks of 64 lanes x VW consecutive ids (coalesced).  Pass 1: the
 // fp64 mass of each quarter and the block total T; the draw target u*T falls in

@@ -23,7 +23,8 @@ _ERRORS = {E_ARG: "invalid argument", E_DTYPE: "unsupported element type", E_WOR
 _TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init", "specdec_verify_greedy",
-           "specdec_verify_sample", "specdec_realign_kv", "specdec_group_by_len")
+           "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
+           "specdec_realign_kv", "specdec_group_by_len")
 
 
 class SpecDecError(RuntimeError):
@@ -55,11 +56,15 @@ def lib():
         L.specdec_workspace_init.argtypes = [vp, sz, vp]
         L.specdec_verify_greedy.argtypes = [vp, ci, i64, ci, ci, ci, vp, vp, vp, vp, vp, sz, vp, vp]
         L.specdec_verify_sample.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.specdec_sample_workspace_bytes.argtypes = [ci, ci, ci]
+        L.specdec_sample_workspace_bytes.restype = sz
+        L.specdec_verify_sample_logits.argtypes = [vp, vp, ci, ci, ci, ci, C.c_float, C.c_float, vp, vp, vp, vp, vp,
+                                                   vp, sz, vp, vp]
         L.specdec_realign_kv.argtypes = [ci, C.POINTER(SeqBufC), C.POINTER(SeqBufC), vp, ci, ci, vp, ci, vp, vp,
                                          vp, vp, C.c_int32, vp, vp]
         L.specdec_group_by_len.argtypes = [vp, ci, ci, vp, vp, vp, vp, vp]
-        for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample", "specdec_realign_kv",
-                  "specdec_group_by_len"):
+        for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample",
+                  "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -157,6 +162,41 @@ def specdec_verify_sample(p, q, draft, u_accept, u_draw, status=None, accept_len
     rc = lib().specdec_verify_sample(p.data_ptr(), q.data_ptr(), B, D, V, draft.data_ptr(), u_accept.data_ptr(),
                                      u_draw.data_ptr(), _ptr(accept_len), _ptr(next_token), _ptr(status), _stream())
     _check(rc, "specdec_verify_sample")
+    return accept_len, next_token
+
+
+def sample_workspace(B, D, V, device="cuda"):
+    """Scratch workspace of sampled verification from logits (nothing kept between calls)."""
+    n = int(lib().specdec_sample_workspace_bytes(B, D, V))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def specdec_verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, temperature, top_p=1.0, ws=None,
+                                 status=None, accept_len=None, next_token=None):
+    """Sampled verification from logits: target [B, D+1, V] and draft_logits [B, D, V]
+    (float32, float16 or bfloat16), turned into p and q by the temperature (and
+    top-p) on the device.  Returns (accept_len, next_token)."""
+    _need(target, "target")
+    if target.dtype not in _TORCH_DT or target.dim() != 3:
+        raise ValueError("target must be a [B, D+1, V] float32/float16/bfloat16 tensor")
+    B, D1, V = target.shape
+    D = D1 - 1
+    _need(draft_logits, "draft_logits", target.dtype)
+    _need(draft, "draft", torch.int32)
+    _need(u_accept, "u_accept", torch.float32)
+    _need(u_draw, "u_draw", torch.float32)
+    if tuple(draft_logits.shape) != (B, D, V) or tuple(draft.shape) != (B, D) or \
+            tuple(u_accept.shape) != (B, D) or tuple(u_draw.shape) != (B, D1):
+        raise ValueError("shape mismatch between the logits, draft and the uniforms")
+    dev = target.device
+    ws = sample_workspace(B, D, V, dev) if ws is None else ws
+    accept_len = _i32(B, dev) if accept_len is None else accept_len
+    next_token = _i32(B, dev) if next_token is None else next_token
+    rc = lib().specdec_verify_sample_logits(target.data_ptr(), draft_logits.data_ptr(), _TORCH_DT[target.dtype], B,
+                                            D, V, float(temperature), float(top_p), draft.data_ptr(),
+                                            u_accept.data_ptr(), u_draw.data_ptr(), _ptr(accept_len),
+                                            _ptr(next_token), ws.data_ptr(), ws.numel(), _ptr(status), _stream())
+    _check(rc, "specdec_verify_sample_logits")
     return accept_len, next_token
 
 
@@ -284,4 +324,5 @@ def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_un
 
 verify_greedy = specdec_verify_greedy
 verify_sample = specdec_verify_sample
+verify_sample_logits = specdec_verify_sample_logits
 group_by_len = specdec_group_by_len

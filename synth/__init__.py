@@ -156,6 +156,21 @@ def tokens_host(cfg: Config, lens, width, left_pad, pad_token=0, rows=None, cap=
     return tok, pos, mask
 
 
+def sampled_logits_round(cfg: Config, rnd: int = 0, B=None, V=None):
+    """The logits behind sampled_round: target logits ~ N(0, sigma) and draft
+    logits = target + N(0, noise), both rounded once to float32, with the same
+    draft ids and uniforms as sampled_round.  Returns target [B,D+1,V],
+    draft_logits [B,D,V], draft [B,D], u_accept [B,D], u_draw [B,D+1]."""
+    B = cfg.B if B is None else B
+    V = cfg.V if V is None else V
+    D, D1 = cfg.D, cfg.D1
+    tl = normals(F32, cfg.seed, S_LOGIT, rnd, B * D1 * V, cfg.sigma).reshape(B, D1, V).astype(np.float64)
+    noise = normals(F32, cfg.seed, S_NOISE, rnd, B * D * V, cfg.draft_noise).reshape(B, D, V).astype(np.float64)
+    dl = tl[:, :D, :] + noise
+    _, _, draft, u_acc, u_draw = sampled_round(cfg, rnd, B=B, V=V)
+    return tl.astype(np.float32), dl.astype(np.float32), draft, u_acc, u_draw
+
+
 def sampled_round(cfg: Config, rnd: int = 0, B=None, V=None):
     """Inputs of a sampled-verification round.
 
