@@ -154,7 +154,7 @@ size_t specdec_sample_workspace_bytes(int B, int D, int V);
  *                overlap.
  * Logits are finite or -inf with at least one finite value per row; NaN is
  * outside the contract.  B = 0 is a no-op.  Errors: E_ARG (B outside
- * [0, 65535], D outside [0, 255], V outside [1, 2^24], temperature or top_p out
+ * [0, 65535], D outside [0, 255], V outside [1, 2^22], temperature or top_p out
  * of range, NULL pointers), E_DTYPE, E_WORKSPACE, E_ALIGN, E_LAUNCH. */
 int specdec_verify_sample_logits(const void *target, const void *draft_logits, int dtype, int B, int D, int V,
                                  float temperature, float top_p, const int32_t *draft, const float *u_accept,

@@ -33,15 +33,19 @@ struct SampleLogitsParams {
   const void *target, *draftl;  // logits [B][D+1][V] and [B][D][V] of `dtype`
   int dtype, B, D, V, S;        // S = splits of kSlChunk logits per row
   double inv_t;                 // 1 / temperature
+  bool vec;                     // rows 16-byte aligned: vector loads
   const int32_t *draft;
   const float *u_accept, *u_draw;
   int32_t *accept_len, *next_token, *status;
   double *stats;                // workspace [B][2D+1][S] x (max, exp-sum)
   double *part;                 // workspace [B][S] x (residual mass, target mass)
+  double *thr;                  // workspace [B][S][kBlock] x the same per thread run
+  double *rowinfo;              // workspace [B] x (M, 1/Z) of the stop position's target and draft rows
   int32_t *stop;                // workspace [B]: stop position
 };
 
-constexpr int kSlChunk = 4096;  // logits per split in sampled verification from logits
+constexpr int kSlChunk = 4096;   // logits per split in sampled verification from logits
+constexpr int kSlThreads = 256;  // threads per workgroup of those kernels
 
 struct RealignParams {
   int mode;

@@ -15,9 +15,10 @@
 //     result in every workgroup of the batch row), and sums the stop row's
 //     residual mass max(0, p - q) (or p at position D) and its target mass
 //     over its split.
+//     Each thread also leaves the masses of its run of kSlPer consecutive ids.
 //  3. k_sl_draw: one workgroup per batch row finds the split in which the
-//     running mass first exceeds u * T and scans that split with an fp64 block
-//     scan for the smallest such id.
+//     running mass first exceeds u * T, then the thread run within it (a block
+//     scan of the run masses), then the id (a wave scan of that run's weights).
 #include <math.h>
 #include <limits.h>
 #include "device_common.h"
@@ -32,7 +33,18 @@
 namespace sd {
 
 constexpr int kSlPer = kSlChunk / kBlock;  // logits per thread per split
+static_assert(kSlPer <= kWave, "a thread run must fit one wave");
+static_assert(kBlock == kSlThreads, "workspace layout assumes kSlThreads threads per workgroup");
+
+// Logits per 16-byte vector, and whether a thread's kSlPer logits are whole vectors.
+template <int DT>
+struct SlVec {
+  static constexpr int E = DT == SPECDEC_F32 ? 4 : 8;
+  static constexpr bool ok = kSlPer % E == 0;
+};
 constexpr int kSlMaxRows = 2 * 255 + 1;     // 2D + 1 rows per batch row, D <= 255
+constexpr int kSlMaxSplits = 1024;          // V <= 2^22
+constexpr int kSlUnroll = 8;               // independent exps in flight per thread (statistics)
 
 template <int DT>
 __device__ __forceinline__ float logit_at(const void *base, int64_t i) {
@@ -53,13 +65,32 @@ __device__ __forceinline__ double block_sum_d(double x, double *scratch) {
   return r;
 }
 
-// Row maximum M and 1/Z from the per-split statistics (split order).
+// Row maximum M and 1/Z from the per-split statistics (split order).  Loads
+// are issued kBatch splits at a time so a row costs ceil(S / kBatch) round
+// trips, not S.
+constexpr int kBatch = 8;
+
 __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t, double &M, double &inv_z) {
   double m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmax(m, st[2 * s]);
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    double ms[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) ms[k] = s0 + k < S ? st[2 * (s0 + k)] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) m = fmax(m, ms[k]);
+  }
   double z = 0.0;
-  for (int s = 0; s < S; ++s)
-    if (st[2 * s] > -INFINITY) z += st[2 * s + 1] * exp((st[2 * s] - m) * inv_t);
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    double ms[kBatch], zs[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      ms[k] = s0 + k < S ? st[2 * (s0 + k)] : -INFINITY;
+      zs[k] = s0 + k < S ? st[2 * (s0 + k) + 1] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (ms[k] > -INFINITY) z += zs[k] * exp((ms[k] - m) * inv_t);
+  }
   M = m;
   inv_z = 1.0 / z;
 }
@@ -71,7 +102,49 @@ __device__ __forceinline__ int64_t draft_row(const SampleLogitsParams &p, int b,
   return ((int64_t)b * p.D + i) * p.V;
 }
 
-template <int DT>
+// kSlPer logits of one split for this thread: id threadIdx.x + k * kBlock
+// (scalar loads) or, with 16-byte vectors of E = 16 / esize logits, ids
+// (threadIdx.x + j * kBlock) * E + e for vector j and lane e.  Ids at or past n
+// read as -inf.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_split(const void *base, int64_t off, int n, float *x) {
+  if (VEC && SlVec<DT>::ok) {
+    constexpr int E = SlVec<DT>::E;
+    constexpr int NV = kSlPer / E;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i0 = (threadIdx.x + j * kBlock) * E;
+      if (i0 + E <= n) {
+        if (DT == SPECDEC_F32) {
+          const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off + i0);
+          x[j * E + 0] = v.x;
+          x[j * E + 1] = v.y;
+          x[j * E + 2] = v.z;
+          x[j * E + 3] = v.w;
+        } else {
+          const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off + i0);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[j * E + 2 * e] = DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] & 0xFFFFu) : bf16_bits_to_f32(w[e] & 0xFFFFu);
+            x[j * E + 2 * e + 1] = DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] >> 16) : bf16_bits_to_f32(w[e] >> 16);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[j * E + e] = i0 + e < n ? logit_at<DT>(base, off + i0 + e) : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSlPer; ++k) {
+      const int i = threadIdx.x + k * kBlock;
+      x[k] = i < n ? logit_at<DT>(base, off + i) : -INFINITY;
+    }
+  }
+}
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
   __shared__ float s_f[kBlock / kWave];
   __shared__ double s_d[kBlock / kWave];
@@ -81,20 +154,16 @@ __global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
   const int64_t off = (r <= D ? target_row(p, b, r) : draft_row(p, b, r - D - 1)) + (int64_t)s * kSlChunk;
   const int n = min(kSlChunk, p.V - s * kSlChunk);
   float x[kSlPer];
-#pragma unroll
-  for (int k = 0; k < kSlPer; ++k) {
-    const int i = threadIdx.x + k * kBlock;
-    x[k] = i < n ? logit_at<DT>(base, off + i) : -INFINITY;
-  }
+  load_split<DT, VEC>(base, off, n, x);
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kSlPer; ++k) m = fmaxf(m, x[k]);
   m = block_max_float(m, s_f);
   double z = 0.0;
   if (m > -INFINITY) {
-#pragma unroll
-    for (int k = 0; k < kSlPer; ++k)
-      if (threadIdx.x + k * kBlock < n) z += exp(((double)x[k] - (double)m) * p.inv_t);
+    const double md = (double)m;
+#pragma unroll kSlUnroll
+    for (int k = 0; k < kSlPer; ++k) z += exp(((double)x[k] - md) * p.inv_t);  // exp(-inf) = 0 past n
   }
   z = block_sum_d(z, s_d);
   if (threadIdx.x == 0) {
@@ -104,7 +173,49 @@ __global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
   }
 }
 
-template <int DT>
+// This thread's kSlPer consecutive logits of a split, ids t * kSlPer + k (the
+// mass and draw kernels scan ids in order); ids at or past n read as -inf.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_run(const void *base, int64_t off, int t, int n, float *x) {
+  const int i0 = t * kSlPer;
+  if (VEC && SlVec<DT>::ok && i0 + kSlPer <= n) {
+    if (DT == SPECDEC_F32) {
+#pragma unroll
+      for (int j = 0; j < kSlPer / 4; ++j) {
+        const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off + i0 + 4 * j);
+        x[4 * j] = v.x;
+        x[4 * j + 1] = v.y;
+        x[4 * j + 2] = v.z;
+        x[4 * j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSlPer / 8; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off + i0 + 8 * j);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * j + 2 * e] = DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] & 0xFFFFu) : bf16_bits_to_f32(w[e] & 0xFFFFu);
+          x[8 * j + 2 * e + 1] = DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] >> 16) : bf16_bits_to_f32(w[e] >> 16);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSlPer; ++k) x[k] = i0 + k < n ? logit_at<DT>(base, off + i0 + k) : -INFINITY;
+  }
+}
+
+// The stop row's weight at one logit: max(0, p - q) at a < D (resid), else p.
+__device__ __forceinline__ double weight(float lt, float lq, bool resid, double Mt, double izt, double Mq, double izq,
+                                         double inv_t) {
+  const double pv = exp(((double)lt - Mt) * inv_t) * izt;  // 0 for -inf
+  if (!resid) return pv;
+  const double d = pv - exp(((double)lq - Mq) * inv_t) * izq;
+  return d > 0.0 ? d : 0.0;
+}
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
   __shared__ double s_m[kSlMaxRows], s_iz[kSlMaxRows];
   __shared__ int s_i[kBlock / kWave];
@@ -136,95 +247,98 @@ __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
   }
   const int a = block_min_int(first, s_i);
   if (s == 0) set_status(p.status, block_or_int(bad, s_i));
-  // residual (a < D) or target (a = D) mass of this split, and the target mass
+  // residual (a < D) or target (a = D) mass of this thread's run of the split
+  // and of the split, and the same for the target alone
   const int n = min(kSlChunk, V - s * kSlChunk);
-  const int64_t to = target_row(p, b, a) + (int64_t)s * kSlChunk;
-  const int64_t qo = a < D ? draft_row(p, b, a) + (int64_t)s * kSlChunk : 0;
+  const bool resid = a < D;
   float lt[kSlPer], lq[kSlPer];
-#pragma unroll
-  for (int k = 0; k < kSlPer; ++k) {
-    const int i = threadIdx.x + k * kBlock;
-    lt[k] = i < n ? logit_at<DT>(p.target, to + i) : 0.0f;
-    lq[k] = (i < n && a < D) ? logit_at<DT>(p.draftl, qo + i) : 0.0f;
-  }
+  load_run<DT, VEC>(p.target, target_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lt);
+  if (resid) load_run<DT, VEC>(p.draftl, draft_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lq);
   const double Mt = s_m[a], izt = s_iz[a];
-  const double Mq = a < D ? s_m[D + 1 + a] : 0.0, izq = a < D ? s_iz[D + 1 + a] : 0.0;
+  const double Mq = resid ? s_m[D + 1 + a] : 0.0, izq = resid ? s_iz[D + 1 + a] : 0.0;
   double wsum = 0.0, psum = 0.0;
-#pragma unroll
+#pragma unroll 4
   for (int k = 0; k < kSlPer; ++k) {
-    if (threadIdx.x + k * kBlock < n) {
-      const double pv = exp(((double)lt[k] - Mt) * p.inv_t) * izt;
-      double w = pv;
-      if (a < D) {
-        const double d = pv - exp(((double)lq[k] - Mq) * p.inv_t) * izq;
-        w = d > 0.0 ? d : 0.0;
-      }
-      wsum += w;
-      psum += pv;
+    const double pv = exp(((double)lt[k] - Mt) * p.inv_t) * izt;
+    double w = pv;
+    if (resid) {
+      const double d = pv - exp(((double)lq[k] - Mq) * p.inv_t) * izq;
+      w = d > 0.0 ? d : 0.0;
     }
+    wsum += w;
+    psum += pv;
   }
+  double *thr = p.thr + (((int64_t)b * p.S + s) * kBlock + threadIdx.x) * 2;
+  thr[0] = wsum;
+  thr[1] = psum;
   wsum = block_sum_d(wsum, s_d);
   psum = block_sum_d(psum, s_d);
   if (threadIdx.x == 0) {
     p.part[((int64_t)b * p.S + s) * 2] = wsum;
     p.part[((int64_t)b * p.S + s) * 2 + 1] = psum;
-    if (s == 0) p.stop[b] = a;
+    if (s == 0) {
+      double *ri = p.rowinfo + (int64_t)b * 4;
+      ri[0] = Mt;
+      ri[1] = izt;
+      ri[2] = Mq;
+      ri[3] = izq;
+      p.stop[b] = a;
+    }
   }
 }
 
-template <int DT>
+// One workgroup per batch row: the split in which the running mass first
+// exceeds u * T (split masses in split order), then the thread run in which it
+// does (thread masses in thread order), then the id (that run's weights in id
+// order, recomputed exactly as the mass kernel formed them).
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
   __shared__ double s_d[kBlock / kWave];
   __shared__ int s_i[kBlock / kWave];
-  __shared__ double s_base, s_target, s_m[2], s_iz[2];
+  __shared__ double s_part[2 * kSlMaxSplits];
+  __shared__ double s_base, s_target;
   __shared__ int s_split, s_flags;  // flags: 1 draw from p, 2 no crossing (take the last positive id), 4 zero mass
-  const int b = blockIdx.x, D = p.D, V = p.V, S = p.S, R = 2 * D + 1;
+  __shared__ int s_run;
+  const int b = blockIdx.x, D = p.D, V = p.V, S = p.S;
   const int a = p.stop[b];
   const double *part = p.part + (int64_t)b * S * 2;
+  for (int k = threadIdx.x; k < 2 * S; k += kBlock) s_part[k] = part[k];
+  __syncthreads();
   if (threadIdx.x == 0) {
-    double T = 0.0;
-    for (int s = 0; s < S; ++s) T += part[2 * s];
+    double T = 0.0, Tp = 0.0;
+    for (int k = 0; k < S; ++k) {
+      T += s_part[2 * k];
+      Tp += s_part[2 * k + 1];
+    }
     int flags = 0;
     if (!(T > 0.0)) {
       flags |= 1;
-      T = 0.0;
-      for (int s = 0; s < S; ++s) T += part[2 * s + 1];
+      T = Tp;
     }
     const int e = flags & 1;
     int split = -1;
-    double base = 0.0;
+    double base = 0.0, target = 0.0;
     if (T > 0.0) {
-      const double target = (double)p.u_draw[(int64_t)b * (D + 1) + a] * T;
+      target = (double)p.u_draw[(int64_t)b * (D + 1) + a] * T;
       double c = 0.0;
-      for (int s = 0; s < S; ++s) {
-        const double cn = c + part[2 * s + e];
-        if (cn > target) { split = s; base = c; break; }
+      for (int k = 0; k < S; ++k) {
+        const double cn = c + s_part[2 * k + e];
+        if (cn > target) { split = k; base = c; break; }
         c = cn;
       }
       if (split < 0) {
         flags |= 2;
-        for (int s = S - 1; s >= 0; --s)
-          if (part[2 * s + e] > 0.0) { split = s; break; }
+        for (int k = S - 1; k >= 0; --k)
+          if (s_part[2 * k + e] > 0.0) { split = k; break; }
       }
-      s_target = target;
     } else {
       flags |= 4;
       split = 0;
-      s_target = 0.0;
     }
     s_split = split;
     s_base = base;
+    s_target = target;
     s_flags = flags;
-  } else if (threadIdx.x == kWave) {
-    double M, iz;
-    merge_row(p.stats + ((int64_t)b * R + a) * S * 2, S, p.inv_t, M, iz);
-    s_m[0] = M;
-    s_iz[0] = iz;
-  } else if (threadIdx.x == 2 * kWave && a < D) {
-    double M, iz;
-    merge_row(p.stats + ((int64_t)b * R + D + 1 + a) * S * 2, S, p.inv_t, M, iz);
-    s_m[1] = M;
-    s_iz[1] = iz;
   }
   __syncthreads();
   const int flags = s_flags, split = s_split;
@@ -236,68 +350,64 @@ __global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
     }
     return;
   }
-  const bool resid = a < D && !(flags & 1);
-  // this thread's contiguous logits of the split, for an in-order scan
-  const int v0 = split * kSlChunk, n = min(kSlChunk, V - v0);
-  const int i0 = threadIdx.x * kSlPer;
-  const int64_t to = target_row(p, b, a) + v0, qo = resid ? draft_row(p, b, a) + v0 : 0;
-  double w[kSlPer];
-  double tsum = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSlPer; ++k) {
-    const int i = i0 + k;
-    double x = 0.0;
-    if (i < n) {
-      const double pv = exp(((double)logit_at<DT>(p.target, to + i) - s_m[0]) * p.inv_t) * s_iz[0];
-      x = pv;
-      if (resid) {
-        const double d = pv - exp(((double)logit_at<DT>(p.draftl, qo + i) - s_m[1]) * p.inv_t) * s_iz[1];
-        x = d > 0.0 ? d : 0.0;
-      }
-    }
-    w[k] = x;
-    tsum += x;
-  }
-  // exclusive block scan of the thread sums, in thread order
+  const int e = flags & 1;
+  const bool resid = a < D && !e;
+  // thread runs of the split: the first whose running mass exceeds the target
+  // (or, with no crossing, the last with positive mass)
+  const double m = p.thr[(((int64_t)b * S + split) * kBlock + threadIdx.x) * 2 + e];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const double incl = wave_incl_scan(tsum, lane);
+  const double incl = wave_incl_scan(m, lane);
   if (lane == kWave - 1) s_d[wv] = incl;
   __syncthreads();
-  double run = s_base + incl - tsum;
-  for (int k = 0; k < wv; ++k) run += s_d[k];
-  int found = INT_MAX, last = -1;
-#pragma unroll
-  for (int k = 0; k < kSlPer; ++k) {
-    run += w[k];
-    if (w[k] > 0.0) last = v0 + i0 + k;
-    if (found == INT_MAX && run > s_target && w[k] > 0.0) found = v0 + i0 + k;
+  double before = s_base + incl - m;
+  for (int k = 0; k < wv; ++k) before += s_d[k];
+  const bool cross = !(flags & 2) && m > 0.0 && before + m > s_target;
+  int run = block_min_int(cross ? (int)threadIdx.x : INT_MAX, s_i);
+  if (run == INT_MAX) run = block_max_int(m > 0.0 ? (int)threadIdx.x : -1, s_i);
+  if (threadIdx.x == (unsigned)max(run, 0)) s_base = before;  // mass before the chosen run
+  __syncthreads();
+  // the chosen run's weights, one id per thread of the first wave, in id order
+  const int v0 = split * kSlChunk, n = min(kSlChunk, V - v0);
+  const int i = max(run, 0) * kSlPer + lane;
+  double w = 0.0;
+  if (threadIdx.x < kSlPer && run >= 0 && i < n) {
+    const float lt = logit_at<DT>(p.target, target_row(p, b, a) + v0 + i);
+    const float lq = resid ? logit_at<DT>(p.draftl, draft_row(p, b, a) + v0 + i) : 0.0f;
+    const double Mt = p.rowinfo[(int64_t)b * 4], izt = p.rowinfo[(int64_t)b * 4 + 1];
+    const double Mq = p.rowinfo[(int64_t)b * 4 + 2], izq = p.rowinfo[(int64_t)b * 4 + 3];
+    w = weight(lt, lq, resid, Mt, izt, Mq, izq, p.inv_t);
   }
-  if (flags & 2) found = INT_MAX;
-  int j = block_min_int(found, s_i);
-  if (j == INT_MAX) j = block_max_int(last, s_i);
-  if (threadIdx.x == 0) {
-    p.accept_len[b] = a;
-    p.next_token[b] = j >= 0 ? j : 0;
+  if (threadIdx.x < kWave) {
+    const double c = s_base + wave_incl_scan(w, lane);
+    const bool hit = !(flags & 2) && w > 0.0 && c > s_target;
+    const unsigned long long hits = __ballot(hit), pos = __ballot(w > 0.0);
+    if (lane == 0) {
+      int j;
+      if (hits) j = __ffsll((long long)hits) - 1;
+      else j = pos ? 63 - __clzll((long long)pos) : -1;
+      p.accept_len[b] = a;
+      p.next_token[b] = j >= 0 ? v0 + max(run, 0) * kSlPer + j : 0;
+    }
   }
 }
 
-template <int DT>
+template <int DT, bool VEC>
 static hipError_t launch_sl(const SampleLogitsParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(k_sl_stats<DT>, dim3((unsigned)p.S, (unsigned)(2 * p.D + 1), (unsigned)p.B), dim3(kBlock), 0,
-                     s, p);
+  hipLaunchKernelGGL((k_sl_stats<DT, VEC>), dim3((unsigned)p.S, (unsigned)(2 * p.D + 1), (unsigned)p.B),
+                     dim3(kBlock), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sl_mass<DT>, dim3((unsigned)p.S, (unsigned)p.B), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_sl_mass<DT, VEC>), dim3((unsigned)p.S, (unsigned)p.B), dim3(kBlock), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sl_draw<DT>, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_sl_draw<DT, VEC>), dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_verify_sample_logits(const SampleLogitsParams &p, hipStream_t s) {
-  if (p.dtype == SPECDEC_F32) return launch_sl<SPECDEC_F32>(p, s);
-  if (p.dtype == SPECDEC_F16) return launch_sl<SPECDEC_F16>(p, s);
-  return launch_sl<SPECDEC_BF16>(p, s);
+  if (p.dtype == SPECDEC_F32) return p.vec ? launch_sl<SPECDEC_F32, true>(p, s) : launch_sl<SPECDEC_F32, false>(p, s);
+  if (p.dtype == SPECDEC_F16) return p.vec ? launch_sl<SPECDEC_F16, true>(p, s) : launch_sl<SPECDEC_F16, false>(p, s);
+  return p.vec ? launch_sl<SPECDEC_BF16, true>(p, s) : launch_sl<SPECDEC_BF16, false>(p, s);
 }
 
 }  // namespace sd
