@@ -42,10 +42,12 @@ def lib():
         L.oracle_verify_sample.argtypes = [C.POINTER(C.c_float), C.POINTER(C.c_float), ci, ci, ci, i32p,
                                            C.POINTER(C.c_float), C.POINTER(C.c_float), i32p, i32p,
                                            C.POINTER(C.c_double)]
-        L.oracle_verify_sample_logits.argtypes = [vp, vp, ci, ci, ci, ci, C.c_float, C.c_float, i32p,
-                                                  C.POINTER(C.c_float), C.POINTER(C.c_float), i32p, i32p,
-                                                  C.POINTER(C.c_double)]
-        L.oracle_softmax_row.argtypes = [vp, ci, ci, C.c_float, C.c_float, C.POINTER(C.c_double)]
+        L.oracle_verify_sample_logits.argtypes = [vp, vp, ci, ci, ci, ci, C.c_float, C.c_float,
+                                                  C.POINTER(C.c_float), i32p, C.POINTER(C.c_float),
+                                                  C.POINTER(C.c_float), i32p, i32p, C.POINTER(C.c_double),
+                                                  C.POINTER(C.c_float)]
+        L.oracle_softmax_row.argtypes = [vp, ci, ci, C.c_float, C.c_float, C.POINTER(C.c_float),
+                                         C.POINTER(C.c_double)]
         L.oracle_realign_eqspec.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, i32p, C.c_int32, i32p, i8p,
                                             i32p, i32p, i32p, C.c_int32, i32p, i32p, i8p, i32p, i32p]
         L.oracle_group_by_len.argtypes = [i32p, ci, ci, i32p, i32p, i32p, i32p]
@@ -115,9 +117,12 @@ def verify_sample(p, q, draft, u_accept, u_draw):
     return acc, nxt, mass
 
 
-def verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, temperature, top_p=1.0):
+def verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, temperature, top_p=1.0, cut=None,
+                         return_cut=False):
     """target [B,D+1,V] and draft_logits [B,D,V] logits (float32 | float16 | uint16 bf16 bits), turned into
-    p and q with the same temperature and top-p; returns (accept_len, next_token, residual mass)."""
+    p and q with the same temperature and top-p; returns (accept_len, next_token, residual mass), and the
+    nucleus thresholds applied [B, 2D+1] (target rows, then draft rows) with return_cut.  `cut` [B, 2D+1]
+    forces those thresholds instead of computing them."""
     t = np.ascontiguousarray(target)
     d = np.ascontiguousarray(draft_logits)
     B, D1, V = t.shape
@@ -127,23 +132,31 @@ def verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, temperat
     draft = _i32(draft).reshape(-1)
     ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(-1)
     ud = np.ascontiguousarray(u_draw, dtype=np.float32).reshape(-1)
+    if cut is not None:
+        cut = np.ascontiguousarray(cut, dtype=np.float32).reshape(-1)
+        if cut.size != B * (2 * D + 1):
+            raise ValueError("cut must hold B * (2D+1) thresholds")
     acc = np.empty(B, np.int32)
     nxt = np.empty(B, np.int32)
     mass = np.empty(B, np.float64)
+    used = np.empty((B, 2 * D + 1), np.float32)
     rc = lib().oracle_verify_sample_logits(t.ctypes.data, d.ctypes.data, _dtype_code(t), B, D, V,
-                                           float(temperature), float(top_p), _p(draft), _p(ua, C.c_float),
-                                           _p(ud, C.c_float), _p(acc), _p(nxt), _p(mass, C.c_double))
+                                           float(temperature), float(top_p), _p(cut, C.c_float), _p(draft),
+                                           _p(ua, C.c_float), _p(ud, C.c_float), _p(acc), _p(nxt),
+                                           _p(mass, C.c_double), _p(used, C.c_float))
     if rc not in (OK, E_PRECOND):
         raise OracleError(rc)
-    return acc, nxt, mass
+    return (acc, nxt, mass, used) if return_cut else (acc, nxt, mass)
 
 
-def softmax_row(logits, temperature, top_p=1.0):
-    """The fp64 probabilities verify_sample_logits forms from one row of logits."""
+def softmax_row(logits, temperature, top_p=1.0, cut=None):
+    """The fp64 probabilities verify_sample_logits forms from one row of logits
+    (with the nucleus threshold `cut` forced when given)."""
     a = np.ascontiguousarray(logits).reshape(-1)
     out = np.empty(a.shape[0], np.float64)
+    c = None if cut is None else np.array([cut], np.float32)
     _check(lib().oracle_softmax_row(a.ctypes.data, _dtype_code(a), a.shape[0], float(temperature), float(top_p),
-                                    _p(out, C.c_double)))
+                                    _p(c, C.c_float), _p(out, C.c_double)))
     return out
 
 

@@ -190,6 +190,9 @@ EXPORT int oracle_verify_sample(const float *p, const float *q, int B, int D, in
  *    rounding leaves the whole mass short of top_p * sum(e), every id is kept.
  *    top_p >= 1 keeps every id;
  *  - p(v) = e(v) / Z over the kept ids, 0 elsewhere; Z is summed in id order.
+ * Where the mass of the ids above a candidate t lies within rounding of
+ * top_p * sum(e), more than one t is correct; a caller may then give t itself
+ * (`cut`), and the row is formed from that nucleus.
  * `order` is V ints of scratch. */
 static const double *g_sort_key;
 static int by_key_desc(const void *x, const void *y) {
@@ -197,59 +200,72 @@ static int by_key_desc(const void *x, const void *y) {
   return a < b ? 1 : (a > b ? -1 : 0);
 }
 
-static void softmax_row(const void *logits, int dtype, int64_t row0, int V, double T, double top_p, double *out,
-                        double *lv, int *order) {
+/* The nucleus threshold t for logits lv and masses e (-inf: every id kept). */
+static double nucleus_cut(const double *lv, const double *e, int V, double top_p, int *order) {
+  if (!(top_p < 1.0)) return -INFINITY;
+  double total = 0.0;
+  for (int v = 0; v < V; ++v) total += e[v];
+  for (int v = 0; v < V; ++v) order[v] = v;
+  g_sort_key = lv;
+  qsort(order, (size_t)V, sizeof(int), by_key_desc);
+  const double need = top_p * total;
+  double cum = 0.0;
+  int k = 0;
+  while (k < V) {
+    const double val = lv[order[k]];
+    while (k < V && lv[order[k]] == val) cum += e[order[k++]];
+    if (cum >= need) return val;
+  }
+  return -INFINITY;
+}
+
+/* One row: out = p; *cut_used (nullable) receives the threshold applied. */
+static void softmax_row(const void *logits, int dtype, int64_t row0, int V, double T, double top_p,
+                        const float *cut, double *out, double *lv, int *order, float *cut_used) {
   double M = -INFINITY;
   for (int v = 0; v < V; ++v) {
     lv[v] = logit_at(logits, dtype, row0 + v);
     if (lv[v] > M) M = lv[v];
   }
   for (int v = 0; v < V; ++v) out[v] = exp((lv[v] - M) / T);
-  if (top_p < 1.0) {
-    double total = 0.0;
-    for (int v = 0; v < V; ++v) total += out[v];
-    for (int v = 0; v < V; ++v) order[v] = v;
-    g_sort_key = lv;
-    qsort(order, (size_t)V, sizeof(int), by_key_desc);
-    const double need = top_p * total;
-    double cum = 0.0, t = -INFINITY;
-    int k = 0, found = 0;
-    while (k < V) {
-      const double val = lv[order[k]];
-      while (k < V && lv[order[k]] == val) cum += out[order[k++]];
-      if (cum >= need) { t = val; found = 1; break; }
-    }
-    if (found)
-      for (int v = 0; v < V; ++v)
-        if (lv[v] < t) out[v] = 0.0;
-  }
+  const double t = cut ? (double)*cut : nucleus_cut(lv, out, V, top_p, order);
+  for (int v = 0; v < V; ++v)
+    if (lv[v] < t) out[v] = 0.0;
   double Z = 0.0;
   for (int v = 0; v < V; ++v) Z += out[v];
   for (int v = 0; v < V; ++v) out[v] /= Z;
+  if (cut_used) *cut_used = (float)t;
 }
 
 /* Logits given: target [B][D+1][V] and draft [B][D][V] of element type dtype
  * (widened exactly), turned into p and q by softmax_row with the same
- * temperature and top-p, then decided as oracle_verify_sample does. */
+ * temperature and top-p, then decided as oracle_verify_sample does.  `cut`
+ * (nullable) gives every row's nucleus threshold instead, [B][2D+1] with the
+ * D+1 target rows of a batch row before its D draft rows; `cut_used`
+ * (nullable, same layout) receives the thresholds applied. */
 EXPORT int oracle_verify_sample_logits(const void *target, const void *draftl, int dtype, int B, int D, int V,
-                                       float temperature, float top_p, const int32_t *draft,
+                                       float temperature, float top_p, const float *cut, const int32_t *draft,
                                        const float *u_accept, const float *u_draw, int32_t *accept_len,
-                                       int32_t *next_token, double *mass) {
+                                       int32_t *next_token, double *mass, float *cut_used) {
   if (B < 0 || D < 0 || V <= 0 || !(temperature > 0.0f) || !isfinite(temperature) || !(top_p > 0.0f) ||
       top_p > 1.0f)
     return O_E_ARG;
   int rc = O_OK;
+  const int R = 2 * D + 1;
   double *P = (double *)malloc(sizeof(double) * (size_t)(D + 1) * V);
   double *Q = (double *)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1) * V);
   double *w = (double *)malloc(sizeof(double) * (size_t)V);
   double *lv = (double *)malloc(sizeof(double) * (size_t)V);
   int *order = (int *)malloc(sizeof(int) * (size_t)V);
   for (int b = 0; b < B; ++b) {
+    const int64_t r0 = (int64_t)b * R;
     for (int i = 0; i <= D; ++i)
-      softmax_row(target, dtype, ((int64_t)b * (D + 1) + i) * V, V, temperature, top_p, P + (int64_t)i * V, lv,
-                  order);
+      softmax_row(target, dtype, ((int64_t)b * (D + 1) + i) * V, V, temperature, top_p, cut ? cut + r0 + i : NULL,
+                  P + (int64_t)i * V, lv, order, cut_used ? cut_used + r0 + i : NULL);
     for (int i = 0; i < D; ++i)
-      softmax_row(draftl, dtype, ((int64_t)b * D + i) * V, V, temperature, top_p, Q + (int64_t)i * V, lv, order);
+      softmax_row(draftl, dtype, ((int64_t)b * D + i) * V, V, temperature, top_p,
+                  cut ? cut + r0 + D + 1 + i : NULL, Q + (int64_t)i * V, lv, order,
+                  cut_used ? cut_used + r0 + D + 1 + i : NULL);
     if (sample_row(P, Q, D, V, draft + (int64_t)b * D, u_accept + (int64_t)b * D, u_draw + (int64_t)b * (D + 1),
                    w, &accept_len[b], &next_token[b], mass ? &mass[b] : NULL))
       rc = O_E_PRECOND;
@@ -263,13 +279,14 @@ EXPORT int oracle_verify_sample_logits(const void *target, const void *draftl, i
 }
 
 /* One row's probabilities as softmax_row computes them (for tests: the band
- * rule needs the exact masses the draw compared). */
-EXPORT int oracle_softmax_row(const void *logits, int dtype, int V, float temperature, float top_p, double *out) {
+ * rule needs the exact masses the draw compared); `cut` as above, nullable. */
+EXPORT int oracle_softmax_row(const void *logits, int dtype, int V, float temperature, float top_p,
+                              const float *cut, double *out) {
   if (V <= 0 || !(temperature > 0.0f) || !isfinite(temperature) || !(top_p > 0.0f) || top_p > 1.0f)
     return O_E_ARG;
   double *lv = (double *)malloc(sizeof(double) * (size_t)V);
   int *order = (int *)malloc(sizeof(int) * (size_t)V);
-  softmax_row(logits, dtype, 0, V, temperature, top_p, out, lv, order);
+  softmax_row(logits, dtype, 0, V, temperature, top_p, cut, out, lv, order, NULL);
   free(lv);
   free(order);
   return O_OK;

@@ -87,6 +87,37 @@ def test_top_p_keeps_every_tie_at_the_cutoff():
     assert np.array_equal(p, oracle.softmax_row(l, 1.0))
 
 
+def test_top_p_reported_and_forced_cutoff():
+    """The threshold the oracle applies is the hand-worked one (the 0.3 logit at
+    top_p 0.7, the 0.15 logit at 0.9, -inf when every id is kept), and forcing
+    a threshold forms exactly that nucleus."""
+    probs = np.array([0.05, 0.5, 0.15, 0.3])
+    l = np.log(probs).astype(np.float32)
+    TL = np.broadcast_to(l, (4, 1, 4)).copy()
+    DL = np.zeros((4, 0, 4), np.float32)
+    draft = np.zeros((4, 0), np.int32)
+    ua = np.zeros((4, 0), np.float32)
+    ud = np.full((4, 1), 0.5, np.float32)
+    for tp, want in ((0.7, l[3]), (0.9, l[2]), (0.4, l[1]), (1.0, -np.inf)):
+        *_, used = oracle.verify_sample_logits(TL, DL, draft, ua, ud, 1.0, top_p=tp, return_cut=True)
+        assert np.all(used == want), (tp, used)
+    # a forced threshold overrides top_p: the 0.15 logit keeps three ids
+    assert np.array_equal(oracle.softmax_row(l, 1.0, top_p=0.7, cut=l[2]), oracle.softmax_row(l, 1.0, top_p=0.9))
+    assert np.array_equal(oracle.softmax_row(l, 1.0, top_p=0.5, cut=-np.inf), oracle.softmax_row(l, 1.0))
+    # verification with the thresholds it computed itself is unchanged
+    rng = np.random.default_rng(17)
+    B, D, V = 6, 3, 400
+    tl = (rng.standard_normal((B, D + 1, V)) * 2).astype(np.float32)
+    dl = (tl[:, :D] + rng.standard_normal((B, D, V)) * 0.5).astype(np.float32)
+    dr = dl.argmax(-1).astype(np.int32)
+    u1 = rng.random((B, D)).astype(np.float32)
+    u2 = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt, mass, used = oracle.verify_sample_logits(tl, dl, dr, u1, u2, 0.8, top_p=0.85, return_cut=True)
+    assert np.all(np.isfinite(used))
+    acc2, nxt2, mass2 = oracle.verify_sample_logits(tl, dl, dr, u1, u2, 0.8, top_p=0.3, cut=used)
+    assert np.array_equal(acc, acc2) and np.array_equal(nxt, nxt2) and np.array_equal(mass, mass2)
+
+
 def test_top_p_invalid_settings_rejected():
     for T, tp in ((0.0, 1.0), (-1.0, 1.0), (np.inf, 1.0), (1.0, 0.0), (1.0, 1.5)):
         with pytest.raises(oracle.OracleError):
