@@ -142,12 +142,23 @@ size_t specdec_sample_workspace_bytes(int B, int D, int V);
  *
  *  target        device [B][D+1][V] target logits of element type `dtype`.
  *  draft_logits  device [B][D][V] draft-model logits of the same type.
- *  temperature   > 0 and finite: p(v) = exp((l(v) - M) / T) / Z with M the
- *                row maximum and Z the row's sum, all in fp64.
- *  top_p         in (0, 1]; only 1 (no nucleus) is accepted by this version.
+ *  temperature   > 0 and finite: e(v) = exp((l(v) - M) / T) with M the row
+ *                maximum, in fp64.
+ *  top_p         in (0, 1].  Below 1 every row (target and draft alike) is cut
+ *                to its nucleus: the ids whose logit is at least t, where t is
+ *                the largest logit value such that the ids at or above it hold
+ *                at least top_p of the row's mass sum(e); every id tied at t is
+ *                kept.  The masses deciding t are summed exactly as integer
+ *                multiples of 2^-41 (of the maximum's mass), so t differs from
+ *                an fp64 evaluation only where the mass above a value is within
+ *                V * 2^-42 of top_p * sum(e).  At 1 every id is kept.
+ *                p(v) = e(v) / Z over the kept ids (Z in fp64), 0 elsewhere.
  *  draft, u_accept, u_draw, accept_len, next_token, status
  *                as for specdec_verify_sample; the acceptance test and the
  *                draw compare fp64 values formed on the device.
+ *  cutoff        nullable device float [B][2D+1] out: the threshold t applied
+ *                to each row, the D+1 target rows of a batch row before its D
+ *                draft rows (-inf when every id is kept).
  *  ws            device workspace of at least specdec_sample_workspace_bytes
  *                (B, D, V) bytes, 16-byte aligned; scratch only, nothing is
  *                kept between calls.  Calls that share a workspace must not
@@ -158,8 +169,8 @@ size_t specdec_sample_workspace_bytes(int B, int D, int V);
  * of range, NULL pointers), E_DTYPE, E_WORKSPACE, E_ALIGN, E_LAUNCH. */
 int specdec_verify_sample_logits(const void *target, const void *draft_logits, int dtype, int B, int D, int V,
                                  float temperature, float top_p, const int32_t *draft, const float *u_accept,
-                                 const float *u_draw, int32_t *accept_len, int32_t *next_token, void *ws,
-                                 size_t ws_bytes, int32_t *status, void *stream);
+                                 const float *u_draw, int32_t *accept_len, int32_t *next_token, float *cutoff,
+                                 void *ws, size_t ws_bytes, int32_t *status, void *stream);
 
 /* --------------------------------------------------------------- realign */
 

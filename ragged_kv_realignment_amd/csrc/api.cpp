@@ -123,7 +123,7 @@ EXPORT int specdec_verify_sample(const float *p, const float *q, int B, int D, i
 // Workspace of specdec_verify_sample_logits: per-split row statistics, per-split
 // masses and the stop position of every batch row.
 struct SlLayout {
-  size_t stats, part, thr, rowinfo, stop, total;
+  size_t stats, part, thr, rowinfo, nuc, stop, total;
 };
 
 static SlLayout sl_layout(int B, int D, int V) {
@@ -134,7 +134,8 @@ static SlLayout sl_layout(int B, int D, int V) {
   l.part = up((size_t)B * R * S * 16);
   l.thr = l.part + up((size_t)B * S * 16);
   l.rowinfo = l.thr + up((size_t)B * S * sd::kSlThreads * 16);
-  l.stop = l.rowinfo + up((size_t)B * 32);
+  l.nuc = l.rowinfo + up((size_t)B * 64);
+  l.stop = l.nuc + up((size_t)B * R * 32);
   l.total = l.stop + up((size_t)B * 4);
   return l;
 }
@@ -147,11 +148,10 @@ EXPORT size_t specdec_sample_workspace_bytes(int B, int D, int V) {
 EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_logits, int dtype, int B, int D,
                                         int V, float temperature, float top_p, const int32_t *draft,
                                         const float *u_accept, const float *u_draw, int32_t *accept_len,
-                                        int32_t *next_token, void *ws, size_t ws_bytes, int32_t *status,
-                                        void *stream) {
+                                        int32_t *next_token, float *cutoff, void *ws, size_t ws_bytes,
+                                        int32_t *status, void *stream) {
   if (B < 0 || B > 65535 || D < 0 || D > 255 || V < 1 || V > (1 << 22)) return SPECDEC_E_ARG;
   if (!(temperature > 0.0f) || !isfinite(temperature) || !(top_p > 0.0f) || top_p > 1.0f) return SPECDEC_E_ARG;
-  if (top_p < 1.0f) return SPECDEC_E_ARG;  // the nucleus is not implemented on the device yet
   if (dtype != SPECDEC_F32 && dtype != SPECDEC_F16 && dtype != SPECDEC_BF16) return SPECDEC_E_DTYPE;
   if (B == 0) return SPECDEC_OK;
   if (!target || !u_draw || !accept_len || !next_token || (D > 0 && (!draft_logits || !draft || !u_accept)))
@@ -168,6 +168,9 @@ EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_lo
   s.V = V;
   s.S = (int)((V + sd::kSlChunk - 1) / sd::kSlChunk);
   s.inv_t = 1.0 / (double)temperature;
+  s.top_p = top_p;
+  s.nucleus = top_p < 1.0f;
+  s.cutoff = cutoff;
   s.draft = draft;
   s.u_accept = u_accept;
   s.u_draw = u_draw;
@@ -179,6 +182,7 @@ EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_lo
   s.part = reinterpret_cast<double *>(w + l.part);
   s.thr = reinterpret_cast<double *>(w + l.thr);
   s.rowinfo = reinterpret_cast<double *>(w + l.rowinfo);
+  s.nuc = reinterpret_cast<double *>(w + l.nuc);
   s.stop = reinterpret_cast<int32_t *>(w + l.stop);
   const size_t e = dtype == SPECDEC_F32 ? 4 : 8;  // logits per 16-byte vector
   s.vec = (size_t)V % e == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&

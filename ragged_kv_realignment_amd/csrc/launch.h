@@ -33,6 +33,8 @@ struct SampleLogitsParams {
   const void *target, *draftl;  // logits [B][D+1][V] and [B][D][V] of `dtype`
   int dtype, B, D, V, S;        // S = splits of kSlChunk logits per row
   double inv_t;                 // 1 / temperature
+  float top_p;                  // nucleus mass, in (0, 1]
+  bool nucleus;                 // top_p < 1: cut every row to its nucleus
   bool vec;                     // rows 16-byte aligned: vector loads
   const int32_t *draft;
   const float *u_accept, *u_draw;
@@ -40,8 +42,11 @@ struct SampleLogitsParams {
   double *stats;                // workspace [B][2D+1][S] x (max, exp-sum)
   double *part;                 // workspace [B][S] x (residual mass, target mass)
   double *thr;                  // workspace [B][S][kBlock] x the same per thread run
-  double *rowinfo;              // workspace [B] x (M, 1/Z) of the stop position's target and draft rows
+  double *rowinfo;              // workspace [B] x 8: (M, 1/Z) of the stop position's target and draft
+                                // rows, then their nucleus thresholds
+  double *nuc;                  // workspace [B][2D+1] x 4: (M, 1/Z, threshold) of every nucleus
   int32_t *stop;                // workspace [B]: stop position
+  float *cutoff;                // optional out [B][2D+1]: every row's threshold (-inf: no nucleus)
 };
 
 constexpr int kSlChunk = 4096;   // logits per split in sampled verification from logits

@@ -7,11 +7,22 @@
 // and draft rows, formed on the fly in fp64: e(v) = exp((l(v) - M) * (1/T)) with
 // M the row maximum, p(v) = e(v) * (1/Z).  Every decision compares fp64 values.
 //
-// Three launches, no state kept in the workspace between calls:
+// With top-p the distribution is cut to its nucleus first: every id whose
+// logit is at least t, where t is the largest logit value such that the ids at
+// or above it hold at least top_p of the row's mass; ties at t are all kept,
+// and p is renormalised over the nucleus.
+//
+// Three launches (four with top-p), no state kept in the workspace between
+// calls:
 //  1. k_sl_stats: one workgroup per (split of kSlChunk logits, row, batch row)
 //     writes the split's maximum and its exp-sum relative to that maximum.
+//  1b. k_sl_nucleus (top-p only): one workgroup per (row, batch row) selects t
+//     by a most-significant-digit-first radix select over the logits' order
+//     keys, with masses held as 2^-41 fixed-point integers so every sum is
+//     exact and order-free, then sums the nucleus mass Z in fp64.
 //  2. k_sl_mass: one workgroup per (split, batch row) merges the statistics of
-//     the 2D+1 rows, evaluates the acceptance test of every draft (the same
+//     the 2D+1 rows (or reads the nucleus ones), evaluates the acceptance test
+//     of every draft (the same
 //     result in every workgroup of the batch row), and sums the stop row's
 //     residual mass max(0, p - q) (or p at position D) and its target mass
 //     over its split.
@@ -173,6 +184,162 @@ __global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
   }
 }
 
+// ------------------------------------------------------------------ top-p
+constexpr int kNucThreads = 1024;  // threads per nucleus workgroup (16 waves)
+constexpr int kNucBins = 2048;     // 11-bit digits: key bits 31..21, 20..10, 9..0
+constexpr int kNucUnroll = 4;      // 16-byte vectors in flight per thread
+constexpr double kFix = 2199023255552.0;  // 2^41: V <= 2^22 masses <= 1 sum below 2^63
+
+// Order key of a logit: larger key = larger value; -0.0 is folded onto +0.0
+// so equal values share a key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Every logit of one row for this thread of kNucThreads, in any order: f(x).
+template <int DT, bool VEC, class F>
+__device__ __forceinline__ void each_logit(const void *base, int64_t off, int V, F &&f) {
+  if (VEC) {
+    constexpr int E = DT == SPECDEC_F32 ? 4 : 8;
+    const int nv = V / E;
+    for (int j0 = threadIdx.x; j0 < nv; j0 += kNucThreads * kNucUnroll) {
+      uint4 v[kNucUnroll];
+#pragma unroll
+      for (int u = 0; u < kNucUnroll; ++u) {
+        const int j = min(j0 + u * kNucThreads, nv - 1);  // in range: a repeated load, never used
+        v[u] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + (off * (16 / E)) + (int64_t)j * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kNucUnroll; ++u) {
+        if (j0 + u * kNucThreads >= nv) break;
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (DT == SPECDEC_F32) {
+            f(__uint_as_float(w[e]));
+          } else {
+            f(DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] & 0xFFFFu) : bf16_bits_to_f32(w[e] & 0xFFFFu));
+            f(DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] >> 16) : bf16_bits_to_f32(w[e] >> 16));
+          }
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += kNucThreads) f(logit_at<DT>(base, off + i));
+  }
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned long long y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// One workgroup per (row r of 2D+1, batch row b): the nucleus threshold t and
+// 1/Z over the nucleus, written to nuc[(b R + r) * 4 + {0, 1, 2}] = (M, 1/Z, t).
+// t is found digit by digit from the top.  At each level the histogram holds,
+// per digit value, the fixed-point mass of the ids whose key agrees with the
+// digits chosen so far; the chosen digit is the largest d whose mass at or
+// above d, plus the mass of everything above the current prefix, reaches
+// need = top_p * (row mass).  After the last digit the key is t's.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p) {
+  __shared__ unsigned long long hist[kNucBins];
+  __shared__ unsigned long long s_wt[kNucThreads / kWave];
+  __shared__ double s_d[kNucThreads / kWave];
+  __shared__ int s_i[kNucThreads / kWave];
+  __shared__ unsigned long long s_above;
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int D = p.D, V = p.V, R = 2 * D + 1;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const void *base = r <= D ? p.target : p.draftl;
+  const int64_t off = r <= D ? target_row(p, b, r) : draft_row(p, b, r - D - 1);
+  // row maximum from the split statistics
+  double m = -INFINITY;
+  for (int k = threadIdx.x; k < p.S; k += kNucThreads) m = fmax(m, p.stats[(((int64_t)b * R + r) * p.S + k) * 2]);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  if (lane == 0) s_d[wv] = m;
+  __syncthreads();
+  double M = s_d[0];
+#pragma unroll
+  for (int k = 1; k < kNucThreads / kWave; ++k) M = fmax(M, s_d[k]);
+  const double inv_t = p.inv_t;
+  auto fixed_mass = [&](float x) -> unsigned long long {
+    return (unsigned long long)(exp(((double)x - M) * inv_t) * kFix + 0.5);
+  };
+  uint32_t prefix = 0;
+  unsigned long long above = 0;
+  double need = 0.0;
+#pragma unroll 1
+  for (int level = 0; level < 3; ++level) {
+    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+    const int bits = level == 2 ? 10 : 11;
+    const uint32_t mask = (1u << bits) - 1u;
+    const int hi = shift + bits;  // key bits from `hi` up are fixed by `prefix` (none at level 0)
+    for (int k = threadIdx.x; k < kNucBins; k += kNucThreads) hist[k] = 0;
+    __syncthreads();
+    each_logit<DT, VEC>(base, off, V, [&](float x) {
+      const uint32_t key = order_key(x);
+      if (hi == 32 || (key >> hi) == prefix) {
+        const unsigned long long fx = fixed_mass(x);
+        if (fx) atomicAdd(&hist[(key >> shift) & mask], fx);
+      }
+    });
+    __syncthreads();
+    // thread j owns bins dh = kNucBins-1-2j and dl = dh-1; scanning j upwards
+    // gives the mass at or above each bin
+    const int dh = kNucBins - 1 - 2 * (int)threadIdx.x, dl = dh - 1;
+    const unsigned long long h_hi = hist[dh], h_lo = hist[dl];
+    unsigned long long incl = wave_incl_scan_u64(h_hi + h_lo, lane);
+    if (lane == kWave - 1) s_wt[wv] = incl;
+    __syncthreads();
+    unsigned long long total = 0;
+#pragma unroll
+    for (int k = 0; k < kNucThreads / kWave; ++k) {
+      if (k < wv) incl += s_wt[k];
+      total += s_wt[k];
+    }
+    if (level == 0) need = (double)p.top_p * (double)total;
+    const unsigned long long suf_lo = incl, suf_hi = incl - h_lo;
+    int cand = -1;
+    if ((double)(above + suf_hi) >= need) cand = dh;
+    else if ((double)(above + suf_lo) >= need) cand = dl;
+    const int d = block_max_int<kNucThreads>(cand, s_i);
+    if (d >= 0 && cand == d) s_above = above + (d == dh ? suf_hi - h_hi : suf_lo - h_lo);
+    __syncthreads();
+    above = s_above;
+    prefix = (prefix << bits) | (uint32_t)max(d, 0);
+  }
+  const float t = key_value(prefix);
+  // Z over the nucleus in fp64: thread sums in its own order, then a fixed-order block sum
+  double z = 0.0;
+  each_logit<DT, VEC>(base, off, V, [&](float x) {
+    if (x >= t) z += exp(((double)x - M) * inv_t);
+  });
+  z = wave_sum(z);
+  __syncthreads();
+  if (lane == 0) s_d[wv] = z;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double zz = 0.0;
+#pragma unroll
+    for (int k = 0; k < kNucThreads / kWave; ++k) zz += s_d[k];
+    double *o = p.nuc + ((int64_t)b * R + r) * 4;
+    o[0] = M;
+    o[1] = 1.0 / zz;
+    o[2] = (double)t;
+  }
+}
+
 // This thread's kSlPer consecutive logits of a split, ids t * kSlPer + k (the
 // mass and draw kernels scan ids in order); ids at or past n read as -inf.
 template <int DT, bool VEC>
@@ -206,27 +373,43 @@ __device__ __forceinline__ void load_run(const void *base, int64_t off, int t, i
   }
 }
 
+// Probability of a logit in a row with maximum M, 1/Z and nucleus threshold
+// cut (-inf: every id): 0 below the cut and for -inf logits.
+__device__ __forceinline__ double prob(float l, double M, double iz, float cut, double inv_t) {
+  return l >= cut ? exp(((double)l - M) * inv_t) * iz : 0.0;
+}
+
 // The stop row's weight at one logit: max(0, p - q) at a < D (resid), else p.
-__device__ __forceinline__ double weight(float lt, float lq, bool resid, double Mt, double izt, double Mq, double izq,
-                                         double inv_t) {
-  const double pv = exp(((double)lt - Mt) * inv_t) * izt;  // 0 for -inf
+__device__ __forceinline__ double weight(float lt, float lq, bool resid, const double *ri, double inv_t) {
+  const double pv = prob(lt, ri[0], ri[1], (float)ri[4], inv_t);
   if (!resid) return pv;
-  const double d = pv - exp(((double)lq - Mq) * inv_t) * izq;
+  const double d = pv - prob(lq, ri[2], ri[3], (float)ri[5], inv_t);
   return d > 0.0 ? d : 0.0;
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
   __shared__ double s_m[kSlMaxRows], s_iz[kSlMaxRows];
+  __shared__ float s_cut[kSlMaxRows];
   __shared__ int s_i[kBlock / kWave];
   __shared__ double s_d[kBlock / kWave];
   const int s = blockIdx.x, b = blockIdx.y;
   const int D = p.D, V = p.V, R = 2 * D + 1;
   for (int r = threadIdx.x; r < R; r += kBlock) {
     double M, iz;
-    merge_row(p.stats + ((int64_t)b * R + r) * p.S * 2, p.S, p.inv_t, M, iz);
+    float cut = -INFINITY;
+    if (p.nucleus) {
+      const double *o = p.nuc + ((int64_t)b * R + r) * 4;
+      M = o[0];
+      iz = o[1];
+      cut = (float)o[2];
+    } else {
+      merge_row(p.stats + ((int64_t)b * R + r) * p.S * 2, p.S, p.inv_t, M, iz);
+    }
     s_m[r] = M;
     s_iz[r] = iz;
+    s_cut[r] = cut;
+    if (s == 0 && p.cutoff) p.cutoff[(int64_t)b * R + r] = cut;
   }
   __syncthreads();
   // acceptance of every draft: u * q(x) <= p(x); q(x) = 0 accepts iff p(x) > 0
@@ -235,9 +418,9 @@ __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
     const int x = p.draft[(int64_t)b * D + i];
     bool ok = false;
     if (x >= 0 && x < V) {
-      const double pt = exp(((double)logit_at<DT>(p.target, target_row(p, b, i) + x) - s_m[i]) * p.inv_t) * s_iz[i];
-      const double qd =
-          exp(((double)logit_at<DT>(p.draftl, draft_row(p, b, i) + x) - s_m[D + 1 + i]) * p.inv_t) * s_iz[D + 1 + i];
+      const double pt = prob(logit_at<DT>(p.target, target_row(p, b, i) + x), s_m[i], s_iz[i], s_cut[i], p.inv_t);
+      const double qd = prob(logit_at<DT>(p.draftl, draft_row(p, b, i) + x), s_m[D + 1 + i], s_iz[D + 1 + i],
+                             s_cut[D + 1 + i], p.inv_t);
       const double u = (double)p.u_accept[(int64_t)b * D + i];
       ok = qd > 0.0 ? (u * qd <= pt) : (pt > 0.0);
     } else {
@@ -253,20 +436,20 @@ __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
   const bool resid = a < D;
   float lt[kSlPer], lq[kSlPer];
   load_run<DT, VEC>(p.target, target_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lt);
-  if (resid) load_run<DT, VEC>(p.draftl, draft_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lq);
-  const double Mt = s_m[a], izt = s_iz[a];
-  const double Mq = resid ? s_m[D + 1 + a] : 0.0, izq = resid ? s_iz[D + 1 + a] : 0.0;
+  if (resid) {
+    load_run<DT, VEC>(p.draftl, draft_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lq);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSlPer; ++k) lq[k] = 0.0f;
+  }
+  // (M, 1/Z) of the stop row's target and draft rows and their thresholds
+  const double ri[6] = {s_m[a], s_iz[a], resid ? s_m[D + 1 + a] : 0.0, resid ? s_iz[D + 1 + a] : 0.0,
+                        (double)s_cut[a], resid ? (double)s_cut[D + 1 + a] : 0.0};
   double wsum = 0.0, psum = 0.0;
 #pragma unroll 4
   for (int k = 0; k < kSlPer; ++k) {
-    const double pv = exp(((double)lt[k] - Mt) * p.inv_t) * izt;
-    double w = pv;
-    if (resid) {
-      const double d = pv - exp(((double)lq[k] - Mq) * p.inv_t) * izq;
-      w = d > 0.0 ? d : 0.0;
-    }
-    wsum += w;
-    psum += pv;
+    wsum += weight(lt[k], lq[k], resid, ri, p.inv_t);
+    psum += prob(lt[k], ri[0], ri[1], (float)ri[4], p.inv_t);
   }
   double *thr = p.thr + (((int64_t)b * p.S + s) * kBlock + threadIdx.x) * 2;
   thr[0] = wsum;
@@ -277,11 +460,9 @@ __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
     p.part[((int64_t)b * p.S + s) * 2] = wsum;
     p.part[((int64_t)b * p.S + s) * 2 + 1] = psum;
     if (s == 0) {
-      double *ri = p.rowinfo + (int64_t)b * 4;
-      ri[0] = Mt;
-      ri[1] = izt;
-      ri[2] = Mq;
-      ri[3] = izq;
+      double *o = p.rowinfo + (int64_t)b * 8;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) o[k] = ri[k];
       p.stop[b] = a;
     }
   }
@@ -373,9 +554,10 @@ __global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
   if (threadIdx.x < kSlPer && run >= 0 && i < n) {
     const float lt = logit_at<DT>(p.target, target_row(p, b, a) + v0 + i);
     const float lq = resid ? logit_at<DT>(p.draftl, draft_row(p, b, a) + v0 + i) : 0.0f;
-    const double Mt = p.rowinfo[(int64_t)b * 4], izt = p.rowinfo[(int64_t)b * 4 + 1];
-    const double Mq = p.rowinfo[(int64_t)b * 4 + 2], izq = p.rowinfo[(int64_t)b * 4 + 3];
-    w = weight(lt, lq, resid, Mt, izt, Mq, izq, p.inv_t);
+    double ri[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) ri[k] = p.rowinfo[(int64_t)b * 8 + k];
+    w = weight(lt, lq, resid, ri, p.inv_t);
   }
   if (threadIdx.x < kWave) {
     const double c = s_base + wave_incl_scan(w, lane);
@@ -397,6 +579,12 @@ static hipError_t launch_sl(const SampleLogitsParams &p, hipStream_t s) {
                      dim3(kBlock), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.nucleus) {
+    hipLaunchKernelGGL((k_sl_nucleus<DT, VEC>), dim3((unsigned)(2 * p.D + 1), (unsigned)p.B), dim3(kNucThreads), 0,
+                       s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_sl_mass<DT, VEC>), dim3((unsigned)p.S, (unsigned)p.B), dim3(kBlock), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

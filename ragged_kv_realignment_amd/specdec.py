@@ -59,7 +59,7 @@ def lib():
         L.specdec_sample_workspace_bytes.argtypes = [ci, ci, ci]
         L.specdec_sample_workspace_bytes.restype = sz
         L.specdec_verify_sample_logits.argtypes = [vp, vp, ci, ci, ci, ci, C.c_float, C.c_float, vp, vp, vp, vp, vp,
-                                                   vp, sz, vp, vp]
+                                                   vp, vp, sz, vp, vp]
         L.specdec_realign_kv.argtypes = [ci, C.POINTER(SeqBufC), C.POINTER(SeqBufC), vp, ci, ci, vp, ci, vp, vp,
                                          vp, vp, C.c_int32, vp, vp]
         L.specdec_group_by_len.argtypes = [vp, ci, ci, vp, vp, vp, vp, vp]
@@ -172,10 +172,11 @@ def sample_workspace(B, D, V, device="cuda"):
 
 
 def specdec_verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, temperature, top_p=1.0, ws=None,
-                                 status=None, accept_len=None, next_token=None):
+                                 status=None, accept_len=None, next_token=None, cutoff=None):
     """Sampled verification from logits: target [B, D+1, V] and draft_logits [B, D, V]
-    (float32, float16 or bfloat16), turned into p and q by the temperature (and
-    top-p) on the device.  Returns (accept_len, next_token)."""
+    (float32, float16 or bfloat16), turned into p and q by the temperature and
+    top-p on the device.  Returns (accept_len, next_token); `cutoff` (float32
+    [B, 2D+1], optional) receives every row's nucleus threshold."""
     _need(target, "target")
     if target.dtype not in _TORCH_DT or target.dim() != 3:
         raise ValueError("target must be a [B, D+1, V] float32/float16/bfloat16 tensor")
@@ -192,10 +193,15 @@ def specdec_verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, 
     ws = sample_workspace(B, D, V, dev) if ws is None else ws
     accept_len = _i32(B, dev) if accept_len is None else accept_len
     next_token = _i32(B, dev) if next_token is None else next_token
+    if cutoff is not None:
+        _need(cutoff, "cutoff", torch.float32)
+        if cutoff.numel() != B * (2 * D + 1):
+            raise ValueError("cutoff must hold B * (2D+1) floats")
     rc = lib().specdec_verify_sample_logits(target.data_ptr(), draft_logits.data_ptr(), _TORCH_DT[target.dtype], B,
                                             D, V, float(temperature), float(top_p), draft.data_ptr(),
                                             u_accept.data_ptr(), u_draw.data_ptr(), _ptr(accept_len),
-                                            _ptr(next_token), ws.data_ptr(), ws.numel(), _ptr(status), _stream())
+                                            _ptr(next_token), _ptr(cutoff), ws.data_ptr(), ws.numel(), _ptr(status),
+                                            _stream())
     _check(rc, "specdec_verify_sample_logits")
     return accept_len, next_token
 

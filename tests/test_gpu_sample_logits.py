@@ -1,9 +1,11 @@
-"""GPU parity of sampled verification from logits (temperature softmax fused
-into the kernels) against the oracle.  Both sides decide in fp64 from the same
-logits; they differ only in the rounding of exp and of the order of sums, so a
-decision may differ only where the oracle's own values put it within the band
-(1e-6 relative) of its threshold, and the GPU's outcome must then be one of
-the admissible ones."""
+"""GPU parity of sampled verification from logits (temperature softmax and the
+top-p nucleus fused into the kernels) against the oracle.  Both sides decide in
+fp64 from the same logits; they differ only in the rounding of exp and of the
+order of sums (and, for the nucleus, in summing masses as 2^-41 fixed-point
+integers), so a decision may differ only where the oracle's own values put it
+within the band (1e-6 relative) of its threshold, and the GPU's outcome must
+then be one of the admissible ones.  A nucleus threshold the GPU chose within
+the band is checked admissible, and the oracle then continues from it."""
 import numpy as np
 import pytest
 import torch
@@ -46,12 +48,34 @@ def _admissible_draw(w, u, j):
     return w[j] > 0 and lo - BAND * T <= t < c[j] + BAND * T
 
 
-def check_round(tl, dl, draft, u_acc, u_draw, temperature, acc, nxt, top_p=1.0):
+def _admissible_cut(l, temperature, top_p, t):
+    """Is t an admissible nucleus threshold of logits l: the mass at or above t
+    reaches top_p and the mass strictly above it does not, within the band?"""
+    e = oracle.softmax_row(l, temperature)
+    lv = l.astype(np.float32) if l.dtype != np.uint16 else (l.astype(np.uint32) << 16).view(np.float32)
+    if not np.isfinite(t) or not np.any(lv == t):
+        return False
+    at_or_above, above = e[lv >= t].sum(), e[lv > t].sum()
+    return at_or_above >= top_p - BAND and above < top_p + BAND
+
+
+def check_round(tl, dl, draft, u_acc, u_draw, temperature, acc, nxt, top_p=1.0, cut=None):
     """Every GPU decision against the oracle's arithmetic; returns the number of
-    rows whose outcome differs from the oracle's (each one shown admissible)."""
-    oacc, onxt, _ = oracle.verify_sample_logits(tl, dl, draft, u_acc, u_draw, temperature, top_p)
+    rows whose outcome differs from the oracle's (each one shown admissible).
+    With top-p, `cut` holds the GPU's nucleus thresholds [B, 2D+1]: each one
+    that differs from the oracle's must be admissible, and the oracle then
+    decides with the GPU's thresholds."""
     B, D1, V = tl.shape
     D = D1 - 1
+    if top_p < 1.0:
+        _, _, _, ocut = oracle.verify_sample_logits(tl, dl, draft, u_acc, u_draw, temperature, top_p,
+                                                    return_cut=True)
+        for b, r in zip(*np.nonzero(cut != ocut)):
+            row = tl[b, r] if r <= D else dl[b, r - D - 1]
+            assert _admissible_cut(row, temperature, top_p, float(cut[b, r])), (b, r, cut[b, r], ocut[b, r])
+    else:
+        cut = np.full((B, 2 * D + 1), -np.inf, np.float32)
+    oacc, onxt, _ = oracle.verify_sample_logits(tl, dl, draft, u_acc, u_draw, temperature, top_p, cut=cut)
     differ = 0
     for b in range(B):
         if acc[b] == oacc[b] and nxt[b] == onxt[b]:
@@ -59,34 +83,43 @@ def check_round(tl, dl, draft, u_acc, u_draw, temperature, acc, nxt, top_p=1.0):
         differ += 1
         a = int(acc[b])
         assert 0 <= a <= D
+        def P(i):
+            return oracle.softmax_row(tl[b, i], temperature, top_p, cut=cut[b, i])
+        def Q(i):
+            return oracle.softmax_row(dl[b, i], temperature, top_p, cut=cut[b, D + 1 + i])
         # acceptance decisions at positions 0..a (accept before a, reject at a < D)
         for i in range(min(a + 1, D)):
             x = int(draft[b, i])
             if not 0 <= x < V:
                 assert i == a, "row %d: an out-of-range draft was accepted" % b
                 continue
-            p = oracle.softmax_row(tl[b, i], temperature, top_p)[x]
-            q = oracle.softmax_row(dl[b, i], temperature, top_p)[x]
+            p, q = P(i)[x], Q(i)[x]
             u = float(u_acc[b, i])
             ok = (u * q <= p) if q > 0 else (p > 0)
             if ok != (i < a):
                 assert q > 0 and abs(u * q - p) <= BAND * p, "row %d: decision at %d outside the band" % (b, i)
-        P = oracle.softmax_row(tl[b, a], temperature, top_p)
-        w = np.maximum(P - oracle.softmax_row(dl[b, a], temperature, top_p), 0.0) if a < D else P
+        Pa = P(a)
+        w = np.maximum(Pa - Q(a), 0.0) if a < D else Pa
         if not w.sum() > 0:
-            w = P
+            w = Pa
         assert _admissible_draw(w, u_draw[b, a], int(nxt[b])), "row %d: draw outside the band" % b
     return differ
 
 
-def _run(sd, tl, dl, draft, u_acc, u_draw, temperature, tdt=torch.float32, status=None):
+def _run(sd, tl, dl, draft, u_acc, u_draw, temperature, tdt=torch.float32, status=None, top_p=1.0,
+         want_cut=False):
     if tdt == torch.bfloat16:
         t, d = _dev(_bf16_bits(tl), torch.bfloat16), _dev(_bf16_bits(dl), torch.bfloat16)
     else:
         np_dt = np.float16 if tdt == torch.float16 else np.float32
         t, d = _dev(tl.astype(np_dt)), _dev(dl.astype(np_dt))
-    acc, nxt = sd.verify_sample_logits(t, d, _dev(draft), _dev(u_acc), _dev(u_draw), temperature, status=status)
+    B, D1, _ = tl.shape
+    cut = torch.full((B, 2 * D1 - 1), 7.0, dtype=torch.float32, device="cuda") if want_cut else None
+    acc, nxt = sd.verify_sample_logits(t, d, _dev(draft), _dev(u_acc), _dev(u_draw), temperature, top_p=top_p,
+                                       status=status, cutoff=cut)
     torch.cuda.synchronize()
+    if want_cut:
+        return acc.cpu().numpy(), nxt.cpu().numpy(), cut.cpu().numpy()
     return acc.cpu().numpy(), nxt.cpu().numpy()
 
 
@@ -213,7 +246,7 @@ def test_host_errors(sd):
     dr = torch.zeros((B, D), dtype=torch.int32, device="cuda")
     ua = torch.zeros((B, D), device="cuda")
     ud = torch.zeros((B, D + 1), device="cuda")
-    for T, tp in ((0.0, 1.0), (-1.0, 1.0), (float("inf"), 1.0), (1.0, 0.0), (1.0, 1.5), (1.0, 0.5)):
+    for T, tp in ((0.0, 1.0), (-1.0, 1.0), (float("inf"), 1.0), (1.0, 0.0), (1.0, 1.5), (1.0, float("nan"))):
         with pytest.raises(sd.SpecDecError) as e:
             sd.verify_sample_logits(t, d, dr, ua, ud, T, top_p=tp)
         assert e.value.code == -1
@@ -226,3 +259,100 @@ def test_host_errors(sd):
     # B = 0 is a no-op
     sd.verify_sample_logits(t[:0], d[:0], dr[:0], ua[:0], ud[:0], 1.0)
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------- top-p
+
+@pytest.mark.parametrize("top_p", [0.9, 0.5])
+def test_stochastic_workload_top_p(sd, top_p):
+    """The stoch workload's logits with a nucleus on every row."""
+    cfg = synth.CONFIGS["stoch"]
+    say("sample logits stoch top_p", top_p)
+    tl, dl, draft, u_acc, u_draw = synth.sampled_logits_round(cfg, 0)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, cfg.temperature, status=status, top_p=top_p,
+                         want_cut=True)
+    assert int(status.item()) == 0
+    *_, ocut = oracle.verify_sample_logits(tl, dl, draft, u_acc, u_draw, cfg.temperature, top_p, return_cut=True)
+    assert np.mean(cut == ocut) > 0.98  # the thresholds agree outside the band
+    assert check_round(tl, dl, draft, u_acc, u_draw, cfg.temperature, acc, nxt, top_p, cut) <= 1
+
+
+@pytest.mark.parametrize("seed", range(9))
+def test_top_p_random(sd, seed):
+    """Random shapes, all three logit types, ties at every value (quantised
+    logits), masked logits, D = 0 and top_p from 0.05 to 0.999."""
+    rng = np.random.default_rng(900 + seed)
+    tdt = [torch.float32, torch.float16, torch.bfloat16][seed % 3]
+    B = int(rng.integers(1, 16))
+    D = int(rng.integers(0, 6)) if seed % 4 else 0
+    V = int([rng.integers(2, 60), rng.integers(1000, 5000), rng.integers(8000, 20000)][seed % 3])
+    T = float([0.5, 1.0, 2.0][(seed // 3) % 3])
+    top_p = float([0.05, 0.6, 0.9, 0.999][seed % 4])
+    say("sample logits top_p random", seed, tdt, B, D, V, T, top_p)
+    tl = (rng.standard_normal((B, D + 1, V)) * 2).astype(np.float32)
+    dl = (tl[:, :D] + rng.standard_normal((B, D, V)) * 0.5).astype(np.float32)
+    if seed % 2 == 0:  # many ties
+        tl, dl = np.round(tl * 2) / 2, np.round(dl * 2) / 2
+    if V > 3:
+        tl[rng.random(tl.shape) < 0.05] = -np.inf
+        dl[rng.random(dl.shape) < 0.05] = -np.inf
+        tl[..., 0] = np.maximum(tl[..., 0], 0.0)
+        dl[..., 0] = np.maximum(dl[..., 0], 0.0)
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    fav = dl.argmax(-1) if D > 0 else np.zeros((B, 0), np.int64)
+    pick = rng.random((B, D)) < 0.6
+    draft[pick] = fav[pick]
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, T, tdt, top_p=top_p, want_cut=True)
+    h_t, h_d = _host_logits(tl, tdt), _host_logits(dl, tdt)
+    check_round(h_t, h_d, draft, u_acc, u_draw, T, acc, nxt, top_p, cut)
+
+
+def test_top_p_large_vocab_bf16(sd):
+    """A 151936-entry bf16 vocabulary with top_p 0.9."""
+    rng = np.random.default_rng(91)
+    B, D, V, T = 4, 3, 151936, 0.9
+    say("sample logits top_p V=151936")
+    tl = (rng.standard_normal((B, D + 1, V)) * 2).astype(np.float32)
+    dl = (tl[:, :D] + rng.standard_normal((B, D, V)) * 0.3).astype(np.float32)
+    draft = dl.argmax(-1).astype(np.int32)
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, T, torch.bfloat16, top_p=0.9, want_cut=True)
+    check_round(_bf16_bits(tl), _bf16_bits(dl), draft, u_acc, u_draw, T, acc, nxt, 0.9, cut)
+
+
+def test_vanishing_top_p_is_greedy(sd):
+    """With a nucleus holding only each row's maximum (distinct logits), p and q
+    are one-hot on the argmaxes, so sampled verification makes greedy
+    verification's decisions (checked against the GPU greedy kernel)."""
+    rng = np.random.default_rng(92)
+    B, D, V = 24, 5, 3000
+    say("sample logits top_p->0")
+    tl = rng.permuted(np.tile(np.arange(V, dtype=np.float32) / 64, (B, D + 1, 1)), axis=2)
+    dl = rng.permuted(np.tile(np.arange(V, dtype=np.float32) / 64, (B, D, 1)), axis=2)
+    for b in range(B):
+        for i in range(int(rng.integers(0, D + 1))):
+            j, m = int(np.argmax(tl[b, i])), int(np.argmax(dl[b, i]))
+            dl[b, i, [j, m]] = dl[b, i, [m, j]]
+    draft = dl.argmax(-1).astype(np.int32)
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, 1.0, top_p=1e-6, want_cut=True)
+    assert np.array_equal(cut[:, :D + 1], tl.max(-1)) and np.array_equal(cut[:, D + 1:], dl.max(-1))
+    gacc, gnxt = sd.verify_greedy(_dev(tl), _dev(draft))
+    assert np.array_equal(acc, gacc.cpu().numpy()) and np.array_equal(nxt, gnxt.cpu().numpy())
+    assert acc.min() < D and acc.max() > 0
+
+
+def test_no_nucleus_reports_minus_inf(sd):
+    rng = np.random.default_rng(93)
+    B, D, V = 3, 2, 500
+    tl = rng.standard_normal((B, D + 1, V)).astype(np.float32)
+    dl = rng.standard_normal((B, D, V)).astype(np.float32)
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    acc, nxt, cut = _run(sd, tl, dl, draft, rng.random((B, D)).astype(np.float32),
+                         rng.random((B, D + 1)).astype(np.float32), 1.0, want_cut=True)
+    assert np.all(cut == -np.inf)
