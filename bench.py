@@ -340,6 +340,46 @@ def bench_chain(args, cfg):
                  config, roof(modes[0]), cpu, extra)
 
 
+def _time_sample_logits(cfg, K):
+    """Sampled verification from the workload's raw fp32 logits (temperature
+    0.8, with and without a top-p 0.9 nucleus), K launches each, timed with
+    events on the launch stream.  Algorithmic bytes: one read of every target
+    and draft logit."""
+    import torch
+    import synth
+    import ragged_kv_realignment_amd as sd
+
+    dev = torch.device("cuda", 0)
+    tl, dl, draft, u_acc, u_draw = synth.sampled_logits_round(cfg, 0)
+    t, d, dd, dua, dud = (torch.from_numpy(x).to(dev) for x in (tl, dl, draft, u_acc, u_draw))
+    ws = sd.sample_workspace(cfg.B, cfg.D, cfg.V, dev)
+    acc = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    nxt = torch.zeros_like(acc)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = float(tl.nbytes + dl.nbytes)
+    out = {"logits": "target [%d][%d][%d] and draft [%d][%d][%d] fp32" % (cfg.B, cfg.D1, cfg.V, cfg.B, cfg.D, cfg.V),
+           "algorithmic_bytes_per_call": nbytes}
+    for top_p in (1.0, 0.9):
+        def call():
+            sd.verify_sample_logits(t, d, dd, dua, dud, cfg.temperature, top_p=top_p, ws=ws, accept_len=acc,
+                                    next_token=nxt, status=status)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = _events(K, 2)
+        for r in range(K):
+            ev[r][0].record()
+            call()
+            ev[r][1].record()
+        torch.cuda.synchronize()
+        ms = _ms(ev, 0, 1)
+        out["top_p=%g" % top_p] = {"avg_call_us": float(ms.mean() * 1e3),
+                                    "achieved_gbs": nbytes / (ms.mean() * 1e-3) / 1e9}
+    if int(status.item()) != 0:
+        raise RuntimeError("device status %d in sampled verification from logits" % int(status.item()))
+    return out
+
+
 def bench_stoch(args, cfg):
     """Sampled verification + EQSPEC realign of the fp16 cache; the same out-of-place
     round is repeated from the same state."""
@@ -403,6 +443,7 @@ def bench_stoch(args, cfg):
     rbytes = float(rb[0])
     re_gbs = rbytes / (re_ms.mean() * 1e-3) / 1e9
     ve_gbs = vbytes / (ver_ms.mean() * 1e-3) / 1e9
+    logits_legs = _time_sample_logits(cfg, K)
     cpu = None
     if not args.no_cpu:
         del src, dst
@@ -431,6 +472,7 @@ def bench_stoch(args, cfg):
               "B": cfg.B, "D": cfg.D, "V": cfg.V, "cap": cfg.cap, "global_batch": cfg.B}
     extra = {"verify": {"kernel": "k_verify_sample", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
                         "algorithmic_bytes_per_launch": vbytes, "avg_launch_us": float(ver_ms.mean() * 1e3)},
+             "verify_from_logits": logits_legs,
              "realign_share_of_round": float(re_ms.sum() / total_ms)}
     return _line("sampled verify+realign rounds/sec and realign HBM GB/s (stoch, B=32)", K / (total_ms * 1e-3), K, W,
                  total_ms / K, "f16", config,
