@@ -234,3 +234,102 @@ def append(kv_pool, tok_pool, len_pool, rows, kv_new, draft, accept_len, next_to
                                _p(len_pool), _p(_i32(rows)), B, D,
                                np.ascontiguousarray(kv_new, dtype=kv_pool.dtype).ctypes.data,
                                _p(_i32(draft).reshape(-1)), _p(_i32(accept_len)), _p(_i32(next_token))))
+
+
+# ----------------------------------------------------------------- paged KV
+
+class PagedState:
+    """A paged KV cache held in numpy arrays, operated on by the oracle's paged
+    functions.  pages [L,2,n_pages,H,page,Dh]; bt [rows,max_blocks] (-1 = none);
+    free [n_pages] stack with n_free entries; tokens [rows, max_blocks*page];
+    len [rows]."""
+
+    def __init__(self, L, H, Dh, n_pages, page, max_blocks, rows, dtype=np.float16, free_order=None):
+        self.pages = np.zeros((L, 2, n_pages, H, page, Dh), dtype)
+        self.bt = np.full((rows, max_blocks), -1, np.int32)
+        self.free = (np.arange(n_pages, dtype=np.int32) if free_order is None
+                     else np.ascontiguousarray(free_order, dtype=np.int32))
+        self.n_free = np.array([n_pages], np.int32)
+        self.tokens = np.zeros((rows, max_blocks * page), np.int32)
+        self.len = np.zeros(rows, np.int32)
+        self.geo = np.array([L, H, Dh, self.pages.itemsize, n_pages, page, max_blocks, rows], np.int32)
+
+    def copy(self):
+        c = PagedState.__new__(PagedState)
+        for k in ("pages", "bt", "free", "n_free", "tokens", "len", "geo"):
+            setattr(c, k, getattr(self, k).copy())
+        return c
+
+
+def _paged_lib():
+    L = lib()
+    if not hasattr(L, "_paged_ready"):
+        vp, i32p, i8p, ci = C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int8), C.c_int
+        L.oracle_paged_append.argtypes = [i32p, vp, i32p, i32p, i32p, i32p, i32p, i32p, ci, ci, vp, i32p, i32p, i32p,
+                                          C.c_int32, i32p, i32p, i32p, i8p, ci]
+        L.oracle_paged_gather.argtypes = [i32p, vp, i32p, i32p, i32p, i32p, ci, ci, vp, i32p, i32p, i8p, i32p, i32p,
+                                          C.c_int32]
+        L.oracle_paged_admit.argtypes = [i32p, vp, i32p, i32p, i32p, i32p, i32p, i32p, ci, vp, i32p, i32p, ci, ci]
+        L.oracle_paged_retire.argtypes = [i32p, i32p, i32p, i32p, i32p, i32p, ci]
+        for f in (L.oracle_paged_append, L.oracle_paged_gather, L.oracle_paged_admit, L.oracle_paged_retire):
+            f.restype = C.c_int
+        L._paged_ready = True
+    return L
+
+
+def paged_append(st, kv_new, draft, accept_len, next_token, rows=None, pad_token=0, rect_cap=None):
+    """One round's realignment on the paged cache `st` (modified in place).
+    Returns dict(width, tokens, pos, mask) with the [B, rect_cap] rectangle view
+    (rect_cap defaults to the pool's row capacity)."""
+    L_, two, B, H, D1, Dh = kv_new.shape
+    D = D1 - 1
+    rows = None if rows is None else _i32(rows)
+    rect_cap = st.tokens.shape[1] if rect_cap is None else rect_cap
+    tok = np.zeros((B, rect_cap), np.int32)
+    pos = np.zeros((B, rect_cap), np.int32)
+    mask = np.zeros((B, rect_cap), np.int8)
+    width = np.zeros(1, np.int32)
+    kv_new = np.ascontiguousarray(kv_new, dtype=st.pages.dtype)
+    rc = _paged_lib().oracle_paged_append(_p(st.geo), st.pages.ctypes.data, _p(st.bt), _p(st.free), _p(st.n_free),
+                                          _p(st.tokens), _p(st.len), _p(rows), B, D, kv_new.ctypes.data,
+                                          _p(_i32(draft).reshape(-1)), _p(_i32(accept_len)), _p(_i32(next_token)),
+                                          pad_token, _p(width), _p(tok), _p(pos), _p(mask, C.c_int8), rect_cap)
+    _check(rc)
+    W = int(width[0])
+    return dict(width=W, tokens=tok[:, :W], pos=pos[:, :W], mask=mask[:, :W])
+
+
+def paged_gather(st, rows=None, B=None, cap_out=None, pad_token=0):
+    """The batch's rows as a left-padded rectangle: dict(kv, tokens, pos, mask, len, width)."""
+    rows = None if rows is None else _i32(rows)
+    B = (len(rows) if rows is not None else st.len.shape[0]) if B is None else B
+    L_, _, _, H, _, Dh = st.pages.shape
+    cap_out = st.tokens.shape[1] if cap_out is None else cap_out
+    kv = np.zeros((L_, 2, B, H, cap_out, Dh), st.pages.dtype)
+    tok = np.zeros((B, cap_out), np.int32)
+    pos = np.zeros((B, cap_out), np.int32)
+    mask = np.zeros((B, cap_out), np.int8)
+    ln = np.zeros(B, np.int32)
+    width = np.zeros(1, np.int32)
+    rc = _paged_lib().oracle_paged_gather(_p(st.geo), st.pages.ctypes.data, _p(st.bt), _p(st.tokens), _p(st.len),
+                                          _p(rows), B, cap_out, kv.ctypes.data, _p(tok), _p(pos),
+                                          _p(mask, C.c_int8), _p(ln), _p(width), pad_token)
+    _check(rc)
+    W = int(width[0])
+    return dict(kv=kv[..., :W, :], tokens=tok[:, :W], pos=pos[:, :W], mask=mask[:, :W], len=ln, width=W)
+
+
+def paged_admit(st, in_kv, in_tok, in_len, S, rows=None):
+    """Rows rows[b] (empty) receive the content of a left-padded rectangle of width S."""
+    L_, _, B, H, cap_in, Dh = in_kv.shape
+    rows = None if rows is None else _i32(rows)
+    in_kv = np.ascontiguousarray(in_kv, dtype=st.pages.dtype)
+    _check(_paged_lib().oracle_paged_admit(_p(st.geo), st.pages.ctypes.data, _p(st.bt), _p(st.free), _p(st.n_free),
+                                           _p(st.tokens), _p(st.len), _p(rows), B, in_kv.ctypes.data,
+                                           _p(_i32(in_tok).reshape(-1)), _p(_i32(in_len)), int(S), cap_in))
+
+
+def paged_retire(st, rows):
+    rows = _i32(rows)
+    _check(_paged_lib().oracle_paged_retire(_p(st.geo), _p(st.bt), _p(st.free), _p(st.n_free), _p(st.len), _p(rows),
+                                            len(rows)))

@@ -529,3 +529,234 @@ EXPORT int oracle_append(int L, int H, int Dh, int esize, int N, int cap_pool, v
   }
   return O_OK;
 }
+
+/* ------------------------------------------------------------ paged KV
+ * [AB] ties the superlinear cost of realignment to contiguous cache layouts.
+ * With a block table the cache is a pool of pages of `page` positions, and a
+ * row's content position j lives in page bt[row][j / page], slot j % page:
+ *   pages       [L][2][n_pages][H][page][Dh], esize-byte elements;
+ *   bt          int32 [rows][max_blocks], -1 where a row has no page;
+ *   free_pages  int32 [n_pages], a stack whose entries [0, *n_free) are free;
+ *   tokens      int32 [rows][max_blocks * page], each row's content from 0;
+ *   len         int32 [rows].
+ * The rectangle of [BD] 2.1 (every row left-padded to the longest) is then a
+ * matter of metadata: row b's pad is S' - len'_b, its position ids run 0.. over
+ * the content.  So EQSPEC's unpad-append-repad ([BD] 2.2) reduces to
+ * appending each row's committed entries and tokens at its length; the KV
+ * already in place never moves.  A gather turns any batch of rows back into the
+ * left-padded rectangle EQSPEC would produce.
+ * Page allocation (one admissible policy, fixed so that results compare byte
+ * for byte; any policy that gives each row distinct free pages is correct):
+ * batch entries in order take their new pages from the top of the free stack,
+ * the entry's first new block getting the topmost remaining page.  Retiring
+ * pushes a row's pages back in block order, entries in batch order.
+ * geo = {L, H, Dh, esize, n_pages, page, max_blocks, rows}. */
+enum { G_L, G_H, G_DH, G_ES, G_NP, G_PAGE, G_MB, G_ROWS };
+
+static int blocks_for(int n, int page) { return (n + page - 1) / page; }
+
+/* byte offset of (layer l, K|V kv, page pg, head h, slot s) in the page pool */
+static size_t page_off(const int32_t *geo, int l, int kv, int pg, int h, int s) {
+  const size_t pbytes = (size_t)geo[G_DH] * (size_t)geo[G_ES];
+  return (((((size_t)l * 2 + kv) * geo[G_NP] + pg) * geo[G_H] + h) * geo[G_PAGE] + s) * pbytes;
+}
+
+static int paged_geo_ok(const int32_t *geo) {
+  return geo[G_L] >= 0 && geo[G_H] > 0 && geo[G_DH] > 0 && geo[G_ES] > 0 && geo[G_NP] >= 0 && geo[G_PAGE] > 0 &&
+         geo[G_MB] > 0 && geo[G_ROWS] > 0;
+}
+
+static int batch_rows_ok(const int32_t *geo, const int32_t *rows, int B) {
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b;
+    if (r < 0 || r >= geo[G_ROWS]) return 0;
+    for (int o = 0; o < b; ++o)
+      if ((rows ? rows[o] : o) == r) return 0;
+  }
+  return 1;
+}
+
+/* One round's realignment on a paged cache: batch entry b (pool row rows[b],
+ * NULL = b) commits n_b = accept_len[b] + 1 tokens (its accepted drafts, then
+ * next_token[b]) and the first n_b of its D+1 speculative KV entries kv_new
+ * [L][2][B][H][D+1][Dh], written at positions len, len+1, ... of the row;
+ * new pages come from the free stack as stated above.  *width = S' =
+ * max_b(len_b + n_b).  The rectangle view (nullable rect_* [B][rect_cap]):
+ * row b left-padded by S' - len'_b with pad_token, position id 0 and mask 0,
+ * then its content with position ids 0.. and mask 1.  Errors (nothing
+ * written): O_E_ARG for bad geometry, rows or accepted lengths outside [0, D];
+ * O_E_CAPACITY when a row would exceed max_blocks * page positions, the batch
+ * needs more pages than are free, or S' exceeds rect_cap. */
+EXPORT int oracle_paged_append(const int32_t *geo, void *pages, int32_t *bt, int32_t *free_pages, int32_t *n_free,
+                               int32_t *tokens, int32_t *len, const int32_t *rows, int B, int D,
+                               const void *kv_new, const int32_t *draft, const int32_t *accept_len,
+                               const int32_t *next_token, int32_t pad_token, int32_t *width, int32_t *rect_tok,
+                               int32_t *rect_pos, int8_t *rect_mask, int rect_cap) {
+  if (!paged_geo_ok(geo) || B < 0 || D < 0 || !batch_rows_ok(geo, rows, B)) return O_E_ARG;
+  const int page = geo[G_PAGE], tcap = geo[G_MB] * page;
+  const size_t pbytes = (size_t)geo[G_DH] * (size_t)geo[G_ES];
+  int Snew = 0, need = 0;
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = len[r], a = accept_len[b];
+    if (a < 0 || a > D || c < 0 || c > tcap) return O_E_ARG;
+    const int cn = c + a + 1;
+    if (cn > tcap) return O_E_CAPACITY;
+    need += blocks_for(cn, page) - blocks_for(c, page);
+    if (cn > Snew) Snew = cn;
+  }
+  if (need > *n_free || (rect_tok && Snew > rect_cap)) return O_E_CAPACITY;
+  /* pages: pop from the top of the free stack, batch entries in order */
+  int top = *n_free;
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = len[r], cn = c + accept_len[b] + 1;
+    for (int blk = blocks_for(c, page); blk < blocks_for(cn, page); ++blk) bt[(size_t)r * geo[G_MB] + blk] =
+        free_pages[--top];
+  }
+  *n_free = top;
+  /* committed KV entries and tokens at the row's end */
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = len[r], a = accept_len[b], n = a + 1;
+    for (int l = 0; l < geo[G_L]; ++l)
+      for (int kv = 0; kv < 2; ++kv)
+        for (int h = 0; h < geo[G_H]; ++h)
+          for (int i = 0; i < n; ++i) {
+            const int j = c + i, pg = bt[(size_t)r * geo[G_MB] + j / page];
+            const size_t src = (((((size_t)l * 2 + kv) * B + b) * geo[G_H] + h) * (size_t)(D + 1) + i) * pbytes;
+            memcpy((unsigned char *)pages + page_off(geo, l, kv, pg, h, j % page),
+                   (const unsigned char *)kv_new + src, pbytes);
+          }
+    int32_t *t = tokens + (size_t)r * tcap + c;
+    for (int i = 0; i < a; ++i) t[i] = draft[(size_t)b * D + i];
+    t[a] = next_token[b];
+    len[r] = c + n;
+  }
+  *width = Snew;
+  /* the rectangle view of the batch: [BD] 2.1's alignment as metadata */
+  if (rect_tok)
+    for (int b = 0; b < B; ++b) {
+      const int r = rows ? rows[b] : b, pad = Snew - len[r];
+      for (int j = 0; j < Snew; ++j) {
+        const int in = j >= pad;
+        rect_tok[(size_t)b * rect_cap + j] = in ? tokens[(size_t)r * tcap + j - pad] : pad_token;
+        if (rect_mask) rect_mask[(size_t)b * rect_cap + j] = (int8_t)in;
+      }
+      if (rect_pos) {
+        int8_t *m = (int8_t *)malloc((size_t)(Snew > 0 ? Snew : 1));
+        for (int j = 0; j < Snew; ++j) m[j] = (int8_t)(j >= pad);
+        positions_from_mask(m, Snew, rect_pos + (size_t)b * rect_cap);
+        free(m);
+      }
+    }
+  return O_OK;
+}
+
+/* The batch's rows as the left-padded rectangle of width W = their longest
+ * length: out_kv [L][2][B][H][cap_out][Dh] (zero bytes on the pad), tokens,
+ * position ids and mask [B][cap_out], out_len [B] and *width = W; positions
+ * [W, cap_out) are not written.  O_E_CAPACITY if W > cap_out. */
+EXPORT int oracle_paged_gather(const int32_t *geo, const void *pages, const int32_t *bt, const int32_t *tokens,
+                               const int32_t *len, const int32_t *rows, int B, int cap_out, void *out_kv,
+                               int32_t *out_tok, int32_t *out_pos, int8_t *out_mask, int32_t *out_len,
+                               int32_t *width, int32_t pad_token) {
+  if (!paged_geo_ok(geo) || B < 0 || !batch_rows_ok(geo, rows, B)) return O_E_ARG;
+  const int page = geo[G_PAGE], tcap = geo[G_MB] * page;
+  const size_t pbytes = (size_t)geo[G_DH] * (size_t)geo[G_ES];
+  int W = 0;
+  for (int b = 0; b < B; ++b) {
+    const int c = len[rows ? rows[b] : b];
+    if (c < 0 || c > tcap) return O_E_ARG;
+    if (c > W) W = c;
+  }
+  if (W > cap_out) return O_E_CAPACITY;
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = len[r], pad = W - c;
+    for (int l = 0; l < geo[G_L]; ++l)
+      for (int kv = 0; kv < 2; ++kv)
+        for (int h = 0; h < geo[G_H]; ++h) {
+          unsigned char *dst =
+              (unsigned char *)out_kv + ((((size_t)l * 2 + kv) * B + b) * geo[G_H] + h) * (size_t)cap_out * pbytes;
+          memset(dst, 0, (size_t)pad * pbytes);
+          for (int j = 0; j < c; ++j)
+            memcpy(dst + (size_t)(pad + j) * pbytes,
+                   (const unsigned char *)pages + page_off(geo, l, kv, bt[(size_t)r * geo[G_MB] + j / page], h,
+                                                           j % page),
+                   pbytes);
+        }
+    int8_t *m = out_mask + (size_t)b * cap_out;
+    for (int j = 0; j < W; ++j) {
+      m[j] = (int8_t)(j >= pad);
+      out_tok[(size_t)b * cap_out + j] = j >= pad ? tokens[(size_t)r * tcap + j - pad] : pad_token;
+    }
+    positions_from_mask(m, W, out_pos + (size_t)b * cap_out);
+    out_len[b] = c;
+  }
+  *width = W;
+  return O_OK;
+}
+
+/* Admit: batch entry b's content, positions [S - in_len[b], S) of a
+ * left-padded rectangle in_kv [L][2][B][H][cap_in][Dh] with tokens
+ * in_tok [B][cap_in] (a prefill's output), becomes pool row rows[b], which
+ * must be empty (length 0, no pages).  Pages come from the free stack as for
+ * append.  Errors (nothing written): O_E_ARG (geometry, rows, a non-empty row,
+ * lengths outside [0, S], S > cap_in), O_E_CAPACITY (too few free pages or
+ * positions). */
+EXPORT int oracle_paged_admit(const int32_t *geo, void *pages, int32_t *bt, int32_t *free_pages, int32_t *n_free,
+                              int32_t *tokens, int32_t *len, const int32_t *rows, int B, const void *in_kv,
+                              const int32_t *in_tok, const int32_t *in_len, int S, int cap_in) {
+  if (!paged_geo_ok(geo) || B < 0 || S < 0 || S > cap_in || !batch_rows_ok(geo, rows, B)) return O_E_ARG;
+  const int page = geo[G_PAGE], tcap = geo[G_MB] * page;
+  const size_t pbytes = (size_t)geo[G_DH] * (size_t)geo[G_ES];
+  int need = 0;
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = in_len[b];
+    if (len[r] != 0 || c < 0 || c > S) return O_E_ARG;
+    if (c > tcap) return O_E_CAPACITY;
+    need += blocks_for(c, page);
+  }
+  if (need > *n_free) return O_E_CAPACITY;
+  int top = *n_free;
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b, c = in_len[b];
+    for (int blk = 0; blk < blocks_for(c, page); ++blk) bt[(size_t)r * geo[G_MB] + blk] = free_pages[--top];
+    for (int l = 0; l < geo[G_L]; ++l)
+      for (int kv = 0; kv < 2; ++kv)
+        for (int h = 0; h < geo[G_H]; ++h) {
+          const unsigned char *src = (const unsigned char *)in_kv +
+                                     ((((size_t)l * 2 + kv) * B + b) * geo[G_H] + h) * (size_t)cap_in * pbytes;
+          for (int j = 0; j < c; ++j)
+            memcpy((unsigned char *)pages + page_off(geo, l, kv, bt[(size_t)r * geo[G_MB] + j / page], h, j % page),
+                   src + (size_t)(S - c + j) * pbytes, pbytes);
+        }
+    for (int j = 0; j < c; ++j) tokens[(size_t)r * tcap + j] = in_tok[(size_t)b * cap_in + S - c + j];
+    len[r] = c;
+  }
+  *n_free = top;
+  return O_OK;
+}
+
+/* Retire: the batch's rows give their pages back (pushed on the free stack in
+ * block order, entries in batch order), their block-table entries become -1
+ * and their lengths 0.  O_E_ARG for bad rows or lengths. */
+EXPORT int oracle_paged_retire(const int32_t *geo, int32_t *bt, int32_t *free_pages, int32_t *n_free, int32_t *len,
+                               const int32_t *rows, int B) {
+  if (!paged_geo_ok(geo) || B < 0 || !batch_rows_ok(geo, rows, B)) return O_E_ARG;
+  const int page = geo[G_PAGE], tcap = geo[G_MB] * page;
+  for (int b = 0; b < B; ++b) {
+    const int c = len[rows ? rows[b] : b];
+    if (c < 0 || c > tcap) return O_E_ARG;
+  }
+  int top = *n_free, back = 0;
+  for (int b = 0; b < B; ++b) back += blocks_for(len[rows ? rows[b] : b], page);
+  if (top < 0 || top + back > geo[G_NP]) return O_E_ARG; /* more pages than exist: a corrupt table */
+  for (int b = 0; b < B; ++b) {
+    const int r = rows ? rows[b] : b;
+    for (int blk = 0; blk < blocks_for(len[r], page); ++blk) {
+      free_pages[top++] = bt[(size_t)r * geo[G_MB] + blk];
+      bt[(size_t)r * geo[G_MB] + blk] = -1;
+    }
+    len[r] = 0;
+  }
+  *n_free = top;
+  return O_OK;
+}
