@@ -268,6 +268,94 @@ int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbu
 int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, int32_t *uniform,
                          int32_t *width, int32_t *n_uniform, void *stream);
 
+/* ------------------------------------------------------------- paged KV */
+
+/* A paged KV cache: rows of sequences whose positions live in pages of a
+ * shared pool, listed per row in a block table.  The arXiv abstract of "Batch
+ * Speculative Decoding Done Right" ties the superlinear cost of realignment
+ * to contiguous layouts; with a block table the left-padded rectangle that
+ * section 2.1 requires (equal pad + content length for every row, position ids
+ * 0.. over the content) is metadata, pad = S' - len, and section 2.2's
+ * unpad-append-repad writes only each row's committed entries.
+ *  pages        device [layers][2 (K, V)][n_pages][heads][page][head_dim] of
+ *               `dtype`: row r's content position j is in page
+ *               block_table[r][j / page], slot j % page.
+ *  block_table  device int32 [rows][max_blocks]: page ids of each row's blocks
+ *               in order; -1 past the row's ceil(len / page) blocks.
+ *  free_pages   device int32 [n_pages]: a stack of free page ids; entries
+ *               [0, *n_free) are free.
+ *  n_free       device int32 [1].
+ *  tokens       device int32 [rows][max_blocks * page]: each row's token ids
+ *               from position 0.
+ *  len          device int32 [rows]: content length of each row.
+ * Allocation: batch entries in order take their new pages from the top of the
+ * free stack, an entry's first new block getting the topmost remaining id;
+ * retiring pushes a row's pages back in block order, entries in batch order.
+ * Every page is free or in exactly one row's table; the calls keep it so. */
+typedef struct {
+  void *pages;
+  int32_t *block_table;
+  int32_t *free_pages;
+  int32_t *n_free;
+  int32_t *tokens;
+  int32_t *len;
+  int32_t rows, n_pages, page, max_blocks, layers, heads, head_dim;
+  int32_t dtype;
+} specdec_paged_t;
+
+/* Realignment on a paged cache.  Batch entry b (pool row rows[b], NULL = b;
+ * rows distinct, else SPECDEC_S_ROWS_DUP and an undefined result) commits
+ * n_b = accept_len[b] + 1 tokens, draft[b][0 .. accept_len-1] then
+ * next_token[b], and the first n_b of its D+1 speculative entries kv_new
+ * [layers][2][B][heads][D+1][head_dim] (device, 16-byte aligned), written at
+ * positions len, len+1, ... of the row; new pages come off the free stack.
+ * No other KV byte moves.  *width (device int32, nullable) receives
+ * S' = max_b(len_b + n_b).  The rectangle view (rect_tokens nullable, then
+ * nothing of it is written; rect_pos and rect_mask nullable; all
+ * [B][rect_cap] on the device): row b left-padded by S' - len'_b with
+ * pad_token, position id 0 and mask 0, then its content with position ids
+ * 0.. and mask 1, on [0, S'); the same tokens, positions and mask that
+ * SPECDEC_EQSPEC writes.  Device conditions (nothing written): a row past
+ * max_blocks * page positions, more new pages than free ones, or S' > rect_cap
+ * set SPECDEC_S_CAPACITY; rows outside [0, rows), lengths outside
+ * [0, max_blocks * page], accepted lengths outside [0, D], or a page id outside
+ * [0, n_pages) where the call would write set SPECDEC_S_LEN_RANGE.
+ * Limits: B <= 1024.  Errors: E_ARG, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH. */
+int specdec_paged_append(const specdec_paged_t *kv, const int32_t *rows, int B, int D, const void *kv_new,
+                         const int32_t *draft, const int32_t *accept_len, const int32_t *next_token,
+                         int32_t pad_token, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
+                         int8_t *rect_mask, int rect_cap, int32_t *status, void *stream);
+
+/* The batch's rows (rows[b], NULL = b) as the left-padded rectangle of width
+ * W = their longest length: out (a specdec_seqbuf_t with out->rows == B and the
+ * cache's geometry) receives KV with zero bytes on the pad, token ids, position
+ * ids, mask and lengths on [0, W), and out->width[0] = W; [W, out->cap) is not
+ * written.  This is the rectangle SPECDEC_EQSPEC would hold.  W > out->cap sets
+ * SPECDEC_S_CAPACITY and a bad row or length SPECDEC_S_LEN_RANGE (nothing
+ * written); a block-table entry outside [0, n_pages) reads as zero bytes and
+ * sets SPECDEC_S_LEN_RANGE.  Errors: E_ARG, E_DTYPE, E_ALIGN, E_ALIAS,
+ * E_LAUNCH. */
+int specdec_paged_gather(const specdec_paged_t *kv, const int32_t *rows, int B, const specdec_seqbuf_t *out,
+                         int32_t pad_token, int32_t *status, void *stream);
+
+/* Admit: the content of a left-padded rectangle `in` (in->rows == B, width
+ * in->width[0] on the device, content of entry b at [width - in->len[b],
+ * width), token ids in in->tokens) becomes pool rows rows[b] (NULL = b), which
+ * must be empty (length 0).  Pages come off the free stack.  Device conditions
+ * (nothing written): too few free pages or a row past max_blocks * page set
+ * SPECDEC_S_CAPACITY; a row that is not empty, lengths outside [0, width],
+ * width outside [0, in->cap] or a bad row set SPECDEC_S_LEN_RANGE.
+ * Errors: E_ARG, E_DTYPE, E_ALIGN, E_ALIAS, E_LAUNCH. */
+int specdec_paged_admit(const specdec_paged_t *kv, const int32_t *rows, int B, const specdec_seqbuf_t *in,
+                        int32_t *status, void *stream);
+
+/* Retire: rows rows[b] (NULL = b) give their pages back to the free stack
+ * (pushed in block order, entries in batch order); their block-table entries
+ * become -1 and their lengths 0.  Bad rows or lengths, or more pages than the
+ * stack holds, set SPECDEC_S_LEN_RANGE; duplicate rows SPECDEC_S_ROWS_DUP
+ * (nothing written either way).  Errors: E_ARG, E_LAUNCH. */
+int specdec_paged_retire(const specdec_paged_t *kv, const int32_t *rows, int B, int32_t *status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

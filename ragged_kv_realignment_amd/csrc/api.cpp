@@ -324,3 +324,128 @@ EXPORT int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *o
   p.n_uniform = n_uniform;
   return launched(sd::launch_group_by_len(p, as_stream(stream)));
 }
+
+// ------------------------------------------------------------------ paged KV
+
+static int check_paged(const specdec_paged_t *k) {
+  if (!k || !k->pages || !k->block_table || !k->free_pages || !k->n_free || !k->tokens || !k->len) return SPECDEC_E_ARG;
+  if (k->rows < 1 || k->n_pages < 1 || k->page < 1 || k->max_blocks < 1 || k->layers < 0 || k->heads < 1 ||
+      k->head_dim < 1)
+    return SPECDEC_E_ARG;
+  if (!dtype_ok(k->dtype)) return SPECDEC_E_DTYPE;
+  if (((size_t)k->head_dim * esize(k->dtype)) % 16 != 0) return SPECDEC_E_ALIGN;
+  if (reinterpret_cast<uintptr_t>(k->pages) % 16 != 0) return SPECDEC_E_ALIGN;
+  // positions of a row and token offsets are 32-bit integers
+  if ((size_t)k->max_blocks * (size_t)k->page >= (1u << 30)) return SPECDEC_E_ARG;
+  return SPECDEC_OK;
+}
+
+static size_t paged_bytes(const specdec_paged_t *k) {
+  return (size_t)k->layers * 2 * (size_t)k->n_pages * k->heads * (size_t)k->page * k->head_dim * esize(k->dtype);
+}
+
+static sd::PagedParams paged_params(int op, const specdec_paged_t *k, const int32_t *rows, int B, int32_t *status) {
+  sd::PagedParams p;
+  memset(&p, 0, sizeof(p));
+  p.op = op;
+  p.pages = k->pages;
+  p.bt = k->block_table;
+  p.free_pages = k->free_pages;
+  p.n_free = k->n_free;
+  p.tokens = k->tokens;
+  p.len = k->len;
+  p.layers = k->layers;
+  p.heads = k->heads;
+  p.units = (int)((size_t)k->head_dim * esize(k->dtype) / 16);
+  p.n_pages = k->n_pages;
+  p.page = k->page;
+  p.max_blocks = k->max_blocks;
+  p.rows = k->rows;
+  p.rowmap = rows;
+  p.B = B;
+  p.status = status;
+  return p;
+}
+
+static bool paged_matches(const specdec_paged_t *k, const specdec_seqbuf_t *s) {
+  return s->layers == k->layers && s->heads == k->heads && s->head_dim == k->head_dim && s->dtype == k->dtype;
+}
+
+EXPORT int specdec_paged_append(const specdec_paged_t *kv, const int32_t *rows, int B, int D, const void *kv_new,
+                                const int32_t *draft, const int32_t *accept_len, const int32_t *next_token,
+                                int32_t pad_token, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
+                                int8_t *rect_mask, int rect_cap, int32_t *status, void *stream) {
+  int rc = check_paged(kv);
+  if (rc) return rc;
+  if (B < 0 || B > sd::kMaxRealignRows || D < 0 || D > 255) return SPECDEC_E_ARG;
+  if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+  if ((rect_tokens || rect_pos || rect_mask) && (!rect_tokens || rect_cap < 1)) return SPECDEC_E_ARG;
+  if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
+  if (B == 0) return SPECDEC_OK;
+  const size_t knew = (size_t)kv->layers * 2 * B * kv->heads * (size_t)(D + 1) * kv->head_dim * esize(kv->dtype);
+  if (overlap(kv_new, knew, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
+  sd::PagedParams p = paged_params(sd::kPagedAppend, kv, rows, B, status);
+  p.D = D;
+  p.kv_new = kv_new;
+  p.draft = draft;
+  p.accept_len = accept_len;
+  p.next_token = next_token;
+  p.pad_token = pad_token;
+  p.width_out = width;
+  p.rect_tok = rect_tokens;
+  p.rect_pos = rect_pos;
+  p.rect_mask = rect_mask;
+  p.rect_cap = rect_cap;
+  return launched(sd::launch_paged(p, as_stream(stream)));
+}
+
+EXPORT int specdec_paged_gather(const specdec_paged_t *kv, const int32_t *rows, int B, const specdec_seqbuf_t *out,
+                                int32_t pad_token, int32_t *status, void *stream) {
+  int rc = check_paged(kv);
+  if (rc) return rc;
+  rc = check_seqbuf_shape(out);
+  if (rc) return rc;
+  if (B < 0 || B > sd::kMaxRealignRows || out->rows != B || !paged_matches(kv, out)) return SPECDEC_E_ARG;
+  if (!out->tokens || !out->width || out->cap < 1) return SPECDEC_E_ARG;
+  if (B == 0) return SPECDEC_OK;
+  if (overlap(out->kv, kv_bytes(out), kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
+  sd::PagedParams p = paged_params(sd::kPagedGather, kv, rows, B, status);
+  p.pad_token = pad_token;
+  p.rect_kv = out->kv;
+  p.rect_tok = out->tokens;
+  p.rect_pos = out->pos;
+  p.rect_mask = out->mask;
+  p.rect_len = out->len;
+  p.rect_width = out->width;
+  p.rect_cap = out->cap;
+  return launched(sd::launch_paged(p, as_stream(stream)));
+}
+
+EXPORT int specdec_paged_admit(const specdec_paged_t *kv, const int32_t *rows, int B, const specdec_seqbuf_t *in,
+                               int32_t *status, void *stream) {
+  int rc = check_paged(kv);
+  if (rc) return rc;
+  rc = check_seqbuf_shape(in);
+  if (rc) return rc;
+  if (B < 0 || B > sd::kMaxRealignRows || in->rows != B || !paged_matches(kv, in)) return SPECDEC_E_ARG;
+  if (!in->tokens || !in->width) return SPECDEC_E_ARG;
+  if (B == 0) return SPECDEC_OK;
+  if (overlap(in->kv, kv_bytes(in), kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
+  sd::PagedParams p = paged_params(sd::kPagedAdmit, kv, rows, B, status);
+  p.rect_kv = in->kv;
+  p.rect_tok = in->tokens;
+  p.rect_cap = in->cap;
+  p.in_len = in->len;
+  p.in_width = in->width;
+  return launched(sd::launch_paged(p, as_stream(stream)));
+}
+
+EXPORT int specdec_paged_retire(const specdec_paged_t *kv, const int32_t *rows, int B, int32_t *status,
+                                void *stream) {
+  int rc = check_paged(kv);
+  if (rc) return rc;
+  if (B < 0 || B > sd::kMaxRealignRows) return SPECDEC_E_ARG;
+  if (B == 0) return SPECDEC_OK;
+  sd::PagedParams p = paged_params(sd::kPagedRetire, kv, rows, B, status);
+  return launched(sd::launch_paged(p, as_stream(stream)));
+}

@@ -71,6 +71,33 @@ struct RealignParams {
   int32_t *status;
 };
 
+constexpr int kPagedAppend = 0, kPagedGather = 1, kPagedAdmit = 2, kPagedRetire = 3;
+
+struct PagedParams {
+  int op;                      // kPaged*
+  void *pages;                 // [L][2][n_pages][H][page][units * 16 bytes]
+  int32_t *bt;                 // [rows][max_blocks] page ids, -1 = none
+  int32_t *free_pages;         // [n_pages] free-page stack
+  int32_t *n_free;             // [1] entries of the stack in use
+  int32_t *tokens;             // [rows][max_blocks * page]
+  int32_t *len;                // [rows]
+  int layers, heads, units, n_pages, page, max_blocks, rows;
+  const int32_t *rowmap;       // [B] pool row of each batch entry, nullable = identity
+  int B, D;
+  const void *kv_new;          // append: [L][2][B][H][D+1][units * 16 bytes]
+  const int32_t *draft, *accept_len, *next_token;
+  int32_t pad_token;
+  // the rectangle side: the view an append writes, a gather's output, an admit's input
+  void *rect_kv;               // [L][2][B][H][rect_cap][units * 16 bytes]
+  int32_t *rect_tok, *rect_pos, *rect_len, *rect_width;
+  int8_t *rect_mask;
+  int rect_cap;
+  const int32_t *in_len, *in_width;  // admit: content lengths [B] and the rectangle's width [1]
+  int32_t *width_out;          // append: S'
+  int32_t *status;
+  int kv_wgs;                  // workgroups that copy KV (set by the launcher)
+};
+
 struct GroupParams {
   const int32_t *len;
   int N, group;
@@ -84,6 +111,7 @@ hipError_t launch_verify_sample_logits(const SampleLogitsParams &p, hipStream_t 
 hipError_t launch_realign(const RealignParams &p, hipStream_t s);
 hipError_t launch_realign_inplace(const RealignParams &p, hipStream_t s);
 hipError_t launch_group_by_len(const GroupParams &p, hipStream_t s);
+hipError_t launch_paged(const PagedParams &p, hipStream_t s);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
 
 }  // namespace sd

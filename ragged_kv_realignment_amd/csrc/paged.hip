@@ -1,0 +1,451 @@
+// Paged KV cache: a row's content lives in pages of a shared pool, listed in
+// the row's block table, so the left-padded rectangle that the alignment
+// invariant asks for ("Batch Speculative Decoding Done Right", section 2.1:
+// equal pad + content length for every row, position ids 0.. over the content)
+// is metadata: row b's pad is S' - len'_b.  EQSPEC's unpad-append-repad
+// (section 2.2) then writes only each row's committed entries at its length;
+// the KV already in the pages never moves.  The arXiv abstract of the same
+// paper ties the superlinear realignment cost to contiguous layouts; this is
+// the layout that removes it.  Committed and discarded speculative entries:
+// "Inference Engineering Part 5/8", section "Acceptance changes across the
+// workload".
+//
+// Layout: pages [L][2][n_pages][H][page][units * 16 bytes]; block table
+// int32 [rows][max_blocks] (-1 = none); a stack of free page ids whose entries
+// [0, n_free) are free; token ids int32 [rows][max_blocks * page] from 0.
+//
+// Page allocation: batch entries in order take their new pages from the top of
+// the free stack, an entry's first new block getting the topmost remaining id;
+// retiring pushes a row's pages back in block order, entries in batch order.
+//
+// Every kernel of a call first runs the same plan (lengths, page counts and
+// their exclusive prefix over the batch, checks) on the unchanged inputs, so
+// all of them agree on the outcome; a call that fails a check writes nothing.
+// The block table, the free stack, lengths and token ids are updated by a
+// last single-workgroup launch, after every workgroup that reads them.
+#include <limits.h>
+#include "device_common.h"
+#include "launch.h"
+#include "specdec.h"
+
+namespace sd {
+
+constexpr int kPgBlock = 256;                   // threads per workgroup
+constexpr int kPgPer = kMaxRealignRows / kPgBlock;  // batch entries per thread in the plan
+static_assert(kPgPer * kPgBlock == kMaxRealignRows, "the plan covers every batch entry");
+
+typedef int i32x4p __attribute__((ext_vector_type(4)));
+
+struct PagedPlan {
+  int r[kMaxRealignRows];   // pool row of each batch entry
+  int c[kMaxRealignRows];   // its length before the call (0 for admit)
+  int n[kMaxRealignRows];   // positions it gains
+  int k0[kMaxRealignRows];  // pages taken by the entries before it
+  int red[kPgBlock / kWave];
+  int need, smax, flags, n_free;
+};
+
+__device__ __forceinline__ int blocks_for(int n, int page) { return (n + page - 1) / page; }
+
+// Exclusive prefix of v over the workgroup's threads (thread order) and the total.
+__device__ __forceinline__ int block_excl_scan(int v, int *red, int &total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) red[w] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kPgBlock / kWave; ++k) {
+    if (k < w) before += red[k];
+    total += red[k];
+  }
+  return before + x - v;
+}
+
+// The plan of an append (ADMIT = false: entry b gains accept_len[b] + 1
+// positions at its length) or an admit (entry b's row must be empty and gains
+// in_len[b] positions).  Returns the status bits of a failed check (0 = go).
+template <bool ADMIT>
+__device__ int paged_plan(const PagedParams &p, PagedPlan &s) {
+  const int B = p.B, tcap = p.max_blocks * p.page;
+  int bad = 0, cap = 0, mx = 0, ksum = 0;
+  int kloc[kPgPer];
+  int width_in = 0;
+  if (ADMIT) width_in = *p.in_width;
+  if (ADMIT && (width_in < 0 || width_in > p.rect_cap)) bad |= SPECDEC_S_LEN_RANGE;
+#pragma unroll
+  for (int e = 0; e < kPgPer; ++e) {
+    const int b = threadIdx.x * kPgPer + e;
+    kloc[e] = 0;
+    if (b >= B) continue;
+    int r = p.rowmap ? p.rowmap[b] : b;
+    if (r < 0 || r >= p.rows) {
+      bad |= SPECDEC_S_LEN_RANGE;
+      r = 0;
+    }
+    int c = p.len[r], n;
+    if (ADMIT) {
+      n = p.in_len[b];
+      if (c != 0 || n < 0 || n > width_in) bad |= SPECDEC_S_LEN_RANGE;
+      c = 0;
+    } else {
+      const int a = p.accept_len[b];
+      if (a < 0 || a > p.D || c < 0 || c > tcap) bad |= SPECDEC_S_LEN_RANGE;
+      n = a + 1;
+    }
+    if (bad) continue;
+    const int cn = c + n;
+    if (cn > tcap) {
+      cap = SPECDEC_S_CAPACITY;
+      continue;
+    }
+    // the block an append starts in must already be a valid page
+    if (!ADMIT && c % p.page != 0) {
+      const int pg = p.bt[(size_t)r * p.max_blocks + c / p.page];
+      if (pg < 0 || pg >= p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
+    }
+    s.r[b] = r;
+    s.c[b] = c;
+    s.n[b] = n;
+    kloc[e] = blocks_for(cn, p.page) - blocks_for(c, p.page);
+    ksum += kloc[e];
+    mx = max(mx, cn);
+  }
+  int total;
+  int base = block_excl_scan(ksum, s.red, total);
+#pragma unroll
+  for (int e = 0; e < kPgPer; ++e) {
+    const int b = threadIdx.x * kPgPer + e;
+    if (b < B) s.k0[b] = base;
+    base += kloc[e];
+  }
+  const int nf = *p.n_free;
+  if (nf < 0 || nf > p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
+  // the pages about to be taken must be valid ids
+  for (int i = threadIdx.x; i < total && i < nf; i += kPgBlock) {
+    const int pg = p.free_pages[nf - 1 - i];
+    if (pg < 0 || pg >= p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
+  }
+  const int smax = block_max_int<kPgBlock>(mx, s.red);
+  int flags = block_or_int<kPgBlock>(bad | cap, s.red);
+  if (!(flags & SPECDEC_S_LEN_RANGE)) {
+    if (total > nf) flags |= SPECDEC_S_CAPACITY;
+    if (!ADMIT && p.rect_tok && smax > p.rect_cap) flags |= SPECDEC_S_CAPACITY;
+  }
+  if (threadIdx.x == 0) {
+    s.need = total;
+    s.smax = smax;
+    s.flags = flags;
+    s.n_free = nf;
+  }
+  __syncthreads();
+  return flags;
+}
+
+// Page id of block `blk` of batch entry b after the call's allocation.
+__device__ __forceinline__ int page_of(const PagedParams &p, const PagedPlan &s, int b, int blk) {
+  const int nb_old = blocks_for(s.c[b], p.page);
+  if (blk < nb_old) return p.bt[(size_t)s.r[b] * p.max_blocks + blk];
+  return p.free_pages[s.n_free - 1 - (s.k0[b] + blk - nb_old)];
+}
+
+__device__ __forceinline__ size_t page_unit(const PagedParams &p, int lk, int pg, int h, int slot) {
+  return ((((size_t)lk * p.n_pages + pg) * p.heads + h) * p.page + slot) * (size_t)p.units;
+}
+
+// Append: workgroups [0, kv_wgs) copy the committed KV entries of every
+// (layer, K|V, entry, head) sequence into their slots; the B workgroups after
+// them write the rectangle view of row b (token ids, position ids, mask over
+// [0, S')) when it is asked for.
+__global__ __launch_bounds__(kPgBlock) void k_paged_append(PagedParams p) {
+  __shared__ PagedPlan s;
+  if (paged_plan<false>(p, s)) return;  // reported by k_paged_commit
+  const int B = p.B, U = p.units, H = p.heads, D1 = p.D + 1;
+  if ((int)blockIdx.x >= p.kv_wgs) {
+    const int b = blockIdx.x - p.kv_wgs;
+    const int r = s.r[b], c = s.c[b], n = s.n[b], W = s.smax, pad = W - c - n;
+    const int tcap = p.max_blocks * p.page;
+    for (int j = threadIdx.x; j < W; j += kPgBlock) {
+      const int k = j - pad;  // content index
+      int t = p.pad_token;
+      if (k >= 0) t = k < c ? p.tokens[(size_t)r * tcap + k] : (k < c + n - 1 ? p.draft[(size_t)b * p.D + k - c]
+                                                                               : p.next_token[b]);
+      p.rect_tok[(size_t)b * p.rect_cap + j] = t;
+      if (p.rect_pos) p.rect_pos[(size_t)b * p.rect_cap + j] = k >= 0 ? k : 0;
+      if (p.rect_mask) p.rect_mask[(size_t)b * p.rect_cap + j] = (int8_t)(k >= 0);
+    }
+    return;
+  }
+  const long nseg = (long)p.layers * 2 * B * H;
+  const i32x4p *nw = static_cast<const i32x4p *>(p.kv_new);
+  i32x4p *pages = static_cast<i32x4p *>(p.pages);
+  const int ups = D1 * U;  // units of one sequence's D+1 speculative entries
+  const int spp = max(1, kPgBlock / ups);
+  const int sq = threadIdx.x / ups, f = threadIdx.x - sq * ups;
+  for (long s0 = (long)blockIdx.x * spp; s0 < nseg; s0 += (long)p.kv_wgs * spp) {
+    const long seg = s0 + sq;
+    if (sq >= spp || seg >= nseg) continue;
+    const int lk = (int)(seg / ((long)B * H));
+    const int rem = (int)(seg - (long)lk * B * H);
+    const int b = rem / H, h = rem - b * H;
+    const int c = s.c[b], n = s.n[b];
+    for (int g = f; g < n * U; g += ups) {
+      const int i = g / U, u = g - i * U, j = c + i;
+      const int pg = page_of(p, s, b, j / p.page);
+      pages[page_unit(p, lk, pg, h, j % p.page) + u] =
+          __builtin_nontemporal_load(nw + ((size_t)seg * D1 + i) * U + u);
+    }
+  }
+}
+
+// Admit: workgroups copy entry b's content, positions [S - in_len[b], S) of
+// the input rectangle, into the pages the plan gives it.
+__global__ __launch_bounds__(kPgBlock) void k_paged_admit(PagedParams p) {
+  __shared__ PagedPlan s;
+  if (paged_plan<true>(p, s)) return;  // reported by k_paged_commit
+  const int B = p.B, U = p.units, H = p.heads;
+  const int S = *p.in_width;
+  const long nseg = (long)p.layers * 2 * B * H;
+  const i32x4p *src = static_cast<const i32x4p *>(p.rect_kv);
+  i32x4p *pages = static_cast<i32x4p *>(p.pages);
+  // units of all sequences, kPgBlock * 4 per workgroup pass
+  const long per_seg = (long)S * U;
+  const long total = nseg * per_seg;
+  for (long q0 = (long)blockIdx.x * kPgBlock * 4; q0 < total; q0 += (long)gridDim.x * kPgBlock * 4) {
+    i32x4p v[4];
+    long dst[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long q = q0 + k * kPgBlock + threadIdx.x;
+      dst[k] = -1;
+      if (q >= total) continue;
+      const long seg = q / per_seg;
+      const int w = (int)(q - seg * per_seg), pos = w / U, u = w - pos * U;
+      const int lk = (int)(seg / ((long)B * H));
+      const int rem = (int)(seg - (long)lk * B * H);
+      const int b = rem / H, h = rem - b * H;
+      const int j = pos - (S - s.n[b]);  // content index
+      if (j < 0) continue;
+      v[k] = __builtin_nontemporal_load(src + (((size_t)seg * p.rect_cap) + pos) * U + u);
+      dst[k] = (long)page_unit(p, lk, page_of(p, s, b, j / p.page), h, j % p.page) + u;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (dst[k] >= 0) pages[dst[k]] = v[k];
+  }
+}
+
+// The last launch of an append or an admit: block table, free-stack count,
+// token ids and lengths (and the width of an append); reports the plan's
+// status bits.  One workgroup.
+template <bool ADMIT>
+__global__ __launch_bounds__(kPgBlock) void k_paged_commit(PagedParams p) {
+  __shared__ PagedPlan s;
+  const int flags = paged_plan<ADMIT>(p, s);
+  if (flags) {
+    if (threadIdx.x == 0) set_status(p.status, flags);
+    return;
+  }
+  const int B = p.B, tcap = p.max_blocks * p.page;
+  int dup = 0;
+  for (int b = threadIdx.x; b < B; b += kPgBlock)
+    for (int o = 0; o < b; ++o) dup |= (s.r[o] == s.r[b]);
+  dup = block_or_int<kPgBlock>(dup, s.red);
+  for (int b = threadIdx.x; b < B; b += kPgBlock) {
+    const int r = s.r[b], c = s.c[b], n = s.n[b];
+    const int nb0 = blocks_for(c, p.page), nb1 = blocks_for(c + n, p.page);
+    for (int blk = nb0; blk < nb1; ++blk) p.bt[(size_t)r * p.max_blocks + blk] = page_of(p, s, b, blk);
+    int32_t *t = p.tokens + (size_t)r * tcap + c;
+    if (ADMIT) {
+      const int S = *p.in_width;
+      const int32_t *src = p.rect_tok + (size_t)b * p.rect_cap + (S - n);
+      for (int k = 0; k < n; ++k) t[k] = src[k];
+    } else {
+      for (int k = 0; k < n - 1; ++k) t[k] = p.draft[(size_t)b * p.D + k];
+      t[n - 1] = p.next_token[b];
+    }
+    p.len[r] = c + n;
+  }
+  if (threadIdx.x == 0) {
+    *p.n_free = s.n_free - s.need;
+    if (!ADMIT && p.width_out) *p.width_out = s.smax;
+    if (dup) set_status(p.status, SPECDEC_S_ROWS_DUP);
+  }
+}
+
+// Gather: the batch's rows as a left-padded rectangle of width W = their
+// longest length (zero KV bytes on the pad), read through the block table.
+// Workgroups [0, kv_wgs) copy KV; the B after them write token ids, position
+// ids, mask and length of one row each (and W).  A block-table entry outside
+// [0, n_pages) is read as zero bytes and sets SPECDEC_S_LEN_RANGE.
+__global__ __launch_bounds__(kPgBlock) void k_paged_gather(PagedParams p) {
+  __shared__ int s_r[kMaxRealignRows], s_c[kMaxRealignRows];
+  __shared__ int s_red[kPgBlock / kWave];
+  const int B = p.B, U = p.units, H = p.heads, tcap = p.max_blocks * p.page;
+  int bad = 0, mx = 0;
+  for (int b = threadIdx.x; b < B; b += kPgBlock) {
+    int r = p.rowmap ? p.rowmap[b] : b;
+    if (r < 0 || r >= p.rows) {
+      bad = 1;
+      r = 0;
+    }
+    const int c = p.len[r];
+    if (c < 0 || c > tcap) bad = 1;
+    s_r[b] = r;
+    s_c[b] = c;
+    mx = max(mx, c);
+  }
+  const int W = block_max_int<kPgBlock>(mx, s_red);
+  bad = block_or_int<kPgBlock>(bad, s_red);
+  if (bad || W > p.rect_cap) {
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+      set_status(p.status, bad ? SPECDEC_S_LEN_RANGE : SPECDEC_S_CAPACITY);
+    return;
+  }
+  if ((int)blockIdx.x >= p.kv_wgs) {
+    const int b = blockIdx.x - p.kv_wgs, r = s_r[b], c = s_c[b], pad = W - c;
+    for (int j = threadIdx.x; j < W; j += kPgBlock) {
+      const int k = j - pad;
+      p.rect_tok[(size_t)b * p.rect_cap + j] = k >= 0 ? p.tokens[(size_t)r * tcap + k] : p.pad_token;
+      if (p.rect_pos) p.rect_pos[(size_t)b * p.rect_cap + j] = k >= 0 ? k : 0;
+      if (p.rect_mask) p.rect_mask[(size_t)b * p.rect_cap + j] = (int8_t)(k >= 0);
+    }
+    if (threadIdx.x == 0) {
+      p.rect_len[b] = c;
+      if (b == 0) *p.rect_width = W;
+    }
+    return;
+  }
+  const long nseg = (long)p.layers * 2 * B * H;
+  const long per_seg = (long)W * U;
+  const long total = nseg * per_seg;
+  const i32x4p *pages = static_cast<const i32x4p *>(p.pages);
+  i32x4p *dst = static_cast<i32x4p *>(p.rect_kv);
+  int oob = 0;
+  for (long q0 = (long)blockIdx.x * kPgBlock * 4; q0 < total; q0 += (long)p.kv_wgs * kPgBlock * 4) {
+    i32x4p v[4];
+    long at[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const long q = q0 + k * kPgBlock + threadIdx.x;
+      at[k] = -1;
+      v[k] = i32x4p{0, 0, 0, 0};
+      if (q >= total) continue;
+      const long seg = q / per_seg;
+      const int w = (int)(q - seg * per_seg), pos = w / U, u = w - pos * U;
+      const int lk = (int)(seg / ((long)B * H));
+      const int rem = (int)(seg - (long)lk * B * H);
+      const int b = rem / H, h = rem - b * H;
+      at[k] = ((long)seg * p.rect_cap + pos) * U + u;
+      const int j = pos - (W - s_c[b]);
+      if (j < 0) continue;  // pad: zero
+      const int pg = p.bt[(size_t)s_r[b] * p.max_blocks + j / p.page];
+      if (pg < 0 || pg >= p.n_pages) {
+        oob = 1;
+        continue;
+      }
+      v[k] = __builtin_nontemporal_load(pages + page_unit(p, lk, pg, h, j % p.page) + u);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (at[k] >= 0) dst[at[k]] = v[k];
+  }
+  if (oob) set_status(p.status, SPECDEC_S_LEN_RANGE);
+}
+
+// Retire: the batch's rows push their pages on the free stack (block order,
+// entries in batch order), their table entries become -1, their lengths 0.
+// One workgroup.
+__global__ __launch_bounds__(kPgBlock) void k_paged_retire(PagedParams p) {
+  __shared__ int s_r[kMaxRealignRows], s_k0[kMaxRealignRows];
+  __shared__ int s_red[kPgBlock / kWave];
+  const int B = p.B, tcap = p.max_blocks * p.page;
+  int bad = 0, ksum = 0;
+  int kloc[kPgPer];
+#pragma unroll
+  for (int e = 0; e < kPgPer; ++e) {
+    const int b = threadIdx.x * kPgPer + e;
+    kloc[e] = 0;
+    if (b >= B) continue;
+    int r = p.rowmap ? p.rowmap[b] : b;
+    if (r < 0 || r >= p.rows) {
+      bad = 1;
+      r = 0;
+    }
+    const int c = p.len[r];
+    if (c < 0 || c > tcap) bad = 1;
+    s_r[b] = r;
+    kloc[e] = bad ? 0 : blocks_for(c, p.page);
+    ksum += kloc[e];
+  }
+  int total;
+  int base = block_excl_scan(ksum, s_red, total);
+#pragma unroll
+  for (int e = 0; e < kPgPer; ++e) {
+    const int b = threadIdx.x * kPgPer + e;
+    if (b < B) s_k0[b] = base;
+    base += kloc[e];
+  }
+  int dup = 0;
+  for (int b = threadIdx.x; b < B; b += kPgBlock)
+    for (int o = 0; o < b; ++o) dup |= (s_r[o] == s_r[b]);
+  const int nf = *p.n_free;
+  if (nf < 0 || nf + total > p.n_pages) bad = 1;
+  bad = block_or_int<kPgBlock>(bad | (dup << 1), s_red);
+  if (bad) {
+    if (threadIdx.x == 0) set_status(p.status, (bad & 1 ? SPECDEC_S_LEN_RANGE : 0) | (bad & 2 ? SPECDEC_S_ROWS_DUP : 0));
+    return;
+  }
+  for (int b = threadIdx.x; b < B; b += kPgBlock) {
+    const int r = s_r[b], nb = blocks_for(p.len[r], p.page);
+    for (int blk = 0; blk < nb; ++blk) {
+      p.free_pages[nf + s_k0[b] + blk] = p.bt[(size_t)r * p.max_blocks + blk];
+      p.bt[(size_t)r * p.max_blocks + blk] = -1;
+    }
+  }
+  __syncthreads();  // every length read above before any is cleared
+  for (int b = threadIdx.x; b < B; b += kPgBlock) p.len[s_r[b]] = 0;
+  if (threadIdx.x == 0) *p.n_free = nf + total;
+}
+
+hipError_t launch_paged(const PagedParams &q, hipStream_t st) {
+  PagedParams p = q;
+  const int cus = device_cus();
+  if (p.op == kPagedAppend) {
+    const int ups = (p.D + 1) * p.units;
+    const long spp = ups < kPgBlock ? kPgBlock / ups : 1;
+    const long nseg = ((long)p.layers * 2 * p.B * p.heads + spp - 1) / spp;
+    p.kv_wgs = (int)(nseg < 8L * cus ? (nseg > 0 ? nseg : 1) : 8L * cus);
+    const int extra = p.rect_tok ? p.B : 0;
+    hipLaunchKernelGGL(k_paged_append, dim3((unsigned)(p.kv_wgs + extra)), dim3(kPgBlock), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_paged_commit<false>, dim3(1), dim3(kPgBlock), 0, st, p);
+  } else if (p.op == kPagedAdmit) {
+    // units of the widest input the buffer allows; workgroups past the real count find none
+    const long units = (long)p.layers * 2 * p.B * p.heads * p.rect_cap * p.units;
+    const long g = (units + kPgBlock * 4 - 1) / (kPgBlock * 4);
+    p.kv_wgs = (int)(g < 16L * cus ? (g > 0 ? g : 1) : 16L * cus);
+    hipLaunchKernelGGL(k_paged_admit, dim3((unsigned)p.kv_wgs), dim3(kPgBlock), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_paged_commit<true>, dim3(1), dim3(kPgBlock), 0, st, p);
+  } else if (p.op == kPagedGather) {
+    const long units = (long)p.layers * 2 * p.B * p.heads * p.rect_cap * p.units;
+    const long g = (units + kPgBlock * 4 - 1) / (kPgBlock * 4);
+    p.kv_wgs = (int)(g < 16L * cus ? (g > 0 ? g : 1) : 16L * cus);
+    hipLaunchKernelGGL(k_paged_gather, dim3((unsigned)(p.kv_wgs + p.B)), dim3(kPgBlock), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(k_paged_retire, dim3(1), dim3(kPgBlock), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sd

@@ -24,7 +24,8 @@ _TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init", "specdec_verify_greedy",
            "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
-           "specdec_realign_kv", "specdec_group_by_len")
+           "specdec_realign_kv", "specdec_group_by_len", "specdec_paged_append", "specdec_paged_gather",
+           "specdec_paged_admit", "specdec_paged_retire")
 
 
 class SpecDecError(RuntimeError):
@@ -63,8 +64,14 @@ def lib():
         L.specdec_realign_kv.argtypes = [ci, C.POINTER(SeqBufC), C.POINTER(SeqBufC), vp, ci, ci, vp, ci, vp, vp,
                                          vp, vp, C.c_int32, vp, vp]
         L.specdec_group_by_len.argtypes = [vp, ci, ci, vp, vp, vp, vp, vp]
+        L.specdec_paged_append.argtypes = [C.POINTER(PagedC), vp, ci, ci, vp, vp, vp, vp, C.c_int32, vp, vp, vp,
+                                           vp, ci, vp, vp]
+        L.specdec_paged_gather.argtypes = [C.POINTER(PagedC), vp, ci, C.POINTER(SeqBufC), C.c_int32, vp, vp]
+        L.specdec_paged_admit.argtypes = [C.POINTER(PagedC), vp, ci, C.POINTER(SeqBufC), vp, vp]
+        L.specdec_paged_retire.argtypes = [C.POINTER(PagedC), vp, ci, vp, vp]
         for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample",
-                  "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len"):
+                  "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len",
+                  "specdec_paged_append", "specdec_paged_gather", "specdec_paged_admit", "specdec_paged_retire"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -332,3 +339,115 @@ verify_greedy = specdec_verify_greedy
 verify_sample = specdec_verify_sample
 verify_sample_logits = specdec_verify_sample_logits
 group_by_len = specdec_group_by_len
+
+
+# ----------------------------------------------------------------- paged KV
+
+class PagedC(C.Structure):
+    _fields_ = [("pages", C.c_void_p), ("block_table", C.c_void_p), ("free_pages", C.c_void_p),
+                ("n_free", C.c_void_p), ("tokens", C.c_void_p), ("len", C.c_void_p), ("rows", C.c_int32),
+                ("n_pages", C.c_int32), ("page", C.c_int32), ("max_blocks", C.c_int32), ("layers", C.c_int32),
+                ("heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+class PagedKV:
+    """Device tensors of a paged KV cache (see specdec_paged_t in include/specdec.h).
+
+    pages [L, 2, n_pages, H, page, Dh]; block_table [rows, max_blocks] int32
+    (-1 = none); free_pages [n_pages] int32 stack with n_free [1] entries in use;
+    tokens [rows, max_blocks*page] int32; len [rows] int32."""
+
+    def __init__(self, pages, block_table, free_pages, n_free, tokens, len):
+        _need(pages, "pages")
+        if pages.dtype not in _TORCH_DT or pages.dim() != 6 or pages.shape[1] != 2:
+            raise ValueError("pages must be a [L, 2, n_pages, H, page, Dh] float32/float16/bfloat16 tensor")
+        L, _, n_pages, H, page, Dh = pages.shape
+        for t, n in ((block_table, "block_table"), (free_pages, "free_pages"), (n_free, "n_free"),
+                     (tokens, "tokens"), (len, "len")):
+            _need(t, n, torch.int32)
+        rows, max_blocks = block_table.shape
+        if tuple(free_pages.shape) != (n_pages,) or n_free.numel() != 1 or \
+                tuple(tokens.shape) != (rows, max_blocks * page) or tuple(len.shape) != (rows,):
+            raise ValueError("inconsistent paged-cache shapes")
+        self.pages, self.block_table, self.free_pages, self.n_free = pages, block_table, free_pages, n_free
+        self.tokens, self.len = tokens, len
+        self.c = PagedC(pages.data_ptr(), block_table.data_ptr(), free_pages.data_ptr(), n_free.data_ptr(),
+                        tokens.data_ptr(), len.data_ptr(), rows, n_pages, page, max_blocks, L, H, Dh,
+                        _TORCH_DT[pages.dtype])
+
+    @staticmethod
+    def empty(layers, rows, heads, head_dim, n_pages, page, max_blocks, dtype, device="cuda", free_order=None):
+        """An empty cache: every page free (stack order `free_order`, default 0..n_pages-1)."""
+        pages = torch.zeros((layers, 2, n_pages, heads, page, head_dim), dtype=dtype, device=device)
+        bt = torch.full((rows, max_blocks), -1, dtype=torch.int32, device=device)
+        fp = (torch.arange(n_pages, dtype=torch.int32, device=device) if free_order is None
+              else free_order.to(device=device, dtype=torch.int32).contiguous())
+        nf = torch.full((1,), n_pages, dtype=torch.int32, device=device)
+        tok = torch.zeros((rows, max_blocks * page), dtype=torch.int32, device=device)
+        ln = torch.zeros(rows, dtype=torch.int32, device=device)
+        return PagedKV(pages, bt, fp, nf, tok, ln)
+
+    @property
+    def page(self):
+        return self.pages.shape[4]
+
+
+def paged_append(cache, kv_new, draft, accept_len, next_token, rows=None, pad_token=0, width=None,
+                 rect_tokens=None, rect_pos=None, rect_mask=None, status=None):
+    """Realignment on a paged cache: append every entry's committed tokens and
+    speculative KV at its length; optionally the [B, rect_cap] rectangle view."""
+    _need(kv_new, "kv_new", cache.pages.dtype)
+    L, _, B, H, D1, Dh = kv_new.shape
+    D = D1 - 1
+    if (L, H, Dh) != (cache.pages.shape[0], cache.pages.shape[3], cache.pages.shape[5]):
+        raise ValueError("kv_new must be [L, 2, B, H, D+1, Dh] of the cache's geometry")
+    for t, n, shape in ((draft, "draft", (B, D)), (accept_len, "accept_len", (B,)), (next_token, "next_token", (B,)),
+                        (rows, "rows", (B,))):
+        if t is not None:
+            _need(t, n, torch.int32)
+            if tuple(t.shape) != shape:
+                raise ValueError("%s must have shape %s" % (n, shape))
+    rect_cap = 0
+    if rect_tokens is not None:
+        _need(rect_tokens, "rect_tokens", torch.int32)
+        rect_cap = rect_tokens.shape[1]
+        for t, n, dt in ((rect_pos, "rect_pos", torch.int32), (rect_mask, "rect_mask", torch.int8)):
+            if t is not None:
+                _need(t, n, dt)
+                if tuple(t.shape) != tuple(rect_tokens.shape):
+                    raise ValueError("%s must match rect_tokens' shape" % n)
+    rc = lib().specdec_paged_append(C.byref(cache.c), _ptr(rows), B, D, kv_new.data_ptr(), _ptr(draft),
+                                    accept_len.data_ptr(), next_token.data_ptr(), pad_token, _ptr(width),
+                                    _ptr(rect_tokens), _ptr(rect_pos), _ptr(rect_mask), rect_cap, _ptr(status),
+                                    _stream())
+    _check(rc, "specdec_paged_append")
+
+
+def paged_gather(cache, out, rows=None, pad_token=0, status=None):
+    """The batch's rows as the left-padded rectangle `out` (a SeqBuf with one row per entry)."""
+    B = out.rows
+    if rows is not None:
+        _need(rows, "rows", torch.int32)
+        if rows.numel() != B:
+            raise ValueError("rows must name one pool row per rectangle row")
+    rc = lib().specdec_paged_gather(C.byref(cache.c), _ptr(rows), B, C.byref(out.c), pad_token, _ptr(status),
+                                    _stream())
+    _check(rc, "specdec_paged_gather")
+
+
+def paged_admit(cache, rect, rows=None, status=None):
+    """Empty pool rows receive the content of the left-padded rectangle `rect` (a SeqBuf)."""
+    B = rect.rows
+    if rows is not None:
+        _need(rows, "rows", torch.int32)
+        if rows.numel() != B:
+            raise ValueError("rows must name one pool row per rectangle row")
+    rc = lib().specdec_paged_admit(C.byref(cache.c), _ptr(rows), B, C.byref(rect.c), _ptr(status), _stream())
+    _check(rc, "specdec_paged_admit")
+
+
+def paged_retire(cache, rows, status=None):
+    """The listed rows return their pages to the free stack and become empty."""
+    _need(rows, "rows", torch.int32)
+    rc = lib().specdec_paged_retire(C.byref(cache.c), rows.data_ptr(), rows.numel(), _ptr(status), _stream())
+    _check(rc, "specdec_paged_retire")
