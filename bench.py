@@ -36,6 +36,7 @@ PEAK_HBM_GBS = 8000.0
 _CSRC = os.path.join(ROOT, "ragged_kv_realignment_amd", "csrc")
 _HEADERS = ("buffer_io.h", "device_common.h", "launch.h")
 KERNEL = {False: "k_realign_eqspec", True: "k_realign_inplace"}
+PAGE = 16  # positions per page of the paged-cache leg
 # counter summary and the sources of the realign kernel it was taken on, per realign mode
 TRAFFIC = {
     False: (os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt"), ("realign.hip",) + _HEADERS),
@@ -55,9 +56,9 @@ def parse():
     ap.add_argument("--cpu-rounds", type=int, default=64, help="oracle sample: rounds")
     ap.add_argument("--cpu-layers", type=int, default=36, help="oracle sample: KV layers realigned (scaled to all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--realign", choices=("both", "inplace", "eqspec"), default="both",
-                    help="chain workloads: realign in place on one buffer, out of place between two, or both "
-                         "(the headline is the first of the two)")
+    ap.add_argument("--realign", choices=("all", "both", "inplace", "eqspec", "paged"), default="all",
+                    help="chain workloads: realign in place on one buffer, out of place between two, on a paged "
+                         "cache, in place and out of place (both), or all three; the headline is the first")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration for profiling)")
     return ap.parse_args()
@@ -137,6 +138,29 @@ def round_bytes_inplace(cfg, lens0, width0, acc_hist):
                 4 * int(acc.sum()) + 16 * B + 8)
         out.append(kv + meta)
         lens, S = lens + n, snew
+    return np.array(out, dtype=np.float64)
+
+
+def round_bytes_paged(cfg, lens0, acc_hist, page):
+    """Algorithmic bytes of each round's realignment on a paged cache: every
+    row's n_b committed entries are read from the speculative KV and written to
+    their page slots; token ids of the old content are read and the rectangle
+    view (token ids, position ids, mask over [0, S')) written; committed token
+    ids, lengths and new block-table entries written."""
+    import numpy as np
+    B = cfg.B
+    P = cfg.kv_pos_bytes
+    lens = lens0.astype(np.int64).copy()
+    out = []
+    for acc in acc_hist:
+        n = acc.astype(np.int64) + 1
+        snew = int((lens + n).max())
+        new_blocks = int(((lens + n + page - 1) // page - (lens + page - 1) // page).sum())
+        kv = 2 * P * int(n.sum())
+        meta = (9 * B * snew + 4 * int(lens.sum()) + 4 * int(n.sum()) + 4 * int(acc.sum()) + 16 * B +
+                4 * new_blocks + 8)
+        out.append(kv + meta)
+        lens = lens + n
     return np.array(out, dtype=np.float64)
 
 
@@ -232,8 +256,16 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
 
     R = max(K, W, 1)
     dev = torch.device("cuda", 0)
-    bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, sdev.TORCH_DT[cfg.kv_dtype])
-            for _ in range(1 if mode == "inplace" else 2)]
+    tdt = sdev.TORCH_DT[cfg.kv_dtype]
+    bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, tdt) for _ in range(1 if mode != "eqspec" else 2)]
+    if mode == "paged":
+        mb = -(-cap // PAGE)
+        cache = sd.PagedKV.empty(cfg.L, cfg.B, cfg.H, cfg.Dh, cfg.B * mb, PAGE, mb, tdt)
+        width = torch.zeros(1, dtype=torch.int32, device=dev)
+        view = (torch.zeros((cfg.B, cap), dtype=torch.int32, device=dev),
+                torch.zeros((cfg.B, cap), dtype=torch.int32, device=dev),
+                torch.zeros((cfg.B, cap), dtype=torch.int8, device=dev))
+        every_row = torch.arange(cfg.B, dtype=torch.int32, device=dev)
     ws = sd.workspace(cfg.B, cfg.D)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     acc_hist = torch.zeros((R, cfg.B), dtype=torch.int32, device=dev)
@@ -250,18 +282,26 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
             if mode == "inplace":
                 sd.realign_eqspec_inplace(bufs[0], w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r],
                                           status=status)
+            elif mode == "paged":
+                sd.paged_append(cache, w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], width=width,
+                                rect_tokens=view[0], rect_pos=view[1], rect_mask=view[2], status=status)
             else:
                 sd.realign_eqspec(bufs[r % 2], bufs[(r + 1) % 2], w.kv_new[r], w.drafts[r], acc_hist[r],
                                   nxt_hist[r], status=status)
             if ev:
                 ev[r][2].record()
 
-    w.load_initial(bufs[0])
-    torch.cuda.synchronize()
+    def reset():
+        w.load_initial(bufs[0])
+        if mode == "paged":
+            sd.paged_retire(cache, every_row, status=status)
+            sd.paged_admit(cache, bufs[0], status=status)
+        torch.cuda.synchronize()
+
+    reset()
     run(W)
     torch.cuda.synchronize()
-    w.load_initial(bufs[0])
-    torch.cuda.synchronize()
+    reset()
     ev = _events(K, 3)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -272,6 +312,8 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
     if int(status.item()) != 0:
         raise RuntimeError("device status %d during the timed rounds (%s)" % (int(status.item()), mode))
     out = {"total_ms": total_ms, "ver_ms": _ms(ev, 0, 1), "re_ms": _ms(ev, 1, 2), "acc": acc_hist[:K].cpu().numpy()}
+    if mode == "paged":
+        del cache
     del bufs
     torch.cuda.empty_cache()
     return out
@@ -293,12 +335,16 @@ def bench_chain(args, cfg):
     cap = max(cfg.cap, cfg.len_hi + R * cfg.D1)
     dev = torch.device("cuda", 0)
     w = sdev.GreedyRounds(cfg, R)
-    modes = ("inplace", "eqspec") if args.realign == "both" else (args.realign,)
+    modes = {"all": ("inplace", "eqspec", "paged"), "both": ("inplace", "eqspec")}.get(args.realign, (args.realign,))
     runs = {m: _time_chain(args, cfg, w, m, K, W, cap) for m in modes}
     with_traffic = cfg.name == "8b-gqa" and K == 64 and W == 8
 
     def roof(mode):
         r = runs[mode]
+        if mode == "paged":
+            pb = round_bytes_paged(cfg, w.lens0, r["acc"], PAGE)
+            gbs = pb.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
+            return _roof("k_paged_append + k_paged_commit", gbs, float(pb.mean()), float(r["re_ms"].mean() * 1e3))
         fn = round_bytes_inplace if mode == "inplace" else (lambda *a: round_bytes(*a)[1])
         rbytes = fn(cfg, w.lens0, w.width0, r["acc"])
         gbs = rbytes.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
@@ -317,15 +363,26 @@ def bench_chain(args, cfg):
                    "avg_launch_us": float(head["ver_ms"].mean() * 1e3)},
         "realign_share_of_round": float(head["re_ms"].sum() / head["total_ms"]),
     })
-    if len(modes) == 2:
+    if "eqspec" in modes and modes[0] != "eqspec":
         o = runs["eqspec"]
         extra["out_of_place"] = {"value": K / (o["total_ms"] * 1e-3), "unit": "rounds/s",
                                  "ms_per_step": o["total_ms"] / K, "roofline": roof("eqspec")}
+    if "paged" in modes and modes[0] != "paged":
+        o = runs["paged"]
+        pb = round_bytes_paged(cfg, w.lens0, o["acc"], PAGE)
+        gbs = pb.sum() / (o["re_ms"].sum() * 1e-3) / 1e9
+        extra["paged"] = {"value": K / (o["total_ms"] * 1e-3), "unit": "rounds/s", "ms_per_step": o["total_ms"] / K,
+                          "page_positions": PAGE,
+                          "realign": {"kernels": "k_paged_append + k_paged_commit", "achieved_gbs": gbs,
+                                      "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": float(pb.mean()),
+                                      "avg_call_us": float(o["re_ms"].mean() * 1e3)},
+                          "realign_share_of_round": float(o["re_ms"].sum() / o["total_ms"])}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, w.plans, w.lens0, w.width0, w.tok0, w.mask0, min(args.cpu_rounds, R),
                            args.cpu_layers)
-    how = {"inplace": " (realigned in place)", "eqspec": " (realigned out of place)"}[modes[0]]
+    how = {"inplace": " (realigned in place)", "eqspec": " (realigned out of place)",
+           "paged": " (paged cache, realigned as metadata)"}[modes[0]]
     workload = "%s: B=%d, D=%d, V=%d %s logits, KV %dx%dx%d %s, lengths U[%d,%d] left-padded, %d chained " \
                "greedy verify+EQSPEC rounds%s" % (
                    cfg.name, cfg.B, cfg.D, cfg.V, synth.DTYPE_NAME[cfg.logit_dtype], cfg.L, cfg.H, cfg.Dh,

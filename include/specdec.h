@@ -288,10 +288,16 @@ int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, i
  *  tokens       device int32 [rows][max_blocks * page]: each row's token ids
  *               from position 0.
  *  len          device int32 [rows]: content length of each row.
+ *  sync         device int32 [SPECDEC_PAGED_SYNC_WORDS]: zero when the cache is
+ *               created; append and admit count their workgroups in it and
+ *               leave it zero.
+ * Calls on one cache must not overlap (they are stream-ordered on one stream).
  * Allocation: batch entries in order take their new pages from the top of the
  * free stack, an entry's first new block getting the topmost remaining id;
  * retiring pushes a row's pages back in block order, entries in batch order.
  * Every page is free or in exactly one row's table; the calls keep it so. */
+#define SPECDEC_PAGED_SYNC_WORDS 256
+
 typedef struct {
   void *pages;
   int32_t *block_table;
@@ -299,6 +305,7 @@ typedef struct {
   int32_t *n_free;
   int32_t *tokens;
   int32_t *len;
+  int32_t *sync;
   int32_t rows, n_pages, page, max_blocks, layers, heads, head_dim;
   int32_t dtype;
 } specdec_paged_t;
@@ -309,7 +316,9 @@ typedef struct {
  * next_token[b], and the first n_b of its D+1 speculative entries kv_new
  * [layers][2][B][heads][D+1][head_dim] (device, 16-byte aligned), written at
  * positions len, len+1, ... of the row; new pages come off the free stack.
- * No other KV byte moves.  *width (device int32, nullable) receives
+ * No other KV byte moves.  The kv_new units this reads are numbered with
+ * 32-bit integers: layers * 2 * B * heads * (D+1) * head_dim * element size
+ * must stay below 2^35 bytes (E_ARG).  *width (device int32, nullable) receives
  * S' = max_b(len_b + n_b).  The rectangle view (rect_tokens nullable, then
  * nothing of it is written; rect_pos and rect_mask nullable; all
  * [B][rect_cap] on the device): row b left-padded by S' - len'_b with

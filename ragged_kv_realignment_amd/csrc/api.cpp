@@ -327,8 +327,11 @@ EXPORT int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *o
 
 // ------------------------------------------------------------------ paged KV
 
+static_assert(SPECDEC_PAGED_SYNC_WORDS == sd::kPagedSyncWords, "the header states the counter words");
+
 static int check_paged(const specdec_paged_t *k) {
-  if (!k || !k->pages || !k->block_table || !k->free_pages || !k->n_free || !k->tokens || !k->len) return SPECDEC_E_ARG;
+  if (!k || !k->pages || !k->block_table || !k->free_pages || !k->n_free || !k->tokens || !k->len || !k->sync)
+    return SPECDEC_E_ARG;
   if (k->rows < 1 || k->n_pages < 1 || k->page < 1 || k->max_blocks < 1 || k->layers < 0 || k->heads < 1 ||
       k->head_dim < 1)
     return SPECDEC_E_ARG;
@@ -354,6 +357,7 @@ static sd::PagedParams paged_params(int op, const specdec_paged_t *k, const int3
   p.n_free = k->n_free;
   p.tokens = k->tokens;
   p.len = k->len;
+  p.sync = k->sync;
   p.layers = k->layers;
   p.heads = k->heads;
   p.units = (int)((size_t)k->head_dim * esize(k->dtype) / 16);
@@ -383,6 +387,7 @@ EXPORT int specdec_paged_append(const specdec_paged_t *kv, const int32_t *rows, 
   if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
   if (B == 0) return SPECDEC_OK;
   const size_t knew = (size_t)kv->layers * 2 * B * kv->heads * (size_t)(D + 1) * kv->head_dim * esize(kv->dtype);
+  if (knew / 16 >= (1u << 31)) return SPECDEC_E_ARG;  // kv_new units are numbered with 32-bit integers
   if (overlap(kv_new, knew, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
   sd::PagedParams p = paged_params(sd::kPagedAppend, kv, rows, B, status);
   p.D = D;

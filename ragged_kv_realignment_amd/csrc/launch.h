@@ -72,6 +72,8 @@ struct RealignParams {
 };
 
 constexpr int kPagedAppend = 0, kPagedGather = 1, kPagedAdmit = 2, kPagedRetire = 3;
+constexpr int kPagedSyncWords = 256;  // int32 words of a paged cache's arrival counters
+constexpr int kPagedMaxGrid = 4096;   // workgroups of one append or admit launch at most
 
 struct PagedParams {
   int op;                      // kPaged*
@@ -81,6 +83,7 @@ struct PagedParams {
   int32_t *n_free;             // [1] entries of the stack in use
   int32_t *tokens;             // [rows][max_blocks * page]
   int32_t *len;                // [rows]
+  int32_t *sync;               // [kPagedSyncWords] arrival counters of append / admit, zero between calls
   int layers, heads, units, n_pages, page, max_blocks, rows;
   const int32_t *rowmap;       // [B] pool row of each batch entry, nullable = identity
   int B, D;

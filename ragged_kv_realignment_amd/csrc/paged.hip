@@ -18,11 +18,13 @@
 // the free stack, an entry's first new block getting the topmost remaining id;
 // retiring pushes a row's pages back in block order, entries in batch order.
 //
-// Every kernel of a call first runs the same plan (lengths, page counts and
+// Every workgroup of a call first runs the same plan (lengths, page counts and
 // their exclusive prefix over the batch, checks) on the unchanged inputs, so
 // all of them agree on the outcome; a call that fails a check writes nothing.
-// The block table, the free stack, lengths and token ids are updated by a
-// last single-workgroup launch, after every workgroup that reads them.
+// Append and admit are one launch each: the workgroup that arrives last at a
+// counter (after every other workgroup has finished reading the inputs)
+// updates the block table, the free stack, lengths and token ids, and resets
+// the counter.
 #include <limits.h>
 #include "device_common.h"
 #include "launch.h"
@@ -36,13 +38,19 @@ static_assert(kPgPer * kPgBlock == kMaxRealignRows, "the plan covers every batch
 
 typedef int i32x4p __attribute__((ext_vector_type(4)));
 
+constexpr int kFreeLds = 2048;  // entries of the free stack a call pops that are staged in LDS
+constexpr int kRectPer = 4;     // positions per thread of a rectangle-view workgroup
+constexpr int kRectChunk = kRectPer * kPgBlock;
+
 struct PagedPlan {
-  int r[kMaxRealignRows];   // pool row of each batch entry
-  int c[kMaxRealignRows];   // its length before the call (0 for admit)
-  int n[kMaxRealignRows];   // positions it gains
-  int k0[kMaxRealignRows];  // pages taken by the entries before it
+  int r[kMaxRealignRows];         // pool row of each batch entry
+  int c[kMaxRealignRows];         // its length before the call (0 for admit)
+  int n[kMaxRealignRows];         // positions it gains
+  int k0[kMaxRealignRows];        // pages taken by the entries before it
+  int first_pg[kMaxRealignRows];  // page of a partly filled block an append starts in
+  int freep[kFreeLds];            // freep[i] = free_pages[n_free - 1 - i], the i-th page popped
   int red[kPgBlock / kWave];
-  int need, smax, flags, n_free;
+  int need, smax, flags, n_free, last;
 };
 
 __device__ __forceinline__ int blocks_for(int n, int page) { return (n + page - 1) / page; }
@@ -71,34 +79,52 @@ __device__ __forceinline__ int block_excl_scan(int v, int *red, int &total) {
 
 // The plan of an append (ADMIT = false: entry b gains accept_len[b] + 1
 // positions at its length) or an admit (entry b's row must be empty and gains
-// in_len[b] positions).  Returns the status bits of a failed check (0 = go).
+// in_len[b] positions), from the call's unchanged inputs.  Returns the status
+// bits of a failed check (0 = go).
 template <bool ADMIT>
 __device__ int paged_plan(const PagedParams &p, PagedPlan &s) {
   const int B = p.B, tcap = p.max_blocks * p.page;
   int bad = 0, cap = 0, mx = 0, ksum = 0;
   int kloc[kPgPer];
+  // every independent input first, so the plan costs two dependent round trips
+  const int nf = *p.n_free;
   int width_in = 0;
   if (ADMIT) width_in = *p.in_width;
-  if (ADMIT && (width_in < 0 || width_in > p.rect_cap)) bad |= SPECDEC_S_LEN_RANGE;
+  int rr[kPgPer], cc[kPgPer], nn[kPgPer];
 #pragma unroll
   for (int e = 0; e < kPgPer; ++e) {
     const int b = threadIdx.x * kPgPer + e;
-    kloc[e] = 0;
+    rr[e] = 0;
+    cc[e] = 0;
+    nn[e] = 0;
     if (b >= B) continue;
     int r = p.rowmap ? p.rowmap[b] : b;
     if (r < 0 || r >= p.rows) {
       bad |= SPECDEC_S_LEN_RANGE;
       r = 0;
     }
-    int c = p.len[r], n;
+    rr[e] = r;
+    cc[e] = p.len[r];
+    nn[e] = ADMIT ? p.in_len[b] : p.accept_len[b] + 1;
+  }
+  // the top of the free stack, one entry per thread, before it is known how
+  // many entries the call pops
+  const bool nf_ok = nf >= 0 && nf <= p.n_pages;
+  const int top = nf_ok && (int)threadIdx.x < nf ? p.free_pages[nf - 1 - (int)threadIdx.x] : -1;
+  if (ADMIT && (width_in < 0 || width_in > p.rect_cap)) bad |= SPECDEC_S_LEN_RANGE;
+#pragma unroll
+  for (int e = 0; e < kPgPer; ++e) {
+    const int b = threadIdx.x * kPgPer + e;
+    kloc[e] = 0;
+    if (b >= B) continue;
+    const int r = rr[e];
+    int c = cc[e];
+    const int n = nn[e];
     if (ADMIT) {
-      n = p.in_len[b];
       if (c != 0 || n < 0 || n > width_in) bad |= SPECDEC_S_LEN_RANGE;
       c = 0;
-    } else {
-      const int a = p.accept_len[b];
-      if (a < 0 || a > p.D || c < 0 || c > tcap) bad |= SPECDEC_S_LEN_RANGE;
-      n = a + 1;
+    } else if (n < 1 || n > p.D + 1 || c < 0 || c > tcap) {
+      bad |= SPECDEC_S_LEN_RANGE;
     }
     if (bad) continue;
     const int cn = c + n;
@@ -106,14 +132,16 @@ __device__ int paged_plan(const PagedParams &p, PagedPlan &s) {
       cap = SPECDEC_S_CAPACITY;
       continue;
     }
-    // the block an append starts in must already be a valid page
+    // a partly filled block an append starts in must already be a valid page
+    int fp = -1;
     if (!ADMIT && c % p.page != 0) {
-      const int pg = p.bt[(size_t)r * p.max_blocks + c / p.page];
-      if (pg < 0 || pg >= p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
+      fp = p.bt[(size_t)r * p.max_blocks + c / p.page];
+      if (fp < 0 || fp >= p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
     }
     s.r[b] = r;
     s.c[b] = c;
     s.n[b] = n;
+    s.first_pg[b] = fp;
     kloc[e] = blocks_for(cn, p.page) - blocks_for(c, p.page);
     ksum += kloc[e];
     mx = max(mx, cn);
@@ -126,12 +154,12 @@ __device__ int paged_plan(const PagedParams &p, PagedPlan &s) {
     if (b < B) s.k0[b] = base;
     base += kloc[e];
   }
-  const int nf = *p.n_free;
-  if (nf < 0 || nf > p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
-  // the pages about to be taken must be valid ids
+  if (!nf_ok) bad |= SPECDEC_S_LEN_RANGE;
+  // the pages about to be popped must be valid ids; the first kFreeLds are staged
   for (int i = threadIdx.x; i < total && i < nf; i += kPgBlock) {
-    const int pg = p.free_pages[nf - 1 - i];
+    const int pg = i < kPgBlock ? top : p.free_pages[nf - 1 - i];
     if (pg < 0 || pg >= p.n_pages) bad |= SPECDEC_S_LEN_RANGE;
+    if (i < kFreeLds) s.freep[i] = pg;
   }
   const int smax = block_max_int<kPgBlock>(mx, s.red);
   int flags = block_or_int<kPgBlock>(bad | cap, s.red);
@@ -149,111 +177,61 @@ __device__ int paged_plan(const PagedParams &p, PagedPlan &s) {
   return flags;
 }
 
-// Page id of block `blk` of batch entry b after the call's allocation.
+// Page id of block `blk` of batch entry b after the call's allocation (blk at
+// or after the entry's first block touched).
 __device__ __forceinline__ int page_of(const PagedParams &p, const PagedPlan &s, int b, int blk) {
   const int nb_old = blocks_for(s.c[b], p.page);
-  if (blk < nb_old) return p.bt[(size_t)s.r[b] * p.max_blocks + blk];
-  return p.free_pages[s.n_free - 1 - (s.k0[b] + blk - nb_old)];
+  if (blk < nb_old) return s.first_pg[b];  // only the partly filled block an append starts in
+  const int i = s.k0[b] + blk - nb_old;
+  return i < kFreeLds ? s.freep[i] : p.free_pages[s.n_free - 1 - i];
 }
 
 __device__ __forceinline__ size_t page_unit(const PagedParams &p, int lk, int pg, int h, int slot) {
   return ((((size_t)lk * p.n_pages + pg) * p.heads + h) * p.page + slot) * (size_t)p.units;
 }
 
-// Append: workgroups [0, kv_wgs) copy the committed KV entries of every
-// (layer, K|V, entry, head) sequence into their slots; the B workgroups after
-// them write the rectangle view of row b (token ids, position ids, mask over
-// [0, S')) when it is asked for.
-__global__ __launch_bounds__(kPgBlock) void k_paged_append(PagedParams p) {
-  __shared__ PagedPlan s;
-  if (paged_plan<false>(p, s)) return;  // reported by k_paged_commit
-  const int B = p.B, U = p.units, H = p.heads, D1 = p.D + 1;
-  if ((int)blockIdx.x >= p.kv_wgs) {
-    const int b = blockIdx.x - p.kv_wgs;
-    const int r = s.r[b], c = s.c[b], n = s.n[b], W = s.smax, pad = W - c - n;
-    const int tcap = p.max_blocks * p.page;
-    for (int j = threadIdx.x; j < W; j += kPgBlock) {
-      const int k = j - pad;  // content index
-      int t = p.pad_token;
-      if (k >= 0) t = k < c ? p.tokens[(size_t)r * tcap + k] : (k < c + n - 1 ? p.draft[(size_t)b * p.D + k - c]
-                                                                               : p.next_token[b]);
-      p.rect_tok[(size_t)b * p.rect_cap + j] = t;
-      if (p.rect_pos) p.rect_pos[(size_t)b * p.rect_cap + j] = k >= 0 ? k : 0;
-      if (p.rect_mask) p.rect_mask[(size_t)b * p.rect_cap + j] = (int8_t)(k >= 0);
+// Every workgroup of a call arrives here once, after all of its reads of the
+// cache's metadata; the last one to arrive returns true and then owns the
+// commit.  No fence is needed: a workgroup's reads have returned their values
+// before its arrival is counted, so the commit's later writes cannot reach
+// them, and the commit reads nothing another workgroup wrote.  Arrivals are
+// counted in two levels so that no counter takes more than kArriveGroup
+// atomics: workgroups in groups of kArriveGroup consecutive ids count in
+// sync[1 + group]; the last of each group resets that counter and counts in
+// sync[0], which the committing workgroup resets.
+constexpr int kArriveGroup = 32;
+static_assert(kArriveGroup * (kPagedSyncWords - 1) >= kPagedMaxGrid, "every group has its counter");
+
+__device__ __forceinline__ bool arrive_last(const PagedParams &p, PagedPlan &s) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int g = blockIdx.x / kArriveGroup;
+    const int groups = ((int)gridDim.x + kArriveGroup - 1) / kArriveGroup;
+    const int in_group = min(kArriveGroup, (int)gridDim.x - g * kArriveGroup);
+    int last = 0;
+    if (atomicAdd(&p.sync[1 + g], 1) == in_group - 1) {
+      p.sync[1 + g] = 0;
+      last = atomicAdd(&p.sync[0], 1) == groups - 1;
     }
-    return;
+    s.last = last;
   }
-  const long nseg = (long)p.layers * 2 * B * H;
-  const i32x4p *nw = static_cast<const i32x4p *>(p.kv_new);
-  i32x4p *pages = static_cast<i32x4p *>(p.pages);
-  const int ups = D1 * U;  // units of one sequence's D+1 speculative entries
-  const int spp = max(1, kPgBlock / ups);
-  const int sq = threadIdx.x / ups, f = threadIdx.x - sq * ups;
-  for (long s0 = (long)blockIdx.x * spp; s0 < nseg; s0 += (long)p.kv_wgs * spp) {
-    const long seg = s0 + sq;
-    if (sq >= spp || seg >= nseg) continue;
-    const int lk = (int)(seg / ((long)B * H));
-    const int rem = (int)(seg - (long)lk * B * H);
-    const int b = rem / H, h = rem - b * H;
-    const int c = s.c[b], n = s.n[b];
-    for (int g = f; g < n * U; g += ups) {
-      const int i = g / U, u = g - i * U, j = c + i;
-      const int pg = page_of(p, s, b, j / p.page);
-      pages[page_unit(p, lk, pg, h, j % p.page) + u] =
-          __builtin_nontemporal_load(nw + ((size_t)seg * D1 + i) * U + u);
-    }
-  }
+  __syncthreads();
+  return s.last;
 }
 
-// Admit: workgroups copy entry b's content, positions [S - in_len[b], S) of
-// the input rectangle, into the pages the plan gives it.
-__global__ __launch_bounds__(kPgBlock) void k_paged_admit(PagedParams p) {
-  __shared__ PagedPlan s;
-  if (paged_plan<true>(p, s)) return;  // reported by k_paged_commit
-  const int B = p.B, U = p.units, H = p.heads;
-  const int S = *p.in_width;
-  const long nseg = (long)p.layers * 2 * B * H;
-  const i32x4p *src = static_cast<const i32x4p *>(p.rect_kv);
-  i32x4p *pages = static_cast<i32x4p *>(p.pages);
-  // units of all sequences, kPgBlock * 4 per workgroup pass
-  const long per_seg = (long)S * U;
-  const long total = nseg * per_seg;
-  for (long q0 = (long)blockIdx.x * kPgBlock * 4; q0 < total; q0 += (long)gridDim.x * kPgBlock * 4) {
-    i32x4p v[4];
-    long dst[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const long q = q0 + k * kPgBlock + threadIdx.x;
-      dst[k] = -1;
-      if (q >= total) continue;
-      const long seg = q / per_seg;
-      const int w = (int)(q - seg * per_seg), pos = w / U, u = w - pos * U;
-      const int lk = (int)(seg / ((long)B * H));
-      const int rem = (int)(seg - (long)lk * B * H);
-      const int b = rem / H, h = rem - b * H;
-      const int j = pos - (S - s.n[b]);  // content index
-      if (j < 0) continue;
-      v[k] = __builtin_nontemporal_load(src + (((size_t)seg * p.rect_cap) + pos) * U + u);
-      dst[k] = (long)page_unit(p, lk, page_of(p, s, b, j / p.page), h, j % p.page) + u;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (dst[k] >= 0) pages[dst[k]] = v[k];
-  }
-}
-
-// The last launch of an append or an admit: block table, free-stack count,
-// token ids and lengths (and the width of an append); reports the plan's
-// status bits.  One workgroup.
+// The commit of an append or an admit, by the last workgroup: block table,
+// free-stack count, token ids, lengths (and the width of an append), status;
+// or only the status bits of a failed plan.  Resets the arrival counter.
 template <bool ADMIT>
-__global__ __launch_bounds__(kPgBlock) void k_paged_commit(PagedParams p) {
-  __shared__ PagedPlan s;
-  const int flags = paged_plan<ADMIT>(p, s);
-  if (flags) {
-    if (threadIdx.x == 0) set_status(p.status, flags);
+__device__ void paged_commit(const PagedParams &p, PagedPlan &s) {
+  const int B = p.B, tcap = p.max_blocks * p.page;
+  if (s.flags) {
+    if (threadIdx.x == 0) {
+      set_status(p.status, s.flags);
+      p.sync[0] = 0;
+    }
     return;
   }
-  const int B = p.B, tcap = p.max_blocks * p.page;
   int dup = 0;
   for (int b = threadIdx.x; b < B; b += kPgBlock)
     for (int o = 0; o < b; ++o) dup |= (s.r[o] == s.r[b]);
@@ -262,22 +240,138 @@ __global__ __launch_bounds__(kPgBlock) void k_paged_commit(PagedParams p) {
     const int r = s.r[b], c = s.c[b], n = s.n[b];
     const int nb0 = blocks_for(c, p.page), nb1 = blocks_for(c + n, p.page);
     for (int blk = nb0; blk < nb1; ++blk) p.bt[(size_t)r * p.max_blocks + blk] = page_of(p, s, b, blk);
-    int32_t *t = p.tokens + (size_t)r * tcap + c;
-    if (ADMIT) {
-      const int S = *p.in_width;
-      const int32_t *src = p.rect_tok + (size_t)b * p.rect_cap + (S - n);
-      for (int k = 0; k < n; ++k) t[k] = src[k];
-    } else {
-      for (int k = 0; k < n - 1; ++k) t[k] = p.draft[(size_t)b * p.D + k];
-      t[n - 1] = p.next_token[b];
-    }
     p.len[r] = c + n;
+  }
+  if (ADMIT) {
+    // token ids: positions [S - n, S) of each input row, all entries at once
+    const int S = *p.in_width;
+    for (long x = threadIdx.x; x < (long)B * S; x += kPgBlock) {
+      const int b = (int)(x / S), j = (int)(x - (long)b * S), n = s.n[b];
+      if (j >= S - n) p.tokens[(size_t)s.r[b] * tcap + j - (S - n)] = p.rect_tok[(size_t)b * p.rect_cap + j];
+    }
+  } else {
+    const int D1 = p.D + 1;
+    for (int x = threadIdx.x; x < B * D1; x += kPgBlock) {
+      const int b = x / D1, k = x - b * D1, n = s.n[b];
+      if (k < n) p.tokens[(size_t)s.r[b] * tcap + s.c[b] + k] = k < n - 1 ? p.draft[(size_t)b * p.D + k]
+                                                                          : p.next_token[b];
+    }
   }
   if (threadIdx.x == 0) {
     *p.n_free = s.n_free - s.need;
     if (!ADMIT && p.width_out) *p.width_out = s.smax;
     if (dup) set_status(p.status, SPECDEC_S_ROWS_DUP);
+    p.sync[0] = 0;
   }
+}
+
+// Append, one launch: workgroups [0, kv_wgs) copy the committed KV entries of
+// every (layer, K|V, entry, head) sequence into their page slots; those after
+// them (when the rectangle view is asked for) write row b's token ids,
+// position ids and mask over [0, S'), kRectChunk positions each; the last
+// workgroup to finish commits.
+__global__ __launch_bounds__(kPgBlock) void k_paged_append(PagedParams p) {
+  __shared__ PagedPlan s;
+  const int flags = paged_plan<false>(p, s);
+  const int B = p.B, U = p.units, H = p.heads, D1 = p.D + 1;
+  if (!flags && (int)blockIdx.x >= p.kv_wgs) {
+    // rectangle view: item (b, chunk) covers positions [chunk * kRectChunk, +kRectChunk) of row b
+    const int chunks = (p.rect_cap + kRectChunk - 1) / kRectChunk;
+    const int rect_wgs = (int)gridDim.x - p.kv_wgs;
+    const int tcap = p.max_blocks * p.page, W = s.smax;
+    for (int item = blockIdx.x - p.kv_wgs; item < p.B * chunks; item += rect_wgs) {
+      const int b = item / chunks, j0 = (item - b * chunks) * kRectChunk;
+      const int r = s.r[b], c = s.c[b], n = s.n[b], pad = W - c - n;
+      int t[kRectPer];
+#pragma unroll
+      for (int k = 0; k < kRectPer; ++k) {  // every load of the chunk before any store
+        const int j = j0 + k * kPgBlock + (int)threadIdx.x, x = j - pad;  // x: content index
+        t[k] = p.pad_token;
+        if (j < W && x >= 0)
+          t[k] = x < c ? p.tokens[(size_t)r * tcap + x] : (x < c + n - 1 ? p.draft[(size_t)b * p.D + x - c]
+                                                                           : p.next_token[b]);
+      }
+#pragma unroll
+      for (int k = 0; k < kRectPer; ++k) {
+        const int j = j0 + k * kPgBlock + (int)threadIdx.x, x = j - pad;
+        if (j >= W) continue;
+        p.rect_tok[(size_t)b * p.rect_cap + j] = t[k];
+        if (p.rect_pos) p.rect_pos[(size_t)b * p.rect_cap + j] = x >= 0 ? x : 0;
+        if (p.rect_mask) p.rect_mask[(size_t)b * p.rect_cap + j] = (int8_t)(x >= 0);
+      }
+    }
+  } else if (!flags) {
+    // flat unit q of kv_new [L*2][B][H][D+1][U] (the host keeps it below 2^31)
+    const int ups = D1 * U;
+    const uint32_t total = (uint32_t)p.layers * 2u * (uint32_t)B * (uint32_t)H * (uint32_t)ups;
+    const FastDiv fd_ups = fast_div((uint32_t)ups), fd_u = fast_div((uint32_t)U), fd_h = fast_div((uint32_t)H),
+                  fd_b = fast_div((uint32_t)B);
+    const i32x4p *nw = static_cast<const i32x4p *>(p.kv_new);
+    i32x4p *pages = static_cast<i32x4p *>(p.pages);
+    constexpr int kPer = 4;
+    for (uint32_t q0 = blockIdx.x * (uint32_t)(kPgBlock * kPer); q0 < total;
+         q0 += (uint32_t)p.kv_wgs * (kPgBlock * kPer)) {
+      i32x4p v[kPer];
+      size_t at[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const uint32_t q = q0 + k * kPgBlock + threadIdx.x;
+        at[k] = SIZE_MAX;
+        if (q >= total) continue;
+        const uint32_t seg = fdiv(q, fd_ups), rest = q - seg * (uint32_t)ups;
+        const uint32_t i = fdiv(rest, fd_u), u = rest - i * (uint32_t)U;
+        const uint32_t t = fdiv(seg, fd_h), h = seg - t * (uint32_t)H;
+        const uint32_t lk = fdiv(t, fd_b), b = t - lk * (uint32_t)B;
+        if ((int)i >= s.n[b]) continue;
+        const int j = s.c[b] + (int)i;
+        v[k] = __builtin_nontemporal_load(nw + q);
+        at[k] = page_unit(p, (int)lk, page_of(p, s, (int)b, j / p.page), (int)h, j % p.page) + u;
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k)
+        if (at[k] != SIZE_MAX) pages[at[k]] = v[k];
+    }
+  }
+  if (arrive_last(p, s)) paged_commit<false>(p, s);
+}
+
+// Admit, one launch: workgroups copy entry b's content, positions
+// [S - in_len[b], S) of the input rectangle, into the pages the plan gives it;
+// the last workgroup to finish commits.
+__global__ __launch_bounds__(kPgBlock) void k_paged_admit(PagedParams p) {
+  __shared__ PagedPlan s;
+  if (!paged_plan<true>(p, s)) {
+    const int B = p.B, U = p.units, H = p.heads;
+    const int S = *p.in_width;
+    const long nseg = (long)p.layers * 2 * B * H;
+    const i32x4p *src = static_cast<const i32x4p *>(p.rect_kv);
+    i32x4p *pages = static_cast<i32x4p *>(p.pages);
+    const long per_seg = (long)S * U;
+    const long total = nseg * per_seg;
+    for (long q0 = (long)blockIdx.x * kPgBlock * 4; q0 < total; q0 += (long)gridDim.x * kPgBlock * 4) {
+      i32x4p v[4];
+      long dst[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const long q = q0 + k * kPgBlock + threadIdx.x;
+        dst[k] = -1;
+        if (q >= total) continue;
+        const long seg = q / per_seg;
+        const int w = (int)(q - seg * per_seg), pos = w / U, u = w - pos * U;
+        const int lk = (int)(seg / ((long)B * H));
+        const int rem = (int)(seg - (long)lk * B * H);
+        const int b = rem / H, h = rem - b * H;
+        const int j = pos - (S - s.n[b]);  // content index
+        if (j < 0) continue;
+        v[k] = __builtin_nontemporal_load(src + (((size_t)seg * p.rect_cap) + pos) * U + u);
+        dst[k] = (long)page_unit(p, lk, page_of(p, s, b, j / p.page), h, j % p.page) + u;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (dst[k] >= 0) pages[dst[k]] = v[k];
+    }
+  }
+  if (arrive_last(p, s)) paged_commit<true>(p, s);
 }
 
 // Gather: the batch's rows as a left-padded rectangle of width W = their
@@ -417,26 +511,22 @@ __global__ __launch_bounds__(kPgBlock) void k_paged_retire(PagedParams p) {
 
 hipError_t launch_paged(const PagedParams &q, hipStream_t st) {
   PagedParams p = q;
-  const int cus = device_cus();
+  const int cus = device_cus() < 1024 ? device_cus() : 1024;
   if (p.op == kPagedAppend) {
-    const int ups = (p.D + 1) * p.units;
-    const long spp = ups < kPgBlock ? kPgBlock / ups : 1;
-    const long nseg = ((long)p.layers * 2 * p.B * p.heads + spp - 1) / spp;
-    p.kv_wgs = (int)(nseg < 8L * cus ? (nseg > 0 ? nseg : 1) : 8L * cus);
-    const int extra = p.rect_tok ? p.B : 0;
+    // at most 2 * 1024 + 1024 workgroups (CU count capped below)
+    const long units = (long)p.layers * 2 * p.B * p.heads * (p.D + 1) * p.units;
+    const long g = (units + kPgBlock * 4 - 1) / (kPgBlock * 4);
+    p.kv_wgs = (int)(g < 2L * cus ? (g > 0 ? g : 1) : 2L * cus);
+    const long items = p.rect_tok ? (long)p.B * ((p.rect_cap + kRectChunk - 1) / kRectChunk) : 0;
+    const int extra = (int)(items < 1024 ? items : 1024);
     hipLaunchKernelGGL(k_paged_append, dim3((unsigned)(p.kv_wgs + extra)), dim3(kPgBlock), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_paged_commit<false>, dim3(1), dim3(kPgBlock), 0, st, p);
   } else if (p.op == kPagedAdmit) {
     // units of the widest input the buffer allows; workgroups past the real count find none
     const long units = (long)p.layers * 2 * p.B * p.heads * p.rect_cap * p.units;
     const long g = (units + kPgBlock * 4 - 1) / (kPgBlock * 4);
-    p.kv_wgs = (int)(g < 16L * cus ? (g > 0 ? g : 1) : 16L * cus);
+    p.kv_wgs = (int)(g < 8L * cus ? (g > 0 ? g : 1) : 8L * cus);
+    if (p.kv_wgs > kPagedMaxGrid) p.kv_wgs = kPagedMaxGrid;
     hipLaunchKernelGGL(k_paged_admit, dim3((unsigned)p.kv_wgs), dim3(kPgBlock), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_paged_commit<true>, dim3(1), dim3(kPgBlock), 0, st, p);
   } else if (p.op == kPagedGather) {
     const long units = (long)p.layers * 2 * p.B * p.heads * p.rect_cap * p.units;
     const long g = (units + kPgBlock * 4 - 1) / (kPgBlock * 4);

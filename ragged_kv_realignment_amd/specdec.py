@@ -343,9 +343,13 @@ group_by_len = specdec_group_by_len
 
 # ----------------------------------------------------------------- paged KV
 
+PAGED_SYNC_WORDS = 256  # SPECDEC_PAGED_SYNC_WORDS
+
+
 class PagedC(C.Structure):
     _fields_ = [("pages", C.c_void_p), ("block_table", C.c_void_p), ("free_pages", C.c_void_p),
-                ("n_free", C.c_void_p), ("tokens", C.c_void_p), ("len", C.c_void_p), ("rows", C.c_int32),
+                ("n_free", C.c_void_p), ("tokens", C.c_void_p), ("len", C.c_void_p), ("sync", C.c_void_p),
+                ("rows", C.c_int32),
                 ("n_pages", C.c_int32), ("page", C.c_int32), ("max_blocks", C.c_int32), ("layers", C.c_int32),
                 ("heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
 
@@ -355,9 +359,10 @@ class PagedKV:
 
     pages [L, 2, n_pages, H, page, Dh]; block_table [rows, max_blocks] int32
     (-1 = none); free_pages [n_pages] int32 stack with n_free [1] entries in use;
-    tokens [rows, max_blocks*page] int32; len [rows] int32."""
+    tokens [rows, max_blocks*page] int32; len [rows] int32; sync [PAGED_SYNC_WORDS]
+    int32, zero (allocated here when not given)."""
 
-    def __init__(self, pages, block_table, free_pages, n_free, tokens, len):
+    def __init__(self, pages, block_table, free_pages, n_free, tokens, len, sync=None):
         _need(pages, "pages")
         if pages.dtype not in _TORCH_DT or pages.dim() != 6 or pages.shape[1] != 2:
             raise ValueError("pages must be a [L, 2, n_pages, H, page, Dh] float32/float16/bfloat16 tensor")
@@ -371,9 +376,13 @@ class PagedKV:
             raise ValueError("inconsistent paged-cache shapes")
         self.pages, self.block_table, self.free_pages, self.n_free = pages, block_table, free_pages, n_free
         self.tokens, self.len = tokens, len
+        self.sync = torch.zeros(PAGED_SYNC_WORDS, dtype=torch.int32, device=pages.device) if sync is None else sync
+        _need(self.sync, "sync", torch.int32)
+        if self.sync.numel() < PAGED_SYNC_WORDS:
+            raise ValueError("sync must hold %d int32 words" % PAGED_SYNC_WORDS)
         self.c = PagedC(pages.data_ptr(), block_table.data_ptr(), free_pages.data_ptr(), n_free.data_ptr(),
-                        tokens.data_ptr(), len.data_ptr(), rows, n_pages, page, max_blocks, L, H, Dh,
-                        _TORCH_DT[pages.dtype])
+                        tokens.data_ptr(), len.data_ptr(), self.sync.data_ptr(), rows, n_pages, page, max_blocks,
+                        L, H, Dh, _TORCH_DT[pages.dtype])
 
     @staticmethod
     def empty(layers, rows, heads, head_dim, n_pages, page, max_blocks, dtype, device="cuda", free_order=None):

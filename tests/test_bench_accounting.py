@@ -75,3 +75,37 @@ def test_round_bytes_inplace_position_count():
     assert np.all(meta > 0) and np.all(meta < 1e6)  # token/position/mask bytes only
     _, full = bench.round_bytes(cfg, lens0, int(lens0.max()), np.array(accs))
     assert np.all(rb < full)
+
+
+def test_round_bytes_paged_counts_written_slots():
+    """Paged byte model: the KV part is the committed entries read once and
+    written once; the slots the oracle's paged append changes are exactly
+    those entries, and the rest of the model is metadata."""
+    cfg = synth.CONFIGS["8b-gqa"]
+    page = bench.PAGE
+    lens = synth.lengths(cfg)
+    S = int(lens.max())
+    tok, _, _ = synth.tokens_host(cfg, lens, S, True)
+    kv = synth.kv_host(cfg, lens, S, True, layer0=0, nlayers=1)
+    mb = -(-cfg.cap // page)
+    st = oracle.PagedState(1, cfg.H, cfg.Dh, cfg.B * mb, page, mb, cfg.B, kv.dtype)
+    cap = max(cfg.cap, S)
+    kvc = np.zeros(kv.shape[:4] + (cap, cfg.Dh), kv.dtype)
+    kvc[..., :kv.shape[4], :] = kv
+    tokc = np.zeros((cfg.B, cap), np.int32)
+    tokc[:, :tok.shape[1]] = tok
+    oracle.paged_admit(st, kvc, tokc, lens, S)
+    accs, written = [], []
+    for r in range(3):
+        plant, _, draft = synth.plan_greedy(cfg, r)
+        acc, nxt, _ = oracle.verify_greedy(synth.logits_host(cfg, r, plant), draft, cfg.B, cfg.D, cfg.V)
+        before = st.pages.copy()
+        oracle.paged_append(st, synth.kvnew_host(cfg, r, 0, 1), draft, acc, nxt)
+        slots = np.any(before.view(np.uint16) != st.pages.view(np.uint16), axis=(0, 1, 3, 5))
+        written.append(int(slots.sum()))
+        accs.append(acc)
+        assert written[-1] == int((acc + 1).sum())
+    pb = bench.round_bytes_paged(cfg, lens, np.array(accs), page)
+    kv_part = 2 * cfg.kv_pos_bytes * np.array(written, dtype=np.float64)
+    meta = pb - kv_part
+    assert np.all(meta > 0) and np.all(meta < 1e6)
