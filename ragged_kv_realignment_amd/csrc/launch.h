@@ -3,9 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace sd {
+#include "realign_params.h"
 
-constexpr int kMaxRealignRows = 1024;  // B limit of every realignment mode
+namespace sd {
 
 struct GreedyParams {
   const void *logits;
@@ -52,24 +52,7 @@ struct SampleLogitsParams {
 constexpr int kSlChunk = 4096;   // logits per split in sampled verification from logits
 constexpr int kSlThreads = 256;  // threads per workgroup of those kernels
 
-struct RealignParams {
-  int mode;
-  // source / destination KV in 16-byte units
-  const void *kv_in;
-  void *kv_out;
-  const void *kv_new;
-  int layers, heads, units;   // units = 16-byte units per position (head_dim * esize / 16)
-  int rows_in, cap_in, rows_out, cap_out;
-  const int32_t *tok_in, *len_in, *width_in;
-  int32_t *tok_out, *pos_out, *len_out, *width_out;
-  int8_t *mask_out;
-  const int32_t *rows;        // GATHER / APPEND row map, nullable
-  int B, group, D;
-  const int32_t *skip_group;
-  const int32_t *draft, *accept_len, *next_token;
-  int32_t pad_token;
-  int32_t *status;
-};
+
 
 constexpr int kPagedAppend = 0, kPagedGather = 1, kPagedAdmit = 2, kPagedRetire = 3;
 constexpr int kPagedSyncWords = 256;  // int32 words of a paged cache's arrival counters
@@ -107,12 +90,9 @@ struct GroupParams {
   int32_t *order, *uniform, *width, *n_uniform;
 };
 
-int device_cus();
 hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s);
 hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s);
 hipError_t launch_verify_sample_logits(const SampleLogitsParams &p, hipStream_t s);
-hipError_t launch_realign(const RealignParams &p, hipStream_t s);
-hipError_t launch_realign_inplace(const RealignParams &p, hipStream_t s);
 hipError_t launch_group_by_len(const GroupParams &p, hipStream_t s);
 hipError_t launch_paged(const PagedParams &p, hipStream_t s);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);

@@ -23,7 +23,7 @@
 #include <limits.h>
 #include "buffer_io.h"
 #include "device_common.h"
-#include "launch.h"
+#include "realign_params.h"
 #include "specdec.h"
 
 namespace sd {

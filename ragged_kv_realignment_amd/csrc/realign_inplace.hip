@@ -6,7 +6,7 @@
 // entries, and pad that appears where content or unused capacity was.
 #include "buffer_io.h"
 #include "device_common.h"
-#include "launch.h"
+#include "realign_params.h"
 #include "specdec.h"
 
 namespace sd {
