@@ -333,3 +333,80 @@ def paged_retire(st, rows):
     rows = _i32(rows)
     _check(_paged_lib().oracle_paged_retire(_p(st.geo), _p(st.bt), _p(st.free), _p(st.n_free), _p(st.len), _p(rows),
                                             len(rows)))
+
+
+# ------------------------------------------------------------ pool lifecycle
+
+class Sched:
+    """Scheduling state of a pool of `slots` sequences: active [slots] slot ids in
+    schedule order (n_active of them), free [slots] free slot ids ascending
+    (n_free of them), q_head: the next queued prompt."""
+
+    def __init__(self, slots, active=None):
+        self.slots = slots
+        self.active = np.zeros(slots, np.int32)
+        self.free = np.zeros(slots, np.int32)
+        act = list(range(slots)) if active is None else list(active)
+        self.active[:len(act)] = act
+        fr = [s for s in range(slots) if s not in set(act)]
+        self.free[:len(fr)] = fr
+        self.n_active = np.array([len(act)], np.int32)
+        self.n_free = np.array([len(fr)], np.int32)
+        self.q_head = np.zeros(1, np.int32)
+
+    def copy(self):
+        c = Sched.__new__(Sched)
+        c.slots = self.slots
+        for k in ("active", "free", "n_active", "n_free", "q_head"):
+            setattr(c, k, getattr(self, k).copy())
+        return c
+
+    def active_list(self):
+        return self.active[:int(self.n_active[0])].copy()
+
+    def free_list(self):
+        return self.free[:int(self.n_free[0])].copy()
+
+
+def _pool_lib():
+    L = lib()
+    if not hasattr(L, "_pool_ready"):
+        vp, i32p, ci = C.c_void_p, C.POINTER(C.c_int32), C.c_int
+        L.oracle_pool_finish.argtypes = [i32p, ci, i32p, ci, i32p, i32p, i32p, i32p, i32p, i32p, ci, ci, C.c_int32,
+                                         C.c_int32, i32p, i32p]
+        L.oracle_pool_admit.argtypes = [ci, ci, ci, ci, vp, i32p, ci, i32p, ci, i32p, i32p, i32p, i32p, i32p, ci, vp,
+                                        i32p, i32p, ci, i32p, i32p]
+        L.oracle_pool_finish.restype = C.c_int
+        L.oracle_pool_admit.restype = C.c_int
+        L._pool_ready = True
+    return L
+
+
+def pool_finish(tok_pool, len_pool, sched, rows, accept_len, D, eos_id, max_len):
+    """Finish at end-of-sequence or max length after a round's append (arrays and
+    `sched` are modified); returns the retired slots in active-list order."""
+    N, cap = tok_pool.shape
+    assert tok_pool.dtype == np.int32 and tok_pool.flags.c_contiguous and len_pool.dtype == np.int32
+    rows = _i32(rows)
+    retired = np.zeros(N, np.int32)
+    nr = np.zeros(1, np.int32)
+    _check(_pool_lib().oracle_pool_finish(_p(tok_pool), cap, _p(len_pool), N, _p(sched.active), _p(sched.n_active),
+                                          _p(sched.free), _p(sched.n_free), _p(rows), _p(_i32(accept_len)),
+                                          rows.shape[0], D, eos_id, max_len, _p(retired), _p(nr)))
+    return retired[:int(nr[0])]
+
+
+def pool_admit(kv_pool, tok_pool, len_pool, sched, pkv, ptok, plen):
+    """Admit queued prompts into the lowest free slots (arrays and `sched` are
+    modified); returns the slots filled, in admission order."""
+    L, _, N, H, cap, Dh = kv_pool.shape
+    Q, pcap = ptok.shape
+    assert kv_pool.flags.c_contiguous and tok_pool.flags.c_contiguous
+    admitted = np.zeros(N, np.int32)
+    na = np.zeros(1, np.int32)
+    pkv = np.ascontiguousarray(pkv, dtype=kv_pool.dtype)
+    _check(_pool_lib().oracle_pool_admit(L, H, Dh, kv_pool.dtype.itemsize, kv_pool.ctypes.data, _p(tok_pool), cap,
+                                         _p(len_pool), N, _p(sched.active), _p(sched.n_active), _p(sched.free),
+                                         _p(sched.n_free), _p(sched.q_head), Q, pkv.ctypes.data,
+                                         _p(_i32(ptok)), _p(_i32(plen)), pcap, _p(admitted), _p(na)))
+    return admitted[:int(na[0])]

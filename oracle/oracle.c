@@ -760,3 +760,112 @@ EXPORT int oracle_paged_retire(const int32_t *geo, int32_t *bt, int32_t *free_pa
   *n_free = top;
   return O_OK;
 }
+
+/* ------------------------------------------------------- pool lifecycle
+ * [BD] 2.3: EXSPEC keeps a pool of active sequences rather than a fixed batch
+ * and regroups them every round; sequences leave the pool when they finish and
+ * new ones join it.  The pages name the pool but not its policies; one
+ * admissible set is fixed here so results compare byte for byte:
+ *  - schedule: every active sequence runs every round; `active` lists their
+ *    pool slots in schedule order;
+ *  - finish: after a round's append, a sequence finishes at the first newly
+ *    committed position p holding the end-of-sequence id, or with p + 1 >=
+ *    max_len; its length becomes p + 1 (later committed entries are dropped),
+ *    it leaves the active list (the others keep their order) and its slot
+ *    joins the free slots, which are kept in ascending order;
+ *  - admit: queued prompts are taken in queue order, each into the lowest free
+ *    slot, and join the end of the active list; a prompt's content (positions
+ *    [0, plen) of the queue's own left-aligned buffer) and token ids are copied
+ *    into the slot.
+ * The pool is left-aligned: slot s holds its content at positions [0, len[s]). */
+
+/* rows [B] is the round's batch order over the active slots (B == *n_active)
+ * and accept_len its accepted lengths; the append has already run.  Writes
+ * retired [*n_retired] (finished slots in active-list order) and updates len,
+ * active, free_slots.  O_E_ARG: rows not a permutation of the active list,
+ * accepted lengths outside [0, D], a length shorter than its committed
+ * tokens, or max_len < 1. */
+EXPORT int oracle_pool_finish(const int32_t *tok_pool, int cap_pool, int32_t *len_pool, int slots, int32_t *active,
+                              int32_t *n_active, int32_t *free_slots, int32_t *n_free, const int32_t *rows,
+                              const int32_t *accept_len, int B, int D, int32_t eos_id, int32_t max_len,
+                              int32_t *retired, int32_t *n_retired) {
+  if (slots < 1 || B != *n_active || B < 0 || B > slots || max_len < 1 || D < 0) return O_E_ARG;
+  int32_t *in_batch = (int32_t *)calloc((size_t)slots, sizeof(int32_t));
+  int32_t *newlen = (int32_t *)malloc(sizeof(int32_t) * (size_t)slots);
+  int rc = O_OK;
+  for (int j = 0; j < B && rc == O_OK; ++j) {
+    const int s = rows[j], a = accept_len[j];
+    if (s < 0 || s >= slots || in_batch[s] || a < 0 || a > D) { rc = O_E_ARG; break; }
+    in_batch[s] = 1;
+    const int cn = len_pool[s], c = cn - (a + 1);
+    if (c < 0 || cn > cap_pool) { rc = O_E_ARG; break; }
+    newlen[s] = -1;
+    for (int p = c; p < cn; ++p)
+      if (tok_pool[(size_t)s * cap_pool + p] == eos_id || p + 1 >= max_len) { newlen[s] = p + 1; break; }
+  }
+  for (int j = 0; j < B && rc == O_OK; ++j)
+    if (active[j] < 0 || active[j] >= slots || !in_batch[active[j]]) rc = O_E_ARG;
+  if (rc != O_OK) { free(in_batch); free(newlen); return rc; }
+  int na = 0, nr = 0;
+  int32_t *is_free = (int32_t *)calloc((size_t)slots, sizeof(int32_t));
+  for (int i = 0; i < *n_free; ++i) is_free[free_slots[i]] = 1;
+  for (int j = 0; j < B; ++j) {
+    const int s = active[j];
+    if (newlen[s] >= 0) {
+      len_pool[s] = newlen[s];
+      retired[nr++] = s;
+      is_free[s] = 1;
+    } else {
+      active[na++] = s;
+    }
+  }
+  int nf = 0;
+  for (int s = 0; s < slots; ++s)
+    if (is_free[s]) free_slots[nf++] = s;
+  *n_active = na;
+  *n_free = nf;
+  *n_retired = nr;
+  free(in_batch); free(newlen); free(is_free);
+  return O_OK;
+}
+
+/* Admit from the queue: prompts [*q_head, Q) of pkv [L][2][Q][H][pcap][Dh],
+ * ptok [Q][pcap], plen [Q], as many as there are free slots.  Writes admitted
+ * [*n_admitted] (slots, in admission order).  O_E_CAPACITY (nothing written)
+ * if an admitted prompt is longer than the pool's cap; O_E_ARG for lengths
+ * outside [0, pcap]. */
+EXPORT int oracle_pool_admit(int L, int H, int Dh, int esize, void *kv_pool, int32_t *tok_pool, int cap_pool,
+                             int32_t *len_pool, int slots, int32_t *active, int32_t *n_active, int32_t *free_slots,
+                             int32_t *n_free, int32_t *q_head, int Q, const void *pkv, const int32_t *ptok,
+                             const int32_t *plen, int pcap, int32_t *admitted, int32_t *n_admitted) {
+  if (L < 0 || H <= 0 || Dh <= 0 || esize <= 0 || slots < 1 || Q < 0 || *q_head < 0 || *q_head > Q) return O_E_ARG;
+  const size_t pbytes = (size_t)Dh * (size_t)esize;
+  int k = *n_free < Q - *q_head ? *n_free : Q - *q_head;
+  for (int i = 0; i < k; ++i) {
+    const int q = *q_head + i;
+    if (plen[q] < 0 || plen[q] > pcap) return O_E_ARG;
+    if (plen[q] > cap_pool) return O_E_CAPACITY;
+  }
+  for (int i = 0; i < k; ++i) {
+    const int s = free_slots[i], q = *q_head + i, n = plen[q];
+    for (int l = 0; l < L; ++l)
+      for (int kv = 0; kv < 2; ++kv)
+        for (int h = 0; h < H; ++h) {
+          const unsigned char *src =
+              (const unsigned char *)pkv + ((((size_t)l * 2 + kv) * Q + q) * H + h) * (size_t)pcap * pbytes;
+          unsigned char *dst =
+              (unsigned char *)kv_pool + ((((size_t)l * 2 + kv) * slots + s) * H + h) * (size_t)cap_pool * pbytes;
+          memcpy(dst, src, (size_t)n * pbytes);
+        }
+    for (int j = 0; j < n; ++j) tok_pool[(size_t)s * cap_pool + j] = ptok[(size_t)q * pcap + j];
+    len_pool[s] = n;
+    active[*n_active + i] = s;
+    admitted[i] = s;
+  }
+  for (int i = k; i < *n_free; ++i) free_slots[i - k] = free_slots[i];
+  *n_free -= k;
+  *n_active += k;
+  *q_head += k;
+  *n_admitted = k;
+  return O_OK;
+}
