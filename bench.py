@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--realign", choices=("all", "both", "inplace", "eqspec", "paged"), default="all",
                     help="chain workloads: realign in place on one buffer, out of place between two, on a paged "
                          "cache, in place and out of place (both), or all three; the headline is the first")
+    ap.add_argument("--lifecycle", action="store_true",
+                    help="exspec: pool rounds with sequences finishing and queued prompts admitted")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration for profiling)")
     return ap.parse_args()
@@ -634,6 +636,119 @@ def bench_exspec(args, cfg):
                  _roof("k_gather", ga_gbs, float(gbytes.mean()), float(ga_ms.mean() * 1e3)), cpu, extra)
 
 
+def bench_lifecycle(args, cfg):
+    """Pool rounds with the sequence lifecycle: the exspec pool (256 slots, full
+    at the start) and a queue of 256 more prompts (lengths uniform in the pool's
+    range).  Each round: group the active sequences, gather the mixed batches,
+    verify, append, finish sequences whose committed tokens hold the
+    end-of-sequence id (planted at the stop position of 1 in 16 sequences per
+    round) or that reach max_len, and admit queued prompts into the freed slots.
+    The host reads the active count once per round to size the next one."""
+    import numpy as np
+    import torch
+    import synth
+    import synth.device as sdev
+    import ragged_kv_realignment_amd as sd
+
+    K = args.steps if args.steps is not None else cfg.rounds
+    N, G, D1, EOS = cfg.B, cfg.group, cfg.D1, 2
+    Q = N
+    dev = torch.device("cuda", 0)
+    tdt = sdev.TORCH_DT[cfg.kv_dtype]
+    cap = max(cfg.cap, cfg.len_hi + K * D1)
+    max_len = cap - D1
+    lens0 = synth.lengths(cfg)
+    pool = sd.SeqBuf.empty(cfg.L, N, cfg.H, cap, cfg.Dh, tdt, pool=True)
+    sdev.fill_kv(cfg, pool.kv, torch.from_numpy(lens0).to(dev), 0, False)
+    tok0, _, _ = synth.tokens_host(cfg, lens0, 0, False, cap=cap)
+    pool.tokens.copy_(torch.from_numpy(tok0))
+    pool.len.copy_(torch.from_numpy(lens0))
+    rng = np.random.default_rng(cfg.seed)
+    qlen = rng.integers(cfg.len_lo, cfg.len_hi + 1, Q).astype(np.int32)
+    queue = sd.SeqBuf.empty(cfg.L, Q, cfg.H, cfg.len_hi, cfg.Dh, tdt, pool=True)
+    sdev.fill_kv(cfg, queue.kv, torch.from_numpy(qlen).to(dev), 0, False)
+    qtok, _, _ = synth.tokens_host(cfg, qlen, 0, False, rows=Q, cap=cfg.len_hi)
+    queue.tokens.copy_(torch.from_numpy(qtok))
+    queue.len.copy_(torch.from_numpy(qlen))
+    sched = sd.Sched(N, active=range(N))
+    ng = (N + G - 1) // G
+    rect = sd.SeqBuf.empty(cfg.L, N, cfg.H, cap, cfg.Dh, tdt, groups=ng)
+    logits = torch.empty((K, N, D1, cfg.V), dtype=sdev.TORCH_DT[cfg.logit_dtype], device=dev)
+    drafts = []
+    keep = []
+    for r in range(K):
+        plant, miss, draft = synth.plan_greedy(cfg, r)
+        for b in np.nonzero(rng.random(N) < 1.0 / 16)[0]:
+            row = b * D1 + int(miss[b])
+            plant[row] = (EOS, -1, -1)
+            if miss[b] < cfg.D and draft[b, miss[b]] == EOS:
+                draft[b, miss[b]] = EOS + 1
+        keep.append(sdev.fill_logits(cfg, r, plant, logits[r]))
+        drafts.append(draft)
+    drafts = torch.from_numpy(np.stack(drafts)).to(dev)
+    kv_new = torch.empty((K, cfg.L, 2, N, cfg.H, D1, cfg.Dh), dtype=tdt, device=dev)
+    for r in range(K):
+        sdev.fill_kvnew(cfg, r, kv_new[r])
+    ws = sd.workspace(N, cfg.D)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    acc = torch.zeros(N, dtype=torch.int32, device=dev)
+    nxt = torch.zeros(N, dtype=torch.int32, device=dev)
+    retired = torch.zeros(N, dtype=torch.int32, device=dev)
+    n_ret = torch.zeros(1, dtype=torch.int32, device=dev)
+    admitted = torch.zeros(N, dtype=torch.int32, device=dev)
+    n_adm = torch.zeros(1, dtype=torch.int32, device=dev)
+    counts = torch.zeros((K, 3), dtype=torch.int32, device=dev)  # active, retired, admitted per round
+    torch.cuda.synchronize()
+    del keep
+    ev = _events(K, 3)
+    B = N
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for r in range(K):
+        if B == 0:
+            break
+        ev[r][0].record()
+        order, uni, wid, nu = sd.group_by_len(pool.len, G, ids=sched.active[:B])
+        sd.gather(pool, rect, order, G, uni, status=status)
+        sd.verify_greedy(logits[r, :B], drafts[r, :B], ws=ws, status=status, accept_len=acc[:B],
+                         next_token=nxt[:B])
+        kvn = kv_new[r] if B == N else kv_new[r, :, :, :B].contiguous()  # the active batch's entries
+        sd.append(pool, kvn, drafts[r, :B], acc[:B], nxt[:B], rows=order, status=status)
+        ev[r][1].record()
+        sd.pool_finish(pool, sched, order, acc[:B], cfg.D, EOS, max_len, retired=retired, n_retired=n_ret,
+                       status=status)
+        sd.pool_admit(pool, sched, queue, admitted=admitted, n_admitted=n_adm, status=status)
+        ev[r][2].record()
+        counts[r, 0] = B
+        counts[r, 1:2].copy_(n_ret)
+        counts[r, 2:3].copy_(n_adm)
+        B = int(sched.n_active.item())  # the host sizes the next round
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    if int(status.item()) != 0:
+        raise RuntimeError("device status %d during the lifecycle rounds" % int(status.item()))
+    cnt = counts.cpu().numpy()
+    done = int((cnt[:, 0] > 0).sum())
+    step_ms, life_ms = _ms(ev[:done], 0, 1), _ms(ev[:done], 1, 2)
+    config = {"workload": "exspec pool with lifecycle: %d slots full at the start, %d queued prompts with lengths "
+                          "U[%d,%d], batches of %d, D=%d, V=%d bf16, KV %dx%dx%d bf16, end-of-sequence planted at the "
+                          "stop position of 1 in 16 sequences per round, max_len %d, %d rounds"
+                          % (N, Q, cfg.len_lo, cfg.len_hi, G, cfg.D, cfg.V, cfg.L, cfg.H, cfg.Dh, max_len, K),
+              "pool": N, "queue": Q, "group": G, "D": cfg.D, "V": cfg.V, "cap": cap, "global_batch": N}
+    extra = {"finished_sequences": int(cnt[:, 1].sum()), "admitted_sequences": int(cnt[:, 2].sum()),
+             "finished_per_s": float(cnt[:, 1].sum() / (total_ms * 1e-3)),
+             "active_per_round": [int(x) for x in cnt[:done, 0]],
+             "round_step_ms": float(step_ms.mean()), "lifecycle_us": float(life_ms.mean() * 1e3),
+             "lifecycle_share_of_round": float(life_ms.sum() / total_ms)}
+    line = _line("EXSPEC pool rounds/sec with the sequence lifecycle (256-slot pool)", done / (total_ms * 1e-3),
+                 done, 0, total_ms / max(done, 1), "bf16", config, None, None, extra)
+    line["roofline"] = {"bound": "latency", "kernels": "k_pool_finish + k_pool_admit_plan + k_pool_admit_copy",
+                        "avg_call_us": float(life_ms.mean() * 1e3), "note": "one-workgroup list updates plus "
+                        "the admitted prompts' KV copy; the round's bytes are in the exspec line"}
+    return line
+
+
 def cpu_exspec(cfg, plans, lens0, rounds):
     """The oracle on the first rounds of the pool chain: grouping, verification of
     all sequences, gather and append of layer 0, scaled to all layers."""
@@ -678,6 +793,8 @@ def main():
     cfg = synth.CONFIGS[args.config]
     if cfg.name == "stoch":
         line = bench_stoch(args, cfg)
+    elif cfg.name == "exspec" and args.lifecycle:
+        line = bench_lifecycle(args, cfg)
     elif cfg.name == "exspec":
         line = bench_exspec(args, cfg)
     else:

@@ -268,6 +268,66 @@ int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbu
 int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, int32_t *uniform,
                          int32_t *width, int32_t *n_uniform, void *stream);
 
+/* Equal-length grouping over a list of pool rows: as specdec_group_by_len with
+ * entry i the pool row ids[i] (device int32 [N]): its length is len[ids[i]]
+ * (len: device int32, one entry per pool row), and `order` lists pool rows
+ * (ids entries) instead of indices.  Errors as for specdec_group_by_len, and
+ * E_ARG for a NULL ids. */
+int specdec_group_by_len_ids(const int32_t *len, const int32_t *ids, int N, int group, int32_t *order,
+                             int32_t *uniform, int32_t *width, int32_t *n_uniform, void *stream);
+
+/* --------------------------------------------------------- pool lifecycle */
+
+/* Scheduling state of a pool of sequences ("Batch Speculative Decoding Done
+ * Right", section 2.3: EXSPEC keeps a pool of active sequences, not a fixed
+ * batch).  All device int32:
+ *  active      [slots]: the active sequences' pool rows in schedule order;
+ *              entries [0, *n_active) are valid.
+ *  n_active    [1].
+ *  free_slots  [slots]: the free pool rows in ascending order; entries
+ *              [0, *n_free) are valid.
+ *  n_free      [1].
+ *  q_head      [1]: the next prompt of the queue to admit.
+ * Every pool row is active or free, never both.  The pool (specdec_seqbuf_t)
+ * is left-aligned: row s holds its content at positions [0, len[s]). */
+typedef struct {
+  int32_t *active;
+  int32_t *n_active;
+  int32_t *free_slots;
+  int32_t *n_free;
+  int32_t *q_head;
+} specdec_sched_t;
+
+/* Finish after a round's append: rows [B] (device) is the round's batch order,
+ * a permutation of the active list (B == *n_active), and accept_len [B] its
+ * accepted lengths (entry j committed accept_len[j] + 1 tokens, now the last
+ * ones of row rows[j]).  A sequence finishes at the first newly committed
+ * position p holding eos_id, or with p + 1 >= max_len (max_len >= 1): its
+ * length becomes p + 1, it leaves the active list (the others keep their
+ * order) and its row joins the free rows.  retired [pool->rows] (device)
+ * receives the finished rows in active-list order and *n_retired (device) their
+ * count.  Device conditions (nothing written): B != *n_active, rows outside the
+ * pool or not active, accepted lengths outside [0, D], a length shorter than its
+ * committed tokens set SPECDEC_S_LEN_RANGE; a row twice SPECDEC_S_ROWS_DUP.
+ * Limits: pool->rows <= 4096.  Errors: E_ARG, E_LAUNCH. */
+int specdec_pool_finish(const specdec_seqbuf_t *pool, const specdec_sched_t *sched, const int32_t *rows,
+                        const int32_t *accept_len, int B, int D, int32_t eos_id, int32_t max_len, int32_t *retired,
+                        int32_t *n_retired, int32_t *status, void *stream);
+
+/* Admit from a prompt queue: `queue` holds Q = queue->rows prompts in the
+ * pool's geometry, left-aligned (prompt q's content at [0, queue->len[q]) of its
+ * row, token ids in queue->tokens).  The next k = min(*n_free, Q - *q_head)
+ * prompts, in queue order, go to the k lowest free rows and join the end of the
+ * active list; their content and token ids are copied and their lengths set.
+ * admitted [pool->rows] (device) receives the rows filled, in order, and
+ * *n_admitted (device) k.  Device conditions (nothing admitted, *n_admitted =
+ * 0): a prompt longer than pool->cap sets SPECDEC_S_CAPACITY; inconsistent
+ * counts or lengths outside [0, queue->cap] SPECDEC_S_LEN_RANGE.
+ * Limits: pool->rows <= 4096.  Errors: E_ARG, E_DTYPE, E_ALIGN, E_ALIAS,
+ * E_LAUNCH. */
+int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_t *sched, const specdec_seqbuf_t *queue,
+                       int32_t *admitted, int32_t *n_admitted, int32_t *status, void *stream);
+
 /* ------------------------------------------------------------- paged KV */
 
 /* A paged KV cache: rows of sequences whose positions live in pages of a

@@ -316,6 +316,7 @@ EXPORT int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *o
   if (N > 0 && (!len || !order || !uniform || !width)) return SPECDEC_E_ARG;
   sd::GroupParams p;
   p.len = len;
+  p.ids = nullptr;
   p.N = N;
   p.group = group;
   p.order = order;
@@ -453,4 +454,89 @@ EXPORT int specdec_paged_retire(const specdec_paged_t *kv, const int32_t *rows, 
   if (B == 0) return SPECDEC_OK;
   sd::PagedParams p = paged_params(sd::kPagedRetire, kv, rows, B, status);
   return launched(sd::launch_paged(p, as_stream(stream)));
+}
+
+// ------------------------------------------------------------ pool lifecycle
+
+EXPORT int specdec_group_by_len_ids(const int32_t *len, const int32_t *ids, int N, int group, int32_t *order,
+                                    int32_t *uniform, int32_t *width, int32_t *n_uniform, void *stream) {
+  if (N < 0 || N > kMaxPool || group < 1) return SPECDEC_E_ARG;
+  if (!n_uniform) return SPECDEC_E_ARG;
+  if (N > 0 && (!len || !ids || !order || !uniform || !width)) return SPECDEC_E_ARG;
+  sd::GroupParams p;
+  p.len = len;
+  p.ids = ids;
+  p.N = N;
+  p.group = group;
+  p.order = order;
+  p.uniform = uniform;
+  p.width = width;
+  p.n_uniform = n_uniform;
+  return launched(sd::launch_group_by_len(p, as_stream(stream)));
+}
+
+static bool sched_ok(const specdec_sched_t *s) {
+  return s && s->active && s->n_active && s->free_slots && s->n_free && s->q_head;
+}
+
+static sd::PoolParams pool_params(const specdec_seqbuf_t *pool, const specdec_sched_t *st, int32_t *status) {
+  sd::PoolParams p;
+  memset(&p, 0, sizeof(p));
+  p.kv = pool->kv;
+  p.tokens = pool->tokens;
+  p.len = pool->len;
+  p.layers = pool->layers;
+  p.heads = pool->heads;
+  p.units = (int)((size_t)pool->head_dim * esize(pool->dtype) / 16);
+  p.slots = pool->rows;
+  p.cap = pool->cap;
+  p.active = st->active;
+  p.n_active = st->n_active;
+  p.free_slots = st->free_slots;
+  p.n_free = st->n_free;
+  p.q_head = st->q_head;
+  p.status = status;
+  return p;
+}
+
+EXPORT int specdec_pool_finish(const specdec_seqbuf_t *pool, const specdec_sched_t *sched, const int32_t *rows,
+                               const int32_t *accept_len, int B, int D, int32_t eos_id, int32_t max_len,
+                               int32_t *retired, int32_t *n_retired, int32_t *status, void *stream) {
+  int rc = check_seqbuf_shape(pool);
+  if (rc) return rc;
+  if (!sched_ok(sched) || !pool->tokens || !retired || !n_retired) return SPECDEC_E_ARG;
+  if (pool->rows < 1 || pool->rows > sd::kMaxPoolSlots || B < 0 || B > pool->rows || D < 0 || max_len < 1)
+    return SPECDEC_E_ARG;
+  if (B > 0 && (!rows || !accept_len)) return SPECDEC_E_ARG;
+  sd::PoolParams p = pool_params(pool, sched, status);
+  p.rows = rows;
+  p.accept_len = accept_len;
+  p.B = B;
+  p.D = D;
+  p.eos_id = eos_id;
+  p.max_len = max_len;
+  p.retired = retired;
+  p.n_retired = n_retired;
+  return launched(sd::launch_pool_finish(p, as_stream(stream)));
+}
+
+EXPORT int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_t *sched, const specdec_seqbuf_t *queue,
+                              int32_t *admitted, int32_t *n_admitted, int32_t *status, void *stream) {
+  int rc = check_seqbuf_shape(pool);
+  if (rc) return rc;
+  rc = check_seqbuf_shape(queue);
+  if (rc) return rc;
+  if (!sched_ok(sched) || !pool->tokens || !queue->tokens || !admitted || !n_admitted) return SPECDEC_E_ARG;
+  if (pool->rows < 1 || pool->rows > sd::kMaxPoolSlots || queue->cap < 1 || !same_geometry(pool, queue))
+    return SPECDEC_E_ARG;
+  if (overlap(queue->kv, kv_bytes(queue), pool->kv, kv_bytes(pool))) return SPECDEC_E_ALIAS;
+  sd::PoolParams p = pool_params(pool, sched, status);
+  p.pkv = queue->kv;
+  p.ptok = queue->tokens;
+  p.plen = queue->len;
+  p.Q = queue->rows;
+  p.pcap = queue->cap;
+  p.admitted = admitted;
+  p.n_admitted = n_admitted;
+  return launched(sd::launch_pool_admit(p, as_stream(stream)));
 }

@@ -2,7 +2,9 @@
 // Right", section 2.3: a pool of active sequences is scheduled in batches of
 // equal length, which need no realignment; only mixed batches are realigned).
 //
-// One workgroup of 1024 threads ranks N <= 4096 lengths held in LDS.  With
+// One workgroup of 1024 threads ranks N <= 4096 lengths held in LDS (entry i's
+// length is len[i], or len[ids[i]] for a list of pool rows, and then the order
+// lists those rows).  With
 // lt_i = #{len < len_i}, eq_i = #{len == len_i} and eqb_i = #{j < i, len_j ==
 // len_i}, id i sits at position lt_i + eqb_i of the (length, id) order; the
 // first floor(eq_i / G) * G ids of each length are full-batch members.  Full
@@ -16,7 +18,7 @@
 namespace sd {
 
 constexpr int kGroupThreads = 1024;
-constexpr int kMaxPool = 4096;
+constexpr int kMaxPool = kMaxPoolSlots;
 
 __global__ __launch_bounds__(kGroupThreads) void k_group_by_len(GroupParams p) {
   __shared__ int s_len[kMaxPool];
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_by_len(GroupParams p) {
   __shared__ int s_nu;
   const int N = p.N, G = p.group;
   if (threadIdx.x == 0) { s_tot = 0; s_nu = 0; }
-  for (int i = threadIdx.x; i < N; i += kGroupThreads) s_len[i] = p.len[i];
+  for (int i = threadIdx.x; i < N; i += kGroupThreads) s_len[i] = p.len[p.ids ? p.ids[i] : i];
   __syncthreads();
   int myfull = 0;
   for (int i = threadIdx.x; i < N; i += kGroupThreads) {
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_by_len(GroupParams p) {
     s_order[s_full[i] ? fb : tot + (rank - fb)] = i;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < N; i += kGroupThreads) p.order[i] = s_order[i];
+  for (int i = threadIdx.x; i < N; i += kGroupThreads) p.order[i] = p.ids ? p.ids[s_order[i]] : s_order[i];
   const int nb = (N + G - 1) / G;
   int nu = 0;
   for (int g = threadIdx.x; g < nb; g += kGroupThreads) {

@@ -86,8 +86,31 @@ struct PagedParams {
 
 struct GroupParams {
   const int32_t *len;
+  const int32_t *ids;          // nullable: entry i is pool row ids[i] (len read there, order lists ids)
   int N, group;
   int32_t *order, *uniform, *width, *n_uniform;
+};
+
+constexpr int kMaxPoolSlots = 4096;  // pool rows a grouping or a lifecycle call handles
+
+struct PoolParams {
+  // the pool (left-aligned rows)
+  void *kv;                    // [L][2][slots][H][cap][units * 16 bytes]
+  int32_t *tokens, *len;       // [slots][cap], [slots]
+  int layers, heads, units, slots, cap;
+  // scheduling state
+  int32_t *active, *n_active, *free_slots, *n_free, *q_head;
+  // finish
+  const int32_t *rows, *accept_len;
+  int B, D;
+  int32_t eos_id, max_len;
+  int32_t *retired, *n_retired;
+  // admit: the prompt queue [L][2][Q][H][pcap][units * 16 bytes], tokens [Q][pcap], lengths [Q]
+  const void *pkv;
+  const int32_t *ptok, *plen;
+  int Q, pcap;
+  int32_t *admitted, *n_admitted;
+  int32_t *status;
 };
 
 hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s);
@@ -95,6 +118,8 @@ hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s);
 hipError_t launch_verify_sample_logits(const SampleLogitsParams &p, hipStream_t s);
 hipError_t launch_group_by_len(const GroupParams &p, hipStream_t s);
 hipError_t launch_paged(const PagedParams &p, hipStream_t s);
+hipError_t launch_pool_finish(const PoolParams &p, hipStream_t s);
+hipError_t launch_pool_admit(const PoolParams &p, hipStream_t s);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
 
 }  // namespace sd

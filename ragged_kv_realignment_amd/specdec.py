@@ -25,7 +25,8 @@ _TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init", "specdec_verify_greedy",
            "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
            "specdec_realign_kv", "specdec_group_by_len", "specdec_paged_append", "specdec_paged_gather",
-           "specdec_paged_admit", "specdec_paged_retire")
+           "specdec_paged_admit", "specdec_paged_retire", "specdec_group_by_len_ids", "specdec_pool_finish",
+           "specdec_pool_admit")
 
 
 class SpecDecError(RuntimeError):
@@ -69,9 +70,14 @@ def lib():
         L.specdec_paged_gather.argtypes = [C.POINTER(PagedC), vp, ci, C.POINTER(SeqBufC), C.c_int32, vp, vp]
         L.specdec_paged_admit.argtypes = [C.POINTER(PagedC), vp, ci, C.POINTER(SeqBufC), vp, vp]
         L.specdec_paged_retire.argtypes = [C.POINTER(PagedC), vp, ci, vp, vp]
+        L.specdec_group_by_len_ids.argtypes = [vp, vp, ci, ci, vp, vp, vp, vp, vp]
+        L.specdec_pool_finish.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), vp, vp, ci, ci, C.c_int32, C.c_int32,
+                                          vp, vp, vp, vp]
+        L.specdec_pool_admit.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), C.POINTER(SeqBufC), vp, vp, vp, vp]
         for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample",
                   "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len",
-                  "specdec_paged_append", "specdec_paged_gather", "specdec_paged_admit", "specdec_paged_retire"):
+                  "specdec_paged_append", "specdec_paged_gather", "specdec_paged_admit", "specdec_paged_retire",
+                  "specdec_group_by_len_ids", "specdec_pool_finish", "specdec_pool_admit"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -319,18 +325,24 @@ def append(pool, kv_new, draft, accept_len, next_token, rows=None, status=None):
                        status)
 
 
-def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_uniform=None):
-    """Equal-length grouping of a pool: returns (order, uniform, width, n_uniform) device tensors."""
+def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_uniform=None, ids=None):
+    """Equal-length grouping of a pool: returns (order, uniform, width, n_uniform) device tensors.
+    With `ids` (pool rows), entry i is row ids[i], its length lens[ids[i]], and order lists rows."""
     _need(lens, "lens", torch.int32)
-    N = lens.numel()
+    N = lens.numel() if ids is None else ids.numel()
     nb = (N + group - 1) // group if group > 0 else 0
     dev = lens.device
     order = _i32(N, dev) if order is None else order
     uniform = _i32(max(nb, 1), dev) if uniform is None else uniform
     width = _i32(max(nb, 1), dev) if width is None else width
     n_uniform = _i32(1, dev) if n_uniform is None else n_uniform
-    rc = lib().specdec_group_by_len(lens.data_ptr(), N, group, order.data_ptr(), uniform.data_ptr(),
-                                    width.data_ptr(), n_uniform.data_ptr(), _stream())
+    if ids is None:
+        rc = lib().specdec_group_by_len(lens.data_ptr(), N, group, order.data_ptr(), uniform.data_ptr(),
+                                        width.data_ptr(), n_uniform.data_ptr(), _stream())
+    else:
+        _need(ids, "ids", torch.int32)
+        rc = lib().specdec_group_by_len_ids(lens.data_ptr(), ids.data_ptr(), N, group, order.data_ptr(),
+                                            uniform.data_ptr(), width.data_ptr(), n_uniform.data_ptr(), _stream())
     _check(rc, "specdec_group_by_len")
     return order, uniform[:nb], width[:nb], n_uniform
 
@@ -460,3 +472,59 @@ def paged_retire(cache, rows, status=None):
     _need(rows, "rows", torch.int32)
     rc = lib().specdec_paged_retire(C.byref(cache.c), rows.data_ptr(), rows.numel(), _ptr(status), _stream())
     _check(rc, "specdec_paged_retire")
+
+
+# ------------------------------------------------------------ pool lifecycle
+
+class SchedC(C.Structure):
+    _fields_ = [("active", C.c_void_p), ("n_active", C.c_void_p), ("free_slots", C.c_void_p),
+                ("n_free", C.c_void_p), ("q_head", C.c_void_p)]
+
+
+class Sched:
+    """Device scheduling state of a pool (see specdec_sched_t): active [slots] rows in
+    schedule order (n_active valid), free_slots [slots] ascending (n_free valid), q_head."""
+
+    def __init__(self, slots, active=(), device="cuda"):
+        act = [int(a) for a in active]
+        fr = [s for s in range(slots) if s not in set(act)]
+        self.active = torch.zeros(slots, dtype=torch.int32, device=device)
+        self.free_slots = torch.zeros(slots, dtype=torch.int32, device=device)
+        if act:
+            self.active[:len(act)] = torch.tensor(act, dtype=torch.int32)
+        if fr:
+            self.free_slots[:len(fr)] = torch.tensor(fr, dtype=torch.int32)
+        self.n_active = torch.tensor([len(act)], dtype=torch.int32, device=device)
+        self.n_free = torch.tensor([len(fr)], dtype=torch.int32, device=device)
+        self.q_head = torch.zeros(1, dtype=torch.int32, device=device)
+        self.c = SchedC(self.active.data_ptr(), self.n_active.data_ptr(), self.free_slots.data_ptr(),
+                        self.n_free.data_ptr(), self.q_head.data_ptr())
+
+
+def pool_finish(pool, sched, rows, accept_len, D, eos_id, max_len, retired=None, n_retired=None, status=None):
+    """Finish sequences at end-of-sequence or max length after a round's append.
+    Returns (retired, n_retired) device tensors."""
+    _need(rows, "rows", torch.int32)
+    _need(accept_len, "accept_len", torch.int32)
+    B = rows.numel()
+    if accept_len.numel() != B:
+        raise ValueError("rows and accept_len must have one entry per batch entry")
+    dev = pool.kv.device
+    retired = _i32(pool.rows, dev) if retired is None else retired
+    n_retired = _i32(1, dev) if n_retired is None else n_retired
+    rc = lib().specdec_pool_finish(C.byref(pool.c), C.byref(sched.c), rows.data_ptr(), accept_len.data_ptr(), B, D,
+                                   eos_id, max_len, retired.data_ptr(), n_retired.data_ptr(), _ptr(status), _stream())
+    _check(rc, "specdec_pool_finish")
+    return retired, n_retired
+
+
+def pool_admit(pool, sched, queue, admitted=None, n_admitted=None, status=None):
+    """Admit queued prompts (a SeqBuf of left-aligned prompts) into the lowest free rows.
+    Returns (admitted, n_admitted) device tensors."""
+    dev = pool.kv.device
+    admitted = _i32(pool.rows, dev) if admitted is None else admitted
+    n_admitted = _i32(1, dev) if n_admitted is None else n_admitted
+    rc = lib().specdec_pool_admit(C.byref(pool.c), C.byref(sched.c), C.byref(queue.c), admitted.data_ptr(),
+                                  n_admitted.data_ptr(), _ptr(status), _stream())
+    _check(rc, "specdec_pool_admit")
+    return admitted, n_admitted

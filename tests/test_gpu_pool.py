@@ -1,0 +1,193 @@
+"""GPU parity of the pool lifecycle against the oracle: grouping over the active
+rows, gather of mixed batches, verification, append, finish at end-of-sequence
+or max length, and admission from a prompt queue, round after round on random
+pools, with every list, length, token id and KV byte of the active rows
+compared.  Status bits leave the state unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import bytes_equal, from_np_raw, say, to_np_raw
+
+pytestmark = pytest.mark.gpu
+
+EOS = 2
+
+
+@pytest.fixture(scope="module")
+def sd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_kv_realignment_amd as m
+    return m
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_group_by_len_ids(sd, seed):
+    rng = np.random.default_rng(1300 + seed)
+    slots = [1, 9, 256, 4096, 100, 37][seed]
+    N = int(rng.integers(0, slots + 1))
+    ids = rng.permutation(slots)[:N].astype(np.int32)
+    lens = rng.integers(0, 30, slots).astype(np.int32)
+    G = int(rng.integers(1, 9))
+    say("group_by_len ids", slots, N, G)
+    order, uni, wid, nu = sd.group_by_len(torch.from_numpy(lens).cuda(), G, ids=torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    oorder, ouni, owid, onu = oracle.group_by_len(lens[ids], G)
+    assert np.array_equal(order.cpu().numpy(), ids[oorder])
+    assert np.array_equal(uni.cpu().numpy(), ouni) and np.array_equal(wid.cpu().numpy(), owid)
+    assert int(nu.item()) == onu
+
+
+def _host_state(pool, sched):
+    torch.cuda.synchronize()
+    na, nf = int(sched.n_active.item()), int(sched.n_free.item())
+    return (sched.active.cpu().numpy()[:na], sched.free_slots.cpu().numpy()[:nf], int(sched.q_head.item()),
+            pool.len.cpu().numpy(), pool.tokens.cpu().numpy(), to_np_raw(pool.kv))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_lifecycle_rounds(sd, seed):
+    """Random pools and prompt queues; every round: group the active rows, gather
+    the mixed batches, verify (from random logits with end-of-sequence ids
+    planted) or take random accepted lengths, append, finish, admit."""
+    rng = np.random.default_rng(1400 + seed)
+    with_verify = seed % 2 == 0
+    dt_np, tdt, Dh = [(np.float16, torch.float16, 64), (np.float32, torch.float32, 4)][seed % 2]
+    slots = int(rng.integers(2, 40))
+    G = int(rng.integers(1, 6))
+    D = int(rng.integers(0, 5))
+    L, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    max_len = int(rng.integers(12, 80))
+    cap = max_len + D + 1
+    Q = int(rng.integers(slots, 4 * slots))
+    pcap = max_len
+    V = 300
+    say("lifecycle", seed, slots, G, D, L, H, Dh, max_len, Q, with_verify)
+    plen = rng.integers(1, max_len, Q).astype(np.int32)
+    pkv = np.zeros((L, 2, Q, H, pcap, Dh), dt_np)
+    ptok = np.zeros((Q, pcap), np.int32)
+    for q in range(Q):
+        pkv[:, :, q, :, :plen[q]] = rng.standard_normal((L, 2, H, plen[q], Dh))
+        ptok[q, :plen[q]] = rng.integers(3, V, plen[q])
+    # host (oracle) state
+    hkv = np.zeros((L, 2, slots, H, cap, Dh), dt_np)
+    htok = np.zeros((slots, cap), np.int32)
+    hlen = np.zeros(slots, np.int32)
+    hs = oracle.Sched(slots, active=[])
+    # device state
+    pool = sd.SeqBuf(from_np_raw(hkv, tdt), torch.from_numpy(htok).cuda(), torch.from_numpy(hlen).cuda())
+    queue = sd.SeqBuf(from_np_raw(pkv, tdt), torch.from_numpy(ptok).cuda(), torch.from_numpy(plen).cuda())
+    ds = sd.Sched(slots)
+    ds.n_active.zero_()
+    ds.free_slots.copy_(torch.arange(slots, dtype=torch.int32))
+    ds.n_free.fill_(slots)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = sd.workspace(slots, D)
+    adm, nadm = sd.pool_admit(pool, ds, queue, status=status)
+    want_adm = oracle.pool_admit(hkv, htok, hlen, hs, pkv, ptok, plen)
+    assert np.array_equal(adm.cpu().numpy()[:int(nadm.item())], want_adm)
+    rounds = retired_total = 0
+    while rounds < 60:
+        act, fr, qh, ln, tk, kv = _host_state(pool, ds)
+        assert np.array_equal(act, hs.active_list()) and np.array_equal(fr, hs.free_list())
+        assert qh == int(hs.q_head[0]) and int(status.item()) == 0
+        assert np.array_equal(ln[act], hlen[act])
+        for s in act:
+            assert np.array_equal(tk[s, :hlen[s]], htok[s, :hlen[s]])
+            assert bytes_equal(kv[:, :, s, :, :hlen[s]], hkv[:, :, s, :, :hlen[s]])
+        if act.size == 0:
+            break
+        B = act.size
+        ids = ds.active[:B]
+        order, uni, wid, nu = sd.group_by_len(pool.len, G, ids=ids)
+        o_order, o_uni, o_wid, _ = oracle.group_by_len(hlen[act], G)
+        rows = act[o_order]
+        assert np.array_equal(order.cpu().numpy(), rows)
+        # gather of the mixed batches
+        rect = sd.SeqBuf.empty(L, B, H, cap, Dh, tdt, groups=len(o_uni))
+        sd.gather(pool, rect, order, G, uni, status=status)
+        want = oracle.gather(hkv, htok, hlen, rows, G, o_uni, cap)
+        gk = to_np_raw(rect.kv)
+        for g in range(len(o_uni)):
+            if o_uni[g]:
+                continue
+            sl, W = slice(g * G, min(B, g * G + G)), int(want["width"][g])
+            assert bytes_equal(gk[:, :, sl, :, :W], want["kv"][:, :, sl, :, :W])
+            assert np.array_equal(rect.tokens.cpu().numpy()[sl, :W], want["tokens"][sl, :W])
+        # verification (or random accepted lengths)
+        draft = rng.integers(3, V, (B, D)).astype(np.int32)
+        if with_verify:
+            logits = rng.standard_normal((B, D + 1, V)).astype(np.float32)
+            hit = rng.random((B, D + 1)) < 0.7
+            for b in range(B):
+                for i in range(D):
+                    if hit[b, i]:
+                        logits[b, i, draft[b, i]] = 9.0
+            logits[rng.random((B, D + 1)) < 0.08, EOS] = 12.0
+            acc, nxt = sd.verify_greedy(torch.from_numpy(logits).cuda(), torch.from_numpy(draft).cuda(), ws=ws,
+                                        status=status)
+            oacc, onxt, _ = oracle.verify_greedy(logits, draft, B, D, V)
+            assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(nxt.cpu().numpy(), onxt)
+        else:
+            oacc = rng.integers(0, D + 1, B).astype(np.int32)
+            draft[rng.random((B, D)) < 0.1] = EOS
+            onxt = rng.integers(3, V, B).astype(np.int32)
+            onxt[rng.random(B) < 0.1] = EOS
+            acc, nxt = torch.from_numpy(oacc).cuda(), torch.from_numpy(onxt).cuda()
+        kvn = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(dt_np)
+        sd.append(pool, from_np_raw(kvn, tdt), torch.from_numpy(draft).cuda(), acc, nxt, rows=order, status=status)
+        oracle.append(hkv, htok, hlen, rows, kvn, draft, oacc, onxt)
+        ret, nret = sd.pool_finish(pool, ds, order, acc, D, EOS, max_len, status=status)
+        want_ret = oracle.pool_finish(htok, hlen, hs, rows, oacc, D, EOS, max_len)
+        assert np.array_equal(ret.cpu().numpy()[:int(nret.item())], want_ret), "round %d retired" % rounds
+        retired_total += want_ret.size
+        adm, nadm = sd.pool_admit(pool, ds, queue, status=status)
+        want_adm = oracle.pool_admit(hkv, htok, hlen, hs, pkv, ptok, plen)
+        assert np.array_equal(adm.cpu().numpy()[:int(nadm.item())], want_adm), "round %d admitted" % rounds
+        rounds += 1
+    say("lifecycle", seed, "rounds", rounds, "retired", retired_total, "queue head", int(hs.q_head[0]))
+    assert retired_total > 0
+
+
+def test_lifecycle_status_bits_change_nothing(sd):
+    say("lifecycle status")
+    rng = np.random.default_rng(1500)
+    slots, cap, L, H, Dh = 6, 16, 1, 1, 8
+    kv = rng.standard_normal((L, 2, slots, H, cap, Dh)).astype(np.float16)
+    tok = rng.integers(3, 50, (slots, cap)).astype(np.int32)
+    ln = np.array([5, 6, 0, 7, 0, 9], np.int32)
+
+    def fresh():
+        pool = sd.SeqBuf(torch.from_numpy(kv).cuda(), torch.from_numpy(tok).cuda(), torch.from_numpy(ln).cuda())
+        return pool, sd.Sched(slots, active=[3, 0, 1, 5])
+
+    def same(pool, ds):
+        torch.cuda.synchronize()
+        assert np.array_equal(pool.len.cpu().numpy(), ln) and np.array_equal(pool.tokens.cpu().numpy(), tok)
+        assert bytes_equal(to_np_raw(pool.kv), kv)
+        assert list(ds.active.cpu().numpy()[:int(ds.n_active.item())]) == [3, 0, 1, 5]
+        assert list(ds.free_slots.cpu().numpy()[:int(ds.n_free.item())]) == [2, 4] and int(ds.q_head.item()) == 0
+
+    def I(*v):
+        return torch.tensor(v, dtype=torch.int32, device="cuda")
+
+    for what, rows, acc, bit in (("not active", I(3, 0, 1, 2), I(0, 0, 0, 0), sd.S_LEN_RANGE),
+                                 ("twice", I(3, 0, 0, 5), I(0, 0, 0, 0), sd.S_ROWS_DUP),
+                                 ("accept range", I(3, 0, 1, 5), I(0, 9, 0, 0), sd.S_LEN_RANGE),
+                                 ("too few rows", I(3, 0, 1), I(0, 0, 0), sd.S_LEN_RANGE)):
+        pool, ds = fresh()
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        sd.pool_finish(pool, ds, rows, acc, 4, EOS, 100, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) & bit, what
+        same(pool, ds)
+    pool, ds = fresh()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qkv = torch.zeros((L, 2, 1, H, 32, Dh), dtype=torch.float16, device="cuda")
+    queue = sd.SeqBuf(qkv, torch.zeros((1, 32), dtype=torch.int32, device="cuda"), I(20))
+    adm, nadm = sd.pool_admit(pool, ds, queue, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & sd.S_CAPACITY and int(nadm.item()) == 0
+    same(pool, ds)
