@@ -8,6 +8,7 @@
 
 #include "launch.h"
 #include "specdec.h"
+#include "verify_finish.h"
 
 #define EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -95,6 +96,7 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
                                                  ws_rowcnt_bytes(B, D));
   p.status = status;
   p.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
+  p.partial = nullptr;
   return launched(sd::launch_verify_greedy(p, as_stream(stream)));
 }
 
@@ -190,10 +192,14 @@ EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_lo
   return launched(sd::launch_verify_sample_logits(s, as_stream(stream)));
 }
 
-EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbuf_t *out,
-                              const int32_t *rows, int B, int group, const int32_t *skip_group, int D,
-                              const void *kv_new, const int32_t *draft, const int32_t *accept_len,
-                              const int32_t *next_token, int32_t pad_token, int32_t *status, void *stream) {
+// Host validation of a realignment call and its launch parameters.  Returns an
+// error code, SPECDEC_OK with `p` filled, or kNothing when B = 0.
+constexpr int kNothing = 1;
+
+static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_seqbuf_t *out, const int32_t *rows,
+                           int B, int group, const int32_t *skip_group, int D, const void *kv_new,
+                           const int32_t *draft, const int32_t *accept_len, const int32_t *next_token,
+                           int32_t pad_token, int32_t *status, sd::RealignParams &p) {
   if (mode != SPECDEC_EQSPEC && mode != SPECDEC_GATHER && mode != SPECDEC_APPEND_INPLACE &&
       mode != SPECDEC_EQSPEC_INPLACE)
     return SPECDEC_E_ARG;
@@ -214,7 +220,6 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
       (1u << 31))
     return SPECDEC_E_ARG;
 
-  sd::RealignParams p;
   memset(&p, 0, sizeof(p));
   p.mode = mode;
   p.kv_in = in->kv;
@@ -244,7 +249,7 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
     if (!in->tokens || !in->width || !out->tokens || !out->pos || !out->mask || !out->width) return SPECDEC_E_ARG;
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-    if (B == 0) return SPECDEC_OK;
+    if (B == 0) return kNothing;
     const size_t kin = kv_bytes(in), kout = kv_bytes(out);
     const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(in->kv, kin, out->kv, kout) || overlap(kv_new, knew, out->kv, kout)) return SPECDEC_E_ALIAS;
@@ -264,7 +269,7 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
     if (!in->tokens || !in->pos || !in->mask || !in->width) return SPECDEC_E_ARG;
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-    if (B == 0) return SPECDEC_OK;
+    if (B == 0) return kNothing;
     const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
     if (overlap(accept_len, B * 4u, in->len, B * 4u) || overlap(next_token, B * 4u, in->tokens, tok_in_bytes) ||
@@ -281,7 +286,7 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
   } else if (mode == SPECDEC_GATHER) {
     if (group < 1) return SPECDEC_E_ARG;
     if (out->rows < B) return SPECDEC_E_ARG;
-    if (B == 0) return SPECDEC_OK;
+    if (B == 0) return kNothing;
     if (overlap(in->kv, kv_bytes(in), out->kv, kv_bytes(out))) return SPECDEC_E_ALIAS;
     if (overlap(in->tokens, tok_in_bytes, out->tokens, tok_out_bytes)) return SPECDEC_E_ALIAS;
     p.tok_in = in->tokens;
@@ -297,7 +302,7 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
       return SPECDEC_E_ARG;
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-    if (B == 0) return SPECDEC_OK;
+    if (B == 0) return kNothing;
     const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
     p.tok_in = in->tokens;
@@ -305,6 +310,17 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
     p.tok_out = out->tokens;
     p.len_out = out->len;
   }
+  return SPECDEC_OK;
+}
+
+EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specdec_seqbuf_t *out,
+                              const int32_t *rows, int B, int group, const int32_t *skip_group, int D,
+                              const void *kv_new, const int32_t *draft, const int32_t *accept_len,
+                              const int32_t *next_token, int32_t pad_token, int32_t *status, void *stream) {
+  sd::RealignParams p;
+  const int rc = realign_prepare(mode, in, out, rows, B, group, skip_group, D, kv_new, draft, accept_len, next_token,
+                                 pad_token, status, p);
+  if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
   return launched(mode == SPECDEC_EQSPEC_INPLACE ? sd::launch_realign_inplace(p, as_stream(stream))
                                                   : sd::launch_realign(p, as_stream(stream)));
 }
@@ -376,21 +392,21 @@ static bool paged_matches(const specdec_paged_t *k, const specdec_seqbuf_t *s) {
   return s->layers == k->layers && s->heads == k->heads && s->head_dim == k->head_dim && s->dtype == k->dtype;
 }
 
-EXPORT int specdec_paged_append(const specdec_paged_t *kv, const int32_t *rows, int B, int D, const void *kv_new,
+static int paged_append_prepare(const specdec_paged_t *kv, const int32_t *rows, int B, int D, const void *kv_new,
                                 const int32_t *draft, const int32_t *accept_len, const int32_t *next_token,
                                 int32_t pad_token, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
-                                int8_t *rect_mask, int rect_cap, int32_t *status, void *stream) {
+                                int8_t *rect_mask, int rect_cap, int32_t *status, sd::PagedParams &p) {
   int rc = check_paged(kv);
   if (rc) return rc;
   if (B < 0 || B > sd::kMaxRealignRows || D < 0 || D > 255) return SPECDEC_E_ARG;
   if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
   if ((rect_tokens || rect_pos || rect_mask) && (!rect_tokens || rect_cap < 1)) return SPECDEC_E_ARG;
   if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-  if (B == 0) return SPECDEC_OK;
+  if (B == 0) return kNothing;
   const size_t knew = (size_t)kv->layers * 2 * B * kv->heads * (size_t)(D + 1) * kv->head_dim * esize(kv->dtype);
   if (knew / 16 >= (1u << 31)) return SPECDEC_E_ARG;  // kv_new units are numbered with 32-bit integers
   if (overlap(kv_new, knew, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
-  sd::PagedParams p = paged_params(sd::kPagedAppend, kv, rows, B, status);
+  p = paged_params(sd::kPagedAppend, kv, rows, B, status);
   p.D = D;
   p.kv_new = kv_new;
   p.draft = draft;
@@ -402,6 +418,17 @@ EXPORT int specdec_paged_append(const specdec_paged_t *kv, const int32_t *rows, 
   p.rect_pos = rect_pos;
   p.rect_mask = rect_mask;
   p.rect_cap = rect_cap;
+  return SPECDEC_OK;
+}
+
+EXPORT int specdec_paged_append(const specdec_paged_t *kv, const int32_t *rows, int B, int D, const void *kv_new,
+                                const int32_t *draft, const int32_t *accept_len, const int32_t *next_token,
+                                int32_t pad_token, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
+                                int8_t *rect_mask, int rect_cap, int32_t *status, void *stream) {
+  sd::PagedParams p;
+  const int rc = paged_append_prepare(kv, rows, B, D, kv_new, draft, accept_len, next_token, pad_token, width,
+                                      rect_tokens, rect_pos, rect_mask, rect_cap, status, p);
+  if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
   return launched(sd::launch_paged(p, as_stream(stream)));
 }
 
@@ -539,4 +566,95 @@ EXPORT int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_
   p.admitted = admitted;
   p.n_admitted = n_admitted;
   return launched(sd::launch_pool_admit(p, as_stream(stream)));
+}
+
+// ------------------------------------------- verification fused into realignment
+
+// Bytes of the per-workgroup keys a fused verification leaves for its consumer.
+static size_t verify_keys_bytes(int B, int D, int V, int dtype) {
+  return ((size_t)B * (size_t)(D + 1) * (size_t)sd::greedy_splits(B, D, V, dtype) * 8 + 255) / 256 * 256;
+}
+
+EXPORT size_t specdec_verify_keys_bytes(int B, int D, int V, int dtype) {
+  if (B < 1 || D < 0 || V < 1 || !dtype_ok(dtype)) return 0;
+  return verify_keys_bytes(B, D, V, dtype);
+}
+
+// The split-vocabulary pass of greedy verification, leaving its keys in ws.
+static int verify_partial_prepare(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                  const int32_t *draft, int32_t *accept_len, int32_t *next_token, void *ws,
+                                  size_t ws_bytes, sd::GreedyParams &g) {
+  if (B < 1 || D < 0 || V < 1 || row_stride < V) return SPECDEC_E_ARG;
+  if (!dtype_ok(dtype)) return SPECDEC_E_DTYPE;
+  if (!logits || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+  if (D + 1 > 256 || (long long)B * (D + 1) > sd::kMaxFinishRows || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  if (!ws || ws_bytes < verify_keys_bytes(B, D, V, dtype) || reinterpret_cast<uintptr_t>(ws) % 8 != 0)
+    return SPECDEC_E_WORKSPACE;
+  memset(&g, 0, sizeof(g));
+  g.logits = logits;
+  g.dtype = dtype;
+  g.row_stride = row_stride;
+  g.B = B;
+  g.D = D;
+  g.V = V;
+  g.draft = draft;
+  g.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
+  g.partial = static_cast<unsigned long long *>(ws);
+  return SPECDEC_OK;
+}
+
+EXPORT int specdec_verify_realign_inplace(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                          const int32_t *draft, const specdec_seqbuf_t *buf, const void *kv_new,
+                                          int32_t pad_token, int32_t *accept_len, int32_t *next_token,
+                                          int32_t *target_tok, void *ws, size_t ws_bytes, int32_t *status,
+                                          void *stream) {
+  if (B == 0) return SPECDEC_OK;
+  sd::GreedyParams g;
+  int rc = verify_partial_prepare(logits, dtype, row_stride, B, D, V, draft, accept_len, next_token, ws, ws_bytes, g);
+  if (rc) return rc;
+  sd::RealignParams p;
+  rc = realign_prepare(SPECDEC_EQSPEC_INPLACE, buf, buf, nullptr, B, 0, nullptr, D, kv_new, draft, accept_len,
+                       next_token, pad_token, status, p);
+  if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
+  const size_t kb = verify_keys_bytes(B, D, V, dtype);
+  if (overlap(ws, kb, buf->kv, kv_bytes(buf)) || (target_tok && overlap(target_tok, (size_t)B * (D + 1) * 4, ws, kb)))
+    return SPECDEC_E_ALIAS;
+  p.vkeys = g.partial;
+  p.vsplits = sd::greedy_splits(B, D, V, dtype);
+  p.V = V;
+  p.vacc = accept_len;
+  p.vnext = next_token;
+  p.vtgt = target_tok;
+  const hipStream_t st = as_stream(stream);
+  const hipError_t e = sd::launch_verify_greedy(g, st);
+  if (e != hipSuccess) return SPECDEC_E_LAUNCH;
+  return launched(sd::launch_realign_inplace(p, st));
+}
+
+EXPORT int specdec_verify_paged_append(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                       const int32_t *draft, const specdec_paged_t *kv, const int32_t *rows,
+                                       const void *kv_new, int32_t pad_token, int32_t *accept_len,
+                                       int32_t *next_token, int32_t *target_tok, int32_t *width,
+                                       int32_t *rect_tokens, int32_t *rect_pos, int8_t *rect_mask, int rect_cap,
+                                       void *ws, size_t ws_bytes, int32_t *status, void *stream) {
+  if (B == 0) return SPECDEC_OK;
+  sd::GreedyParams g;
+  int rc = verify_partial_prepare(logits, dtype, row_stride, B, D, V, draft, accept_len, next_token, ws, ws_bytes, g);
+  if (rc) return rc;
+  sd::PagedParams p;
+  rc = paged_append_prepare(kv, rows, B, D, kv_new, draft, accept_len, next_token, pad_token, width, rect_tokens,
+                            rect_pos, rect_mask, rect_cap, status, p);
+  if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
+  const size_t kb = verify_keys_bytes(B, D, V, dtype);
+  if (overlap(ws, kb, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
+  p.vkeys = g.partial;
+  p.vsplits = sd::greedy_splits(B, D, V, dtype);
+  p.V = V;
+  p.vacc = accept_len;
+  p.vnext = next_token;
+  p.vtgt = target_tok;
+  const hipStream_t st = as_stream(stream);
+  const hipError_t e = sd::launch_verify_greedy(g, st);
+  if (e != hipSuccess) return SPECDEC_E_LAUNCH;
+  return launched(sd::launch_paged(p, st));
 }

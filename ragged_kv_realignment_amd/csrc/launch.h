@@ -19,7 +19,12 @@ struct GreedyParams {
   unsigned int *counters;     // [B] workspace
   int32_t *status;
   bool vec;                   // 16-byte aligned rows: vector loads
+  unsigned long long *partial; // non-null: write each workgroup's key to partial[row * splits + split] and stop
 };
+
+// Greedy verification split into per-workgroup keys (the finish is left to a
+// consumer kernel): the split count launch_verify_greedy uses for these sizes.
+int greedy_splits(int B, int D, int V, int dtype);
 
 struct SampleParams {
   const float *p, *q;
@@ -82,6 +87,11 @@ struct PagedParams {
   int32_t *width_out;          // append: S'
   int32_t *status;
   int kv_wgs;                  // workgroups that copy KV (set by the launcher)
+  // greedy verification finished by the append (see verify_finish.h): the
+  // split-vocabulary keys [B*(D+1)][vsplits], the vocabulary size, the outputs
+  const unsigned long long *vkeys;
+  int vsplits, V;
+  int32_t *vacc, *vnext, *vtgt;
 };
 
 struct GroupParams {

@@ -69,9 +69,11 @@ __device__ __forceinline__ int first_eq(u32x4 r, float M) {
 
 
 // One workgroup scans `chunk` ids of one logit row (row = b*(D+1) + i): every
-// thread issues all its 16-byte loads before consuming any, the workgroup
-// reduces to one (value, id), and thread 0 folds it into the row's 64-bit key
-// with an atomic max.  The atomic's return is consumed before the per-batch-row
+// thread issues all its 16-byte loads before consuming any, forms the 64-bit
+// key of its own (largest value, lowest id holding it), and one block maximum
+// of the keys gives the workgroup's; thread 0 folds it into the row's key with
+// an atomic max.  (With `partial` set, the key is stored per workgroup instead
+// and a consumer kernel finishes.)  The atomic's return is consumed before the per-batch-row
 // counter is incremented, so a workgroup that sees the counter complete also
 // sees every key (both are device-scope atomics, performed at the device's
 // coherence point; the keys are read back with device-scope atomic loads).  The
@@ -118,46 +120,59 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
   } else {
     for (int v = start + threadIdx.x; v < end; v += NT) m = fmaxf(m, load_scalar<DT>(rowp, v));
   }
-  __shared__ float s_f[NT / kWave];
-  __shared__ int s_i[NT / kWave];
+  __shared__ unsigned long long s_k[NT / kWave];
   __shared__ int s_last, s_a, s_bad;
   __shared__ int s_t[NT];
-  const float M = block_max_float<NT>(m, s_f);
 
-  // 2. the lowest id holding M: only threads whose own maximum is M look
+  // 2. this thread's (largest value, lowest id holding it) as one monotone key:
+  //    its vectors are in increasing id order, so the first that holds m wins
   int bi = INT_MAX;
-  if (m == M) {
-    if constexpr (VEC) {
+  if constexpr (VEC) {
 #pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int k = u * NT + (int)threadIdx.x;
-        if (bi == INT_MAX && k < nvec) {
-          const int at = first_eq<DT>(r[u], M);
-          if (at < VW) bi = start + k * VW + at;
-        }
+    for (int u = 0; u < VPT; ++u) {
+      const int k = u * NT + (int)threadIdx.x;
+      if (bi == INT_MAX && k < nvec) {
+        const int at = first_eq<DT>(r[u], m);
+        if (at < VW) bi = start + k * VW + at;
       }
-      if (bi == INT_MAX && tail_id >= 0 && tail_x == M) bi = tail_id;
-    } else {
-      for (int v = start + threadIdx.x; v < end; v += NT)
-        if (load_scalar<DT>(rowp, v) == M) { bi = v; break; }
     }
+    if (bi == INT_MAX && tail_id >= 0 && tail_x == m) bi = tail_id;
+  } else {
+    for (int v = start + threadIdx.x; v < end; v += NT)
+      if (load_scalar<DT>(rowp, v) == m) { bi = v; break; }
   }
-  bi = block_min_int<NT>(bi, s_i);
+  // a thread with no id (past the end) holds the smallest key
+  unsigned long long key = bi == INT_MAX ? 0ull : argmax_key(m, bi);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const unsigned long long o = __shfl_xor(key, off);
+    key = o > key ? o : key;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) s_k[threadIdx.x / kWave] = key;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned long long old = atomicMax(&p.keys[row], argmax_key(M, bi));
-    // opaque zero computed from the atomic's result: the counter update below
-    // cannot issue before the key update has completed
-    uint32_t dep = (uint32_t)old;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(dep));
-    // two-level completion count (splits per row, then D+1 rows per batch row)
-    // keeps the number of atomics on any one address small
-    int last = 0;
-    const unsigned prev = atomicAdd(&p.row_counters[row + (int)dep], 1u);
-    if (prev == (unsigned)(splits - 1)) {
-      store_agent(&p.row_counters[row], 0u);
-      last = atomicAdd(&p.counters[b], 1u) == (unsigned)(D1 - 1);
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) key = s_k[w] > key ? s_k[w] : key;
+    key = s_k[0] > key ? s_k[0] : key;
+    if (p.partial) {
+      p.partial[(size_t)row * splits + split] = key;
+      s_last = 0;
+    } else {
+      const unsigned long long old = atomicMax(&p.keys[row], key);
+      // opaque zero computed from the atomic's result: the counter update below
+      // cannot issue before the key update has completed
+      uint32_t dep = (uint32_t)old;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(dep));
+      // two-level completion count (splits per row, then D+1 rows per batch row)
+      // keeps the number of atomics on any one address small
+      int last = 0;
+      const unsigned prev = atomicAdd(&p.row_counters[row + (int)dep], 1u);
+      if (prev == (unsigned)(splits - 1)) {
+        store_agent(&p.row_counters[row], 0u);
+        last = atomicAdd(&p.counters[b], 1u) == (unsigned)(D1 - 1);
+      }
+      s_last = last;
     }
-    s_last = last;
     s_a = D;
     s_bad = 0;
   }
@@ -194,18 +209,28 @@ int device_cus() {
   return cus;
 }
 
-template <int DT>
-static hipError_t launch_greedy_dt(const GreedyParams &p, hipStream_t s) {
-  constexpr int VW = 16 / Elem<DT>::size;
-  const long rows = (long)p.B * (p.D + 1);
-  const int cus = device_cus();
-  constexpr int step = kBlock * VW;  // ids covered by one vector per thread
-  // Aim at ~8 workgroups per CU; a workgroup covers between one and
-  // SPECDEC_VG_VPT vectors per thread, all loaded before any is consumed.
-  const long want = (8L * cus + rows - 1) / rows;
-  long chunk = (p.V + want - 1) / want;
+// Ids per workgroup: aim at ~8 workgroups per CU; a workgroup covers between
+// one and SPECDEC_VG_VPT vectors per thread, all loaded before any is consumed.
+static long greedy_chunk(int B, int D, int V, int dtype) {
+  const int VW = 16 / (dtype == 0 ? 4 : 2);
+  const long rows = (long)B * (D + 1);
+  const long step = (long)kBlock * VW;  // ids covered by one vector per thread
+  const long want = (8L * device_cus() + rows - 1) / rows;
+  long chunk = (V + want - 1) / want;
   chunk = (chunk + step - 1) / step * step;
   if (chunk > (long)SPECDEC_VG_VPT * step) chunk = (long)SPECDEC_VG_VPT * step;
+  return chunk;
+}
+
+int greedy_splits(int B, int D, int V, int dtype) {
+  const long chunk = greedy_chunk(B, D, V, dtype);
+  return (int)((V + chunk - 1) / chunk);
+}
+
+template <int DT>
+static hipError_t launch_greedy_dt(const GreedyParams &p, hipStream_t s) {
+  const long rows = (long)p.B * (p.D + 1);
+  const long chunk = greedy_chunk(p.B, p.D, p.V, DT);
   const int splits = (int)((p.V + chunk - 1) / chunk);
   const dim3 grid((unsigned)(rows * splits));
   if (p.vec)
