@@ -277,8 +277,10 @@ def _roof(kernel, gbs, bytes_per_launch, us, traffic=None):
 
 def _time_chain(args, cfg, w, mode, K, W, cap):
     """Times K chained rounds (after W untimed ones and a reset of the initial
-    state) with the realignment done in place on one buffer ("inplace") or out
-    of place between two ("eqspec").  Per-launch HIP events on the launch stream."""
+    state) with the realignment done in place on one buffer ("inplace"), out of
+    place between two ("eqspec"), or on a paged cache ("paged", also replayed
+    from a HIP graph).  Per-launch HIP events on the launch stream."""
+    import numpy as np
     import torch
     import synth.device as sdev
     import ragged_kv_realignment_amd as sd
@@ -287,6 +289,7 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
     dev = torch.device("cuda", 0)
     tdt = sdev.TORCH_DT[cfg.kv_dtype]
     bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, tdt) for _ in range(1 if mode != "eqspec" else 2)]
+    kws = sd.keys_workspace(cfg.B, cfg.D, cfg.V, w.logits.dtype, dev) if mode == "paged" else None
     if mode == "paged":
         mb = -(-cap // PAGE)
         cache = sd.PagedKV.empty(cfg.L, cfg.B, cfg.H, cfg.Dh, cfg.B * mb, PAGE, mb, tdt)
@@ -304,6 +307,15 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
         for r in range(n):
             if ev:
                 ev[r][0].record()
+            if mode == "paged":  # verification finished inside the append kernel
+                if ev:
+                    ev[r][1].record()
+                sd.verify_paged_append(w.logits[r], w.drafts[r], cache, w.kv_new[r], ws=kws, accept_len=acc_hist[r],
+                                       next_token=nxt_hist[r], width=width, rect_tokens=view[0], rect_pos=view[1],
+                                       rect_mask=view[2], status=status)
+                if ev:
+                    ev[r][2].record()
+                continue
             sd.verify_greedy(w.logits[r], w.drafts[r], ws=ws, status=status, accept_len=acc_hist[r],
                              next_token=nxt_hist[r])
             if ev:
@@ -311,9 +323,6 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
             if mode == "inplace":
                 sd.realign_eqspec_inplace(bufs[0], w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r],
                                           status=status)
-            elif mode == "paged":
-                sd.paged_append(cache, w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], width=width,
-                                rect_tokens=view[0], rect_pos=view[1], rect_mask=view[2], status=status)
             else:
                 sd.realign_eqspec(bufs[r % 2], bufs[(r + 1) % 2], w.kv_new[r], w.drafts[r], acc_hist[r],
                                   nxt_hist[r], status=status)
@@ -342,6 +351,24 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
         raise RuntimeError("device status %d during the timed rounds (%s)" % (int(status.item()), mode))
     out = {"total_ms": total_ms, "ver_ms": _ms(ev, 0, 1), "re_ms": _ms(ev, 1, 2), "acc": acc_hist[:K].cpu().numpy()}
     if mode == "paged":
+        # the same K rounds captured once in a HIP graph and replayed from the
+        # initial state: no host work per round; the replay must reproduce the
+        # eager rounds exactly
+        want_len, want_tok = cache.len.clone(), cache.tokens.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(K)
+        reset()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        if not (np.array_equal(acc_hist[:K].cpu().numpy(), out["acc"]) and torch.equal(cache.len, want_len) and
+                torch.equal(cache.tokens, want_tok)):
+            raise RuntimeError("the graph replay differs from the eager rounds")
+        out["graph_ms"] = g0.elapsed_time(g1)
+        del g
         del cache
     del bufs
     torch.cuda.empty_cache()
@@ -373,7 +400,8 @@ def bench_chain(args, cfg):
         if mode == "paged":
             pb = round_bytes_paged(cfg, w.lens0, r["acc"], PAGE)
             gbs = pb.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
-            return _roof("k_paged_append", gbs, float(pb.mean()), float(r["re_ms"].mean() * 1e3))
+            return _roof("k_verify_greedy (keys only) + k_paged_append", gbs, float(pb.mean()),
+                         float(r["re_ms"].mean() * 1e3))
         fn = round_bytes_inplace if mode == "inplace" else (lambda *a: round_bytes(*a)[1])
         rbytes = fn(cfg, w.lens0, w.width0, r["acc"])
         gbs = rbytes.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
@@ -403,11 +431,15 @@ def bench_chain(args, cfg):
         pb = round_bytes_paged(cfg, w.lens0, o["acc"], PAGE)
         gbs = pb.sum() / (o["re_ms"].sum() * 1e-3) / 1e9
         extra["paged"] = {"value": K / (o["total_ms"] * 1e-3), "unit": "rounds/s", "ms_per_step": o["total_ms"] / K,
+                          "graph": {"value": K / (o["graph_ms"] * 1e-3), "unit": "rounds/s",
+                                    "ms_per_step": o["graph_ms"] / K,
+                                    "how": "the same %d rounds captured in one HIP graph, replayed once" % K},
                           "page_positions": PAGE,
-                          "realign": {"kernels": "k_paged_append", "achieved_gbs": gbs,
-                                      "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": float(pb.mean()),
-                                      "avg_call_us": float(o["re_ms"].mean() * 1e3)},
-                          "realign_share_of_round": float(o["re_ms"].sum() / o["total_ms"])}
+                          "call": "specdec_verify_paged_append (greedy verification finished inside the append)",
+                          "realign": {"kernels": "k_verify_greedy (keys only) + k_paged_append",
+                                      "achieved_gbs": gbs, "frac": gbs / PEAK_HBM_GBS,
+                                      "algorithmic_bytes_per_call": float(pb.mean()),
+                                      "avg_call_us": float(o["re_ms"].mean() * 1e3)}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, w.plans, w.lens0, w.width0, w.tok0, w.mask0, min(args.cpu_rounds, R),
@@ -425,7 +457,7 @@ def bench_chain(args, cfg):
     }
     metric = METRIC if cfg.name == "8b-gqa" else METRIC.replace("at B=16", "at B=%d (%s)" % (cfg.B, cfg.name))
     headroof = roof(modes[0])
-    if modes[0] != "paged":  # a copy-shaped kernel: its rate against the measured streaming rate
+    if modes[0] in ("inplace", "eqspec"):  # a copy-shaped kernel: its rate against the measured streaming rate
         headroof["frac_of_practical"] = headroof["achieved"] / ceiling["read_write_gbs"]
     return _line(metric, K / (head["total_ms"] * 1e-3), K, W, head["total_ms"] / K, synth.DTYPE_NAME[cfg.kv_dtype],
                  config, headroof, cpu, extra)

@@ -276,42 +276,6 @@ int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, i
 int specdec_group_by_len_ids(const int32_t *len, const int32_t *ids, int N, int group, int32_t *order,
                              int32_t *uniform, int32_t *width, int32_t *n_uniform, void *stream);
 
-/* --------------------------- verification fused into realignment */
-
-/* Greedy verification and a realignment in one call: the split-vocabulary pass
- * of specdec_verify_greedy leaves one 64-bit key per (row, split) workgroup in
- * `ws`, and the realignment kernel finishes verification itself (every
- * workgroup reduces the keys; one writes accept_len, next_token and target_tok),
- * so no device-wide completion runs between the two.  Results are identical to
- * specdec_verify_greedy followed by the realignment.
- * Bytes of `ws` for B rows, D drafts, V logits of type dtype (0 for bad sizes);
- * the value depends on the current device's compute-unit count. */
-size_t specdec_verify_keys_bytes(int B, int D, int V, int dtype);
-
-/* specdec_verify_greedy (logits, dtype, row_stride, B, D, V, draft; outputs
- * accept_len, next_token, target_tok as there) followed by
- * specdec_realign_kv(SPECDEC_EQSPEC_INPLACE) of rectangle `buf` with kv_new and
- * pad_token.  ws: device, at least specdec_verify_keys_bytes(B, D, V, dtype)
- * bytes, 8-byte aligned, scratch only.  Limits: B * (D+1) <= 2048, D + 1 <= 256,
- * and those of both calls.  Device conditions and errors: those of both calls.
- * A realignment condition (capacity, lengths) leaves the rectangle untouched;
- * the verification outputs are written regardless. */
-int specdec_verify_realign_inplace(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
-                                   const int32_t *draft, const specdec_seqbuf_t *buf, const void *kv_new,
-                                   int32_t pad_token, int32_t *accept_len, int32_t *next_token, int32_t *target_tok,
-                                   void *ws, size_t ws_bytes, int32_t *status, void *stream);
-
-/* specdec_verify_greedy followed by specdec_paged_append (arguments as there;
- * the append's accepted lengths and next tokens are the verification's).
- * ws as for specdec_verify_realign_inplace.  Limits: B * (D+1) <= 2048 and
- * those of both calls. */
-int specdec_verify_paged_append(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
-                                const int32_t *draft, const specdec_paged_t *kv, const int32_t *rows,
-                                const void *kv_new, int32_t pad_token, int32_t *accept_len, int32_t *next_token,
-                                int32_t *target_tok, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
-                                int8_t *rect_mask, int rect_cap, void *ws, size_t ws_bytes, int32_t *status,
-                                void *stream);
-
 /* --------------------------------------------------------- pool lifecycle */
 
 /* Scheduling state of a pool of sequences ("Batch Speculative Decoding Done
@@ -460,6 +424,32 @@ int specdec_paged_admit(const specdec_paged_t *kv, const int32_t *rows, int B, c
  * stack holds, set SPECDEC_S_LEN_RANGE; duplicate rows SPECDEC_S_ROWS_DUP
  * (nothing written either way).  Errors: E_ARG, E_LAUNCH. */
 int specdec_paged_retire(const specdec_paged_t *kv, const int32_t *rows, int B, int32_t *status, void *stream);
+
+/* ------------------------------ verification fused into the paged append */
+
+/* Greedy verification and the paged append in one call: the split-vocabulary
+ * pass of specdec_verify_greedy leaves one 64-bit key per (row, split)
+ * workgroup in `ws`, and the append kernel finishes verification itself (every
+ * workgroup reduces the keys; one writes accept_len, next_token and target_tok),
+ * so no device-wide completion runs between the two.  Results are identical to
+ * specdec_verify_greedy followed by specdec_paged_append.
+ * Bytes of `ws` for B rows, D drafts, V logits of type dtype (0 for bad sizes);
+ * the value depends on the current device's compute-unit count. */
+size_t specdec_verify_keys_bytes(int B, int D, int V, int dtype);
+
+/* specdec_verify_greedy (logits, dtype, row_stride, B, D, V, draft; outputs
+ * accept_len, next_token, target_tok as there) followed by specdec_paged_append
+ * (the other arguments as there; its accepted lengths and next tokens are the
+ * verification's).  ws: device, at least specdec_verify_keys_bytes(B, D, V,
+ * dtype) bytes, 8-byte aligned, scratch only.  Limits: B * (D+1) <= 2048,
+ * D + 1 <= 256, and those of both calls.  A condition of the append leaves the
+ * cache untouched; the verification outputs are written regardless. */
+int specdec_verify_paged_append(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                const int32_t *draft, const specdec_paged_t *kv, const int32_t *rows,
+                                const void *kv_new, int32_t pad_token, int32_t *accept_len, int32_t *next_token,
+                                int32_t *target_tok, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
+                                int8_t *rect_mask, int rect_cap, void *ws, size_t ws_bytes, int32_t *status,
+                                void *stream);
 
 #ifdef __cplusplus
 }

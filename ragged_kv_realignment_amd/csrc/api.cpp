@@ -603,34 +603,6 @@ static int verify_partial_prepare(const void *logits, int dtype, int64_t row_str
   return SPECDEC_OK;
 }
 
-EXPORT int specdec_verify_realign_inplace(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
-                                          const int32_t *draft, const specdec_seqbuf_t *buf, const void *kv_new,
-                                          int32_t pad_token, int32_t *accept_len, int32_t *next_token,
-                                          int32_t *target_tok, void *ws, size_t ws_bytes, int32_t *status,
-                                          void *stream) {
-  if (B == 0) return SPECDEC_OK;
-  sd::GreedyParams g;
-  int rc = verify_partial_prepare(logits, dtype, row_stride, B, D, V, draft, accept_len, next_token, ws, ws_bytes, g);
-  if (rc) return rc;
-  sd::RealignParams p;
-  rc = realign_prepare(SPECDEC_EQSPEC_INPLACE, buf, buf, nullptr, B, 0, nullptr, D, kv_new, draft, accept_len,
-                       next_token, pad_token, status, p);
-  if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
-  const size_t kb = verify_keys_bytes(B, D, V, dtype);
-  if (overlap(ws, kb, buf->kv, kv_bytes(buf)) || (target_tok && overlap(target_tok, (size_t)B * (D + 1) * 4, ws, kb)))
-    return SPECDEC_E_ALIAS;
-  p.vkeys = g.partial;
-  p.vsplits = sd::greedy_splits(B, D, V, dtype);
-  p.V = V;
-  p.vacc = accept_len;
-  p.vnext = next_token;
-  p.vtgt = target_tok;
-  const hipStream_t st = as_stream(stream);
-  const hipError_t e = sd::launch_verify_greedy(g, st);
-  if (e != hipSuccess) return SPECDEC_E_LAUNCH;
-  return launched(sd::launch_realign_inplace(p, st));
-}
-
 EXPORT int specdec_verify_paged_append(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
                                        const int32_t *draft, const specdec_paged_t *kv, const int32_t *rows,
                                        const void *kv_new, int32_t pad_token, int32_t *accept_len,

@@ -8,7 +8,6 @@
 #include "device_common.h"
 #include "realign_params.h"
 #include "specdec.h"
-#include "verify_finish.h"
 
 namespace sd {
 
@@ -60,25 +59,16 @@ __device__ __forceinline__ void ip_step(int k, int nch, int first, int step, int
   ip_store(k < nch ? rd : r0, (first + k * step) * kIpChunk + t, cur);
 }
 
-// FUSED: greedy verification is finished here from the split-vocabulary keys
-// (every workgroup reduces them; workgroup 0 writes the verification outputs).
-template <bool FUSED>
 __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
   __shared__ int s_c[kMaxRealignRows];
   __shared__ int s_n[kMaxRealignRows];
   __shared__ int s_red[kIpWaves];
   __shared__ int s_red2[kIpWaves];
-  __shared__ unsigned long long s_vkey[FUSED ? kMaxFinishRows : 1];
-  __shared__ int s_acc[FUSED ? kMaxRealignRows : 1], s_nxt[FUSED ? kMaxRealignRows : 1];
   const int B = p.B, D = p.D, U = p.units, H = p.heads;
-  if constexpr (FUSED) {
-    const int dbad = verify_finish<kIpBlock>(p.vkeys, p.vsplits, B, D, p.draft, p.V, s_vkey, s_acc, s_nxt, s_red);
-    if (blockIdx.x == 0) verify_outputs<kIpBlock>(B, D, s_vkey, s_acc, s_nxt, dbad, p.vacc, p.vnext, p.vtgt, p.status);
-  }
   const int S = p.width_in[0];
   int mx = 0, bad = (S < 0 || S > p.cap_in) ? SPECDEC_S_LEN_RANGE : 0;
   for (int b = threadIdx.x; b < B; b += kIpBlock) {
-    const int c = p.len_in[b], a = FUSED ? s_acc[b] : p.accept_len[b];
+    const int c = p.len_in[b], a = p.accept_len[b];
     if (c < 0 || c > S || a < 0 || a > D) bad = SPECDEC_S_LEN_RANGE;
     s_c[b] = c;
     s_n[b] = a + 1;
@@ -193,7 +183,7 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
       for (int j = t; j < Snew; j += kIpBlock) {
         const int cj = j - pout;
         if (cj < 0) tok[j] = p.pad_token;
-        else if (cj >= c) tok[j] = (cj - c < a) ? p.draft[(size_t)b * D + (cj - c)] : (FUSED ? s_nxt[b] : p.next_token[b]);
+        else if (cj >= c) tok[j] = (cj - c < a) ? p.draft[(size_t)b * D + (cj - c)] : p.next_token[b];
         p.pos_out[(size_t)b * p.cap_in + j] = cj < 0 ? 0 : cj;
         p.mask_out[(size_t)b * p.cap_in + j] = (int8_t)(cj >= 0);
       }
@@ -202,8 +192,7 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
 }
 
 // Lengths and width of the in-place realignment, after k_realign_inplace (which
-// reads them in every workgroup).  With a fused verification, accept_len is the
-// output k_realign_inplace's workgroup 0 wrote.
+// reads them in every workgroup).
 __global__ __launch_bounds__(kIpBlock) void k_inplace_meta(RealignParams p) {
   const int B = p.B, D = p.D;
   const int S = p.width_in[0];
@@ -229,12 +218,7 @@ __global__ __launch_bounds__(kIpBlock) void k_inplace_meta(RealignParams p) {
 hipError_t launch_realign_inplace(const RealignParams &p, hipStream_t s) {
   // one workgroup per sequence and per row
   const long g = (long)p.layers * 2 * p.B * p.heads + p.B;
-  if (p.vkeys)
-    hipLaunchKernelGGL(k_realign_inplace<true>, dim3((unsigned)(g < (1L << 30) ? g : (1L << 30))), dim3(kIpBlock), 0,
-                       s, p);
-  else
-    hipLaunchKernelGGL(k_realign_inplace<false>, dim3((unsigned)(g < (1L << 30) ? g : (1L << 30))), dim3(kIpBlock), 0,
-                       s, p);
+  hipLaunchKernelGGL(k_realign_inplace, dim3((unsigned)(g < (1L << 30) ? g : (1L << 30))), dim3(kIpBlock), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_inplace_meta, dim3(1), dim3(kIpBlock), 0, s, p);

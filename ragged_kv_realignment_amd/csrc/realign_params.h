@@ -27,12 +27,6 @@ struct RealignParams {
   const int32_t *draft, *accept_len, *next_token;
   int32_t pad_token;
   int32_t *status;
-  // greedy verification finished by this kernel (EQSPEC in place only): the
-  // split-vocabulary pass's keys [B*(D+1)][vsplits], the vocabulary size, and
-  // the verification outputs (accept_len above then names vacc, written here)
-  const unsigned long long *vkeys;
-  int vsplits, V;
-  int32_t *vacc, *vnext, *vtgt;
 };
 
 int device_cus();

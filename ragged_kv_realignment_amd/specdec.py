@@ -26,8 +26,7 @@ EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init
            "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
            "specdec_realign_kv", "specdec_group_by_len", "specdec_paged_append", "specdec_paged_gather",
            "specdec_paged_admit", "specdec_paged_retire", "specdec_group_by_len_ids", "specdec_pool_finish",
-           "specdec_pool_admit", "specdec_verify_keys_bytes", "specdec_verify_realign_inplace",
-           "specdec_verify_paged_append")
+           "specdec_pool_admit", "specdec_verify_keys_bytes", "specdec_verify_paged_append")
 
 
 class SpecDecError(RuntimeError):
@@ -77,15 +76,13 @@ def lib():
         L.specdec_pool_admit.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), C.POINTER(SeqBufC), vp, vp, vp, vp]
         L.specdec_verify_keys_bytes.argtypes = [ci, ci, ci, ci]
         L.specdec_verify_keys_bytes.restype = sz
-        L.specdec_verify_realign_inplace.argtypes = [vp, ci, C.c_int64, ci, ci, ci, vp, C.POINTER(SeqBufC), vp,
-                                                     C.c_int32, vp, vp, vp, vp, sz, vp, vp]
         L.specdec_verify_paged_append.argtypes = [vp, ci, C.c_int64, ci, ci, ci, vp, C.POINTER(PagedC), vp, vp,
                                                   C.c_int32, vp, vp, vp, vp, vp, vp, vp, ci, vp, sz, vp, vp]
         for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample",
                   "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len",
                   "specdec_paged_append", "specdec_paged_gather", "specdec_paged_admit", "specdec_paged_retire",
                   "specdec_group_by_len_ids", "specdec_pool_finish", "specdec_pool_admit",
-                  "specdec_verify_realign_inplace", "specdec_verify_paged_append"):
+                  "specdec_verify_paged_append"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -557,24 +554,6 @@ def _greedy_args(logits, draft):
     if tuple(draft.shape) != (B, D1 - 1):
         raise ValueError("draft must be [B, D]")
     return B, D1 - 1, V
-
-
-def verify_realign_inplace(logits, draft, buf, kv_new, ws=None, accept_len=None, next_token=None, target_tok=None,
-                           pad_token=0, status=None):
-    """Greedy verification and the in-place EQSPEC realignment of `buf` in one call.
-    Returns (accept_len, next_token)."""
-    B, D, V = _greedy_args(logits, draft)
-    _need(kv_new, "kv_new", buf.kv.dtype)
-    dev = logits.device
-    ws = keys_workspace(B, D, V, logits.dtype, dev) if ws is None else ws
-    accept_len = _i32(B, dev) if accept_len is None else accept_len
-    next_token = _i32(B, dev) if next_token is None else next_token
-    rc = lib().specdec_verify_realign_inplace(logits.data_ptr(), _TORCH_DT[logits.dtype], V, B, D, V, _ptr(draft),
-                                              C.byref(buf.c), kv_new.data_ptr(), pad_token, accept_len.data_ptr(),
-                                              next_token.data_ptr(), _ptr(target_tok), ws.data_ptr(), ws.numel(),
-                                              _ptr(status), _stream())
-    _check(rc, "specdec_verify_realign_inplace")
-    return accept_len, next_token
 
 
 def verify_paged_append(logits, draft, cache, kv_new, ws=None, rows=None, accept_len=None, next_token=None,

@@ -1,16 +1,13 @@
-"""GPU parity of greedy verification fused into realignment: one call that
-leaves per-workgroup keys and lets the realignment kernel finish verification
-gives, byte for byte, what specdec_verify_greedy followed by the in-place EQSPEC
-realignment (or the paged append) gives, on random inputs with ties, drafts out
-of range and zero-length rows, and over chained rounds of the 8b-gqa workload
-(whose separate calls are checked against the oracle elsewhere)."""
+"""GPU parity of greedy verification fused into the paged append: one call that
+leaves per-workgroup keys and lets the append kernel finish verification gives,
+byte for byte, what specdec_verify_greedy followed by specdec_paged_append
+gives (those separate calls are checked against the oracle elsewhere), on
+random inputs with ties, drafts out of range, zero-length rows and D = 0."""
 import numpy as np
 import pytest
 import torch
 
-import synth
-import synth.device as sdev
-from tests.gpu_util import bytes_equal, from_np_raw, say, to_np_raw
+from tests.gpu_util import bytes_equal, say, to_np_raw
 
 pytestmark = pytest.mark.gpu
 
@@ -50,42 +47,6 @@ def _logits(rng, B, D, V, ldt, draft_bad=False):
     if draft_bad and D > 0:
         draft[0, -1] = V + 3
     return torch.from_numpy(logits).to("cuda", ldt), torch.from_numpy(draft).cuda()
-
-
-def _same(a, b, what):
-    torch.cuda.synchronize()
-    for k in ("tokens", "pos", "mask", "len", "width"):
-        assert torch.equal(getattr(a, k), getattr(b, k)), (what, k)
-    assert bytes_equal(to_np_raw(a.kv), to_np_raw(b.kv)), (what, "kv")
-
-
-@pytest.mark.parametrize("seed", range(8))
-def test_fused_inplace_random(sd, seed):
-    rng = np.random.default_rng(1600 + seed)
-    ldt = [torch.float32, torch.float16, torch.bfloat16][seed % 3]
-    tdt = [torch.float16, torch.float32][seed % 2]
-    B = int(rng.integers(1, 40))
-    D = int(rng.integers(0, 8)) if seed % 4 else 0
-    V = int([rng.integers(2, 300), rng.integers(3000, 40000)][seed % 2])
-    L, H, Dh = int(rng.integers(1, 3)), int(rng.integers(1, 3)), 64 if tdt == torch.float16 else 4
-    lens = rng.integers(0, 300, B).astype(np.int32)
-    S = int(lens.max()) + int(rng.integers(0, 20))
-    cap = S + D + 1
-    say("fused inplace", seed, B, D, V, ldt, tdt)
-    a, b = _rect(sd, rng, B, L, H, Dh, tdt, lens, S, cap)
-    logits, draft = _logits(rng, B, D, V, ldt, draft_bad=seed % 3 == 1)
-    kv_new = torch.from_numpy(rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(np.float32)).to("cuda", tdt)
-    st1 = torch.zeros(1, dtype=torch.int32, device="cuda")
-    st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
-    t1 = torch.full((B, D + 1), -1, dtype=torch.int32, device="cuda")
-    t2 = torch.full((B, D + 1), -1, dtype=torch.int32, device="cuda")
-    acc1, nxt1 = sd.verify_greedy(logits, draft, target_tok=t1, status=st1)
-    sd.realign_eqspec_inplace(a, kv_new, draft, acc1, nxt1, pad_token=seed % 3, status=st1)
-    acc2, nxt2 = sd.verify_realign_inplace(logits, draft, b, kv_new, target_tok=t2, pad_token=seed % 3, status=st2)
-    torch.cuda.synchronize()
-    assert torch.equal(acc1, acc2) and torch.equal(nxt1, nxt2) and torch.equal(t1, t2)
-    assert int(st1.item()) == int(st2.item())
-    _same(a, b, "inplace")
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -128,42 +89,19 @@ def test_fused_paged_random(sd, seed):
         assert bytes_equal(to_np_raw(ca.pages), to_np_raw(cb.pages)), r
 
 
-def test_fused_chain_8b_gqa(sd):
-    """Eight chained rounds of the 8b-gqa workload: fused calls against separate
-    ones on two copies of the rectangle."""
-    cfg = synth.CONFIGS["8b-gqa"]
-    rounds = 8
-    say("fused chain 8b-gqa")
-    tdt = sdev.TORCH_DT[cfg.kv_dtype]
-    w = sdev.GreedyRounds(cfg, rounds)
-    a = sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cfg.cap, cfg.Dh, tdt)
-    b = sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cfg.cap, cfg.Dh, tdt)
-    w.load_initial(a)
-    w.load_initial(b)
-    ws = sd.keys_workspace(cfg.B, cfg.D, cfg.V, w.logits.dtype)
-    status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    for r in range(rounds):
-        acc1, nxt1 = sd.verify_greedy(w.logits[r], w.drafts[r], status=status)
-        sd.realign_eqspec_inplace(a, w.kv_new[r], w.drafts[r], acc1, nxt1, status=status)
-        acc2, nxt2 = sd.verify_realign_inplace(w.logits[r], w.drafts[r], b, w.kv_new[r], ws=ws, status=status)
-        torch.cuda.synchronize()
-        assert torch.equal(acc1, acc2) and torch.equal(nxt1, nxt2), r
-    assert int(status.item()) == 0
-    _same(a, b, "8b chain")
-
-
 def test_fused_host_errors(sd):
     say("fused host errors")
     B, D, V = 3, 2, 100
-    buf = sd.SeqBuf.empty(1, B, 1, 16, 8, torch.float16)
     logits = torch.zeros((B, D + 1, V), device="cuda")
     draft = torch.zeros((B, D), dtype=torch.int32, device="cuda")
     kv_new = torch.zeros((1, 2, B, 1, D + 1, 8), dtype=torch.float16, device="cuda")
+    cache = sd.PagedKV.empty(1, B, 1, 8, 16, 4, 4, torch.float16)
     with pytest.raises(sd.SpecDecError) as e:  # workspace too small
-        sd.verify_realign_inplace(logits, draft, buf, kv_new, ws=torch.empty(8, dtype=torch.uint8, device="cuda"))
+        sd.verify_paged_append(logits, draft, cache, kv_new, ws=torch.empty(8, dtype=torch.uint8, device="cuda"))
     assert e.value.code == -3
     big = torch.zeros((700, 4, 10), device="cuda")  # B * (D+1) above 2048
-    with pytest.raises((sd.SpecDecError, ValueError)):
-        sd.verify_realign_inplace(big, torch.zeros((700, 3), dtype=torch.int32, device="cuda"),
-                                  sd.SeqBuf.empty(1, 700, 1, 16, 8, torch.float16),
-                                  torch.zeros((1, 2, 700, 1, 4, 8), dtype=torch.float16, device="cuda"))
+    with pytest.raises(sd.SpecDecError) as e:
+        sd.verify_paged_append(big, torch.zeros((700, 3), dtype=torch.int32, device="cuda"),
+                               sd.PagedKV.empty(1, 700, 1, 8, 2800, 4, 4, torch.float16),
+                               torch.zeros((1, 2, 700, 1, 4, 8), dtype=torch.float16, device="cuda"))
+    assert e.value.code == -1

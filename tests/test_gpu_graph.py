@@ -1,0 +1,99 @@
+"""Chained rounds of the fused greedy verification + paged append captured in a
+HIP graph: every replay, with the program's own eager work (a reset of the
+cache) and synchronisations between replays, reproduces the eager rounds byte
+for byte (accepted lengths, next tokens, pages, block table, free stack,
+token ids, lengths and the rectangle view)."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import bytes_equal, say, to_np_raw
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_kv_realignment_amd as m
+    return m
+
+
+def test_paged_rounds_graph_replays(sd):
+    rng = np.random.default_rng(1800)
+    B, D, V, L, H, Dh, page, R = 12, 4, 5000, 2, 2, 64, 8, 10
+    lens = rng.integers(20, 300, B).astype(np.int32)
+    S = int(lens.max())
+    cap = S + R * (D + 1)
+    mb = -(-cap // page)
+    say("graph replay", B, D, V, R)
+    kv = np.zeros((L, 2, B, H, cap, Dh), np.float16)
+    tok = np.zeros((B, cap), np.int32)
+    for b in range(B):
+        kv[:, :, b, :, S - lens[b]:S] = rng.standard_normal((L, 2, H, lens[b], Dh))
+        tok[b, S - lens[b]:S] = rng.integers(1, V, lens[b])
+    rect = sd.SeqBuf(torch.from_numpy(kv).cuda(), torch.from_numpy(tok).cuda(), torch.from_numpy(lens).cuda(),
+                     torch.zeros((B, cap), dtype=torch.int32, device="cuda"),
+                     torch.zeros((B, cap), dtype=torch.int8, device="cuda"),
+                     torch.tensor([S], dtype=torch.int32, device="cuda"))
+    cache = sd.PagedKV.empty(L, B, H, Dh, B * mb, page, mb, torch.float16)
+    logits = torch.from_numpy(rng.standard_normal((R, B, D + 1, V)).astype(np.float32)).cuda()
+    drafts = rng.integers(0, V, (R, B, D)).astype(np.int32)
+    am = logits.argmax(-1).cpu().numpy()
+    for r in range(R):
+        for b in range(B):
+            k = int(rng.integers(0, D + 1))
+            drafts[r, b, :k] = am[r, b, :k]
+    drafts = torch.from_numpy(drafts).cuda()
+    kv_new = torch.from_numpy(rng.standard_normal((R, L, 2, B, H, D + 1, Dh)).astype(np.float16)).cuda()
+    ws = sd.keys_workspace(B, D, V, logits.dtype)
+    acc = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    nxt = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    width = torch.zeros(1, dtype=torch.int32, device="cuda")
+    view = (torch.zeros((B, cap), dtype=torch.int32, device="cuda"),
+            torch.zeros((B, cap), dtype=torch.int32, device="cuda"),
+            torch.zeros((B, cap), dtype=torch.int8, device="cuda"))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    sd.paged_admit(cache, rect, status=status)
+    torch.cuda.synchronize()
+    names = ("pages", "block_table", "free_pages", "n_free", "tokens", "len", "sync")
+    initial = {k: getattr(cache, k).clone() for k in names}
+
+    def reset():  # eager work between replays: the cache back to its state after the admission
+        for k in names:
+            getattr(cache, k).copy_(initial[k])
+        torch.cuda.synchronize()
+
+    def rounds():
+        for r in range(R):
+            sd.verify_paged_append(logits[r], drafts[r], cache, kv_new[r], ws=ws, accept_len=acc[r],
+                                   next_token=nxt[r], width=width, rect_tokens=view[0], rect_pos=view[1],
+                                   rect_mask=view[2], status=status)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return ([t.clone() for t in (acc, nxt, width, *view, cache.block_table, cache.n_free, cache.tokens,
+                                      cache.len)], to_np_raw(cache.pages), cache.free_pages[:int(cache.n_free.item())]
+                .clone())
+
+    reset()
+    rounds()
+    want = snapshot()
+    assert int(status.item()) == 0
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rounds()
+    for rep in range(3):
+        reset()
+        acc.zero_()
+        nxt.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for i, (x, y) in enumerate(zip(got[0], want[0])):
+            assert torch.equal(x, y), (rep, i)
+        assert bytes_equal(got[1], want[1]), rep
+        assert torch.equal(got[2], want[2]), rep
+    assert int(status.item()) == 0
