@@ -287,3 +287,44 @@ def test_paged_host_errors(sd):
     with pytest.raises(sd.SpecDecError) as e:  # a rectangle of another head count
         sd.paged_gather(cache, sd.SeqBuf.empty(1, 2, 2, 8, 8, torch.float16))
     assert e.value.code == -1
+
+
+def test_paged_largest_batch(sd):
+    """B = 1024 batch entries (the limit) over a pool of 1100 rows with pages of
+    4 positions: two rounds of append, then gather, against the oracle."""
+    rng = np.random.default_rng(1210)
+    rows, B, D, L, H, Dh, page = 1100, 1024, 3, 1, 1, 8, 4
+    maxlen = 30
+    cap = maxlen + 2 * (D + 1)
+    mb = -(-cap // page)
+    n_pages = rows * mb
+    say("paged largest batch", rows, B)
+    st = oracle.PagedState(L, H, Dh, n_pages, page, mb, rows, np.float16,
+                           free_order=rng.permutation(n_pages).astype(np.int32))
+    cache = _dev_state(sd, st, torch.float16)
+    prow = rng.permutation(rows)[:B].astype(np.int32)
+    lens = rng.integers(0, maxlen, B).astype(np.int32)
+    S = int(lens.max())
+    kv, tok = _rect(rng, B, L, H, Dh, np.float16, lens, S, cap)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    prow_d = torch.from_numpy(prow).cuda()
+    sd.paged_admit(cache, _seqbuf(sd, kv, tok, lens, S, torch.float16), rows=prow_d, status=status)
+    oracle.paged_admit(st, kv, tok, lens, S, rows=prow)
+    for r in range(2):
+        kv_new = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(np.float16)
+        acc = rng.integers(0, D + 1, B).astype(np.int32)
+        draft = rng.integers(1, 500, (B, D)).astype(np.int32)
+        nxt = rng.integers(1, 500, B).astype(np.int32)
+        rt = torch.full((B, cap), -7, dtype=torch.int32, device="cuda")
+        sd.paged_append(cache, torch.from_numpy(kv_new).cuda(), torch.from_numpy(draft).cuda(),
+                        torch.from_numpy(acc).cuda(), torch.from_numpy(nxt).cuda(), rows=prow_d, rect_tokens=rt,
+                        status=status)
+        view = oracle.paged_append(st, kv_new, draft, acc, nxt, rows=prow, rect_cap=cap)
+        _same_state(cache, st, "largest batch round %d" % r)
+        assert np.array_equal(rt.cpu().numpy()[:, :view["width"]], view["tokens"])
+    out = sd.SeqBuf.empty(L, B, H, cap, Dh, torch.float16)
+    sd.paged_gather(cache, out, rows=prow_d, status=status)
+    want = oracle.paged_gather(st, rows=prow, cap_out=cap)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert bytes_equal(to_np_raw(out.kv)[..., :want["width"], :], want["kv"])

@@ -191,3 +191,56 @@ def test_lifecycle_status_bits_change_nothing(sd):
     torch.cuda.synchronize()
     assert int(status.item()) & sd.S_CAPACITY and int(nadm.item()) == 0
     same(pool, ds)
+
+
+def test_lifecycle_largest_pool(sd):
+    """4096 pool rows (the limit), 3000 of them active in a shuffled schedule
+    order: one round of append, finish and admit against the oracle."""
+    rng = np.random.default_rng(1510)
+    slots, D, L, H, Dh, max_len, G = 4096, 3, 1, 1, 4, 40, 8
+    cap = max_len + D + 1
+    say("lifecycle largest pool", slots)
+    act = rng.permutation(slots)[:3000].astype(np.int32)
+    ln = np.zeros(slots, np.int32)
+    ln[act] = rng.integers(1, max_len, act.size)
+    tok = rng.integers(3, 99, (slots, cap)).astype(np.int32)
+    kv = rng.standard_normal((L, 2, slots, H, cap, Dh)).astype(np.float32)
+    Q, pcap = 1500, max_len
+    plen = rng.integers(1, max_len, Q).astype(np.int32)
+    pkv = rng.standard_normal((L, 2, Q, H, pcap, Dh)).astype(np.float32)
+    ptok = rng.integers(3, 99, (Q, pcap)).astype(np.int32)
+    hs = oracle.Sched(slots, active=list(act))
+    pool = sd.SeqBuf(torch.from_numpy(kv).cuda(), torch.from_numpy(tok).cuda(), torch.from_numpy(ln).cuda())
+    queue = sd.SeqBuf(torch.from_numpy(pkv).cuda(), torch.from_numpy(ptok).cuda(), torch.from_numpy(plen).cuda())
+    ds = sd.Sched(slots, active=list(act))
+    B = act.size
+    order, uni, wid, nu = sd.group_by_len(pool.len, G, ids=ds.active[:B])
+    o_order, _, _, _ = oracle.group_by_len(ln[act], G)
+    rows = act[o_order]
+    assert np.array_equal(order.cpu().numpy(), rows)
+    acc = rng.integers(0, D + 1, B).astype(np.int32)
+    draft = rng.integers(3, 99, (B, D)).astype(np.int32)
+    draft[rng.random((B, D)) < 0.05] = EOS
+    nxt = rng.integers(3, 99, B).astype(np.int32)
+    kvn = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(np.float32)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hkv, htok, hlen = kv.copy(), tok.copy(), ln.copy()
+    for j0 in range(0, B, 1024):  # an append call takes at most 1024 entries
+        j1 = min(B, j0 + 1024)
+        sd.append(pool, torch.from_numpy(np.ascontiguousarray(kvn[:, :, j0:j1])).cuda(),
+                  torch.from_numpy(draft[j0:j1]).cuda(), torch.from_numpy(acc[j0:j1]).cuda(),
+                  torch.from_numpy(nxt[j0:j1]).cuda(), rows=order[j0:j1], status=status)
+    oracle.append(hkv, htok, hlen, rows, kvn, draft, acc, nxt)
+    ret, nret = sd.pool_finish(pool, ds, order, torch.from_numpy(acc).cuda(), D, EOS, max_len, status=status)
+    want_ret = oracle.pool_finish(htok, hlen, hs, rows, acc, D, EOS, max_len)
+    adm, nadm = sd.pool_admit(pool, ds, queue, status=status)
+    want_adm = oracle.pool_admit(hkv, htok, hlen, hs, pkv, ptok, plen)
+    act2, fr2, qh, ln2, tk2, kv2 = _host_state(pool, ds)
+    assert int(status.item()) == 0
+    assert np.array_equal(ret.cpu().numpy()[:int(nret.item())], want_ret) and want_ret.size > 0
+    assert np.array_equal(adm.cpu().numpy()[:int(nadm.item())], want_adm) and want_adm.size > 0
+    assert np.array_equal(act2, hs.active_list()) and np.array_equal(fr2, hs.free_list()) and qh == int(hs.q_head[0])
+    assert np.array_equal(ln2[act2], hlen[act2])
+    for s in act2[::37]:
+        assert np.array_equal(tk2[s, :hlen[s]], htok[s, :hlen[s]])
+        assert bytes_equal(kv2[:, :, s, :, :hlen[s]], hkv[:, :, s, :, :hlen[s]])
