@@ -125,3 +125,55 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError):
         S.lib()
+
+
+def test_paged_and_pool_host_errors():
+    """The paged-cache, lifecycle and fused entry points reject bad arguments on
+    the host (nothing here reaches a HIP call)."""
+    L = S.lib()
+    good = S.PagedC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 8, 4, 2, 2, 64, S.BF16)
+    kv_new = FAKE
+    app = L.specdec_paged_append
+
+    def call(c, **kw):
+        a = dict(rows=None, B=2, D=3, kv_new=kv_new, draft=FAKE, acc=FAKE, nxt=FAKE, rect=None, cap=0)
+        a.update(kw)
+        return app(C.byref(c), a["rows"], a["B"], a["D"], a["kv_new"], a["draft"], a["acc"], a["nxt"], 0, None,
+                   a["rect"], None, None, a["cap"], None, None)
+
+    assert call(good, B=-1) == S.E_ARG
+    assert call(good, B=1025) == S.E_ARG
+    assert call(good, kv_new=None) == S.E_ARG
+    assert call(good, kv_new=FAKE + 8) == S.E_ALIGN
+    assert call(good, rect=FAKE, cap=0) == S.E_ARG
+    bad = S.PagedC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 16, 8, 4, 2, 2, 64, S.BF16)  # no arrival counter
+    assert call(bad) == S.E_ARG
+    bad = S.PagedC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 8, 4, 2, 2, 64, 7)
+    assert call(bad) == S.E_DTYPE
+    bad = S.PagedC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 8, 4, 2, 2, 4, S.BF16)  # 8-byte positions
+    assert call(bad) == S.E_ALIGN
+    assert L.specdec_paged_retire(C.byref(good), FAKE, -1, None, None) == S.E_ARG
+    # lifecycle: more than 4096 pool rows, bad max_len
+    pool = S.SeqBufC(FAKE, FAKE, None, None, FAKE, None, 5000, 16, 2, 2, 64, S.BF16)
+    sched = S.SchedC(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.specdec_pool_finish(C.byref(pool), C.byref(sched), FAKE, FAKE, 1, 3, 2, 10, FAKE, FAKE, None,
+                                 None) == S.E_ARG
+    pool = S.SeqBufC(FAKE, FAKE, None, None, FAKE, None, 64, 16, 2, 2, 64, S.BF16)
+    assert L.specdec_pool_finish(C.byref(pool), C.byref(sched), FAKE, FAKE, 1, 3, 2, 0, FAKE, FAKE, None,
+                                 None) == S.E_ARG
+    nos = S.SchedC(FAKE, None, FAKE, FAKE, FAKE)
+    assert L.specdec_pool_admit(C.byref(pool), C.byref(nos), C.byref(pool), FAKE, FAKE, None, None) == S.E_ARG
+    # grouping over pool rows needs the ids
+    assert L.specdec_group_by_len_ids(FAKE, None, 8, 2, FAKE, FAKE, FAKE, FAKE, None) == S.E_ARG
+    # fused verification: B * (D+1) above 2048, workspace too small
+    f = L.specdec_verify_paged_append
+    assert f(FAKE, S.BF16, 100, 700, 3, 100, FAKE, C.byref(good), None, FAKE, 0, FAKE, FAKE, None, None, None,
+             None, None, 0, FAKE, 1 << 20, None, None) == S.E_ARG
+    assert f(FAKE, S.BF16, 100, 2, 3, 100, FAKE, C.byref(good), None, FAKE, 0, FAKE, FAKE, None, None, None,
+             None, None, 0, FAKE, 8, None, None) == S.E_WORKSPACE
+    assert L.specdec_verify_keys_bytes(0, 3, 100, S.BF16) == 0
+    # sampled verification from logits: temperature and top-p ranges
+    g = L.specdec_verify_sample_logits
+    for T, tp in ((0.0, 1.0), (1.0, 0.0), (1.0, 1.5), (float("nan"), 1.0)):
+        assert g(FAKE, FAKE, S.F32, 2, 3, 100, T, tp, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None,
+                 None) == S.E_ARG
