@@ -71,7 +71,10 @@ const char *specdec_version(void);
 
 /* ------------------------------------------------------------------ verify */
 
-/* Bytes of the workspace specdec_verify_greedy needs for B rows and D drafts. */
+/* Bytes of the workspace specdec_verify_greedy needs for B rows and D drafts:
+ * one 128-byte line for each of its B*(D+1) keys and B batch-row counters (a
+ * base aligned to 128 bytes keeps every one of them on a line of its own;
+ * 8-byte alignment is the requirement). */
 size_t specdec_workspace_bytes(int B, int D);
 
 /* Clears a workspace (device memory, ws_bytes >= specdec_workspace_bytes) once,
@@ -349,14 +352,14 @@ int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_t *sche
  *               from position 0.
  *  len          device int32 [rows]: content length of each row.
  *  sync         device int32 [SPECDEC_PAGED_SYNC_WORDS]: zero when the cache is
- *               created; append and admit count their workgroups in it and
- *               leave it zero.
+ *               created; append and admit count their workgroups in it (one
+ *               counter per 128-byte line) and leave it zero.
  * Calls on one cache must not overlap (they are stream-ordered on one stream).
  * Allocation: batch entries in order take their new pages from the top of the
  * free stack, an entry's first new block getting the topmost remaining id;
  * retiring pushes a row's pages back in block order, entries in batch order.
  * Every page is free or in exactly one row's table; the calls keep it so. */
-#define SPECDEC_PAGED_SYNC_WORDS 256
+#define SPECDEC_PAGED_SYNC_WORDS 4128
 
 typedef struct {
   void *pages;

@@ -32,7 +32,8 @@ size_t kv_bytes(const specdec_seqbuf_t *s) {
          esize(s->dtype);
 }
 
-size_t ws_keys_bytes(int B, int D) { return ((size_t)B * (size_t)(D + 1) * 8 + 255) / 256 * 256; }
+// greedy workspace: one atomic line per key and per batch-row counter
+size_t ws_keys_bytes(int B, int D) { return (size_t)B * (size_t)(D + 1) * sd::kAtomicLine; }
 
 int check_seqbuf_shape(const specdec_seqbuf_t *s) {
   if (!s || !s->kv || !s->len) return SPECDEC_E_ARG;
@@ -57,11 +58,10 @@ bool same_buffers(const specdec_seqbuf_t *a, const specdec_seqbuf_t *b) {
 
 EXPORT const char *specdec_version(void) { return "specdec 0.1 gfx950"; }
 
-static size_t ws_rowcnt_bytes(int B, int D) { return ((size_t)B * (size_t)(D + 1) * 4 + 255) / 256 * 256; }
 
 EXPORT size_t specdec_workspace_bytes(int B, int D) {
   if (B < 0 || D < 0) return 0;
-  return ws_keys_bytes(B, D) + ws_rowcnt_bytes(B, D) + ((size_t)B * 4 + 255) / 256 * 256;
+  return ws_keys_bytes(B, D) + (size_t)B * sd::kAtomicLine;
 }
 
 EXPORT int specdec_workspace_init(void *ws, size_t ws_bytes, void *stream) {
@@ -91,9 +91,7 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
   p.next_token = next_token;
   p.target_tok = target_tok;
   p.keys = static_cast<unsigned long long *>(ws);
-  p.row_counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D));
-  p.counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D) +
-                                                 ws_rowcnt_bytes(B, D));
+  p.counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D));
   p.status = status;
   p.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
   p.partial = nullptr;

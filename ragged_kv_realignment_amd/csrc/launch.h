@@ -14,13 +14,22 @@ struct GreedyParams {
   int B, D, V;
   const int32_t *draft;
   int32_t *accept_len, *next_token, *target_tok;
-  unsigned long long *keys;   // [B*(D+1)] workspace
-  unsigned int *row_counters; // [B*(D+1)] workspace
-  unsigned int *counters;     // [B] workspace
+  // workspace, one kAtomicLine-byte line per word: keys[r * kKeyStride] for
+  // r < B*(D+1), counters[b * kCountStride] for b < B
+  unsigned long long *keys;
+  unsigned int *counters;
   int32_t *status;
   bool vec;                   // 16-byte aligned rows: vector loads
   unsigned long long *partial; // non-null: write each workgroup's key to partial[row * splits + split] and stop
 };
+
+// Words that many workgroups update with device-scope atomics each get a
+// 128-byte line of their own: atomics that share a line are serialized by the
+// memory system, so packed words queue for microseconds where a lone word's
+// round trip takes a few hundred nanoseconds.
+constexpr int kAtomicLine = 128;
+constexpr int kKeyStride = kAtomicLine / 8;
+constexpr int kCountStride = kAtomicLine / 4;
 
 // Greedy verification split into per-workgroup keys (the finish is left to a
 // consumer kernel): the split count launch_verify_greedy uses for these sizes.
@@ -60,8 +69,13 @@ constexpr int kSlThreads = 256;  // threads per workgroup of those kernels
 
 
 constexpr int kPagedAppend = 0, kPagedGather = 1, kPagedAdmit = 2, kPagedRetire = 3;
-constexpr int kPagedSyncWords = 256;  // int32 words of a paged cache's arrival counters
 constexpr int kPagedMaxGrid = 4096;   // workgroups of one append or admit launch at most
+// Arrival counting of append / admit: workgroups in groups of kArriveGroup
+// consecutive ids, one counter line per group plus the root line (group
+// sizes 8 to 64 measured alike on MI355X).
+constexpr int kArriveGroup = 32;
+constexpr int kSyncStride = kAtomicLine / 4;  // int32 words between two counters
+constexpr int kPagedSyncWords = (1 + kPagedMaxGrid / kArriveGroup) * kSyncStride;
 
 struct PagedParams {
   int op;                      // kPaged*
@@ -71,7 +85,8 @@ struct PagedParams {
   int32_t *n_free;             // [1] entries of the stack in use
   int32_t *tokens;             // [rows][max_blocks * page]
   int32_t *len;                // [rows]
-  int32_t *sync;               // [kPagedSyncWords] arrival counters of append / admit, zero between calls
+  int32_t *sync;               // [kPagedSyncWords] arrival counters of append / admit (one per
+                               // kSyncStride words), zero between calls
   int layers, heads, units, n_pages, page, max_blocks, rows;
   const int32_t *rowmap;       // [B] pool row of each batch entry, nullable = identity
   int B, D;

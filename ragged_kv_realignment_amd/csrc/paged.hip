@@ -199,12 +199,12 @@ __device__ __forceinline__ size_t page_unit(const PagedParams &p, int lk, int pg
 // commit.  No fence is needed: a workgroup's reads have returned their values
 // before its arrival is counted, so the commit's later writes cannot reach
 // them, and the commit reads nothing another workgroup wrote.  Arrivals are
-// counted in two levels so that no counter takes more than kArriveGroup
-// atomics: workgroups in groups of kArriveGroup consecutive ids count in
-// sync[1 + group]; the last of each group resets that counter and counts in
-// sync[0], which the committing workgroup resets.
-constexpr int kArriveGroup = 32;
-static_assert(kArriveGroup * (kPagedSyncWords - 1) >= kPagedMaxGrid, "every group has its counter");
+// counted in two levels so that no counter takes more than a few dozen
+// atomics: workgroups in groups of kArriveGroup consecutive ids count in their
+// group's counter; the last of each group resets it and counts in the root
+// counter sync[0], which the committing workgroup resets.  Counters sit
+// kSyncStride words apart, one per 128-byte line.
+static_assert(kArriveGroup * (kPagedSyncWords / kSyncStride - 1) >= kPagedMaxGrid, "every group has its counter");
 
 __device__ __forceinline__ bool arrive_last(const PagedParams &p, PagedPlan &s) {
   __syncthreads();
@@ -212,9 +212,10 @@ __device__ __forceinline__ bool arrive_last(const PagedParams &p, PagedPlan &s) 
     const int g = blockIdx.x / kArriveGroup;
     const int groups = ((int)gridDim.x + kArriveGroup - 1) / kArriveGroup;
     const int in_group = min(kArriveGroup, (int)gridDim.x - g * kArriveGroup);
+    int32_t *gc = p.sync + (size_t)(1 + g) * kSyncStride;
     int last = 0;
-    if (atomicAdd(&p.sync[1 + g], 1) == in_group - 1) {
-      p.sync[1 + g] = 0;
+    if (atomicAdd(gc, 1) == in_group - 1) {
+      *gc = 0;
       last = atomicAdd(&p.sync[0], 1) == groups - 1;
     }
     s.last = last;

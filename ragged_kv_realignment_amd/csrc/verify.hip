@@ -61,92 +61,123 @@ __device__ __forceinline__ int first_eq(u32x4 r, float M) {
   return at;
 }
 
-// Tuning: 16-byte vectors each thread loads at once, and workgroups per CU the
-// split aims for.  Defaults are the measured best on MI355X.
+// Tuning: 16-byte vectors each thread loads at once.  The default is the
+// measured best on MI355X.
 #ifndef SPECDEC_VG_VPT
 #define SPECDEC_VG_VPT 4
 #endif
 
+// max(x, the value DPP control CTRL brings from another lane); rows outside
+// RMASK keep x.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_max(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, RMASK, 0xF, false);
+  return fmaxf(x, __int_as_float(y));
+}
 
-// One workgroup scans `chunk` ids of one logit row (row = b*(D+1) + i): every
-// thread issues all its 16-byte loads before consuming any, forms the 64-bit
-// key of its own (largest value, lowest id holding it), and one block maximum
-// of the keys gives the workgroup's; thread 0 folds it into the row's key with
-// an atomic max.  (With `partial` set, the key is stored per workgroup instead
-// and a consumer kernel finishes.)  The atomic's return is consumed before the per-batch-row
-// counter is incremented, so a workgroup that sees the counter complete also
-// sees every key (both are device-scope atomics, performed at the device's
-// coherence point; the keys are read back with device-scope atomic loads).  The
-// last workgroup of row-block b reads the D+1 keys in parallel, runs the
-// first-mismatch scan and leaves keys and counter zeroed for the next call.
+// Largest value over the wave (NaN only where every lane holds NaN), as a
+// wave-uniform value: swaps within quads, half-row and row mirrors, then the
+// row broadcasts carry each row's maximum into the last row.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// One workgroup scans `chunk` ids of one logit row (row = b*(D+1) + i;
+// workgroups are numbered split-major, so the splits of a row are spread over
+// the launch and finish at different times).  Every thread issues all of its
+// 16-byte loads before consuming any and keeps each vector's maximum.  Each
+// wave then takes its maximum M and the lowest id holding it: ids grow with
+// the vector slot across the whole workgroup, then with the lane, so the first
+// slot whose ballot of "my vector's maximum is M" is non-empty, at its lowest
+// lane, holds it, and one search of that lane's vector gives the id.  The
+// waves' 64-bit (value, ~id) keys are combined by thread 0.
+//
+// Finish: thread 0 folds the key into the row's key with an atomic max, then
+// counts the workgroup in batch row b's counter (D+1 rows x splits arrivals).
+// The max's result is consumed before the count is issued, so the workgroup
+// that sees the count complete also sees every key (both are device-scope
+// atomics performed at the device's coherence point; the keys are read back
+// with device-scope atomic loads).  That last workgroup reads the D+1 keys in
+// parallel, runs the first-mismatch scan and leaves keys and counter zeroed.
+// Each key and counter has a 128-byte line of its own.  With `partial` set
+// the key is stored per workgroup instead and a consumer kernel finishes.
 template <int DT, bool VEC, int NT, int VPT>
 __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits, int chunk) {
   constexpr int ES = Elem<DT>::size;
   constexpr int VW = 16 / ES;
-  const int wg = blockIdx.x;
-  const int row = wg / splits;
-  const int split = wg - row * splits;
+  const int rows = (int)gridDim.x / splits;
+  const int split = (int)blockIdx.x / rows;
+  const int row = (int)blockIdx.x - split * rows;
   const int D = p.D, D1 = p.D + 1;
   const int b = row / D1;
   const int start = split * chunk;
   const int end = min(p.V, start + chunk);
   const char *rowp = static_cast<const char *>(p.logits) + (size_t)row * (size_t)p.row_stride * ES;
-
-  // 1. every thread's largest value; all of its vector loads are issued before
-  //    any is used (one workgroup pass covers the chunk: chunk <= VPT*NT*VW)
-  float m = -INFINITY;
-  u32x4 r[VPT];
-  float tail_x = -INFINITY;
-  int tail_id = -1;
-  int nvec = 0;
-  const u32x4 *vp = nullptr;
-  if constexpr (VEC) {
-    nvec = (end - start) / VW;
-    vp = reinterpret_cast<const u32x4 *>(rowp) + start / VW;
-    if (nvec > 0) {
-#pragma unroll
-      for (int u = 0; u < VPT; ++u)  // indices past the end re-read the last vector and are ignored
-        r[u] = __builtin_nontemporal_load(vp + min(u * NT + (int)threadIdx.x, nvec - 1));
-#pragma unroll
-      for (int u = 0; u < VPT; ++u)
-        if (u * NT + (int)threadIdx.x < nvec) m = fmaxf(m, vmax<DT>(r[u]));
-    }
-    const int tv = start + nvec * VW + threadIdx.x;  // ragged last vector of the row
-    if (tv < end) {
-      tail_x = load_scalar<DT>(rowp, tv);
-      tail_id = tv;
-      m = fmaxf(m, tail_x);
-    }
-  } else {
-    for (int v = start + threadIdx.x; v < end; v += NT) m = fmaxf(m, load_scalar<DT>(rowp, v));
-  }
   __shared__ unsigned long long s_k[NT / kWave];
   __shared__ int s_last, s_a, s_bad;
   __shared__ int s_t[NT];
 
-  // 2. this thread's (largest value, lowest id holding it) as one monotone key:
-  //    its vectors are in increasing id order, so the first that holds m wins
-  int bi = INT_MAX;
+  unsigned long long key = 0ull;  // the smallest key: no id (a thread or wave past the end)
   if constexpr (VEC) {
+    // 1. loads (one workgroup pass covers the chunk: chunk <= VPT*NT*VW);
+    //    slots past the end re-read the last vector and are ignored
+    const int nvec = (end - start) / VW;
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp) + start / VW;
+    u32x4 r[VPT];
+    float vm[VPT];
+    float m = -INFINITY;
+    if (nvec > 0) {
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int k = u * NT + (int)threadIdx.x;
-      if (bi == INT_MAX && k < nvec) {
-        const int at = first_eq<DT>(r[u], m);
-        if (at < VW) bi = start + k * VW + at;
+      for (int u = 0; u < VPT; ++u)
+        r[u] = __builtin_nontemporal_load(vp + min(u * NT + (int)threadIdx.x, nvec - 1));
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        vm[u] = u * NT + (int)threadIdx.x < nvec ? vmax<DT>(r[u]) : -INFINITY;
+        m = fmaxf(m, vm[u]);
       }
     }
-    if (bi == INT_MAX && tail_id >= 0 && tail_x == m) bi = tail_id;
+    float tail_x = -INFINITY;  // the ragged end of the chunk: one scalar per thread
+    const int tv = start + nvec * VW + threadIdx.x;
+    if (tv < end) {
+      tail_x = load_scalar<DT>(rowp, tv);
+      m = fmaxf(m, tail_x);
+    }
+    // 2. the wave's maximum and the lowest id holding it (all wave-uniform)
+    const float M = wave_max_uniform(m);
+    int wid = INT_MAX;
+    if (nvec > 0) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const unsigned long long hit = __ballot(u * NT + (int)threadIdx.x < nvec && vm[u] == M);
+        if (wid == INT_MAX && hit) {
+          const int at = start + (u * NT + (int)threadIdx.x) * VW + first_eq<DT>(r[u], M);
+          wid = __builtin_amdgcn_readlane(at, __builtin_ctzll(hit));
+        }
+      }
+    }
+    if (wid == INT_MAX) {  // the tail's ids follow every vector's
+      const unsigned long long hit = __ballot(tv < end && tail_x == M);
+      if (hit) wid = __builtin_amdgcn_readlane(tv, __builtin_ctzll(hit));
+    }
+    if (wid != INT_MAX) key = argmax_key(M, wid);
   } else {
+    float m = -INFINITY;
+    for (int v = start + threadIdx.x; v < end; v += NT) m = fmaxf(m, load_scalar<DT>(rowp, v));
+    int bi = INT_MAX;
     for (int v = start + threadIdx.x; v < end; v += NT)
       if (load_scalar<DT>(rowp, v) == m) { bi = v; break; }
-  }
-  // a thread with no id (past the end) holds the smallest key
-  unsigned long long key = bi == INT_MAX ? 0ull : argmax_key(m, bi);
+    if (bi != INT_MAX) key = argmax_key(m, bi);
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const unsigned long long o = __shfl_xor(key, off);
-    key = o > key ? o : key;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const unsigned long long o = __shfl_xor(key, off);
+      key = o > key ? o : key;
+    }
   }
   if ((threadIdx.x & (kWave - 1)) == 0) s_k[threadIdx.x / kWave] = key;
   __syncthreads();
@@ -158,20 +189,12 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
       p.partial[(size_t)row * splits + split] = key;
       s_last = 0;
     } else {
-      const unsigned long long old = atomicMax(&p.keys[row], key);
-      // opaque zero computed from the atomic's result: the counter update below
-      // cannot issue before the key update has completed
+      const unsigned long long old = atomicMax(&p.keys[(size_t)row * kKeyStride], key);
+      // opaque zero computed from the atomic's result: the count below cannot
+      // issue before the key update has completed
       uint32_t dep = (uint32_t)old;
       asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(dep));
-      // two-level completion count (splits per row, then D+1 rows per batch row)
-      // keeps the number of atomics on any one address small
-      int last = 0;
-      const unsigned prev = atomicAdd(&p.row_counters[row + (int)dep], 1u);
-      if (prev == (unsigned)(splits - 1)) {
-        store_agent(&p.row_counters[row], 0u);
-        last = atomicAdd(&p.counters[b], 1u) == (unsigned)(D1 - 1);
-      }
-      s_last = last;
+      s_last = atomicAdd(&p.counters[(size_t)(b + (int)dep) * kCountStride], 1u) == (unsigned)(D1 * splits - 1);
     }
     s_a = D;
     s_bad = 0;
@@ -181,7 +204,7 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
   // D + 1 <= NT (checked on the host): one position per thread
   const int i = threadIdx.x;
   if (i < D1) {
-    unsigned long long *kp = &p.keys[(size_t)b * D1 + i];
+    unsigned long long *kp = &p.keys[((size_t)b * D1 + i) * kKeyStride];
     const int t = key_id(load_agent(kp));
     store_agent(kp, 0ull);
     s_t[i] = t;
@@ -197,7 +220,7 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
     const int a = s_a;
     p.accept_len[b] = a;
     p.next_token[b] = s_t[a];
-    store_agent(&p.counters[b], 0u);
+    store_agent(&p.counters[(size_t)b * kCountStride], 0u);
     if (s_bad) set_status(p.status, SPECDEC_S_DRAFT_RANGE);
   }
 }

@@ -360,7 +360,7 @@ group_by_len = specdec_group_by_len
 
 # ----------------------------------------------------------------- paged KV
 
-PAGED_SYNC_WORDS = 256  # SPECDEC_PAGED_SYNC_WORDS
+PAGED_SYNC_WORDS = 4128  # SPECDEC_PAGED_SYNC_WORDS
 
 
 class PagedC(C.Structure):
