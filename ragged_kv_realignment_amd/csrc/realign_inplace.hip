@@ -29,7 +29,7 @@ namespace sd {
 #define SPECDEC_IP_BLOCK 1024  // threads per workgroup (one sequence)
 #endif
 #ifndef SPECDEC_IP_PASSES
-#define SPECDEC_IP_PASSES 8   // 16-byte units per thread per chunk
+#define SPECDEC_IP_PASSES 6   // 16-byte units per thread per chunk (measured best of 2-8)
 #endif
 constexpr int kIpBlock = SPECDEC_IP_BLOCK;
 constexpr int kIpWaves = kIpBlock / kWave;
