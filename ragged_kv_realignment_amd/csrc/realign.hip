@@ -40,13 +40,18 @@ constexpr int kMaxB = kMaxRealignRows;
 #ifndef SPECDEC_GA_TILES_PER_WG
 #define SPECDEC_GA_TILES_PER_WG 8  // GATHER grid: tiles per workgroup if every group were gathered
 #endif
+// Positions per thread per tile: short rows take small tiles, rows that hold
+// at least two large tiles take large ones (see launch_realign).
 #ifndef SPECDEC_RA_PASSES
-#define SPECDEC_RA_PASSES 4      // positions per thread per tile
+#define SPECDEC_RA_PASSES 4
+#endif
+#ifndef SPECDEC_RA_PASSES_LONG
+#define SPECDEC_RA_PASSES_LONG 12
 #endif
 #ifndef SPECDEC_RA_INTERLEAVE
 #define SPECDEC_RA_INTERLEAVE 1  // tile t -> workgroup t mod grid (1) or contiguous ranges (0)
 #endif
-constexpr int kPasses = SPECDEC_RA_PASSES;
+constexpr int kPassesShort = SPECDEC_RA_PASSES, kPassesLong = SPECDEC_RA_PASSES_LONG;
 constexpr int kRaBlock = SPECDEC_RA_BLOCK;
 
 // A destination tile of the pipelined copy: positions [j_lo, j_lo + TP) of one
@@ -67,6 +72,7 @@ __device__ __forceinline__ Tile empty_tile() {
   return t;
 }
 
+template <int kPasses>
 __device__ __forceinline__ void load_tile(const Tile &t, i32x4 *v, int poff, int PP, int U, int u, bool act) {
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
@@ -76,6 +82,7 @@ __device__ __forceinline__ void load_tile(const Tile &t, i32x4 *v, int poff, int
   }
 }
 
+template <int kPasses>
 __device__ __forceinline__ void store_tile(const Tile &t, const i32x4 *v, int poff, int PP, int U, int u, bool act) {
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
@@ -132,20 +139,20 @@ __device__ __forceinline__ Sched my_tiles(uint32_t ntiles) {
 // Software-pipelined copy over this workgroup's tiles: a tile's loads are
 // issued before the previous tile's stores, so waiting for loads never waits
 // for stores (the gfx9 vector-memory counter is in order).
-template <typename TileAt>
+template <int kPasses, typename TileAt>
 __device__ __forceinline__ void run_tiles(uint32_t ntiles, TileAt tile_at, int poff, int PP, int U, int u,
                                           bool act) {
   const Sched sc = my_tiles(ntiles);
   if (sc.first >= sc.end) return;
   Tile cur = tile_at(sc.first);
   i32x4 v[kPasses];
-  load_tile(cur, v, poff, PP, U, u, act);
+  load_tile<kPasses>(cur, v, poff, PP, U, u, act);
   for (uint32_t t = sc.first; t < sc.end; t += sc.step) {
     const uint32_t tn = t + sc.step;
     Tile nxt = tn < sc.end ? tile_at(tn) : empty_tile();
     i32x4 w[kPasses];
-    load_tile(nxt, w, poff, PP, U, u, act);
-    store_tile(cur, v, poff, PP, U, u, act);
+    load_tile<kPasses>(nxt, w, poff, PP, U, u, act);
+    store_tile<kPasses>(cur, v, poff, PP, U, u, act);
     cur = nxt;
 #pragma unroll
     for (int k = 0; k < kPasses; ++k) v[k] = w[k];
@@ -169,6 +176,7 @@ __device__ __forceinline__ Tile eq_tile(const char *in, char *out, const Realign
 }
 
 // ------------------------------------------------------------------ EQSPEC
+template <int kPasses>
 __global__ __launch_bounds__(kRaBlock) void k_realign_eqspec(RealignParams p) {
   __shared__ int s_c[kMaxB];
   __shared__ int s_n[kMaxB];
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(kRaBlock) void k_realign_eqspec(RealignParams p) {
     const int b = (int)(sh - fdiv(sh, fd_b) * B);
     return eq_tile(in, out, p, seg, chunk, b, s_c, s_n, S, Snew, TP, pos_bytes);
   };
-  run_tiles((uint32_t)(nseg * chunks), tile_at, poff, PP, U, u, active);
+  run_tiles<kPasses>((uint32_t)(nseg * chunks), tile_at, poff, PP, U, u, active);
 
   // token ids, position ids and mask of every row, on [0, Snew)
   for (int b = blockIdx.x; b < B; b += gridDim.x) {
@@ -266,6 +274,7 @@ __global__ __launch_bounds__(kRaBlock) void k_realign_eqspec(RealignParams p) {
 // ------------------------------------------------------------------ GATHER
 // Pool rows (content at [0, len)) -> one left-padded rectangle per group of
 // `group` batch entries, for every group not marked in skip_group.
+template <int kPasses>
 __global__ __launch_bounds__(kRaBlock) void k_gather(RealignParams p) {
   __shared__ int s_r[kMaxB];
   __shared__ int s_c[kMaxB];
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(kRaBlock) void k_gather(RealignParams p) {
       t2.a_hi = W;
       return t2;
     };
-    run_tiles((uint32_t)(nseg * chunks), tile_at, poff, PP, U, u, active);
+    run_tiles<kPasses>((uint32_t)(nseg * chunks), tile_at, poff, PP, U, u, active);
   }
 
   for (int k = blockIdx.x; k < nact; k += gridDim.x) {
@@ -467,20 +476,31 @@ __global__ __launch_bounds__(kRaBlock) void k_append_meta(RealignParams p) {
 
 hipError_t launch_realign(const RealignParams &p, hipStream_t s) {
   const int cus = device_cus();
+  // Large tiles when the output rows hold at least two of them: measured on
+  // MI355X, 12 positions per thread were 10-20% faster than 4 for rows of
+  // 2,057-4,256 positions (and even at 2,432) and 5% slower at 1,344.
+  const long pp = kRaBlock / p.units;  // positions per pass
+  const bool long_rows = p.cap_out >= 2 * pp * kPassesLong;
+  const long tp = pp * (long_rows ? kPassesLong : kPassesShort);
   // tiles of the widest output the buffers allow (the true width is known only
   // on the device); workgroups past the real tile count find no tile
-  const long tp = (long)(kRaBlock / p.units) * kPasses;
   const long seqs = (long)p.layers * 2 * p.B * p.heads;
   const long tiles_max = seqs * ((p.cap_out + tp - 1) / tp);
   int grid = 8 * cus;
   if (p.mode == SPECDEC_EQSPEC) {
     const long g = (tiles_max + SPECDEC_RA_TILES_PER_WG - 1) / SPECDEC_RA_TILES_PER_WG;
     if (g > grid) grid = (int)(g < (1L << 30) ? g : (1L << 30));
-    hipLaunchKernelGGL(k_realign_eqspec, dim3(grid), dim3(kRaBlock), 0, s, p);
+    if (long_rows)
+      hipLaunchKernelGGL(k_realign_eqspec<kPassesLong>, dim3(grid), dim3(kRaBlock), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_realign_eqspec<kPassesShort>, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else if (p.mode == SPECDEC_GATHER) {
     const long g = (tiles_max + SPECDEC_GA_TILES_PER_WG - 1) / SPECDEC_GA_TILES_PER_WG;
     if (g > grid) grid = (int)(g < (1L << 30) ? g : (1L << 30));
-    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kRaBlock), 0, s, p);
+    if (long_rows)
+      hipLaunchKernelGGL(k_gather<kPassesLong>, dim3(grid), dim3(kRaBlock), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_gather<kPassesShort>, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else {
     const long ups = (long)(p.D + 1) * p.units;
     const long spp = ups < kRaBlock ? kRaBlock / ups : 1;
