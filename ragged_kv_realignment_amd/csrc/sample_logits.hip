@@ -185,10 +185,17 @@ __global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
 }
 
 // ------------------------------------------------------------------ top-p
-constexpr int kNucThreads = 1024;  // threads per nucleus workgroup (16 waves)
-constexpr int kNucBins = 2048;     // 11-bit digits: key bits 31..21, 20..10, 9..0
-constexpr int kNucUnroll = 4;      // 16-byte vectors in flight per thread
+#ifndef SPECDEC_NUC_THREADS
+#define SPECDEC_NUC_THREADS 512
+#endif
+constexpr int kNucThreads = SPECDEC_NUC_THREADS;  // threads per nucleus workgroup
+constexpr int kNucBins = 2048;      // first level: bins in y = (M - x) / T
+constexpr int kNucSub = 1024;       // later levels: bins in the order key
+constexpr int kNucUnroll = 4;       // 16-byte vectors in flight per thread
 constexpr double kFix = 2199023255552.0;  // 2^41: V <= 2^22 masses <= 1 sum below 2^63
+// exp(-y) * 2^41 < 0.5 (a fixed-point mass of 0) for every y >= kNucSpan
+constexpr double kNucSpan = 29.2;
+constexpr double kNucScale = kNucBins / kNucSpan;
 
 // Order key of a logit: larger key = larger value; -0.0 is folded onto +0.0
 // so equal values share a key.
@@ -243,20 +250,74 @@ __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long l
   return x;
 }
 
+// One level of the selection over NB bins, a higher bin holding larger
+// logits: the largest bin d whose mass at or above it, plus `above` (the mass
+// of everything above the level's interval), reaches `need` (at the first
+// level need < 0 asks for top_p times the level's total, stored back).
+// s_above receives the mass above bin d and s_cmass bin d's mass.
+template <int NB>
+__device__ __forceinline__ int nuc_select(const unsigned long long *hist, unsigned long long above, double &need,
+                                          float top_p, unsigned long long *s_wt, int *s_i,
+                                          unsigned long long *s_above, unsigned long long *s_cmass) {
+  constexpr int PER = NB / kNucThreads;
+  static_assert(PER * kNucThreads == NB, "every thread owns the same number of bins");
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int top = NB - 1 - (int)threadIdx.x * PER;  // this thread's bins: top, top - 1, ...
+  unsigned long long h[PER], tsum = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    h[k] = hist[top - k];
+    tsum += h[k];
+  }
+  unsigned long long incl = wave_incl_scan_u64(tsum, lane);
+  if (lane == kWave - 1) s_wt[wv] = incl;
+  __syncthreads();
+  unsigned long long total = 0;
+#pragma unroll
+  for (int k = 0; k < kNucThreads / kWave; ++k) {
+    if (k < wv) incl += s_wt[k];
+    total += s_wt[k];
+  }
+  if (need < 0.0) need = (double)top_p * (double)total;
+  unsigned long long run = incl - tsum;  // mass of the bins above this thread's
+  int cand = -1;
+  unsigned long long cand_above = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (cand < 0 && (double)(above + run + h[k]) >= need) {
+      cand = top - k;
+      cand_above = above + run;
+    }
+    run += h[k];
+  }
+  const int d = max(block_max_int<kNucThreads>(cand, s_i), 0);
+  if (cand == d) {
+    *s_above = cand_above;
+    *s_cmass = h[top - d];
+  }
+  __syncthreads();
+  return d;
+}
+
 // One workgroup per (row r of 2D+1, batch row b): the nucleus threshold t and
 // 1/Z over the nucleus, written to nuc[(b R + r) * 4 + {0, 1, 2}] = (M, 1/Z, t).
-// t is found digit by digit from the top.  At each level the histogram holds,
-// per digit value, the fixed-point mass of the ids whose key agrees with the
-// digits chosen so far; the chosen digit is the largest d whose mass at or
-// above d, plus the mass of everything above the current prefix, reaches
-// need = top_p * (row mass).  After the last digit the key is t's.
+// Masses are exp(-y) with y = (M - x) / T, held as 2^-41 fixed-point integers
+// so every sum is exact and order-free.  t is selected level by level: the
+// first level bins the logits by y (monotone in the logit, and spread over the
+// bins whatever the logits' exponents), the later ones bin the 32-bit order
+// keys of the chosen bin's interval; every level tracks each bin's smallest
+// and largest key, and the levels go on until the chosen bin holds a single
+// key (each later level shrinks the interval at least kNucSub-fold, so at most
+// five follow the first).  Z is the exact sum of the masses at or above t.
+// Each level reads the row once.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p) {
   __shared__ unsigned long long hist[kNucBins];
+  __shared__ uint32_t s_bmin[kNucBins], s_bmax[kNucBins];
   __shared__ unsigned long long s_wt[kNucThreads / kWave];
   __shared__ double s_d[kNucThreads / kWave];
   __shared__ int s_i[kNucThreads / kWave];
-  __shared__ unsigned long long s_above;
+  __shared__ unsigned long long s_above, s_cmass;
   const int r = blockIdx.x, b = blockIdx.y;
   const int D = p.D, V = p.V, R = 2 * D + 1;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -268,75 +329,73 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
   if (lane == 0) s_d[wv] = m;
+  for (int k = threadIdx.x; k < kNucBins; k += kNucThreads) {
+    hist[k] = 0;
+    s_bmin[k] = 0xFFFFFFFFu;
+    s_bmax[k] = 0;
+  }
   __syncthreads();
   double M = s_d[0];
 #pragma unroll
   for (int k = 1; k < kNucThreads / kWave; ++k) M = fmax(M, s_d[k]);
   const double inv_t = p.inv_t;
-  auto fixed_mass = [&](float x) -> unsigned long long {
-    return (unsigned long long)(exp(((double)x - M) * inv_t) * kFix + 0.5);
-  };
-  uint32_t prefix = 0;
-  unsigned long long above = 0;
-  double need = 0.0;
-#pragma unroll 1
-  for (int level = 0; level < 3; ++level) {
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int bits = level == 2 ? 10 : 11;
-    const uint32_t mask = (1u << bits) - 1u;
-    const int hi = shift + bits;  // key bits from `hi` up are fixed by `prefix` (none at level 0)
-    for (int k = threadIdx.x; k < kNucBins; k += kNucThreads) hist[k] = 0;
-    __syncthreads();
-    each_logit<DT, VEC>(base, off, V, [&](float x) {
+  auto for_each = [&](auto &&f) { each_logit<DT, VEC>(base, off, V, f); };
+  // y of a logit, and the first level's bin (larger logits in higher bins)
+  auto y_of = [&](float x) { return (M - (double)x) * inv_t; };
+  auto bin0 = [&](double y) { return kNucBins - 1 - min(kNucBins - 1, max(0, (int)(y * kNucScale))); };
+  auto fixed_mass = [&](double y) -> unsigned long long { return (unsigned long long)(exp(-y) * kFix + 0.5); };
+
+  // first level: bins in y
+  for_each([&](float x) {
+    const double y = y_of(x);
+    if (y < kNucSpan) {  // false for -inf logits
+      const int k = bin0(y);
+      const unsigned long long fx = fixed_mass(y);
+      if (fx) atomicAdd(&hist[k], fx);
       const uint32_t key = order_key(x);
-      if (hi == 32 || (key >> hi) == prefix) {
-        const unsigned long long fx = fixed_mass(x);
-        if (fx) atomicAdd(&hist[(key >> shift) & mask], fx);
+      atomicMin(&s_bmin[k], key);
+      atomicMax(&s_bmax[k], key);
+    }
+  });
+  __syncthreads();
+  double need = -1.0;
+  const int d0 = nuc_select<kNucBins>(hist, 0ull, need, p.top_p, s_wt, s_i, &s_above, &s_cmass);
+  uint32_t lo = s_bmin[d0], hi = s_bmax[d0];
+  unsigned long long above = s_above;
+  __syncthreads();  // every thread has the interval before the bins are cleared
+  // later levels: bins in the key over [lo, hi]
+#pragma unroll 1
+  for (int level = 0; level < 8 && lo != hi; ++level) {
+    const unsigned long long width = (unsigned long long)(hi - lo) + 1ull;
+    for (int k = threadIdx.x; k < kNucSub; k += kNucThreads) {
+      hist[k] = 0;
+      s_bmin[k] = 0xFFFFFFFFu;
+      s_bmax[k] = 0;
+    }
+    __syncthreads();
+    for_each([&](float x) {
+      const uint32_t key = order_key(x);
+      if (key >= lo && key <= hi) {
+        const int sb = (int)(((unsigned long long)(key - lo) * kNucSub) / width);
+        const double y = y_of(x);
+        const unsigned long long fx = y < kNucSpan ? fixed_mass(y) : 0ull;
+        if (fx) atomicAdd(&hist[sb], fx);
+        atomicMin(&s_bmin[sb], key);
+        atomicMax(&s_bmax[sb], key);
       }
     });
     __syncthreads();
-    // thread j owns bins dh = kNucBins-1-2j and dl = dh-1; scanning j upwards
-    // gives the mass at or above each bin
-    const int dh = kNucBins - 1 - 2 * (int)threadIdx.x, dl = dh - 1;
-    const unsigned long long h_hi = hist[dh], h_lo = hist[dl];
-    unsigned long long incl = wave_incl_scan_u64(h_hi + h_lo, lane);
-    if (lane == kWave - 1) s_wt[wv] = incl;
-    __syncthreads();
-    unsigned long long total = 0;
-#pragma unroll
-    for (int k = 0; k < kNucThreads / kWave; ++k) {
-      if (k < wv) incl += s_wt[k];
-      total += s_wt[k];
-    }
-    if (level == 0) need = (double)p.top_p * (double)total;
-    const unsigned long long suf_lo = incl, suf_hi = incl - h_lo;
-    int cand = -1;
-    if ((double)(above + suf_hi) >= need) cand = dh;
-    else if ((double)(above + suf_lo) >= need) cand = dl;
-    const int d = block_max_int<kNucThreads>(cand, s_i);
-    if (d >= 0 && cand == d) s_above = above + (d == dh ? suf_hi - h_hi : suf_lo - h_lo);
-    __syncthreads();
+    const int d = nuc_select<kNucSub>(hist, above, need, p.top_p, s_wt, s_i, &s_above, &s_cmass);
+    lo = s_bmin[d];
+    hi = s_bmax[d];
     above = s_above;
-    prefix = (prefix << bits) | (uint32_t)max(d, 0);
+    __syncthreads();  // every thread has the interval before the bins are cleared
   }
-  const float t = key_value(prefix);
-  // Z over the nucleus in fp64: thread sums in its own order, then a fixed-order block sum
-  double z = 0.0;
-  each_logit<DT, VEC>(base, off, V, [&](float x) {
-    if (x >= t) z += exp(((double)x - M) * inv_t);
-  });
-  z = wave_sum(z);
-  __syncthreads();
-  if (lane == 0) s_d[wv] = z;
-  __syncthreads();
   if (threadIdx.x == 0) {
-    double zz = 0.0;
-#pragma unroll
-    for (int k = 0; k < kNucThreads / kWave; ++k) zz += s_d[k];
     double *o = p.nuc + ((int64_t)b * R + r) * 4;
     o[0] = M;
-    o[1] = 1.0 / zz;
-    o[2] = (double)t;
+    o[1] = kFix / (double)(above + s_cmass);
+    o[2] = (double)key_value(hi);
   }
 }
 
