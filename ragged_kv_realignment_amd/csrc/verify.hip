@@ -273,51 +273,118 @@ hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s) {
 
 // ---------------------------------------------------------------- sampled
 
-__device__ __forceinline__ double resid(const float *pa, const float *qa, int v) {
-  const double d = qa ? (double)pa[v] - (double)qa[v] : (double)pa[v];
-  return d > 0.0 ? d : 0.0;
-}
+constexpr int kSampleThreads = 1024;  // threads per sampled-verification workgroup (one per batch row)
+constexpr int kSampleBatch = 8;       // 16-byte vectors (of p and of q) a thread has in flight
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Residual masses w of ids v0 .. v0+VW-1 (0 past V).  VW = 4 reads 16-byte vectors.
-template <int VW>
-__device__ __forceinline__ void load_w(const float *pa, const float *qa, int v0, int V, double *w) {
-  if constexpr (VW == 4) {
-    if (v0 + 4 <= V) {
-      const f32x4 pp = *reinterpret_cast<const f32x4 *>(pa + v0);
-      f32x4 qq = (f32x4)(0.0f);
-      if (qa) qq = *reinterpret_cast<const f32x4 *>(qa + v0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double d = qa ? (double)pp[e] - (double)qq[e] : (double)pp[e];
-        w[e] = d > 0.0 ? d : 0.0;
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < VW; ++e) w[e] = (v0 + e < V) ? resid(pa, qa, v0 + e) : 0.0;
+// Residual mass max(0, p - q) of one id in fp64 (q absent: p).
+__device__ __forceinline__ double resid_w(float pv, float qv, bool has_q) {
+  const double d = has_q ? (double)pv - (double)qv : (double)pv;
+  return d > 0.0 ? d : 0.0;
 }
 
-// One workgroup per row b.  Each wave owns a contiguous quarter of the row and
-// reads it in chunks of 64 lanes x VW consecutive ids (coalesced).  Pass 1: the
-// fp64 mass of each quarter and the block total T; the draw target u*T falls in
-// the quarter whose running mass first exceeds it, which that wave re-walks
-// chunk by chunk with an fp64 wave scan.  Several waves may claim the crossing
-// when rounding puts u*T at a quarter boundary; the lowest id wins.
+// The fp64 sum of this thread's run [lo, hi) of weights, in id order, and its
+// last id with a positive weight (-1 if none).  VW = 4: the run starts on a
+// 16-byte boundary and is read as vectors, kSampleBatch of p (and of q) in
+// flight at once.
 template <int VW>
-__global__ __launch_bounds__(kBlock) void k_verify_sample(SampleParams p) {
-  constexpr int NW = kBlock / kWave;
-  constexpr int CH = kWave * VW;
+__device__ __forceinline__ double run_mass(const float *pa, const float *qa, int lo, int hi, int &last) {
+  double m = 0.0;
+  last = -1;
+  if constexpr (VW == 4) {
+    for (int v0 = lo; v0 < hi; v0 += 4 * kSampleBatch) {
+      f32x4 pp[kSampleBatch], qq[kSampleBatch];
+#pragma unroll
+      for (int k = 0; k < kSampleBatch; ++k) {
+        const int v = min(v0 + 4 * k, hi - 4);  // in range: a repeated load, never used
+        pp[k] = *reinterpret_cast<const f32x4 *>(pa + v);
+        qq[k] = qa ? *reinterpret_cast<const f32x4 *>(qa + v) : (f32x4)(0.0f);
+      }
+#pragma unroll
+      for (int k = 0; k < kSampleBatch; ++k) {
+        const int v = v0 + 4 * k;
+        if (v >= hi) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double w = resid_w(pp[k][e], qq[k][e], qa != nullptr);
+          m += w;
+          if (w > 0.0) last = v + e;
+        }
+      }
+    }
+  } else {
+    for (int v = lo; v < hi; ++v) {
+      const double w = resid_w(pa[v], qa ? qa[v] : 0.0f, qa != nullptr);
+      m += w;
+      if (w > 0.0) last = v;
+    }
+  }
+  return m;
+}
+
+// The first id of the run [lo, hi) at which before + (the run's weights summed
+// in id order, as run_mass sums them) passes target, or -1: the same loads in
+// the same batches, so the partial sums end exactly at run_mass's result.
+template <int VW>
+__device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo, int hi, double before,
+                                        double target) {
+  double c = 0.0;
+  if constexpr (VW == 4) {
+    for (int v0 = lo; v0 < hi; v0 += 4 * kSampleBatch) {
+      f32x4 pp[kSampleBatch], qq[kSampleBatch];
+#pragma unroll
+      for (int k = 0; k < kSampleBatch; ++k) {
+        const int v = min(v0 + 4 * k, hi - 4);
+        pp[k] = *reinterpret_cast<const f32x4 *>(pa + v);
+        qq[k] = qa ? *reinterpret_cast<const f32x4 *>(qa + v) : (f32x4)(0.0f);
+      }
+#pragma unroll
+      for (int k = 0; k < kSampleBatch; ++k) {
+        const int v = v0 + 4 * k;
+        if (v >= hi) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c += resid_w(pp[k][e], qq[k][e], qa != nullptr);
+          if (before + c > target) return v + e;
+        }
+      }
+    }
+  } else {
+    for (int v = lo; v < hi; ++v) {
+      c += resid_w(pa[v], qa ? qa[v] : 0.0f, qa != nullptr);
+      if (before + c > target) return v;
+    }
+  }
+  return -1;
+}
+
+// One 1024-thread workgroup per batch row b.  Acceptance of every draft is
+// evaluated in parallel (first rejection by an LDS min).  Then one pass over
+// the stop row: thread t sums the weights of its run of consecutive ids (runs
+// of ceil(V / 1024) ids rounded up to a multiple of 4) in id order, in fp64.
+// A block scan of the run sums in thread order gives T and each run's starting
+// mass; the draw target u * T falls in the first run whose end passes it, and
+// that run's own thread walks it again in the same order from the run's
+// starting mass, so its partial sums end exactly at the mass the choice used
+// and the crossing id is found inside the run.  A zero residual falls back to
+// p at the stop position; no crossing (rounding at the top of the row) takes
+// the last id with positive weight.
+template <int VW>
+__global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p) {
+  constexpr int NW = kSampleThreads / kWave;
   const int b = blockIdx.x;
   const int D = p.D, D1 = p.D + 1, V = p.V;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  __shared__ int s_a, s_bad, s_j, s_lastpos;
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  __shared__ int s_a, s_bad, s_run, s_last;
   __shared__ double s_wt[NW];
-  if (threadIdx.x == 0) { s_a = D; s_bad = 0; s_j = INT_MAX; s_lastpos = -1; }
+  __shared__ int s_i[NW];
+  if (threadIdx.x == 0) {
+    s_a = D;
+    s_bad = 0;
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < D; i += kBlock) {
+  for (int i = threadIdx.x; i < D; i += kSampleThreads) {
     const int x = p.draft[(size_t)b * D + i];
     bool ok = false;
     if (x >= 0 && x < V) {
@@ -334,79 +401,44 @@ __global__ __launch_bounds__(kBlock) void k_verify_sample(SampleParams p) {
   const int a = s_a;
   const float *pa = p.p + ((size_t)b * D1 + a) * V;
   const float *qa = a < D ? p.q + ((size_t)b * D + a) * V : nullptr;
-  const int nchunks = (V + CH - 1) / CH;
-  const int per = (nchunks + NW - 1) / NW;
-  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
+  const int R = ((V + kSampleThreads - 1) / kSampleThreads + 3) / 4 * 4;  // ids per run
+  const int lo = min(V, (int)threadIdx.x * R), hi = min(V, lo + R);
 
-  double T = 0.0, before = 0.0, mine = 0.0;
+  double T = 0.0, before = 0.0, m = 0.0;
+  int last = -1;
   for (int pass = 0; pass < 2; ++pass) {
-    double acc = 0.0;
-    int lastpos = -1;
-    for (int c = c0; c < c1; ++c) {
-      double w[VW];
-      const int v0 = c * CH + lane * VW;
-      load_w<VW>(pa, qa, v0, V, w);
-#pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        acc += w[e];
-        if (w[e] > 0.0) lastpos = v0 + e;
-      }
-    }
-    mine = wave_sum(acc);
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) lastpos = max(lastpos, __shfl_xor(lastpos, off));
-    if (lane == 0) {
-      s_wt[wave] = mine;
-      if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
-    }
+    m = run_mass<VW>(pa, qa, lo, hi, last);
+    // run sums in thread order: exclusive prefix `before` and total T
+    double incl = wave_incl_scan(m, lane);
+    if (lane == kWave - 1) s_wt[wv] = incl;
     __syncthreads();
     T = 0.0;
-    before = 0.0;
+    before = incl - m;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
-      if (k < wave) before += s_wt[k];
+      if (k < wv) before += s_wt[k];
       T += s_wt[k];
     }
     __syncthreads();
     if (T > 0.0 || qa == nullptr) break;
     qa = nullptr;  // zero residual mass: fall back to p at this position
-    if (threadIdx.x == 0) s_lastpos = -1;
-    __syncthreads();
   }
 
   int j = 0;
   if (T > 0.0) {
     const double target = (double)p.u_draw[(size_t)b * D1 + a] * T;
-    if (before + mine > target) {
-      double run = before;
-      for (int c = c0; c < c1; ++c) {
-        double w[VW];
-        const int v0 = c * CH + lane * VW;
-        load_w<VW>(pa, qa, v0, V, w);
-        double sl = 0.0;
-#pragma unroll
-        for (int e = 0; e < VW; ++e) sl += w[e];
-        const double incl = wave_incl_scan(sl, lane);
-        const double chunk_total = __shfl(incl, kWave - 1);
-        if (run + chunk_total > target) {
-          // the crossing lies in this chunk: the first lane whose ids reach past u*T
-          double cum = run + incl - sl;
-          int cand = INT_MAX;
-#pragma unroll
-          for (int e = 0; e < VW; ++e) {
-            cum += w[e];
-            if (cand == INT_MAX && cum > target) cand = v0 + e;
-          }
-#pragma unroll
-          for (int off = kWave / 2; off > 0; off >>= 1) cand = min(cand, __shfl_xor(cand, off));
-          if (lane == 0 && cand != INT_MAX) atomicMin(&s_j, cand);
-          if (cand != INT_MAX) break;
-        }
-        run += chunk_total;
-      }
+    const bool cross = m > 0.0 && before + m > target;
+    const int run = block_min_int<kSampleThreads>(cross ? (int)threadIdx.x : INT_MAX, s_i);
+    const int lastpos = block_max_int<kSampleThreads>(last, s_i);
+    if (run == INT_MAX) {
+      if (threadIdx.x == 0) s_last = lastpos;
+    } else if ((int)threadIdx.x == run) {
+      // this thread's run again, same order: the first id whose cumulative mass passes the target
+      const int hit = run_walk<VW>(pa, qa, lo, hi, before, target);
+      s_last = hit >= 0 ? hit : last;  // (always found: the partial sums end at m)
     }
     __syncthreads();
-    j = s_j != INT_MAX ? s_j : s_lastpos;
+    j = s_last;
   } else if (threadIdx.x == 0) {
     atomicOr(&s_bad, SPECDEC_S_PROB);
   }
@@ -422,9 +454,9 @@ hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s) {
   const bool vec = p.V % 4 == 0 && reinterpret_cast<uintptr_t>(p.p) % 16 == 0 &&
                    (p.q == nullptr || reinterpret_cast<uintptr_t>(p.q) % 16 == 0);
   if (vec)
-    hipLaunchKernelGGL(k_verify_sample<4>, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_verify_sample<4>, dim3((unsigned)p.B), dim3(kSampleThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(k_verify_sample<1>, dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+    hipLaunchKernelGGL(k_verify_sample<1>, dim3((unsigned)p.B), dim3(kSampleThreads), 0, s, p);
   return hipGetLastError();
 }
 
