@@ -292,7 +292,6 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
     dev = torch.device("cuda", 0)
     tdt = sdev.TORCH_DT[cfg.kv_dtype]
     bufs = [sd.SeqBuf.empty(cfg.L, cfg.B, cfg.H, cap, cfg.Dh, tdt) for _ in range(1 if mode != "eqspec" else 2)]
-    kws = sd.keys_workspace(cfg.B, cfg.D, cfg.V, w.logits.dtype, dev) if mode == "paged" else None
     if mode == "paged":
         mb = -(-cap // PAGE)
         cache = sd.PagedKV.empty(cfg.L, cfg.B, cfg.H, cfg.Dh, cfg.B * mb, PAGE, mb, tdt)
@@ -310,20 +309,14 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
         for r in range(n):
             if ev:
                 ev[r][0].record()
-            if mode == "paged":  # verification finished inside the append kernel
-                if ev:
-                    ev[r][1].record()
-                sd.verify_paged_append(w.logits[r], w.drafts[r], cache, w.kv_new[r], ws=kws, accept_len=acc_hist[r],
-                                       next_token=nxt_hist[r], width=width, rect_tokens=view[0], rect_pos=view[1],
-                                       rect_mask=view[2], status=status)
-                if ev:
-                    ev[r][2].record()
-                continue
             sd.verify_greedy(w.logits[r], w.drafts[r], ws=ws, status=status, accept_len=acc_hist[r],
                              next_token=nxt_hist[r])
             if ev:
                 ev[r][1].record()
-            if mode == "inplace":
+            if mode == "paged":
+                sd.paged_append(cache, w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r], width=width,
+                                rect_tokens=view[0], rect_pos=view[1], rect_mask=view[2], status=status)
+            elif mode == "inplace":
                 sd.realign_eqspec_inplace(bufs[0], w.kv_new[r], w.drafts[r], acc_hist[r], nxt_hist[r],
                                           status=status)
             else:
@@ -420,7 +413,7 @@ def bench_chain(args, cfg):
         if mode == "paged":
             pb = round_bytes_paged(cfg, w.lens0, r["acc"], PAGE)
             gbs = pb.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
-            return _roof("k_verify_greedy (keys only) + k_paged_append", gbs, float(pb.mean()),
+            return _roof("k_paged_append", gbs, float(pb.mean()),
                          float(r["re_ms"].mean() * 1e3))
         fn = round_bytes_inplace if mode == "inplace" else (lambda *a: round_bytes(*a)[1])
         rbytes = fn(cfg, w.lens0, w.width0, r["acc"])
@@ -458,8 +451,8 @@ def bench_chain(args, cfg):
                                     "ms_per_step": o["graph_ms"] / K,
                                     "how": "the same %d rounds captured in one HIP graph, replayed once" % K},
                           "page_positions": PAGE,
-                          "call": "specdec_verify_paged_append (greedy verification finished inside the append)",
-                          "realign": {"kernels": "k_verify_greedy (keys only) + k_paged_append",
+                          "call": "specdec_verify_greedy, then specdec_paged_append",
+                          "realign": {"kernels": "k_paged_append",
                                       "achieved_gbs": gbs, "frac": gbs / PEAK_HBM_GBS,
                                       "algorithmic_bytes_per_call": float(pb.mean()),
                                       "avg_call_us": float(o["re_ms"].mean() * 1e3)}}

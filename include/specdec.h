@@ -428,32 +428,6 @@ int specdec_paged_admit(const specdec_paged_t *kv, const int32_t *rows, int B, c
  * (nothing written either way).  Errors: E_ARG, E_LAUNCH. */
 int specdec_paged_retire(const specdec_paged_t *kv, const int32_t *rows, int B, int32_t *status, void *stream);
 
-/* ------------------------------ verification fused into the paged append */
-
-/* Greedy verification and the paged append in one call: the split-vocabulary
- * pass of specdec_verify_greedy leaves one 64-bit key per (row, split)
- * workgroup in `ws`, and the append kernel finishes verification itself (every
- * workgroup reduces the keys; one writes accept_len, next_token and target_tok),
- * so no device-wide completion runs between the two.  Results are identical to
- * specdec_verify_greedy followed by specdec_paged_append.
- * Bytes of `ws` for B rows, D drafts, V logits of type dtype (0 for bad sizes);
- * the value depends on the current device's compute-unit count. */
-size_t specdec_verify_keys_bytes(int B, int D, int V, int dtype);
-
-/* specdec_verify_greedy (logits, dtype, row_stride, B, D, V, draft; outputs
- * accept_len, next_token, target_tok as there) followed by specdec_paged_append
- * (the other arguments as there; its accepted lengths and next tokens are the
- * verification's).  ws: device, at least specdec_verify_keys_bytes(B, D, V,
- * dtype) bytes, 8-byte aligned, scratch only.  Limits: B * (D+1) <= 2048,
- * D + 1 <= 256, and those of both calls.  A condition of the append leaves the
- * cache untouched; the verification outputs are written regardless. */
-int specdec_verify_paged_append(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
-                                const int32_t *draft, const specdec_paged_t *kv, const int32_t *rows,
-                                const void *kv_new, int32_t pad_token, int32_t *accept_len, int32_t *next_token,
-                                int32_t *target_tok, int32_t *width, int32_t *rect_tokens, int32_t *rect_pos,
-                                int8_t *rect_mask, int rect_cap, void *ws, size_t ws_bytes, int32_t *status,
-                                void *stream);
-
 #ifdef __cplusplus
 }
 #endif

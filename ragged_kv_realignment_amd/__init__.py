@@ -8,4 +8,4 @@ from .specdec import (  # noqa: F401
     SeqBuf, SpecDecError, append, gather, group_by_len, lib, realign_eqspec, realign_eqspec_inplace, specdec_group_by_len,
     specdec_realign_kv, specdec_verify_greedy, specdec_verify_sample, specdec_verify_sample_logits, specdec_version,
     sample_workspace, verify_greedy, verify_sample, verify_sample_logits, workspace, PagedKV, paged_admit,
-    paged_append, paged_gather, paged_retire, Sched, pool_admit, pool_finish, keys_workspace, verify_paged_append)
+    paged_append, paged_gather, paged_retire, Sched, pool_admit, pool_finish)

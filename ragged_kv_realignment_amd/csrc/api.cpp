@@ -8,7 +8,6 @@
 
 #include "launch.h"
 #include "specdec.h"
-#include "verify_finish.h"
 
 #define EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -94,7 +93,6 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
   p.counters = reinterpret_cast<unsigned int *>(static_cast<char *>(ws) + ws_keys_bytes(B, D));
   p.status = status;
   p.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
-  p.partial = nullptr;
   return launched(sd::launch_verify_greedy(p, as_stream(stream)));
 }
 
@@ -564,67 +562,4 @@ EXPORT int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_
   p.admitted = admitted;
   p.n_admitted = n_admitted;
   return launched(sd::launch_pool_admit(p, as_stream(stream)));
-}
-
-// ------------------------------------------- verification fused into realignment
-
-// Bytes of the per-workgroup keys a fused verification leaves for its consumer.
-static size_t verify_keys_bytes(int B, int D, int V, int dtype) {
-  return ((size_t)B * (size_t)(D + 1) * (size_t)sd::greedy_splits(B, D, V, dtype) * 8 + 255) / 256 * 256;
-}
-
-EXPORT size_t specdec_verify_keys_bytes(int B, int D, int V, int dtype) {
-  if (B < 1 || D < 0 || V < 1 || !dtype_ok(dtype)) return 0;
-  return verify_keys_bytes(B, D, V, dtype);
-}
-
-// The split-vocabulary pass of greedy verification, leaving its keys in ws.
-static int verify_partial_prepare(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
-                                  const int32_t *draft, int32_t *accept_len, int32_t *next_token, void *ws,
-                                  size_t ws_bytes, sd::GreedyParams &g) {
-  if (B < 1 || D < 0 || V < 1 || row_stride < V) return SPECDEC_E_ARG;
-  if (!dtype_ok(dtype)) return SPECDEC_E_DTYPE;
-  if (!logits || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
-  if (D + 1 > 256 || (long long)B * (D + 1) > sd::kMaxFinishRows || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
-  if (!ws || ws_bytes < verify_keys_bytes(B, D, V, dtype) || reinterpret_cast<uintptr_t>(ws) % 8 != 0)
-    return SPECDEC_E_WORKSPACE;
-  memset(&g, 0, sizeof(g));
-  g.logits = logits;
-  g.dtype = dtype;
-  g.row_stride = row_stride;
-  g.B = B;
-  g.D = D;
-  g.V = V;
-  g.draft = draft;
-  g.vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && ((size_t)row_stride * esize(dtype)) % 16 == 0;
-  g.partial = static_cast<unsigned long long *>(ws);
-  return SPECDEC_OK;
-}
-
-EXPORT int specdec_verify_paged_append(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
-                                       const int32_t *draft, const specdec_paged_t *kv, const int32_t *rows,
-                                       const void *kv_new, int32_t pad_token, int32_t *accept_len,
-                                       int32_t *next_token, int32_t *target_tok, int32_t *width,
-                                       int32_t *rect_tokens, int32_t *rect_pos, int8_t *rect_mask, int rect_cap,
-                                       void *ws, size_t ws_bytes, int32_t *status, void *stream) {
-  if (B == 0) return SPECDEC_OK;
-  sd::GreedyParams g;
-  int rc = verify_partial_prepare(logits, dtype, row_stride, B, D, V, draft, accept_len, next_token, ws, ws_bytes, g);
-  if (rc) return rc;
-  sd::PagedParams p;
-  rc = paged_append_prepare(kv, rows, B, D, kv_new, draft, accept_len, next_token, pad_token, width, rect_tokens,
-                            rect_pos, rect_mask, rect_cap, status, p);
-  if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
-  const size_t kb = verify_keys_bytes(B, D, V, dtype);
-  if (overlap(ws, kb, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
-  p.vkeys = g.partial;
-  p.vsplits = sd::greedy_splits(B, D, V, dtype);
-  p.V = V;
-  p.vacc = accept_len;
-  p.vnext = next_token;
-  p.vtgt = target_tok;
-  const hipStream_t st = as_stream(stream);
-  const hipError_t e = sd::launch_verify_greedy(g, st);
-  if (e != hipSuccess) return SPECDEC_E_LAUNCH;
-  return launched(sd::launch_paged(p, st));
 }

@@ -20,7 +20,6 @@ struct GreedyParams {
   unsigned int *counters;
   int32_t *status;
   bool vec;                   // 16-byte aligned rows: vector loads
-  unsigned long long *partial; // non-null: write each workgroup's key to partial[row * splits + split] and stop
 };
 
 // Words that many workgroups update with device-scope atomics each get a
@@ -30,10 +29,6 @@ struct GreedyParams {
 constexpr int kAtomicLine = 128;
 constexpr int kKeyStride = kAtomicLine / 8;
 constexpr int kCountStride = kAtomicLine / 4;
-
-// Greedy verification split into per-workgroup keys (the finish is left to a
-// consumer kernel): the split count launch_verify_greedy uses for these sizes.
-int greedy_splits(int B, int D, int V, int dtype);
 
 struct SampleParams {
   const float *p, *q;
@@ -102,11 +97,6 @@ struct PagedParams {
   int32_t *width_out;          // append: S'
   int32_t *status;
   int kv_wgs;                  // workgroups that copy KV (set by the launcher)
-  // greedy verification finished by the append (see verify_finish.h): the
-  // split-vocabulary keys [B*(D+1)][vsplits], the vocabulary size, the outputs
-  const unsigned long long *vkeys;
-  int vsplits, V;
-  int32_t *vacc, *vnext, *vtgt;
 };
 
 struct GroupParams {

@@ -29,7 +29,6 @@
 #include "device_common.h"
 #include "launch.h"
 #include "specdec.h"
-#include "verify_finish.h"
 
 namespace sd {
 
@@ -81,11 +80,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int *red, int &total) {
 
 // The plan of an append (ADMIT = false: entry b gains accept_len[b] + 1
 // positions at its length) or an admit (entry b's row must be empty and gains
-// in_len[b] positions), from the call's unchanged inputs.  With FUSED the
-// accepted lengths and next tokens come from finishing greedy verification
-// here (vacc, s.nxt).  Returns the status bits of a failed check (0 = go).
-template <bool ADMIT, bool FUSED = false>
-__device__ int paged_plan(const PagedParams &p, PagedPlan &s, const int *vacc = nullptr) {
+// in_len[b] positions), from the call's unchanged inputs.  Returns the status
+// bits of a failed check (0 = go).
+template <bool ADMIT>
+__device__ int paged_plan(const PagedParams &p, PagedPlan &s) {
   const int B = p.B, tcap = p.max_blocks * p.page;
   int bad = 0, cap = 0, mx = 0, ksum = 0;
   int kloc[kPgPer];
@@ -108,8 +106,8 @@ __device__ int paged_plan(const PagedParams &p, PagedPlan &s, const int *vacc = 
     }
     rr[e] = r;
     cc[e] = p.len[r];
-    nn[e] = ADMIT ? p.in_len[b] : (FUSED ? vacc[b] : p.accept_len[b]) + 1;
-    if (!ADMIT && !FUSED) s.nxt[b] = p.next_token[b];
+    nn[e] = ADMIT ? p.in_len[b] : p.accept_len[b] + 1;
+    if (!ADMIT) s.nxt[b] = p.next_token[b];
   }
   // the top of the free stack, one entry per thread, before it is known how
   // many entries the call pops
@@ -275,18 +273,9 @@ __device__ void paged_commit(const PagedParams &p, PagedPlan &s) {
 // them (when the rectangle view is asked for) write row b's token ids,
 // position ids and mask over [0, S'), kRectChunk positions each; the last
 // workgroup to finish commits.
-template <bool FUSED>
 __global__ __launch_bounds__(kPgBlock) void k_paged_append(PagedParams p) {
   __shared__ PagedPlan s;
-  __shared__ unsigned long long s_vkey[FUSED ? kMaxFinishRows : 1];
-  __shared__ int s_vacc[FUSED ? kMaxRealignRows : 1];
-  if constexpr (FUSED) {
-    const int dbad = verify_finish<kPgBlock>(p.vkeys, p.vsplits, p.B, p.D, p.draft, p.V, s_vkey, s_vacc, s.nxt,
-                                             s.red);
-    if (blockIdx.x == 0) verify_outputs<kPgBlock>(p.B, p.D, s_vkey, s_vacc, s.nxt, dbad, p.vacc, p.vnext, p.vtgt,
-                                                  p.status);
-  }
-  const int flags = paged_plan<false, FUSED>(p, s, s_vacc);
+  const int flags = paged_plan<false>(p, s);
   const int B = p.B, U = p.units, H = p.heads, D1 = p.D + 1;
   if (!flags && (int)blockIdx.x >= p.kv_wgs) {
     // rectangle view: item (b, chunk) covers positions [chunk * kRectChunk, +kRectChunk) of row b
@@ -533,10 +522,7 @@ hipError_t launch_paged(const PagedParams &q, hipStream_t st) {
     p.kv_wgs = (int)(g < 2L * cus ? (g > 0 ? g : 1) : 2L * cus);
     const long items = p.rect_tok ? (long)p.B * ((p.rect_cap + kRectChunk - 1) / kRectChunk) : 0;
     const int extra = (int)(items < 1024 ? items : 1024);
-    if (p.vkeys)
-      hipLaunchKernelGGL(k_paged_append<true>, dim3((unsigned)(p.kv_wgs + extra)), dim3(kPgBlock), 0, st, p);
-    else
-      hipLaunchKernelGGL(k_paged_append<false>, dim3((unsigned)(p.kv_wgs + extra)), dim3(kPgBlock), 0, st, p);
+    hipLaunchKernelGGL(k_paged_append, dim3((unsigned)(p.kv_wgs + extra)), dim3(kPgBlock), 0, st, p);
   } else if (p.op == kPagedAdmit) {
     // units of the widest input the buffer allows; workgroups past the real count find none
     const long units = (long)p.layers * 2 * p.B * p.heads * p.rect_cap * p.units;

@@ -105,8 +105,7 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
 // atomics performed at the device's coherence point; the keys are read back
 // with device-scope atomic loads).  That last workgroup reads the D+1 keys in
 // parallel, runs the first-mismatch scan and leaves keys and counter zeroed.
-// Each key and counter has a 128-byte line of its own.  With `partial` set
-// the key is stored per workgroup instead and a consumer kernel finishes.
+// Each key and counter has a 128-byte line of its own.
 template <int DT, bool VEC, int NT, int VPT>
 __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits, int chunk) {
   constexpr int ES = Elem<DT>::size;
@@ -185,17 +184,12 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
 #pragma unroll
     for (int w = 1; w < NT / kWave; ++w) key = s_k[w] > key ? s_k[w] : key;
     key = s_k[0] > key ? s_k[0] : key;
-    if (p.partial) {
-      p.partial[(size_t)row * splits + split] = key;
-      s_last = 0;
-    } else {
-      const unsigned long long old = atomicMax(&p.keys[(size_t)row * kKeyStride], key);
-      // opaque zero computed from the atomic's result: the count below cannot
-      // issue before the key update has completed
-      uint32_t dep = (uint32_t)old;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(dep));
-      s_last = atomicAdd(&p.counters[(size_t)(b + (int)dep) * kCountStride], 1u) == (unsigned)(D1 * splits - 1);
-    }
+    const unsigned long long old = atomicMax(&p.keys[(size_t)row * kKeyStride], key);
+    // opaque zero computed from the atomic's result: the count below cannot
+    // issue before the key update has completed
+    uint32_t dep = (uint32_t)old;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(dep));
+    s_last = atomicAdd(&p.counters[(size_t)(b + (int)dep) * kCountStride], 1u) == (unsigned)(D1 * splits - 1);
     s_a = D;
     s_bad = 0;
   }
@@ -243,11 +237,6 @@ static long greedy_chunk(int B, int D, int V, int dtype) {
   chunk = (chunk + step - 1) / step * step;
   if (chunk > (long)SPECDEC_VG_VPT * step) chunk = (long)SPECDEC_VG_VPT * step;
   return chunk;
-}
-
-int greedy_splits(int B, int D, int V, int dtype) {
-  const long chunk = greedy_chunk(B, D, V, dtype);
-  return (int)((V + chunk - 1) / chunk);
 }
 
 template <int DT>

@@ -26,7 +26,7 @@ EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init
            "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
            "specdec_realign_kv", "specdec_group_by_len", "specdec_paged_append", "specdec_paged_gather",
            "specdec_paged_admit", "specdec_paged_retire", "specdec_group_by_len_ids", "specdec_pool_finish",
-           "specdec_pool_admit", "specdec_verify_keys_bytes", "specdec_verify_paged_append")
+           "specdec_pool_admit")
 
 
 class SpecDecError(RuntimeError):
@@ -74,15 +74,10 @@ def lib():
         L.specdec_pool_finish.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), vp, vp, ci, ci, C.c_int32, C.c_int32,
                                           vp, vp, vp, vp]
         L.specdec_pool_admit.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), C.POINTER(SeqBufC), vp, vp, vp, vp]
-        L.specdec_verify_keys_bytes.argtypes = [ci, ci, ci, ci]
-        L.specdec_verify_keys_bytes.restype = sz
-        L.specdec_verify_paged_append.argtypes = [vp, ci, C.c_int64, ci, ci, ci, vp, C.POINTER(PagedC), vp, vp,
-                                                  C.c_int32, vp, vp, vp, vp, vp, vp, vp, ci, vp, sz, vp, vp]
         for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample",
                   "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len",
                   "specdec_paged_append", "specdec_paged_gather", "specdec_paged_admit", "specdec_paged_retire",
-                  "specdec_group_by_len_ids", "specdec_pool_finish", "specdec_pool_admit",
-                  "specdec_verify_paged_append"):
+                  "specdec_group_by_len_ids", "specdec_pool_finish", "specdec_pool_admit"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -533,47 +528,3 @@ def pool_admit(pool, sched, queue, admitted=None, n_admitted=None, status=None):
                                   n_admitted.data_ptr(), _ptr(status), _stream())
     _check(rc, "specdec_pool_admit")
     return admitted, n_admitted
-
-
-# --------------------------------------- verification fused into realignment
-
-def keys_workspace(B, D, V, dtype=torch.bfloat16, device="cuda"):
-    """Scratch for the per-workgroup keys of a fused verification."""
-    n = int(lib().specdec_verify_keys_bytes(B, D, V, _TORCH_DT[dtype]))
-    if n == 0:
-        raise ValueError("bad sizes for a fused verification")
-    return torch.empty(n, dtype=torch.uint8, device=device)
-
-
-def _greedy_args(logits, draft):
-    _need(logits, "logits")
-    if logits.dtype not in _TORCH_DT or logits.dim() != 3:
-        raise ValueError("logits must be a [B, D+1, V] float32/float16/bfloat16 tensor")
-    B, D1, V = logits.shape
-    _need(draft, "draft", torch.int32)
-    if tuple(draft.shape) != (B, D1 - 1):
-        raise ValueError("draft must be [B, D]")
-    return B, D1 - 1, V
-
-
-def verify_paged_append(logits, draft, cache, kv_new, ws=None, rows=None, accept_len=None, next_token=None,
-                        target_tok=None, pad_token=0, width=None, rect_tokens=None, rect_pos=None, rect_mask=None,
-                        status=None):
-    """Greedy verification and the paged append in one call.  Returns (accept_len, next_token)."""
-    B, D, V = _greedy_args(logits, draft)
-    _need(kv_new, "kv_new", cache.pages.dtype)
-    dev = logits.device
-    ws = keys_workspace(B, D, V, logits.dtype, dev) if ws is None else ws
-    accept_len = _i32(B, dev) if accept_len is None else accept_len
-    next_token = _i32(B, dev) if next_token is None else next_token
-    rect_cap = 0
-    if rect_tokens is not None:
-        _need(rect_tokens, "rect_tokens", torch.int32)
-        rect_cap = rect_tokens.shape[1]
-    rc = lib().specdec_verify_paged_append(logits.data_ptr(), _TORCH_DT[logits.dtype], V, B, D, V, _ptr(draft),
-                                           C.byref(cache.c), _ptr(rows), kv_new.data_ptr(), pad_token,
-                                           accept_len.data_ptr(), next_token.data_ptr(), _ptr(target_tok),
-                                           _ptr(width), _ptr(rect_tokens), _ptr(rect_pos), _ptr(rect_mask), rect_cap,
-                                           ws.data_ptr(), ws.numel(), _ptr(status), _stream())
-    _check(rc, "specdec_verify_paged_append")
-    return accept_len, next_token

@@ -1,5 +1,5 @@
-"""Chained rounds of the fused greedy verification + paged append captured in a
-HIP graph: every replay, with the program's own eager work (a reset of the
+"""Chained rounds of greedy verification + paged append captured in a HIP
+graph: every replay, with the program's own eager work (a reset of the
 cache) and synchronisations between replays, reproduces the eager rounds byte
 for byte (accepted lengths, next tokens, pages, block table, free stack,
 token ids, lengths and the rectangle view)."""
@@ -47,7 +47,7 @@ def test_paged_rounds_graph_replays(sd):
             drafts[r, b, :k] = am[r, b, :k]
     drafts = torch.from_numpy(drafts).cuda()
     kv_new = torch.from_numpy(rng.standard_normal((R, L, 2, B, H, D + 1, Dh)).astype(np.float16)).cuda()
-    ws = sd.keys_workspace(B, D, V, logits.dtype)
+    ws = sd.workspace(B, D)
     acc = torch.zeros((R, B), dtype=torch.int32, device="cuda")
     nxt = torch.zeros((R, B), dtype=torch.int32, device="cuda")
     width = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -68,9 +68,9 @@ def test_paged_rounds_graph_replays(sd):
 
     def rounds():
         for r in range(R):
-            sd.verify_paged_append(logits[r], drafts[r], cache, kv_new[r], ws=ws, accept_len=acc[r],
-                                   next_token=nxt[r], width=width, rect_tokens=view[0], rect_pos=view[1],
-                                   rect_mask=view[2], status=status)
+            sd.verify_greedy(logits[r], drafts[r], ws=ws, status=status, accept_len=acc[r], next_token=nxt[r])
+            sd.paged_append(cache, kv_new[r], drafts[r], acc[r], nxt[r], width=width, rect_tokens=view[0],
+                            rect_pos=view[1], rect_mask=view[2], status=status)
 
     def snapshot():
         torch.cuda.synchronize()
