@@ -356,3 +356,40 @@ def test_no_nucleus_reports_minus_inf(sd):
     acc, nxt, cut = _run(sd, tl, dl, draft, rng.random((B, D)).astype(np.float32),
                          rng.random((B, D + 1)).astype(np.float32), 1.0, want_cut=True)
     assert np.all(cut == -np.inf)
+
+
+@pytest.mark.parametrize("case", ["constant", "single_id", "two_values", "one_spike"])
+def test_top_p_degenerate_rows(sd, case):
+    """Rows the nucleus selection reaches in one step or at its edges: every
+    logit equal (the nucleus is the whole row, ties at t all kept), a
+    one-entry vocabulary, two values repeated over the row (t is the larger
+    when its ids hold top_p), and one logit far above the rest (the nucleus
+    is that id alone)."""
+    rng = np.random.default_rng(95)
+    B, D = 4, 3
+    V = 1 if case == "single_id" else 3001
+    say("sample logits top_p degenerate", case)
+    if case == "constant":
+        tl = np.full((B, D + 1, V), 1.25, np.float32)
+    elif case == "single_id":
+        tl = rng.standard_normal((B, D + 1, V)).astype(np.float32)
+    elif case == "two_values":
+        tl = np.where(rng.random((B, D + 1, V)) < 0.3, 2.0, -1.0).astype(np.float32)
+    else:
+        tl = rng.standard_normal((B, D + 1, V)).astype(np.float32)
+        tl[..., 17] = 60.0
+    dl = tl[:, :D].copy()
+    dl[..., :V // 2] += 0.25 if V > 1 else 0.0
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    for top_p in (0.3, 0.999):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, 1.0, status=status, top_p=top_p, want_cut=True)
+        assert int(status.item()) == 0, (case, top_p)
+        *_, ocut = oracle.verify_sample_logits(tl, dl, draft, u_acc, u_draw, 1.0, top_p, return_cut=True)
+        assert np.array_equal(cut, ocut), (case, top_p)
+        check_round(tl, dl, draft, u_acc, u_draw, 1.0, acc, nxt, top_p, cut)
+        if case == "one_spike":  # the target rows' nucleus is the spike alone
+            assert np.all(cut[:, :D + 1] == 60.0)
+            assert np.all(nxt[acc == D] == 17)
