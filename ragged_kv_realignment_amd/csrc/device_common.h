@@ -14,23 +14,9 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// (value, id) order used by the argmax: larger value wins, the lower id on equal
-// values.  Float comparison makes -0.0 == +0.0.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-__device__ __forceinline__ void wave_argmax(float &bv, int &bi) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-}
-
-// Monotone 64-bit key of (value, id): larger key = larger value, then lower id.
-// -0.0 is folded onto +0.0 first so the key order matches float comparison.
+// Monotone 64-bit key of (value, id) for the argmax: a larger key is a larger
+// value, then a lower id on equal values.  -0.0 is folded onto +0.0 first so
+// the key order matches float comparison.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int id) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;
