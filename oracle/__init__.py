@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 F32, F16, BF16 = 0, 1, 2
 OK, E_ARG, E_CAPACITY, E_PRECOND = 0, -1, -2, -3
 
-_lib = None
+_libs = {}
+_threaded = False
 
 
 class OracleError(RuntimeError):
@@ -28,10 +29,23 @@ class OracleError(RuntimeError):
         self.code = code
 
 
+def use_threads(flag):
+    """Route later calls to the OpenMP build (True) or the single-threaded one
+    (False, the default).  Both compute the same bytes; the threaded build only
+    serves to time the oracle on all host cores."""
+    global _threaded
+    _threaded = bool(flag)
+
+
+def threads():
+    """Threads the library in use may run its loops on."""
+    return int(lib().oracle_threads())
+
+
 def lib():
-    global _lib
-    if _lib is None:
-        path = os.path.join(HERE, "liboracle.so")
+    name = "liboracle_omp.so" if _threaded else "liboracle.so"
+    if name not in _libs:
+        path = os.path.join(HERE, name)
         if not os.path.exists(path):
             from . import _build
             _build.build()
@@ -58,8 +72,10 @@ def lib():
                   L.oracle_softmax_row, L.oracle_realign_eqspec, L.oracle_group_by_len, L.oracle_gather,
                   L.oracle_append):
             f.restype = C.c_int
-        _lib = L
-    return _lib
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = C.c_int
+        _libs[name] = L
+    return _libs[name]
 
 
 def _p(a, t=C.c_int32):

@@ -1,8 +1,9 @@
 /* Reference oracle for the verify-and-resynchronize step of batch speculative
- * decoding.  TEST INFRASTRUCTURE ONLY: plain, slow, single-threaded C that the
- * tests, the smoke check and the benchmark's CPU-baseline leg call to decide
- * what the GPU path must produce.  It shares no code, header or table with the
- * GPU library and never runs on the product path.
+ * decoding.  TEST INFRASTRUCTURE ONLY: plain, slow C (single-threaded in the
+ * build the tests load) that the tests, the smoke check and the benchmark's
+ * CPU-baseline leg call to decide what the GPU path must produce.  It shares
+ * no code, header or table with the GPU library and never runs on the product
+ * path.
  *
  * Sources (the pages this follows):
  *  [NL]  "Inference Engineering Part 5/8: When Speculative Decoding Backfires",
@@ -18,13 +19,33 @@
  * Readings where the pages leave a choice open are stated at each function.
  * Floating point: greedy compares exactly widened values; sampled acceptance
  * and residual masses are evaluated in fp64.  Parity of every function here
- * is pinned by the CPU tests (worked examples, closed forms, brute force). */
+ * is pinned by the CPU tests (worked examples, closed forms, brute force).
+ *
+ * Threads: the library the tests load is built without OpenMP and runs every
+ * loop in order on one thread.  The same source built with -fopenmp
+ * (liboracle_omp.so) serves only to time the oracle on all host cores: there
+ * greedy verification splits its batch rows and the EQSPEC realignment its
+ * (layer, K|V, row, head) KV segments over threads.  Each of those units
+ * writes only its own outputs, so both builds produce the same bytes (the
+ * threaded realignment additionally needs kv_out apart from kv_in). */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define EXPORT __attribute__((visibility("default")))
+
+/* Threads the loops below may use: 1 unless built with OpenMP. */
+EXPORT int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2 };
 enum { O_OK = 0, O_E_ARG = -1, O_E_CAPACITY = -2, O_E_PRECOND = -3 };
@@ -69,8 +90,10 @@ EXPORT int oracle_verify_greedy(const void *logits, int dtype, int64_t row_strid
                                 const int32_t *draft, int32_t *accept_len, int32_t *next_token,
                                 int32_t *target_tok) {
   if (B < 0 || D < 0 || V <= 0 || row_stride < V) return O_E_ARG;
-  int32_t *t = (int32_t *)malloc(sizeof(int32_t) * (size_t)(D + 1));
+  int32_t *targets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1) * (size_t)(D + 1));
+#pragma omp parallel for schedule(dynamic)
   for (int b = 0; b < B; ++b) {
+    int32_t *t = targets + (size_t)b * (D + 1);
     for (int i = 0; i <= D; ++i) {
       const int64_t row = ((int64_t)b * (D + 1) + i) * row_stride;
       int best = 0;
@@ -87,7 +110,7 @@ EXPORT int oracle_verify_greedy(const void *logits, int dtype, int64_t row_strid
     accept_len[b] = a;
     next_token[b] = t[a];
   }
-  free(t);
+  free(targets);
   return O_OK;
 }
 
@@ -368,7 +391,10 @@ EXPORT int oracle_realign_eqspec(int L, int H, int Dh, int esize, int B, int cap
   }
   *width_out = Snew;
   /* the same unpad / append / repad on every (layer, K|V, head) KV sequence */
+#pragma omp parallel
+  {
   unsigned char *tmp = (unsigned char *)malloc(pbytes * (size_t)(cap_in + D + 1));
+#pragma omp for collapse(4) schedule(static)
   for (int l = 0; l < L; ++l)
     for (int kv = 0; kv < 2; ++kv)
       for (int b = 0; b < B; ++b)
@@ -387,6 +413,7 @@ EXPORT int oracle_realign_eqspec(int L, int H, int Dh, int esize, int B, int cap
           memcpy(dst + (size_t)pad * pbytes, tmp, k * pbytes);
         }
   free(tmp);
+  }
   for (int b = 0; b < B; ++b) free(content[b]);
   free(content); free(clen);
   return O_OK;
