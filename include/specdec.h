@@ -74,7 +74,8 @@ const char *specdec_version(void);
 /* Bytes of the workspace specdec_verify_greedy needs for B rows and D drafts:
  * one 128-byte line for each of its B*(D+1) keys and B batch-row counters (a
  * base aligned to 128 bytes keeps every one of them on a line of its own;
- * 8-byte alignment is the requirement). */
+ * 8-byte alignment is the requirement).  Returns 0 for sizes the verification
+ * rejects: B or D negative, D > 255, or B*(D+1) > 2^24. */
 size_t specdec_workspace_bytes(int B, int D);
 
 /* Clears a workspace (device memory, ws_bytes >= specdec_workspace_bytes) once,

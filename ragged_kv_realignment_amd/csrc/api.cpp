@@ -32,7 +32,7 @@ size_t kv_bytes(const specdec_seqbuf_t *s) {
 }
 
 // greedy workspace: one atomic line per key and per batch-row counter
-size_t ws_keys_bytes(int B, int D) { return (size_t)B * (size_t)(D + 1) * sd::kAtomicLine; }
+size_t ws_keys_bytes(int B, int D) { return (size_t)B * ((size_t)D + 1) * sd::kAtomicLine; }
 
 int check_seqbuf_shape(const specdec_seqbuf_t *s) {
   if (!s || !s->kv || !s->len) return SPECDEC_E_ARG;
@@ -59,7 +59,9 @@ EXPORT const char *specdec_version(void) { return "specdec 0.1 gfx950"; }
 
 
 EXPORT size_t specdec_workspace_bytes(int B, int D) {
-  if (B < 0 || D < 0) return 0;
+  // 0 for sizes specdec_verify_greedy rejects anyway (and whose byte count
+  // could wrap)
+  if (B < 0 || D < 0 || D > 255 || (long long)B * ((long long)D + 1) > (1LL << 24)) return 0;
   return ws_keys_bytes(B, D) + (size_t)B * sd::kAtomicLine;
 }
 
@@ -75,7 +77,7 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
   if (!dtype_ok(dtype)) return SPECDEC_E_DTYPE;
   if (B == 0) return SPECDEC_OK;
   if (!logits || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
-  if (D + 1 > 256 || (long long)B * (D + 1) > (1LL << 24) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  if (D > 255 || (long long)B * ((long long)D + 1) > (1LL << 24) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
   if (!ws || ws_bytes < specdec_workspace_bytes(B, D) || reinterpret_cast<uintptr_t>(ws) % 8 != 0)
     return SPECDEC_E_WORKSPACE;
   sd::GreedyParams p;
@@ -209,7 +211,7 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
   if (units > 256) return SPECDEC_E_ARG;
   // one (layer, K|V, row, head) sequence is addressed with 32-bit byte offsets
   if ((size_t)in->cap * units * 16 >= (1u << 31) || (size_t)out->cap * units * 16 >= (1u << 31) ||
-      (size_t)(D + 1) * units * 16 >= (1u << 31))
+      ((size_t)D + 1) * units * 16 >= (1u << 31))
     return SPECDEC_E_ARG;
   // tiles are numbered with 32-bit integers
   if ((size_t)out->layers * 2 * (size_t)(out->rows > B ? out->rows : B) * out->heads * ((size_t)out->cap + 1) >=
@@ -247,7 +249,7 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
     if (B == 0) return kNothing;
     const size_t kin = kv_bytes(in), kout = kv_bytes(out);
-    const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
+    const size_t knew = (size_t)in->layers * 2 * B * in->heads * ((size_t)D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(in->kv, kin, out->kv, kout) || overlap(kv_new, knew, out->kv, kout)) return SPECDEC_E_ALIAS;
     if (overlap(in->tokens, tok_in_bytes, out->tokens, tok_out_bytes) || overlap(in->len, B * 4u, out->len, B * 4u) ||
         overlap(in->width, 4, out->width, 4) || overlap(accept_len, B * 4u, out->len, B * 4u))
@@ -266,7 +268,7 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
     if (B == 0) return kNothing;
-    const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
+    const size_t knew = (size_t)in->layers * 2 * B * in->heads * ((size_t)D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
     if (overlap(accept_len, B * 4u, in->len, B * 4u) || overlap(next_token, B * 4u, in->tokens, tok_in_bytes) ||
         (D > 0 && overlap(draft, (size_t)B * D * 4, in->tokens, tok_in_bytes)))
@@ -299,7 +301,7 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
     if (B == 0) return kNothing;
-    const size_t knew = (size_t)in->layers * 2 * B * in->heads * (size_t)(D + 1) * in->head_dim * esize(in->dtype);
+    const size_t knew = (size_t)in->layers * 2 * B * in->heads * ((size_t)D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
     p.tok_in = in->tokens;
     p.len_in = in->len;
@@ -399,7 +401,7 @@ static int paged_append_prepare(const specdec_paged_t *kv, const int32_t *rows, 
   if ((rect_tokens || rect_pos || rect_mask) && (!rect_tokens || rect_cap < 1)) return SPECDEC_E_ARG;
   if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
   if (B == 0) return kNothing;
-  const size_t knew = (size_t)kv->layers * 2 * B * kv->heads * (size_t)(D + 1) * kv->head_dim * esize(kv->dtype);
+  const size_t knew = (size_t)kv->layers * 2 * B * kv->heads * ((size_t)D + 1) * kv->head_dim * esize(kv->dtype);
   if (knew / 16 >= (1u << 31)) return SPECDEC_E_ARG;  // kv_new units are numbered with 32-bit integers
   if (overlap(kv_new, knew, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
   p = paged_params(sd::kPagedAppend, kv, rows, B, status);

@@ -40,6 +40,10 @@ def test_version_and_workspace_size():
     L = S.lib()
     assert L.specdec_workspace_bytes(16, 5) >= 16 * 6 * 8 + 16 * 4
     assert L.specdec_workspace_bytes(-1, 5) == 0
+    # sizes the verification rejects report 0 instead of a wrapped byte count
+    assert L.specdec_workspace_bytes(16, 256) == 0
+    assert L.specdec_workspace_bytes(2**31 - 1, 2**31 - 1) == 0
+    assert L.specdec_workspace_bytes(1 << 16, 255) == (1 << 16) * 257 * 128
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation on the host
@@ -59,6 +63,8 @@ def test_verify_greedy_host_errors():
 
     assert call(B=-1) == S.E_ARG
     assert call(D=-1) == S.E_ARG
+    assert call(D=256) == S.E_ARG
+    assert call(D=2**31 - 1) == S.E_ARG
     assert call(V=0) == S.E_ARG
     assert call(rs=99) == S.E_ARG
     assert call(dt=7) == S.E_DTYPE
@@ -106,6 +112,10 @@ def test_realign_host_errors():
     assert call(S.GATHER, src, _sb(kv=FAKE * 2000, rows=3), group=2) == S.E_ARG
     assert call(S.APPEND_INPLACE, src, dst) == S.E_ARG                         # not the same pool
     assert call(S.APPEND_INPLACE, src, src, kv_new=None) == S.E_ARG
+    # the largest draft counts are rejected, never wrapped into a small size
+    for mode in (S.EQSPEC, S.EQSPEC_INPLACE, S.APPEND_INPLACE):
+        assert call(mode, src, dst if mode == S.EQSPEC else src, D=2**31 - 1) == S.E_ARG
+        assert call(mode, src, dst if mode == S.EQSPEC else src, D=2**27) == S.E_ARG
 
 
 def test_group_by_len_host_errors():
