@@ -109,6 +109,29 @@ def test_inplace_random(sd, seed):
     _check_inplace(sd, kv, tok, pos, mask, lens, S, kv_new, acc, draft, nxt, tdt, pad_token=int(seed % 3))
 
 
+@pytest.mark.parametrize("shape", [
+    # B, D, L, H, Dh, dtype, cap: the largest batch (one row per thread of the
+    # prologue), the widest position, an odd number of 16-byte units, no drafts
+    (1024, 3, 1, 2, 8, np.float16, 14),
+    (3, 2, 1, 1, 1024, np.float32, 10),
+    (5, 4, 2, 3, 96, np.float16, 40),
+    (7, 0, 1, 2, 8, np.float32, 9),
+])
+def test_inplace_limits(sd, shape):
+    B, D, L, H, Dh, dt_np, cap = shape
+    tdt = torch.float16 if dt_np == np.float16 else torch.float32
+    rng = np.random.default_rng(7 * B + Dh)
+    lens = rng.integers(0, cap - D - 1, B).astype(np.int32)
+    S = int(lens.max())
+    say("inplace limits", shape)
+    kv, tok, pos, mask = _rect(rng, B, L, H, Dh, dt_np, lens, S, cap)
+    kv_new = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(dt_np)
+    acc = rng.integers(0, D + 1, B).astype(np.int32)
+    draft = rng.integers(1, 500, (B, D)).astype(np.int32)
+    nxt = rng.integers(1, 500, B).astype(np.int32)
+    _check_inplace(sd, kv, tok, pos, mask, lens, S, kv_new, acc, draft, nxt, tdt)
+
+
 def test_inplace_long_token_rows(sd):
     """Rows of several chunks of token ids (a chunk is 4 ids per thread of a
     1024-thread workgroup), both move directions."""

@@ -172,6 +172,22 @@ def test_random_small(sd, seed):
     check_round(h_t, h_d, draft, u_acc, u_draw, T, acc, nxt)
 
 
+@pytest.mark.parametrize("shape", [(2, 255, 40), (600, 1, 300), (1, 255, 4100)])
+def test_longest_draft_and_many_rows(sd, shape):
+    """D = 255 (the longest draft; 511 rows of statistics per batch entry),
+    many batch entries, and D = 255 with two splits of logits per row."""
+    B, D, V = shape
+    rng = np.random.default_rng(B + D + V)
+    say("sample logits limits", shape)
+    tl = (rng.standard_normal((B, D + 1, V)) * 2).astype(np.float32)
+    dl = (tl[:, :D] + rng.standard_normal((B, D, V)) * 0.3).astype(np.float32)
+    draft = dl.argmax(-1).astype(np.int32)  # mostly accepted, so long prefixes are judged
+    u_acc = (rng.random((B, D)) * 0.9).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt = _run(sd, tl, dl, draft, u_acc, u_draw, 1.0, torch.float32)
+    check_round(tl, dl, draft, u_acc, u_draw, 1.0, acc, nxt)
+
+
 def test_large_vocab_bf16(sd):
     """A 151936-entry bf16 vocabulary (38 splits)."""
     rng = np.random.default_rng(71)

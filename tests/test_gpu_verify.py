@@ -67,7 +67,7 @@ def test_greedy_ties_signed_zero_and_infinities(sd, enc):
 
 @pytest.mark.parametrize("enc", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 0, 1), (1, 0, 7), (3, 2, 9), (5, 4, 1000), (2, 6, 4099), (7, 3, 70001),
-                                   (1, 0, 196608), (120, 4, 3001), (100, 5, 20480)])
+                                   (1, 0, 196608), (120, 4, 3001), (100, 5, 20480), (40000, 3, 7)])
 def test_greedy_discrete_random(sd, enc, shape):
     """Logits drawn from a few values (many exact ties, -0 and +0), odd V, a
     ragged last vector, several workgroups per row, many rows."""
