@@ -48,12 +48,11 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_by_len(GroupParams p) {
   const int tot = s_tot;
   for (int i = threadIdx.x; i < N; i += kGroupThreads) {
     const int li = s_len[i];
-    int lt = 0, eq = 0, eqb = 0, fb = 0;  // fb: full members ranked before i
+    int lt = 0, eqb = 0, fb = 0;  // fb: full members ranked before i
     for (int j = 0; j < N; ++j) {
       const int lj = s_len[j];
       const int less = lj < li, e = lj == li;
       lt += less;
-      eq += e;
       eqb += e & (j < i);
       fb += s_full[j] & (less | (e & (j < i)));
     }

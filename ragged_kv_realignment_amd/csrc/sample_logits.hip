@@ -566,7 +566,6 @@ __global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
   __shared__ double s_part[2 * kSlMaxSplits];
   __shared__ double s_base, s_target;
   __shared__ int s_split, s_flags;  // flags: 1 draw from p, 2 no crossing (take the last positive id), 4 zero mass
-  __shared__ int s_run;
   const int b = blockIdx.x, D = p.D, V = p.V, S = p.S;
   const int a = p.stop[b];
   const double *part = p.part + (int64_t)b * S * 2;

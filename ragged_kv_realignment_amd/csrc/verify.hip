@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
   const int b = blockIdx.x;
   const int D = p.D, D1 = p.D + 1, V = p.V;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  __shared__ int s_a, s_bad, s_run, s_last;
+  __shared__ int s_a, s_bad, s_last;
   __shared__ double s_wt[NW];
   __shared__ int s_i[NW];
   if (threadIdx.x == 0) {
