@@ -109,3 +109,18 @@ def test_round_bytes_paged_counts_written_slots():
     kv_part = 2 * cfg.kv_pos_bytes * np.array(written, dtype=np.float64)
     meta = pb - kv_part
     assert np.all(meta > 0) and np.all(meta < 1e6)
+
+
+def test_cpu_baseline_reports_both_oracle_builds():
+    """The benchmark's CPU leg on the tiny workload: the single-threaded
+    oracle's rate as the value (one core), the OpenMP build's beside it, and
+    the threaded build switched off again afterwards."""
+    cfg = synth.CONFIGS["tiny"]
+    lens = synth.lengths(cfg)
+    S = int(lens.max())
+    tok, pos, mask = synth.tokens_host(cfg, lens, S, True)
+    plans = [synth.plan_greedy(cfg, r) for r in range(3)]
+    cpu = bench.cpu_baseline(cfg, plans, lens, S, tok, mask, 3, cfg.L)
+    assert cpu["value"] > 0 and cpu["cores"] == 1 and cpu["kind"] == "oracle" and cpu["unit"] == "rounds/s"
+    assert cpu["all_cores"]["value"] > 0 and cpu["all_cores"]["cores"] >= 1
+    assert oracle.threads() == 1
