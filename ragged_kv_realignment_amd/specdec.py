@@ -103,6 +103,19 @@ def _need(t, name, dtype=None, cuda=True):
     return t
 
 
+def _out(t, name, n, dtype=torch.int32, device=None):
+    """A caller-supplied output (or None): a contiguous device tensor of `dtype`
+    with room for n elements, on `device` when given."""
+    if t is None:
+        return None
+    _need(t, name, dtype)
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if t.numel() < n:
+        raise ValueError("%s needs at least %d elements, has %d" % (name, n, t.numel()))
+    return t
+
+
 def _check(rc, where):
     if rc != OK:
         raise SpecDecError(rc, where)
@@ -147,8 +160,10 @@ def specdec_verify_greedy(logits, draft, ws=None, status=None, accept_len=None, 
         raise ValueError("draft must be [B, D]")
     dev = logits.device
     ws = workspace(B, D, dev) if ws is None else ws
-    accept_len = _i32(B, dev) if accept_len is None else accept_len
-    next_token = _i32(B, dev) if next_token is None else next_token
+    accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
+    next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
+    _out(target_tok, "target_tok", B * D1, device=dev)
+    _out(status, "status", 1, device=dev)
     rc = lib().specdec_verify_greedy(logits.data_ptr(), _TORCH_DT[logits.dtype], row_stride, B, D, V, _ptr(draft),
                                      _ptr(accept_len), _ptr(next_token), _ptr(target_tok), ws.data_ptr(),
                                      ws.numel(), _ptr(status), _stream())
@@ -170,8 +185,9 @@ def specdec_verify_sample(p, q, draft, u_accept, u_draw, status=None, accept_len
             tuple(u_draw.shape) != (B, D1):
         raise ValueError("shape mismatch between p, q, draft and the uniforms")
     dev = p.device
-    accept_len = _i32(B, dev) if accept_len is None else accept_len
-    next_token = _i32(B, dev) if next_token is None else next_token
+    accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
+    next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
+    _out(status, "status", 1, device=dev)
     rc = lib().specdec_verify_sample(p.data_ptr(), q.data_ptr(), B, D, V, draft.data_ptr(), u_accept.data_ptr(),
                                      u_draw.data_ptr(), _ptr(accept_len), _ptr(next_token), _ptr(status), _stream())
     _check(rc, "specdec_verify_sample")
@@ -204,8 +220,9 @@ def specdec_verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, 
         raise ValueError("shape mismatch between the logits, draft and the uniforms")
     dev = target.device
     ws = sample_workspace(B, D, V, dev) if ws is None else ws
-    accept_len = _i32(B, dev) if accept_len is None else accept_len
-    next_token = _i32(B, dev) if next_token is None else next_token
+    accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
+    next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
+    _out(status, "status", 1, device=dev)
     if cutoff is not None:
         _need(cutoff, "cutoff", torch.float32)
         if cutoff.numel() != B * (2 * D + 1):
@@ -285,6 +302,7 @@ def specdec_realign_kv(mode, src, dst, rows=None, B=None, group=0, skip_group=No
                         (rows, "rows", (B,))):
         if t is not None and tuple(t.shape) != shape:
             raise ValueError("%s must have shape %s" % (n, shape))
+    _out(status, "status", 1)
     if mode == GATHER:
         ng = (B + group - 1) // max(group, 1)
         if skip_group is not None and skip_group.numel() < ng:
@@ -332,10 +350,10 @@ def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_un
     N = lens.numel() if ids is None else ids.numel()
     nb = (N + group - 1) // group if group > 0 else 0
     dev = lens.device
-    order = _i32(N, dev) if order is None else order
-    uniform = _i32(max(nb, 1), dev) if uniform is None else uniform
-    width = _i32(max(nb, 1), dev) if width is None else width
-    n_uniform = _i32(1, dev) if n_uniform is None else n_uniform
+    order = _i32(N, dev) if order is None else _out(order, "order", N, device=dev)
+    uniform = _i32(max(nb, 1), dev) if uniform is None else _out(uniform, "uniform", nb, device=dev)
+    width = _i32(max(nb, 1), dev) if width is None else _out(width, "width", nb, device=dev)
+    n_uniform = _i32(1, dev) if n_uniform is None else _out(n_uniform, "n_uniform", 1, device=dev)
     if ids is None:
         rc = lib().specdec_group_by_len(lens.data_ptr(), N, group, order.data_ptr(), uniform.data_ptr(),
                                         width.data_ptr(), n_uniform.data_ptr(), _stream())
@@ -437,6 +455,8 @@ def paged_append(cache, kv_new, draft, accept_len, next_token, rows=None, pad_to
                 _need(t, n, dt)
                 if tuple(t.shape) != tuple(rect_tokens.shape):
                     raise ValueError("%s must match rect_tokens' shape" % n)
+    _out(width, "width", 1)
+    _out(status, "status", 1)
     rc = lib().specdec_paged_append(C.byref(cache.c), _ptr(rows), B, D, kv_new.data_ptr(), _ptr(draft),
                                     accept_len.data_ptr(), next_token.data_ptr(), pad_token, _ptr(width),
                                     _ptr(rect_tokens), _ptr(rect_pos), _ptr(rect_mask), rect_cap, _ptr(status),
@@ -451,6 +471,7 @@ def paged_gather(cache, out, rows=None, pad_token=0, status=None):
         _need(rows, "rows", torch.int32)
         if rows.numel() != B:
             raise ValueError("rows must name one pool row per rectangle row")
+    _out(status, "status", 1)
     rc = lib().specdec_paged_gather(C.byref(cache.c), _ptr(rows), B, C.byref(out.c), pad_token, _ptr(status),
                                     _stream())
     _check(rc, "specdec_paged_gather")
@@ -463,6 +484,7 @@ def paged_admit(cache, rect, rows=None, status=None):
         _need(rows, "rows", torch.int32)
         if rows.numel() != B:
             raise ValueError("rows must name one pool row per rectangle row")
+    _out(status, "status", 1)
     rc = lib().specdec_paged_admit(C.byref(cache.c), _ptr(rows), B, C.byref(rect.c), _ptr(status), _stream())
     _check(rc, "specdec_paged_admit")
 
@@ -470,6 +492,7 @@ def paged_admit(cache, rect, rows=None, status=None):
 def paged_retire(cache, rows, status=None):
     """The listed rows return their pages to the free stack and become empty."""
     _need(rows, "rows", torch.int32)
+    _out(status, "status", 1)
     rc = lib().specdec_paged_retire(C.byref(cache.c), rows.data_ptr(), rows.numel(), _ptr(status), _stream())
     _check(rc, "specdec_paged_retire")
 
@@ -510,8 +533,9 @@ def pool_finish(pool, sched, rows, accept_len, D, eos_id, max_len, retired=None,
     if accept_len.numel() != B:
         raise ValueError("rows and accept_len must have one entry per batch entry")
     dev = pool.kv.device
-    retired = _i32(pool.rows, dev) if retired is None else retired
-    n_retired = _i32(1, dev) if n_retired is None else n_retired
+    retired = _i32(pool.rows, dev) if retired is None else _out(retired, "retired", pool.rows, device=dev)
+    n_retired = _i32(1, dev) if n_retired is None else _out(n_retired, "n_retired", 1, device=dev)
+    _out(status, "status", 1, device=dev)
     rc = lib().specdec_pool_finish(C.byref(pool.c), C.byref(sched.c), rows.data_ptr(), accept_len.data_ptr(), B, D,
                                    eos_id, max_len, retired.data_ptr(), n_retired.data_ptr(), _ptr(status), _stream())
     _check(rc, "specdec_pool_finish")
@@ -522,8 +546,9 @@ def pool_admit(pool, sched, queue, admitted=None, n_admitted=None, status=None):
     """Admit queued prompts (a SeqBuf of left-aligned prompts) into the lowest free rows.
     Returns (admitted, n_admitted) device tensors."""
     dev = pool.kv.device
-    admitted = _i32(pool.rows, dev) if admitted is None else admitted
-    n_admitted = _i32(1, dev) if n_admitted is None else n_admitted
+    admitted = _i32(pool.rows, dev) if admitted is None else _out(admitted, "admitted", pool.rows, device=dev)
+    n_admitted = _i32(1, dev) if n_admitted is None else _out(n_admitted, "n_admitted", 1, device=dev)
+    _out(status, "status", 1, device=dev)
     rc = lib().specdec_pool_admit(C.byref(pool.c), C.byref(sched.c), C.byref(queue.c), admitted.data_ptr(),
                                   n_admitted.data_ptr(), _ptr(status), _stream())
     _check(rc, "specdec_pool_admit")

@@ -266,3 +266,30 @@ def test_greedy_longest_draft(sd):
     assert np.array_equal(tgt, otgt) and np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
     with pytest.raises(sd.SpecDecError):  # D = 256 is past the limit
         _gpu_greedy(sd, np.zeros((2 * 257, V), np.float32), torch.float32, 2, 256, V, np.zeros((2, 256), np.int32))
+
+
+def test_caller_outputs_are_checked_before_launch(sd):
+    """Outputs the caller supplies must be int32 (float32 for the cutoff),
+    contiguous, on the logits' device and large enough: otherwise the binding
+    raises before anything is launched, so no kernel writes past them."""
+    say("caller outputs checked")
+    B, D, V = 4, 3, 64
+    logits = torch.zeros((B, D + 1, V), dtype=torch.float32, device="cuda")
+    draft = torch.zeros((B, D), dtype=torch.int32, device="cuda")
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32, device="cuda")
+    bad = [dict(accept_len=i32(B - 1)), dict(next_token=i32(B - 1)), dict(target_tok=i32(B * (D + 1) - 1)),
+           dict(status=torch.zeros(1, dtype=torch.float32, device="cuda")), dict(status=i32(0)),
+           dict(accept_len=torch.zeros(B, dtype=torch.int64, device="cuda")),
+           dict(next_token=i32(2 * B)[::2]), dict(accept_len=torch.zeros(B, dtype=torch.int32))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            sd.verify_greedy(logits, draft, **kw)
+    acc, nxt = sd.verify_greedy(logits, draft, accept_len=i32(B), next_token=i32(B + 3), status=i32(1))
+    torch.cuda.synchronize()
+    assert acc.shape == (B,) and np.array_equal(acc.cpu().numpy(), np.full(B, D))  # all-equal rows: id 0 wins
+    with pytest.raises(ValueError):
+        sd.group_by_len(i32(16), 4, order=i32(15))
+    with pytest.raises(ValueError):
+        sd.verify_sample(torch.zeros((B, D + 1, V), device="cuda"), torch.zeros((B, D, V), device="cuda"), draft,
+                         torch.zeros((B, D), device="cuda"), torch.zeros((B, D + 1), device="cuda"),
+                         accept_len=i32(1))
