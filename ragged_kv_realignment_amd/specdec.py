@@ -254,8 +254,15 @@ class SeqBuf:
                 if tuple(t.shape) != (rows, cap):
                     raise ValueError("%s must be [rows, cap]" % n)
         _need(len, "len", torch.int32)
+        if len.numel() != rows:
+            raise ValueError("len must hold one length per row")
         if width is not None:
             _need(width, "width", torch.int32)
+            if width.numel() < 1:
+                raise ValueError("width needs at least one entry")
+        for t in (tokens, len, pos, mask, width):
+            if t is not None and t.device != kv.device:
+                raise ValueError("every tensor of a SeqBuf must be on the KV's device")
         self.c = SeqBufC(kv.data_ptr(), _ptr(tokens), _ptr(pos), _ptr(mask), len.data_ptr(), _ptr(width), rows, cap,
                          L, H, Dh, _TORCH_DT[kv.dtype])
 

@@ -270,8 +270,9 @@ def test_greedy_longest_draft(sd):
 
 def test_caller_outputs_are_checked_before_launch(sd):
     """Outputs the caller supplies must be int32 (float32 for the cutoff),
-    contiguous, on the logits' device and large enough: otherwise the binding
-    raises before anything is launched, so no kernel writes past them."""
+    contiguous, on the logits' device and large enough, and a SeqBuf's lengths
+    and width must fit its rows: otherwise the binding raises before anything
+    is launched, so no kernel reads or writes past them."""
     say("caller outputs checked")
     B, D, V = 4, 3, 64
     logits = torch.zeros((B, D + 1, V), dtype=torch.float32, device="cuda")
@@ -293,3 +294,11 @@ def test_caller_outputs_are_checked_before_launch(sd):
         sd.verify_sample(torch.zeros((B, D + 1, V), device="cuda"), torch.zeros((B, D, V), device="cuda"), draft,
                          torch.zeros((B, D), device="cuda"), torch.zeros((B, D + 1), device="cuda"),
                          accept_len=i32(1))
+    kv = torch.zeros((1, 2, 3, 1, 8, 8), dtype=torch.float16, device="cuda")
+    tok = torch.zeros((3, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):  # one length per row
+        sd.SeqBuf(kv, tok, i32(2))
+    with pytest.raises(ValueError):  # an empty width
+        sd.SeqBuf(kv, tok, i32(3), width=i32(0))
+    with pytest.raises(ValueError):  # lengths on the host
+        sd.SeqBuf(kv, tok, torch.zeros(3, dtype=torch.int32))
