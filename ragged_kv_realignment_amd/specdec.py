@@ -159,7 +159,7 @@ def specdec_verify_greedy(logits, draft, ws=None, status=None, accept_len=None, 
     if tuple(draft.shape) != (B, D):
         raise ValueError("draft must be [B, D]")
     dev = logits.device
-    ws = workspace(B, D, dev) if ws is None else ws
+    ws = workspace(B, D, dev) if ws is None else _out(ws, "ws", 1, torch.uint8, device=dev)
     accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
     next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
     _out(target_tok, "target_tok", B * D1, device=dev)
@@ -219,7 +219,7 @@ def specdec_verify_sample_logits(target, draft_logits, draft, u_accept, u_draw, 
             tuple(u_accept.shape) != (B, D) or tuple(u_draw.shape) != (B, D1):
         raise ValueError("shape mismatch between the logits, draft and the uniforms")
     dev = target.device
-    ws = sample_workspace(B, D, V, dev) if ws is None else ws
+    ws = sample_workspace(B, D, V, dev) if ws is None else _out(ws, "ws", 1, torch.uint8, device=dev)
     accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
     next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
     _out(status, "status", 1, device=dev)
