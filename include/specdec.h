@@ -32,6 +32,10 @@
  *    that sets CAPACITY or LEN_RANGE writes none of its outputs.
  *  - Results are deterministic: identical inputs give identical bytes.
  *  - Calls on different streams must not share output buffers or workspaces.
+ *  - An empty batch (B = 0, or a rectangle of 0 rows) is a no-op after the
+ *    checks of the call's persistent structures: nothing is written.  A buffer
+ *    holding no bytes may be passed as NULL (a zero-size tensor has no
+ *    address).
  */
 #ifndef SPECDEC_H
 #define SPECDEC_H
@@ -327,6 +331,7 @@ int specdec_pool_finish(const specdec_seqbuf_t *pool, const specdec_sched_t *sch
  * *n_admitted (device) k.  Device conditions (nothing admitted, *n_admitted =
  * 0): a prompt longer than pool->cap sets SPECDEC_S_CAPACITY; inconsistent
  * counts or lengths outside [0, queue->cap] SPECDEC_S_LEN_RANGE.
+ * An empty queue (queue->rows = 0) admits nothing.
  * Limits: pool->rows <= 4096.  Errors: E_ARG, E_DTYPE, E_ALIGN, E_ALIAS,
  * E_LAUNCH. */
 int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_t *sched, const specdec_seqbuf_t *queue,

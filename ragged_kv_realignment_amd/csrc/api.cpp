@@ -35,9 +35,11 @@ size_t kv_bytes(const specdec_seqbuf_t *s) {
 size_t ws_keys_bytes(int B, int D) { return (size_t)B * ((size_t)D + 1) * sd::kAtomicLine; }
 
 int check_seqbuf_shape(const specdec_seqbuf_t *s) {
-  if (!s || !s->kv || !s->len) return SPECDEC_E_ARG;
+  if (!s) return SPECDEC_E_ARG;
   if (s->rows < 0 || s->cap < 0 || s->layers < 0 || s->heads < 1 || s->head_dim < 1) return SPECDEC_E_ARG;
   if (!dtype_ok(s->dtype)) return SPECDEC_E_DTYPE;
+  // an empty buffer may come without an address (a zero-size tensor has none)
+  if ((!s->kv && kv_bytes(s) > 0) || (!s->len && s->rows > 0)) return SPECDEC_E_ARG;
   if (((size_t)s->head_dim * esize(s->dtype)) % 16 != 0) return SPECDEC_E_ALIGN;
   if (reinterpret_cast<uintptr_t>(s->kv) % 16 != 0) return SPECDEC_E_ALIGN;
   return SPECDEC_OK;
@@ -244,10 +246,10 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
   const size_t tok_in_bytes = (size_t)in->rows * in->cap * 4, tok_out_bytes = (size_t)out->rows * out->cap * 4;
   if (mode == SPECDEC_EQSPEC) {
     if (in->rows != B || out->rows != B) return SPECDEC_E_ARG;
+    if (B == 0) return kNothing;
     if (!in->tokens || !in->width || !out->tokens || !out->pos || !out->mask || !out->width) return SPECDEC_E_ARG;
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-    if (B == 0) return kNothing;
     const size_t kin = kv_bytes(in), kout = kv_bytes(out);
     const size_t knew = (size_t)in->layers * 2 * B * in->heads * ((size_t)D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(in->kv, kin, out->kv, kout) || overlap(kv_new, knew, out->kv, kout)) return SPECDEC_E_ALIAS;
@@ -264,10 +266,10 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
     p.width_out = out->width;
   } else if (mode == SPECDEC_EQSPEC_INPLACE) {
     if (in->rows != B || !same_buffers(in, out)) return SPECDEC_E_ARG;
+    if (B == 0) return kNothing;
     if (!in->tokens || !in->pos || !in->mask || !in->width) return SPECDEC_E_ARG;
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-    if (B == 0) return kNothing;
     const size_t knew = (size_t)in->layers * 2 * B * in->heads * ((size_t)D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
     if (overlap(accept_len, B * 4u, in->len, B * 4u) || overlap(next_token, B * 4u, in->tokens, tok_in_bytes) ||
@@ -298,9 +300,9 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
     if (in->kv != out->kv || in->len != out->len || in->tokens != out->tokens || in->rows != out->rows ||
         in->cap != out->cap)
       return SPECDEC_E_ARG;
+    if (B == 0) return kNothing;
     if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
     if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-    if (B == 0) return kNothing;
     const size_t knew = (size_t)in->layers * 2 * B * in->heads * ((size_t)D + 1) * in->head_dim * esize(in->dtype);
     if (overlap(kv_new, knew, in->kv, kv_bytes(in))) return SPECDEC_E_ALIAS;
     p.tok_in = in->tokens;
@@ -397,10 +399,10 @@ static int paged_append_prepare(const specdec_paged_t *kv, const int32_t *rows, 
   int rc = check_paged(kv);
   if (rc) return rc;
   if (B < 0 || B > sd::kMaxRealignRows || D < 0 || D > 255) return SPECDEC_E_ARG;
+  if (B == 0) return kNothing;
   if (!kv_new || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
   if ((rect_tokens || rect_pos || rect_mask) && (!rect_tokens || rect_cap < 1)) return SPECDEC_E_ARG;
   if (reinterpret_cast<uintptr_t>(kv_new) % 16 != 0) return SPECDEC_E_ALIGN;
-  if (B == 0) return kNothing;
   const size_t knew = (size_t)kv->layers * 2 * B * kv->heads * ((size_t)D + 1) * kv->head_dim * esize(kv->dtype);
   if (knew / 16 >= (1u << 31)) return SPECDEC_E_ARG;  // kv_new units are numbered with 32-bit integers
   if (overlap(kv_new, knew, kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
@@ -437,8 +439,8 @@ EXPORT int specdec_paged_gather(const specdec_paged_t *kv, const int32_t *rows, 
   rc = check_seqbuf_shape(out);
   if (rc) return rc;
   if (B < 0 || B > sd::kMaxRealignRows || out->rows != B || !paged_matches(kv, out)) return SPECDEC_E_ARG;
-  if (!out->tokens || !out->width || out->cap < 1) return SPECDEC_E_ARG;
   if (B == 0) return SPECDEC_OK;
+  if (!out->tokens || !out->width || out->cap < 1) return SPECDEC_E_ARG;
   if (overlap(out->kv, kv_bytes(out), kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
   sd::PagedParams p = paged_params(sd::kPagedGather, kv, rows, B, status);
   p.pad_token = pad_token;
@@ -459,8 +461,8 @@ EXPORT int specdec_paged_admit(const specdec_paged_t *kv, const int32_t *rows, i
   rc = check_seqbuf_shape(in);
   if (rc) return rc;
   if (B < 0 || B > sd::kMaxRealignRows || in->rows != B || !paged_matches(kv, in)) return SPECDEC_E_ARG;
-  if (!in->tokens || !in->width) return SPECDEC_E_ARG;
   if (B == 0) return SPECDEC_OK;
+  if (!in->tokens || !in->width) return SPECDEC_E_ARG;
   if (overlap(in->kv, kv_bytes(in), kv->pages, paged_bytes(kv))) return SPECDEC_E_ALIAS;
   sd::PagedParams p = paged_params(sd::kPagedAdmit, kv, rows, B, status);
   p.rect_kv = in->kv;
@@ -551,7 +553,8 @@ EXPORT int specdec_pool_admit(const specdec_seqbuf_t *pool, const specdec_sched_
   if (rc) return rc;
   rc = check_seqbuf_shape(queue);
   if (rc) return rc;
-  if (!sched_ok(sched) || !pool->tokens || !queue->tokens || !admitted || !n_admitted) return SPECDEC_E_ARG;
+  if (!sched_ok(sched) || !pool->tokens || (!queue->tokens && queue->rows > 0) || !admitted || !n_admitted)
+    return SPECDEC_E_ARG;
   if (pool->rows < 1 || pool->rows > sd::kMaxPoolSlots || queue->cap < 1 || !same_geometry(pool, queue))
     return SPECDEC_E_ARG;
   if (overlap(queue->kv, kv_bytes(queue), pool->kv, kv_bytes(pool))) return SPECDEC_E_ALIAS;
