@@ -1,8 +1,7 @@
-"""Chained rounds of greedy verification + paged append captured in a HIP
-graph: every replay, with the program's own eager work (a reset of the
-cache) and synchronisations between replays, reproduces the eager rounds byte
-for byte (accepted lengths, next tokens, pages, block table, free stack,
-token ids, lengths and the rectangle view)."""
+"""Chained rounds captured in one HIP graph (greedy verification + paged
+append; greedy verification + in-place realignment): every replay, with the
+program's own eager work (a reset of the cache) and synchronisations between
+replays, reproduces the eager rounds byte for byte."""
 import numpy as np
 import pytest
 import torch
@@ -96,4 +95,78 @@ def test_paged_rounds_graph_replays(sd):
             assert torch.equal(x, y), (rep, i)
         assert bytes_equal(got[1], want[1]), rep
         assert torch.equal(got[2], want[2]), rep
+    assert int(status.item()) == 0
+
+
+def test_inplace_rounds_graph_replays(sd):
+    """Chained rounds of greedy verification + in-place EQSPEC realignment of a
+    left-padded rectangle captured in one HIP graph: every replay, with an
+    eager reset of the rectangle and synchronisations between replays,
+    reproduces the eager rounds byte for byte (accepted lengths, next tokens,
+    KV, token ids, position ids, mask, lengths and width)."""
+    rng = np.random.default_rng(1900)
+    B, D, V, L, H, Dh, R = 12, 4, 5000, 2, 2, 64, 10
+    lens = rng.integers(20, 300, B).astype(np.int32)
+    S = int(lens.max())
+    cap = S + R * (D + 1)
+    say("graph replay in place", B, D, V, R)
+    kv = np.zeros((L, 2, B, H, cap, Dh), np.float16)
+    tok = np.zeros((B, cap), np.int32)
+    pos = np.zeros((B, cap), np.int32)
+    mask = np.zeros((B, cap), np.int8)
+    for b in range(B):
+        kv[:, :, b, :, S - lens[b]:S] = rng.standard_normal((L, 2, H, lens[b], Dh))
+        tok[b, S - lens[b]:S] = rng.integers(1, V, lens[b])
+        pos[b, S - lens[b]:S] = np.arange(lens[b])
+        mask[b, S - lens[b]:S] = 1
+    buf = sd.SeqBuf(torch.from_numpy(kv).cuda(), torch.from_numpy(tok).cuda(), torch.from_numpy(lens).cuda(),
+                    torch.from_numpy(pos).cuda(), torch.from_numpy(mask).cuda(),
+                    torch.tensor([S], dtype=torch.int32, device="cuda"))
+    logits = torch.from_numpy(rng.standard_normal((R, B, D + 1, V)).astype(np.float32)).cuda()
+    drafts = rng.integers(0, V, (R, B, D)).astype(np.int32)
+    am = logits.argmax(-1).cpu().numpy()
+    for r in range(R):
+        for b in range(B):
+            k = int(rng.integers(0, D + 1))
+            drafts[r, b, :k] = am[r, b, :k]
+    drafts = torch.from_numpy(drafts).cuda()
+    kv_new = torch.from_numpy(rng.standard_normal((R, L, 2, B, H, D + 1, Dh)).astype(np.float16)).cuda()
+    ws = sd.workspace(B, D)
+    acc = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    nxt = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    names = ("kv", "tokens", "pos", "mask", "len", "width")
+    initial = {k: getattr(buf, k).clone() for k in names}
+
+    def reset():  # eager work between replays: the rectangle back to its first state
+        for k in names:
+            getattr(buf, k).copy_(initial[k])
+        torch.cuda.synchronize()
+
+    def rounds():
+        for r in range(R):
+            sd.verify_greedy(logits[r], drafts[r], ws=ws, status=status, accept_len=acc[r], next_token=nxt[r])
+            sd.realign_eqspec_inplace(buf, kv_new[r], drafts[r], acc[r], nxt[r], status=status)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (acc, nxt, buf.tokens, buf.pos, buf.mask, buf.len, buf.width)], to_np_raw(buf.kv)
+
+    reset()
+    rounds()
+    want = snapshot()
+    assert int(status.item()) == 0 and int(want[0][0].sum()) > 0  # some drafts were accepted
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rounds()
+    for rep in range(3):
+        reset()
+        acc.zero_()
+        nxt.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for i, (x, y) in enumerate(zip(got[0], want[0])):
+            assert torch.equal(x, y), (rep, i)
+        assert bytes_equal(got[1], want[1]), rep
     assert int(status.item()) == 0
