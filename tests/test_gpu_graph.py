@@ -170,3 +170,46 @@ def test_inplace_rounds_graph_replays(sd):
             assert torch.equal(x, y), (rep, i)
         assert bytes_equal(got[1], want[1]), rep
     assert int(status.item()) == 0
+
+
+def test_sample_logits_graph_replays(sd):
+    """Sampled verification from logits with a top-p nucleus, three calls
+    captured in one HIP graph: every replay gives the eager accepted lengths,
+    next tokens and nucleus thresholds (the workspace holds nothing between
+    calls, so no clearing is captured)."""
+    rng = np.random.default_rng(2000)
+    B, D, V, R = 6, 3, 9000, 3
+    say("graph replay sampled from logits", B, D, V, R)
+    tl = torch.from_numpy((rng.standard_normal((R, B, D + 1, V)) * 2).astype(np.float32)).cuda()
+    dl = (tl[:, :, :D] + torch.from_numpy((rng.standard_normal((R, B, D, V)) * 0.5).astype(np.float32)).cuda())
+    dl = dl.contiguous()
+    draft = dl.argmax(-1).to(torch.int32).contiguous()
+    u_acc = torch.from_numpy(rng.random((R, B, D)).astype(np.float32)).cuda()
+    u_draw = torch.from_numpy(rng.random((R, B, D + 1)).astype(np.float32)).cuda()
+    ws = sd.sample_workspace(B, D, V)
+    acc = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    nxt = torch.zeros((R, B), dtype=torch.int32, device="cuda")
+    cut = torch.zeros((R, B * (2 * D + 1)), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def calls():
+        for r in range(R):
+            sd.verify_sample_logits(tl[r], dl[r], draft[r], u_acc[r], u_draw[r], 0.8, top_p=0.9, ws=ws,
+                                    status=status, accept_len=acc[r], next_token=nxt[r], cutoff=cut[r])
+
+    calls()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (acc, nxt, cut)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        for t in (acc, nxt, cut):
+            t.zero_()
+        ws.fill_(0x5A)  # eager work between replays that disturbs the workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip((acc, nxt, cut), want)):
+            assert torch.equal(x, y), (rep, i)
+    assert int(status.item()) == 0
