@@ -65,7 +65,9 @@ __device__ __forceinline__ float logit_at(const void *base, int64_t i) {
 }
 
 // exp(y) for y <= 0 in fp64 (-inf, and anything below -745, give 0; NaN stays
-// NaN): 2^k * 2^(j/64) * e^r with n = rint(64 y / ln 2), j = n mod 64,
+// NaN), by P. T. P. Tang's table-driven method ("Table-driven implementation
+// of the exponential function in IEEE floating-point arithmetic", ACM TOMS
+// 15(2), 1989): 2^k * 2^(j/64) * e^r with n = rint(64 y / ln 2), j = n mod 64,
 // k = (n - j) / 64 and r = y - n (ln 2 / 64), |r| <= ln 2 / 128, formed with
 // two fused multiply-adds on a two-part constant; e^r is its degree-5 Taylor
 // polynomial (truncation below 4e-17 of the result) and 2^(j/64) comes from a

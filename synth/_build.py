@@ -8,8 +8,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB = os.path.join(HERE, "libsynth_host.so")
 DEV_LIB = os.path.join(HERE, "libsynth_dev.so")
 
-HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+HIPCC = "/opt/rocm/bin/hipcc"
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC"]
+# packed fp32 arithmetic off, for the device pass only (the host compiler does
+# not know the feature)
+DEVICE_FEATURES = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _run(cmd):
@@ -25,7 +28,13 @@ def build_host():
 
 
 def build_device():
-    _run(["/opt/rocm/bin/hipcc", *HIP_FLAGS, "-o", DEV_LIB + ".tmp", "gen_device.hip"])
+    obj = os.path.join(HERE, "_build")
+    os.makedirs(obj, exist_ok=True)
+    fb, o = os.path.join(obj, "gen_device.fb"), os.path.join(obj, "gen_device.o")
+    _run([HIPCC, *COMMON, "--cuda-device-only", *DEVICE_FEATURES, "-c", "gen_device.hip", "-o", fb])
+    _run([HIPCC, *COMMON, "--cuda-host-only", "-Xclang", "-fcuda-include-gpubinary", "-Xclang", fb,
+          "-c", "gen_device.hip", "-o", o])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", DEV_LIB + ".tmp", o])
     os.replace(DEV_LIB + ".tmp", DEV_LIB)
 
 
