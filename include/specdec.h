@@ -61,6 +61,7 @@ extern "C" {
 #define SPECDEC_E_ALIGN (-5)     /* a KV position (head_dim * element size) is not a multiple of 16 bytes,
                                     or a KV/kv_new base pointer is not 16-byte aligned */
 #define SPECDEC_E_LAUNCH (-6)    /* the HIP runtime refused a launch */
+#define SPECDEC_E_SCRATCH (-7)   /* the call needs more workspace than the library's static scratch holds */
 
 /* device status bits */
 #define SPECDEC_S_DRAFT_RANGE 1  /* a draft id outside [0, V) (it never matches; results still written) */
@@ -113,6 +114,30 @@ int specdec_workspace_init(void *ws, size_t ws_bytes, void *stream);
 int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
                           const int32_t *draft, int32_t *accept_len, int32_t *next_token,
                           int32_t *target_tok, void *ws, size_t ws_bytes, int32_t *status, void *stream);
+
+/* Bytes of the device array that backs specdec_verify_greedy_noalloc: 4 MiB,
+ * held by every GPU the library runs on until the process ends. */
+#define SPECDEC_STATIC_SCRATCH_BYTES (4u << 20)
+
+/* Greedy verification for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid allocation):
+ * specdec_verify_greedy with its workspace taken from a device array inside
+ * the library instead of from the caller.  Arguments, results, status bits and
+ * errors are those of specdec_verify_greedy, with no ws / ws_bytes.
+ *  - The call allocates and frees nothing.  The first call on a device looks
+ *    up that device's copy of the array and clears it with a fill kernel on
+ *    `stream`; every call leaves it cleared again.
+ *  - Limit: specdec_workspace_bytes(B, D) <= SPECDEC_STATIC_SCRATCH_BYTES, i.e.
+ *    B * (D + 2) <= 32768 lines of 128 bytes; larger batches return
+ *    SPECDEC_E_SCRATCH before anything is enqueued.
+ *  - Every call on one device shares that device's array: calls that may run
+ *    at the same time on one device (different streams, or a captured graph
+ *    replayed beside an eager call) race and must be serialised by the caller.
+ * Errors: those of specdec_verify_greedy except E_WORKSPACE, plus E_SCRATCH;
+ * E_LAUNCH also when the array's address cannot be looked up. */
+int specdec_verify_greedy_noalloc(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                  const int32_t *draft, int32_t *accept_len, int32_t *next_token,
+                                  int32_t *target_tok, int32_t *status, void *stream);
 
 /* Sampled verification (speculative sampling; "Inference Engineering Part
  * 5/8", section "Exactness Means Different Things For Greedy And Sampled

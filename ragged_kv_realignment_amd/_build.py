@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspecdec.so")
 OBJ = os.path.join(HERE, "_build")
 HIP_SOURCES = ["csrc/verify.hip", "csrc/realign.hip", "csrc/realign_inplace.hip", "csrc/sample_logits.hip",
-               "csrc/group.hip", "csrc/paged.hip", "csrc/pool.hip"]
+               "csrc/group.hip", "csrc/paged.hip", "csrc/pool.hip", "csrc/scratch.hip"]
 CPP_SOURCES = ["csrc/api.cpp"]
 HIPCC = "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I" + os.path.join(ROOT, "include")]

@@ -100,6 +100,23 @@ EXPORT int specdec_verify_greedy(const void *logits, int dtype, int64_t row_stri
   return launched(sd::launch_verify_greedy(p, as_stream(stream)));
 }
 
+EXPORT int specdec_verify_greedy_noalloc(const void *logits, int dtype, int64_t row_stride, int B, int D, int V,
+                                         const int32_t *draft, int32_t *accept_len, int32_t *next_token,
+                                         int32_t *target_tok, int32_t *status, void *stream) {
+  // the argument checks of specdec_verify_greedy come first, so both calls
+  // reject the same arguments the same way; the size limit needs no HIP call
+  if (B < 0 || D < 0 || V < 1 || row_stride < V) return SPECDEC_E_ARG;
+  if (!dtype_ok(dtype)) return SPECDEC_E_DTYPE;
+  if (B == 0) return SPECDEC_OK;
+  if (!logits || !accept_len || !next_token || (D > 0 && !draft)) return SPECDEC_E_ARG;
+  if (D > 255 || (long long)B * ((long long)D + 1) > (1LL << 24) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  if (specdec_workspace_bytes(B, D) > SPECDEC_STATIC_SCRATCH_BYTES) return SPECDEC_E_SCRATCH;
+  void *ws = nullptr;
+  if (sd::static_scratch(&ws, as_stream(stream)) != hipSuccess) return SPECDEC_E_LAUNCH;
+  return specdec_verify_greedy(logits, dtype, row_stride, B, D, V, draft, accept_len, next_token, target_tok, ws,
+                               SPECDEC_STATIC_SCRATCH_BYTES, status, stream);
+}
+
 EXPORT int specdec_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
                                  const float *u_accept, const float *u_draw, int32_t *accept_len,
                                  int32_t *next_token, int32_t *status, void *stream) {

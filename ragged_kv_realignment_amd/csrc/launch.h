@@ -136,5 +136,6 @@ hipError_t launch_paged(const PagedParams &p, hipStream_t s);
 hipError_t launch_pool_finish(const PoolParams &p, hipStream_t s);
 hipError_t launch_pool_admit(const PoolParams &p, hipStream_t s);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t s);
+hipError_t static_scratch(void **out, hipStream_t s);
 
 }  // namespace sd

@@ -15,18 +15,19 @@ LIB_PATH = os.path.join(HERE, "libspecdec.so")
 
 F32, F16, BF16 = 0, 1, 2
 EQSPEC, GATHER, APPEND_INPLACE, EQSPEC_INPLACE = 0, 1, 2, 3
-OK, E_ARG, E_DTYPE, E_WORKSPACE, E_ALIAS, E_ALIGN, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+OK, E_ARG, E_DTYPE, E_WORKSPACE, E_ALIAS, E_ALIGN, E_LAUNCH, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 S_DRAFT_RANGE, S_CAPACITY, S_LEN_RANGE, S_PROB, S_ROWS_DUP = 1, 2, 4, 8, 16
 
 _ERRORS = {E_ARG: "invalid argument", E_DTYPE: "unsupported element type", E_WORKSPACE: "workspace too small",
-           E_ALIAS: "output overlaps an input", E_ALIGN: "misaligned KV buffer", E_LAUNCH: "kernel launch failed"}
+           E_ALIAS: "output overlaps an input", E_ALIGN: "misaligned KV buffer", E_LAUNCH: "kernel launch failed",
+           E_SCRATCH: "batch too large for the library's static scratch"}
 _TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init", "specdec_verify_greedy",
            "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
            "specdec_realign_kv", "specdec_group_by_len", "specdec_paged_append", "specdec_paged_gather",
            "specdec_paged_admit", "specdec_paged_retire", "specdec_group_by_len_ids", "specdec_pool_finish",
-           "specdec_pool_admit")
+           "specdec_pool_admit", "specdec_verify_greedy_noalloc")
 
 
 class SpecDecError(RuntimeError):
@@ -57,6 +58,7 @@ def lib():
         L.specdec_workspace_bytes.restype = sz
         L.specdec_workspace_init.argtypes = [vp, sz, vp]
         L.specdec_verify_greedy.argtypes = [vp, ci, i64, ci, ci, ci, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.specdec_verify_greedy_noalloc.argtypes = [vp, ci, i64, ci, ci, ci, vp, vp, vp, vp, vp, vp]
         L.specdec_verify_sample.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
         L.specdec_sample_workspace_bytes.argtypes = [ci, ci, ci]
         L.specdec_sample_workspace_bytes.restype = sz
@@ -74,7 +76,8 @@ def lib():
         L.specdec_pool_finish.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), vp, vp, ci, ci, C.c_int32, C.c_int32,
                                           vp, vp, vp, vp]
         L.specdec_pool_admit.argtypes = [C.POINTER(SeqBufC), C.POINTER(SchedC), C.POINTER(SeqBufC), vp, vp, vp, vp]
-        for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_sample",
+        for f in ("specdec_workspace_init", "specdec_verify_greedy", "specdec_verify_greedy_noalloc",
+                  "specdec_verify_sample",
                   "specdec_verify_sample_logits", "specdec_realign_kv", "specdec_group_by_len",
                   "specdec_paged_append", "specdec_paged_gather", "specdec_paged_admit", "specdec_paged_retire",
                   "specdec_group_by_len_ids", "specdec_pool_finish", "specdec_pool_admit"):
@@ -137,12 +140,8 @@ def _i32(shape, device):
     return torch.empty(shape, dtype=torch.int32, device=device)
 
 
-def specdec_verify_greedy(logits, draft, ws=None, status=None, accept_len=None, next_token=None, target_tok=None):
-    """Greedy verification of drafts [B, D] against logits [B, D+1, V].
-
-    Rows of `logits` may be strided (last dim contiguous, a uniform stride
-    between the B*(D+1) rows).  Returns (accept_len [B], next_token [B]).
-    """
+def _greedy_shape(logits, draft):
+    """(B, D, V, row_stride) of a greedy verification, after the tensor checks."""
     if logits.dtype not in _TORCH_DT or not logits.is_cuda or logits.dim() != 3:
         raise ValueError("logits must be a [B, D+1, V] float32/float16/bfloat16 device tensor")
     B, D1, V = logits.shape
@@ -158,16 +157,45 @@ def specdec_verify_greedy(logits, draft, ws=None, status=None, accept_len=None, 
     _need(draft, "draft", torch.int32)
     if tuple(draft.shape) != (B, D):
         raise ValueError("draft must be [B, D]")
+    return B, D, V, row_stride
+
+
+def specdec_verify_greedy(logits, draft, ws=None, status=None, accept_len=None, next_token=None, target_tok=None):
+    """Greedy verification of drafts [B, D] against logits [B, D+1, V].
+
+    Rows of `logits` may be strided (last dim contiguous, a uniform stride
+    between the B*(D+1) rows).  Returns (accept_len [B], next_token [B]).
+    """
+    B, D, V, row_stride = _greedy_shape(logits, draft)
     dev = logits.device
     ws = workspace(B, D, dev) if ws is None else _out(ws, "ws", 1, torch.uint8, device=dev)
     accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
     next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
-    _out(target_tok, "target_tok", B * D1, device=dev)
+    _out(target_tok, "target_tok", B * (D + 1), device=dev)
     _out(status, "status", 1, device=dev)
     rc = lib().specdec_verify_greedy(logits.data_ptr(), _TORCH_DT[logits.dtype], row_stride, B, D, V, _ptr(draft),
                                      _ptr(accept_len), _ptr(next_token), _ptr(target_tok), ws.data_ptr(),
                                      ws.numel(), _ptr(status), _stream())
     _check(rc, "specdec_verify_greedy")
+    return accept_len, next_token
+
+
+def specdec_verify_greedy_noalloc(logits, draft, accept_len, next_token, status=None, target_tok=None):
+    """Greedy verification with the library's static workspace: the caller
+    passes every output, and the call allocates nothing (no torch tensor
+    either).  Returns (accept_len, next_token)."""
+    B, D, V, row_stride = _greedy_shape(logits, draft)
+    dev = logits.device
+    _out(accept_len, "accept_len", B, device=dev)
+    _out(next_token, "next_token", B, device=dev)
+    if accept_len is None or next_token is None:
+        raise ValueError("accept_len and next_token are required")
+    _out(target_tok, "target_tok", B * (D + 1), device=dev)
+    _out(status, "status", 1, device=dev)
+    rc = lib().specdec_verify_greedy_noalloc(logits.data_ptr(), _TORCH_DT[logits.dtype], row_stride, B, D, V,
+                                             _ptr(draft), _ptr(accept_len), _ptr(next_token), _ptr(target_tok),
+                                             _ptr(status), _stream())
+    _check(rc, "specdec_verify_greedy_noalloc")
     return accept_len, next_token
 
 
@@ -373,6 +401,7 @@ def specdec_group_by_len(lens, group, order=None, uniform=None, width=None, n_un
 
 
 verify_greedy = specdec_verify_greedy
+verify_greedy_noalloc = specdec_verify_greedy_noalloc
 verify_sample = specdec_verify_sample
 verify_sample_logits = specdec_verify_sample_logits
 group_by_len = specdec_group_by_len

@@ -126,6 +126,18 @@ def test_group_by_len_host_errors():
     assert f(FAKE, 16, 8, None, FAKE, FAKE, FAKE, None) == S.E_ARG
 
 
+def test_verify_greedy_noalloc_host_errors():
+    """Rejected before any HIP call: the static scratch holds 32768 lines of 128 bytes."""
+    f = S.lib().specdec_verify_greedy_noalloc
+    assert f(FAKE, S.F32, 1, 16385, 0, 1, None, FAKE, FAKE, None, None, None) == S.E_SCRATCH
+    assert f(FAKE, S.F32, 1, 2, 16383, 1, FAKE, FAKE, FAKE, None, None, None) == S.E_ARG   # D > 255
+    assert f(FAKE, S.F32, 1, 5462, 4, 1, FAKE, FAKE, FAKE, None, None, None) == S.E_SCRATCH
+    assert f(FAKE, S.F32, 1, -1, 4, 1, FAKE, FAKE, FAKE, None, None, None) == S.E_ARG
+    assert f(FAKE, 9, 1, 1, 4, 1, FAKE, FAKE, FAKE, None, None, None) == S.E_DTYPE
+    assert f(None, S.F32, 1, 1, 4, 1, FAKE, FAKE, FAKE, None, None, None) == S.E_ARG
+    assert f(FAKE, S.F32, 1, 0, 4, 1, None, None, None, None, None, None) == S.OK   # empty batch: no-op
+
+
 def test_workspace_init_null():
     assert S.lib().specdec_workspace_init(None, 256, None) == S.E_WORKSPACE
 
