@@ -37,7 +37,9 @@ _CSRC = os.path.join(ROOT, "ragged_kv_realignment_amd", "csrc")
 _HEADERS = ("buffer_io.h", "device_common.h", "realign_params.h")
 KERNEL = {False: "k_realign_eqspec", True: "k_realign_inplace"}
 PAGE = 16  # positions per page of the paged-cache leg
+SPIN_CYCLES_PER_LAUNCH = 200000  # GPU spin ahead of a pass, per launch queued behind it (~100 us at 2 GHz)
 # counter summary and the sources of the realign kernel it was taken on, per realign mode
+VERIFY_SOURCES = ("verify.hip", "device_common.h", "launch.h")
 TRAFFIC = {
     False: (os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt"), ("realign.hip",) + _HEADERS),
     True: (os.path.join(ROOT, "profiles", "realign_inplace_8b_gqa_traffic.txt"),
@@ -68,27 +70,43 @@ def parse():
     return ap.parse_args()
 
 
-def realign_kernel_sha(inplace=False):
-    """First 16 hex digits of the SHA-256 of the realign kernel's sources."""
+def source_sha(names):
+    """First 16 hex digits of the SHA-256 of kernel sources under csrc/."""
     h = hashlib.sha256()
-    for name in TRAFFIC[inplace][1]:
+    for name in names:
         with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_per_launch(inplace=False):
-    """HBM bytes per realign launch from the committed counter summary, or None
-    when it is missing or was taken on different kernel sources."""
-    path = TRAFFIC[inplace][0]
+def realign_kernel_sha(inplace=False):
+    return source_sha(TRAFFIC[inplace][1])
+
+
+def _counter_ratio(path, sha_key, ratio_key, sources):
+    """(traffic / algorithmic ratio, how) from a committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m_sha = re.search(r"^kernel_source_sha256_16:\s*(\w+)", txt, re.M)
-    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
-    if not m_sha or not m_b or m_sha.group(1) != realign_kernel_sha(inplace):
+    m_sha = re.search(r"^%s:\s*(\w+)" % sha_key, txt, re.M)
+    m_r = re.search(r"^%s:\s*([0-9.eE+]+)" % ratio_key, txt, re.M)
+    if not m_sha or not m_r or m_sha.group(1) != source_sha(sources):
         return None
-    return float(m_b.group(1))
+    return float(m_r.group(1)), "rocprofv3 FETCH_SIZE + WRITE_SIZE over algorithmic bytes = %s (%s, taken over the " \
+        "64-round chain on kernel sources %s), applied to this run's algorithmic bytes per launch" % (
+            m_r.group(1), os.path.relpath(path, ROOT), m_sha.group(1))
+
+
+def traffic_ratio(inplace=False):
+    return _counter_ratio(TRAFFIC[inplace][0], "kernel_source_sha256_16", "traffic_over_algorithmic",
+                          TRAFFIC[inplace][1])
+
+
+def verify_traffic(alg_bytes):
+    r = _counter_ratio(TRAFFIC[True][0], "verify_source_sha256_16", "verify_traffic_over_algorithmic",
+                       VERIFY_SOURCES)
+    return None if r is None else {"bytes_per_launch": r[0] * alg_bytes, "how": r[1]}
 
 
 def round_bytes(cfg, lens0, width0, acc_hist):
@@ -412,6 +430,116 @@ def _time_chain(args, cfg, w, mode, K, W, cap):
     return out
 
 
+def cycle_stats(acc, D, rounds_per_s=None):
+    """Per-cycle measurements of verification: where the first rejection fell
+    (accept length a = the position of the first rejected draft; a = D means
+    none was rejected), drafts accepted and tokens committed (a + 1) per round,
+    and the committed-token rate at the measured round rate."""
+    import numpy as np
+    acc = np.asarray(acc, dtype=np.int64)
+    hist = np.bincount(acc.reshape(-1), minlength=D + 1)[:D + 1]
+    per_round = (acc + 1).sum(axis=1)
+    out = {"accept_len_histogram": hist.tolist(),
+           "first_rejection_position_histogram": hist[:D].tolist(),
+           "no_rejection_rows": int(hist[D]),
+           "accepted_drafts_per_round": float(acc.sum(axis=1).mean()),
+           "committed_tokens_per_round": float(per_round.mean()),
+           "committed_tokens_per_row_round": float((acc + 1).mean()),
+           "committed_tokens_per_round_min_max": [int(per_round.min()), int(per_round.max())]}
+    if rounds_per_s:
+        out["committed_tokens_per_s"] = float(per_round.mean() * rounds_per_s)
+    return out
+
+
+def host_info():
+    """The host the benchmark ran on: logical CPUs, CPUs this process may use, RAM."""
+    ram = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    ram = int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_count": os.cpu_count(), "cpus_usable": aff, "ram_bytes": ram}
+
+
+def device_memory(dev, kv_bytes=None, kv_content_bytes=None):
+    import torch
+    out = {"peak_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
+           "device_total_bytes": int(torch.cuda.get_device_properties(dev).total_memory)}
+    if kv_bytes is not None:
+        out["kv_cache_bytes"] = int(kv_bytes)
+    if kv_content_bytes is not None:
+        out["kv_content_bytes_final"] = int(kv_content_bytes)
+    return out
+
+
+def _measure_lib():
+    import ctypes as C
+    L = C.CDLL(os.path.join(ROOT, "ragged_kv_realignment_amd", "libspecdec_measure.so"))
+    L.specdec_measure_read_floor.argtypes = [C.c_void_p, C.c_int, C.c_int64, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                             C.c_int, C.c_void_p]
+    L.specdec_measure_read_floor.restype = C.c_int
+    return L
+
+
+def verify_alone(cfg, w, K):
+    """Greedy verification over the K rounds' logits with nothing between the
+    launches, beside two references on the same cold buffers: a bare read with
+    verification's exact launch shape and loads (its floor), and torch.argmax
+    (a library doing the same arithmetic).  Each is timed twice: HIP events
+    around every launch, and events around the whole pass of K launches (the
+    pass average carries no per-launch event, but the gaps between launches)."""
+    import numpy as np
+    import torch
+    import ragged_kv_realignment_amd as sd
+
+    dev = torch.device("cuda", 0)
+    ws = sd.workspace(cfg.B, cfg.D)
+    acc = torch.zeros((K, cfg.B), dtype=torch.int32, device=dev)
+    nxt = torch.zeros((K, cfg.B), dtype=torch.int32, device=dev)
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    M = _measure_lib()
+    es = 4 if cfg.logit_dtype == 0 else 2
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def floor(r):
+        g = M.specdec_measure_read_floor(w.logits[r].data_ptr(), es, cfg.V, cfg.B, cfg.D, cfg.V, sink.data_ptr(),
+                                         sink.numel(), stream)
+        if g < 0:
+            raise RuntimeError("bare-read launch failed")
+
+    kernels = {
+        "verify": lambda r: sd.verify_greedy(w.logits[r], w.drafts[r], ws=ws, accept_len=acc[r], next_token=nxt[r]),
+        "floor": floor,
+        "torch_argmax": lambda r: torch.argmax(w.logits[r], dim=-1),
+    }
+    out = {}
+    for name, fn in kernels.items():
+        fn(0)
+        torch.cuda.synchronize()
+        # each pass starts behind a spin kernel long enough for the host to
+        # queue all K launches, so the pass runs at the GPU's pace rather than
+        # the host's (the binding's checks take longer than a launch runs)
+        ev = _events(K, 2)
+        torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * K)
+        for r in range(K):
+            ev[r][0].record()
+            fn(r)
+            ev[r][1].record()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * K)
+        a.record()
+        for r in range(K):
+            fn(r)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = {"avg_launch_us": float(_ms(ev, 0, 1).mean() * 1e3), "pass_avg_us": a.elapsed_time(b) * 1e3 / K}
+    return out
+
+
 def bench_chain(args, cfg):
     """Chained greedy verify + EQSPEC rounds of a left-padded batch (8b-gqa, 7b-mha).
 
@@ -430,7 +558,7 @@ def bench_chain(args, cfg):
     w = sdev.GreedyRounds(cfg, R)
     modes = {"all": ("inplace", "eqspec", "paged"), "both": ("inplace", "eqspec")}.get(args.realign, (args.realign,))
     runs = {m: _time_chain(args, cfg, w, m, K, W, cap) for m in modes}
-    with_traffic = cfg.name == "8b-gqa" and K == 64 and W == 8
+    with_traffic = cfg.name == "8b-gqa"  # the workload the counters were taken on
 
     def roof(mode):
         r = runs[mode]
@@ -442,12 +570,18 @@ def bench_chain(args, cfg):
         fn = round_bytes_inplace if mode == "inplace" else (lambda *a: round_bytes(*a)[1])
         rbytes = fn(cfg, w.lens0, w.width0, r["acc"])
         gbs = rbytes.sum() / (r["re_ms"].sum() * 1e-3) / 1e9
-        return _roof(KERNEL[mode == "inplace"], gbs, float(rbytes.mean()), float(r["re_ms"].mean() * 1e3),
-                     traffic_per_launch(mode == "inplace") if with_traffic else None)
+        tr = traffic_ratio(mode == "inplace") if with_traffic else None
+        out = _roof(KERNEL[mode == "inplace"], gbs, float(rbytes.mean()), float(r["re_ms"].mean() * 1e3),
+                    None if tr is None else tr[0] * float(rbytes.mean()))
+        if tr is not None:
+            out["traffic_how"] = tr[1]
+        return out
 
     head = runs[modes[0]]
     vbytes, _ = round_bytes(cfg, w.lens0, w.width0, head["acc"])
     ve_gbs = vbytes.sum() / (head["ver_ms"].sum() * 1e-3) / 1e9
+    alone = verify_alone(cfg, w, K)
+    logit_bytes = cfg.B * cfg.D1 * cfg.V * (4 if cfg.logit_dtype == 0 else 2)
     extra = {}
     if args.copy_calib_gib > 0:
         extra["copy_calibration"] = copy_calibration(args.copy_calib_gib, dev)
@@ -456,7 +590,17 @@ def bench_chain(args, cfg):
     extra.update({
         "verify": {"kernel": "k_verify_greedy", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
                    "algorithmic_bytes_per_launch": float(vbytes.mean()),
-                   "avg_launch_us": float(head["ver_ms"].mean() * 1e3)},
+                   "avg_launch_us": float(head["ver_ms"].mean() * 1e3),
+                   "traffic": verify_traffic(float(vbytes.mean())),
+                   "alone": {**alone["verify"], "how": "the same %d launches with nothing between them" % K},
+                   "practical_floor": {
+                       **alone["floor"], "gbs": logit_bytes / (alone["floor"]["avg_launch_us"] * 1e-6) / 1e9,
+                       "kernel": "bare read of the same cold logits with verification's grid, workgroups and "
+                                 "16-byte loads, no reduction (libspecdec_measure.so)"},
+                   "frac_of_practical": alone["floor"]["avg_launch_us"] / alone["verify"]["avg_launch_us"],
+                   "frac_of_practical_pass": alone["floor"]["pass_avg_us"] / alone["verify"]["pass_avg_us"],
+                   "torch_argmax": {**alone["torch_argmax"],
+                                    "kernel": "torch.argmax(logits, -1) over the same buffers (first maximum)"}},
         "realign_share_of_round": float(head["re_ms"].sum() / head["instrumented_ms"]),
         "timing": {"trials_ms": head["trials_ms"], "instrumented_pass_ms": head["instrumented_ms"],
                    "how": "value and ms_per_step: median of the uninstrumented passes; per-kernel figures: one more "
@@ -496,6 +640,12 @@ def bench_chain(args, cfg):
         "global_batch": cfg.B,
     }
     metric = METRIC if cfg.name == "8b-gqa" else METRIC.replace("at B=16", "at B=%d (%s)" % (cfg.B, cfg.name))
+    rps = K / (head["total_ms"] * 1e-3)
+    final_lens = w.lens0.astype("int64") + (head["acc"].astype("int64") + 1).sum(axis=0)
+    extra["cycle"] = cycle_stats(head["acc"], cfg.D, rps)
+    extra["memory"] = device_memory(dev, kv_bytes=cfg.L * 2 * cfg.B * cfg.H * cap * cfg.Dh * (
+        4 if cfg.kv_dtype == 0 else 2), kv_content_bytes=cfg.kv_pos_bytes * int(final_lens.sum()))
+    extra["host"] = host_info()
     headroof = roof(modes[0])
     if modes[0] in ("inplace", "eqspec"):  # a copy-shaped kernel: its rate against the measured streaming rate
         headroof["frac_of_practical"] = headroof["achieved"] / ceiling["read_write_gbs"]

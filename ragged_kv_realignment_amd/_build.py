@@ -11,6 +11,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspecdec.so")
+# the benchmark's measurement kernel (a bare read with verification's launch shape), not part of the C ABI
+MEASURE_LIB = os.path.join(HERE, "libspecdec_measure.so")
+MEASURE_SOURCES = ["csrc/measure.hip"]
 OBJ = os.path.join(HERE, "_build")
 HIP_SOURCES = ["csrc/verify.hip", "csrc/realign.hip", "csrc/realign_inplace.hip", "csrc/sample_logits.hip",
                "csrc/group.hip", "csrc/paged.hip", "csrc/pool.hip", "csrc/scratch.hip"]
@@ -41,15 +44,20 @@ def _compile_cpp(src, extra):
     return out, _run([HIPCC, *COMMON, *extra, "-c", src, "-o", out])
 
 
-def build(extra_flags=(), out=LIB):
+def build(extra_flags=(), out=LIB, measure=True):
     os.makedirs(OBJ, exist_ok=True)
-    jobs = [(_compile_hip, s) for s in HIP_SOURCES] + [(_compile_cpp, s) for s in CPP_SOURCES]
+    srcs = HIP_SOURCES + (MEASURE_SOURCES if measure else [])
+    jobs = [(_compile_hip, s) for s in srcs] + [(_compile_cpp, s) for s in CPP_SOURCES]
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         done = list(ex.map(lambda j: j[0](j[1], list(extra_flags)), jobs))
-    objs = [o for o, _ in done]
+    obj = {src: o for (_, src), (o, _) in zip(jobs, done)}
     err = "".join(e for _, e in done)
-    err += _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out + ".tmp", *objs])
-    os.replace(out + ".tmp", out)
+    links = [(out, [obj[s] for s in HIP_SOURCES + CPP_SOURCES])]
+    if measure:
+        links.append((MEASURE_LIB, [obj[s] for s in MEASURE_SOURCES]))
+    for lib, objs in links:
+        err += _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs])
+        os.replace(lib + ".tmp", lib)
     return err
 
 

@@ -1,0 +1,79 @@
+// Measurement kernel for the benchmark, built into its own library
+// (libspecdec_measure.so) and not part of the C ABI: a bare streaming read of
+// a logits buffer with exactly the launch shape and loads of greedy
+// verification (the same grid, 256-thread workgroups, four 16-byte
+// non-temporal loads per thread, the same split of each row), and no
+// reduction.  Its duration is the floor that verification's loads alone take
+// on the same cold buffer; the benchmark reports verification against it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;  // as greedy verification
+constexpr int kVpt = 4;        // 16-byte vectors per thread, as greedy verification
+
+// Ids per workgroup, by greedy verification's rule: about 8 workgroups per CU,
+// between one and kVpt vectors per thread.
+long chunk_for(int B, int D, int V, int es) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int vw = 16 / es;
+  const long rows = (long)B * (D + 1);
+  const long step = (long)kThreads * vw;
+  const long want = (8L * cus + rows - 1) / rows;
+  long chunk = (V + want - 1) / want;
+  chunk = (chunk + step - 1) / step * step;
+  if (chunk > (long)kVpt * step) chunk = (long)kVpt * step;
+  return chunk;
+}
+
+__global__ __launch_bounds__(kThreads) void k_read_floor(const char *logits, int64_t row_bytes, int V, int es,
+                                                         int splits, int chunk, uint32_t *sink) {
+  const int vw = 16 / es;
+  const int rows = (int)gridDim.x / splits;
+  const int split = (int)blockIdx.x / rows;
+  const int row = (int)blockIdx.x - split * rows;
+  const int start = split * chunk;
+  const int end = min(V, start + chunk);
+  const char *rowp = logits + (size_t)row * (size_t)row_bytes;
+  const int nvec = (end - start) / vw;
+  const u32x4 *vp = reinterpret_cast<const u32x4 *>(rowp) + start / vw;
+  uint32_t x = 0;
+  if (nvec > 0) {
+    u32x4 r[kVpt];
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u)
+      r[u] = __builtin_nontemporal_load(vp + min(u * kThreads + (int)threadIdx.x, nvec - 1));
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) x ^= r[u][0] ^ r[u][1] ^ r[u][2] ^ r[u][3];
+  }
+  const int tv = start + nvec * vw + threadIdx.x;
+  if (tv < end) x ^= es == 4 ? reinterpret_cast<const uint32_t *>(rowp)[tv]
+                             : (uint32_t)reinterpret_cast<const uint16_t *>(rowp)[tv];
+  // never true in practice; keeps the loads
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+}  // namespace
+
+// Launches the bare read over rows (b, i), b < B, i <= D, of `logits` (16-byte
+// aligned rows of row_stride elements of es bytes).  sink: device uint32
+// [grid], written only on a 2^-32 chance.  Returns the grid size, or -1.
+extern "C" __attribute__((visibility("default"))) int specdec_measure_read_floor(
+    const void *logits, int es, int64_t row_stride, int B, int D, int V, uint32_t *sink, int sink_words,
+    void *stream) {
+  if (!logits || !sink || (es != 2 && es != 4) || B < 1 || D < 0 || V < 1 || row_stride < V) return -1;
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0 || ((size_t)row_stride * es) % 16 != 0) return -1;
+  const long chunk = chunk_for(B, D, V, es);
+  const long splits = (V + chunk - 1) / chunk;
+  const long grid = (long)B * (D + 1) * splits;
+  if (grid > sink_words || grid > 0x7FFFFFFFL) return -1;
+  hipLaunchKernelGGL(k_read_floor, dim3((unsigned)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const char *>(logits), (int64_t)row_stride * es, V, es, (int)splits, (int)chunk,
+                     sink);
+  return hipGetLastError() == hipSuccess ? (int)grid : -1;
+}

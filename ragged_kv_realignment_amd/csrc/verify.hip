@@ -100,12 +100,30 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
 //
 // Finish: thread 0 folds the key into the row's key with an atomic max, then
 // counts the workgroup in batch row b's counter (D+1 rows x splits arrivals).
-// The max's result is consumed before the count is issued, so the workgroup
-// that sees the count complete also sees every key (both are device-scope
-// atomics performed at the device's coherence point; the keys are read back
-// with device-scope atomic loads).  That last workgroup reads the D+1 keys in
-// parallel, runs the first-mismatch scan and leaves keys and counter zeroed.
-// Each key and counter has a 128-byte line of its own.
+// The workgroup whose count completes the row reads the D+1 keys in parallel,
+// runs the first-mismatch scan and leaves keys and counter zeroed.  Each key
+// and counter has a 128-byte line of its own.
+//
+// Ordering.  The HIP memory model would have every arrival be an agent-scope
+// release and the last workgroup take an agent-scope acquire.  On gfx950 these
+// compile to a write-back of the whole L2 before each count (buffer_wbl2) and
+// an L2 invalidate (buffer_inv) in the last workgroup; measured on MI355X over
+// the 8b-gqa logits, they cost 14 to 75 us per call (the call itself takes
+// about 8.4 us).  The kernel relies instead on three properties of gfx950 that
+// the ISA gives and the language model does not promise:
+//  1. a returning atomic (the max) hands back its result only once it has been
+//     performed at the device's coherence point, where every atomic on that
+//     line is performed;
+//  2. the count is a data dependency of that result (an opaque zero computed
+//     from it is part of the counter's address), so it is issued only after
+//     the max has been performed;
+//  3. the last workgroup reads the keys with agent-scope loads, which bypass
+//     the non-coherent L2 (the sc1 bit) and are issued only after its own count
+//     has returned.
+// Every max therefore precedes its count, every count precedes the last one,
+// and the last workgroup's key loads observe all of them.  A compiler that
+// moved the count ahead of the max would break property 2; the dependency
+// through the inline asm is what forbids it.
 template <int DT, bool VEC, int NT, int VPT>
 __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits, int chunk) {
   constexpr int ES = Elem<DT>::size;

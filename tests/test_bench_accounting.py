@@ -124,3 +124,22 @@ def test_cpu_baseline_reports_both_oracle_builds():
     assert cpu["value"] > 0 and cpu["cores"] == 1 and cpu["kind"] == "oracle" and cpu["unit"] == "rounds/s"
     assert cpu["all_cores"]["value"] > 0 and cpu["all_cores"]["cores"] >= 1
     assert oracle.threads() == 1
+
+
+def test_cycle_stats_histogram_and_rates():
+    import numpy as np
+    import bench
+    acc = np.array([[0, 5, 2], [5, 5, 1]])  # 2 rounds x 3 rows, D = 5
+    c = bench.cycle_stats(acc, 5, rounds_per_s=10.0)
+    assert c["accept_len_histogram"] == [1, 1, 1, 0, 0, 3]
+    assert c["first_rejection_position_histogram"] == [1, 1, 1, 0, 0] and c["no_rejection_rows"] == 3
+    assert c["accepted_drafts_per_round"] == 9.0                 # (0+5+2 + 5+5+1) / 2
+    assert c["committed_tokens_per_round"] == 12.0               # (1+6+3 + 6+6+2) / 2
+    assert c["committed_tokens_per_round_min_max"] == [10, 14]
+    assert c["committed_tokens_per_s"] == 120.0
+
+
+def test_host_info_reports_cpus_and_ram():
+    import bench
+    h = bench.host_info()
+    assert h["cpu_count"] >= 1 and h["ram_bytes"] > 0
