@@ -10,6 +10,7 @@ Every function is pinned by CPU tests against values the pages fix (their
 worked examples), closed forms and brute force; see oracle.c for the passages
 each one follows and the readings taken where the pages leave a choice.
 """
+import contextlib
 import ctypes as C
 import os
 
@@ -31,10 +32,23 @@ class OracleError(RuntimeError):
 
 def use_threads(flag):
     """Route later calls to the OpenMP build (True) or the single-threaded one
-    (False, the default).  Both compute the same bytes; the threaded build only
-    serves to time the oracle on all host cores."""
+    (False, the default).  Both compute the same bytes (a CPU test checks it);
+    the threaded build times the oracle on all host cores and runs the
+    every-layer checks of the full-size GPU tests, where one thread would take
+    minutes."""
     global _threaded
     _threaded = bool(flag)
+
+
+@contextlib.contextmanager
+def threaded():
+    """Calls inside the block use the OpenMP build."""
+    prev = _threaded
+    use_threads(True)
+    try:
+        yield
+    finally:
+        use_threads(prev)
 
 
 def threads():

@@ -72,3 +72,35 @@ def advance(tokens, kv, committed, kv_new):
     tokens: list of ids; kv [L,2,H,c,Dh]; kv_new [L,2,H,D+1,Dh]."""
     n = len(committed)
     return list(tokens) + list(committed), np.concatenate([kv, kv_new[:, :, :, :n, :]], axis=3)
+
+
+def chain_final(kv0, lens0, width0, kv_new_rounds, acc_rounds, left_pad=True):
+    """KV of a batch after a chain of rounds, one sequence at a time: each row's
+    content is its initial content followed by the first a+1 speculative entries
+    of every round, in round order (advance() applied round after round, written
+    as one concatenation per row).  The rows are then laid out as the batch
+    stores them: left-padded to the longest (a rectangle) or left-aligned (a
+    pool), zero elsewhere.
+
+    kv0 [L,2,B,H,cap,Dh] holds row b's content at [width0 - lens0[b], width0)
+    (left_pad) or [0, lens0[b]) (a pool); kv_new_rounds[r] [L,2,B,H,D+1,Dh];
+    acc_rounds[r] [B].  Returns (kv [L,2,B,H,W,Dh], lens [B], W) with W the
+    longest final length."""
+    L, _, B, H, _, Dh = kv0.shape
+    seqs = []
+    for b in range(B):
+        c = int(lens0[b])
+        lo = width0 - c if left_pad else 0
+        parts = [kv0[:, :, b, :, lo:lo + c]]
+        for kvn, acc in zip(kv_new_rounds, acc_rounds):
+            parts.append(kvn[:, :, b, :, :int(acc[b]) + 1])
+        seqs.append(np.concatenate(parts, axis=3))
+    lens = np.array([s.shape[3] for s in seqs], dtype=np.int32)
+    W = int(lens.max()) if B else 0
+    out = np.zeros((L, 2, B, H, W, Dh), dtype=kv0.dtype)
+    for b, s in enumerate(seqs):
+        if left_pad:
+            out[:, :, b, :, W - s.shape[3]:] = s
+        else:
+            out[:, :, b, :, :s.shape[3]] = s
+    return out, lens, W

@@ -8,6 +8,7 @@ import oracle
 import synth
 import synth.device as sdev
 from tests import invariants as inv
+from tests.full_layers import device_equal
 from tests.gpu_util import bytes_equal, say, to_np_raw
 
 pytestmark = pytest.mark.gpu
@@ -157,7 +158,10 @@ def test_exspec_pool_workload(sd):
         plant, miss, draft = synth.plan_greedy(cfg, r)
         keep = sdev.fill_logits(cfg, r, plant, logits)
         sdev.fill_kvnew(cfg, r, kv_new)
-        if r in check_rounds:
+        if r == R - 1:
+            rect.kv.view(torch.uint8).fill_(CANARY_KV)  # every layer of the last gather is checked
+            rect.tokens.fill_(CANARY_I32)
+        elif r in check_rounds:
             rect.kv[lcheck].view(torch.uint8).fill_(CANARY_KV)
             rect.tokens.fill_(CANARY_I32)
         order, uni, wid, nu = sd.group_by_len(pool.len, G)
@@ -184,9 +188,12 @@ def test_exspec_pool_workload(sd):
     lens = lens0.copy()
     tok = tok0.copy()
     kvs = {l: synth.kv_host(cfg, lens0, 0, False, layer0=l, nlayers=1) for l in (0, cfg.L - 1)}
+    rounds = []
     for r in range(R):
         h = hist[r]
         order, uni, wid, nu = oracle.group_by_len(lens, G)
+        if r == R - 1:
+            last_gather = dict(order=order, uni=uni, wid=wid, lens=lens.copy(), tok=tok.copy())
         assert np.array_equal(h["order"], order) and np.array_equal(h["uni"], uni), "round %d grouping" % r
         assert np.array_equal(h["wid"], wid) and h["nu"] == nu
         if r == 0:
@@ -208,6 +215,7 @@ def test_exspec_pool_workload(sd):
         lg = synth.logits_host(cfg, r, plant)
         oacc, onxt, _ = oracle.verify_greedy(lg, draft, N, cfg.D, cfg.V)
         assert np.array_equal(h["acc"], oacc) and np.array_equal(h["nxt"], onxt), "round %d verify" % r
+        rounds.append((draft, oacc, onxt))
         for l in kvs:
             kvn = synth.kvnew_host(cfg, r, layer0=l, nlayers=1)
             lens_l = lens.copy()
@@ -220,3 +228,32 @@ def test_exspec_pool_workload(sd):
     assert np.array_equal(final_tok, tok)
     for l in kvs:
         assert bytes_equal(final_kv[l], kvs[l][0]), "final pool layer %d" % l
+
+    # every layer: the last round's gather and the final pool, each layer's pool
+    # regenerated and carried through the rounds' appends by the oracle (its
+    # OpenMP build: a layer of the pool is 1.1 GB)
+    lg_ = last_gather
+    with oracle.threaded():
+        for l in range(cfg.L):
+            say("exspec every layer", l)
+            kv_l = synth.kv_host(cfg, lens0, 0, False, layer0=l, nlayers=1)
+            lens_l = lens0.copy()
+            for r in range(R):
+                if r == R - 1:
+                    want = oracle.gather(kv_l, lg_["tok"], lens_l, lg_["order"], G, lg_["uni"], cfg.cap)
+                    for g in range(ng):
+                        sl = slice(g * G, g * G + G)
+                        if lg_["uni"][g]:
+                            assert bool((rect.kv[l][:, sl].view(torch.uint8) == CANARY_KV).all()), \
+                                "layer %d: uniform batch %d was copied" % (l, g)
+                            continue
+                        W = int(lg_["wid"][g])
+                        assert device_equal(rect.kv[l][:, sl, :, :W], want["kv"][0, :, sl, :, :W]), \
+                            "last gather, layer %d group %d" % (l, g)
+                    del want
+                draft, oacc, onxt = rounds[r]
+                kvn = synth.kvnew_host(cfg, r, layer0=l, nlayers=1)
+                oracle.append(kv_l, None, lens_l, np.arange(N), kvn, draft, oacc, onxt)
+            assert np.array_equal(lens_l, final_len)
+            assert device_equal(pool.kv[l], kv_l[0]), "final pool layer %d" % l
+            del kv_l

@@ -12,6 +12,7 @@ import oracle
 import synth
 import synth.device as sdev
 from tests import invariants as inv
+from tests.full_layers import check_chain_final_layers
 from tests.gpu_util import bytes_equal, from_np_raw, say, to_np_raw
 
 pytestmark = pytest.mark.gpu
@@ -195,10 +196,12 @@ def _run_chain_inplace(sd, name, rounds, check_rounds, layers):
     lens, S = w.lens0.copy(), w.width0
     tok, mask = w.tok0.copy(), w.mask0.copy()
     state = {l: synth.kv_host(cfg, lens, S, True, layer0=l, nlayers=1) for l in layers}
+    oacc_hist = []
     for r in range(rounds):
         plant, miss, draft = w.plans[r]
         logits = synth.logits_host(cfg, r, plant)
         oacc, onxt, _ = oracle.verify_greedy(logits, draft, cfg.B, cfg.D, cfg.V)
+        oacc_hist.append(oacc)
         assert np.array_equal(hist["acc"][r], oacc), "round %d accept_len" % r
         assert np.array_equal(hist["nxt"][r], onxt), "round %d next_token" % r
         new_state, out = {}, None
@@ -216,6 +219,8 @@ def _run_chain_inplace(sd, name, rounds, check_rounds, layers):
         for k in ("tokens", "pos", "mask"):
             assert np.array_equal(hist[k][r][:, :Wr], out[k][:, :Wr]), "round %d %s" % (r, k)
         state, lens, S, tok, mask = new_state, out["len"], Wr, out["tokens"], out["mask"]
+    Wf = check_chain_final_layers(cfg, w.lens0, w.width0, oacc_hist, lambda l: buf.kv[l], "inplace chain " + name)
+    assert Wf == S
 
 
 def test_inplace_chain_7b_mha(sd):

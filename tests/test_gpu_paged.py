@@ -11,6 +11,7 @@ import torch
 import oracle
 import synth
 import synth.device as sdev
+from tests.full_layers import check_chain_final_layers
 from tests.gpu_util import bytes_equal, from_np_raw, say, to_np_raw
 
 pytestmark = pytest.mark.gpu
@@ -181,10 +182,12 @@ def _run_chain_paged(sd, name, rounds, check_rounds, layers):
     lens, S = w.lens0.copy(), w.width0
     tok, mask = w.tok0.copy(), w.mask0.copy()
     state = {l: synth.kv_host(cfg, lens, S, True, layer0=l, nlayers=1) for l in layers}
+    oacc_hist = []
     for r in range(rounds):
         plant, miss, draft = w.plans[r]
         logits = synth.logits_host(cfg, r, plant)
         oacc, onxt, _ = oracle.verify_greedy(logits, draft, cfg.B, cfg.D, cfg.V)
+        oacc_hist.append(oacc)
         assert np.array_equal(hist["acc"][r], oacc), "round %d accept_len" % r
         assert np.array_equal(hist["nxt"][r], onxt), "round %d next_token" % r
         new_state, out = {}, None
@@ -203,6 +206,15 @@ def _run_chain_paged(sd, name, rounds, check_rounds, layers):
         for k in ("tokens", "pos", "mask"):
             assert np.array_equal(hist[k][r][:, :Wr], out[k][:, :Wr]), "round %d %s" % (r, k)
         state, lens, S, tok, mask = new_state, out["len"], Wr, out["tokens"], out["mask"]
+    # every layer of the final paged cache, through a gather into the rectangle
+    say("paged chain", name, "final gather")
+    rect.kv.view(torch.uint8).fill_(0xA5)
+    sd.paged_gather(cache, rect, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and int(rect.width[0].item()) == S
+    Wf = check_chain_final_layers(cfg, w.lens0, w.width0, oacc_hist, lambda l: rect.kv[l], "paged chain " + name,
+                                  canary=0xA5)
+    assert Wf == S
 
 
 def test_paged_chain_7b_mha(sd):

@@ -10,6 +10,7 @@ import synth
 import synth.device as sdev
 from oracle import brute
 from tests import invariants as inv
+from tests.full_layers import check_chain_final_layers, device_equal
 from tests.gpu_util import bytes_equal, from_np_raw, say, to_np_raw
 
 pytestmark = pytest.mark.gpu
@@ -134,7 +135,8 @@ def _run_chain(sd, name, rounds, check_rounds, layers):
     """`rounds` chained greedy verify + EQSPEC rounds on the GPU, checked round by
     round against the oracle run on the same generated inputs.  Token ids,
     position ids, mask, lengths, widths, accepted lengths and next tokens are
-    compared at every round; KV bytes of `layers` at `check_rounds`."""
+    compared at every round; KV bytes of `layers` at `check_rounds`, and of every
+    layer after the last round."""
     cfg = synth.CONFIGS[name]
     say("chain", name, "setup")
     tdt = sdev.TORCH_DT[cfg.kv_dtype]
@@ -165,10 +167,12 @@ def _run_chain(sd, name, rounds, check_rounds, layers):
     lens, S = w.lens0.copy(), w.width0
     tok, mask = w.tok0.copy(), w.mask0.copy()
     state = {l: synth.kv_host(cfg, lens, S, True, layer0=l, nlayers=1) for l in layers}
+    oacc_hist = []
     for r in range(rounds):
         plant, miss, draft = w.plans[r]
         logits = synth.logits_host(cfg, r, plant)
         oacc, onxt, _ = oracle.verify_greedy(logits, draft, cfg.B, cfg.D, cfg.V)
+        oacc_hist.append(oacc)
         assert np.array_equal(hist["acc"][r], oacc), "round %d accept_len" % r
         assert np.array_equal(hist["nxt"][r], onxt), "round %d next_token" % r
         new_state = {}
@@ -191,6 +195,10 @@ def _run_chain(sd, name, rounds, check_rounds, layers):
         committed = [list(draft[b, :oacc[b]]) + [int(onxt[b])] for b in range(cfg.B)]
         inv.check_round(tok, mask, S, out["tokens"], out["pos"], out["mask"], out["len"], Wr, oacc, committed, cfg.D)
         state, lens, S, tok, mask = new_state, out["len"], Wr, out["tokens"], out["mask"]
+    final = bufs[rounds % 2]
+    Wf = check_chain_final_layers(cfg, w.lens0, w.width0, oacc_hist, lambda l: final.kv[l], "eqspec chain " + name,
+                                  canary=CANARY_KV)
+    assert Wf == S
 
 
 def test_eqspec_chain_7b_mha(sd):
@@ -287,19 +295,23 @@ def test_stochastic_round_realign(sd):
     assert np.array_equal(gacc, oacc)
     ambiguous = np.nonzero(gnxt != onxt)[0]
     assert len(ambiguous) == 0, "a draw fell inside the tie band; see the band rule"
-    say("stoch oracle")
     W = None
-    for l in (0, cfg.L - 1):
-        kv_l = synth.kv_host(cfg, lens, S, True, layer0=l, nlayers=1)
-        kvn_l = synth.kvnew_host(cfg, 0, layer0=l, nlayers=1)
-        out = oracle.realign_eqspec(kv_l, kvn_l, lens, S, tok, mask, oacc, onxt, draft)
-        W = out["width"]
-        g = to_np_raw(dst.kv[l])
-        assert bytes_equal(g[..., :W, :], out["kv"][0, ..., :W, :]), "layer %d" % l
-        assert np.all(g[..., W:, :].view(np.uint8) == CANARY_KV)
+    with oracle.threaded():  # every layer (1 GB each): the OpenMP build of the same oracle
+        for l in range(cfg.L):
+            say("stoch oracle, layer", l)
+            kv_l = synth.kv_host(cfg, lens, S, True, layer0=l, nlayers=1)
+            kvn_l = synth.kvnew_host(cfg, 0, layer0=l, nlayers=1)
+            out = oracle.realign_eqspec(kv_l, kvn_l, lens, S, tok, mask, oacc, onxt, draft)
+            W = out["width"]
+            assert device_equal(dst.kv[l][..., :W, :], out["kv"][0, ..., :W, :]), "layer %d" % l
+            assert bool((dst.kv[l][..., W:, :].contiguous().view(torch.uint8) == CANARY_KV).all())
+            if l == 0:
+                meta = {k: out[k] for k in ("tokens", "pos", "mask", "len")}
+            del kv_l, out
     assert int(dst.width.item()) == W
+    assert np.array_equal(dst.len.cpu().numpy(), meta["len"])
     for k in ("tokens", "pos", "mask"):
-        assert np.array_equal(getattr(dst, k).cpu().numpy()[:, :W], out[k][:, :W]), k
+        assert np.array_equal(getattr(dst, k).cpu().numpy()[:, :W], meta[k][:, :W]), k
 
 
 @pytest.mark.parametrize("shape", [

@@ -302,3 +302,35 @@ def test_caller_outputs_are_checked_before_launch(sd):
         sd.SeqBuf(kv, tok, i32(3), width=i32(0))
     with pytest.raises(ValueError):  # lengths on the host
         sd.SeqBuf(kv, tok, torch.zeros(3, dtype=torch.int32))
+
+
+def test_greedy_full_shape_unplanted_natural_ties(sd):
+    """Full-shape 8b-gqa rounds (B=16, D=5, V=151936 bf16) with unplanted N(0,2)
+    logits: the maximum lies wherever the draws put it, and bf16's coarse grid
+    makes it tie in several rows, at ids more than one split of the vocabulary
+    apart (8192 ids is the largest split the launcher uses).  The oracle decides
+    every target choice; the drafts follow its choices up to each row's
+    designed first mismatch."""
+    cfg = synth.CONFIGS["8b-gqa"]
+    B, D, V = cfg.B, cfg.D, cfg.V
+    cross_rows = 0
+    for rnd in range(200, 204):   # rounds past the chain's: fresh draws
+        say("greedy unplanted full shape", rnd)
+        host = synth.logits_host(cfg, rnd, None, nrows=B * cfg.D1)
+        f = (host.astype(np.uint32) << 16).view(np.float32)
+        top = f.max(axis=1, keepdims=True)
+        for row in np.nonzero((f == top).sum(axis=1) > 1)[0]:
+            ids = np.nonzero(f[row] == top[row])[0]
+            cross_rows += int(ids.max() - ids.min() >= 8192)
+        _, _, tgt = oracle.verify_greedy(host, np.zeros((B, D), np.int32), B, D, V)
+        _, miss, _ = synth.plan_greedy(cfg, rnd)
+        draft = np.array(tgt[:, :D], np.int32)
+        for b in range(B):
+            if miss[b] < D:
+                draft[b, miss[b]] = (tgt[b, miss[b]] + 1) % V
+        acc, nxt, gtgt, st = _gpu_greedy(sd, host, torch.bfloat16, B, D, V, draft)
+        oacc, onxt, otgt = oracle.verify_greedy(host, draft, B, D, V)
+        assert np.array_equal(oacc, np.minimum(miss, D))
+        assert np.array_equal(gtgt, otgt) and np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
+        assert st == 0
+    assert cross_rows >= 10, "the draws should tie at the maximum across splits in several rows"

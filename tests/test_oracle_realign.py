@@ -276,3 +276,39 @@ def test_checker_rejects_unshifted_kv():
     kv2[..., :S, :] = kv[..., :S, :]
     with pytest.raises(inv.InvariantError):
         inv.check_kv_round(kv, lens, S, kv2, out["len"], out["width"], kv_new, acc)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_chain_final_equals_batched_oracle_chain(seed):
+    """The per-sequence chain model (brute.chain_final) equals the batched oracle
+    applied round after round, on random chains of 1-9 rounds; the pool layout
+    equals oracle.append applied round after round."""
+    rng = np.random.default_rng(900 + seed)
+    B, D = int(rng.integers(1, 7)), int(rng.integers(0, 5))
+    L, H, Dh = int(rng.integers(1, 3)), int(rng.integers(1, 3)), 4
+    R = int(rng.integers(1, 10))
+    cap = 20 + R * (D + 1)
+    dtype = [np.float32, np.float16][seed % 2]
+    lens, S, kv, tok, mask, _, _, draft, nxt = _random_rect(rng, B, D, L, H, Dh, 20, dtype)
+    kv = np.concatenate([kv, np.zeros((L, 2, B, H, cap - 20, Dh), dtype)], axis=4)
+    tok = np.concatenate([tok, np.zeros((B, cap - 20), np.int32)], axis=1)
+    mask = np.concatenate([mask, np.zeros((B, cap - 20), np.int8)], axis=1)
+    news = [rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(dtype) for _ in range(R)]
+    accs = [rng.integers(0, D + 1, B).astype(np.int32) for _ in range(R)]
+    want, want_lens, W = brute.chain_final(kv, lens, S, news, accs)
+    cur, cl, cS, ct, cm = kv, lens, S, tok, mask
+    for r in range(R):
+        out = oracle.realign_eqspec(cur, news[r], cl, cS, ct, cm, accs[r], nxt, draft)
+        cur, cl, cS, ct, cm = out["kv"], out["len"], out["width"], out["tokens"], out["mask"]
+    assert cS == W and np.array_equal(cl, want_lens)
+    assert np.array_equal(cur[..., :W, :].view(np.uint8), want.view(np.uint8))
+    # pool layout: rows left-aligned, appended in place
+    pool = np.zeros((L, 2, B, H, cap, Dh), dtype)
+    for b in range(B):
+        pool[:, :, b, :, :lens[b]] = kv[:, :, b, :, S - lens[b]:S]
+    ptok, plen = np.zeros((B, cap), np.int32), lens.copy()
+    for r in range(R):
+        oracle.append(pool, ptok, plen, np.arange(B), news[r], draft, accs[r], nxt)
+    pw, plens, PW = brute.chain_final(pool, lens, 0, news, accs, left_pad=False)
+    assert np.array_equal(plens, plen) and PW == W
+    assert np.array_equal(pool[..., :PW, :].view(np.uint8), pw.view(np.uint8))
