@@ -236,6 +236,7 @@ typedef struct {
 #define SPECDEC_GATHER 1         /* pool rows -> one left-padded rectangle per group (no append) */
 #define SPECDEC_APPEND_INPLACE 2 /* pool rows: append committed entries at each row's length */
 #define SPECDEC_EQSPEC_INPLACE 3 /* rectangle -> the same rectangle: unpad, append, repad in place */
+#define SPECDEC_EQSPEC_INPLACE_ZERO_PAD 4 /* as SPECDEC_EQSPEC_INPLACE, for an input whose pad may hold any bytes */
 
 /* Realignment ("Batch Speculative Decoding Done Right", sections 2.1-2.3;
  * committed and discarded speculative KV: "Inference Engineering Part 5/8",
@@ -272,6 +273,13 @@ typedef struct {
  *   bytes that change: about twice each shifted row's content, its committed
  *   entries and any newly exposed pad, instead of the whole new rectangle.
  *   Device conditions as for EQSPEC; a failing call writes nothing.
+ * SPECDEC_EQSPEC_INPLACE_ZERO_PAD: SPECDEC_EQSPEC_INPLACE for a rectangle whose
+ *   pad positions may hold any KV bytes (a left-padded prefill writes KV at its
+ *   pad positions): every row's new pad [0, S' - len - n_b) is written with zero
+ *   bytes, so the result equals EQSPEC's on [0, S') whatever the input pad held.
+ *   It writes P * sum_b min(pad_b, pad'_b) bytes more than SPECDEC_EQSPEC_INPLACE
+ *   (P the KV bytes of one position over layers, K|V and heads); use it for the
+ *   first round after such a prefill, after which the pad is zero.
  * Limits: B <= 1024; head_dim * element size a multiple of 16 bytes; KV
  * pointers 16-byte aligned (E_ALIGN).  Device conditions: S' > out cap,
  * W_g > out cap or len + n_b > cap set SPECDEC_S_CAPACITY; lengths outside

@@ -218,7 +218,7 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
                            const int32_t *draft, const int32_t *accept_len, const int32_t *next_token,
                            int32_t pad_token, int32_t *status, sd::RealignParams &p) {
   if (mode != SPECDEC_EQSPEC && mode != SPECDEC_GATHER && mode != SPECDEC_APPEND_INPLACE &&
-      mode != SPECDEC_EQSPEC_INPLACE)
+      mode != SPECDEC_EQSPEC_INPLACE && mode != SPECDEC_EQSPEC_INPLACE_ZERO_PAD)
     return SPECDEC_E_ARG;
   if (B < 0 || B > sd::kMaxRealignRows || D < 0) return SPECDEC_E_ARG;
   int rc = check_seqbuf_shape(in);
@@ -281,7 +281,7 @@ static int realign_prepare(int mode, const specdec_seqbuf_t *in, const specdec_s
     p.mask_out = out->mask;
     p.len_out = out->len;
     p.width_out = out->width;
-  } else if (mode == SPECDEC_EQSPEC_INPLACE) {
+  } else if (mode == SPECDEC_EQSPEC_INPLACE || mode == SPECDEC_EQSPEC_INPLACE_ZERO_PAD) {
     if (in->rows != B || !same_buffers(in, out)) return SPECDEC_E_ARG;
     if (B == 0) return kNothing;
     if (!in->tokens || !in->pos || !in->mask || !in->width) return SPECDEC_E_ARG;
@@ -338,8 +338,8 @@ EXPORT int specdec_realign_kv(int mode, const specdec_seqbuf_t *in, const specde
   const int rc = realign_prepare(mode, in, out, rows, B, group, skip_group, D, kv_new, draft, accept_len, next_token,
                                  pad_token, status, p);
   if (rc != SPECDEC_OK) return rc == kNothing ? SPECDEC_OK : rc;
-  return launched(mode == SPECDEC_EQSPEC_INPLACE ? sd::launch_realign_inplace(p, as_stream(stream))
-                                                  : sd::launch_realign(p, as_stream(stream)));
+  const bool inplace = mode == SPECDEC_EQSPEC_INPLACE || mode == SPECDEC_EQSPEC_INPLACE_ZERO_PAD;
+  return launched(inplace ? sd::launch_realign_inplace(p, as_stream(stream)) : sd::launch_realign(p, as_stream(stream)));
 }
 
 EXPORT int specdec_group_by_len(const int32_t *len, int N, int group, int32_t *order, int32_t *uniform,

@@ -22,9 +22,11 @@ namespace sd {
 // and the chunk is stored after it.  Positions vacated by a move to higher
 // positions become pad (zero bytes); the committed entries follow the content.
 // Sequences whose shift is 0 only append.  The old pad is taken to hold zero
-// bytes, as every realignment leaves it.  Token ids, position ids and mask of
-// row b are rebuilt by workgroup nseg + b; lengths and width are written by
-// k_inplace_meta.
+// bytes, as every realignment leaves it; with SPECDEC_EQSPEC_INPLACE_ZERO_PAD
+// the whole new pad is written with zeros instead (for an input whose pad holds
+// other bytes, as a left-padded prefill leaves it).  Token ids, position ids
+// and mask of row b are rebuilt by workgroup nseg + b; lengths and width are
+// written by k_inplace_meta.
 #ifndef SPECDEC_IP_BLOCK
 #define SPECDEC_IP_BLOCK 1024  // threads per workgroup (one sequence)
 #endif
@@ -102,6 +104,7 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
     return;
   }
   const long nseg = (long)p.layers * 2 * B * H;
+  const bool zero_pad = p.mode == SPECDEC_EQSPEC_INPLACE_ZERO_PAD;
   const uint32_t pos_bytes = (uint32_t)U * 16u;
   const int t = threadIdx.x;
   char *kv = static_cast<char *>(p.kv_out);
@@ -145,11 +148,13 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
       } else {
         asm volatile("" : "+v"(e0));
       }
-      if (shift > 0) {
-        // positions [pin, pout) become pad: zero bytes (vacated content, or for a
-        // short row positions past the old width)
-        const __amdgpu_buffer_rsrc_t rz = rsrc(base + (size_t)pin * pos_bytes, (uint32_t)shift * pos_bytes);
-        for (int f = t; f < shift * U; f += kIpBlock) bst((i32x4)(0), rz, (uint32_t)f * 16u);
+      // positions [z0, pout) become pad: zero bytes.  z0 = pin: what the content
+      // vacates, or for a short row positions past the old width (nothing when
+      // shift <= 0).  z0 = 0 when the input pad may hold other bytes.
+      const int z0 = zero_pad ? 0 : pin;
+      if (pout > z0) {
+        const __amdgpu_buffer_rsrc_t rz = rsrc(base + (size_t)z0 * pos_bytes, (uint32_t)(pout - z0) * pos_bytes);
+        for (int f = t; f < (pout - z0) * U; f += kIpBlock) bst((i32x4)(0), rz, (uint32_t)f * 16u);
       }
       bst(e0, rc, (uint32_t)t * 16u);
       for (int f = t + kIpBlock; f < n * U; f += kIpBlock) bst(bld(ra, (uint32_t)f * 16u), rc, (uint32_t)f * 16u);

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecdec.so")
 
 F32, F16, BF16 = 0, 1, 2
-EQSPEC, GATHER, APPEND_INPLACE, EQSPEC_INPLACE = 0, 1, 2, 3
+EQSPEC, GATHER, APPEND_INPLACE, EQSPEC_INPLACE, EQSPEC_INPLACE_ZERO_PAD = 0, 1, 2, 3, 4
 OK, E_ARG, E_DTYPE, E_WORKSPACE, E_ALIAS, E_ALIGN, E_LAUNCH, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 S_DRAFT_RANGE, S_CAPACITY, S_LEN_RANGE, S_PROB, S_ROWS_DUP = 1, 2, 4, 8, 16
 
@@ -344,7 +344,7 @@ def specdec_realign_kv(mode, src, dst, rows=None, B=None, group=0, skip_group=No
             raise ValueError("skip_group needs one entry per group")
         if dst.width is not None and dst.width.numel() < ng:
             raise ValueError("the rectangle's width tensor needs one entry per group")
-    if mode in (EQSPEC, EQSPEC_INPLACE) and (src.width is None or dst.width is None or dst.pos is None or
+    if mode in (EQSPEC, EQSPEC_INPLACE, EQSPEC_INPLACE_ZERO_PAD) and (src.width is None or dst.width is None or dst.pos is None or
                                              dst.mask is None):
         raise ValueError("EQSPEC needs width on both sides and pos/mask on the output")
     rc = lib().specdec_realign_kv(mode, C.byref(src.c), C.byref(dst.c), _ptr(rows), B, group, _ptr(skip_group), D,
@@ -359,10 +359,12 @@ def realign_eqspec(src, dst, kv_new, draft, accept_len, next_token, pad_token=0,
                        pad_token, status)
 
 
-def realign_eqspec_inplace(buf, kv_new, draft, accept_len, next_token, pad_token=0, status=None):
-    """EQSPEC unpad-append-repad of rectangle `buf` in place (its pad must hold zero KV bytes)."""
-    specdec_realign_kv(EQSPEC_INPLACE, buf, buf, None, buf.rows, 0, None, kv_new, draft, accept_len, next_token,
-                       pad_token, status)
+def realign_eqspec_inplace(buf, kv_new, draft, accept_len, next_token, pad_token=0, status=None, zero_pad=False):
+    """EQSPEC unpad-append-repad of rectangle `buf` in place.  Its pad must hold
+    zero KV bytes, unless zero_pad=True, which writes the whole new pad with
+    zeros (for the first round after a prefill that wrote KV at pad positions)."""
+    specdec_realign_kv(EQSPEC_INPLACE_ZERO_PAD if zero_pad else EQSPEC_INPLACE, buf, buf, None, buf.rows, 0, None,
+                       kv_new, draft, accept_len, next_token, pad_token, status)
 
 
 def gather(pool, rect, rows, group, skip_group=None, pad_token=0, status=None):

@@ -113,7 +113,10 @@ def test_realign_host_errors():
     assert call(S.APPEND_INPLACE, src, dst) == S.E_ARG                         # not the same pool
     assert call(S.APPEND_INPLACE, src, src, kv_new=None) == S.E_ARG
     # the largest draft counts are rejected, never wrapped into a small size
-    for mode in (S.EQSPEC, S.EQSPEC_INPLACE, S.APPEND_INPLACE):
+    assert call(5, src, src) == S.E_ARG
+    assert call(S.EQSPEC_INPLACE_ZERO_PAD, src, dst) == S.E_ARG                # in place: the same buffers
+    assert call(S.EQSPEC_INPLACE_ZERO_PAD, src, src, kv_new=None) == S.E_ARG
+    for mode in (S.EQSPEC, S.EQSPEC_INPLACE, S.EQSPEC_INPLACE_ZERO_PAD, S.APPEND_INPLACE):
         assert call(mode, src, dst if mode == S.EQSPEC else src, D=2**31 - 1) == S.E_ARG
         assert call(mode, src, dst if mode == S.EQSPEC else src, D=2**27) == S.E_ARG
 

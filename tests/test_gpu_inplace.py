@@ -49,7 +49,7 @@ def _rect(rng, B, L, H, Dh, dt_np, lens, S, cap):
     return kv, tok, pos, mask
 
 
-def _check_inplace(sd, kv, tok, pos, mask, lens, S, kv_new, acc, draft, nxt, tdt, pad_token=0):
+def _check_inplace(sd, kv, tok, pos, mask, lens, S, kv_new, acc, draft, nxt, tdt, pad_token=0, zero_pad=False):
     """Runs the in-place realignment on the device copy of the rectangle and
     compares it with the oracle and with the input bytes past the new width."""
     B = lens.shape[0]
@@ -59,7 +59,7 @@ def _check_inplace(sd, kv, tok, pos, mask, lens, S, kv_new, acc, draft, nxt, tdt
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     sd.realign_eqspec_inplace(buf, from_np_raw(kv_new, tdt), torch.from_numpy(draft).cuda(),
                               torch.from_numpy(acc).cuda(), torch.from_numpy(nxt).cuda(), pad_token=pad_token,
-                              status=status)
+                              status=status, zero_pad=zero_pad)
     torch.cuda.synchronize()
     want = oracle.realign_eqspec(kv, kv_new, lens, S, tok, mask, acc, nxt, draft, pad_token=pad_token)
     W = want["width"]
@@ -232,6 +232,58 @@ def test_inplace_chain_8b_gqa(sd):
     cfg = synth.CONFIGS["8b-gqa"]
     _run_chain_inplace(sd, "8b-gqa", cfg.rounds, {0, 1, cfg.rounds // 2, cfg.rounds - 1},
                        [0, cfg.L // 2, cfg.L - 1])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_inplace_zero_pad_garbage_input_pad(sd, seed):
+    """An input whose pad positions hold arbitrary bytes (as a left-padded
+    prefill leaves them): the zero-pad mode gives the EQSPEC result on [0, S')
+    byte for byte, rows that move either way and rows that only append alike;
+    positions past the new width keep their bytes."""
+    rng = np.random.default_rng(1300 + seed)
+    dt_np, tdt, Dh = _GEOMS[seed % len(_GEOMS)]
+    U = Dh * np.dtype(dt_np).itemsize // 16
+    B = int(rng.integers(2, 12))
+    D = int(rng.integers(0, 6))
+    L, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    maxlen = 60 if U == 256 else int(rng.integers(20, 700))
+    lens = rng.integers(0, maxlen, B).astype(np.int32)
+    lens[0] = 0 if seed % 2 else lens[0]
+    S = int(lens.max()) + (int(rng.integers(0, 100)) if seed % 3 == 0 else 0)
+    cap = S + D + 1 + int(rng.integers(0, 4))
+    say("inplace zero pad", seed, B, D, L, H, Dh, S, cap)
+    kv, tok, pos, mask = _rect(rng, B, L, H, Dh, dt_np, lens, S, cap)
+    raw = kv.view(np.uint8)
+    for b in range(B):   # garbage bytes on every row's pad, all layers, K and V, heads
+        nb = (S - lens[b]) * Dh * np.dtype(dt_np).itemsize
+        if nb:
+            raw[:, :, b, :, :nb] = rng.integers(0, 256, raw[:, :, b, :, :nb].shape, dtype=np.uint8)
+    kv_new = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(dt_np)
+    acc = rng.integers(0, D + 1, B).astype(np.int32)
+    draft = rng.integers(1, 500, (B, D)).astype(np.int32)
+    nxt = rng.integers(1, 500, B).astype(np.int32)
+    _check_inplace(sd, kv, tok, pos, mask, lens, S, kv_new, acc, draft, nxt, tdt, zero_pad=True)
+
+
+def test_inplace_default_mode_keeps_garbage_pad(sd):
+    """The default in-place mode leaves bytes below both the old and the new pad
+    untouched: the precondition (a zero input pad) is real, and the zero-pad
+    mode is the one for such inputs."""
+    rng = np.random.default_rng(1400)
+    B, D, L, H, Dh = 3, 2, 1, 1, 8
+    lens = np.array([4, 9, 6], np.int32)
+    S, cap = 9, 14
+    kv, tok, pos, mask = _rect(rng, B, L, H, Dh, np.float16, lens, S, cap)
+    kv[:, :, 0, :, :S - lens[0]] = 7.0            # row 0: pad 5, new pad >= 5 - 3
+    buf = sd.SeqBuf(from_np_raw(kv, torch.float16), torch.from_numpy(tok).cuda(),
+                    torch.from_numpy(lens).cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(mask).cuda(),
+                    torch.tensor([S], dtype=torch.int32, device="cuda"))
+    kv_new = torch.zeros((L, 2, B, H, D + 1, Dh), dtype=torch.float16, device="cuda")
+    acc = torch.tensor([0, 2, 1], dtype=torch.int32, device="cuda")  # S' = 12; row 0's new pad is 7
+    z = torch.zeros((B, D), dtype=torch.int32, device="cuda")
+    sd.realign_eqspec_inplace(buf, kv_new, z, acc, torch.ones(B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert bool((buf.kv[0, :, 0, :, :5].float() == 7.0).all()), "positions [0, 5) of row 0 were rewritten"
 
 
 def test_inplace_status_bits_write_nothing(sd):
