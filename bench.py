@@ -725,12 +725,13 @@ def bench_stoch(args, cfg):
     acc = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
     nxt = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sws = sd.sample_verify_workspace(cfg.B, cfg.D, cfg.V)
 
     def run(n, ev=None):
         for r in range(n):
             if ev:
                 ev[r][0].record()
-            sd.verify_sample(dp, dq, dd, dua, dud, status=status, accept_len=acc, next_token=nxt)
+            sd.verify_sample(dp, dq, dd, dua, dud, status=status, accept_len=acc, next_token=nxt, ws=sws)
             if ev:
                 ev[r][1].record()
             sd.realign_eqspec(src, dst, kv_new, dd, acc, nxt, status=status)
@@ -756,6 +757,16 @@ def bench_stoch(args, cfg):
     rbytes = float(rb[0])
     re_gbs = rbytes / (re_ms.mean() * 1e-3) / 1e9
     ve_gbs = vbytes / (ver_ms.mean() * 1e-3) / 1e9
+    # sampled verification alone: K launches queued behind a spin kernel, events
+    # around the pass (no per-launch event, nothing between the launches)
+    torch.cuda._sleep(SPIN_CYCLES_PER_LAUNCH * K)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(K):
+        sd.verify_sample(dp, dq, dd, dua, dud, status=status, accept_len=acc, next_token=nxt, ws=sws)
+    a1.record()
+    torch.cuda.synchronize()
+    ver_alone_us = a0.elapsed_time(a1) * 1e3 / K
     logits_legs = _time_sample_logits(cfg, K)
     cpu = None
     if not args.no_cpu:
@@ -798,8 +809,16 @@ def bench_stoch(args, cfg):
                           "one sampled verify + EQSPEC round repeated" % (cfg.B, cfg.D, cfg.V, cfg.L, cfg.H, cfg.Dh,
                                                                          cfg.len_lo, cfg.len_hi),
               "B": cfg.B, "D": cfg.D, "V": cfg.V, "cap": cfg.cap, "global_batch": cfg.B}
+    vroof = _roof("k_verify_sample", ve_gbs, vbytes, float(ver_ms.mean() * 1e3))
+    vroof["alone"] = {"pass_avg_us": ver_alone_us, "gbs": vbytes / (ver_alone_us * 1e-6) / 1e9,
+                      "frac": vbytes / (ver_alone_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                      "how": "%d launches queued behind a spin kernel, events around the pass" % K}
     extra = {"verify": {"kernel": "k_verify_sample", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
-                        "algorithmic_bytes_per_launch": vbytes, "avg_launch_us": float(ver_ms.mean() * 1e3)},
+                        "algorithmic_bytes_per_launch": vbytes, "avg_launch_us": float(ver_ms.mean() * 1e3),
+                        "roofline": vroof},
+             "cycle": cycle_stats(a[None, :], cfg.D, K / (total_ms * 1e-3)),
+             "memory": device_memory(dev),
+             "host": host_info(),
              "verify_from_logits": logits_legs,
              "realign_share_of_round": float(re_ms.sum() / total_ms)}
     return _line("sampled verify+realign rounds/sec and realign HBM GB/s (stoch, B=32)", K / (total_ms * 1e-3), K, W,

@@ -139,6 +139,14 @@ int specdec_verify_greedy_noalloc(const void *logits, int dtype, int64_t row_str
                                   const int32_t *draft, int32_t *accept_len, int32_t *next_token,
                                   int32_t *target_tok, int32_t *status, void *stream);
 
+/* Bytes of the workspace specdec_verify_sample needs for B rows: B blocks of
+ * 65,920 bytes, one per batch row at a place that depends on the row alone (a
+ * 128-byte counter line, 16 bytes for each of the row's at most 16 splits, then
+ * 16 bytes for each of its at most 16 x 256 runs of ids).  A workspace sized for B rows therefore serves any later call
+ * with at most B rows, whatever its D and V.  Returns 0 for sizes the call
+ * rejects (B < 0, D < 0, V < 1, B or V > 2^30). */
+size_t specdec_verify_sample_workspace_bytes(int B, int D, int V);
+
 /* Sampled verification (speculative sampling; "Inference Engineering Part
  * 5/8", section "Exactness Means Different Things For Greedy And Sampled
  * Output": accept with probability min(1, p(x)/q(x)), replace from
@@ -158,10 +166,15 @@ int specdec_verify_greedy_noalloc(const void *logits, int dtype, int64_t row_str
  *              exceeds u * sum(w).  A zero sum falls back to p; an all-zero row
  *              gives id 0 and SPECDEC_S_PROB.
  *  accept_len, next_token  device int32 [B] out, as for greedy verification.
- * B = 0 is a no-op.  Errors: E_ARG, E_LAUNCH. */
+ *  ws          device workspace of at least
+ *              specdec_verify_sample_workspace_bytes(B, D, V) bytes, 16-byte
+ *              aligned, cleared once by specdec_workspace_init; every call
+ *              leaves its counters cleared again.
+ * Each batch row is spread over up to 16 workgroups; the last to finish draws.
+ * B = 0 is a no-op.  Errors: E_ARG (also D > 255), E_WORKSPACE, E_LAUNCH. */
 int specdec_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
                           const float *u_accept, const float *u_draw, int32_t *accept_len,
-                          int32_t *next_token, int32_t *status, void *stream);
+                          int32_t *next_token, void *ws, size_t ws_bytes, int32_t *status, void *stream);
 
 /* Bytes of the workspace specdec_verify_sample_logits needs for B rows, D
  * drafts and V logits per row. */

@@ -117,25 +117,39 @@ EXPORT int specdec_verify_greedy_noalloc(const void *logits, int dtype, int64_t 
                                SPECDEC_STATIC_SCRATCH_BYTES, status, stream);
 }
 
+// sampled verification's workspace: a fixed-size block per batch row (a
+// counter line and the row's run masses), so one workspace serves any later
+// call with as many rows or fewer, whatever its D and V
+EXPORT size_t specdec_verify_sample_workspace_bytes(int B, int D, int V) {
+  if (B < 0 || D < 0 || V < 1 || (long long)B > (1LL << 30) || (long long)V > (1LL << 30)) return 0;
+  return (size_t)B * sd::kSampleRowBytes;
+}
+
 EXPORT int specdec_verify_sample(const float *p, const float *q, int B, int D, int V, const int32_t *draft,
                                  const float *u_accept, const float *u_draw, int32_t *accept_len,
-                                 int32_t *next_token, int32_t *status, void *stream) {
-  if (B < 0 || D < 0 || V < 1) return SPECDEC_E_ARG;
+                                 int32_t *next_token, void *ws, size_t ws_bytes, int32_t *status, void *stream) {
+  if (B < 0 || D < 0 || D > 255 || V < 1) return SPECDEC_E_ARG;
   if (B == 0) return SPECDEC_OK;
   if (!p || !u_draw || !accept_len || !next_token || (D > 0 && (!q || !draft || !u_accept))) return SPECDEC_E_ARG;
   if ((long long)B > (1LL << 30) || (long long)V > (1LL << 30)) return SPECDEC_E_ARG;
+  const size_t need = specdec_verify_sample_workspace_bytes(B, D, V);
+  if (need == 0) return SPECDEC_E_ARG;
+  if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16 != 0) return SPECDEC_E_WORKSPACE;
   sd::SampleParams s;
   s.p = p;
   s.q = q;
   s.B = B;
   s.D = D;
   s.V = V;
+  sd::sample_shape(V, s.R, s.S);
   s.draft = draft;
   s.u_accept = u_accept;
   s.u_draw = u_draw;
   s.accept_len = accept_len;
   s.next_token = next_token;
   s.status = status;
+  if ((long long)B * s.S >= (1LL << 31)) return SPECDEC_E_ARG;
+  s.ws = static_cast<char *>(ws);
   return launched(sd::launch_verify_sample(s, as_stream(stream)));
 }
 

@@ -33,10 +33,21 @@ constexpr int kCountStride = kAtomicLine / 4;
 struct SampleParams {
   const float *p, *q;
   int B, D, V;
+  int R, S;                   // ids per run, splits (workgroups) per batch row
   const int32_t *draft;
   const float *u_accept, *u_draw;
   int32_t *accept_len, *next_token, *status;
+  // workspace: one block of kSampleRowBytes per batch row, at a place that
+  // depends on the row alone: a counter line (zero between calls), then the
+  // (residual, p) mass of each of the row's S splits (kSampleSplits slots),
+  // then of each of its S * kSampleThreads runs
+  char *ws;
 };
+
+constexpr int kSampleThreads = 256;  // threads per sampled-verification workgroup (one run each)
+constexpr int kSampleSplits = 16;    // workgroups per batch row at most (runs grow with V beyond 32768)
+constexpr size_t kSampleRowBytes = kAtomicLine + (size_t)kSampleSplits * 16 + (size_t)kSampleSplits * kSampleThreads * 16;
+void sample_shape(int V, int &R, int &S);
 
 struct SampleLogitsParams {
   const void *target, *draftl;  // logits [B][D+1][V] and [B][D][V] of `dtype`

@@ -280,10 +280,11 @@ hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s) {
 
 // ---------------------------------------------------------------- sampled
 
-constexpr int kSampleThreads = 1024;  // threads per sampled-verification workgroup (one per batch row)
-constexpr int kSampleBatch = 8;       // 16-byte vectors (of p and of q) a thread has in flight
+constexpr int kSampleBatch = 8;  // 16-byte vectors (of p and of q) a thread has in flight
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+constexpr int kCoherentPolicy = 16;  // buffer cache policy sc1: through to the device's coherence point
 
 // Residual mass max(0, p - q) of one id in fp64 (q absent: p).
 __device__ __forceinline__ double resid_w(float pv, float qv, bool has_q) {
@@ -291,52 +292,50 @@ __device__ __forceinline__ double resid_w(float pv, float qv, bool has_q) {
   return d > 0.0 ? d : 0.0;
 }
 
-// The fp64 sum of this thread's run [lo, hi) of weights, in id order, and its
-// last id with a positive weight (-1 if none).  VW = 4: the run starts on a
-// 16-byte boundary and is read as vectors, kSampleBatch of p (and of q) in
-// flight at once.
-template <int VW>
-__device__ __forceinline__ double run_mass(const float *pa, const float *qa, int lo, int hi, int &last) {
-  double m = 0.0;
-  last = -1;
+// The fp64 sums of one run [lo, hi) of ids, in id order: of the residual
+// weights w = max(0, p - q) (q absent: w = p) into mw, and of max(0, p) into mp
+// (the fallback when the residual has no mass).  VW = 4: the run starts on a
+// 16-byte boundary and is read as vectors, NB of p (and of q) in flight at once.
+template <int VW, int NB>
+__device__ __forceinline__ void run_mass(const float *pa, const float *qa, int lo, int hi, double &mw, double &mp) {
+  mw = 0.0;
+  mp = 0.0;
   if constexpr (VW == 4) {
-    for (int v0 = lo; v0 < hi; v0 += 4 * kSampleBatch) {
-      f32x4 pp[kSampleBatch], qq[kSampleBatch];
+    for (int v0 = lo; v0 < hi; v0 += 4 * NB) {
+      f32x4 pp[NB], qq[NB];
 #pragma unroll
-      for (int k = 0; k < kSampleBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
         const int v = min(v0 + 4 * k, hi - 4);  // in range: a repeated load, never used
-        pp[k] = *reinterpret_cast<const f32x4 *>(pa + v);
-        qq[k] = qa ? *reinterpret_cast<const f32x4 *>(qa + v) : (f32x4)(0.0f);
+        pp[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(pa + v));
+        qq[k] = qa ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(qa + v)) : (f32x4)(0.0f);
       }
 #pragma unroll
-      for (int k = 0; k < kSampleBatch; ++k) {
-        const int v = v0 + 4 * k;
-        if (v >= hi) break;
+      for (int k = 0; k < NB; ++k) {
+        if (v0 + 4 * k >= hi) break;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const double w = resid_w(pp[k][e], qq[k][e], qa != nullptr);
-          m += w;
-          if (w > 0.0) last = v + e;
+          mw += resid_w(pp[k][e], qq[k][e], qa != nullptr);
+          mp += resid_w(pp[k][e], 0.0f, false);
         }
       }
     }
   } else {
     for (int v = lo; v < hi; ++v) {
-      const double w = resid_w(pa[v], qa ? qa[v] : 0.0f, qa != nullptr);
-      m += w;
-      if (w > 0.0) last = v;
+      mw += resid_w(pa[v], qa ? qa[v] : 0.0f, qa != nullptr);
+      mp += resid_w(pa[v], 0.0f, false);
     }
   }
-  return m;
 }
 
 // The first id of the run [lo, hi) at which before + (the run's weights summed
-// in id order, as run_mass sums them) passes target, or -1: the same loads in
-// the same batches, so the partial sums end exactly at run_mass's result.
+// in id order, as run_mass sums them) passes target; else the run's last id
+// with a positive weight (-1 if none).  The same loads in the same batches, so
+// the partial sums end exactly at run_mass's result.
 template <int VW>
 __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo, int hi, double before,
                                         double target) {
   double c = 0.0;
+  int last = -1;
   if constexpr (VW == 4) {
     for (int v0 = lo; v0 < hi; v0 += 4 * kSampleBatch) {
       f32x4 pp[kSampleBatch], qq[kSampleBatch];
@@ -352,46 +351,87 @@ __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo
         if (v >= hi) break;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          c += resid_w(pp[k][e], qq[k][e], qa != nullptr);
+          const double w = resid_w(pp[k][e], qq[k][e], qa != nullptr);
+          c += w;
+          if (w > 0.0) last = v + e;
           if (before + c > target) return v + e;
         }
       }
     }
   } else {
     for (int v = lo; v < hi; ++v) {
-      c += resid_w(pa[v], qa ? qa[v] : 0.0f, qa != nullptr);
+      const double w = resid_w(pa[v], qa ? qa[v] : 0.0f, qa != nullptr);
+      c += w;
+      if (w > 0.0) last = v;
       if (before + c > target) return v;
     }
   }
-  return -1;
+  return last;
 }
 
-// One 1024-thread workgroup per batch row b.  Acceptance of every draft is
-// evaluated in parallel (first rejection by an LDS min).  Then one pass over
-// the stop row: thread t sums the weights of its run of consecutive ids (runs
-// of ceil(V / 1024) ids rounded up to a multiple of 4) in id order, in fp64.
-// A block scan of the run sums in thread order gives T and each run's starting
-// mass; the draw target u * T falls in the first run whose end passes it, and
-// that run's own thread walks it again in the same order from the run's
-// starting mass, so its partial sums end exactly at the mass the choice used
-// and the crossing id is found inside the run.  A zero residual falls back to
-// p at the stop position; no crossing (rounding at the top of the row) takes
-// the last id with positive weight.
-template <int VW>
+// Sampled verification spread over the chip: batch row b's stop row is cut
+// into S splits of kSampleThreads runs of R consecutive ids (run g = split *
+// kSampleThreads + thread covers ids [g R, g R + R)); one workgroup per (split,
+// batch row), numbered split-major.
+//  1. Every workgroup of row b evaluates the acceptance of each draft (u q(x)
+//     <= p(x), exactly, in fp64) and takes the first rejection a (the stop
+//     position); it is the same in every workgroup.
+//  2. Each thread sums its run of the stop row in id order in fp64: the
+//     residual weights max(0, p_a - q_a) (p_D for the bonus) and, for the
+//     fallback, p_a.  The workgroup adds its runs' sums in a fixed order into
+//     the split's totals.  Run sums and split totals go to row b's workspace
+//     block.
+//  3. The workgroup counts itself in row b's counter; the last of the S to
+//     arrive draws.  Every thread adds the split totals in split order (the
+//     same arithmetic in every thread): the total T, and the first split whose
+//     end passes the target u_draw[a] * T.  That split's run sums are loaded,
+//     one per thread, and scanned in thread order; the first run whose end
+//     passes the target is walked again, id by id in the order step 2 summed
+//     it, from its starting mass, so the partial sums end exactly at the run's
+//     sum and the crossing id lies inside it.  Rounding that leaves no crossing
+//     takes the last id with positive weight.  A zero residual falls back to
+//     p_a; an all-zero row gives id 0 and SPECDEC_S_PROB.
+// Ordering.  Sums are stored and loaded with the sc1 cache policy (written
+// through to, and read from, the device's coherence point, past the
+// non-coherent L2), and every thread waits for its stores to complete (vmcnt)
+// before the workgroup's barrier; the count is issued after it, and the last
+// workgroup loads the sums only after its own count has returned.  As with
+// greedy verification's finish, this rests on gfx950's ordering, not on a
+// release/acquire pair, whose L2 write-back and invalidate would cost more
+// than the whole call.
+__device__ __forceinline__ void st_pair(__amdgpu_buffer_rsrc_t r, uint32_t off, double a, double b) {
+  const long long la = __double_as_longlong(a), lb = __double_as_longlong(b);
+  const i32x4v v = {(int)la, (int)(la >> 32), (int)lb, (int)(lb >> 32)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherentPolicy);
+}
+
+__device__ __forceinline__ void ld_pair(__amdgpu_buffer_rsrc_t r, uint32_t off, double &a, double &b) {
+  const i32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentPolicy);
+  a = __longlong_as_double(((long long)(unsigned)v[1] << 32) | (unsigned)v[0]);
+  b = __longlong_as_double(((long long)(unsigned)v[3] << 32) | (unsigned)v[2]);
+}
+
+template <int VW, int NB>
 __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p) {
   constexpr int NW = kSampleThreads / kWave;
-  const int b = blockIdx.x;
+  const int B = p.B, S = p.S, R = p.R;
+  const int split = (int)blockIdx.x / B;
+  const int b = (int)blockIdx.x - split * B;
   const int D = p.D, D1 = p.D + 1, V = p.V;
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  __shared__ int s_a, s_bad, s_last;
-  __shared__ double s_wt[NW];
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+  __shared__ int s_a, s_bad, s_last, s_sel;
+  __shared__ double s_w[NW], s_p[NW];
   __shared__ int s_i[NW];
-  if (threadIdx.x == 0) {
+  __shared__ float s_ud;
+  if (t == 0) {
     s_a = D;
     s_bad = 0;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < D; i += kSampleThreads) {
+  // the draw's uniform at every possible stop position, loaded with the
+  // acceptance inputs (D + 1 <= kSampleThreads) and kept for the stop position
+  const float ud = t <= D ? p.u_draw[(size_t)b * D1 + t] : 0.0f;
+  for (int i = t; i < D; i += kSampleThreads) {
     const int x = p.draft[(size_t)b * D + i];
     bool ok = false;
     if (x >= 0 && x < V) {
@@ -406,64 +446,147 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
   }
   __syncthreads();
   const int a = s_a;
+  if (t == a) s_ud = ud;
   const float *pa = p.p + ((size_t)b * D1 + a) * V;
   const float *qa = a < D ? p.q + ((size_t)b * D + a) * V : nullptr;
-  const int R = ((V + kSampleThreads - 1) / kSampleThreads + 3) / 4 * 4;  // ids per run
-  const int lo = min(V, (int)threadIdx.x * R), hi = min(V, lo + R);
+  char *blk = p.ws + (size_t)b * kSampleRowBytes;
+  unsigned int *counter = reinterpret_cast<unsigned int *>(blk);
+  // (residual, p) totals of every split, then of every run: 16 bytes each
+  const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(blk + kAtomicLine, (short)0,
+                                                                      kSampleSplits * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      blk + kAtomicLine + kSampleSplits * 16, (short)0, kSampleSplits * kSampleThreads * 16, 0x00020000);
 
-  double T = 0.0, before = 0.0, m = 0.0;
-  int last = -1;
-  for (int pass = 0; pass < 2; ++pass) {
-    m = run_mass<VW>(pa, qa, lo, hi, last);
-    // run sums in thread order: exclusive prefix `before` and total T
-    double incl = wave_incl_scan(m, lane);
-    if (lane == kWave - 1) s_wt[wv] = incl;
-    __syncthreads();
-    T = 0.0;
-    before = incl - m;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      if (k < wv) before += s_wt[k];
-      T += s_wt[k];
+  // 2. this thread's run of the stop row, and the split's totals
+  {
+    const int g = split * kSampleThreads + t;
+    const int lo = min(V, g * R), hi = min(V, lo + R);
+    double mw, mp;
+    run_mass<VW, NB>(pa, qa, lo, hi, mw, mp);
+    st_pair(rr, (uint32_t)g * 16u, mw, mp);
+    const double ww = wave_sum(mw), wp = wave_sum(mp);
+    if (lane == 0) {
+      s_w[wv] = ww;
+      s_p[wv] = wp;
     }
     __syncthreads();
-    if (T > 0.0 || qa == nullptr) break;
-    qa = nullptr;  // zero residual mass: fall back to p at this position
+    if (t == 0) {
+      double tw = 0.0, tp = 0.0;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        tw += s_w[k];
+        tp += s_p[k];
+      }
+      st_pair(rt, (uint32_t)split * 16u, tw, tp);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  __syncthreads();
+  if (t == 0) s_last = atomicAdd(counter, 1u) == (unsigned)(S - 1);
+  __syncthreads();
+  if (!s_last) return;
 
+  // 3. the draw, by the last of row b's workgroups: the split totals in split
+  // order (every thread alike)
+  double sw[kSampleSplits], sp[kSampleSplits];
+#pragma unroll
+  for (int k = 0; k < kSampleSplits; ++k) {
+    if (k < S) ld_pair(rt, (uint32_t)k * 16u, sw[k], sp[k]);
+    else sw[k] = sp[k] = 0.0;
+  }
+  double Tw = 0.0, Tp = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampleSplits; ++k) {
+    Tw += sw[k];
+    Tp += sp[k];
+  }
+  const bool use_p = !(Tw > 0.0);  // zero residual: fall back to p at the stop position
+  const double T = use_p ? Tp : Tw;
+  const float *qw = use_p ? nullptr : qa;
   int j = 0;
   if (T > 0.0) {
-    const double target = (double)p.u_draw[(size_t)b * D1 + a] * T;
-    const bool cross = m > 0.0 && before + m > target;
-    const int run = block_min_int<kSampleThreads>(cross ? (int)threadIdx.x : INT_MAX, s_i);
-    const int lastpos = block_max_int<kSampleThreads>(last, s_i);
-    if (run == INT_MAX) {
-      if (threadIdx.x == 0) s_last = lastpos;
-    } else if ((int)threadIdx.x == run) {
-      // this thread's run again, same order: the first id whose cumulative mass passes the target
-      const int hit = run_walk<VW>(pa, qa, lo, hi, before, target);
-      s_last = hit >= 0 ? hit : last;  // (always found: the partial sums end at m)
+    const double target = (double)s_ud * T;
+    // the first split whose end passes the target (else the last with mass)
+    double P = 0.0, Plast = 0.0;
+    int ss = -1, slast = 0;
+#pragma unroll
+    for (int k = 0; k < kSampleSplits; ++k) {
+      const double m = use_p ? sp[k] : sw[k];
+      if (k < S && ss < 0) {
+        if (m > 0.0) {
+          slast = k;
+          Plast = P;
+          if (P + m > target) ss = k;
+        }
+        if (ss < 0) P += m;
+      }
+    }
+    const bool found = ss >= 0;
+    if (!found) {
+      ss = slast;
+      P = Plast;
+    }
+    const double tgt = found ? target : INFINITY;  // no crossing: walk to the last id with mass
+    // that split's runs, one per thread, scanned in thread order
+    const int g = ss * kSampleThreads + t;
+    double rw, rp;
+    ld_pair(rr, (uint32_t)g * 16u, rw, rp);
+    const double m = use_p ? rp : rw;
+    const double incl = wave_incl_scan(m, lane);
+    if (lane == kWave - 1) s_w[wv] = incl;
+    __syncthreads();
+    double before = P + (incl - m);
+    {
+      double e = 0.0;
+#pragma unroll
+      for (int k = 0; k < NW; ++k)
+        if (k < wv) e += s_w[k];
+      before = P + (e + (incl - m));
+    }
+    const bool cross = m > 0.0 && before + m > tgt;
+    const int who = block_min_int<kSampleThreads>(cross ? t : INT_MAX, s_i);
+    const int lastt = block_max_int<kSampleThreads>(m > 0.0 ? t : -1, s_i);
+    const int me = who != INT_MAX ? who : lastt;
+    if (t == me) {
+      const int lo = min(V, g * R), hi = min(V, lo + R);
+      const int hit = run_walk<VW>(pa, qw, lo, hi, before, who != INT_MAX ? tgt : INFINITY);
+      s_sel = hit >= 0 ? hit : 0;
     }
     __syncthreads();
-    j = s_last;
-  } else if (threadIdx.x == 0) {
+    j = s_sel;
+  } else if (t == 0) {
     atomicOr(&s_bad, SPECDEC_S_PROB);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     p.accept_len[b] = a;
     p.next_token[b] = j;
+    store_agent(counter, 0u);
     set_status(p.status, s_bad);
   }
+}
+
+// Ids per run and splits per row of sampled verification: runs of at least 8
+// ids (a multiple of 4), long enough that a row needs at most kSampleSplits
+// workgroups (R >= V / (kSampleSplits * kSampleThreads), so S <= kSampleSplits).
+void sample_shape(int V, int &R, int &S) {
+  const long per = ((long)V + (long)kSampleSplits * kSampleThreads - 1) / ((long)kSampleSplits * kSampleThreads);
+  R = (int)((per < 8 ? 8 : per) + 3) / 4 * 4;
+  S = (int)(((long)V + (long)kSampleThreads * R - 1) / ((long)kSampleThreads * R));
+  if (S < 1) S = 1;
 }
 
 hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s) {
   const bool vec = p.V % 4 == 0 && reinterpret_cast<uintptr_t>(p.p) % 16 == 0 &&
                    (p.q == nullptr || reinterpret_cast<uintptr_t>(p.q) % 16 == 0);
-  if (vec)
-    hipLaunchKernelGGL(k_verify_sample<4>, dim3((unsigned)p.B), dim3(kSampleThreads), 0, s, p);
+  const dim3 grid((unsigned)((long)p.B * p.S));
+  // vectors in flight per batch of a run: all of a run of 8 ids, else 8
+  if (vec && p.R == 8)
+    hipLaunchKernelGGL((k_verify_sample<4, 2>), grid, dim3(kSampleThreads), 0, s, p);
+  else if (vec)
+    hipLaunchKernelGGL((k_verify_sample<4, kSampleBatch>), grid, dim3(kSampleThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(k_verify_sample<1>, dim3((unsigned)p.B), dim3(kSampleThreads), 0, s, p);
+    hipLaunchKernelGGL((k_verify_sample<1, 1>), grid, dim3(kSampleThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ EXPORTS = ("specdec_version", "specdec_workspace_bytes", "specdec_workspace_init
            "specdec_verify_sample", "specdec_sample_workspace_bytes", "specdec_verify_sample_logits",
            "specdec_realign_kv", "specdec_group_by_len", "specdec_paged_append", "specdec_paged_gather",
            "specdec_paged_admit", "specdec_paged_retire", "specdec_group_by_len_ids", "specdec_pool_finish",
-           "specdec_pool_admit", "specdec_verify_greedy_noalloc")
+           "specdec_pool_admit", "specdec_verify_greedy_noalloc", "specdec_verify_sample_workspace_bytes")
 
 
 class SpecDecError(RuntimeError):
@@ -59,7 +59,9 @@ def lib():
         L.specdec_workspace_init.argtypes = [vp, sz, vp]
         L.specdec_verify_greedy.argtypes = [vp, ci, i64, ci, ci, ci, vp, vp, vp, vp, vp, sz, vp, vp]
         L.specdec_verify_greedy_noalloc.argtypes = [vp, ci, i64, ci, ci, ci, vp, vp, vp, vp, vp, vp]
-        L.specdec_verify_sample.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+        L.specdec_verify_sample.argtypes = [vp, vp, ci, ci, ci, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.specdec_verify_sample_workspace_bytes.argtypes = [ci, ci, ci]
+        L.specdec_verify_sample_workspace_bytes.restype = sz
         L.specdec_sample_workspace_bytes.argtypes = [ci, ci, ci]
         L.specdec_sample_workspace_bytes.restype = sz
         L.specdec_verify_sample_logits.argtypes = [vp, vp, ci, ci, ci, ci, C.c_float, C.c_float, vp, vp, vp, vp, vp,
@@ -199,7 +201,18 @@ def specdec_verify_greedy_noalloc(logits, draft, accept_len, next_token, status=
     return accept_len, next_token
 
 
-def specdec_verify_sample(p, q, draft, u_accept, u_draw, status=None, accept_len=None, next_token=None):
+def sample_verify_workspace(B, D, V, device="cuda"):
+    """A cleared workspace for sampled verification of B rows, D drafts, V ids
+    (reusable by later calls on the same stream)."""
+    n = int(lib().specdec_verify_sample_workspace_bytes(B, D, V))
+    if n == 0:
+        raise SpecDecError(E_ARG, "specdec_verify_sample_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib().specdec_workspace_init(ws.data_ptr(), ws.numel(), _stream()), "specdec_workspace_init")
+    return ws
+
+
+def specdec_verify_sample(p, q, draft, u_accept, u_draw, status=None, accept_len=None, next_token=None, ws=None):
     """Sampled verification: p [B, D+1, V], q [B, D, V] float32 probabilities,
     uniforms u_accept [B, D] and u_draw [B, D+1].  Returns (accept_len, next_token)."""
     _need(p, "p", torch.float32)
@@ -216,8 +229,14 @@ def specdec_verify_sample(p, q, draft, u_accept, u_draw, status=None, accept_len
     accept_len = _i32(B, dev) if accept_len is None else _out(accept_len, "accept_len", B, device=dev)
     next_token = _i32(B, dev) if next_token is None else _out(next_token, "next_token", B, device=dev)
     _out(status, "status", 1, device=dev)
+    if B == 0:
+        ws_ptr, ws_n = None, 0
+    else:
+        ws = sample_verify_workspace(B, D, V, dev) if ws is None else _out(ws, "ws", 1, torch.uint8, device=dev)
+        ws_ptr, ws_n = ws.data_ptr(), ws.numel()
     rc = lib().specdec_verify_sample(p.data_ptr(), q.data_ptr(), B, D, V, draft.data_ptr(), u_accept.data_ptr(),
-                                     u_draw.data_ptr(), _ptr(accept_len), _ptr(next_token), _ptr(status), _stream())
+                                     u_draw.data_ptr(), _ptr(accept_len), _ptr(next_token), ws_ptr, ws_n,
+                                     _ptr(status), _stream())
     _check(rc, "specdec_verify_sample")
     return accept_len, next_token
 

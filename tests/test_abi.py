@@ -77,12 +77,29 @@ def test_verify_greedy_host_errors():
 
 
 def test_verify_sample_host_errors():
-    f = S.lib().specdec_verify_sample
-    assert f(FAKE, FAKE, -1, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
-    assert f(FAKE, FAKE, 2, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
-    assert f(None, FAKE, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
-    assert f(FAKE, None, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.E_ARG
-    assert f(FAKE, FAKE, 0, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == S.OK
+    L = S.lib()
+    f = L.specdec_verify_sample
+    need = L.specdec_verify_sample_workspace_bytes(2, 2, 10)
+    assert f(FAKE, FAKE, -1, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None, None) == S.E_ARG
+    assert f(FAKE, FAKE, 2, 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None, None) == S.E_ARG
+    assert f(None, FAKE, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None, None) == S.E_ARG
+    assert f(FAKE, None, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None, None) == S.E_ARG
+    assert f(FAKE, FAKE, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None, None) == S.E_WORKSPACE
+    assert f(FAKE, FAKE, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None, None) == S.E_WORKSPACE
+    assert f(FAKE, FAKE, 2, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, need, None, None) == S.E_WORKSPACE
+    assert f(FAKE, FAKE, 2, 256, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None, None) == S.E_ARG   # D > 255
+    assert f(FAKE, FAKE, 0, 2, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == S.OK
+
+
+def test_verify_sample_workspace_size():
+    L = S.lib()
+    # a fixed block per row: a counter line, then 16 bytes for each of at most 16 splits and 16 x 256 runs
+    row = 128 + 16 * 16 + 16 * 256 * 16
+    assert L.specdec_verify_sample_workspace_bytes(32, 8, 32000) == 32 * row
+    assert L.specdec_verify_sample_workspace_bytes(1, 0, 1) == row
+    assert L.specdec_verify_sample_workspace_bytes(3, 2, 151936) == 3 * row
+    assert L.specdec_verify_sample_workspace_bytes(-1, 2, 10) == 0
+    assert L.specdec_verify_sample_workspace_bytes(1, 2, 0) == 0
 
 
 def _sb(kv=FAKE, rows=4, cap=64, layers=2, heads=2, head_dim=128, dtype=S.BF16, tokens=FAKE, pos=FAKE, mask=FAKE,

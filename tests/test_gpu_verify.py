@@ -218,6 +218,85 @@ def test_sample_random_small(sd, seed):
     _check_sampled(p, q, draft, u_acc, u_draw, acc.cpu().numpy(), nxt.cpu().numpy())
 
 
+@pytest.mark.parametrize("V", [32000, 151936, 100003, 65537, 4097])
+def test_sample_many_splits(sd, V):
+    """Rows spread over many workgroups (up to 16 splits of 256 runs; an odd V
+    takes the scalar path): peaked and flat rows, draws near the top and the
+    bottom of the cumulative mass, all against the oracle within the band."""
+    rng = np.random.default_rng(V)
+    B, D = 6, 3
+    say("sample many splits", V)
+    logits = rng.standard_normal((B, D + 1, V)) * np.array([0.5, 2.0, 4.0, 1.0, 3.0, 0.1])[:, None, None]
+    p = np.exp(logits - logits.max(-1, keepdims=True))
+    p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+    ql = logits[:, :D] + 0.5 * rng.standard_normal((B, D, V))
+    q = np.exp(ql - ql.max(-1, keepdims=True))
+    q = (q / q.sum(-1, keepdims=True)).astype(np.float32)
+    qd = q.astype(np.float64)
+    qd /= qd.sum(-1, keepdims=True)
+    draft = np.array([[int(rng.choice(V, p=qd[b, i])) for i in range(D)] for b in range(B)], np.int32)
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    u_draw[0] = 1.0 - 2.0 ** -24   # the top of the mass
+    u_draw[1] = 0.0                # the bottom
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)), status=status)
+    torch.cuda.synchronize()
+    _check_sampled(p, q, draft, u_acc, u_draw, acc.cpu().numpy(), nxt.cpu().numpy())
+    assert int(status.item()) == 0
+
+
+def test_sample_workspace_reused_across_shapes(sd):
+    """One workspace, sized for the most rows, serves calls of different
+    vocabularies and batch sizes one after another: each row's counter and runs
+    sit at a place that depends on the row alone, every call leaves its
+    counters cleared and writes every run sum it reads."""
+    rng = np.random.default_rng(5150)
+    shapes = ((40, 4, 151936), (3, 2, 1000), (40, 4, 32000), (1, 0, 7), (17, 4, 151936))
+    need = max(int(sd.lib().specdec_verify_sample_workspace_bytes(*sh)) for sh in shapes)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert sd.lib().specdec_workspace_init(ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream) == 0
+    for B, D, V in shapes:
+        say("sample workspace reuse", B, D, V)
+        p = rng.random((B, D + 1, V)).astype(np.float32)
+        p /= p.sum(-1, keepdims=True)
+        q = rng.random((B, D, V)).astype(np.float32)
+        q /= q.sum(-1, keepdims=True)
+        draft = rng.integers(0, V, (B, D)).astype(np.int32)
+        u_acc = rng.random((B, D)).astype(np.float32)
+        u_draw = rng.random((B, D + 1)).astype(np.float32)
+        acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)), ws=ws)
+        torch.cuda.synchronize()
+        _check_sampled(p, q, draft, u_acc, u_draw, acc.cpu().numpy(), nxt.cpu().numpy())
+
+
+def test_sample_longest_draft(sd):
+    """D = 255, the longest draft: a row that accepts every draft (p = q) draws
+    its bonus with u_draw[255]; a row rejected at position 200 draws there."""
+    rng = np.random.default_rng(2550)
+    B, D, V = 3, 255, 300
+    say("sample D=255")
+    p = rng.random((B, D + 1, V)).astype(np.float32)
+    p /= p.sum(-1, keepdims=True)
+    q = p[:, :D].copy()
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    u_acc = rng.random((B, D)).astype(np.float32)
+    q[1, 200] = 0.0
+    q[1, 200, draft[1, 200]] = 1.0          # q puts all mass on the draft
+    p[1, 200, draft[1, 200]] = 0.0          # which p never takes: certain rejection
+    p[1, 200] /= p[1, 200].sum()
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)))
+    torch.cuda.synchronize()
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    assert acc[0] == D and acc[2] == D and acc[1] == 200
+    _check_sampled(p, q, draft, u_acc, u_draw, acc, nxt)
+    with pytest.raises(sd.SpecDecError):  # D = 256 is past the limit
+        sd.verify_sample(*(torch.zeros(sh, device="cuda") for sh in ((1, 257, 8), (1, 256, 8))),
+                         torch.zeros((1, 256), dtype=torch.int32, device="cuda"),
+                         torch.zeros((1, 256), device="cuda"), torch.zeros((1, 257), device="cuda"))
+
+
 def test_sample_worked_split(sd):
     """The newsletter page's 40/60 example through the kernel, with stratified uniforms."""
     say("sample worked split")
