@@ -4,8 +4,11 @@
 // probability min(1, p(x)/q(x)), replace from normalize(max(0, p - q)), bonus
 // from the target after the full draft; the draft and the target use the same
 // sampling settings).  p and q are softmax(logits / temperature) of the target
-// and draft rows, formed on the fly in fp64: e(v) = exp((l(v) - M) * (1/T)) with
-// M the row maximum, p(v) = e(v) * (1/Z).  Every decision compares fp64 values.
+// and draft rows, formed on the fly: e(v) = exp((l(v) - M) * (1/T)) with M the
+// row maximum, p(v) = e(v) * (1/Z), the exponent reduced in fp64 and the
+// exponential of its fraction taken by the hardware's fp32 exp2 (exp_fast:
+// about 1e-7 relative error, ten times inside the 1e-6 tolerance the decisions
+// are held to).  Sums and every comparison are in fp64.
 //
 // With top-p the distribution is cut to its nucleus first: every id whose
 // logit is at least t, where t is the largest logit value such that the ids at
@@ -92,6 +95,24 @@ __device__ __forceinline__ double exp_le0(double y, const double *tab) {
   return ldexp(tab[j] * e, k);
 }
 
+// e^y for y <= 0 with about 1e-7 relative error: y log2(e) = n + f in fp64
+// with n an integer and |f| <= 1/2; 2^f by the hardware's fp32 exp2 (f rounded
+// to fp32 costs at most 2e-8 relative, the instruction a few times 6e-8 on
+// [2^-1/2, 2^1/2]); then scaled by 2^n.  -inf, and anything below -708 (whose
+// e^y is under 1e-307, nothing beside the row's largest term, which is 1),
+// give 0.  About a third of the fp64 instructions of the library exp: the
+// statistics kernel, which takes one exponential per logit, is then bound by
+// its reads rather than by fp64 arithmetic.
+constexpr double kLog2e = 0x1.71547652b82fep+0;
+
+__device__ __forceinline__ double exp_fast(double y) {
+  if (!(y > -708.0)) return 0.0;
+  const double t = y * kLog2e;
+  const double n = rint(t);
+  const float f = (float)(t - n);
+  return ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
+}
+
 // Block sum in a fixed order: wave sums, then the wave totals in wave order.
 __device__ __forceinline__ double block_sum_d(double x, double *scratch) {
   x = wave_sum(x);
@@ -128,7 +149,7 @@ __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t,
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k)
-      if (ms[k] > -INFINITY) z += zs[k] * exp((ms[k] - m) * inv_t);
+      if (ms[k] > -INFINITY) z += zs[k] * exp_fast((ms[k] - m) * inv_t);
   }
   M = m;
   inv_z = 1.0 / z;
@@ -202,7 +223,7 @@ __global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
   if (m > -INFINITY) {
     const double md = (double)m;
 #pragma unroll kSlUnroll
-    for (int k = 0; k < kSlPer; ++k) z += exp(((double)x[k] - md) * p.inv_t);  // exp(-inf) = 0 past n
+    for (int k = 0; k < kSlPer; ++k) z += exp_fast(((double)x[k] - md) * p.inv_t);  // -inf past n: 0
   }
   z = block_sum_d(z, s_d);
   if (threadIdx.x == 0) {
@@ -465,7 +486,7 @@ __device__ __forceinline__ void load_run(const void *base, int64_t off, int t, i
 // Probability of a logit in a row with maximum M, 1/Z and nucleus threshold
 // cut (-inf: every id): 0 below the cut and for -inf logits.
 __device__ __forceinline__ double prob(float l, double M, double iz, float cut, double inv_t) {
-  return l >= cut ? exp(((double)l - M) * inv_t) * iz : 0.0;
+  return l >= cut ? exp_fast(((double)l - M) * inv_t) * iz : 0.0;
 }
 
 // The stop row's weight at one logit: max(0, p - q) at a < D (resid), else p.
