@@ -910,6 +910,8 @@ def bench_exspec(args, cfg):
         del pool, rect, logits, kv_new
         torch.cuda.empty_cache()
         cpu = cpu_exspec(cfg, plans, lens0, min(args.cpu_rounds, K, 4))
+    eq_bytes, eq_inplace = eqspec_pool_bytes(cfg, lens0, accs)
+    ex_bytes = gbytes + np.array(abytes, dtype=np.float64)
     config = {"workload": "exspec: pool of %d sequences, batches of %d, D=%d, V=%d bf16 logits, KV %dx%dx%d bf16, 16 "
                           "distinct lengths in [512,4096], %d rounds" % (N, G, cfg.D, cfg.V, cfg.L, cfg.H, cfg.Dh, K),
               "pool": N, "group": G, "D": cfg.D, "V": cfg.V, "cap": cap, "global_batch": N}
@@ -918,7 +920,21 @@ def bench_exspec(args, cfg):
              "group_us": float(g_ms.mean() * 1e3), "append_us": float(ap_ms.mean() * 1e3),
              "append_gbs": float(np.sum(abytes) / (ap_ms.sum() * 1e-3) / 1e9),
              "gather_us": float(ga_ms.mean() * 1e3), "mixed_batches_per_round": mixed,
-             "realign_share_of_round": float((ga_ms.sum() + g_ms.sum()) / total_ms)}
+             "uniform_batches_per_round": [ng - m for m in mixed],
+             "realign_share_of_round": float((ga_ms.sum() + g_ms.sum()) / total_ms),
+             "vs_eqspec": {
+                 "exspec_bytes_per_round": float(ex_bytes.mean()),
+                 "exspec_bytes_round_1": float(ex_bytes[0]),
+                 "eqspec_out_of_place_bytes_per_round": float(eq_bytes.mean()),
+                 "eqspec_in_place_bytes_per_round": float(eq_inplace.mean()),
+                 "exspec_over_eqspec": float(ex_bytes.sum() / eq_bytes.sum()),
+                 "how": "EXSPEC: the gather of mixed batches plus the in-place append (algorithmic bytes of these "
+                        "rounds); EQSPEC: the same pool held as fixed batches of %d consecutive rows, each a "
+                        "left-padded rectangle realigned every round with the same accepted lengths "
+                        "(out of place, and the in-place variant's moved bytes)" % G},
+             "cycle": cycle_stats(accs, cfg.D, K / (total_ms * 1e-3)),
+             "memory": device_memory(dev),
+             "host": host_info()}
     return _line("EXSPEC pool rounds/sec and gather HBM GB/s (256-sequence pool)", K / (total_ms * 1e-3), K, W,
                  total_ms / K, "bf16", config,
                  _roof("k_gather", ga_gbs, float(gbytes.mean()), float(ga_ms.mean() * 1e3)), cpu, extra)
@@ -963,6 +979,7 @@ def bench_lifecycle(args, cfg):
     rect = sd.SeqBuf.empty(cfg.L, N, cfg.H, cap, cfg.Dh, tdt, groups=ng)
     logits = torch.empty((K, N, D1, cfg.V), dtype=sdev.TORCH_DT[cfg.logit_dtype], device=dev)
     drafts = []
+    plants = []
     keep = []
     for r in range(K):
         plant, miss, draft = synth.plan_greedy(cfg, r)
@@ -973,6 +990,8 @@ def bench_lifecycle(args, cfg):
                 draft[b, miss[b]] = EOS + 1
         keep.append(sdev.fill_logits(cfg, r, plant, logits[r]))
         drafts.append(draft)
+        plants.append(plant)
+    host_drafts = drafts
     drafts = torch.from_numpy(np.stack(drafts)).to(dev)
     kv_new = torch.empty((K, cfg.L, 2, N, cfg.H, D1, cfg.Dh), dtype=tdt, device=dev)
     for r in range(K):
@@ -1029,17 +1048,23 @@ def bench_lifecycle(args, cfg):
              "active_per_round": [int(x) for x in cnt[:done, 0]],
              "round_step_ms": float(step_ms.mean()), "lifecycle_us": float(life_ms.mean() * 1e3),
              "lifecycle_share_of_round": float(life_ms.sum() / total_ms)}
+    cpu = None
+    if not args.no_cpu:
+        del pool, queue, rect, logits, kv_new
+        torch.cuda.empty_cache()
+        cpu = cpu_lifecycle(cfg, plants, host_drafts, lens0, tok0, qlen, qtok, cap, EOS, max_len,
+                            min(args.cpu_rounds, done, 2))
     line = _line("EXSPEC pool rounds/sec with the sequence lifecycle (256-slot pool)", done / (total_ms * 1e-3),
-                 done, 0, total_ms / max(done, 1), "bf16", config, None, None, extra)
+                 done, 0, total_ms / max(done, 1), "bf16", config, None, cpu, extra)
     line["roofline"] = {"bound": "latency", "kernels": "k_pool_finish + k_pool_admit_plan + k_pool_admit_copy",
                         "avg_call_us": float(life_ms.mean() * 1e3), "note": "one-workgroup list updates plus "
                         "the admitted prompts' KV copy; the round's bytes are in the exspec line"}
     return line
 
 
-def cpu_exspec(cfg, plans, lens0, rounds):
-    """The oracle on the first rounds of the pool chain: grouping, verification of
-    all sequences, gather and append of layer 0, scaled to all layers."""
+def _oracle_pool_rounds(cfg, plans, lens0, rounds):
+    """(grouping + verification seconds, layer-0 gather + append seconds) of
+    the oracle over the first rounds of the pool chain."""
     import numpy as np
     import oracle
     import synth
@@ -1061,12 +1086,111 @@ def cpu_exspec(cfg, plans, lens0, rounds):
         t2 = time.perf_counter()
         t_fix += t1 - t0
         t_lay += t2 - t1
-    per = (t_fix + t_lay * cfg.L) / rounds
+    return t_fix, t_lay
+
+
+def cpu_exspec(cfg, plans, lens0, rounds):
+    """The oracle on the first rounds of the pool chain: grouping, verification of
+    all sequences, gather and append of layer 0, scaled to all layers; the
+    single-threaded build, and beside it the OpenMP build of the same source."""
+    import oracle
+    N = cfg.B
+    t_fix, t_lay = _oracle_pool_rounds(cfg, plans, lens0, rounds)
+    with oracle.threaded():
+        threads = oracle.threads()
+        m_fix, m_lay = _oracle_pool_rounds(cfg, plans, lens0, rounds)
+    per, m_per = (t_fix + t_lay * cfg.L) / rounds, (m_fix + m_lay * cfg.L) / rounds
     return {"value": 1.0 / per, "unit": "rounds/s", "cores": 1, "kind": "oracle",
             "sample": "rounds 0-%d of the pool chain: grouping and greedy verify of all %d sequences (%.1f ms/round), "
                       "gather + append of layer 0 (%.1f ms/round) scaled by %d layers; single-threaded C oracle"
                       % (rounds - 1, N, 1e3 * t_fix / rounds, 1e3 * t_lay / rounds, cfg.L),
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(),
+            "all_cores": {"value": 1.0 / m_per, "unit": "rounds/s", "cores": threads, "kind": "oracle (OpenMP build)",
+                          "sample": "the same sample on %d threads: grouping and verify %.1f ms/round, layer 0 "
+                                    "%.1f ms/round before scaling" % (threads, 1e3 * m_fix / rounds,
+                                                                      1e3 * m_lay / rounds)}}
+
+
+def cpu_lifecycle(cfg, plants, drafts, lens0, tok0, qlen, qtok, cap, eos, max_len, rounds):
+    """The oracle on the first rounds of the lifecycle chain, with the same
+    inputs: grouping of the active sequences, their greedy verification, the
+    gather and append of layer 0, finishing and admission (the prompt copy of
+    layer 0); the layer-0 work is scaled to all layers.  Single-threaded build,
+    and the OpenMP build beside it."""
+    import numpy as np
+    import oracle
+    import synth
+    N, G, D = cfg.B, cfg.group, cfg.D
+    Q, qcap = qtok.shape
+
+    def run():
+        kv = synth.kv_host(cfg, lens0, 0, False, layer0=0, nlayers=1, cap=cap)
+        tok, lens = tok0.copy(), lens0.astype(np.int32).copy()
+        qkv = synth.kv_host(cfg, qlen, 0, False, layer0=0, nlayers=1, rows=Q, cap=qcap)
+        sched = oracle.Sched(N, range(N))
+        t_fix = t_lay = 0.0
+        for r in range(rounds):
+            act = sched.active_list()
+            B = len(act)
+            lg = synth.logits_host(cfg, r, plants[r], nrows=B * cfg.D1)
+            kvn = synth.kvnew_host(cfg, r, layer0=0, nlayers=1)[:, :, :B]
+            t0 = time.perf_counter()
+            order_l, uni, wid, nu = oracle.group_by_len(lens[act], G)
+            order = act[order_l]
+            acc, nxt, _ = oracle.verify_greedy(lg, drafts[r][:B], B, D, cfg.V)
+            t1 = time.perf_counter()
+            oracle.gather(kv, tok, lens, order, G, uni, cap)
+            oracle.append(kv, tok, lens, order, kvn, drafts[r][:B], acc, nxt)
+            t2 = time.perf_counter()
+            oracle.pool_finish(tok, lens, sched, order, acc, D, eos, max_len)
+            t3 = time.perf_counter()
+            oracle.pool_admit(kv, tok, lens, sched, qkv, qtok, qlen)
+            t4 = time.perf_counter()
+            t_fix += (t1 - t0) + (t3 - t2)
+            t_lay += (t2 - t1) + (t4 - t3)
+        return t_fix, t_lay
+
+    t_fix, t_lay = run()
+    with oracle.threaded():
+        threads = oracle.threads()
+        m_fix, m_lay = run()
+    per, m_per = (t_fix + t_lay * cfg.L) / rounds, (m_fix + m_lay * cfg.L) / rounds
+    return {"value": 1.0 / per, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": "rounds 0-%d of the lifecycle chain: grouping, greedy verify and finishing of the active "
+                      "sequences (%.1f ms/round), gather + append + admission of layer 0 (%.1f ms/round) scaled by "
+                      "%d layers; single-threaded C oracle" % (rounds - 1, 1e3 * t_fix / rounds,
+                                                             1e3 * t_lay / rounds, cfg.L),
+            "host_cpus": os.cpu_count(),
+            "all_cores": {"value": 1.0 / m_per, "unit": "rounds/s", "cores": threads, "kind": "oracle (OpenMP build)",
+                          "sample": "the same sample on %d threads" % threads}}
+
+
+def eqspec_pool_bytes(cfg, lens0, accs):
+    """Bytes per round of the same pool kept as EQSPEC rectangles instead: the
+    256 sequences in fixed batches of `group` consecutive pool rows, each a
+    left-padded rectangle realigned every round (unpad, append, repad out of
+    place), P * (sum c + sum n + group * S') per batch; and the in-place
+    variant's moved bytes, P * (2 * sum of moved rows' c + sum of shifts + 2 * sum n)."""
+    import numpy as np
+    N, G, P = cfg.B, cfg.group, cfg.kv_pos_bytes
+    lens = lens0.astype(np.int64).copy()
+    width = [int(lens[g:g + G].max()) for g in range(0, N, G)]
+    out, inpl = [], []
+    for acc in accs:
+        n = acc.astype(np.int64) + 1
+        tot = ip = 0
+        for k, g in enumerate(range(0, N, G)):
+            c, nb = lens[g:g + G], n[g:g + G]
+            snew = int((c + nb).max())
+            tot += P * (int(c.sum()) + int(nb.sum()) + len(c) * snew)
+            shift = snew - width[k] - nb
+            moved = (shift != 0) & (c > 0)
+            ip += P * (2 * int(c[moved].sum()) + int(np.maximum(shift, 0).sum()) + 2 * int(nb.sum()))
+            width[k] = snew
+        out.append(tot)
+        inpl.append(ip)
+        lens = lens + n
+    return np.array(out, dtype=np.float64), np.array(inpl, dtype=np.float64)
 
 
 def main():
