@@ -110,9 +110,21 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
   char *kv = static_cast<char *>(p.kv_out);
   const char *nw = static_cast<const char *>(p.kv_new);
 
-  for (long w = blockIdx.x; w < nseg + B; w += gridDim.x) {
-    if (w < nseg) {
-      const int b = (int)((w / H) % B);
+  for (long x = blockIdx.x; x < nseg + B; x += gridDim.x) {
+    if (x < nseg) {
+      // Sequence w of this workgroup.  The dispatcher deals workgroups to the
+      // 8 XCDs in turn (x mod 8) and, within an XCD, to its 4 shader engines in
+      // turn ((x / 8) mod 4), whichever has a free CU; a row's sequences are
+      // all moved or all append-only, so with the heads innermost (w = x) every
+      // sequence of row b lands on one engine per XCD (b mod 4 when H = 8) and
+      // the engines carry unequal loads.  Rotating each (layer, K|V) block of
+      // B*H sequences by lk*H spreads every row over all 32 (XCD, engine)
+      // streams.
+      const long BH = (long)B * H, lk = x / BH;
+      long bh = x - lk * BH - (lk * H) % BH;
+      if (bh < 0) bh += BH;
+      const long w = lk * BH + bh;
+      const int b = (int)(bh / H);
       const int c = uni(s_c[b]), n = uni(s_n[b]);
       const int pin = S - c, pout = Snew - c - n, shift = pout - pin;
       char *base = kv + (size_t)w * p.cap_in * pos_bytes;
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(kIpBlock) void k_realign_inplace(RealignParams p) {
       for (int f = t + kIpBlock; f < n * U; f += kIpBlock) bst(bld(ra, (uint32_t)f * 16u), rc, (uint32_t)f * 16u);
     } else {
       // token ids, position ids and mask of row b
-      const int b = (int)(w - nseg);
+      const int b = (int)(x - nseg);
       const int c = uni(s_c[b]), n = uni(s_n[b]), a = n - 1;
       const int pin = S - c, pout = Snew - c - n, shift = pout - pin;
       int32_t *tok = p.tok_out + (size_t)b * p.cap_in;
