@@ -103,6 +103,12 @@ def traffic_ratio(inplace=False):
                           TRAFFIC[inplace][1])
 
 
+def verify_sample_traffic(alg_bytes):
+    r = _counter_ratio(os.path.join(ROOT, "profiles", "verify_sample_stoch_traffic.txt"),
+                       "verify_sample_source_sha256_16", "verify_sample_traffic_over_algorithmic", VERIFY_SOURCES)
+    return None if r is None else (r[0] * alg_bytes, r[1].replace("64-round chain", "stoch round"))
+
+
 def verify_traffic(alg_bytes):
     r = _counter_ratio(TRAFFIC[True][0], "verify_source_sha256_16", "verify_traffic_over_algorithmic",
                        VERIFY_SOURCES)
@@ -825,10 +831,14 @@ def bench_stoch(args, cfg):
                           "one sampled verify + EQSPEC round repeated" % (cfg.B, cfg.D, cfg.V, cfg.L, cfg.H, cfg.Dh,
                                                                          cfg.len_lo, cfg.len_hi),
               "B": cfg.B, "D": cfg.D, "V": cfg.V, "cap": cfg.cap, "global_batch": cfg.B}
-    vroof = _roof("k_verify_sample", ve_gbs, vbytes, float(ver_ms.mean() * 1e3))
+    vt = verify_sample_traffic(vbytes)
+    vroof = _roof("k_verify_sample", ve_gbs, vbytes, float(ver_ms.mean() * 1e3), None if vt is None else vt[0])
+    if vt is not None:
+        vroof["traffic_how"] = vt[1]
     vroof["alone"] = {"pass_avg_us": ver_alone_us, "gbs": vbytes / (ver_alone_us * 1e-6) / 1e9,
                       "frac": vbytes / (ver_alone_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                      "how": "%d launches queued behind a spin kernel, events around the pass" % K}
+                      "how": "%d launches queued behind a spin kernel, events around the pass (the same p and q "
+                             "each time: the stop rows stay in the Infinity Cache)" % K}
     extra = {"verify": {"kernel": "k_verify_sample", "achieved_gbs": ve_gbs, "frac": ve_gbs / PEAK_HBM_GBS,
                         "algorithmic_bytes_per_launch": vbytes, "avg_launch_us": float(ver_ms.mean() * 1e3),
                         "roofline": vroof},
