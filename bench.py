@@ -39,7 +39,7 @@ KERNEL = {False: "k_realign_eqspec", True: "k_realign_inplace"}
 PAGE = 16  # positions per page of the paged-cache leg
 SPIN_CYCLES_PER_LAUNCH = 200000  # GPU spin ahead of a pass, per launch queued behind it (~100 us at 2 GHz)
 # counter summary and the sources of the realign kernel it was taken on, per realign mode
-VERIFY_SOURCES = ("verify.hip", "device_common.h", "launch.h")
+VERIFY_SOURCES = ("verify.hip", "coherent.h", "device_common.h", "launch.h", "wave_dpp.h")
 TRAFFIC = {
     False: (os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt"), ("realign.hip",) + _HEADERS),
     True: (os.path.join(ROOT, "profiles", "realign_inplace_8b_gqa_traffic.txt"),

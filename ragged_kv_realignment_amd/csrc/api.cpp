@@ -153,23 +153,25 @@ EXPORT int specdec_verify_sample(const float *p, const float *q, int B, int D, i
   return launched(sd::launch_verify_sample(s, as_stream(stream)));
 }
 
-// Workspace of specdec_verify_sample_logits: per-split row statistics, per-split
-// masses and the stop position of every batch row.
+// Workspace of specdec_verify_sample_logits: per-split row statistics, the
+// logits at the draft tokens, the stop row's per-split and per-run masses, the
+// stop row's parameters and the nucleus of every row.
 struct SlLayout {
-  size_t stats, part, thr, rowinfo, nuc, stop, total;
+  size_t stats, gath, part, thr, rowinfo, nuc, total;
 };
 
 static SlLayout sl_layout(int B, int D, int V) {
   const size_t S = ((size_t)V + sd::kSlChunk - 1) / sd::kSlChunk, R = 2 * (size_t)D + 1;
+  const size_t Ss = ((size_t)V + sd::kSlStatChunk - 1) / sd::kSlStatChunk;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   SlLayout l;
   l.stats = 0;
-  l.part = up((size_t)B * R * S * 16);
+  l.gath = up((size_t)B * R * Ss * 16);
+  l.part = l.gath + up((size_t)B * D * 8);
   l.thr = l.part + up((size_t)B * S * 16);
   l.rowinfo = l.thr + up((size_t)B * S * sd::kSlThreads * 16);
   l.nuc = l.rowinfo + up((size_t)B * 64);
-  l.stop = l.nuc + up((size_t)B * R * 32);
-  l.total = l.stop + up((size_t)B * 4);
+  l.total = l.nuc + up((size_t)B * R * 32);
   return l;
 }
 
@@ -200,6 +202,7 @@ EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_lo
   s.D = D;
   s.V = V;
   s.S = (int)((V + sd::kSlChunk - 1) / sd::kSlChunk);
+  s.Ss = (int)((V + sd::kSlStatChunk - 1) / sd::kSlStatChunk);
   s.inv_t = 1.0 / (double)temperature;
   s.top_p = top_p;
   s.nucleus = top_p < 1.0f;
@@ -212,11 +215,11 @@ EXPORT int specdec_verify_sample_logits(const void *target, const void *draft_lo
   s.status = status;
   char *w = static_cast<char *>(ws);
   s.stats = reinterpret_cast<double *>(w + l.stats);
+  s.gath = reinterpret_cast<float *>(w + l.gath);
   s.part = reinterpret_cast<double *>(w + l.part);
   s.thr = reinterpret_cast<double *>(w + l.thr);
   s.rowinfo = reinterpret_cast<double *>(w + l.rowinfo);
   s.nuc = reinterpret_cast<double *>(w + l.nuc);
-  s.stop = reinterpret_cast<int32_t *>(w + l.stop);
   const size_t e = dtype == SPECDEC_F32 ? 4 : 8;  // logits per 16-byte vector
   s.vec = (size_t)V % e == 0 && reinterpret_cast<uintptr_t>(target) % 16 == 0 &&
           (D == 0 || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);

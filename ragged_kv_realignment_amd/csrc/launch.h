@@ -51,7 +51,9 @@ void sample_shape(int V, int &R, int &S);
 
 struct SampleLogitsParams {
   const void *target, *draftl;  // logits [B][D+1][V] and [B][D][V] of `dtype`
-  int dtype, B, D, V, S;        // S = splits of kSlChunk logits per row
+  int dtype, B, D, V;
+  int S;                        // splits of kSlChunk logits per stop row (mass and draw)
+  int Ss;                       // splits of kSlStatChunk logits per row (statistics)
   double inv_t;                 // 1 / temperature
   float top_p;                  // nucleus mass, in (0, 1]
   bool nucleus;                 // top_p < 1: cut every row to its nucleus
@@ -59,18 +61,35 @@ struct SampleLogitsParams {
   const int32_t *draft;
   const float *u_accept, *u_draw;
   int32_t *accept_len, *next_token, *status;
-  double *stats;                // workspace [B][2D+1][S] x (max, exp-sum)
-  double *part;                 // workspace [B][S] x (residual mass, target mass)
-  double *thr;                  // workspace [B][S][kBlock] x the same per thread run
-  double *rowinfo;              // workspace [B] x 8: (M, 1/Z) of the stop position's target and draft
-                                // rows, then their nucleus thresholds
+  double *stats;                // workspace [B][2D+1][Ss] x (max, exp-sum)
+  float *gath;                  // workspace [B][D] x (target logit, draft logit) at the draft token
+  double *part;                 // workspace [B][S] x (residual mass, target mass) of the stop row
+  double *thr;                  // workspace [B][S][kSlThreads] x the same per thread run
+  double *rowinfo;              // workspace [B] x 8: (M, 1/Z) of the stop row's target and draft rows,
+                                // their nucleus thresholds, the draw's uniform, the stop position
   double *nuc;                  // workspace [B][2D+1] x 4: (M, 1/Z, threshold) of every nucleus
-  int32_t *stop;                // workspace [B]: stop position
   float *cutoff;                // optional out [B][2D+1]: every row's threshold (-inf: no nucleus)
 };
 
-constexpr int kSlChunk = 4096;   // logits per split in sampled verification from logits
-constexpr int kSlThreads = 256;  // threads per workgroup of those kernels
+// Sampled verification from logits.  The statistics kernel reads each row in
+// splits of kSlStatChunk logits (kSlStatThreads threads of kSlStatPer logits);
+// the mass and draw kernels cut the stop row into splits of kSlChunk logits, a
+// run of kSlChunk / kSlThreads consecutive ids per thread.  Compile-time knobs
+// (measured defaults).
+#ifndef SPECDEC_SL_STAT_THREADS
+#define SPECDEC_SL_STAT_THREADS 256
+#endif
+#ifndef SPECDEC_SL_STAT_PER
+#define SPECDEC_SL_STAT_PER 16
+#endif
+#ifndef SPECDEC_SL_THREADS
+#define SPECDEC_SL_THREADS 512
+#endif
+constexpr int kSlStatThreads = SPECDEC_SL_STAT_THREADS;
+constexpr int kSlStatPer = SPECDEC_SL_STAT_PER;
+constexpr int kSlStatChunk = kSlStatThreads * kSlStatPer;
+constexpr int kSlChunk = 4096;
+constexpr int kSlThreads = SPECDEC_SL_THREADS;
 
 
 

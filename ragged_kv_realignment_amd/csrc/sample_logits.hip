@@ -15,28 +15,26 @@
 // or above it hold at least top_p of the row's mass; ties at t are all kept,
 // and p is renormalised over the nucleus.
 //
-// Three launches (four with top-p), no state kept in the workspace between
-// calls:
-//  1. k_sl_stats: one workgroup per (split of kSlChunk logits, row, batch row)
-//     writes the split's maximum and its exp-sum relative to that maximum.
+// Three launches (four with top-p); the workspace keeps nothing between calls:
+//  1. k_sl_stats: one workgroup per (split of kSlStatChunk logits, row, batch row)
+//     writes the split's maximum and its exp-sum relative to that maximum; the
+//     split that holds the row's draft token also leaves that token's logit.
 //  1b. k_sl_nucleus (top-p only): one workgroup per (row, batch row) selects t
-//     by a most-significant-digit-first radix select over the logits' order
-//     keys, with masses held as 2^-41 fixed-point integers so every sum is
-//     exact and order-free, then sums the nucleus mass Z in fp64.
-//  2. k_sl_mass: one workgroup per (split, batch row) merges the statistics of
-//     the 2D+1 rows (or reads the nucleus ones), evaluates the acceptance test
-//     of every draft (the same
-//     result in every workgroup of the batch row), and sums the stop row's
-//     residual mass max(0, p - q) (or p at position D) and its target mass
-//     over its split.
-//     Each thread also leaves the masses of its run of kSlPer consecutive ids.
-//  3. k_sl_draw: one workgroup per batch row finds the split in which the
-//     running mass first exceeds u * T, then the thread run within it (a block
-//     scan of the run masses), then the id (a wave scan of that run's weights).
+//     level by level, each level one read of the row: the first bins the
+//     logits by y = (M - l) / T, the later ones bin the order keys of the
+//     chosen bin's interval; masses are 2^-41 fixed-point integers, so every
+//     sum is exact and order-free, and Z is the fixed-point mass at or above t.
+//  2. k_sl_mass: one workgroup per (split, batch row) evaluates every
+//     acceptance test (the same result in every workgroup of a batch row) and
+//     sums the stop row's residual mass max(0, p - q) (or p at position D) over
+//     its split and over each thread's run of kSlRun ids.
+//  3. k_sl_draw: one workgroup per (split, batch row); the one whose split
+//     holds the crossing of u * T finds the run, then the id.
 #include <math.h>
 #include <limits.h>
 #include "device_common.h"
 #include "launch.h"
+#include "wave_dpp.h"
 #include "specdec.h"
 
 // p and q are each rounded before p - q is formed (as the definition has it):
@@ -46,19 +44,19 @@
 
 namespace sd {
 
-constexpr int kSlPer = kSlChunk / kBlock;  // logits per thread per split
-static_assert(kSlPer <= kWave, "a thread run must fit one wave");
-static_assert(kBlock == kSlThreads, "workspace layout assumes kSlThreads threads per workgroup");
+constexpr int kSlRun = kSlChunk / kSlThreads;  // ids of one thread's run of the stop row
+static_assert(kSlChunk % kSlThreads == 0 && kSlRun <= kWave, "a thread run must fit one wave");
+static_assert(kSlThreads >= 256 && kSlThreads % kWave == 0, "one thread per draft position, D <= 255");
+static_assert(kSlStatThreads % kWave == 0, "whole waves");
 
-// Logits per 16-byte vector, and whether a thread's kSlPer logits are whole vectors.
-template <int DT>
+// Logits per 16-byte vector, and whether PER logits of a thread are whole vectors.
+template <int DT, int PER>
 struct SlVec {
   static constexpr int E = DT == SPECDEC_F32 ? 4 : 8;
-  static constexpr bool ok = kSlPer % E == 0;
+  static constexpr bool ok = PER % E == 0;
 };
 constexpr int kSlMaxRows = 2 * 255 + 1;     // 2D + 1 rows per batch row, D <= 255
-constexpr int kSlMaxSplits = 1024;          // V <= 2^22
-constexpr int kSlUnroll = 8;               // independent exps in flight per thread (statistics)
+constexpr int kSlMaxSplits = (1 << 22) / kSlChunk;  // V <= 2^22
 
 template <int DT>
 __device__ __forceinline__ float logit_at(const void *base, int64_t i) {
@@ -75,7 +73,7 @@ __device__ __forceinline__ float logit_at(const void *base, int64_t i) {
 // two fused multiply-adds on a two-part constant; e^r is its degree-5 Taylor
 // polynomial (truncation below 4e-17 of the result) and 2^(j/64) comes from a
 // 64-entry table in LDS that exp_tab_fill writes (measured: faster than the
-// library exp in the nucleus kernel, no faster in the others, which keep it).
+// library exp in the nucleus kernel; the other kernels take exp_fast below).
 constexpr double kLn2By64Hi = 0x1.62e42fefa39efp-7;
 constexpr double kLn2By64Lo = 0x1.abc9e3b39803fp-62;
 constexpr double k64ByLn2 = 0x1.71547652b82fep+6;
@@ -105,34 +103,32 @@ __device__ __forceinline__ double exp_le0(double y, const double *tab) {
 // its reads rather than by fp64 arithmetic.
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 
+// Branch-free (a select at the end), so that the exponentials of a thread's
+// ids interleave instead of each sitting behind its own exec-mask branch.
 __device__ __forceinline__ double exp_fast(double y) {
-  if (!(y > -708.0)) return 0.0;
-  const double t = y * kLog2e;
+  const double t = fmax(y, -708.0) * kLog2e;
   const double n = rint(t);
   const float f = (float)(t - n);
-  return ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
-}
-
-// Block sum in a fixed order: wave sums, then the wave totals in wave order.
-__device__ __forceinline__ double block_sum_d(double x, double *scratch) {
-  x = wave_sum(x);
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = x;
-  __syncthreads();
-  double r = scratch[0];
-#pragma unroll
-  for (int k = 1; k < kBlock / kWave; ++k) r += scratch[k];
-  return r;
+  const double r = ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
+  return y > -708.0 ? r : 0.0;
 }
 
 // Row maximum M and 1/Z from the per-split statistics (split order).  Loads
-// are issued kBatch splits at a time so a row costs ceil(S / kBatch) round
-// trips, not S.
+// are issued kBatch splits at a time, and the first kBatch are kept for the
+// sum, so a row of up to kBatch splits costs one round trip.
 constexpr int kBatch = 8;
 
 __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t, double &M, double &inv_z) {
+  double m0[kBatch], z0[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    m0[k] = k < S ? st[2 * k] : -INFINITY;
+    z0[k] = k < S ? st[2 * k + 1] : 0.0;
+  }
   double m = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) m = fmax(m, m0[k]);
+  for (int s0 = kBatch; s0 < S; s0 += kBatch) {
     double ms[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) ms[k] = s0 + k < S ? st[2 * (s0 + k)] : -INFINITY;
@@ -140,7 +136,12 @@ __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t,
     for (int k = 0; k < kBatch; ++k) m = fmax(m, ms[k]);
   }
   double z = 0.0;
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const double e = z0[k] * exp_fast((m0[k] - m) * inv_t);
+    z += m0[k] > -INFINITY ? e : 0.0;
+  }
+  for (int s0 = kBatch; s0 < S; s0 += kBatch) {
     double ms[kBatch], zs[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
@@ -148,8 +149,10 @@ __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t,
       zs[k] = s0 + k < S ? st[2 * (s0 + k) + 1] : 0.0;
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (ms[k] > -INFINITY) z += zs[k] * exp_fast((ms[k] - m) * inv_t);
+    for (int k = 0; k < kBatch; ++k) {
+      const double e = zs[k] * exp_fast((ms[k] - m) * inv_t);
+      z += ms[k] > -INFINITY ? e : 0.0;
+    }
   }
   M = m;
   inv_z = 1.0 / z;
@@ -168,17 +171,18 @@ __device__ __forceinline__ int64_t draft_row(const SampleLogitsParams &p, int b,
 // ordinary loads twice as slow (statistics on the stoch logits: 28.9 against
 // 16.1 us after a 512 MiB fill; alike after a read).
 #define SL_LOAD(ptr) __builtin_nontemporal_load(ptr)
-// kSlPer logits of one split for this thread: id threadIdx.x + k * kBlock
-// (scalar loads) or, with 16-byte vectors of E = 16 / esize logits, ids
-// (threadIdx.x + j * kBlock) * E + e for vector j and lane e.  Ids at or past n
-// read as -inf.  Every vector load is issued before any is used (an index past
-// the split's whole vectors re-reads its last one, never used); the ragged end
-// of a split, if any, is read by scalar loads afterwards.
+// kSlStatPer logits of one statistics split for this thread: id
+// threadIdx.x + k * kSlStatThreads (scalar loads) or, with 16-byte vectors of
+// E = 16 / esize logits, ids (threadIdx.x + j * kSlStatThreads) * E + e for
+// vector j and lane e.  Ids at or past n read as -inf.  Every vector load is
+// issued before any is used (an index past the split's whole vectors re-reads
+// its last one, never used); the ragged end of a split, if any, is read by
+// scalar loads afterwards.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_split(const void *base, int64_t off, int n, float *x) {
-  if (VEC && SlVec<DT>::ok) {
-    constexpr int E = SlVec<DT>::E;
-    constexpr int NV = kSlPer / E;
+  if (VEC && SlVec<DT, kSlStatPer>::ok) {
+    constexpr int E = SlVec<DT, kSlStatPer>::E;
+    constexpr int NV = kSlStatPer / E;
     const int nv = n / E;  // whole vectors of the split
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 *vp = DT == SPECDEC_F32
@@ -187,11 +191,11 @@ __device__ __forceinline__ void load_split(const void *base, int64_t off, int n,
     u32x4 v[NV];
     if (nv > 0) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) v[j] = SL_LOAD(vp + min((int)threadIdx.x + j * kBlock, nv - 1));
+      for (int j = 0; j < NV; ++j) v[j] = SL_LOAD(vp + min((int)threadIdx.x + j * kSlStatThreads, nv - 1));
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int vi = threadIdx.x + j * kBlock;
+      const int vi = threadIdx.x + j * kSlStatThreads;
       const uint32_t w[4] = {v[j][0], v[j][1], v[j][2], v[j][3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -209,37 +213,66 @@ __device__ __forceinline__ void load_split(const void *base, int64_t off, int n,
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kSlPer; ++k) {
-      const int i = threadIdx.x + k * kBlock;
+    for (int k = 0; k < kSlStatPer; ++k) {
+      const int i = threadIdx.x + k * kSlStatThreads;
       x[k] = i < n ? logit_at<DT>(base, off + i) : -INFINITY;
     }
   }
 }
 
+// Thread and slot of load_split's x[] that hold the split's id lx.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_sl_stats(SampleLogitsParams p) {
-  __shared__ float s_f[kBlock / kWave];
-  __shared__ double s_d[kBlock / kWave];
+__device__ __forceinline__ void split_owner(int lx, int &thread, int &slot) {
+  if (VEC && SlVec<DT, kSlStatPer>::ok) {
+    constexpr int E = SlVec<DT, kSlStatPer>::E;
+    const int vi = lx / E;
+    thread = vi % kSlStatThreads;
+    slot = (vi / kSlStatThreads) * E + lx % E;
+  } else {
+    thread = lx % kSlStatThreads;
+    slot = lx / kSlStatThreads;
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kSlStatThreads) void k_sl_stats(SampleLogitsParams p) {
+  __shared__ float s_f[kSlStatThreads / kWave];
+  __shared__ double s_d[kSlStatThreads / kWave];
   const int s = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int D = p.D, R = 2 * D + 1;
   const void *base = r <= D ? p.target : p.draftl;
-  const int64_t off = (r <= D ? target_row(p, b, r) : draft_row(p, b, r - D - 1)) + (int64_t)s * kSlChunk;
-  const int n = min(kSlChunk, p.V - s * kSlChunk);
-  float x[kSlPer];
+  const int64_t off = (r <= D ? target_row(p, b, r) : draft_row(p, b, r - D - 1)) + (int64_t)s * kSlStatChunk;
+  const int n = min(kSlStatChunk, p.V - s * kSlStatChunk);
+  // the draft token this row is tested at: target rows i < D and draft rows
+  const int gi = r < D ? r : r - D - 1;
+  const int gx = r != D ? p.draft[(int64_t)b * D + gi] : -1;
+  float x[kSlStatPer];
   load_split<DT, VEC>(base, off, n, x);
+  // the split that holds the token leaves its logit for the acceptance test
+  const int lx = gx - s * kSlStatChunk;
+  if (r != D && lx >= 0 && lx < n) {
+    int owner, slot;
+    split_owner<DT, VEC>(lx, owner, slot);
+    if ((int)threadIdx.x == owner) {
+      float v = x[0];
+#pragma unroll
+      for (int k = 1; k < kSlStatPer; ++k) v = k == slot ? x[k] : v;
+      p.gath[((int64_t)b * D + gi) * 2 + (r > D ? 1 : 0)] = v;
+    }
+  }
   float m = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kSlPer; ++k) m = fmaxf(m, x[k]);
-  m = block_max_float(m, s_f);
+  for (int k = 0; k < kSlStatPer; ++k) m = fmaxf(m, x[k]);
+  m = block_max_f32<kSlStatThreads>(m, s_f);
   double z = 0.0;
   if (m > -INFINITY) {
     const double md = (double)m;
-#pragma unroll kSlUnroll
-    for (int k = 0; k < kSlPer; ++k) z += exp_fast(((double)x[k] - md) * p.inv_t);  // -inf past n: 0
+#pragma unroll
+    for (int k = 0; k < kSlStatPer; ++k) z += exp_fast(((double)x[k] - md) * p.inv_t);  // -inf past n: 0
   }
-  z = block_sum_d(z, s_d);
+  z = block_sum_d<kSlStatThreads>(z, s_d);
   if (threadIdx.x == 0) {
-    double *st = p.stats + (((int64_t)b * R + r) * p.S + s) * 2;
+    double *st = p.stats + (((int64_t)b * R + r) * p.Ss + s) * 2;
     st[0] = (double)m;
     st[1] = z;
   }
@@ -388,7 +421,7 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
   const int64_t off = r <= D ? target_row(p, b, r) : draft_row(p, b, r - D - 1);
   // row maximum from the split statistics
   double m = -INFINITY;
-  for (int k = threadIdx.x; k < p.S; k += kNucThreads) m = fmax(m, p.stats[(((int64_t)b * R + r) * p.S + k) * 2]);
+  for (int k = threadIdx.x; k < p.Ss; k += kNucThreads) m = fmax(m, p.stats[(((int64_t)b * R + r) * p.Ss + k) * 2]);
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
   if (lane == 0) s_d[wv] = m;
@@ -462,16 +495,16 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
   }
 }
 
-// This thread's kSlPer consecutive logits of a split, ids t * kSlPer + k (the
+// This thread's kSlRun consecutive logits of a split, ids t * kSlRun + k (the
 // mass and draw kernels scan ids in order); ids at or past n read as -inf.
 template <int DT, bool VEC>
 __device__ __forceinline__ void load_run(const void *base, int64_t off, int t, int n, float *x) {
-  const int i0 = t * kSlPer;
+  const int i0 = t * kSlRun;
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  if (VEC && SlVec<DT>::ok && i0 + kSlPer <= n) {
+  if (VEC && SlVec<DT, kSlRun>::ok && i0 + kSlRun <= n) {
     if (DT == SPECDEC_F32) {
 #pragma unroll
-      for (int j = 0; j < kSlPer / 4; ++j) {
+      for (int j = 0; j < kSlRun / 4; ++j) {
         const u32x4 v = SL_LOAD(reinterpret_cast<const u32x4 *>(static_cast<const float *>(base) + off + i0 + 4 * j));
         x[4 * j] = __uint_as_float(v[0]);
         x[4 * j + 1] = __uint_as_float(v[1]);
@@ -480,7 +513,7 @@ __device__ __forceinline__ void load_run(const void *base, int64_t off, int t, i
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < kSlPer / 8; ++j) {
+      for (int j = 0; j < kSlRun / 8; ++j) {
         const u32x4 v = SL_LOAD(reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + off + i0 + 8 * j));
         const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
@@ -492,14 +525,15 @@ __device__ __forceinline__ void load_run(const void *base, int64_t off, int t, i
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kSlPer; ++k) x[k] = i0 + k < n ? logit_at<DT>(base, off + i0 + k) : -INFINITY;
+    for (int k = 0; k < kSlRun; ++k) x[k] = i0 + k < n ? logit_at<DT>(base, off + i0 + k) : -INFINITY;
   }
 }
 
 // Probability of a logit in a row with maximum M, 1/Z and nucleus threshold
 // cut (-inf: every id): 0 below the cut and for -inf logits.
 __device__ __forceinline__ double prob(float l, double M, double iz, float cut, double inv_t) {
-  return l >= cut ? exp_fast(((double)l - M) * inv_t) * iz : 0.0;
+  const double v = exp_fast(((double)l - M) * inv_t) * iz;
+  return l >= cut ? v : 0.0;
 }
 
 // The stop row's weight at one logit: max(0, p - q) at a < D (resid), else p.
@@ -510,15 +544,38 @@ __device__ __forceinline__ double weight(float lt, float lq, bool resid, const d
   return d > 0.0 ? d : 0.0;
 }
 
+// One workgroup per (split, batch row).  Every load it needs before the stop
+// position is known goes out in one round trip: the draft tokens, the two
+// logits at each (left by the statistics kernel), the uniforms, and the rows'
+// statistics (or nuclei).  Every workgroup of batch row b then evaluates every
+// acceptance test and takes the same stop position a; the second round trip
+// reads its split of the stop row.  Each thread sums its run of kSlRun
+// consecutive ids in id order: the weights w (max(0, p - q) at a < D, p at
+// a = D) and, for the fallback, p.  Run sums and the split's totals (wave
+// sums, then the waves in order) go to the workspace; split 0 also leaves the
+// stop row's (M, 1/Z, threshold), the draw's uniform and a.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
+__global__ __launch_bounds__(kSlThreads) void k_sl_mass(SampleLogitsParams p) {
+  constexpr int NW = kSlThreads / kWave;
   __shared__ double s_m[kSlMaxRows], s_iz[kSlMaxRows];
   __shared__ float s_cut[kSlMaxRows];
-  __shared__ int s_i[kBlock / kWave];
-  __shared__ double s_d[kBlock / kWave];
+  __shared__ double s_w[NW], s_p[NW];
+  __shared__ int s_i[NW];
+  __shared__ float s_ud;
   const int s = blockIdx.x, b = blockIdx.y;
-  const int D = p.D, V = p.V, R = 2 * D + 1;
-  for (int r = threadIdx.x; r < R; r += kBlock) {
+  const int S = p.S, D = p.D, V = p.V, R = 2 * D + 1;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+
+  int x = -1;
+  float gt = 0.0f, gd = 0.0f, ua = 0.0f, ud = 0.0f;
+  if (t < D) {
+    x = p.draft[(int64_t)b * D + t];
+    gt = p.gath[((int64_t)b * D + t) * 2];
+    gd = p.gath[((int64_t)b * D + t) * 2 + 1];
+    ua = p.u_accept[(int64_t)b * D + t];
+  }
+  if (t <= D) ud = p.u_draw[(int64_t)b * (D + 1) + t];
+  for (int r = t; r < R; r += kSlThreads) {
     double M, iz;
     float cut = -INFINITY;
     if (p.nucleus) {
@@ -527,7 +584,7 @@ __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
       iz = o[1];
       cut = (float)o[2];
     } else {
-      merge_row(p.stats + ((int64_t)b * R + r) * p.S * 2, p.S, p.inv_t, M, iz);
+      merge_row(p.stats + ((int64_t)b * R + r) * p.Ss * 2, p.Ss, p.inv_t, M, iz);
     }
     s_m[r] = M;
     s_iz[r] = iz;
@@ -535,85 +592,112 @@ __global__ __launch_bounds__(kBlock) void k_sl_mass(SampleLogitsParams p) {
     if (s == 0 && p.cutoff) p.cutoff[(int64_t)b * R + r] = cut;
   }
   __syncthreads();
-  // acceptance of every draft: u * q(x) <= p(x); q(x) = 0 accepts iff p(x) > 0
-  int first = D, bad = 0;
-  for (int i = threadIdx.x; i < D; i += kBlock) {
-    const int x = p.draft[(int64_t)b * D + i];
-    bool ok = false;
+  // u q(x) <= p(x); q(x) = 0 accepts iff p(x) > 0
+  bool reject = false, bad = false;
+  if (t < D) {
     if (x >= 0 && x < V) {
-      const double pt = prob(logit_at<DT>(p.target, target_row(p, b, i) + x), s_m[i], s_iz[i], s_cut[i], p.inv_t);
-      const double qd = prob(logit_at<DT>(p.draftl, draft_row(p, b, i) + x), s_m[D + 1 + i], s_iz[D + 1 + i],
-                             s_cut[D + 1 + i], p.inv_t);
-      const double u = (double)p.u_accept[(int64_t)b * D + i];
-      ok = qd > 0.0 ? (u * qd <= pt) : (pt > 0.0);
+      const double pt = prob(gt, s_m[t], s_iz[t], s_cut[t], p.inv_t);
+      const double qd = prob(gd, s_m[D + 1 + t], s_iz[D + 1 + t], s_cut[D + 1 + t], p.inv_t);
+      reject = !(qd > 0.0 ? ((double)ua * qd <= pt) : (pt > 0.0));
     } else {
-      bad = SPECDEC_S_DRAFT_RANGE;
+      reject = bad = true;
     }
-    if (!ok) first = min(first, i);
   }
-  const int a = block_min_int(first, s_i);
-  if (s == 0) set_status(p.status, block_or_int(bad, s_i));
-  // residual (a < D) or target (a = D) mass of this thread's run of the split
-  // and of the split, and the same for the target alone
-  const int n = min(kSlChunk, V - s * kSlChunk);
+  const int a = min(block_first<kSlThreads>(reject, s_i), D);
+  if (s == 0) {
+    const bool any_bad = block_first<kSlThreads>(bad, s_i) != INT_MAX;
+    if (t == 0 && any_bad) set_status(p.status, SPECDEC_S_DRAFT_RANGE);
+  }
+  if (s == 0 && t == a) s_ud = ud;
+
+  // this thread's run of the stop row's split, and the split's totals
   const bool resid = a < D;
-  float lt[kSlPer], lq[kSlPer];
-  load_run<DT, VEC>(p.target, target_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lt);
-  if (resid) {
-    load_run<DT, VEC>(p.draftl, draft_row(p, b, a) + (int64_t)s * kSlChunk, threadIdx.x, n, lq);
-  } else {
-#pragma unroll
-    for (int k = 0; k < kSlPer; ++k) lq[k] = 0.0f;
-  }
-  // (M, 1/Z) of the stop row's target and draft rows and their thresholds
   const double ri[6] = {s_m[a], s_iz[a], resid ? s_m[D + 1 + a] : 0.0, resid ? s_iz[D + 1 + a] : 0.0,
                         (double)s_cut[a], resid ? (double)s_cut[D + 1 + a] : 0.0};
+  float lt[kSlRun], lq[kSlRun];
+  const int n = min(kSlChunk, V - s * kSlChunk);
+  load_run<DT, VEC>(p.target, target_row(p, b, a) + (int64_t)s * kSlChunk, t, n, lt);
+  if (resid) {
+    load_run<DT, VEC>(p.draftl, draft_row(p, b, a) + (int64_t)s * kSlChunk, t, n, lq);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSlRun; ++k) lq[k] = 0.0f;
+  }
   double wsum = 0.0, psum = 0.0;
-#pragma unroll 4
-  for (int k = 0; k < kSlPer; ++k) {
+#pragma unroll
+  for (int k = 0; k < kSlRun; ++k) {
     wsum += weight(lt[k], lq[k], resid, ri, p.inv_t);
     psum += prob(lt[k], ri[0], ri[1], (float)ri[4], p.inv_t);
   }
-  double *thr = p.thr + (((int64_t)b * p.S + s) * kBlock + threadIdx.x) * 2;
+  double *thr = p.thr + (((int64_t)b * S + s) * kSlThreads + t) * 2;
   thr[0] = wsum;
   thr[1] = psum;
-  wsum = block_sum_d(wsum, s_d);
-  psum = block_sum_d(psum, s_d);
-  if (threadIdx.x == 0) {
-    p.part[((int64_t)b * p.S + s) * 2] = wsum;
-    p.part[((int64_t)b * p.S + s) * 2 + 1] = psum;
+  wsum = wave_total_f64(wsum);
+  psum = wave_total_f64(psum);
+  if (lane == 0) {
+    s_w[wv] = wsum;
+    s_p[wv] = psum;
+  }
+  __syncthreads();
+  if (t == 0) {
+    double tw = s_w[0], tp = s_p[0];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) {
+      tw += s_w[k];
+      tp += s_p[k];
+    }
+    p.part[((int64_t)b * S + s) * 2] = tw;
+    p.part[((int64_t)b * S + s) * 2 + 1] = tp;
     if (s == 0) {
       double *o = p.rowinfo + (int64_t)b * 8;
 #pragma unroll
       for (int k = 0; k < 6; ++k) o[k] = ri[k];
-      p.stop[b] = a;
+      o[6] = (double)s_ud;
+      o[7] = (double)a;
     }
   }
 }
 
-// One workgroup per batch row: the split in which the running mass first
-// exceeds u * T (split masses in split order), then the thread run in which it
-// does (thread masses in thread order), then the id (that run's weights in id
-// order, recomputed exactly as the mass kernel formed them).
+// One workgroup per (split, batch row).  In one round trip every workgroup
+// reads the batch row's split totals, its own split's run sums and the stop
+// row's parameters; each then finds, alike, the split in which the running
+// mass (split totals in split order) first exceeds u T.  Only that split's
+// workgroup goes on: a block scan of its run sums in thread order picks the
+// run that crosses, and the run's weights, formed again with the mass kernel's
+// functions (one id per lane) and added in id order as the mass kernel added
+// them, give the id; the partial sums end at the run's sum, so the crossing lies
+// inside the run.  A zero residual falls back to p; when rounding leaves no
+// crossing, the last id with positive weight is taken; an all-zero row gives id
+// 0 and SPECDEC_S_PROB.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
-  __shared__ double s_d[kBlock / kWave];
-  __shared__ int s_i[kBlock / kWave];
+__global__ __launch_bounds__(kSlThreads) void k_sl_draw(SampleLogitsParams p) {
+  constexpr int NW = kSlThreads / kWave;
   __shared__ double s_part[2 * kSlMaxSplits];
-  __shared__ double s_base, s_target;
-  __shared__ int s_split, s_flags;  // flags: 1 draw from p, 2 no crossing (take the last positive id), 4 zero mass
-  const int b = blockIdx.x, D = p.D, V = p.V, S = p.S;
-  const int a = p.stop[b];
+  __shared__ double s_w[NW];
+  __shared__ int s_i[NW];
+  __shared__ double s_base, s_target, s_wt[kSlRun];
+  __shared__ int s_split, s_flags;
+  const int s = blockIdx.x, b = blockIdx.y;
+  const int S = p.S, D = p.D, V = p.V;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
   const double *part = p.part + (int64_t)b * S * 2;
-  for (int k = threadIdx.x; k < 2 * S; k += kBlock) s_part[k] = part[k];
+  for (int k = t; k < S; k += kSlThreads) {
+    s_part[2 * k] = part[2 * k];
+    s_part[2 * k + 1] = part[2 * k + 1];
+  }
+  const double *thr = p.thr + (((int64_t)b * S + s) * kSlThreads + t) * 2;
+  const double rw = thr[0], rp = thr[1];
+  double ri[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ri[k] = p.rowinfo[(int64_t)b * 8 + k];
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     double T = 0.0, Tp = 0.0;
     for (int k = 0; k < S; ++k) {
       T += s_part[2 * k];
       Tp += s_part[2 * k + 1];
     }
-    int flags = 0;
+    int flags = 0;  // 1: draw from p, 2: no crossing (take the last positive id), 4: zero mass
     if (!(T > 0.0)) {
       flags |= 1;
       T = Tp;
@@ -622,17 +706,24 @@ __global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
     int split = -1;
     double base = 0.0, target = 0.0;
     if (T > 0.0) {
-      target = (double)p.u_draw[(int64_t)b * (D + 1) + a] * T;
+      target = ri[6] * T;
       double c = 0.0;
       for (int k = 0; k < S; ++k) {
         const double cn = c + s_part[2 * k + e];
-        if (cn > target) { split = k; base = c; break; }
+        if (cn > target) {
+          split = k;
+          base = c;
+          break;
+        }
         c = cn;
       }
       if (split < 0) {
         flags |= 2;
         for (int k = S - 1; k >= 0; --k)
-          if (s_part[2 * k + e] > 0.0) { split = k; break; }
+          if (s_part[2 * k + e] > 0.0) {
+            split = k;
+            break;
+          }
       }
     } else {
       flags |= 4;
@@ -644,61 +735,74 @@ __global__ __launch_bounds__(kBlock) void k_sl_draw(SampleLogitsParams p) {
     s_flags = flags;
   }
   __syncthreads();
-  const int flags = s_flags, split = s_split;
+  const int flags = s_flags, a = (int)ri[7];
+  if (s_split != s) return;
   if (flags & 4) {
-    if (threadIdx.x == 0) {
+    if (t == 0) {
       p.accept_len[b] = a;
       p.next_token[b] = 0;
       set_status(p.status, SPECDEC_S_PROB);
     }
     return;
   }
-  const int e = flags & 1;
-  const bool resid = a < D && !e;
-  // thread runs of the split: the first whose running mass exceeds the target
-  // (or, with no crossing, the last with positive mass)
-  const double m = p.thr[(((int64_t)b * S + split) * kBlock + threadIdx.x) * 2 + e];
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  const double incl = wave_incl_scan(m, lane);
-  if (lane == kWave - 1) s_d[wv] = incl;
+  const bool use_p = flags & 1, resid = a < D && !use_p;
+  const double target = s_target;
+  // the runs of this split, scanned in thread order
+  const double m = use_p ? rp : rw;
+  const double incl = wave_scan_f64(m);
+  if (lane == kWave - 1) s_w[wv] = incl;
   __syncthreads();
-  double before = s_base + incl - m;
-  for (int k = 0; k < wv; ++k) before += s_d[k];
-  const bool cross = !(flags & 2) && m > 0.0 && before + m > s_target;
-  int run = block_min_int(cross ? (int)threadIdx.x : INT_MAX, s_i);
-  if (run == INT_MAX) run = block_max_int(m > 0.0 ? (int)threadIdx.x : -1, s_i);
-  if (threadIdx.x == (unsigned)max(run, 0)) s_base = before;  // mass before the chosen run
-  __syncthreads();
-  // the chosen run's weights, one id per thread of the first wave, in id order
-  const int v0 = split * kSlChunk, n = min(kSlChunk, V - v0);
-  const int i = max(run, 0) * kSlPer + lane;
-  double w = 0.0;
-  if (threadIdx.x < kSlPer && run >= 0 && i < n) {
-    const float lt = logit_at<DT>(p.target, target_row(p, b, a) + v0 + i);
-    const float lq = resid ? logit_at<DT>(p.draftl, draft_row(p, b, a) + v0 + i) : 0.0f;
-    double ri[6];
+  double ex = 0.0;
 #pragma unroll
-    for (int k = 0; k < 6; ++k) ri[k] = p.rowinfo[(int64_t)b * 8 + k];
-    w = weight(lt, lq, resid, ri, p.inv_t);
-  }
-  if (threadIdx.x < kWave) {
-    const double c = s_base + wave_incl_scan(w, lane);
-    const bool hit = !(flags & 2) && w > 0.0 && c > s_target;
-    const unsigned long long hits = __ballot(hit), pos = __ballot(w > 0.0);
-    if (lane == 0) {
-      int j;
-      if (hits) j = __ffsll((long long)hits) - 1;
-      else j = pos ? 63 - __clzll((long long)pos) : -1;
+  for (int k = 0; k < NW; ++k)
+    if (k < wv) ex += s_w[k];
+  const double before = s_base + (ex + (incl - m));
+  const bool cross = !(flags & 2) && m > 0.0 && before + m > target;
+  const int who = block_first<kSlThreads>(cross, s_i);
+  const int run = who != INT_MAX ? who : block_last<kSlThreads>(m > 0.0, s_i);
+  if (run < 0) {  // no run with mass: not reached when the split was chosen for its mass
+    if (t == 0) {
       p.accept_len[b] = a;
-      p.next_token[b] = j >= 0 ? v0 + max(run, 0) * kSlPer + j : 0;
+      p.next_token[b] = 0;
     }
+    return;
+  }
+  // the run's weights, one id per lane of the first wave
+  const int v0 = s * kSlChunk + run * kSlRun;
+  if (t < kSlRun) {
+    double w = 0.0;
+    if (v0 + t < V) {
+      const float lt = logit_at<DT>(p.target, target_row(p, b, a) + v0 + t);
+      const float lq = resid ? logit_at<DT>(p.draftl, draft_row(p, b, a) + v0 + t) : 0.0f;
+      w = use_p ? prob(lt, ri[0], ri[1], (float)ri[4], p.inv_t) : weight(lt, lq, resid, ri, p.inv_t);
+    }
+    s_wt[t] = w;
+  }
+  if (t == run) s_base = before;  // the mass before the run
+  __syncthreads();
+  if (t == 0) {
+    // the same additions, in the same order, as the run's sum
+    const double bef = s_base;
+    int j = -1, lastpos = -1;
+    double c = 0.0;
+    for (int k = 0; k < kSlRun; ++k) {
+      const double w = s_wt[k];
+      c += w;
+      if (w > 0.0) {
+        lastpos = k;
+        if (j < 0 && who != INT_MAX && bef + c > target) j = k;
+      }
+    }
+    j = j >= 0 ? j : lastpos;
+    p.accept_len[b] = a;
+    p.next_token[b] = j >= 0 ? v0 + j : 0;
   }
 }
 
 template <int DT, bool VEC>
 static hipError_t launch_sl(const SampleLogitsParams &p, hipStream_t s) {
-  hipLaunchKernelGGL((k_sl_stats<DT, VEC>), dim3((unsigned)p.S, (unsigned)(2 * p.D + 1), (unsigned)p.B),
-                     dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_sl_stats<DT, VEC>), dim3((unsigned)p.Ss, (unsigned)(2 * p.D + 1), (unsigned)p.B),
+                     dim3(kSlStatThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.nucleus) {
@@ -707,10 +811,10 @@ static hipError_t launch_sl(const SampleLogitsParams &p, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_sl_mass<DT, VEC>), dim3((unsigned)p.S, (unsigned)p.B), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_sl_mass<DT, VEC>), dim3((unsigned)p.S, (unsigned)p.B), dim3(kSlThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_sl_draw<DT, VEC>), dim3((unsigned)p.B), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL((k_sl_draw<DT, VEC>), dim3((unsigned)p.S, (unsigned)p.B), dim3(kSlThreads), 0, s, p);
   return hipGetLastError();
 }
 

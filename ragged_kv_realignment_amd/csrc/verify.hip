@@ -12,8 +12,10 @@
 // normalize(max(0, p - q)), take the bonus from p after the full draft.
 #include <math.h>
 #include <limits.h>
+#include "coherent.h"
 #include "device_common.h"
 #include "launch.h"
+#include "wave_dpp.h"
 #include "specdec.h"
 
 namespace sd {
@@ -283,8 +285,6 @@ hipError_t launch_verify_greedy(const GreedyParams &p, hipStream_t s) {
 constexpr int kSampleBatch = 8;  // 16-byte vectors (of p and of q) a thread has in flight
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4v __attribute__((ext_vector_type(4)));
-constexpr int kCoherentPolicy = 16;  // buffer cache policy sc1: through to the device's coherence point
 
 // Residual mass max(0, p - q) of one id in fp64 (q absent: p).
 __device__ __forceinline__ double resid_w(float pv, float qv, bool has_q) {
@@ -311,11 +311,11 @@ __device__ __forceinline__ void run_mass(const float *pa, const float *qa, int l
       }
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
-        if (v0 + 4 * k >= hi) break;
+        const bool in = v0 + 4 * k < hi;  // a repeated vector adds +0 (sums start at +0, terms are >= 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          mw += resid_w(pp[k][e], qq[k][e], qa != nullptr);
-          mp += resid_w(pp[k][e], 0.0f, false);
+          mw += in ? resid_w(pp[k][e], qq[k][e], qa != nullptr) : 0.0;
+          mp += in ? resid_w(pp[k][e], 0.0f, false) : 0.0;
         }
       }
     }
@@ -399,18 +399,6 @@ __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo
 // greedy verification's finish, this rests on gfx950's ordering, not on a
 // release/acquire pair, whose L2 write-back and invalidate would cost more
 // than the whole call.
-__device__ __forceinline__ void st_pair(__amdgpu_buffer_rsrc_t r, uint32_t off, double a, double b) {
-  const long long la = __double_as_longlong(a), lb = __double_as_longlong(b);
-  const i32x4v v = {(int)la, (int)(la >> 32), (int)lb, (int)(lb >> 32)};
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherentPolicy);
-}
-
-__device__ __forceinline__ void ld_pair(__amdgpu_buffer_rsrc_t r, uint32_t off, double &a, double &b) {
-  const i32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentPolicy);
-  a = __longlong_as_double(((long long)(unsigned)v[1] << 32) | (unsigned)v[0]);
-  b = __longlong_as_double(((long long)(unsigned)v[3] << 32) | (unsigned)v[2]);
-}
-
 template <int VW, int NB>
 __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p) {
   constexpr int NW = kSampleThreads / kWave;
@@ -419,43 +407,38 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
   const int b = (int)blockIdx.x - split * B;
   const int D = p.D, D1 = p.D + 1, V = p.V;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
-  __shared__ int s_a, s_bad, s_last, s_sel;
+  __shared__ int s_bad, s_last, s_sel;
   __shared__ double s_w[NW], s_p[NW];
   __shared__ int s_i[NW];
   __shared__ float s_ud;
-  if (t == 0) {
-    s_a = D;
-    s_bad = 0;
-  }
-  __syncthreads();
+  if (t == 0) s_bad = 0;
   // the draw's uniform at every possible stop position, loaded with the
-  // acceptance inputs (D + 1 <= kSampleThreads) and kept for the stop position
+  // acceptance inputs (D + 1 <= kSampleThreads, one position per thread) and
+  // kept for the stop position
   const float ud = t <= D ? p.u_draw[(size_t)b * D1 + t] : 0.0f;
-  for (int i = t; i < D; i += kSampleThreads) {
-    const int x = p.draft[(size_t)b * D + i];
-    bool ok = false;
+  bool reject = false, bad = false;
+  if (t < D) {
+    const int x = p.draft[(size_t)b * D + t];
     if (x >= 0 && x < V) {
-      const double px = p.p[((size_t)b * D1 + i) * V + x];
-      const double qx = p.q[((size_t)b * D + i) * V + x];
-      const double u = p.u_accept[(size_t)b * D + i];
-      ok = qx > 0.0 ? (u * qx <= px) : (px > 0.0);
+      const double px = p.p[((size_t)b * D1 + t) * V + x];
+      const double qx = p.q[((size_t)b * D + t) * V + x];
+      const double u = p.u_accept[(size_t)b * D + t];
+      reject = !(qx > 0.0 ? (u * qx <= px) : (px > 0.0));
     } else {
-      atomicOr(&s_bad, SPECDEC_S_DRAFT_RANGE);
+      reject = bad = true;
     }
-    if (!ok) atomicMin(&s_a, i);
   }
-  __syncthreads();
-  const int a = s_a;
+  const int a = min(block_first<kSampleThreads>(reject, s_i), D);
+  if (block_first<kSampleThreads>(bad, s_i) != INT_MAX && t == 0) s_bad = SPECDEC_S_DRAFT_RANGE;
   if (t == a) s_ud = ud;
   const float *pa = p.p + ((size_t)b * D1 + a) * V;
   const float *qa = a < D ? p.q + ((size_t)b * D + a) * V : nullptr;
   char *blk = p.ws + (size_t)b * kSampleRowBytes;
   unsigned int *counter = reinterpret_cast<unsigned int *>(blk);
   // (residual, p) totals of every split, then of every run: 16 bytes each
-  const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(blk + kAtomicLine, (short)0,
-                                                                      kSampleSplits * 16, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-      blk + kAtomicLine + kSampleSplits * 16, (short)0, kSampleSplits * kSampleThreads * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rt = coherent_rsrc(blk + kAtomicLine, kSampleSplits * 16);
+  const __amdgpu_buffer_rsrc_t rr = coherent_rsrc(blk + kAtomicLine + kSampleSplits * 16,
+                                                  kSampleSplits * kSampleThreads * 16);
 
   // 2. this thread's run of the stop row, and the split's totals
   {
@@ -464,7 +447,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
     double mw, mp;
     run_mass<VW, NB>(pa, qa, lo, hi, mw, mp);
     st_pair(rr, (uint32_t)g * 16u, mw, mp);
-    const double ww = wave_sum(mw), wp = wave_sum(mp);
+    const double ww = wave_total_f64(mw), wp = wave_total_f64(mp);
     if (lane == 0) {
       s_w[wv] = ww;
       s_p[wv] = wp;
@@ -532,7 +515,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
     double rw, rp;
     ld_pair(rr, (uint32_t)g * 16u, rw, rp);
     const double m = use_p ? rp : rw;
-    const double incl = wave_incl_scan(m, lane);
+    const double incl = wave_scan_f64(m);
     if (lane == kWave - 1) s_w[wv] = incl;
     __syncthreads();
     double before = P + (incl - m);
@@ -544,9 +527,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
       before = P + (e + (incl - m));
     }
     const bool cross = m > 0.0 && before + m > tgt;
-    const int who = block_min_int<kSampleThreads>(cross ? t : INT_MAX, s_i);
-    const int lastt = block_max_int<kSampleThreads>(m > 0.0 ? t : -1, s_i);
-    const int me = who != INT_MAX ? who : lastt;
+    const int who = block_first<kSampleThreads>(cross, s_i);
+    const int me = who != INT_MAX ? who : block_last<kSampleThreads>(m > 0.0, s_i);
     if (t == me) {
       const int lo = min(V, g * R), hi = min(V, lo + R);
       const int hit = run_walk<VW>(pa, qw, lo, hi, before, who != INT_MAX ? tgt : INFINITY);
