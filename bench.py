@@ -40,6 +40,7 @@ PAGE = 16  # positions per page of the paged-cache leg
 SPIN_CYCLES_PER_LAUNCH = 200000  # GPU spin ahead of a pass, per launch queued behind it (~100 us at 2 GHz)
 # counter summary and the sources of the realign kernel it was taken on, per realign mode
 VERIFY_SOURCES = ("verify.hip", "coherent.h", "device_common.h", "launch.h", "wave_dpp.h")
+SAMPLE_LOGITS_SOURCES = ("sample_logits.hip", "device_common.h", "launch.h", "wave_dpp.h")
 TRAFFIC = {
     False: (os.path.join(ROOT, "profiles", "realign_eqspec_8b_gqa_traffic.txt"), ("realign.hip",) + _HEADERS),
     True: (os.path.join(ROOT, "profiles", "realign_inplace_8b_gqa_traffic.txt"),
@@ -107,6 +108,17 @@ def verify_sample_traffic(alg_bytes):
     r = _counter_ratio(os.path.join(ROOT, "profiles", "verify_sample_stoch_traffic.txt"),
                        "verify_sample_source_sha256_16", "verify_sample_traffic_over_algorithmic", VERIFY_SOURCES)
     return None if r is None else (r[0] * alg_bytes, r[1].replace("64-round chain", "stoch round"))
+
+
+def sample_logits_traffic(alg_bytes):
+    r = _counter_ratio(os.path.join(ROOT, "profiles", "verify_sample_stoch_traffic.txt"),
+                       "sample_logits_source_sha256_16", "sample_logits_traffic_over_algorithmic",
+                       SAMPLE_LOGITS_SOURCES)
+    if r is None:
+        return None
+    return {"bytes_per_call": r[0] * alg_bytes,
+            "how": r[1].replace("64-round chain", "stoch logits (statistics, mass and draw at top_p 1)")
+                       .replace("per launch", "per call")}
 
 
 def verify_traffic(alg_bytes):
@@ -710,6 +722,8 @@ def _time_sample_logits(cfg, K):
                                     "warm": {"avg_call_us": float(warm * 1e3),
                                              "achieved_gbs": nbytes / (warm * 1e-3) / 1e9,
                                              "how": "logits in the Infinity Cache: calls queued back to back"}}
+        if top_p == 1.0:
+            out["top_p=1"]["traffic"] = sample_logits_traffic(nbytes)
     if int(status.item()) != 0:
         raise RuntimeError("device status %d in sampled verification from logits" % int(status.item()))
     return out
