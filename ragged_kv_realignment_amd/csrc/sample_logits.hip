@@ -6,7 +6,7 @@
 // sampling settings).  p and q are softmax(logits / temperature) of the target
 // and draft rows, formed on the fly: e(v) = exp((l(v) - M) * (1/T)) with M the
 // row maximum, p(v) = e(v) * (1/Z), the exponent reduced in fp64 and the
-// exponential of its fraction taken by the hardware's fp32 exp2 (exp_fast:
+// exponential of its fraction taken by the hardware's fp32 exp2 (exp2_fast:
 // about 1e-7 relative error, ten times inside the 1e-6 tolerance the decisions
 // are held to).  Sums and every comparison are in fp64.
 //
@@ -73,7 +73,7 @@ __device__ __forceinline__ float logit_at(const void *base, int64_t i) {
 // two fused multiply-adds on a two-part constant; e^r is its degree-5 Taylor
 // polynomial (truncation below 4e-17 of the result) and 2^(j/64) comes from a
 // 64-entry table in LDS that exp_tab_fill writes (measured: faster than the
-// library exp in the nucleus kernel; the other kernels take exp_fast below).
+// library exp in the nucleus kernel; the other kernels take exp2_fast below).
 constexpr double kLn2By64Hi = 0x1.62e42fefa39efp-7;
 constexpr double kLn2By64Lo = 0x1.abc9e3b39803fp-62;
 constexpr double k64ByLn2 = 0x1.71547652b82fep+6;
@@ -93,24 +93,22 @@ __device__ __forceinline__ double exp_le0(double y, const double *tab) {
   return ldexp(tab[j] * e, k);
 }
 
-// e^y for y <= 0 with about 1e-7 relative error: y log2(e) = n + f in fp64
-// with n an integer and |f| <= 1/2; 2^f by the hardware's fp32 exp2 (f rounded
-// to fp32 costs at most 2e-8 relative, the instruction a few times 6e-8 on
-// [2^-1/2, 2^1/2]); then scaled by 2^n.  -inf, and anything below -708 (whose
-// e^y is under 1e-307, nothing beside the row's largest term, which is 1),
-// give 0.  About a third of the fp64 instructions of the library exp: the
-// statistics kernel, which takes one exponential per logit, is then bound by
-// its reads rather than by fp64 arithmetic.
+// 2^t for t <= 0 with about 1e-7 relative error, t = y log2(e) for e^y: t =
+// n + f in fp64 with n an integer and |f| <= 1/2; 2^f by the hardware's fp32
+// exp2 (f rounded to fp32 costs at most 2e-8 relative, the instruction a few
+// times 6e-8 on [2^-1/2, 2^1/2]); then scaled by 2^n.  t is clamped at -1100
+// first, where the scaling underflows to 0, so -inf and NaN give 0 with no
+// branch or select (the exponentials of a thread's ids then interleave), and
+// anything below about -1074 gives 0 as well.  Callers form t from an exact
+// fp64 difference times (1/T) log2(e), one rounding.  About a third of the fp64
+// instructions of the library exp.
 constexpr double kLog2e = 0x1.71547652b82fep+0;
 
-// Branch-free (a select at the end), so that the exponentials of a thread's
-// ids interleave instead of each sitting behind its own exec-mask branch.
-__device__ __forceinline__ double exp_fast(double y) {
-  const double t = fmax(y, -708.0) * kLog2e;
-  const double n = rint(t);
-  const float f = (float)(t - n);
-  const double r = ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
-  return y > -708.0 ? r : 0.0;
+__device__ __forceinline__ double exp2_fast(double t) {
+  const double tc = fmax(t, -1100.0);
+  const double n = rint(tc);
+  const float f = (float)(tc - n);
+  return ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
 }
 
 // Row maximum M and 1/Z from the per-split statistics (split order).  Loads
@@ -118,7 +116,8 @@ __device__ __forceinline__ double exp_fast(double y) {
 // sum, so a row of up to kBatch splits costs one round trip.
 constexpr int kBatch = 8;
 
-__device__ __forceinline__ void merge_row(const double *st, int S, double inv_t, double &M, double &inv_z) {
+// c2 = (1/T) log2(e).
+__device__ __forceinline__ void merge_row(const double *st, int S, double c2, double &M, double &inv_z) {
   double m0[kBatch], z0[kBatch];
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
@@ -138,7 +137,7 @@ __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t,
   double z = 0.0;
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
-    const double e = z0[k] * exp_fast((m0[k] - m) * inv_t);
+    const double e = z0[k] * exp2_fast((m0[k] - m) * c2);
     z += m0[k] > -INFINITY ? e : 0.0;
   }
   for (int s0 = kBatch; s0 < S; s0 += kBatch) {
@@ -150,7 +149,7 @@ __device__ __forceinline__ void merge_row(const double *st, int S, double inv_t,
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const double e = zs[k] * exp_fast((ms[k] - m) * inv_t);
+      const double e = zs[k] * exp2_fast((ms[k] - m) * c2);
       z += ms[k] > -INFINITY ? e : 0.0;
     }
   }
@@ -260,6 +259,7 @@ __global__ __launch_bounds__(kSlStatThreads) void k_sl_stats(SampleLogitsParams 
       p.gath[((int64_t)b * D + gi) * 2 + (r > D ? 1 : 0)] = v;
     }
   }
+  const double c2 = p.inv_t * kLog2e;
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kSlStatPer; ++k) m = fmaxf(m, x[k]);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kSlStatThreads) void k_sl_stats(SampleLogitsParams 
   if (m > -INFINITY) {
     const double md = (double)m;
 #pragma unroll
-    for (int k = 0; k < kSlStatPer; ++k) z += exp_fast(((double)x[k] - md) * p.inv_t);  // -inf past n: 0
+    for (int k = 0; k < kSlStatPer; ++k) z += exp2_fast(((double)x[k] - md) * c2);  // -inf past n: 0
   }
   z = block_sum_d<kSlStatThreads>(z, s_d);
   if (threadIdx.x == 0) {
@@ -531,16 +531,16 @@ __device__ __forceinline__ void load_run(const void *base, int64_t off, int t, i
 
 // Probability of a logit in a row with maximum M, 1/Z and nucleus threshold
 // cut (-inf: every id): 0 below the cut and for -inf logits.
-__device__ __forceinline__ double prob(float l, double M, double iz, float cut, double inv_t) {
-  const double v = exp_fast(((double)l - M) * inv_t) * iz;
+__device__ __forceinline__ double prob(float l, double M, double iz, float cut, double c2) {
+  const double v = exp2_fast(((double)l - M) * c2) * iz;
   return l >= cut ? v : 0.0;
 }
 
 // The stop row's weight at one logit: max(0, p - q) at a < D (resid), else p.
-__device__ __forceinline__ double weight(float lt, float lq, bool resid, const double *ri, double inv_t) {
-  const double pv = prob(lt, ri[0], ri[1], (float)ri[4], inv_t);
+__device__ __forceinline__ double weight(float lt, float lq, bool resid, const double *ri, double c2) {
+  const double pv = prob(lt, ri[0], ri[1], (float)ri[4], c2);
   if (!resid) return pv;
-  const double d = pv - prob(lq, ri[2], ri[3], (float)ri[5], inv_t);
+  const double d = pv - prob(lq, ri[2], ri[3], (float)ri[5], c2);
   return d > 0.0 ? d : 0.0;
 }
 
@@ -565,6 +565,7 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_mass(SampleLogitsParams p) {
   const int s = blockIdx.x, b = blockIdx.y;
   const int S = p.S, D = p.D, V = p.V, R = 2 * D + 1;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+  const double c2 = p.inv_t * kLog2e;
 
   int x = -1;
   float gt = 0.0f, gd = 0.0f, ua = 0.0f, ud = 0.0f;
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_mass(SampleLogitsParams p) {
       iz = o[1];
       cut = (float)o[2];
     } else {
-      merge_row(p.stats + ((int64_t)b * R + r) * p.Ss * 2, p.Ss, p.inv_t, M, iz);
+      merge_row(p.stats + ((int64_t)b * R + r) * p.Ss * 2, p.Ss, c2, M, iz);
     }
     s_m[r] = M;
     s_iz[r] = iz;
@@ -596,8 +597,8 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_mass(SampleLogitsParams p) {
   bool reject = false, bad = false;
   if (t < D) {
     if (x >= 0 && x < V) {
-      const double pt = prob(gt, s_m[t], s_iz[t], s_cut[t], p.inv_t);
-      const double qd = prob(gd, s_m[D + 1 + t], s_iz[D + 1 + t], s_cut[D + 1 + t], p.inv_t);
+      const double pt = prob(gt, s_m[t], s_iz[t], s_cut[t], c2);
+      const double qd = prob(gd, s_m[D + 1 + t], s_iz[D + 1 + t], s_cut[D + 1 + t], c2);
       reject = !(qd > 0.0 ? ((double)ua * qd <= pt) : (pt > 0.0));
     } else {
       reject = bad = true;
@@ -626,8 +627,8 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_mass(SampleLogitsParams p) {
   double wsum = 0.0, psum = 0.0;
 #pragma unroll
   for (int k = 0; k < kSlRun; ++k) {
-    wsum += weight(lt[k], lq[k], resid, ri, p.inv_t);
-    psum += prob(lt[k], ri[0], ri[1], (float)ri[4], p.inv_t);
+    wsum += weight(lt[k], lq[k], resid, ri, c2);
+    psum += prob(lt[k], ri[0], ri[1], (float)ri[4], c2);
   }
   double *thr = p.thr + (((int64_t)b * S + s) * kSlThreads + t) * 2;
   thr[0] = wsum;
@@ -680,6 +681,7 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_draw(SampleLogitsParams p) {
   const int s = blockIdx.x, b = blockIdx.y;
   const int S = p.S, D = p.D, V = p.V;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+  const double c2 = p.inv_t * kLog2e;
   const double *part = p.part + (int64_t)b * S * 2;
   for (int k = t; k < S; k += kSlThreads) {
     s_part[2 * k] = part[2 * k];
@@ -774,7 +776,7 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_draw(SampleLogitsParams p) {
     if (v0 + t < V) {
       const float lt = logit_at<DT>(p.target, target_row(p, b, a) + v0 + t);
       const float lq = resid ? logit_at<DT>(p.draftl, draft_row(p, b, a) + v0 + t) : 0.0f;
-      w = use_p ? prob(lt, ri[0], ri[1], (float)ri[4], p.inv_t) : weight(lt, lq, resid, ri, p.inv_t);
+      w = use_p ? prob(lt, ri[0], ri[1], (float)ri[4], c2) : weight(lt, lq, resid, ri, c2);
     }
     s_wt[t] = w;
   }
