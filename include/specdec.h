@@ -189,15 +189,19 @@ size_t specdec_sample_workspace_bytes(int B, int D, int V);
  *  target        device [B][D+1][V] target logits of element type `dtype`.
  *  draft_logits  device [B][D][V] draft-model logits of the same type.
  *  temperature   > 0 and finite: e(v) = exp((l(v) - M) / T) with M the row
- *                maximum, in fp64.
+ *                maximum, with about 1e-7 relative error (the exponent formed
+ *                in fp64 from an exact difference, 2^f of its fraction by the
+ *                hardware's fp32 exp2); sums and comparisons in fp64.
  *  top_p         in (0, 1].  Below 1 every row (target and draft alike) is cut
  *                to its nucleus: the ids whose logit is at least t, where t is
  *                the largest logit value such that the ids at or above it hold
  *                at least top_p of the row's mass sum(e); every id tied at t is
- *                kept.  The masses deciding t are summed exactly as integer
- *                multiples of 2^-41 (of the maximum's mass), so t differs from
- *                an fp64 evaluation only where the mass above a value is within
- *                V * 2^-42 of top_p * sum(e).  At 1 every id is kept.
+ *                kept.  The masses deciding t carry the relative error of e
+ *                (about 1e-7) and are summed exactly as integer multiples of
+ *                2^-41 (of the maximum's mass), so t differs from an fp64
+ *                evaluation only where the mass above a value is within about
+ *                1e-7 relative (plus V * 2^-42) of top_p * sum(e).  At 1 every
+ *                id is kept.
  *                p(v) = e(v) / Z over the kept ids (Z in fp64), 0 elsewhere.
  *  draft, u_accept, u_draw, accept_len, next_token, status
  *                as for specdec_verify_sample; the acceptance test and the

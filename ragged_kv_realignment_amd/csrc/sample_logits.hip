@@ -65,34 +65,6 @@ __device__ __forceinline__ float logit_at(const void *base, int64_t i) {
   return DT == SPECDEC_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
 }
 
-// exp(y) for y <= 0 in fp64 (-inf, and anything below -745, give 0; NaN stays
-// NaN), by P. T. P. Tang's table-driven method ("Table-driven implementation
-// of the exponential function in IEEE floating-point arithmetic", ACM TOMS
-// 15(2), 1989): 2^k * 2^(j/64) * e^r with n = rint(64 y / ln 2), j = n mod 64,
-// k = (n - j) / 64 and r = y - n (ln 2 / 64), |r| <= ln 2 / 128, formed with
-// two fused multiply-adds on a two-part constant; e^r is its degree-5 Taylor
-// polynomial (truncation below 4e-17 of the result) and 2^(j/64) comes from a
-// 64-entry table in LDS that exp_tab_fill writes (measured: faster than the
-// library exp in the nucleus kernel; the other kernels take exp2_fast below).
-constexpr double kLn2By64Hi = 0x1.62e42fefa39efp-7;
-constexpr double kLn2By64Lo = 0x1.abc9e3b39803fp-62;
-constexpr double k64ByLn2 = 0x1.71547652b82fep+6;
-constexpr int kExpTab = 64;
-
-__device__ __forceinline__ void exp_tab_fill(double *tab) {
-  for (int j = threadIdx.x; j < kExpTab; j += blockDim.x) tab[j] = exp2((double)j / kExpTab);
-}
-
-__device__ __forceinline__ double exp_le0(double y, const double *tab) {
-  if (!(y > -745.0)) return y != y ? y : 0.0;
-  const double n = rint(y * k64ByLn2);
-  const double r = fma(-n, kLn2By64Lo, fma(-n, kLn2By64Hi, y));
-  const int ni = (int)n;
-  const int j = ni & (kExpTab - 1), k = (ni - j) >> 6;
-  const double e = fma(fma(fma(fma(fma(1.0 / 120.0, r, 1.0 / 24.0), r, 1.0 / 6.0), r, 0.5), r, 1.0), r, 1.0);
-  return ldexp(tab[j] * e, k);
-}
-
 // 2^t for t <= 0 with about 1e-7 relative error, t = y log2(e) for e^y: t =
 // n + f in fp64 with n an integer and |f| <= 1/2; 2^f by the hardware's fp32
 // exp2 (f rounded to fp32 costs at most 2e-8 relative, the instruction a few
@@ -395,7 +367,8 @@ __device__ __forceinline__ int nuc_select(const unsigned long long *hist, unsign
 
 // One workgroup per (row r of 2D+1, batch row b): the nucleus threshold t and
 // 1/Z over the nucleus, written to nuc[(b R + r) * 4 + {0, 1, 2}] = (M, 1/Z, t).
-// Masses are exp(-y) with y = (M - x) / T, held as 2^-41 fixed-point integers
+// Masses are exp(-y) with y = (M - x) / T (exp2_fast, about 1e-7 relative
+// error like every mass of this path), rounded to 2^-41 fixed-point integers
 // so every sum is exact and order-free.  t is selected level by level: the
 // first level bins the logits by y (monotone in the logit, and spread over the
 // bins whatever the logits' exponents), the later ones bin the 32-bit order
@@ -412,8 +385,6 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
   __shared__ double s_d[kNucThreads / kWave];
   __shared__ int s_i[kNucThreads / kWave];
   __shared__ unsigned long long s_above, s_cmass;
-  __shared__ double s_tab[kExpTab];
-  exp_tab_fill(s_tab);
   const int r = blockIdx.x, b = blockIdx.y;
   const int D = p.D, V = p.V, R = 2 * D + 1;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -439,7 +410,9 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
   // y of a logit, and the first level's bin (larger logits in higher bins)
   auto y_of = [&](float x) { return (M - (double)x) * inv_t; };
   auto bin0 = [&](double y) { return kNucBins - 1 - min(kNucBins - 1, max(0, (int)(y * kNucScale))); };
-  auto fixed_mass = [&](double y) -> unsigned long long { return (unsigned long long)(exp_le0(-y, s_tab) * kFix + 0.5); };
+  auto fixed_mass = [&](double y) -> unsigned long long {
+    return (unsigned long long)(exp2_fast(-y * kLog2e) * kFix + 0.5);
+  };
 
   // first level: bins in y
   for_each([&](float x) {
