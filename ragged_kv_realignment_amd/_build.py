@@ -11,7 +11,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspecdec.so")
-# the benchmark's measurement kernel (a bare read with verification's launch shape), not part of the C ABI
+# the benchmark's measurement kernels (bare reads with library kernels' launch shapes), not part of the C ABI
 MEASURE_LIB = os.path.join(HERE, "libspecdec_measure.so")
 MEASURE_SOURCES = ["csrc/measure.hip"]
 OBJ = os.path.join(HERE, "_build")
