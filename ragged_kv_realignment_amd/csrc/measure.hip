@@ -35,11 +35,29 @@ long chunk_for(int B, int D, int V, int es) {
   return chunk;
 }
 
+// Division by a divisor fixed per launch with a multiply-high (Granlund and
+// Montgomery, PLDI 1994), as greedy verification numbers its workgroups.
+struct Div {
+  uint32_t d, m, s;
+};
+Div make_div(uint32_t d) {
+  Div f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1ull);
+  return f;
+}
+__device__ __forceinline__ uint32_t div_by(uint32_t n, const Div &f) {
+  return (uint32_t)(((unsigned long long)__umulhi(n, f.m) + n) >> f.s);
+}
+
 __global__ __launch_bounds__(kThreads) void k_read_floor(const char *logits, int64_t row_bytes, int V, int es,
-                                                         int splits, int chunk, uint32_t *sink) {
+                                                         int chunk, Div rows_div, uint32_t *sink) {
   const int vw = 16 / es;
-  const int rows = (int)gridDim.x / splits;
-  const int split = (int)blockIdx.x / rows;
+  const int rows = (int)rows_div.d;
+  const int split = (int)div_by(blockIdx.x, rows_div);
   const int row = (int)blockIdx.x - split * rows;
   const int start = split * chunk;
   const int end = min(V, start + chunk);
@@ -116,8 +134,8 @@ extern "C" __attribute__((visibility("default"))) int specdec_measure_read_floor
   const long grid = (long)B * (D + 1) * splits;
   if (grid > sink_words || grid > 0x7FFFFFFFL) return -1;
   hipLaunchKernelGGL(k_read_floor, dim3((unsigned)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const char *>(logits), (int64_t)row_stride * es, V, es, (int)splits, (int)chunk,
-                     sink);
+                     static_cast<const char *>(logits), (int64_t)row_stride * es, V, es, (int)chunk,
+                     make_div((uint32_t)((long)B * (D + 1))), sink);
   return hipGetLastError() == hipSuccess ? (int)grid : -1;
 }
 
