@@ -219,16 +219,17 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
   }
   __syncthreads();
   if (!s_last) return;
-  // D + 1 <= NT (checked on the host): one position per thread
+  // D + 1 <= NT (checked on the host): one position per thread.  The draft
+  // token and the key are loaded together (one round trip), and the keys are
+  // cleared only after the outputs, so no wait covers those stores.
   const int i = threadIdx.x;
+  unsigned long long *kp = &p.keys[((size_t)b * D1 + min(i, D)) * kKeyStride];
   if (i < D1) {
-    unsigned long long *kp = &p.keys[((size_t)b * D1 + i) * kKeyStride];
+    const int d = i < D ? p.draft[(size_t)b * D + i] : 0;
     const int t = key_id(load_agent(kp));
-    store_agent(kp, 0ull);
     s_t[i] = t;
     if (p.target_tok) p.target_tok[(size_t)b * D1 + i] = t;
     if (i < D) {
-      const int d = p.draft[(size_t)b * D + i];
       if (d < 0 || d >= p.V) s_bad = 1;
       if (d != t) atomicMin(&s_a, i);
     }
@@ -241,6 +242,7 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(GreedyParams p, int splits
     store_agent(&p.counters[(size_t)b * kCountStride], 0u);
     if (s_bad) set_status(p.status, SPECDEC_S_DRAFT_RANGE);
   }
+  if (i < D1) store_agent(kp, 0ull);
 }
 
 int device_cus() {
