@@ -655,16 +655,18 @@ __global__ __launch_bounds__(kSlThreads) void k_sl_draw(SampleLogitsParams p) {
   const int S = p.S, D = p.D, V = p.V;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
   const double c2 = p.inv_t * kLog2e;
-  const double *part = p.part + (int64_t)b * S * 2;
-  for (int k = t; k < S; k += kSlThreads) {
-    s_part[2 * k] = part[2 * k];
-    s_part[2 * k + 1] = part[2 * k + 1];
-  }
+  // one round trip: this thread's run sums and the stop row's parameters are
+  // issued before the split totals, whose LDS copy waits for all of them
   const double *thr = p.thr + (((int64_t)b * S + s) * kSlThreads + t) * 2;
   const double rw = thr[0], rp = thr[1];
   double ri[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) ri[k] = p.rowinfo[(int64_t)b * 8 + k];
+  const double *part = p.part + (int64_t)b * S * 2;
+  for (int k = t; k < S; k += kSlThreads) {
+    s_part[2 * k] = part[2 * k];
+    s_part[2 * k + 1] = part[2 * k + 1];
+  }
   __syncthreads();
   if (t == 0) {
     double T = 0.0, Tp = 0.0;
