@@ -348,24 +348,25 @@ __device__ __forceinline__ void run_mass(const float *pa, const float *qa, int l
 
 // The first id of the run [lo, hi) at which before + (the run's weights summed
 // in id order, as run_mass sums them) passes target; else the run's last id
-// with a positive weight (-1 if none).  The same loads in the same batches, so
-// the partial sums end exactly at run_mass's result.
-template <int VW>
+// with a positive weight (-1 if none).  The same additions in the same order
+// (loads in batches of NB vectors, as run_mass), so the partial sums end
+// exactly at run_mass's result.
+template <int VW, int NB>
 __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo, int hi, double before,
                                         double target) {
   double c = 0.0;
   int last = -1;
   if constexpr (VW == 4) {
-    for (int v0 = lo; v0 < hi; v0 += 4 * kSampleBatch) {
-      f32x4 pp[kSampleBatch], qq[kSampleBatch];
+    for (int v0 = lo; v0 < hi; v0 += 4 * NB) {
+      f32x4 pp[NB], qq[NB];
 #pragma unroll
-      for (int k = 0; k < kSampleBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
         const int v = min(v0 + 4 * k, hi - 4);
         pp[k] = *reinterpret_cast<const f32x4 *>(pa + v);
         qq[k] = qa ? *reinterpret_cast<const f32x4 *>(qa + v) : (f32x4)(0.0f);
       }
 #pragma unroll
-      for (int k = 0; k < kSampleBatch; ++k) {
+      for (int k = 0; k < NB; ++k) {
         const int v = v0 + 4 * k;
         if (v >= hi) break;
 #pragma unroll
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
     const int me = who != INT_MAX ? who : block_last<kSampleThreads>(m > 0.0, s_i);
     if (t == me) {
       const int lo = min(V, g * R), hi = min(V, lo + R);
-      const int hit = run_walk<VW>(pa, qw, lo, hi, before, who != INT_MAX ? tgt : INFINITY);
+      const int hit = run_walk<VW, NB>(pa, qw, lo, hi, before, who != INT_MAX ? tgt : INFINITY);
       s_sel = hit >= 0 ? hit : 0;
     }
     __syncthreads();
