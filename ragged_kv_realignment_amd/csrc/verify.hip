@@ -402,9 +402,10 @@ __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo
 //     the split's totals.  Run sums and split totals go to row b's workspace
 //     block.
 //  3. The workgroup counts itself in row b's counter; the last of the S to
-//     arrive draws.  Every thread adds the split totals in split order (the
-//     same arithmetic in every thread): the total T, and the first split whose
-//     end passes the target u_draw[a] * T.  That split's run sums are loaded,
+//     arrive draws.  Each wave scans the split totals across its lanes, lane k
+//     holding split k (the same arithmetic in every wave): the total T, and
+//     the first split with mass whose end passes the target u_draw[a] * T.
+//     That split's run sums are loaded,
 //     one per thread, and scanned in thread order; the first run whose end
 //     passes the target is walked again, id by id in the order step 2 summed
 //     it, from its starting mass, so the partial sums end exactly at the run's
@@ -489,46 +490,27 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
   __syncthreads();
   if (!s_last) return;
 
-  // 3. the draw, by the last of row b's workgroups: the split totals in split
-  // order (every thread alike)
-  double sw[kSampleSplits], sp[kSampleSplits];
-#pragma unroll
-  for (int k = 0; k < kSampleSplits; ++k) {
-    if (k < S) ld_pair(rt, (uint32_t)k * 16u, sw[k], sp[k]);
-    else sw[k] = sp[k] = 0.0;
-  }
-  double Tw = 0.0, Tp = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSampleSplits; ++k) {
-    Tw += sw[k];
-    Tp += sp[k];
-  }
+  // 3. the draw, by the last of row b's workgroups.  Lane k of every wave holds
+  // split k's totals (k < S <= 64); a DPP scan in lane order gives each split's
+  // running mass and, in the last lane, the totals, alike in every wave.
+  double mw, mp;
+  ld_pair(rt, (uint32_t)min(lane, S - 1) * 16u, mw, mp);
+  if (lane >= S) mw = mp = 0.0;
+  const double iw = wave_scan_f64(mw), ip = wave_scan_f64(mp);
+  const double Tw = lane_f64(iw, kWave - 1), Tp = lane_f64(ip, kWave - 1);
   const bool use_p = !(Tw > 0.0);  // zero residual: fall back to p at the stop position
   const double T = use_p ? Tp : Tw;
   const float *qw = use_p ? nullptr : qa;
   int j = 0;
   if (T > 0.0) {
     const double target = (double)s_ud * T;
-    // the first split whose end passes the target (else the last with mass)
-    double P = 0.0, Plast = 0.0;
-    int ss = -1, slast = 0;
-#pragma unroll
-    for (int k = 0; k < kSampleSplits; ++k) {
-      const double m = use_p ? sp[k] : sw[k];
-      if (k < S && ss < 0) {
-        if (m > 0.0) {
-          slast = k;
-          Plast = P;
-          if (P + m > target) ss = k;
-        }
-        if (ss < 0) P += m;
-      }
-    }
-    const bool found = ss >= 0;
-    if (!found) {
-      ss = slast;
-      P = Plast;
-    }
+    // the first split with mass whose end passes the target (else the last
+    // split with mass) and the mass before it
+    const double ms = use_p ? mp : mw, is = use_p ? ip : iw;
+    const unsigned long long hit = __ballot(ms > 0.0 && is > target), pos = __ballot(ms > 0.0);
+    const bool found = hit != 0;
+    const int ss = found ? __builtin_ctzll(hit) : 63 - __builtin_clzll(pos);
+    const double P = lane_f64(is - ms, ss);
     const double tgt = found ? target : INFINITY;  // no crossing: walk to the last id with mass
     // that split's runs, one per thread, scanned in thread order
     const int g = ss * kSampleThreads + t;
