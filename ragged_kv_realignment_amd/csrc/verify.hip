@@ -439,11 +439,15 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
   const float ud = t <= D ? p.u_draw[(size_t)b * D1 + t] : 0.0f;
   bool reject = false, bad = false;
   if (t < D) {
+    // the uniform is loaded with the draft token, not behind the gather that
+    // depends on the token (the empty asm keeps the compiler from sinking it)
     const int x = p.draft[(size_t)b * D + t];
+    float uf = p.u_accept[(size_t)b * D + t];
+    asm volatile("" : "+v"(uf));
     if (x >= 0 && x < V) {
       const double px = p.p[((size_t)b * D1 + t) * V + x];
       const double qx = p.q[((size_t)b * D + t) * V + x];
-      const double u = p.u_accept[(size_t)b * D + t];
+      const double u = uf;
       reject = !(qx > 0.0 ? (u * qx <= px) : (px > 0.0));
     } else {
       reject = bad = true;
