@@ -389,6 +389,63 @@ __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo
   return last;
 }
 
+// A run of exactly 4 NB ids [lo, hi) loaded as run_mass loads it (NB vectors
+// of p and of q, out-of-range vectors repeating the last one), for a walk from
+// registers.  Without q the q loads re-read p (not used), so no branch splits
+// the loads.
+template <int NB>
+__device__ __forceinline__ void run_load(const float *pa, const float *qa, int lo, int hi, f32x4 (&pp)[NB],
+                                         f32x4 (&qq)[NB]) {
+  const float *qs = qa ? qa : pa;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int v = min(lo + 4 * k, hi - 4);
+    pp[k] = *reinterpret_cast<const f32x4 *>(pa + v);
+    qq[k] = *reinterpret_cast<const f32x4 *>(qs + v);
+  }
+}
+
+// run_mass's two sums of a run held in registers by run_load: the same
+// additions in the same order, so the same values.
+template <int NB>
+__device__ __forceinline__ void run_sums_regs(const f32x4 (&pp)[NB], const f32x4 (&qq)[NB], bool has_q, int lo,
+                                              int hi, double &mw, double &mp) {
+  mw = 0.0;
+  mp = 0.0;
+  if (lo >= hi) return;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const bool in = lo + 4 * k < hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mw += in ? resid_w(pp[k][e], qq[k][e], has_q) : 0.0;
+      mp += in ? resid_w(pp[k][e], 0.0f, false) : 0.0;
+    }
+  }
+}
+
+// run_walk over a run held in registers by run_load: the same additions in
+// the same order as run_mass.
+template <int NB>
+__device__ __forceinline__ int run_walk_regs(const f32x4 (&pp)[NB], const f32x4 (&qq)[NB], bool has_q, int lo,
+                                             int hi, double before, double target) {
+  double c = 0.0;
+  int last = -1;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int v = lo + 4 * k;
+    if (v >= hi) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double w = resid_w(pp[k][e], qq[k][e], has_q);
+      c += w;
+      if (w > 0.0) last = v + e;
+      if (before + c > target) return v + e;
+    }
+  }
+  return last;
+}
+
 // Sampled verification spread over the chip: batch row b's stop row is cut
 // into S splits of kSampleThreads runs of R consecutive ids (run g = split *
 // kSampleThreads + thread covers ids [g R, g R + R)); one workgroup per (split,
@@ -399,28 +456,33 @@ __device__ __forceinline__ int run_walk(const float *pa, const float *qa, int lo
 //  2. Each thread sums its run of the stop row in id order in fp64: the
 //     residual weights max(0, p_a - q_a) (p_D for the bonus) and, for the
 //     fallback, p_a.  The workgroup adds its runs' sums in a fixed order into
-//     the split's totals.  Run sums and split totals go to row b's workspace
-//     block.
+//     the split's totals, which go to row b's workspace block.
 //  3. The workgroup counts itself in row b's counter; the last of the S to
 //     arrive draws.  Each wave scans the split totals across its lanes, lane k
 //     holding split k (the same arithmetic in every wave): the total T, and
 //     the first split with mass whose end passes the target u_draw[a] * T.
-//     That split's run sums are loaded,
-//     one per thread, and scanned in thread order; the first run whose end
-//     passes the target is walked again, id by id in the order step 2 summed
-//     it, from its starting mass, so the partial sums end exactly at the run's
-//     sum and the crossing id lies inside it.  Rounding that leaves no crossing
-//     takes the last id with positive weight.  A zero residual falls back to
-//     p_a; an all-zero row gives id 0 and SPECDEC_S_PROB.
+//     That split's run sums, one per thread, are scanned in thread order; the
+//     first run whose end passes the target is walked again, id by id in the
+//     order step 2 summed it, from its starting mass, so the partial sums end
+//     exactly at the run's sum and the crossing id lies inside it.  Rounding
+//     that leaves no crossing takes the last id with positive weight.  A zero
+//     residual falls back to p_a; an all-zero row gives id 0 and
+//     SPECDEC_S_PROB.
+// The run sums of step 3: with PRE (runs of exactly 4 NB ids, e.g. 8) each
+// thread of the drawing workgroup loads its run of the chosen split and forms
+// its sums again, with step 2's additions in step 2's order (so the same
+// values), and the crossing run is walked from the registers that hold it;
+// step 2 then stores only the split totals.  Otherwise step 2 also stores every
+// run's sums in the workspace block and step 3 loads the chosen split's.
 // Ordering.  Sums are stored and loaded with the sc1 cache policy (written
 // through to, and read from, the device's coherence point, past the
-// non-coherent L2), and every thread waits for its stores to complete (vmcnt)
-// before the workgroup's barrier; the count is issued after it, and the last
-// workgroup loads the sums only after its own count has returned.  As with
-// greedy verification's finish, this rests on gfx950's ordering, not on a
+// non-coherent L2); every store waits to complete (vmcnt) before the count,
+// which thread 0 issues after the workgroup's barrier, and the last workgroup
+// loads the sums only after its own count has returned.  As with greedy
+// verification's finish, this rests on gfx950's ordering, not on a
 // release/acquire pair, whose L2 write-back and invalidate would cost more
 // than the whole call.
-template <int VW, int NB>
+template <int VW, int NB, bool PRE>
 __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p, FastDiv b_div) {
   constexpr int NW = kSampleThreads / kWave;
   const int B = p.B, S = p.S, R = p.R;
@@ -471,12 +533,13 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
     const int lo = min(V, g * R), hi = min(V, lo + R);
     double mw, mp;
     run_mass<VW, NB>(pa, qa, lo, hi, mw, mp);
-    st_pair(rr, (uint32_t)g * 16u, mw, mp);
+    if constexpr (!PRE) st_pair(rr, (uint32_t)g * 16u, mw, mp);
     const double ww = wave_total_f64(mw), wp = wave_total_f64(mp);
     if (lane == 0) {
       s_w[wv] = ww;
       s_p[wv] = wp;
     }
+    if constexpr (!PRE) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t == 0) {
       double tw = 0.0, tp = 0.0;
@@ -486,11 +549,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
         tp += s_p[k];
       }
       st_pair(rt, (uint32_t)split * 16u, tw, tp);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      s_last = atomicAdd(counter, 1u) == (unsigned)(S - 1);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  __syncthreads();
-  if (t == 0) s_last = atomicAdd(counter, 1u) == (unsigned)(S - 1);
   __syncthreads();
   if (!s_last) return;
 
@@ -518,8 +580,15 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
     const double tgt = found ? target : INFINITY;  // no crossing: walk to the last id with mass
     // that split's runs, one per thread, scanned in thread order
     const int g = ss * kSampleThreads + t;
+    const int lo = min(V, g * R), hi = min(V, lo + R);
+    f32x4 pp[NB], qq[NB];
     double rw, rp;
-    ld_pair(rr, (uint32_t)g * 16u, rw, rp);
+    if constexpr (PRE) {
+      run_load<NB>(pa, qa, lo, hi, pp, qq);
+      run_sums_regs<NB>(pp, qq, qa != nullptr, lo, hi, rw, rp);
+    } else {
+      ld_pair(rr, (uint32_t)g * 16u, rw, rp);
+    }
     const double m = use_p ? rp : rw;
     const double incl = wave_scan_f64(m);
     if (lane == kWave - 1) s_w[wv] = incl;
@@ -536,8 +605,12 @@ __global__ __launch_bounds__(kSampleThreads) void k_verify_sample(SampleParams p
     const int who = block_first<kSampleThreads>(cross, s_i);
     const int me = who != INT_MAX ? who : block_last<kSampleThreads>(m > 0.0, s_i);
     if (t == me) {
-      const int lo = min(V, g * R), hi = min(V, lo + R);
-      const int hit = run_walk<VW, NB>(pa, qw, lo, hi, before, who != INT_MAX ? tgt : INFINITY);
+      const double tw = who != INT_MAX ? tgt : INFINITY;
+      int hit;
+      if constexpr (PRE)
+        hit = run_walk_regs<NB>(pp, qq, !use_p && qa != nullptr, lo, hi, before, tw);
+      else
+        hit = run_walk<VW, NB>(pa, qw, lo, hi, before, tw);
       s_sel = hit >= 0 ? hit : 0;
     }
     __syncthreads();
@@ -571,11 +644,11 @@ hipError_t launch_verify_sample(const SampleParams &p, hipStream_t s) {
   // vectors in flight per batch of a run: all of a run of 8 ids, else 8
   const FastDiv b_div = host_fast_div((uint32_t)p.B);
   if (vec && p.R == 8)
-    hipLaunchKernelGGL((k_verify_sample<4, 2>), grid, dim3(kSampleThreads), 0, s, p, b_div);
+    hipLaunchKernelGGL((k_verify_sample<4, 2, true>), grid, dim3(kSampleThreads), 0, s, p, b_div);
   else if (vec)
-    hipLaunchKernelGGL((k_verify_sample<4, kSampleBatch>), grid, dim3(kSampleThreads), 0, s, p, b_div);
+    hipLaunchKernelGGL((k_verify_sample<4, kSampleBatch, false>), grid, dim3(kSampleThreads), 0, s, p, b_div);
   else
-    hipLaunchKernelGGL((k_verify_sample<1, 1>), grid, dim3(kSampleThreads), 0, s, p, b_div);
+    hipLaunchKernelGGL((k_verify_sample<1, 1, false>), grid, dim3(kSampleThreads), 0, s, p, b_div);
   return hipGetLastError();
 }
 
