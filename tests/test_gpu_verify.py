@@ -330,6 +330,34 @@ def test_sample_zero_row_status(sd):
     assert int(status.item()) & sd.S_PROB
 
 
+@pytest.mark.parametrize("V", [32000, 151936, 4097])
+def test_sample_zero_residual_falls_back_to_p(sd, V):
+    """Unnormalised inputs where p = q / 2 at the first position: u = 0.9
+    rejects the draft there, max(0, p - q) has no mass, and the draw falls back
+    to p at that position (runs of 8 ids walked from registers, longer runs,
+    and the scalar path)."""
+    rng = np.random.default_rng(77 + V)
+    B, D = 5, 2
+    say("sample zero residual", V)
+    q = rng.random((B, D, V)).astype(np.float32)
+    q /= q.sum(-1, keepdims=True)
+    p = rng.random((B, D + 1, V)).astype(np.float32)
+    p /= p.sum(-1, keepdims=True)
+    p[:, 0] = 0.5 * q[:, 0]
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    u_acc = np.full((B, D), 0.9, np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    u_draw[0, 0] = 1.0 - 2.0 ** -24
+    u_draw[1, 0] = 0.0
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)), status=status)
+    torch.cuda.synchronize()
+    acc, nxt = acc.cpu().numpy(), nxt.cpu().numpy()
+    assert np.all(acc == 0)
+    _check_sampled(p, q, draft, u_acc, u_draw, acc, nxt)
+    assert int(status.item()) == 0
+
+
 def test_greedy_longest_draft(sd):
     """D = 255, the longest draft the kernel accepts (D + 1 = 256 positions)."""
     say("greedy D=255")
