@@ -129,6 +129,17 @@ __device__ __forceinline__ FastDiv fast_div(uint32_t d) {
   return f;
 }
 
+// The same s and m computed on the host, for divisors fixed per launch.
+inline FastDiv host_fast_div(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1ull);
+  return f;
+}
+
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
   return (uint32_t)(((unsigned long long)__umulhi(n, f.m) + n) >> f.s);
 }

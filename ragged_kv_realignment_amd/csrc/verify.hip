@@ -265,18 +265,6 @@ static long greedy_chunk(int B, int D, int V, int dtype) {
   return chunk;
 }
 
-// Host construction of FastDiv (the same s and m as fast_div in
-// device_common.h), for divisors fixed per launch.
-static FastDiv host_fast_div(uint32_t d) {
-  FastDiv f;
-  f.d = d;
-  uint32_t s = 0;
-  while ((1ull << s) < d) ++s;
-  f.s = s;
-  f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1ull);
-  return f;
-}
-
 template <int DT>
 static hipError_t launch_greedy_dt(const GreedyParams &p, hipStream_t s) {
   const long rows = (long)p.B * (p.D + 1);

@@ -229,7 +229,8 @@ def test_paged_chain_8b_gqa(sd):
 
 def test_paged_status_bits_write_nothing(sd):
     """Too few free pages, a row past its block capacity, a rectangle view too
-    narrow, accepted lengths out of range, a bad row, duplicate rows and an
+    narrow, accepted lengths out of range, a bad row, duplicate rows, a free
+    stack whose top is no page id or whose count exceeds the pages, and an
     admit into a row that is not empty: each sets its bit and changes nothing
     (duplicates: the bit only; the result is undefined)."""
     rng = np.random.default_rng(1200)
@@ -245,6 +246,10 @@ def test_paged_status_bits_write_nothing(sd):
     long_row, _, _ = state(np.array([4, 10, 2], np.int32))   # row 1 holds 10 of its 12 positions
     short = base.copy()
     short.n_free[0] = 2                                      # 2 free; acc 3 everywhere needs 3
+    bad_page = base.copy()
+    bad_page.free[bad_page.n_free[0] - 1] = 999              # the top of the free stack is no page
+    bad_count = base.copy()
+    bad_count.n_free[0] = 99                                 # more free entries than pages
     kv_new = torch.from_numpy(rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(np.float16)).cuda()
     draft = torch.zeros((B, D), dtype=torch.int32, device="cuda")
     nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
@@ -258,7 +263,9 @@ def test_paged_status_bits_write_nothing(sd):
              ("accept range", base, I(0, 4, 0), None, 16, sd.S_LEN_RANGE),
              ("accept negative", base, I(0, -1, 0), None, 16, sd.S_LEN_RANGE),
              ("bad row", base, I(0, 0, 0), I(0, 1, 9), 16, sd.S_LEN_RANGE),
-             ("dup rows", base, I(0, 0, 0), I(0, 1, 1), 16, sd.S_ROWS_DUP)]
+             ("dup rows", base, I(0, 0, 0), I(0, 1, 1), 16, sd.S_ROWS_DUP),
+             ("free page id", bad_page, I(3, 3, 3), None, 16, sd.S_LEN_RANGE),
+             ("free count", bad_count, I(3, 3, 3), None, 16, sd.S_LEN_RANGE)]
     for what, st, acc, rows, rcap, bit in cases:
         say("paged status", what)
         cache = _dev_state(sd, st, torch.float16)
