@@ -41,6 +41,27 @@ def test_group_by_len_random(sd, seed):
     assert int(nu.item()) == onu
 
 
+@pytest.mark.parametrize("N,G,kind", [(777, 5, "wide"), (4096, 8, "equal"), (1024, 3, "wide"), (255, 16, "equal")])
+def test_group_by_len_wide_values(sd, N, G, kind):
+    """Lengths over the whole int32 range (negative ones included: ranked as
+    signed integers) and pools of one length, against the oracle."""
+    rng = np.random.default_rng(N + G)
+    if kind == "wide":
+        vals = rng.integers(-2**31, 2**31 - 1, 40, dtype=np.int64).astype(np.int32)
+        vals[:3] = (-2**31, 2**31 - 1, 0)
+        lens = vals[rng.integers(0, len(vals), N)]
+    else:
+        lens = np.full(N, 1234, np.int32)
+    say("group_by_len", kind, N, G)
+    order, uni, wid, nu = sd.group_by_len(torch.from_numpy(lens).cuda(), G)
+    torch.cuda.synchronize()
+    oorder, ouni, owid, onu = oracle.group_by_len(lens, G)
+    assert np.array_equal(order.cpu().numpy(), oorder)
+    assert np.array_equal(uni.cpu().numpy(), ouni)
+    assert np.array_equal(wid.cpu().numpy(), owid)
+    assert int(nu.item()) == onu
+
+
 def test_group_by_len_host_errors(sd):
     say("group_by_len host errors")
     with pytest.raises(sd.SpecDecError):
