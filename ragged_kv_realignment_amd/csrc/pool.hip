@@ -180,12 +180,30 @@ __global__ __launch_bounds__(kPoolThreads) void k_pool_admit_plan(PoolParams p) 
     p.len[s] = p.plen[q];
   }
   for (int i = k + (int)threadIdx.x; i < nf; i += kPoolThreads) p.free_slots[i - k] = s_fr[i];
-  // token ids of the admitted prompts
-  for (int i = 0; i < k; ++i) {
-    const int q = qh + i, n = p.plen[q];
-    int32_t *to = p.tokens + (size_t)s_fr[i] * p.cap;
-    const int32_t *from = p.ptok + (size_t)q * p.pcap;
-    for (int j = threadIdx.x; j < n; j += kPoolThreads) to[j] = from[j];
+  // token ids of the admitted prompts: one wave per prompt, the waves over
+  // the prompts at once, eight loads per lane in flight (positions past the
+  // prompt re-read its first token and are not stored)
+  {
+    constexpr int kR = 8;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    for (int i = w; i < k; i += kPoolThreads / kWave) {
+      const int q = qh + i, n = p.plen[q];
+      int32_t *to = p.tokens + (size_t)s_fr[i] * p.cap;
+      const int32_t *from = p.ptok + (size_t)q * p.pcap;
+      for (int j0 = lane; j0 < n; j0 += kWave * kR) {
+        int v[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const int j = j0 + r * kWave;
+          v[r] = from[j < n ? j : 0];
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const int j = j0 + r * kWave;
+          if (j < n) to[j] = v[r];
+        }
+      }
+    }
   }
   if (threadIdx.x == 0) {
     *p.n_active = na + k;
@@ -212,18 +230,42 @@ __global__ __launch_bounds__(256) void k_pool_admit_copy(PoolParams p) {
     const int q = q0 + i, s = p.admitted[i], n = p.plen[q];
     const i32x4q *from = src + ((((size_t)lk * p.Q + q) * H + h) * p.pcap) * U;
     i32x4q *to = dst + ((((size_t)lk * p.slots + s) * H + h) * p.cap) * U;
-    // four 16-byte units per thread in flight before their stores
-    for (int u0 = threadIdx.x; u0 < n * U; u0 += 4 * 256) {
-      i32x4q v[4];
+    // four 16-byte units per thread per step, two steps in flight: a step's
+    // loads are issued two steps ahead, each right after the stores of the
+    // registers they refill, so (the vector-memory counter being in order) the
+    // wait for a step's loads never covers earlier stores.  Units past the
+    // sequence re-read its first unit and are not stored, so no load sits
+    // behind a branch.
+    const int nu = n * U;
+    if (nu <= 0) continue;
+    constexpr int kStep = 4 * 256;
+    i32x4q a[4], b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int ua = threadIdx.x + t * 256, ub = ua + kStep;
+      a[t] = __builtin_nontemporal_load(from + (ua < nu ? ua : 0));
+      b[t] = __builtin_nontemporal_load(from + (ub < nu ? ub : 0));
+    }
+    for (int u0 = threadIdx.x; u0 < nu; u0 += 2 * kStep) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int u = u0 + t * 256;
-        if (u < n * U) v[t] = __builtin_nontemporal_load(from + u);
+        if (u < nu) to[u] = a[t];
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int u = u0 + t * 256;
-        if (u < n * U) to[u] = v[t];
+        const int u = u0 + 2 * kStep + t * 256;
+        a[t] = __builtin_nontemporal_load(from + (u < nu ? u : 0));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int u = u0 + kStep + t * 256;
+        if (u < nu) to[u] = b[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int u = u0 + 3 * kStep + t * 256;
+        b[t] = __builtin_nontemporal_load(from + (u < nu ? u : 0));
       }
     }
   }
