@@ -347,3 +347,35 @@ def test_paged_largest_batch(sd):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert bytes_equal(to_np_raw(out.kv)[..., :want["width"], :], want["kv"])
+
+
+def test_paged_append_many_passes(sd):
+    """An append whose speculative KV holds more 16-byte units (4.2M) than the
+    copy grid takes in one pass (3,072 workgroups of 1,024 units), so each copy
+    workgroup loops; no row map, pages of 16; against the oracle."""
+    rng = np.random.default_rng(1220)
+    rows, B, D, L, H, Dh, page = 128, 128, 7, 4, 32, 128, 16
+    maxlen = 12
+    cap = maxlen + D + 1
+    mb = -(-cap // page)
+    n_pages = rows * mb
+    say("paged many passes", L, B, H, D + 1, Dh)
+    st = oracle.PagedState(L, H, Dh, n_pages, page, mb, rows, np.float16,
+                           free_order=rng.permutation(n_pages).astype(np.int32))
+    cache = _dev_state(sd, st, torch.float16)
+    lens = rng.integers(0, maxlen, B).astype(np.int32)
+    S = int(lens.max())
+    kv, tok = _rect(rng, B, L, H, Dh, np.float16, lens, S, cap)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sd.paged_admit(cache, _seqbuf(sd, kv, tok, lens, S, torch.float16), status=status)
+    oracle.paged_admit(st, kv, tok, lens, S)
+    kv_new = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(np.float16)
+    assert kv_new.size * 2 // 16 > 3072 * 1024
+    acc = rng.integers(0, D + 1, B).astype(np.int32)
+    draft = rng.integers(1, 500, (B, D)).astype(np.int32)
+    nxt = rng.integers(1, 500, B).astype(np.int32)
+    sd.paged_append(cache, torch.from_numpy(kv_new).cuda(), torch.from_numpy(draft).cuda(),
+                    torch.from_numpy(acc).cuda(), torch.from_numpy(nxt).cuda(), status=status)
+    oracle.paged_append(st, kv_new, draft, acc, nxt)
+    _same_state(cache, st, "many passes")
+    assert int(status.item()) == 0
