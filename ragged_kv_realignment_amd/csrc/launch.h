@@ -85,10 +85,13 @@ struct SampleLogitsParams {
 #ifndef SPECDEC_SL_THREADS
 #define SPECDEC_SL_THREADS 512
 #endif
+#ifndef SPECDEC_SL_CHUNK
+#define SPECDEC_SL_CHUNK 4096
+#endif
 constexpr int kSlStatThreads = SPECDEC_SL_STAT_THREADS;
 constexpr int kSlStatPer = SPECDEC_SL_STAT_PER;
 constexpr int kSlStatChunk = kSlStatThreads * kSlStatPer;
-constexpr int kSlChunk = 4096;
+constexpr int kSlChunk = SPECDEC_SL_CHUNK;
 constexpr int kSlThreads = SPECDEC_SL_THREADS;
 
 
