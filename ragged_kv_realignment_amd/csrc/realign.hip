@@ -37,6 +37,9 @@ constexpr int kMaxB = kMaxRealignRows;
 #ifndef SPECDEC_RA_TILES_PER_WG
 #define SPECDEC_RA_TILES_PER_WG 2  // EQSPEC grid: tiles of the widest possible output per workgroup
 #endif
+#ifndef SPECDEC_AP_WGS_PER_CU
+#define SPECDEC_AP_WGS_PER_CU 2  // in-place append: workgroups per CU at most
+#endif
 #ifndef SPECDEC_GA_TILES_PER_WG
 #define SPECDEC_GA_TILES_PER_WG 8  // GATHER grid: tiles per workgroup if every group were gathered
 #endif
@@ -414,34 +417,60 @@ __device__ int append_check(const RealignParams &p, int *s_r, int *s_c, int *s_n
   return block_or_int<kRaBlock>(bad, s_red);
 }
 
+// Divisors of the append's sequence numbering, fixed per launch (computed on
+// the host): seg = (lk * B + b) * H + h.
+struct AppendKvDivs {
+  FastDiv bh, h;
+};
+
 // KV entries: tile = one (layer, K|V, entry, head) sequence, n_b positions.
-__global__ __launch_bounds__(kRaBlock) void k_append_kv(RealignParams p) {
+// A workgroup pass covers kRaBlock / ((D+1) U) sequences, one 16-byte unit per
+// thread (unit g of a sequence, g < (D+1) U, copied when g < n_b U).  Each
+// workgroup takes passes s0, s0 + step, ... in two alternating registers: a
+// pass's load is issued two passes ahead, right after the store of the
+// register it refills.  A unit not copied re-reads the sequence's first unit
+// and is not stored, so no load sits behind a branch.  Few workgroups (two per
+// CU) carry many passes: each one first checks the whole batch (two round
+// trips and a reduction), which a pass-per-workgroup grid paid over and over.
+__global__ __launch_bounds__(kRaBlock) void k_append_kv(RealignParams p, AppendKvDivs dv) {
   __shared__ int s_r[kMaxB];
   __shared__ int s_c[kMaxB];
   __shared__ int s_n[kMaxB];
   __shared__ int s_red[kRaBlock / kWave];
   if (append_check(p, s_r, s_c, s_n, s_red)) return;  // reported by k_append_meta
   const int B = p.B, U = p.units, H = p.heads, D1 = p.D + 1;
-  const long nseg = (long)p.layers * 2 * B * H;
-  const char *nw = static_cast<const char *>(p.kv_new);
-  char *pool = static_cast<char *>(p.kv_out);
-  const size_t pos_bytes = (size_t)U * 16;
-  // a workgroup pass covers kRaBlock / ((D+1)*U) sequences
+  const uint32_t nseg = (uint32_t)p.layers * 2u * (uint32_t)B * (uint32_t)H;
+  const i32x4 *nw = static_cast<const i32x4 *>(p.kv_new);
+  i32x4 *pool = static_cast<i32x4 *>(p.kv_out);
   const int ups = D1 * U;
   const int spp = max(1, kRaBlock / ups);
   const int sq = threadIdx.x / ups, f = threadIdx.x - sq * ups;
-  for (long s0 = (long)blockIdx.x * spp; s0 < nseg; s0 += (long)gridDim.x * spp) {
-    const long seg = s0 + sq;
-    if (sq >= spp || seg >= nseg) continue;
-    const long lk = seg / ((long)B * H);
-    const int rem = (int)(seg - lk * B * H);
-    const int b = rem / H, h = rem - b * H;
-    const int r = s_r[b], c = s_c[b], n = s_n[b];
-    const char *src = nw + (size_t)seg * D1 * pos_bytes;
-    char *dst = pool + (((size_t)(lk * p.rows_in + r) * H + h) * p.cap_in + c) * pos_bytes;
-    for (int g = f; g < n * U; g += ups)
-      *reinterpret_cast<i32x4 *>(dst + (size_t)g * 16) =
-          __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + (size_t)g * 16));
+  const uint32_t step = gridDim.x * (uint32_t)spp;
+  // this thread's unit of pass s0: its source, and its destination or SIZE_MAX
+  auto unit = [&](uint32_t s0, size_t &src, size_t &dst) {
+    const uint32_t seg = s0 + (uint32_t)sq;
+    src = 0;
+    dst = SIZE_MAX;
+    if (sq >= spp || seg >= nseg) return;
+    const uint32_t lk = fdiv(seg, dv.bh), rem = seg - lk * (uint32_t)(B * H);
+    const uint32_t b = fdiv(rem, dv.h), h = rem - b * (uint32_t)H;
+    src = (size_t)seg * ups;
+    if (f >= s_n[b] * U) return;
+    src += f;
+    dst = (((size_t)lk * p.rows_in + s_r[b]) * H + h) * (size_t)p.cap_in * U + (size_t)s_c[b] * U + f;
+  };
+  size_t sa, da, sb, db;
+  const uint32_t s0 = blockIdx.x * (uint32_t)spp;
+  unit(s0, sa, da);
+  unit(s0 + step, sb, db);
+  i32x4 a = __builtin_nontemporal_load(nw + sa), b = __builtin_nontemporal_load(nw + sb);
+  for (uint32_t s = s0; s < nseg; s += 2 * step) {
+    if (da != SIZE_MAX) pool[da] = a;
+    unit(s + 2 * step, sa, da);
+    a = __builtin_nontemporal_load(nw + sa);
+    if (db != SIZE_MAX) pool[db] = b;
+    unit(s + 3 * step, sb, db);
+    b = __builtin_nontemporal_load(nw + sb);
   }
 }
 
@@ -502,11 +531,15 @@ hipError_t launch_realign(const RealignParams &p, hipStream_t s) {
     else
       hipLaunchKernelGGL(k_gather<kPassesShort>, dim3(grid), dim3(kRaBlock), 0, s, p);
   } else {
+    // a few workgroups per CU, each carrying many passes
     const long ups = (long)(p.D + 1) * p.units;
     const long spp = ups < kRaBlock ? kRaBlock / ups : 1;
-    const long nseg = ((long)p.layers * 2 * p.B * p.heads + spp - 1) / spp;
-    const long g = nseg < grid ? nseg : grid;
-    hipLaunchKernelGGL(k_append_kv, dim3((unsigned)(g > 0 ? g : 1)), dim3(kRaBlock), 0, s, p);
+    const long passes = ((long)p.layers * 2 * p.B * p.heads + spp - 1) / spp;
+    const long g = passes < SPECDEC_AP_WGS_PER_CU * (long)cus ? passes : SPECDEC_AP_WGS_PER_CU * (long)cus;
+    AppendKvDivs dv;
+    dv.bh = host_fast_div((uint32_t)(p.B * p.heads));
+    dv.h = host_fast_div((uint32_t)p.heads);
+    hipLaunchKernelGGL(k_append_kv, dim3((unsigned)(g > 0 ? g : 1)), dim3(kRaBlock), 0, s, p, dv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_append_meta, dim3(1), dim3(kRaBlock), 0, s, p);
