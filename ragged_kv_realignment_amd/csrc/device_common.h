@@ -69,6 +69,35 @@ __device__ __forceinline__ int block_or_int(int v, int *scratch) {
   return r;
 }
 
+// Whether two of the n non-negative values v[0..n) are equal (n <= TAB / 2,
+// TAB a power of two): each value is inserted into an open-addressing table
+// of TAB ints in LDS by compare-and-swap (multiplicative hash, linear
+// probing); an insert that meets its own value has found a duplicate.  At most
+// half the table fills, so every probe sequence ends at an empty slot.  Every
+// thread of the workgroup calls it; the result is the same in all of them.
+template <int NT, int TAB>
+__device__ __forceinline__ int block_any_duplicate(const int *v, int n, int *tab, int *scratch) {
+  static_assert((TAB & (TAB - 1)) == 0, "the table size is a power of two");
+  constexpr int kShift = 32 - __builtin_ctz(TAB);
+  for (int i = threadIdx.x; i < TAB; i += NT) tab[i] = -1;
+  __syncthreads();
+  int dup = 0;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const int x = v[i];
+    uint32_t h = ((uint32_t)x * 2654435761u) >> kShift;
+    while (true) {
+      const int old = atomicCAS(&tab[h], -1, x);
+      if (old == -1) break;
+      if (old == x) {
+        dup = 1;
+        break;
+      }
+      h = (h + 1) & (TAB - 1);
+    }
+  }
+  return block_or_int<NT>(dup, scratch);
+}
+
 template <int NT = kBlock>
 __device__ __forceinline__ float block_max_float(float v, float *scratch) {
 #pragma unroll

@@ -379,10 +379,8 @@ __device__ __forceinline__ bool arrive_finish(const PagedParams &p, PagedPlan &s
 template <bool ADMIT>
 __device__ void paged_commit_tables(const PagedParams &p, PagedPlan &s) {
   const int B = p.B, tcap = p.max_blocks * p.page;
-  int dup = 0;
-  for (int b = threadIdx.x; b < B; b += kPgBlock)
-    for (int o = 0; o < b; ++o) dup |= (s.r[o] == s.r[b]);
-  dup = block_or_int<kPgBlock>(dup, s.red);
+  __shared__ int s_tab[2 * kMaxRealignRows];
+  const int dup = block_any_duplicate<kPgBlock, 2 * kMaxRealignRows>(s.r, B, s_tab, s.red);
   for (int b = threadIdx.x; b < B; b += kPgBlock) {
     const int r = s.r[b], c = s.c[b], n = s.n[b];
     const int nb0 = blocks_for(c, p.page), nb1 = blocks_for(c + n, p.page);

@@ -487,10 +487,8 @@ __global__ __launch_bounds__(kRaBlock) void k_append_meta(RealignParams p) {
     return;
   }
   const int B = p.B;
-  int dup = 0;
-  for (int b = threadIdx.x; b < B; b += kRaBlock)
-    for (int o = 0; o < b; ++o) dup |= (s_r[o] == s_r[b]);
-  dup = block_or_int<kRaBlock>(dup, s_red);
+  __shared__ int s_tab[2 * kMaxB];
+  const int dup = block_any_duplicate<kRaBlock, 2 * kMaxB>(s_r, B, s_tab, s_red);
   for (int b = threadIdx.x; b < B; b += kRaBlock) {
     const int r = s_r[b], c = s_c[b], n = s_n[b], a = n - 1;
     if (p.tok_out) {

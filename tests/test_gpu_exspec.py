@@ -152,6 +152,41 @@ def test_gather_append_small(sd):
     assert int(status.item()) & sd.S_ROWS_DUP
 
 
+@pytest.mark.parametrize("dup_at", [None, (0, 1023), (511, 512), (3, 900)])
+def test_append_duplicate_rows_large_batch(sd, dup_at):
+    """1,024 batch entries (the limit) naming distinct pool rows, or two of
+    them naming the same row: the duplicate is found wherever it sits (status
+    bit), and distinct rows never raise it (the append then matches the
+    oracle)."""
+    rng = np.random.default_rng(1300 if dup_at is None else 1300 + dup_at[0])
+    rows_n, B, D, L, H, Dh, cap = 1100, 1024, 2, 1, 1, 8, 16
+    lens = rng.integers(0, 10, rows_n).astype(np.int32)
+    kv = rng.standard_normal((L, 2, rows_n, H, cap, Dh)).astype(np.float16)
+    tok = rng.integers(1, 100, (rows_n, cap)).astype(np.int32)
+    rows = rng.permutation(rows_n)[:B].astype(np.int32)
+    if dup_at is not None:
+        rows[dup_at[1]] = rows[dup_at[0]]
+    kv_new = rng.standard_normal((L, 2, B, H, D + 1, Dh)).astype(np.float16)
+    acc = rng.integers(0, D + 1, B).astype(np.int32)
+    draft = rng.integers(1, 100, (B, D)).astype(np.int32)
+    nxt = rng.integers(1, 100, B).astype(np.int32)
+    say("append dup large", dup_at)
+    pool = sd.SeqBuf(torch.from_numpy(kv).cuda(), torch.from_numpy(tok).cuda(), torch.from_numpy(lens).cuda())
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sd.append(pool, torch.from_numpy(kv_new).cuda(), torch.from_numpy(draft).cuda(), torch.from_numpy(acc).cuda(),
+              torch.from_numpy(nxt).cuda(), rows=torch.from_numpy(rows).cuda(), status=status)
+    torch.cuda.synchronize()
+    if dup_at is not None:
+        assert int(status.item()) & sd.S_ROWS_DUP
+        return
+    assert int(status.item()) == 0
+    wkv, wtok, wlen = kv.copy(), tok.copy(), lens.copy()
+    oracle.append(wkv, wtok, wlen, rows, kv_new, draft, acc, nxt)
+    assert bytes_equal(to_np_raw(pool.kv), wkv)
+    assert np.array_equal(pool.tokens.cpu().numpy(), wtok)
+    assert np.array_equal(pool.len.cpu().numpy(), wlen)
+
+
 def test_exspec_pool_workload(sd):
     """The 256-sequence pool (40 layers x 2 KV heads x 128, bf16), 32 rounds:
     group by length, gather mixed batches, verify all rows, append in place."""
