@@ -255,52 +255,96 @@ __global__ __launch_bounds__(kSlStatThreads) void k_sl_stats(SampleLogitsParams 
 #define SPECDEC_NUC_THREADS 512
 #endif
 constexpr int kNucThreads = SPECDEC_NUC_THREADS;  // threads per nucleus workgroup
-constexpr int kNucBins = 2048;      // first level: bins in y = (M - x) / T
+constexpr int kNucBins = 2048;      // first level: bins in u = -kNucScale t
 constexpr int kNucSub = 1024;       // later levels: bins in the order key
 constexpr int kNucUnroll = 4;       // 16-byte vectors in flight per thread
+// three workgroups per CU (their LDS fits; 768 rows resident at once): at
+// most 80 VGPRs
+#ifndef SPECDEC_NUC_WAVES
+#define SPECDEC_NUC_WAVES 6
+#endif
+constexpr int kNucWavesPerSimd = SPECDEC_NUC_WAVES;
 constexpr double kFix = 2199023255552.0;  // 2^41: V <= 2^22 masses <= 1 sum below 2^63
-// exp(-y) * 2^41 < 0.5 (a fixed-point mass of 0) for every y >= kNucSpan
-constexpr double kNucSpan = 29.2;
-constexpr double kNucScale = kNucBins / kNucSpan;
+// 2^t * 2^41 rounds to a fixed-point mass of 0 for every t <= -kNucSpan: the
+// first level's bins are units of u = -t kNucScale over (-kNucSpan, 0] (u <
+// 2016, the top 2016 of the bins), and logits past it (with -inf and NaN) go to
+// one spare slot per lane past the bins, which no selection reads
+constexpr double kNucSpan = 42.0;
+constexpr double kNucScale = 48.0;
+constexpr int kNucSlots = kNucBins + kWave;
+static_assert(kNucSpan * kNucScale < kNucBins, "u below the bin count");
 
 // Order key of a logit: larger key = larger value; -0.0 is folded onto +0.0
-// so equal values share a key.
+// (by adding +0.0) so equal values share a key.
 __device__ __forceinline__ uint32_t order_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// The largest float at or below d, and the smallest at or above it.
+__device__ __forceinline__ float float_below(double d) {
+  const float f = (float)d;
+  return (double)f > d ? nextafterf(f, -INFINITY) : f;
+}
+__device__ __forceinline__ float float_above(double d) {
+  const float f = (float)d;
+  return (double)f < d ? nextafterf(f, INFINITY) : f;
+}
+
+// The fixed-point mass round(2^t * 2^41) (ties to even) for -kNucSpan < t <= 0:
+// 2^t = e 2^n as in exp2_fast, e the fp32 exp2 of the fraction; e 2^(n + 41) <
+// 2^42 is exact in fp64, and adding 2^52 rounds it to an integer that the low
+// 52 bits of the sum hold.
+__device__ __forceinline__ unsigned long long fixed41(double t) {
+  const double n = rint(t);
+  const float e = __builtin_amdgcn_exp2f((float)(t - n));
+  const double v = ldexp((double)e, (int)n + 41);
+  return (unsigned long long)__double_as_longlong(v + 0x1p52) & 0xFFFFFFFFFFFFFull;
+}
+
+// The logits of one 16-byte vector, in order: f(x).
+template <int DT, class F>
+__device__ __forceinline__ void each_in_vector(const uint4 &v, F &&f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (DT == SPECDEC_F32) {
+      f(__uint_as_float(w[e]));
+    } else {
+      f(DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] & 0xFFFFu) : bf16_bits_to_f32(w[e] & 0xFFFFu));
+      f(DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] >> 16) : bf16_bits_to_f32(w[e] >> 16));
+    }
+  }
+}
+
 // Every logit of one row for this thread of kNucThreads, in any order: f(x).
+// Vectors go kNucUnroll at a time, every load issued before any is used: whole
+// batches with no test, then the last batch with clamped loads (a repeated
+// load, never used) and a test per vector.
 template <int DT, bool VEC, class F>
 __device__ __forceinline__ void each_logit(const void *base, int64_t off, int V, F &&f) {
   if (VEC) {
     constexpr int E = DT == SPECDEC_F32 ? 4 : 8;
     const int nv = V / E;
-    for (int j0 = threadIdx.x; j0 < nv; j0 += kNucThreads * kNucUnroll) {
+    const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + off * (16 / E));
+    int j0 = threadIdx.x;
+    for (; j0 + (kNucUnroll - 1) * kNucThreads < nv; j0 += kNucThreads * kNucUnroll) {
       uint4 v[kNucUnroll];
 #pragma unroll
-      for (int u = 0; u < kNucUnroll; ++u) {
-        const int j = min(j0 + u * kNucThreads, nv - 1);  // in range: a repeated load, never used
-        v[u] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + (off * (16 / E)) + (int64_t)j * 16);
-      }
+      for (int u = 0; u < kNucUnroll; ++u) v[u] = row[j0 + u * kNucThreads];
 #pragma unroll
-      for (int u = 0; u < kNucUnroll; ++u) {
-        if (j0 + u * kNucThreads >= nv) break;
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      for (int u = 0; u < kNucUnroll; ++u) each_in_vector<DT>(v[u], f);
+    }
+    if (j0 < nv) {
+      uint4 v[kNucUnroll];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (DT == SPECDEC_F32) {
-            f(__uint_as_float(w[e]));
-          } else {
-            f(DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] & 0xFFFFu) : bf16_bits_to_f32(w[e] & 0xFFFFu));
-            f(DT == SPECDEC_F16 ? f16_bits_to_f32(w[e] >> 16) : bf16_bits_to_f32(w[e] >> 16));
-          }
-        }
-      }
+      for (int u = 0; u < kNucUnroll; ++u) v[u] = row[min(j0 + u * kNucThreads, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < kNucUnroll; ++u)
+        if (j0 + u * kNucThreads < nv) each_in_vector<DT>(v[u], f);
     }
   } else {
     for (int i = threadIdx.x; i < V; i += kNucThreads) f(logit_at<DT>(base, off + i));
@@ -367,20 +411,25 @@ __device__ __forceinline__ int nuc_select(const unsigned long long *hist, unsign
 
 // One workgroup per (row r of 2D+1, batch row b): the nucleus threshold t and
 // 1/Z over the nucleus, written to nuc[(b R + r) * 4 + {0, 1, 2}] = (M, 1/Z, t).
-// Masses are exp(-y) with y = (M - x) / T (exp2_fast, about 1e-7 relative
-// error like every mass of this path), rounded to 2^-41 fixed-point integers
-// so every sum is exact and order-free.  t is selected level by level: the
-// first level bins the logits by y (monotone in the logit, and spread over the
-// bins whatever the logits' exponents), the later ones bin the 32-bit order
-// keys of the chosen bin's interval; every level tracks each bin's smallest
-// and largest key, and the levels go on until the chosen bin holds a single
-// key (each later level shrinks the interval at least kNucSub-fold, so at most
-// five follow the first).  Z is the exact sum of the masses at or above t.
-// Each level reads the row once.
+// Masses are 2^t with t = (x - M) (1/T) log2(e), the exponent the other
+// kernels form (2^f by the fp32 exp2 as in exp2_fast, about 1e-7 relative error
+// like every mass of this path), rounded to 2^-41 fixed-point integers so
+// every sum is exact and order-free.  The threshold is selected level by
+// level, each level one read of the row:
+//  - the first bins the logits by the integer part of u = -t kNucScale
+//    (monotone in the logit, and spread over the bins whatever the logits'
+//    exponents), with one LDS atomic per logit;
+//  - the second takes the chosen bin's logits (the same test, repeated) and
+//    bins them by the fraction of u, tracking each bin's smallest and largest
+//    32-bit order key;
+//  - the later ones bin the order keys of the chosen bin's interval in
+//    power-of-two runs of keys, until the chosen bin holds a single key (each
+//    shrinks the interval at least kNucSub / 2-fold, so at most four follow).
+// Z is the exact sum of the masses at or above the threshold.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p) {
-  __shared__ unsigned long long hist[kNucBins];
-  __shared__ uint32_t s_bmin[kNucBins], s_bmax[kNucBins];
+__global__ __launch_bounds__(kNucThreads, kNucWavesPerSimd) void k_sl_nucleus(SampleLogitsParams p) {
+  __shared__ unsigned long long hist[kNucSlots];
+  __shared__ uint32_t s_bmin[kNucSub], s_bmax[kNucSub];
   __shared__ unsigned long long s_wt[kNucThreads / kWave];
   __shared__ double s_d[kNucThreads / kWave];
   __shared__ int s_i[kNucThreads / kWave];
@@ -396,46 +445,64 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
   if (lane == 0) s_d[wv] = m;
-  for (int k = threadIdx.x; k < kNucBins; k += kNucThreads) {
+  for (int k = threadIdx.x; k < kNucSlots; k += kNucThreads) hist[k] = 0;
+  __syncthreads();
+  double M = s_d[0];
+#pragma unroll
+  for (int k = 1; k < kNucThreads / kWave; ++k) M = fmax(M, s_d[k]);
+  const double c2 = p.inv_t * kLog2e, mc2 = M * c2;
+  auto for_each = [&](auto &&f) { each_logit<DT, VEC>(base, off, V, f); };
+  // t of a logit, the exponent of its mass 2^t: x c2 - M c2 in one rounding
+  // (M c2 rounded once: an error near 1e-16 |M c2|, far below the exponential's)
+  auto t_of = [&](float x) { return fma((double)x, c2, -mc2); };
+
+  // first level: bins in u (larger logits in higher bins), with no branch
+  for_each([&](float x) {
+    const double t = t_of(x);
+    const int k = t > -kNucSpan ? kNucBins - 1 - (int)(-t * kNucScale) : kNucBins + lane;  // NaN: spare
+    atomicAdd(&hist[k], fixed41(t));  // a spare slot's sum is never read
+  });
+  __syncthreads();
+  double need = -1.0;
+  const int d0 = nuc_select<kNucBins>(hist, 0ull, need, p.top_p, s_wt, s_i, &s_above, &s_cmass);
+  unsigned long long above = s_above;
+  // second level: the logits of bin d0 (the same test as the first level's),
+  // binned by the fraction of their u
+  for (int k = threadIdx.x; k < kNucSub; k += kNucThreads) {
     hist[k] = 0;
     s_bmin[k] = 0xFFFFFFFFu;
     s_bmax[k] = 0;
   }
   __syncthreads();
-  double M = s_d[0];
-#pragma unroll
-  for (int k = 1; k < kNucThreads / kWave; ++k) M = fmax(M, s_d[k]);
-  const double inv_t = p.inv_t;
-  auto for_each = [&](auto &&f) { each_logit<DT, VEC>(base, off, V, f); };
-  // y of a logit, and the first level's bin (larger logits in higher bins)
-  auto y_of = [&](float x) { return (M - (double)x) * inv_t; };
-  auto bin0 = [&](double y) { return kNucBins - 1 - min(kNucBins - 1, max(0, (int)(y * kNucScale))); };
-  auto fixed_mass = [&](double y) -> unsigned long long {
-    return (unsigned long long)(exp2_fast(-y * kLog2e) * kFix + 0.5);
-  };
-
-  // first level: bins in y
+  const int u0 = kNucBins - 1 - d0;
+  // the bin's logits lie in [M - (u0 + 1) w, M - u0 w], w = 1 / (kNucScale c2);
+  // a float interval a thousandth of w wider, rounded outwards, is tested first
+  const double w = 1.0 / (kNucScale * c2);
+  const float xlo = float_below(M - (double)(u0 + 1) * w - 1e-3 * w);
+  const float xhi = float_above(M - (double)u0 * w + 1e-3 * w);
   for_each([&](float x) {
-    const double y = y_of(x);
-    if (y < kNucSpan) {  // false for -inf logits
-      const int k = bin0(y);
-      const unsigned long long fx = fixed_mass(y);
-      if (fx) atomicAdd(&hist[k], fx);
+    if (!(x >= xlo && x <= xhi)) return;
+    const double t = t_of(x);
+    const double u = -t * kNucScale;
+    const int ui = (int)u;
+    if (t > -kNucSpan && ui == u0) {
+      const int sb = kNucSub - 1 - (int)((u - (double)ui) * kNucSub);  // u - ui is exact, in [0, 1)
+      atomicAdd(&hist[sb], fixed41(t));
       const uint32_t key = order_key(x);
-      atomicMin(&s_bmin[k], key);
-      atomicMax(&s_bmax[k], key);
+      atomicMin(&s_bmin[sb], key);
+      atomicMax(&s_bmax[sb], key);
     }
   });
   __syncthreads();
-  double need = -1.0;
-  const int d0 = nuc_select<kNucBins>(hist, 0ull, need, p.top_p, s_wt, s_i, &s_above, &s_cmass);
-  uint32_t lo = s_bmin[d0], hi = s_bmax[d0];
-  unsigned long long above = s_above;
+  const int d1 = nuc_select<kNucSub>(hist, above, need, p.top_p, s_wt, s_i, &s_above, &s_cmass);
+  uint32_t lo = s_bmin[d1], hi = s_bmax[d1];
+  above = s_above;
   __syncthreads();  // every thread has the interval before the bins are cleared
   // later levels: bins in the key over [lo, hi]
 #pragma unroll 1
   for (int level = 0; level < 8 && lo != hi; ++level) {
-    const unsigned long long width = (unsigned long long)(hi - lo) + 1ull;
+    // bins of 2^sh keys: (hi - lo) >> sh < kNucSub, and the interval shrinks at least kNucSub / 2-fold
+    const int sh = max(0, 32 - __clz(hi - lo) - 10);
     for (int k = threadIdx.x; k < kNucSub; k += kNucThreads) {
       hist[k] = 0;
       s_bmin[k] = 0xFFFFFFFFu;
@@ -445,9 +512,8 @@ __global__ __launch_bounds__(kNucThreads) void k_sl_nucleus(SampleLogitsParams p
     for_each([&](float x) {
       const uint32_t key = order_key(x);
       if (key >= lo && key <= hi) {
-        const int sb = (int)(((unsigned long long)(key - lo) * kNucSub) / width);
-        const double y = y_of(x);
-        const unsigned long long fx = y < kNucSpan ? fixed_mass(y) : 0ull;
+        const int sb = (int)((key - lo) >> sh);
+        const unsigned long long fx = fixed41(t_of(x));  // in the interval: t > -kNucSpan
         if (fx) atomicAdd(&hist[sb], fx);
         atomicMin(&s_bmin[sb], key);
         atomicMax(&s_bmax[sb], key);

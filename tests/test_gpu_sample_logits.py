@@ -327,6 +327,44 @@ def test_top_p_random(sd, seed):
     check_round(h_t, h_d, draft, u_acc, u_draw, T, acc, nxt, top_p, cut)
 
 
+@pytest.mark.parametrize("case", ["offset", "coarse_floats", "small_scale", "cold", "hot", "hot_bf16"])
+def test_top_p_scales(sd, case):
+    """Logit scales and temperatures at the edges of the selection's binning:
+    logits near 3e4 and near 1e6 (float spacing as wide as, or wider than, a
+    first-level bin, and many ties), logits of size 1e-3 at T = 1e-4, cold rows
+    (T = 0.02: most masses round to 0) and hot rows (T = 50: hundreds of logits
+    in the chosen first-level bin)."""
+    rng = np.random.default_rng(97)
+    B, D, V = 4, 3, 6007
+    base = rng.standard_normal((B, D + 1, V))
+    T, tdt = 1.0, torch.float32
+    if case == "offset":
+        tl = base * 2 + 3.0e4
+    elif case == "coarse_floats":
+        tl = base * 3 + 1.0e6
+    elif case == "small_scale":
+        tl, T = base * 1e-3, 1e-4
+    elif case == "cold":
+        tl, T = base * 2, 0.02
+    else:
+        tl, T = base * 2, 50.0
+        tdt = torch.bfloat16 if case == "hot_bf16" else torch.float32
+    tl = tl.astype(np.float32)
+    dl = (tl[:, :D] + rng.standard_normal((B, D, V)) * (0.2 * float(tl.std()))).astype(np.float32)
+    draft = dl.argmax(-1).astype(np.int32)
+    draft[:, 1] = rng.integers(0, V, B)
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    say("sample logits top_p scales", case)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, T, tdt, status=status, top_p=0.9, want_cut=True)
+    assert int(status.item()) == 0
+    h_t, h_d = _host_logits(tl, tdt), _host_logits(dl, tdt)
+    *_, ocut = oracle.verify_sample_logits(h_t, h_d, draft, u_acc, u_draw, T, 0.9, return_cut=True)
+    assert np.mean(cut == ocut) > 0.9, case  # the thresholds agree outside the band
+    check_round(h_t, h_d, draft, u_acc, u_draw, T, acc, nxt, 0.9, cut)
+
+
 def test_top_p_large_vocab_bf16(sd):
     """A 151936-entry bf16 vocabulary with top_p 0.9."""
     rng = np.random.default_rng(91)
