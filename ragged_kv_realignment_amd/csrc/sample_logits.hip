@@ -450,11 +450,10 @@ __global__ __launch_bounds__(kNucThreads, kNucWavesPerSimd) void k_sl_nucleus(Sa
   double M = s_d[0];
 #pragma unroll
   for (int k = 1; k < kNucThreads / kWave; ++k) M = fmax(M, s_d[k]);
-  const double c2 = p.inv_t * kLog2e, mc2 = M * c2;
+  const double c2 = p.inv_t * kLog2e;
   auto for_each = [&](auto &&f) { each_logit<DT, VEC>(base, off, V, f); };
-  // t of a logit, the exponent of its mass 2^t: x c2 - M c2 in one rounding
-  // (M c2 rounded once: an error near 1e-16 |M c2|, far below the exponential's)
-  auto t_of = [&](float x) { return fma((double)x, c2, -mc2); };
+  // t of a logit, the exponent of its mass 2^t, as the other kernels form it
+  auto t_of = [&](float x) { return ((double)x - M) * c2; };
 
   // first level: bins in u (larger logits in higher bins), with no branch
   for_each([&](float x) {
