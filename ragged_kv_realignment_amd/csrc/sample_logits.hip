@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kSlStatThreads) void k_sl_stats(SampleLogitsParams 
 constexpr int kNucThreads = SPECDEC_NUC_THREADS;  // threads per nucleus workgroup
 constexpr int kNucBins = 2048;      // first level: bins in u = -kNucScale t
 constexpr int kNucSub = 1024;       // later levels: bins in the order key
-constexpr int kNucUnroll = 4;       // 16-byte vectors in flight per thread
+constexpr int kNucUnroll = 3;       // 16-byte vectors in flight per thread (4 spills under the VGPR cap)
 // three workgroups per CU (their LDS fits; 768 rows resident at once): at
 // most 80 VGPRs
 #ifndef SPECDEC_NUC_WAVES
