@@ -21,9 +21,10 @@
 //     split that holds the row's draft token also leaves that token's logit.
 //  1b. k_sl_nucleus (top-p only): one workgroup per (row, batch row) selects t
 //     level by level, each level one read of the row: the first bins the
-//     logits by y = (M - l) / T, the later ones bin the order keys of the
-//     chosen bin's interval; masses are 2^-41 fixed-point integers, so every
-//     sum is exact and order-free, and Z is the fixed-point mass at or above t.
+//     logits by (M - l) / T, the second the chosen bin's logits more finely,
+//     the later ones the order keys of the chosen bin's interval; masses are
+//     2^-41 fixed-point integers, so every sum is exact and order-free, and Z
+//     is the fixed-point mass at or above t.
 //  2. k_sl_mass: one workgroup per (split, batch row) evaluates every
 //     acceptance test (the same result in every workgroup of a batch row) and
 //     sums the stop row's residual mass max(0, p - q) (or p at position D) over
