@@ -365,6 +365,37 @@ def test_top_p_scales(sd, case):
     check_round(h_t, h_d, draft, u_acc, u_draw, T, acc, nxt, 0.9, cut)
 
 
+@pytest.mark.parametrize("case", ["random_f32", "flat_f32", "random_bf16"])
+def test_max_vocab(sd, case):
+    """The largest vocabulary the call takes, 2^22 ids: 1,024 statistics and
+    mass splits per row, and with all target logits equal the nucleus's
+    fixed-point total at its bound (2^22 masses of 2^41 units sum to 2^63);
+    top_p 1 and 0.9."""
+    rng = np.random.default_rng(99)
+    B, D, V = 1, 2, 1 << 22
+    tdt = torch.bfloat16 if case == "random_bf16" else torch.float32
+    say("sample logits max vocab", case)
+    if case == "flat_f32":
+        tl = np.full((B, D + 1, V), 0.5, np.float32)
+        dl = np.full((B, D, V), 0.5, np.float32)
+        dl[..., : V // 2] = 0.25  # q below p on half the ids: a residual to draw from
+    else:
+        tl = (rng.standard_normal((B, D + 1, V)) * 2).astype(np.float32)
+        dl = (tl[:, :D] + rng.standard_normal((B, D, V)) * 0.5).astype(np.float32)
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    draft[0, 0] = int(np.argmax(dl[0, 0]))
+    u_acc = rng.random((B, D)).astype(np.float32)
+    u_draw = rng.random((B, D + 1)).astype(np.float32)
+    h_t, h_d = _host_logits(tl, tdt), _host_logits(dl, tdt)
+    for top_p in (1.0, 0.9):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        acc, nxt, cut = _run(sd, tl, dl, draft, u_acc, u_draw, 1.0, tdt, status=status, top_p=top_p, want_cut=True)
+        assert int(status.item()) == 0, (case, top_p)
+        if case == "flat_f32" and top_p < 1.0:  # every target id ties at the threshold
+            assert np.all(cut[:, :D + 1] == 0.5)
+        check_round(h_t, h_d, draft, u_acc, u_draw, 1.0, acc, nxt, top_p, cut if top_p < 1.0 else None)
+
+
 def test_top_p_large_vocab_bf16(sd):
     """A 151936-entry bf16 vocabulary with top_p 0.9."""
     rng = np.random.default_rng(91)
