@@ -441,3 +441,29 @@ def test_greedy_full_shape_unplanted_natural_ties(sd):
         assert np.array_equal(gtgt, otgt) and np.array_equal(acc, oacc) and np.array_equal(nxt, onxt)
         assert st == 0
     assert cross_rows >= 10, "the draws should tie at the maximum across splits in several rows"
+
+
+def test_greedy_max_vocab(sd):
+    """The largest vocabulary the call takes, 2^30 ids (one batch row, D = 1:
+    two bf16 rows of 2 GiB, 131,072 workgroups per row): random finite logits
+    below 2 in magnitude, the maximum 3.0 planted at three ids of row 0 (the
+    lowest, 5, far from the others, so splits across the whole row compete) and
+    at the last id of row 1 (the bonus)."""
+    B, D, V = 1, 1, 1 << 30
+    say("greedy max vocab", V)
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 1 << 16, size=(B * (D + 1), V), dtype=np.uint16)
+    bits &= np.uint16(0xBFFF)  # exponent at most 127: finite, |x| < 2
+    bits[0, [V - 1, V // 2 + 7, 5]] = np.uint16(0x4040)  # 3.0
+    bits[1, V - 1] = np.uint16(0x4040)
+    draft = np.array([[5]], np.int32)
+    logits = torch.from_numpy(bits).cuda().view(torch.bfloat16).reshape(B, D + 1, V)
+    tgt = torch.empty((B, D + 1), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_greedy(logits, torch.from_numpy(draft).cuda(), status=status, target_tok=tgt)
+    torch.cuda.synchronize()
+    oacc, onxt, otgt = oracle.verify_greedy(bits, draft, B, D, V)
+    assert np.array_equal(otgt, [[5, V - 1]])
+    assert np.array_equal(tgt.cpu().numpy(), otgt) and int(status.item()) == 0
+    assert np.array_equal(acc.cpu().numpy(), oacc) and np.array_equal(nxt.cpu().numpy(), onxt)
+    assert int(oacc[0]) == 1 and int(onxt[0]) == V - 1
