@@ -246,6 +246,30 @@ def test_sample_many_splits(sd, V):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("V", [1 << 26, (1 << 24) + 3])
+def test_sample_long_runs(sd, V):
+    """Vocabularies far past the 16 x 256 runs a row is cut into, so every run
+    holds thousands of ids (16,384 at V = 2^26; an odd V takes the scalar
+    path): sums and the draw's walk over long runs, draws at the top, the
+    bottom and the middle of the mass, against the oracle within the band."""
+    rng = np.random.default_rng(V % 1000)
+    B, D = 3, 1
+    say("sample long runs", V)
+    p = rng.random((B, D + 1, V), dtype=np.float32)
+    p[:, :, : V // 3] *= 0.01  # a third of the ids carry little mass
+    p /= p.sum(-1, keepdims=True, dtype=np.float64).astype(np.float32)
+    q = rng.random((B, D, V), dtype=np.float32)
+    q /= q.sum(-1, keepdims=True, dtype=np.float64).astype(np.float32)
+    draft = rng.integers(0, V, (B, D)).astype(np.int32)
+    u_acc = np.full((B, D), 0.999, np.float32)  # rejections mostly: the residual draw
+    u_draw = np.array([[1.0 - 2.0 ** -24] * (D + 1), [0.0] * (D + 1), [0.5] * (D + 1)], np.float32)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    acc, nxt = sd.verify_sample(*(torch.from_numpy(x).cuda() for x in (p, q, draft, u_acc, u_draw)), status=status)
+    torch.cuda.synchronize()
+    _check_sampled(p, q, draft, u_acc, u_draw, acc.cpu().numpy(), nxt.cpu().numpy())
+    assert int(status.item()) == 0
+
+
 def test_sample_workspace_reused_across_shapes(sd):
     """One workspace, sized for the most rows, serves calls of different
     vocabularies and batch sizes one after another: each row's counter and runs
